@@ -1,0 +1,128 @@
+"""Seeded synthetic inputs for the integer training step.
+
+This module only draws random numbers; it holds none of the method's
+arithmetic.  Both the GPU library's tests/benchmarks and the CPU oracle consume
+the arrays it returns, so the two sides always see identical bytes.
+
+Generator: SplitMix64 (Steele, Lea and Flood, "Fast splittable pseudorandom
+number generators", OOPSLA 2014), used counter-style: element i of stream
+(seed, sid) is mix64(base + (i + 1) * GAMMA) with base = (seed << 32) | sid.
+Uniform integers: lo + (u mod (hi - lo + 1)).  Normals: Box-Muller on
+consecutive pairs, u1 = ((x0 >> 11) + 1) * 2^-53 in (0, 1],
+u2 = (x1 >> 11) * 2^-53, then sigma * z rounded half away from zero and
+clipped.  Stream ids: X=1, W=2, dY=3, labels=4, W1..W3=5..7, exponents of
+X/W/dY = 8..10.
+"""
+import numpy as np
+
+GAMMA = np.uint64(0x9E3779B97F4A7C15)
+_M1 = np.uint64(0xBF58476D1CE4E5B9)
+_M2 = np.uint64(0x94D049BB133111EB)
+_CHUNK = 1 << 22
+
+SID_X, SID_W, SID_DY, SID_LABELS, SID_W1, SID_W2, SID_W3, SID_EX, SID_EW, SID_EDY = range(1, 11)
+
+
+def _mix64(z):
+    z = (z ^ (z >> np.uint64(30))) * _M1
+    z = (z ^ (z >> np.uint64(27))) * _M2
+    return z ^ (z >> np.uint64(31))
+
+
+def splitmix64(seed: int, sid: int, n: int, start: int = 0) -> np.ndarray:
+    """n raw 64-bit outputs of stream (seed, sid), starting at counter `start`."""
+    base = np.uint64(((int(seed) & 0xFFFFFFFF) << 32) | (int(sid) & 0xFFFFFFFF))
+    i = np.arange(start + 1, start + n + 1, dtype=np.uint64)
+    with np.errstate(over="ignore"):
+        return _mix64(base + i * GAMMA)
+
+
+def uniform_int(seed, sid, shape, lo, hi, dtype=np.int8):
+    n = int(np.prod(shape))
+    rng = np.uint64(hi - lo + 1)
+    out = np.empty(n, dtype)
+    for s in range(0, n, _CHUNK):
+        m = min(_CHUNK, n - s)
+        u = splitmix64(seed, sid, m, s)
+        out[s:s + m] = (np.int64(lo) + (u % rng).astype(np.int64)).astype(dtype)
+    return out.reshape(shape)
+
+
+def normal_int(seed, sid, shape, sigma, lo, hi, dtype=np.int8):
+    """round_half_away(sigma * N(0,1)) clipped to [lo, hi]."""
+    n = int(np.prod(shape))
+    npairs = (n + 1) // 2
+    out = np.empty(2 * npairs, dtype)
+    for p0 in range(0, npairs, _CHUNK):
+        pm = min(_CHUNK, npairs - p0)
+        u = splitmix64(seed, sid, 2 * pm, 2 * p0)
+        u1 = ((u[0::2] >> np.uint64(11)).astype(np.float64) + 1.0) * (2.0 ** -53)
+        u2 = (u[1::2] >> np.uint64(11)).astype(np.float64) * (2.0 ** -53)
+        r = np.sqrt(-2.0 * np.log(u1))
+        t = 2.0 * np.pi * u2
+        z = np.empty(2 * pm, np.float64)
+        z[0::2] = r * np.cos(t)
+        z[1::2] = r * np.sin(t)
+        v = sigma * z
+        v = np.sign(v) * np.floor(np.abs(v) + 0.5)
+        out[2 * p0:2 * (p0 + pm)] = np.clip(v, lo, hi).astype(dtype)
+    return out[:n].reshape(shape)
+
+
+# ---------------------------------------------------------------------------
+# The five workloads.  Size arguments default to the full configuration;
+# parity tests pass smaller sizes with the same value distributions.
+# ---------------------------------------------------------------------------
+
+def single_linear(B=16, IN=64, OUT=32, seed=0):
+    """Single int8 linear layer: X ~ U[-128,127], W ~ round(N(0,30)),
+    incoming deltas ~ U[-64,63]."""
+    return dict(
+        X=uniform_int(seed, SID_X, (B, IN), -128, 127),
+        W=normal_int(seed, SID_W, (OUT, IN), 30.0, -128, 127),
+        dY=uniform_int(seed, SID_DY, (B, OUT), -64, 63),
+    )
+
+
+def mlp(B=256, sizes=(784, 256, 128, 10), seed=0):
+    """Int8 MLP: inputs ~ U[0,127], labels ~ U{0..C-1}, W_l ~ round(N(0,25))."""
+    Ws = []
+    for l in range(len(sizes) - 1):
+        Ws.append(normal_int(seed, SID_W1 + l, (sizes[l + 1], sizes[l]), 25.0, -128, 127))
+    return dict(
+        X=uniform_int(seed, SID_X, (B, sizes[0]), 0, 127),
+        labels=uniform_int(seed, SID_LABELS, (B,), 0, sizes[-1] - 1, dtype=np.int32),
+        Ws=Ws,
+    )
+
+
+def large_linear(T=8192, IN=4096, OUT=4096, seed=0):
+    """Large int8 linear layer: X ~ round(N(0,40)), W ~ round(N(0,20)),
+    deltas ~ U[-64,63]."""
+    return dict(
+        X=normal_int(seed, SID_X, (T, IN), 40.0, -128, 127),
+        W=normal_int(seed, SID_W, (OUT, IN), 20.0, -128, 127),
+        dY=uniform_int(seed, SID_DY, (T, OUT), -64, 63),
+    )
+
+
+def conv3x3(N=128, H=56, W=56, Cin=64, Cout=64, seed=0):
+    """Int8 3x3 conv layer (NHWC / OHWI): X ~ U[0,127], W ~ round(N(0,15)),
+    deltas ~ U[-64,63] shaped like the output."""
+    return dict(
+        X=uniform_int(seed, SID_X, (N, H, W, Cin), 0, 127),
+        W=normal_int(seed, SID_W, (Cout, 3, 3, Cin), 15.0, -128, 127),
+        dY=uniform_int(seed, SID_DY, (N, H, W, Cout), -64, 63),
+    )
+
+
+def dfp16_gemm(M=25088, K=256, N=1024, seed=0):
+    """DFP-16 1x1-conv GEMM: int16 mantissas round(N(0,4000)) clipped to the
+    int16 range, one shared exponent per tensor ~ U{-20..-8}."""
+    e = lambda sid: int(uniform_int(seed, sid, (1,), -20, -8, dtype=np.int32)[0])
+    return dict(
+        X=normal_int(seed, SID_X, (M, K), 4000.0, -32768, 32767, dtype=np.int16),
+        W=normal_int(seed, SID_W, (N, K), 4000.0, -32768, 32767, dtype=np.int16),
+        dY=normal_int(seed, SID_DY, (M, N), 4000.0, -32768, 32767, dtype=np.int16),
+        eX=e(SID_EX), eW=e(SID_EW), edY=e(SID_EDY),
+    )

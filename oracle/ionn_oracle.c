@@ -1,0 +1,608 @@
+/*
+ * ionn_oracle.c -- CPU oracle for the integer-only training step.
+ *
+ * TEST INFRASTRUCTURE ONLY (see ionn_oracle.h).  Plain C99, no intrinsics,
+ * no blocking or fusion: every function is the definition written out.
+ * Parallel loops (OpenMP) split independent outputs only, so results do not
+ * depend on the thread count.
+ */
+#include "ionn_oracle.h"
+
+#include <stddef.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+int ora_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+    return omp_get_max_threads();
+#else
+    (void)n;
+    return 1;
+#endif
+}
+
+int ora_get_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* Reinterpret a 32-bit pattern as two's-complement int32 (defined behaviour). */
+static int32_t u32_to_i32(uint32_t u)
+{
+    if (u <= 0x7fffffffu) return (int32_t)u;
+    return -(int32_t)(~u) - 1;
+}
+
+static int exact_in_i32(int64_t v)
+{
+    return v >= -2147483648LL && v <= 2147483647LL;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Primitives.                                                               */
+/* ------------------------------------------------------------------------ */
+
+/* |x| as an unsigned 32-bit value, so |INT32_MIN| = 2^31 is representable
+ * (reading U2). */
+uint32_t ora_abs_u32(int32_t x)
+{
+    int64_t v = x;
+    return (uint32_t)(v < 0 ? -v : v);
+}
+
+/* [TI] step 1: max_val = max(|G|) over the whole tensor; 0 for an empty one. */
+uint32_t ora_absmax_i32(const int32_t *x, int64_t n)
+{
+    uint32_t m = 0;
+    for (int64_t j = 0; j < n; ++j) {
+        uint32_t a = ora_abs_u32(x[j]);
+        if (a > m) m = a;
+    }
+    return m;
+}
+
+/* Number of binary digits of m: 0 for m = 0, else floor(log2 m) + 1.  This is
+ * exactly ceil(log2(m + 1)) of [TI] step 2, computed without floating point
+ * (reading U1). */
+int ora_bitlen_u32(uint32_t m)
+{
+    int b = 0;
+    while (m != 0) {
+        ++b;
+        m >>= 1;
+    }
+    return b;
+}
+
+/* [TI] step 2: shift = max(0, bits_needed - target_bits). */
+int ora_niti_shift(uint32_t max_val, int target_bits)
+{
+    int s = ora_bitlen_u32(max_val) - target_bits;
+    return s > 0 ? s : 0;
+}
+
+/* floor(v / 2^s) for a 64-bit value, 0 <= s <= 62. */
+static int64_t floor_div_pow2_i64(int64_t v, int s)
+{
+    int64_t d = (int64_t)1 << s;
+    if (v >= 0) return v / d;
+    return -((-v + d - 1) / d);
+}
+
+/* floor(x / 2^s): an arithmetic right shift, written out because >> on a
+ * negative int is implementation-defined in C99. */
+int32_t ora_floor_shift(int32_t x, int s)
+{
+    return (int32_t)floor_div_pow2_i64((int64_t)x, s);
+}
+
+/* [TI] step 3 "round-half-up" shift: floor((x + 2^(s-1)) / 2^s) for s >= 1,
+ * x for s = 0.  Ties go toward +infinity (reading U3).  The sum is formed in
+ * 64 bits, so x near INT32_MAX does not overflow (reading U4). */
+int32_t ora_rhu(int32_t x, int s)
+{
+    if (s <= 0) return x;
+    return (int32_t)floor_div_pow2_i64((int64_t)x + ((int64_t)1 << (s - 1)), s);
+}
+
+/* rhu applied to every element of x (for exhaustive tests of the primitive). */
+void ora_rhu_array(const int32_t *x, int64_t n, int s, int32_t *out)
+{
+    for (int64_t j = 0; j < n; ++j) out[j] = ora_rhu(x[j], s);
+}
+
+/* [TI] step 5: saturate to the int8 range. */
+int32_t ora_sat8(int64_t v)
+{
+    if (v > 127) return 127;
+    if (v < -128) return -128;
+    return (int32_t)v;
+}
+
+/* The same saturation for the int16 mantissas of DFP-16 ([DFP] 3). */
+int32_t ora_sat16(int64_t v)
+{
+    if (v > 32767) return 32767;
+    if (v < -32768) return -32768;
+    return (int32_t)v;
+}
+
+/* Least r with 2^r >= n (0 for n <= 1). */
+int ora_ceil_log2(int64_t n)
+{
+    int r = 0;
+    while (((int64_t)1 << r) < n) ++r;
+    return r;
+}
+
+/* ------------------------------------------------------------------------ */
+/* NITI quantiser ([TI] steps 1-3) and update ([TI] steps 1-5).              */
+/* ------------------------------------------------------------------------ */
+
+/* Requantise an int32 tensor to int8 with one dynamic per-tensor shift:
+ * s = shift(max|acc|, target_bits); out = sat8(rhu(acc, s)); ReLU if asked.
+ * target_bits = 7 is the delta-propagation setting of [TI] section 3.  The
+ * rounding can reach +2^tb (e.g. 255 >> 1 -> 128); the int8 output saturates
+ * it (reading U6).  Returns s. */
+int ora_niti_requant(const int32_t *acc, int64_t n, int target_bits, int relu,
+                     int8_t *out)
+{
+    int s = ora_niti_shift(ora_absmax_i32(acc, n), target_bits);
+    for (int64_t j = 0; j < n; ++j) {
+        int32_t v = ora_sat8(ora_rhu(acc[j], s));
+        if (relu && v < 0) v = 0;
+        out[j] = (int8_t)v;
+    }
+    return s;
+}
+
+/* NITI weight update, in place on W:
+ *   s  = shift(max|G|, target_bits)            steps 1-2
+ *   Gq = rhu(G, s)           (kept in int32)   step 3
+ *   ws = max(0, s - mu_weight)                 step 4
+ *   d  = rhu(Gq, ws)                           step 4 (second rounding, U5)
+ *   W  = sat8(W - d)                           step 5
+ * gq_out (nullable) receives Gq. */
+void ora_niti_update(const int32_t *G, int8_t *W, int64_t n, int target_bits,
+                     int mu_weight, int32_t *gq_out, int *shift_out,
+                     int *weight_shift_out)
+{
+    int s = ora_niti_shift(ora_absmax_i32(G, n), target_bits);
+    int ws = s - mu_weight;
+    if (ws < 0) ws = 0;
+    for (int64_t j = 0; j < n; ++j) {
+        int32_t gq = ora_rhu(G[j], s);
+        int32_t d = ora_rhu(gq, ws);
+        if (gq_out) gq_out[j] = gq;
+        W[j] = (int8_t)ora_sat8((int64_t)W[j] - (int64_t)d);
+    }
+    if (shift_out) *shift_out = s;
+    if (weight_shift_out) *weight_shift_out = ws;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Linear layer: Y = X W^T, dX = dY W, G = dY^T X  ([TGR] W[oc*IC+ic]).       */
+/* ------------------------------------------------------------------------ */
+
+int32_t ora_linear_fwd_at(const int8_t *X, const int8_t *W, int64_t B,
+                          int64_t IN, int64_t OUT, int64_t b, int64_t o)
+{
+    uint32_t acc = 0;
+    (void)B;
+    (void)OUT;
+    for (int64_t i = 0; i < IN; ++i)
+        acc += (uint32_t)((int32_t)X[b * IN + i] * (int32_t)W[o * IN + i]);
+    return u32_to_i32(acc);
+}
+
+int32_t ora_linear_dgrad_at(const int8_t *dY, const int8_t *W, int64_t B,
+                            int64_t IN, int64_t OUT, int64_t b, int64_t i)
+{
+    uint32_t acc = 0;
+    (void)B;
+    for (int64_t o = 0; o < OUT; ++o)
+        acc += (uint32_t)((int32_t)dY[b * OUT + o] * (int32_t)W[o * IN + i]);
+    return u32_to_i32(acc);
+}
+
+int32_t ora_linear_wgrad_at(const int8_t *dY, const int8_t *X, int64_t B,
+                            int64_t IN, int64_t OUT, int64_t o, int64_t i)
+{
+    uint32_t acc = 0;
+    for (int64_t b = 0; b < B; ++b)
+        acc += (uint32_t)((int32_t)dY[b * OUT + o] * (int32_t)X[b * IN + i]);
+    return u32_to_i32(acc);
+}
+
+/* Y[b][o] = sum_i X[b][i] * W[o][i]. */
+int64_t ora_linear_fwd(const int8_t *X, const int8_t *W, int32_t *Y,
+                       int64_t B, int64_t IN, int64_t OUT)
+{
+    int64_t wraps = 0;
+#pragma omp parallel for schedule(static) reduction(+ : wraps)
+    for (int64_t b = 0; b < B; ++b) {
+        for (int64_t o = 0; o < OUT; ++o) {
+            uint32_t acc = 0;
+            int64_t exact = 0;
+            for (int64_t i = 0; i < IN; ++i) {
+                int32_t p = (int32_t)X[b * IN + i] * (int32_t)W[o * IN + i];
+                acc += (uint32_t)p;
+                exact += p;
+            }
+            Y[b * OUT + o] = u32_to_i32(acc);
+            wraps += !exact_in_i32(exact);
+        }
+    }
+    return wraps;
+}
+
+/* dX[b][i] = sum_o dY[b][o] * W[o][i]. */
+int64_t ora_linear_dgrad(const int8_t *dY, const int8_t *W, int32_t *dX,
+                         int64_t B, int64_t IN, int64_t OUT)
+{
+    int64_t wraps = 0;
+#pragma omp parallel for schedule(static) reduction(+ : wraps)
+    for (int64_t b = 0; b < B; ++b) {
+        for (int64_t i = 0; i < IN; ++i) {
+            uint32_t acc = 0;
+            int64_t exact = 0;
+            for (int64_t o = 0; o < OUT; ++o) {
+                int32_t p = (int32_t)dY[b * OUT + o] * (int32_t)W[o * IN + i];
+                acc += (uint32_t)p;
+                exact += p;
+            }
+            dX[b * IN + i] = u32_to_i32(acc);
+            wraps += !exact_in_i32(exact);
+        }
+    }
+    return wraps;
+}
+
+/* G[o][i] = sum_b dY[b][o] * X[b][i]. */
+int64_t ora_linear_wgrad(const int8_t *dY, const int8_t *X, int32_t *G,
+                         int64_t B, int64_t IN, int64_t OUT)
+{
+    int64_t wraps = 0;
+#pragma omp parallel for schedule(static) reduction(+ : wraps)
+    for (int64_t o = 0; o < OUT; ++o) {
+        for (int64_t i = 0; i < IN; ++i) {
+            uint32_t acc = 0;
+            int64_t exact = 0;
+            for (int64_t b = 0; b < B; ++b) {
+                int32_t p = (int32_t)dY[b * OUT + o] * (int32_t)X[b * IN + i];
+                acc += (uint32_t)p;
+                exact += p;
+            }
+            G[o * IN + i] = u32_to_i32(acc);
+            wraps += !exact_in_i32(exact);
+        }
+    }
+    return wraps;
+}
+
+/* ReLU backward: a delta survives only where the stored activation was
+ * positive (the ReLU mask of the forward pass, [TI] section 4.2). */
+void ora_relu_mask(int32_t *d, const int8_t *act, int64_t n)
+{
+    for (int64_t j = 0; j < n; ++j)
+        if (!(act[j] > 0)) d[j] = 0;
+}
+
+/* Output error of a classifier trained toward a target magnitude for the
+ * true class and 0 elsewhere. */
+void ora_output_error(const int8_t *out, const int32_t *labels, int64_t B,
+                      int64_t C, int target_mag, int32_t *e)
+{
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t c = 0; c < C; ++c)
+            e[b * C + c] =
+                (c == (int64_t)labels[b] ? target_mag : 0) - (int32_t)out[b * C + c];
+}
+
+/* ------------------------------------------------------------------------ */
+/* Convolution, stride 1, zero padding P, NHWC activations, OHWI weights.    */
+/* Output spatial size: Ho = H + 2P - KH + 1, Wo = Wd + 2P - KW + 1.          */
+/* ------------------------------------------------------------------------ */
+
+static int64_t conv_out_dim(int64_t in, int k, int p) { return in + 2 * p - k + 1; }
+
+int32_t ora_conv_fwd_at(const int8_t *X, const int8_t *W, int64_t N, int64_t H,
+                        int64_t Wd, int64_t Cin, int64_t Cout, int KH, int KW,
+                        int P, int64_t n, int64_t h, int64_t w, int64_t co)
+{
+    uint32_t acc = 0;
+    (void)N;
+    (void)Cout;
+    for (int kh = 0; kh < KH; ++kh) {
+        int64_t y = h + kh - P;
+        if (y < 0 || y >= H) continue;
+        for (int kw = 0; kw < KW; ++kw) {
+            int64_t x = w + kw - P;
+            if (x < 0 || x >= Wd) continue;
+            for (int64_t ci = 0; ci < Cin; ++ci)
+                acc += (uint32_t)((int32_t)X[((n * H + y) * Wd + x) * Cin + ci] *
+                                  (int32_t)W[((co * KH + kh) * KW + kw) * Cin + ci]);
+        }
+    }
+    return u32_to_i32(acc);
+}
+
+int32_t ora_conv_dgrad_at(const int8_t *dY, const int8_t *W, int64_t N,
+                          int64_t H, int64_t Wd, int64_t Cin, int64_t Cout,
+                          int KH, int KW, int P, int64_t n, int64_t h,
+                          int64_t w, int64_t ci)
+{
+    int64_t Ho = conv_out_dim(H, KH, P), Wo = conv_out_dim(Wd, KW, P);
+    uint32_t acc = 0;
+    (void)N;
+    for (int kh = 0; kh < KH; ++kh) {
+        int64_t y = h - kh + P; /* output row that read input row h via tap kh */
+        if (y < 0 || y >= Ho) continue;
+        for (int kw = 0; kw < KW; ++kw) {
+            int64_t x = w - kw + P;
+            if (x < 0 || x >= Wo) continue;
+            for (int64_t co = 0; co < Cout; ++co)
+                acc += (uint32_t)((int32_t)dY[((n * Ho + y) * Wo + x) * Cout + co] *
+                                  (int32_t)W[((co * KH + kh) * KW + kw) * Cin + ci]);
+        }
+    }
+    return u32_to_i32(acc);
+}
+
+int32_t ora_conv_wgrad_at(const int8_t *dY, const int8_t *X, int64_t N,
+                          int64_t H, int64_t Wd, int64_t Cin, int64_t Cout,
+                          int KH, int KW, int P, int64_t co, int64_t kh,
+                          int64_t kw, int64_t ci)
+{
+    int64_t Ho = conv_out_dim(H, KH, P), Wo = conv_out_dim(Wd, KW, P);
+    uint32_t acc = 0;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t h = 0; h < Ho; ++h) {
+            int64_t y = h + kh - P;
+            if (y < 0 || y >= H) continue;
+            for (int64_t w = 0; w < Wo; ++w) {
+                int64_t x = w + kw - P;
+                if (x < 0 || x >= Wd) continue;
+                acc += (uint32_t)((int32_t)dY[((n * Ho + h) * Wo + w) * Cout + co] *
+                                  (int32_t)X[((n * H + y) * Wd + x) * Cin + ci]);
+            }
+        }
+    return u32_to_i32(acc);
+}
+
+/* Y[n,h,w,co] = sum_{kh,kw,ci} X[n, h+kh-P, w+kw-P, ci] * W[co,kh,kw,ci]. */
+int64_t ora_conv_fwd(const int8_t *X, const int8_t *W, int32_t *Y, int64_t N,
+                     int64_t H, int64_t Wd, int64_t Cin, int64_t Cout, int KH,
+                     int KW, int P)
+{
+    int64_t Ho = conv_out_dim(H, KH, P), Wo = conv_out_dim(Wd, KW, P);
+    int64_t wraps = 0;
+#pragma omp parallel for collapse(2) schedule(static) reduction(+ : wraps)
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t h = 0; h < Ho; ++h)
+            for (int64_t w = 0; w < Wo; ++w)
+                for (int64_t co = 0; co < Cout; ++co) {
+                    uint32_t acc = 0;
+                    int64_t exact = 0;
+                    for (int kh = 0; kh < KH; ++kh) {
+                        int64_t y = h + kh - P;
+                        if (y < 0 || y >= H) continue;
+                        for (int kw = 0; kw < KW; ++kw) {
+                            int64_t x = w + kw - P;
+                            if (x < 0 || x >= Wd) continue;
+                            for (int64_t ci = 0; ci < Cin; ++ci) {
+                                int32_t p =
+                                    (int32_t)X[((n * H + y) * Wd + x) * Cin + ci] *
+                                    (int32_t)W[((co * KH + kh) * KW + kw) * Cin + ci];
+                                acc += (uint32_t)p;
+                                exact += p;
+                            }
+                        }
+                    }
+                    Y[((n * Ho + h) * Wo + w) * Cout + co] = u32_to_i32(acc);
+                    wraps += !exact_in_i32(exact);
+                }
+    return wraps;
+}
+
+/* dX[n,h,w,ci] = sum_{kh,kw,co} dY[n, h-kh+P, w-kw+P, co] * W[co,kh,kw,ci]
+ * (the adjoint of the forward map: every product X*W that fed an output
+ * sends dY*W back to the input it read). */
+int64_t ora_conv_dgrad(const int8_t *dY, const int8_t *W, int32_t *dX,
+                       int64_t N, int64_t H, int64_t Wd, int64_t Cin,
+                       int64_t Cout, int KH, int KW, int P)
+{
+    int64_t Ho = conv_out_dim(H, KH, P), Wo = conv_out_dim(Wd, KW, P);
+    int64_t wraps = 0;
+#pragma omp parallel for collapse(2) schedule(static) reduction(+ : wraps)
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t h = 0; h < H; ++h)
+            for (int64_t w = 0; w < Wd; ++w)
+                for (int64_t ci = 0; ci < Cin; ++ci) {
+                    uint32_t acc = 0;
+                    int64_t exact = 0;
+                    for (int kh = 0; kh < KH; ++kh) {
+                        int64_t y = h - kh + P;
+                        if (y < 0 || y >= Ho) continue;
+                        for (int kw = 0; kw < KW; ++kw) {
+                            int64_t x = w - kw + P;
+                            if (x < 0 || x >= Wo) continue;
+                            for (int64_t co = 0; co < Cout; ++co) {
+                                int32_t p =
+                                    (int32_t)dY[((n * Ho + y) * Wo + x) * Cout + co] *
+                                    (int32_t)W[((co * KH + kh) * KW + kw) * Cin + ci];
+                                acc += (uint32_t)p;
+                                exact += p;
+                            }
+                        }
+                    }
+                    dX[((n * H + h) * Wd + w) * Cin + ci] = u32_to_i32(acc);
+                    wraps += !exact_in_i32(exact);
+                }
+    return wraps;
+}
+
+/* G[co,kh,kw,ci] = sum_{n,h,w} dY[n,h,w,co] * X[n, h+kh-P, w+kw-P, ci]. */
+int64_t ora_conv_wgrad(const int8_t *dY, const int8_t *X, int32_t *G,
+                       int64_t N, int64_t H, int64_t Wd, int64_t Cin,
+                       int64_t Cout, int KH, int KW, int P)
+{
+    int64_t Ho = conv_out_dim(H, KH, P), Wo = conv_out_dim(Wd, KW, P);
+    int64_t wraps = 0;
+#pragma omp parallel for collapse(2) schedule(static) reduction(+ : wraps)
+    for (int64_t co = 0; co < Cout; ++co)
+        for (int kh = 0; kh < KH; ++kh)
+            for (int kw = 0; kw < KW; ++kw)
+                for (int64_t ci = 0; ci < Cin; ++ci) {
+                    uint32_t acc = 0;
+                    int64_t exact = 0;
+                    for (int64_t n = 0; n < N; ++n)
+                        for (int64_t h = 0; h < Ho; ++h) {
+                            int64_t y = h + kh - P;
+                            if (y < 0 || y >= H) continue;
+                            for (int64_t w = 0; w < Wo; ++w) {
+                                int64_t x = w + kw - P;
+                                if (x < 0 || x >= Wd) continue;
+                                int32_t p =
+                                    (int32_t)dY[((n * Ho + h) * Wo + w) * Cout + co] *
+                                    (int32_t)X[((n * H + y) * Wd + x) * Cin + ci];
+                                acc += (uint32_t)p;
+                                exact += p;
+                            }
+                        }
+                    G[((co * KH + kh) * KW + kw) * Cin + ci] = u32_to_i32(acc);
+                    wraps += !exact_in_i32(exact);
+                }
+    return wraps;
+}
+
+/* ------------------------------------------------------------------------ */
+/* DFP-16 ([DFP] sections 3, 3.1, 4).                                        */
+/*                                                                            */
+/* A DFP tensor is an integer tensor I plus one shared exponent E, value       */
+/* I * 2^E.  A product of two DFP-16 tensors is a 32-bit tensor with exponent */
+/* Ea + Eb.  Overflow management: the reduction is split into chunks of       */
+/* `chunk` terms; each chunk's int32 partial is right-shifted (round-half-up)  */
+/* by r = ceil(log2(number of chunks)) before the chunks are summed, so the    */
+/* sum of chunk results stays in int32 (readings U17, U18, U22).  The result  */
+/* then has exponent Ea + Eb + r.  Down-conversion right-shifts the int32      */
+/* tensor by Rs = max(0, bitlen(max|acc|) - 15) so it fits 16 bits (U19).      */
+/* ------------------------------------------------------------------------ */
+
+int ora_dfp_chunk_shift(int64_t L, int chunk)
+{
+    int64_t nc = (L + chunk - 1) / chunk;
+    return nc <= 1 ? 0 : ora_ceil_log2(nc);
+}
+
+int32_t ora_dfp_contract_at(const int16_t *A, int64_t sam, int64_t sak,
+                            const int16_t *B, int64_t sbk, int64_t sbn,
+                            int64_t L, int chunk, int64_t m, int64_t n)
+{
+    int r = ora_dfp_chunk_shift(L, chunk);
+    uint32_t acc = 0;
+    for (int64_t k0 = 0; k0 < L; k0 += chunk) {
+        uint32_t p = 0;
+        for (int64_t k = k0; k < k0 + chunk && k < L; ++k)
+            p += (uint32_t)((int32_t)A[m * sam + k * sak] * (int32_t)B[k * sbk + n * sbn]);
+        acc += (uint32_t)ora_rhu(u32_to_i32(p), r);
+    }
+    return u32_to_i32(acc);
+}
+
+int64_t ora_dfp_contract(const int16_t *A, int64_t sam, int64_t sak,
+                         const int16_t *B, int64_t sbk, int64_t sbn, int64_t M,
+                         int64_t N, int64_t L, int chunk, int32_t *acc_out)
+{
+    int r = ora_dfp_chunk_shift(L, chunk);
+    int64_t wraps = 0;
+#pragma omp parallel for schedule(static) reduction(+ : wraps)
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            uint32_t acc = 0;
+            for (int64_t k0 = 0; k0 < L; k0 += chunk) {
+                uint32_t p = 0;
+                int64_t exact = 0;
+                for (int64_t k = k0; k < k0 + chunk && k < L; ++k) {
+                    int32_t a = A[m * sam + k * sak], b = B[k * sbk + n * sbn];
+                    p += (uint32_t)(a * b);
+                    exact += (int64_t)a * b;
+                }
+                wraps += !exact_in_i32(exact);
+                acc += (uint32_t)ora_rhu(u32_to_i32(p), r);
+            }
+            acc_out[m * N + n] = u32_to_i32(acc);
+        }
+    }
+    return wraps;
+}
+
+int ora_dfp_downconvert(const int32_t *acc, int64_t n, int16_t *out)
+{
+    int rs = ora_niti_shift(ora_absmax_i32(acc, n), 15);
+    for (int64_t j = 0; j < n; ++j)
+        out[j] = (int16_t)ora_sat16(ora_rhu(acc[j], rs));
+    return rs;
+}
+
+static int dfp_finish(const int32_t *acc, int64_t n, int16_t *out, int e_in,
+                      int r, int *e_out)
+{
+    int rs = ora_dfp_downconvert(acc, n, out);
+    int e = e_in + r + rs;
+    *e_out = e;
+    /* One signed 8-bit shared exponent per tensor ([DFP] 3). */
+    return (e < -128 || e > 127) ? -1 : 0;
+}
+
+/* Forward: Y[M][N] = X[M][K] . W[N][K]^T, reduced over K. */
+int ora_dfp16_fwd(const int16_t *X, int eX, const int16_t *W, int eW,
+                  int16_t *Y, int *eY, int32_t *acc, int64_t M, int64_t K,
+                  int64_t N, int chunk)
+{
+    ora_dfp_contract(X, K, 1, W, 1, K, M, N, K, chunk, acc);
+    return dfp_finish(acc, M * N, Y, eX + eW, ora_dfp_chunk_shift(K, chunk), eY);
+}
+
+/* Backward data: dX[M][K] = dY[M][N] . W[N][K], reduced over N. */
+int ora_dfp16_dgrad(const int16_t *dY, int edY, const int16_t *W, int eW,
+                    int16_t *dX, int *edX, int32_t *acc, int64_t M, int64_t K,
+                    int64_t N, int chunk)
+{
+    ora_dfp_contract(dY, N, 1, W, K, 1, M, K, N, chunk, acc);
+    return dfp_finish(acc, M * K, dX, edY + eW, ora_dfp_chunk_shift(N, chunk), edX);
+}
+
+/* Weight gradient: G[N][K] = dY[M][N]^T . X[M][K], reduced over M. */
+int ora_dfp16_wgrad(const int16_t *dY, int edY, const int16_t *X, int eX,
+                    int16_t *G, int *eG, int32_t *acc, int64_t M, int64_t K,
+                    int64_t N, int chunk)
+{
+    ora_dfp_contract(dY, 1, N, X, K, 1, N, K, M, chunk, acc);
+    return dfp_finish(acc, N * K, G, edY + eX, ora_dfp_chunk_shift(M, chunk), eG);
+}
+
+/* [APT] Equation 4 as the text describes it: the mean magnitude of a layer's
+ * gradient over its N parameters, divided by the layer's minimum weight
+ * resolution epsilon.  With the gradient stored as DFP (g * 2^e_g) and
+ * epsilon = 2^e_w (one step of the weight mantissa, reading U20):
+ *   Gavg = (sum |g| / N) * 2^(e_g - e_w).
+ * The sum is exact in int64; the scaling by a power of two is exact. */
+double ora_gavg(const int16_t *g, int64_t n, int e_g, int e_w)
+{
+    int64_t sum = 0;
+    if (n <= 0) return 0.0;
+    for (int64_t j = 0; j < n; ++j) sum += g[j] < 0 ? -(int64_t)g[j] : (int64_t)g[j];
+    double v = (double)sum / (double)n;
+    int e = e_g - e_w;
+    for (; e > 0; --e) v *= 2.0;
+    for (; e < 0; ++e) v *= 0.5;
+    return v;
+}

@@ -1,0 +1,142 @@
+/*
+ * ionn_oracle.h -- CPU oracle for the integer-only training step.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This is the plain, slow, obviously-correct
+ * reference that the GPU library is checked against.  Only the test suite,
+ * the smoke check and the benchmark's CPU-baseline leg may load it.  It shares
+ * no code, header, table or helper with the GPU library, and it never calls
+ * into it.
+ *
+ * Sources (cited by page title and section):
+ *  [TI]   "Integer On-Device Training: Overview" (TI C2000 MCU-AI user guide),
+ *         section 3 "The NITI Algorithm" -> "The Solution: Dynamic Shifts",
+ *         steps 1-5, and the note on delta propagation (target_bits = 7).
+ *  [APT]  "Adaptive Precision Training for Resource Constrained Devices",
+ *         the quantisation-underflow discussion (epsilon, Equations 2-3) and
+ *         the Gavg metric (Equation 4).
+ *  [DFP]  "Mixed Precision Training of Convolutional Neural Networks using
+ *         Integer Operations" (source-linked summary), section 3 "The Dynamic
+ *         Fixed Point Format", 3.1 "DFP Tensor Primitives", and section 4
+ *         "Handling overflows".
+ *  [TGR]  "Compilation Pipeline" (TiGrIS), the fully-connected weight index
+ *         W[oc*IC + ic] and the NHWC activation layout.
+ *
+ * Conventions: row-major everywhere.  Linear: X[B][IN], W[OUT][IN],
+ * Y[B][OUT].  Conv: NHWC activations, OHWI weights W[Cout][KH][KW][Cin],
+ * cross-correlation (no kernel flip), stride 1, zero padding P.
+ *
+ * All accumulation is modulo 2^32 (done in uint32_t, then reinterpreted as
+ * two's-complement int32).  Functions that accumulate also report how many
+ * outputs would differ from the exact (int64) sum, i.e. how many wrapped.
+ *
+ * Where the pages leave a step open, the reading taken is stated next to the
+ * function (ids U1..U22 of the design notes).
+ */
+#ifndef IONN_ORACLE_H
+#define IONN_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Thread count used by the parallel loops (OpenMP); returns the count in use. */
+int ora_set_threads(int n);
+int ora_get_threads(void);
+
+/* ---- primitives ([TI] steps 1-3, 5) ---- */
+uint32_t ora_abs_u32(int32_t x);
+uint32_t ora_absmax_i32(const int32_t *x, int64_t n);
+int      ora_bitlen_u32(uint32_t m);
+int      ora_niti_shift(uint32_t max_val, int target_bits);
+int32_t  ora_floor_shift(int32_t x, int s);
+int32_t  ora_rhu(int32_t x, int s);
+void     ora_rhu_array(const int32_t *x, int64_t n, int s, int32_t *out);
+int32_t  ora_sat8(int64_t v);
+int32_t  ora_sat16(int64_t v);
+int      ora_ceil_log2(int64_t n);
+
+/* ---- NITI quantiser and update ([TI] steps 1-5) ---- */
+int ora_niti_requant(const int32_t *acc, int64_t n, int target_bits, int relu,
+                     int8_t *out);
+void ora_niti_update(const int32_t *G, int8_t *W, int64_t n, int target_bits,
+                     int mu_weight, int32_t *gq_out, int *shift_out,
+                     int *weight_shift_out);
+
+/* ---- linear contractions ---- */
+int64_t ora_linear_fwd(const int8_t *X, const int8_t *W, int32_t *Y,
+                       int64_t B, int64_t IN, int64_t OUT);
+int64_t ora_linear_dgrad(const int8_t *dY, const int8_t *W, int32_t *dX,
+                         int64_t B, int64_t IN, int64_t OUT);
+int64_t ora_linear_wgrad(const int8_t *dY, const int8_t *X, int32_t *G,
+                         int64_t B, int64_t IN, int64_t OUT);
+/* One output of each contraction, for sampled checks at full size. */
+int32_t ora_linear_fwd_at(const int8_t *X, const int8_t *W, int64_t B,
+                          int64_t IN, int64_t OUT, int64_t b, int64_t o);
+int32_t ora_linear_dgrad_at(const int8_t *dY, const int8_t *W, int64_t B,
+                            int64_t IN, int64_t OUT, int64_t b, int64_t i);
+int32_t ora_linear_wgrad_at(const int8_t *dY, const int8_t *X, int64_t B,
+                            int64_t IN, int64_t OUT, int64_t o, int64_t i);
+/* Elementwise mask: d[j] = (act[j] > 0) ? d[j] : 0 (ReLU backward). */
+void ora_relu_mask(int32_t *d, const int8_t *act, int64_t n);
+/* Output error e[b][c] = (c == label[b] ? target_mag : 0) - out[b][c]. */
+void ora_output_error(const int8_t *out, const int32_t *labels, int64_t B,
+                      int64_t C, int target_mag, int32_t *e);
+
+/* ---- convolution, stride 1, zero pad P, NHWC / OHWI ---- */
+int64_t ora_conv_fwd(const int8_t *X, const int8_t *W, int32_t *Y, int64_t N,
+                     int64_t H, int64_t Wd, int64_t Cin, int64_t Cout, int KH,
+                     int KW, int P);
+int64_t ora_conv_dgrad(const int8_t *dY, const int8_t *W, int32_t *dX,
+                       int64_t N, int64_t H, int64_t Wd, int64_t Cin,
+                       int64_t Cout, int KH, int KW, int P);
+int64_t ora_conv_wgrad(const int8_t *dY, const int8_t *X, int32_t *G,
+                       int64_t N, int64_t H, int64_t Wd, int64_t Cin,
+                       int64_t Cout, int KH, int KW, int P);
+int32_t ora_conv_fwd_at(const int8_t *X, const int8_t *W, int64_t N, int64_t H,
+                        int64_t Wd, int64_t Cin, int64_t Cout, int KH, int KW,
+                        int P, int64_t n, int64_t h, int64_t w, int64_t co);
+int32_t ora_conv_dgrad_at(const int8_t *dY, const int8_t *W, int64_t N,
+                          int64_t H, int64_t Wd, int64_t Cin, int64_t Cout,
+                          int KH, int KW, int P, int64_t n, int64_t h,
+                          int64_t w, int64_t ci);
+int32_t ora_conv_wgrad_at(const int8_t *dY, const int8_t *X, int64_t N,
+                          int64_t H, int64_t Wd, int64_t Cin, int64_t Cout,
+                          int KH, int KW, int P, int64_t co, int64_t kh,
+                          int64_t kw, int64_t ci);
+
+/* ---- DFP16 ([DFP] 3.1 and 4) ---- */
+/* Generic chunked contraction with element strides:
+ *   acc[m*N + n] = sum_c rhu(p_c, r),  p_c = sum_{k in chunk c} A(m,k)*B(k,n)
+ * where A(m,k) = A[m*sam + k*sak], B(k,n) = B[k*sbk + n*sbn], L = reduction
+ * length, chunk = chunk length, r = chunk_shift(L, chunk).  Returns the number
+ * of chunk partials whose exact value left the int32 range. */
+int     ora_dfp_chunk_shift(int64_t L, int chunk);
+int64_t ora_dfp_contract(const int16_t *A, int64_t sam, int64_t sak,
+                         const int16_t *B, int64_t sbk, int64_t sbn, int64_t M,
+                         int64_t N, int64_t L, int chunk, int32_t *acc);
+int32_t ora_dfp_contract_at(const int16_t *A, int64_t sam, int64_t sak,
+                            const int16_t *B, int64_t sbk, int64_t sbn,
+                            int64_t L, int chunk, int64_t m, int64_t n);
+/* Down-conversion: Rs = max(0, bitlen(max|acc|) - 15); out = sat16(rhu(acc, Rs)).
+ * Returns Rs. */
+int ora_dfp_downconvert(const int32_t *acc, int64_t n, int16_t *out);
+/* The three roles; exponents are plain ints; returns 0, or -1 when the
+ * output exponent leaves the signed 8-bit range. */
+int ora_dfp16_fwd(const int16_t *X, int eX, const int16_t *W, int eW,
+                  int16_t *Y, int *eY, int32_t *acc_tmp, int64_t M, int64_t K,
+                  int64_t N, int chunk);
+int ora_dfp16_dgrad(const int16_t *dY, int edY, const int16_t *W, int eW,
+                    int16_t *dX, int *edX, int32_t *acc_tmp, int64_t M,
+                    int64_t K, int64_t N, int chunk);
+int ora_dfp16_wgrad(const int16_t *dY, int edY, const int16_t *X, int eX,
+                    int16_t *G, int *eG, int32_t *acc_tmp, int64_t M,
+                    int64_t K, int64_t N, int chunk);
+/* Gavg = mean(|g|) * 2^(e_g - e_w)   ([APT] Equation 4, epsilon = 2^e_w). */
+double ora_gavg(const int16_t *g, int64_t n, int e_g, int e_w);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
