@@ -1,0 +1,254 @@
+#!/usr/bin/env python3
+"""Benchmark of the integer training step on one MI355X.
+
+Main line: the large int8 Linear training step (tokens 8192, in 4096,
+out 4096): forward, dgrad and wgrad contractions (each 8192x4096x4096,
+int8 x int8 -> int32, with the fused max-abs) and the NITI update of the
+16.8M weights.  Throughput counts 2*M*N*K ops per contraction (824.6 G int8
+ops per step); requantisation and update ALU work is not counted.  Inputs are
+seeded synthetic tensors with the workload's distributions, resident in HBM
+before the timed region.  Every kernel launch is bracketed by HIP events on
+the stream it runs on, so per-kernel averages come from the same timed steps.
+
+Also reported: the oracle (plain C, CPU) timed on a bounded sample of the
+same workload on this host, and secondary measurements of the conv and DFP-16
+steps.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-secondary]
+       [--no-cpu-baseline]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+PEAK_INT8_TOPS = 5000.0     # MI355X dense int8 matrix peak (5.0 POP/s)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+T, IN, OUT = 8192, 4096, 4096
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-rows", type=int, default=512,
+                    help="token rows of the workload the CPU oracle runs")
+    return ap.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Timer:
+    """HIP events on the current stream around named launches."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.marks = []
+
+    def mark(self, name):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        self.marks.append((name, e))
+
+    def per_name(self):
+        out = {}
+        for (name, e0), (_, e1) in zip(self.marks, self.marks[1:]):
+            if name is None:
+                continue
+            out.setdefault(name, []).append(e0.elapsed_time(e1))
+        return out
+
+
+def bench_linear(torch, steps_mod, args):
+    from integer_only_nn_amd import ops
+    import ionn_synth
+    dev = torch.device("cuda:0")
+    log("generating the large-linear inputs")
+    d = ionn_synth.large_linear()
+    X = torch.from_numpy(d["X"]).to(dev)
+    W = torch.from_numpy(d["W"]).to(dev)
+    dY = torch.from_numpy(d["dY"]).to(dev)
+    buf = steps_mod.LinearStepBuffers.make(T, IN, OUT, dev)
+    s = buf.scal
+
+    def step(tm=None):
+        m = tm.mark if tm else (lambda n: None)
+        m("fill")
+        ops.ionn_fill_u32(s[0:3], 0)
+        m("fwd")
+        ops.int_linear_fwd(X, W, buf.Y, absmax_Y=s[0:1])
+        m("dgrad")
+        ops.int_linear_dgrad(dY, W, buf.dX, absmax_dX=s[1:2])
+        m("wgrad")
+        ops.int_linear_wgrad(dY, X, buf.G, absmax_G=s[2:3])
+        m("update")
+        ops.niti_quantize_update(buf.G, s[2:3], 8, 2, W, shifts_out=s[4:6])
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    tm = Timer(torch)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(args.steps):
+        step(tm)
+    tm.mark(None)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    per = {k: float(np.mean(v)) for k, v in tm.per_name().items()}
+
+    # the same step with the propagated delta requantised to 7 bits (untimed above)
+    def step_req():
+        step()
+        ops.niti_quantize(buf.dX, s[1:2], 7, False, buf.delta, shift_out=s[3:4])
+    for _ in range(2):
+        step_req()
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(args.steps):
+        step_req()
+    t1.record()
+    torch.cuda.synchronize()
+    ms_req = t0.elapsed_time(t1) / args.steps
+    shifts = buf.scal.cpu().tolist()
+    return ms, per, ms_req, shifts
+
+
+def bench_conv(torch, steps_mod, nsteps):
+    import ionn_synth
+    dev = torch.device("cuda:0")
+    d = ionn_synth.conv3x3()
+    X, Wt, dY = (torch.from_numpy(d[k]).to(dev) for k in ("X", "W", "dY"))
+    buf = steps_mod.ConvStepBuffers.make(128, 56, 56, 64, 64, dev)
+    for _ in range(3):
+        steps_mod.conv_step(X, Wt, dY, buf)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(nsteps):
+        steps_mod.conv_step(X, Wt, dY, buf)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / nsteps
+
+
+def bench_dfp16(torch, steps_mod, nsteps):
+    import ionn_synth
+    dev = torch.device("cuda:0")
+    d = ionn_synth.dfp16_gemm()
+    X, W, dY = (torch.from_numpy(d[k]).to(dev) for k in ("X", "W", "dY"))
+    e = lambda v: torch.tensor([v], dtype=torch.int32, device=dev)
+    eX, eW, edY = e(d["eX"]), e(d["eW"]), e(d["edY"])
+    buf = steps_mod.DfpStepBuffers.make(25088, 256, 1024, dev)
+    for _ in range(3):
+        steps_mod.dfp16_step(X, eX, W, eW, dY, edY, buf)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(nsteps):
+        steps_mod.dfp16_step(X, eX, W, eW, dY, edY, buf)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / nsteps
+
+
+def cpu_baseline(rows):
+    """The oracle (plain C, OpenMP) on a bounded sample of the large-linear
+    step: `rows` token rows through fwd and dgrad, wgrad over `rows` tokens,
+    then the NITI update of all 16.8M weights.  Returns TOPS for the sample."""
+    import oracle
+    import ionn_synth
+    d = ionn_synth.large_linear(T=rows, IN=IN, OUT=OUT)
+    X, W, dY = d["X"], d["W"], d["dY"]
+    t0 = time.perf_counter()
+    oracle.linear_fwd(X, W)
+    oracle.linear_dgrad(dY, W)
+    G = oracle.linear_wgrad(dY, X)
+    oracle.niti_update(G, W, 8, 2)
+    dt = time.perf_counter() - t0
+    ops_done = 3 * 2.0 * rows * IN * OUT
+    return ops_done / dt / 1e12, dt, oracle.get_threads()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported by this build "
+              "(the per-GPU step is the unit; see the sharding notes in DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from integer_only_nn_amd import lib, steps as steps_mod
+    lib()  # fail loudly if the HIP library is missing
+    assert torch.cuda.is_available(), "no ROCm device visible"
+
+    ms, per, ms_req, shifts = bench_linear(torch, steps_mod, args)
+    ops_step = 3 * 2.0 * T * IN * OUT
+    tops = ops_step / (ms * 1e-3) / 1e12
+    gemm = {k: per[k] for k in ("fwd", "dgrad", "wgrad")}
+    dom = max(gemm, key=gemm.get)
+    achieved = 2.0 * T * IN * OUT / (gemm[dom] * 1e-3) / 1e12
+    upd_bytes = 6.0 * IN * OUT
+    upd_gbs = upd_bytes / (per["update"] * 1e-3) / 1e9
+    log(f"step {ms:.3f} ms  {tops:.1f} TOPS  per-kernel ms {per}")
+
+    result = {
+        "metric": "INT8 training-step TOPS (fwd+dgrad+wgrad+NITI update), % of INT8 MFMA peak",
+        "value": round(tops, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic (seeded SplitMix64: X~round(N(0,40)), W~round(N(0,20)), dY~U[-64,63])",
+        "config": {"workload": "large int8 linear training step", "tokens": T, "in": IN,
+                   "out": OUT, "target_bits_weight": 8, "mu_weight": 2, "parallelism": "none"},
+        "pct_of_int8_peak": round(100.0 * tops / PEAK_INT8_TOPS, 2),
+        "tokens_per_s": round(T / (ms * 1e-3), 1),
+        "kernel_ms": {k: round(v, 4) for k, v in per.items()},
+        "roofline": {"bound": "mfma", "kernel": f"int_linear_{dom}", "achieved": round(achieved, 1),
+                     "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_INT8_TOPS, 4),
+                     "traffic": None},
+        "update_pass": {"bound": "hbm", "achieved": round(upd_gbs, 1), "peak": PEAK_HBM_GBS,
+                        "unit": "GB/s", "frac": round(upd_gbs / PEAK_HBM_GBS, 4),
+                        "bytes_per_launch": upd_bytes},
+        "ms_per_step_with_delta_requant": round(ms_req, 4),
+        "shifts": {"s_delta": shifts[3], "s_weight": shifts[4], "ws": shifts[5]},
+    }
+    if not args.no_secondary:
+        log("secondary: conv and DFP-16 steps")
+        c_ms = bench_conv(torch, steps_mod, 10)
+        f_ms = bench_dfp16(torch, steps_mod, 10)
+        conv_ops = 3 * 2.0 * 128 * 56 * 56 * 64 * 9 * 64
+        dfp_ops = 3 * 2.0 * 25088 * 256 * 1024
+        result["secondary"] = {
+            "conv3x3_step": {"shape": "N128 56x56 64->64 NHWC", "ms_per_step": round(c_ms, 4),
+                             "TOPS": round(conv_ops / (c_ms * 1e-3) / 1e12, 2),
+                             "images_per_s": round(128 / (c_ms * 1e-3), 1)},
+            "dfp16_step": {"shape": "M25088 K256 N1024", "ms_per_step": round(f_ms, 4),
+                           "int16_TOPS": round(dfp_ops / (f_ms * 1e-3) / 1e12, 2),
+                           "images_per_s": round(128 / (f_ms * 1e-3), 1)},
+        }
+    if not args.no_cpu_baseline:
+        log("cpu baseline: oracle on a bounded sample")
+        ctops, dt, threads = cpu_baseline(args.cpu_sample_rows)
+        result["cpu_baseline"] = {
+            "value": round(ctops, 4), "unit": "TOPS", "cores": threads, "kind": "oracle",
+            "sample": f"{args.cpu_sample_rows} of {T} token rows through fwd, dgrad and wgrad "
+                      f"(3 x 2 x {args.cpu_sample_rows} x {IN} x {OUT} ops) plus the full "
+                      f"16.8M-weight update; {dt:.1f} s"}
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,243 @@
+/*
+ * ionn.h -- C ABI of the integer-only training-step library for AMD MI355X
+ * (gfx950).  Library file: libionn.so.
+ *
+ * What the calls compute is defined by these pages (cited by title and
+ * section):
+ *  [TI]   "Integer On-Device Training: Overview" (TI C2000 MCU-AI guide):
+ *         section 3 "The NITI Algorithm" -> "The Solution: Dynamic Shifts"
+ *         (steps 1-5, delta propagation with target_bits = 7); section 4
+ *         (layers fill an activation buffer and a ReLU mask in the forward
+ *         pass; the backward pass reads the loss delta and updates weights);
+ *         section 7 (Conv2D, Conv2D+ReLU, Linear, Linear+ReLU layers; grouped
+ *         and dilated convolutions are refused).
+ *  [DFP]  "Mixed Precision Training of Convolutional Neural Networks using
+ *         Integer Operations" (source-linked summary): section 3 (DFP-P
+ *         tensor = integers + one shared signed 8-bit exponent), 3.1 (product
+ *         exponent Ea+Eb; down-conversion by a right shift Rs), 4 "Handling
+ *         overflows" (short int32 partial chains).
+ *  [APT]  "Adaptive Precision Training for Resource Constrained Devices"
+ *         (quantisation underflow, epsilon; the Gavg metric, Equation 4).
+ *  [TGR]  "Compilation Pipeline" (TiGrIS): fully-connected weight index
+ *         W[oc*IC + ic]; NHWC activations.
+ *
+ * Conventions for every call:
+ *  - Tensors are DEVICE pointers, allocated and owned by the caller; the
+ *    library keeps no pointer after a call returns and allocates nothing.
+ *  - Row-major layouts.  Linear: X[B][IN], W[OUT][IN], Y[B][OUT].  Conv:
+ *    NHWC activations, OHWI weights W[Cout][KH][KW][Cin], cross-correlation.
+ *  - int8 x int8 products accumulate in int32 modulo 2^32 (two's-complement
+ *    wrap), so results do not depend on summation order.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Every call checks
+ *    its arguments on the host, then enqueues its kernels on `stream` and
+ *    returns without waiting.  On any error nothing is enqueued.
+ *  - absmax arguments are device uint32 scalars that the call MAX-COMBINES
+ *    into: *absmax = max(*absmax, max |t|) with |INT32_MIN| = 2^31.  Set them
+ *    to 0 first (ionn_fill_u32) when a fresh maximum is wanted.  Several
+ *    calls may accumulate into one scalar (e.g. a tensor produced in parts).
+ *  - Shifts and exponents produced by a call are written to device memory, so
+ *    consecutive calls chain on the stream without a host round trip.
+ *  - Return value: IONN_OK (0) or one of the IONN_ERR_* codes below;
+ *    ionn_last_error() gives a message for the calling thread's last error.
+ */
+#ifndef IONN_H
+#define IONN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    IONN_OK = 0,
+    IONN_ERR_ARG = 1,    /* a required pointer is NULL, or a flag is invalid   */
+    IONN_ERR_SHAPE = 2,  /* a size is negative, too large, or inconsistent     */
+    IONN_ERR_RANGE = 3,  /* target_bits, mu_weight, chunk ... out of range     */
+    IONN_ERR_ALIGN = 4,  /* a pointer lacks the alignment the call documents   */
+    IONN_ERR_UNSUPPORTED = 5, /* geometry outside what the library implements */
+    IONN_ERR_HIP = 6,    /* a HIP runtime call or kernel launch failed         */
+    IONN_ERR_WORKSPACE = 7 /* workspace NULL or smaller than required          */
+};
+
+/* Message for a status code (static string). */
+const char *ionn_status_str(int status);
+/* Message describing the calling thread's most recent error ("" if none). */
+const char *ionn_last_error(void);
+/* Library version, e.g. "ionn 0.1.0 gfx950". */
+const char *ionn_version(void);
+
+/* ------------------------------------------------------------------------ */
+/* Small helpers.                                                            */
+/* ------------------------------------------------------------------------ */
+
+/* dst[0..n) = value.  A kernel, not hipMemset, so it is safe inside captured
+ * HIP graphs.  n >= 0. */
+int ionn_fill_u32(uint32_t *dst, int64_t n, uint32_t value, void *stream);
+
+/* [TI] step 1, "max_val = max(|G|)": max-combines max |x[j]| over j < n into
+ * *absmax.  n >= 0 (n = 0 leaves *absmax unchanged). */
+int ionn_absmax_i32(const int32_t *x, int64_t n, uint32_t *absmax, void *stream);
+
+/* ------------------------------------------------------------------------ */
+/* Linear layer contractions (int8 x int8 -> int32).                         */
+/* Sizes: B, IN, OUT >= 0 and each < 2^31.                                   */
+/* ------------------------------------------------------------------------ */
+
+/* Forward product of a Linear layer ([TI] section 7, [TGR] FC index):
+ *   Y[b][o] = sum_i X[b][i] * W[o][i].
+ * X: int8 [B][IN]; W: int8 [OUT][IN]; Y: int32 [B][OUT] (written).
+ * absmax_Y (nullable): max-combined with max |Y|. */
+int int_linear_fwd(const int8_t *X, const int8_t *W, int32_t *Y, int64_t B,
+                   int64_t IN, int64_t OUT, uint32_t *absmax_Y, void *stream);
+
+/* Delta propagation (dgrad) of a Linear layer ([TI] section 3, delta
+ * propagation; section 4, ReLU mask):
+ *   dX[b][i] = sum_o dY[b][o] * W[o][i],
+ * then, if relu_act is not NULL, dX[b][i] = 0 wherever relu_act[b][i] <= 0
+ * (relu_act is the int8 [B][IN] output of the layer below, whose ReLU mask is
+ * "activation > 0").  dY: int8 [B][OUT]; W: int8 [OUT][IN]; dX: int32
+ * [B][IN] (written).  absmax_dX (nullable) sees the masked values. */
+int int_linear_dgrad(const int8_t *dY, const int8_t *W, const int8_t *relu_act,
+                     int32_t *dX, int64_t B, int64_t IN, int64_t OUT,
+                     uint32_t *absmax_dX, void *stream);
+
+/* Weight gradient of a Linear layer, the tensor G of [TI] section 3:
+ *   G[o][i] = sum_b dY[b][o] * X[b][i].
+ * dY: int8 [B][OUT]; X: int8 [B][IN]; G: int32 [OUT][IN] (written).
+ * absmax_G (nullable): max-combined with max |G|. */
+int int_linear_wgrad(const int8_t *dY, const int8_t *X, int32_t *G, int64_t B,
+                     int64_t IN, int64_t OUT, uint32_t *absmax_G, void *stream);
+
+/* ------------------------------------------------------------------------ */
+/* NITI quantiser and update ([TI] section 3, steps 1-5).                    */
+/* ------------------------------------------------------------------------ */
+
+/* Requantise an int32 tensor to int8 with one dynamic per-tensor shift:
+ *   m  = *absmax (device; the caller has max-combined max |acc| into it);
+ *   s  = max(0, bitlen(m) - target_bits)            (bitlen = ceil(log2(m+1)))
+ *   out[j] = sat8(rhu(acc[j], s)), then max(out, 0) if relu != 0,
+ * where rhu(x, s) = floor((x + 2^(s-1)) / 2^s) ("round-half-up", ties toward
+ * +infinity) and sat8 clamps to [-128, 127].  target_bits = 7 is the delta
+ * propagation setting.  shift_out (nullable, device int32) receives s.
+ * n >= 0; target_bits in [1, 31]; relu in {0, 1}. */
+int niti_quantize(const int32_t *acc, int64_t n, const uint32_t *absmax,
+                  int target_bits, int relu, int8_t *out, int32_t *shift_out,
+                  void *stream);
+
+/* NITI weight update, in place on W:
+ *   s  = max(0, bitlen(*absmax) - target_bits)
+ *   ws = max(0, s - mu_weight)
+ *   Gq = rhu(G[j], s)          (int32, not clamped)
+ *   d  = rhu(Gq, ws)
+ *   W[j] = sat8(W[j] - d)
+ * Every W element is rewritten.  shifts_out (nullable, device int32[2])
+ * receives {s, ws}.  gq_out (nullable, device int32[n]) receives Gq.
+ * n >= 0; target_bits in [1, 31]; mu_weight in [0, 31]. */
+int niti_quantize_update(const int32_t *G, int64_t n, const uint32_t *absmax,
+                         int target_bits, int mu_weight, int8_t *W,
+                         int32_t *shifts_out, int32_t *gq_out, void *stream);
+
+/* Output error of a classifier whose loss pushes the true class toward a
+ * target magnitude and the others toward 0 ([TI] sections 4 and 6.2: user
+ * loss writes the delta for the backward pass):
+ *   e[b][c] = (c == labels[b] ? target_mag : 0) - out[b][c].
+ * out: int8 [B][C]; labels: int32 [B] (values outside [0, C) match no class);
+ * e: int32 [B][C] (written); absmax_e (nullable) max-combined.
+ * target_mag in [-128, 127]. */
+int int_output_error(const int8_t *out, const int32_t *labels, int64_t B,
+                     int64_t C, int target_mag, int32_t *e, uint32_t *absmax_e,
+                     void *stream);
+
+/* ------------------------------------------------------------------------ */
+/* Conv2D contractions ([TI] section 7), NHWC / OHWI, cross-correlation.     */
+/* Supported geometry: KH = KW = 3, stride 1, pad 1, dilation 1, groups 1;   */
+/* anything else returns IONN_ERR_UNSUPPORTED (the page's export refuses     */
+/* grouped and dilated convolutions outright).  Output size = input size.   */
+/* N, H, W, Cin, Cout >= 0; Cin and Cout must be multiples of 16 (else       */
+/* IONN_ERR_UNSUPPORTED); every tensor must fit in 2^31 elements.            */
+/* ------------------------------------------------------------------------ */
+
+typedef struct ionn_conv_desc {
+    int64_t N, H, W, Cin, Cout;
+    int32_t KH, KW, stride, pad, dilation, groups;
+} ionn_conv_desc;
+
+/* Y[n,h,w,co] = sum_{kh,kw,ci} X[n,h+kh-1,w+kw-1,ci] * Wt[co,kh,kw,ci]
+ * (zero outside the image).  X: int8 [N][H][W][Cin]; Wt: int8
+ * [Cout][3][3][Cin]; Y: int32 [N][H][W][Cout] (written). */
+int int_conv_fwd(const int8_t *X, const int8_t *Wt, int32_t *Y,
+                 const ionn_conv_desc *desc, uint32_t *absmax_Y, void *stream);
+
+/* dX[n,h,w,ci] = sum_{kh,kw,co} dY[n,h-kh+1,w-kw+1,co] * Wt[co,kh,kw,ci].
+ * dY: int8 [N][H][W][Cout]; dX: int32 [N][H][W][Cin] (written). */
+int int_conv_dgrad(const int8_t *dY, const int8_t *Wt, int32_t *dX,
+                   const ionn_conv_desc *desc, uint32_t *absmax_dX,
+                   void *stream);
+
+/* G[co,kh,kw,ci] = sum_{n,h,w} dY[n,h,w,co] * X[n,h+kh-1,w+kw-1,ci].
+ * G: int32 [Cout][3][3][Cin] (written; the call clears it first). */
+int int_conv_wgrad(const int8_t *dY, const int8_t *X, int32_t *G,
+                   const ionn_conv_desc *desc, uint32_t *absmax_G,
+                   void *stream);
+
+/* ------------------------------------------------------------------------ */
+/* DFP-16 shared-exponent contractions ([DFP] sections 3, 3.1, 4).           */
+/*                                                                            */
+/* A DFP-16 tensor is int16 mantissas I plus one shared exponent E (value     */
+/* I * 2^E); E is a device int32 scalar that must lie in [-128, 127].  Each   */
+/* contraction multiplies int16 x int16 -> int32 and sums the reduction in    */
+/* chunks of `chunk` terms (the last chunk may be shorter).  Overflow         */
+/* management: each chunk's int32 partial p_c is shifted down by              */
+/* r = ceil(log2(number of chunks)) (0 for one chunk) with round-half-up      */
+/* before the chunks are summed, acc = sum_c rhu(p_c, r) (int32).  Adaptive  */
+/* down-conversion: Rs = max(0, bitlen(max |acc|) - 15),                      */
+/* out = sat16(rhu(acc, Rs)), E_out = Ea + Eb + r + Rs.  If E_out leaves the  */
+/* signed 8-bit range the output exponent is still written and the device     */
+/* status word (status_out, nullable int32) is set to 1, else 0.              */
+/*                                                                            */
+/* Sizes: M, K, N >= 1, every tensor below 2^31 elements; chunk must be 64;  */
+/* the int16 output must be 16-byte aligned.  `workspace` is device memory of */
+/* at least dfp16_workspace_bytes(M, K, N, which) bytes, 256-byte aligned;    */
+/* its contents on entry are ignored (it holds the int32 accumulator, the     */
+/* max-abs scalar and, for dgrad/wgrad, K-major copies of the operands).      */
+/* ------------------------------------------------------------------------ */
+
+enum { IONN_DFP16_FWD = 0, IONN_DFP16_DGRAD = 1, IONN_DFP16_WGRAD = 2 };
+
+size_t dfp16_workspace_bytes(int64_t M, int64_t K, int64_t N, int which);
+
+/* Y[M][N] = X[M][K] . W[N][K]^T, reduced over K. */
+int dfp16_gemm_fwd(const int16_t *X, const int32_t *eX, const int16_t *W,
+                   const int32_t *eW, int16_t *Y, int32_t *eY, int64_t M,
+                   int64_t K, int64_t N, int chunk, void *workspace,
+                   size_t workspace_bytes, int32_t *status_out, void *stream);
+
+/* dX[M][K] = dY[M][N] . W[N][K], reduced over N. */
+int dfp16_gemm_dgrad(const int16_t *dY, const int32_t *edY, const int16_t *W,
+                     const int32_t *eW, int16_t *dX, int32_t *edX, int64_t M,
+                     int64_t K, int64_t N, int chunk, void *workspace,
+                     size_t workspace_bytes, int32_t *status_out,
+                     void *stream);
+
+/* G[N][K] = dY[M][N]^T . X[M][K], reduced over M. */
+int dfp16_gemm_wgrad(const int16_t *dY, const int32_t *edY, const int16_t *X,
+                     const int32_t *eX, int16_t *G, int32_t *eG, int64_t M,
+                     int64_t K, int64_t N, int chunk, void *workspace,
+                     size_t workspace_bytes, int32_t *status_out,
+                     void *stream);
+
+/* Gavg of a layer ([APT] Equation 4): the mean gradient magnitude over the
+ * layer's n parameters relative to the weights' resolution epsilon = 2^eW:
+ *   gavg = (sum_j |G[j]| / n) * 2^(eG - eW),
+ * the sum exact in int64, the division and scaling in IEEE double.
+ * G: int16 [n]; eG, eW: device int32; gavg_out: device double (written).
+ * n >= 1. */
+int dfp16_gavg(const int16_t *G, const int32_t *eG, const int32_t *eW,
+               int64_t n, double *gavg_out, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* IONN_H */

@@ -1,0 +1,94 @@
+// Internal helpers shared by the library's translation units: host-side
+// argument checking and error state, and the device-side integer primitives
+// of the NITI quantiser ("Integer On-Device Training: Overview", section 3,
+// steps 1-5).  Device code targets gfx950 only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/ionn.h"
+
+namespace ionn {
+
+// ---------------------------------------------------------------------------
+// Host: error state and checks.
+// ---------------------------------------------------------------------------
+
+void set_error(const char *fmt, ...) __attribute__((format(printf, 1, 2)));
+void clear_error();
+
+#define IONN_REQUIRE(cond, code, ...)      \
+    do {                                   \
+        if (!(cond)) {                     \
+            ::ionn::set_error(__VA_ARGS__); \
+            return (code);                 \
+        }                                  \
+    } while (0)
+
+// Check the launch that was just enqueued.
+int check_launch(const char *what);
+
+inline hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
+
+inline bool aligned(const void *p, size_t a) {
+    return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0;
+}
+
+constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
+
+// ---------------------------------------------------------------------------
+// Device: integer primitives.
+// ---------------------------------------------------------------------------
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+// |x| as uint32 so |INT32_MIN| = 2^31.
+__device__ __forceinline__ uint32_t abs_u32(int32_t x) {
+    return x < 0 ? 0u - static_cast<uint32_t>(x) : static_cast<uint32_t>(x);
+}
+
+// Number of binary digits: 0 for 0, else floor(log2 m) + 1 == ceil(log2(m+1)).
+__device__ __forceinline__ int bitlen_u32(uint32_t m) {
+    return m ? 32 - __builtin_clz(m) : 0;
+}
+
+// shift = max(0, bitlen(max_val) - target_bits).
+__device__ __forceinline__ int niti_shift(uint32_t max_val, int target_bits) {
+    int s = bitlen_u32(max_val) - target_bits;
+    return s > 0 ? s : 0;
+}
+
+// Round-half-up right shift floor((x + 2^(s-1)) / 2^s), computed without the
+// overflowing add: floor(x / 2^s) plus bit (s-1) of x.  s in [0, 31].
+__device__ __forceinline__ int32_t rhu(int32_t x, int s) {
+    if (s == 0) return x;
+    return (x >> s) + ((x >> (s - 1)) & 1);
+}
+
+__device__ __forceinline__ int32_t sat8(int32_t v) { return v < -128 ? -128 : (v > 127 ? 127 : v); }
+__device__ __forceinline__ int32_t sat16(int32_t v) {
+    return v < -32768 ? -32768 : (v > 32767 ? 32767 : v);
+}
+
+// Max over the 64 lanes of a wavefront.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        uint32_t o = __shfl_xor(v, off, 64);
+        v = o > v ? o : v;
+    }
+    return v;
+}
+
+__device__ __forceinline__ int64_t wave_sum_i64(int64_t v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+}  // namespace ionn

@@ -1,0 +1,480 @@
+// DFP-16 shared-exponent contractions ("Mixed Precision Training of
+// Convolutional Neural Networks using Integer Operations", sections 3, 3.1
+// and 4 "Handling overflows") and the Gavg metric ("Adaptive Precision
+// Training for Resource Constrained Devices", Equation 4).
+//
+// gfx950 has no int16 matrix instruction, so each int16 mantissa is split
+// exactly into two int8 digits:  a = 256*ah + al + 128  with
+//   ah = a >> 8            (the signed high byte, in [-128, 127])
+//   al = (a & 255) - 128   (the low byte with its top bit flipped, in [-128, 127]).
+// For one 64-term chunk (k over the chunk, A' = a - 128, B' = b - 128):
+//   sum a*b = 65536*sum(ah*bh) + 256*sum(ah*bl + al*bh) + sum(al*bl)
+//             + 128*sum(A') + 128*sum(B') + 2^20                  (mod 2^32)
+// Four v_mfma_i32_16x16x64_i8 per 16x16 block give the digit products (the
+// two cross terms chained into one accumulator); the row sums of A' and column
+// sums of B' come from the same instruction against an all-ones fragment.
+// Zero padding (a = 0: ah = 0, al = -128) contributes exactly 0, so every chunk
+// is evaluated as a full 64-term chunk.
+//
+// Overflow management: each chunk's int32 partial p_c is shifted down by
+// r = ceil(log2(number of chunks)) with round-half-up before it joins the
+// int32 accumulator, so the sum of chunks stays in range.  The accumulator
+// then goes through adaptive down-conversion: Rs = max(0, bitlen(max|acc|)
+// - 15), out = sat16(rhu(acc, Rs)), E_out = Ea + Eb + r + Rs.
+#include "common.h"
+
+namespace ionn {
+
+int launch_absmax_i32(const int32_t *x, int64_t n, uint32_t *absmax, hipStream_t st);
+
+namespace {
+
+constexpr int kChunk = 64;
+constexpr int kPad = 16;
+
+// Split 8 int16 (4 dwords) into 8 high bytes and 8 flipped low bytes.
+__device__ __forceinline__ void split8(v4i w, uint32_t &h0, uint32_t &h1, uint32_t &l0,
+                                       uint32_t &l1) {
+    auto hi = [](uint32_t a, uint32_t b) {
+        return ((a >> 8) & 0xffu) | ((a >> 16) & 0xff00u) | ((b << 8) & 0xff0000u) | (b & 0xff000000u);
+    };
+    auto lo = [](uint32_t a, uint32_t b) {
+        return ((a & 0xffu) | ((a >> 8) & 0xff00u) | ((b & 0xffu) << 16) | ((b << 8) & 0xff000000u)) ^
+               0x80808080u;
+    };
+    h0 = hi(uint32_t(w.x), uint32_t(w.y));
+    h1 = hi(uint32_t(w.z), uint32_t(w.w));
+    l0 = lo(uint32_t(w.x), uint32_t(w.y));
+    l1 = lo(uint32_t(w.z), uint32_t(w.w));
+}
+
+// K-major int16 operand: element (r, k) at base[r * ld + k].
+struct Src16 {
+    const int16_t *base;
+    int64_t ld;
+    int rows, kdim;
+    bool vec;  // base 16-byte aligned and ld % 8 == 0
+    template <bool EDGE>
+    __device__ __forceinline__ v4i chunk(int r, int k) const {  // 8 elements k..k+7
+        const int16_t *p = base + int64_t(r) * ld + k;
+        if (!EDGE || (r < rows && k + 8 <= kdim && vec)) return *reinterpret_cast<const v4i *>(p);
+        uint32_t w[4] = {0, 0, 0, 0};
+        if (r < rows)
+            for (int e = 0; e < 8; ++e)
+                if (k + e < kdim) w[e >> 1] |= uint32_t(uint16_t(p[e])) << (16 * (e & 1));
+        return v4i{int(w[0]), int(w[1]), int(w[2]), int(w[3])};
+    }
+};
+
+// Tile of R rows x 64 k (int16) -> LDS planes hi[R][64+kPad], lo[R][64+kPad].
+template <int R, int NT, bool EDGE>
+struct Loader16 {
+    static constexpr int kChunks = R * kChunk / 8;
+    static constexpr int kPer = (kChunks + NT - 1) / NT;
+    v4i reg[kPer];
+    __device__ __forceinline__ void load(const Src16 &s, int r0, int k0, int tid) {
+#pragma unroll
+        for (int it = 0; it < kPer; ++it) {
+            const int id = it * NT + tid;
+            v4i v = {0, 0, 0, 0};
+            if (kChunks % NT == 0 || id < kChunks) v = s.template chunk<EDGE>(r0 + id / 8, k0 + 8 * (id % 8));
+            reg[it] = v;
+        }
+    }
+    __device__ __forceinline__ void store(int8_t *hi, int8_t *lo, int tid) const {
+#pragma unroll
+        for (int it = 0; it < kPer; ++it) {
+            const int id = it * NT + tid;
+            if (kChunks % NT == 0 || id < kChunks) {
+                uint32_t h0, h1, l0, l1;
+                split8(reg[it], h0, h1, l0, l1);
+                const int off = (id / 8) * (kChunk + kPad) + 8 * (id % 8);
+                *reinterpret_cast<uint2 *>(hi + off) = make_uint2(h0, h1);
+                *reinterpret_cast<uint2 *>(lo + off) = make_uint2(l0, l1);
+            }
+        }
+    }
+};
+
+struct DfpArgs {
+    Src16 a, b;          // A [M][L], B [N][L], both K-major
+    int32_t *acc;        // [M][N], ldc = N
+    uint32_t *absmax;    // max-combined (non-atomic epilogue only)
+    int M, N, L;
+    int r;               // per-chunk shift
+    int split;           // K splits (gridDim.y)
+    bool atomic;         // accumulate with atomicAdd (split > 1)
+};
+
+template <int BM, int BN, int WGM, int WGN, bool EDGE>
+__global__ __launch_bounds__(WGM *WGN * 64) void dfp16_kernel(DfpArgs g) {
+    constexpr int NT = WGM * WGN * 64;
+    constexpr int WTM = BM / WGM, WTN = BN / WGN;
+    constexpr int FM = WTM / 16, FN = WTN / 16;
+    constexpr int ROW = kChunk + kPad;
+    constexpr int PLANE_A = BM * ROW, PLANE_B = BN * ROW;
+    constexpr int STAGE = 2 * PLANE_A + 2 * PLANE_B;
+    __shared__ __attribute__((aligned(16))) int8_t lds[2 * STAGE];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / WGN, wn = wave % WGN;
+    const int tiles_n = (g.N + BN - 1) / BN;
+    const int tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int nchunks = (g.L + kChunk - 1) / kChunk;
+    const int c_begin = int(int64_t(nchunks) * blockIdx.y / g.split);
+    const int c_end = int(int64_t(nchunks) * (blockIdx.y + 1) / g.split);
+
+    Loader16<BM, NT, EDGE> la;
+    Loader16<BN, NT, EDGE> lb;
+    v4i acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = v4i{0, 0, 0, 0};
+
+    if (c_begin < c_end) {
+        la.load(g.a, m0, c_begin * kChunk, tid);
+        lb.load(g.b, n0, c_begin * kChunk, tid);
+        la.store(lds, lds + PLANE_A, tid);
+        lb.store(lds + 2 * PLANE_A, lds + 2 * PLANE_A + PLANE_B, tid);
+    }
+    __syncthreads();
+
+    const v4i ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
+    const v4i zero = {0, 0, 0, 0};
+    const int frow = lane & 15, fk = (lane >> 4) * 16;
+    const int r = g.r;
+    for (int c = c_begin; c < c_end; ++c) {
+        const int cur = (c - c_begin) & 1;
+        const int8_t *Ah = lds + cur * STAGE, *Al = Ah + PLANE_A;
+        const int8_t *Bh = Ah + 2 * PLANE_A, *Bl = Bh + PLANE_B;
+        if (c + 1 < c_end) {
+            la.load(g.a, m0, (c + 1) * kChunk, tid);
+            lb.load(g.b, n0, (c + 1) * kChunk, tid);
+        }
+        v4i ah[FM], al[FM], rt[FM];
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int off = (wm * WTM + i * 16 + frow) * ROW + fk;
+            ah[i] = *reinterpret_cast<const v4i *>(Ah + off);
+            al[i] = *reinterpret_cast<const v4i *>(Al + off);
+            // row sums of A' = 256*ah + al, every value of the fragment is the
+            // sum for this lane's row m
+            v4i sh = __builtin_amdgcn_mfma_i32_16x16x64_i8(ones, ah[i], zero, 0, 0, 0);
+            v4i sl = __builtin_amdgcn_mfma_i32_16x16x64_i8(ones, al[i], zero, 0, 0, 0);
+            const uint32_t ra = (uint32_t(sh.x) << 8) + uint32_t(sl.x);
+            rt[i].x = int(ra * 128u + (1u << 20));
+        }
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int off = (wn * WTN + j * 16 + frow) * ROW + fk;
+            const v4i bh = *reinterpret_cast<const v4i *>(Bh + off);
+            const v4i bl = *reinterpret_cast<const v4i *>(Bl + off);
+            // column sums of B' for this lane's four columns
+            const v4i ch = __builtin_amdgcn_mfma_i32_16x16x64_i8(bh, ones, zero, 0, 0, 0);
+            const v4i cl = __builtin_amdgcn_mfma_i32_16x16x64_i8(bl, ones, zero, 0, 0, 0);
+            uint32_t ct[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) ct[v] = ((uint32_t(ch[v]) << 8) + uint32_t(cl[v])) * 128u;
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                const v4i hh = __builtin_amdgcn_mfma_i32_16x16x64_i8(bh, ah[i], zero, 0, 0, 0);
+                v4i x = __builtin_amdgcn_mfma_i32_16x16x64_i8(bl, ah[i], zero, 0, 0, 0);
+                x = __builtin_amdgcn_mfma_i32_16x16x64_i8(bh, al[i], x, 0, 0, 0);
+                const v4i ll = __builtin_amdgcn_mfma_i32_16x16x64_i8(bl, al[i], zero, 0, 0, 0);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const uint32_t p = (uint32_t(hh[v]) << 16) + (uint32_t(x[v]) << 8) +
+                                       uint32_t(ll[v]) + uint32_t(rt[i].x) + ct[v];
+                    acc[i][j][v] += rhu(int32_t(p), r);
+                }
+            }
+        }
+        if (c + 1 < c_end) {
+            int8_t *nxt = lds + (cur ^ 1) * STAGE;
+            la.store(nxt, nxt + PLANE_A, tid);
+            lb.store(nxt + 2 * PLANE_A, nxt + 2 * PLANE_A + PLANE_B, tid);
+        }
+        __syncthreads();
+    }
+
+    uint32_t amax = 0;
+    const int em = lane & 15, en = (lane >> 4) * 4;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+        const int m = m0 + wm * WTM + i * 16 + em;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int n = n0 + wn * WTN + j * 16 + en;
+            int32_t *cp = g.acc + int64_t(m) * g.N + n;
+            if (g.atomic) {
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    if (m < g.M && n + v < g.N) atomicAdd(cp + v, acc[i][j][v]);
+            } else if (!EDGE || (m < g.M && n + 4 <= g.N)) {
+                *reinterpret_cast<v4i *>(cp) = acc[i][j];
+#pragma unroll
+                for (int v = 0; v < 4; ++v) amax = max(amax, abs_u32(acc[i][j][v]));
+            } else {
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    if (m < g.M && n + v < g.N) {
+                        cp[v] = acc[i][j][v];
+                        amax = max(amax, abs_u32(acc[i][j][v]));
+                    }
+            }
+        }
+    }
+    if (!g.atomic && g.absmax) {
+        amax = wave_max_u32(amax);
+        if (lane == 0 && amax != 0) atomicMax(g.absmax, amax);
+    }
+}
+
+// out = sat16(rhu(acc, Rs)), Rs from the tensor max; exponent bookkeeping.
+__global__ __launch_bounds__(256) void downconvert_kernel(const int32_t *__restrict__ acc, int64_t n,
+                                                          const uint32_t *__restrict__ absmax,
+                                                          const int32_t *__restrict__ ea,
+                                                          const int32_t *__restrict__ eb, int r,
+                                                          int16_t *__restrict__ out,
+                                                          int32_t *__restrict__ e_out,
+                                                          int32_t *__restrict__ status) {
+    const int rs = niti_shift(*absmax, 15);
+    const int64_t tid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    const int64_t nt = int64_t(gridDim.x) * blockDim.x;
+    if (tid == 0) {
+        const int e = *ea + *eb + r + rs;
+        *e_out = e;
+        if (status) *status = (e < -128 || e > 127) ? 1 : 0;
+    }
+    const int64_t n8 = n / 8;
+    const v4i *av = reinterpret_cast<const v4i *>(acc);
+    v4i *ov = reinterpret_cast<v4i *>(out);
+    for (int64_t g = tid; g < n8; g += nt) {
+        const v4i a0 = av[2 * g], a1 = av[2 * g + 1];
+        auto q = [&](int32_t v) { return uint32_t(uint16_t(int16_t(sat16(rhu(v, rs))))); };
+        ov[g] = v4i{int(q(a0.x) | (q(a0.y) << 16)), int(q(a0.z) | (q(a0.w) << 16)),
+                    int(q(a1.x) | (q(a1.y) << 16)), int(q(a1.z) | (q(a1.w) << 16))};
+    }
+    for (int64_t i = n8 * 8 + tid; i < n; i += nt) out[i] = int16_t(sat16(rhu(acc[i], rs)));
+}
+
+// dst[c][r] = src[r][c] for an R x C int16 matrix (64x64 tiles through LDS).
+__global__ __launch_bounds__(256) void transpose16_kernel(const int16_t *__restrict__ src,
+                                                          int16_t *__restrict__ dst, int R, int C) {
+    __shared__ int16_t t[64][65];
+    const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+    for (int i = ty; i < 64; i += 4)
+        if (r0 + i < R && c0 + tx < C) t[i][tx] = src[int64_t(r0 + i) * C + c0 + tx];
+    __syncthreads();
+    for (int i = ty; i < 64; i += 4)
+        if (c0 + i < C && r0 + tx < R) dst[int64_t(c0 + i) * R + r0 + tx] = t[tx][i];
+}
+
+__global__ void zero_i32_kernel(int32_t *C, int64_t n) {
+    for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+         i += int64_t(gridDim.x) * blockDim.x)
+        C[i] = 0;
+}
+
+// Gavg: one workgroup sums |g| exactly in int64, then scales in double.
+__global__ __launch_bounds__(1024) void gavg_kernel(const int16_t *__restrict__ g, int64_t n,
+                                                    const int32_t *__restrict__ eg,
+                                                    const int32_t *__restrict__ ew,
+                                                    double *__restrict__ out) {
+    __shared__ int64_t part[16];
+    int64_t s = 0;
+    for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
+        const int32_t v = g[i];
+        s += v < 0 ? -v : v;
+    }
+    s = wave_sum_i64(s);
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = s;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int64_t tot = 0;
+        for (int w = 0; w < int(blockDim.x / 64); ++w) tot += part[w];
+        double v = double(tot) / double(n);
+        int e = *eg - *ew;
+        for (; e > 0; --e) v *= 2.0;
+        for (; e < 0; ++e) v *= 0.5;
+        *out = v;
+    }
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+int chunk_shift(int64_t L) {
+    const int64_t nc = (L + kChunk - 1) / kChunk;
+    int r = 0;
+    while ((int64_t(1) << r) < nc) ++r;
+    return nc <= 1 ? 0 : r;
+}
+
+// acc[M][N] = sum_c rhu(p_c, r) for A [M][L], B [N][L] (K-major int16).
+int contract(const Src16 &a, const Src16 &b, int M, int N, int L, int32_t *acc, uint32_t *absmax,
+             hipStream_t st) {
+    DfpArgs g{a, b, acc, absmax, M, N, L, chunk_shift(L), 1, false};
+    const int tiles = ((M + 127) / 128) * ((N + 127) / 128);
+    const int nchunks = (L + kChunk - 1) / kChunk;
+    if (tiles < 512 && nchunks >= 16) {
+        int split = (1024 + tiles - 1) / tiles;
+        if (split > nchunks / 4) split = nchunks / 4;
+        g.split = split < 1 ? 1 : split;
+    }
+    g.atomic = g.split > 1;
+    if (g.atomic) {
+        zero_i32_kernel<<<dim3(1024), dim3(256), 0, st>>>(acc, int64_t(M) * N);
+        if (int rc = check_launch("dfp16 contraction")) return rc;
+    }
+    const bool even = M % 128 == 0 && N % 128 == 0 && L % kChunk == 0 && a.vec && b.vec;
+    dim3 grid(tiles, g.split), block(256);
+    if (even) dfp16_kernel<128, 128, 2, 2, false><<<grid, block, 0, st>>>(g);
+    else dfp16_kernel<128, 128, 2, 2, true><<<grid, block, 0, st>>>(g);
+    if (int rc = check_launch("dfp16 contraction")) return rc;
+    if (g.atomic) return launch_absmax_i32(acc, int64_t(M) * N, absmax, st);
+    return IONN_OK;
+}
+
+struct Workspace {
+    int32_t *acc;
+    uint32_t *absmax;
+    int16_t *t0, *t1;
+};
+
+size_t ws_bytes(int64_t M, int64_t K, int64_t N, int which, Workspace *w, void *base) {
+    int64_t out = which == IONN_DFP16_FWD ? M * N : which == IONN_DFP16_DGRAD ? M * K : N * K;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t o = off;
+        off += align256(bytes);
+        return base ? static_cast<char *>(base) + o : nullptr;
+    };
+    char *acc = take(size_t(out) * 4);
+    char *am = take(4);
+    char *t0 = nullptr, *t1 = nullptr;
+    if (which == IONN_DFP16_DGRAD) t0 = take(size_t(N) * K * 2);           // W^T [K][N]
+    if (which == IONN_DFP16_WGRAD) {
+        t0 = take(size_t(N) * M * 2);                                        // dY^T [N][M]
+        t1 = take(size_t(K) * M * 2);                                        // X^T  [K][M]
+    }
+    if (w) *w = Workspace{reinterpret_cast<int32_t *>(acc), reinterpret_cast<uint32_t *>(am),
+                          reinterpret_cast<int16_t *>(t0), reinterpret_cast<int16_t *>(t1)};
+    return off;
+}
+
+int transpose16(const int16_t *src, int16_t *dst, int R, int C, hipStream_t st) {
+    dim3 grid((C + 63) / 64, (R + 63) / 64);
+    transpose16_kernel<<<grid, dim3(256), 0, st>>>(src, dst, R, C);
+    return check_launch("dfp16 transpose");
+}
+
+int finish(const Workspace &w, int64_t n, const int32_t *ea, const int32_t *eb, int r, int16_t *out,
+           int32_t *e_out, int32_t *status, hipStream_t st) {
+    int64_t blocks = (n / 8 + 255) / 256;
+    if (blocks < 1) blocks = 1;
+    if (blocks > 8192) blocks = 8192;
+    downconvert_kernel<<<dim3(unsigned(blocks)), dim3(256), 0, st>>>(w.acc, n, w.absmax, ea, eb, r,
+                                                                    out, e_out, status);
+    return check_launch("dfp16 down-conversion");
+}
+
+int check_common(const void *A, const int32_t *eA, const void *B, const int32_t *eB, void *out,
+                 int32_t *eout, int64_t M, int64_t K, int64_t N, int chunk, void *ws,
+                 size_t ws_size, int which, const char *name) {
+    IONN_REQUIRE(M >= 1 && K >= 1 && N >= 1 && M <= kMaxDim && K <= kMaxDim && N <= kMaxDim &&
+                     M * N <= kMaxDim && M * K <= kMaxDim && N * K <= kMaxDim,
+                 IONN_ERR_SHAPE, "%s: sizes must be >= 1 with every tensor below 2^31 elements",
+                 name);
+    IONN_REQUIRE(chunk == kChunk, IONN_ERR_RANGE, "%s: chunk must be 64 (got %d)", name, chunk);
+    IONN_REQUIRE(A && eA && B && eB && out && eout, IONN_ERR_ARG, "%s: NULL argument", name);
+    IONN_REQUIRE(ws != nullptr && aligned(ws, 256) &&
+                     ws_size >= ws_bytes(M, K, N, which, nullptr, nullptr),
+                 IONN_ERR_WORKSPACE, "%s: workspace must be 256-byte aligned and hold %zu bytes",
+                 name, ws_bytes(M, K, N, which, nullptr, nullptr));
+    IONN_REQUIRE(aligned(A, 2) && aligned(B, 2) && aligned(out, 16) && aligned(eA, 4) &&
+                     aligned(eB, 4) && aligned(eout, 4),
+                 IONN_ERR_ALIGN, "%s: misaligned pointer (out needs 16 bytes)", name);
+    return IONN_OK;
+}
+
+}  // namespace
+}  // namespace ionn
+
+using namespace ionn;
+
+extern "C" {
+
+size_t dfp16_workspace_bytes(int64_t M, int64_t K, int64_t N, int which) {
+    if (M < 1 || K < 1 || N < 1 || which < 0 || which > 2) return 0;
+    return ws_bytes(M, K, N, which, nullptr, nullptr);
+}
+
+int dfp16_gemm_fwd(const int16_t *X, const int32_t *eX, const int16_t *W, const int32_t *eW,
+                   int16_t *Y, int32_t *eY, int64_t M, int64_t K, int64_t N, int chunk,
+                   void *workspace, size_t workspace_bytes, int32_t *status_out, void *stream) {
+    clear_error();
+    if (int rc = check_common(X, eX, W, eW, Y, eY, M, K, N, chunk, workspace, workspace_bytes,
+                              IONN_DFP16_FWD, "dfp16_gemm_fwd"))
+        return rc;
+    hipStream_t st = as_stream(stream);
+    Workspace w;
+    ws_bytes(M, K, N, IONN_DFP16_FWD, &w, workspace);
+    zero_i32_kernel<<<dim3(1), dim3(64), 0, st>>>(reinterpret_cast<int32_t *>(w.absmax), 1);
+    Src16 a{X, K, int(M), int(K), aligned(X, 16) && K % 8 == 0};
+    Src16 b{W, K, int(N), int(K), aligned(W, 16) && K % 8 == 0};
+    if (int rc = contract(a, b, int(M), int(N), int(K), w.acc, w.absmax, st)) return rc;
+    return finish(w, M * N, eX, eW, chunk_shift(K), Y, eY, status_out, st);
+}
+
+int dfp16_gemm_dgrad(const int16_t *dY, const int32_t *edY, const int16_t *W, const int32_t *eW,
+                     int16_t *dX, int32_t *edX, int64_t M, int64_t K, int64_t N, int chunk,
+                     void *workspace, size_t workspace_bytes, int32_t *status_out, void *stream) {
+    clear_error();
+    if (int rc = check_common(dY, edY, W, eW, dX, edX, M, K, N, chunk, workspace, workspace_bytes,
+                              IONN_DFP16_DGRAD, "dfp16_gemm_dgrad"))
+        return rc;
+    hipStream_t st = as_stream(stream);
+    Workspace w;
+    ws_bytes(M, K, N, IONN_DFP16_DGRAD, &w, workspace);
+    zero_i32_kernel<<<dim3(1), dim3(64), 0, st>>>(reinterpret_cast<int32_t *>(w.absmax), 1);
+    if (int rc = transpose16(W, w.t0, int(N), int(K), st)) return rc;  // W^T [K][N]
+    Src16 a{dY, N, int(M), int(N), aligned(dY, 16) && N % 8 == 0};
+    Src16 b{w.t0, N, int(K), int(N), N % 8 == 0};
+    if (int rc = contract(a, b, int(M), int(K), int(N), w.acc, w.absmax, st)) return rc;
+    return finish(w, M * K, edY, eW, chunk_shift(N), dX, edX, status_out, st);
+}
+
+int dfp16_gemm_wgrad(const int16_t *dY, const int32_t *edY, const int16_t *X, const int32_t *eX,
+                     int16_t *G, int32_t *eG, int64_t M, int64_t K, int64_t N, int chunk,
+                     void *workspace, size_t workspace_bytes, int32_t *status_out, void *stream) {
+    clear_error();
+    if (int rc = check_common(dY, edY, X, eX, G, eG, M, K, N, chunk, workspace, workspace_bytes,
+                              IONN_DFP16_WGRAD, "dfp16_gemm_wgrad"))
+        return rc;
+    hipStream_t st = as_stream(stream);
+    Workspace w;
+    ws_bytes(M, K, N, IONN_DFP16_WGRAD, &w, workspace);
+    zero_i32_kernel<<<dim3(1), dim3(64), 0, st>>>(reinterpret_cast<int32_t *>(w.absmax), 1);
+    if (int rc = transpose16(dY, w.t0, int(M), int(N), st)) return rc;  // dY^T [N][M]
+    if (int rc = transpose16(X, w.t1, int(M), int(K), st)) return rc;   // X^T  [K][M]
+    Src16 a{w.t0, M, int(N), int(M), M % 8 == 0};
+    Src16 b{w.t1, M, int(K), int(M), M % 8 == 0};
+    if (int rc = contract(a, b, int(N), int(K), int(M), w.acc, w.absmax, st)) return rc;
+    return finish(w, N * K, edY, eX, chunk_shift(M), G, eG, status_out, st);
+}
+
+int dfp16_gavg(const int16_t *G, const int32_t *eG, const int32_t *eW, int64_t n, double *gavg_out,
+               void *stream) {
+    clear_error();
+    IONN_REQUIRE(n >= 1, IONN_ERR_SHAPE, "dfp16_gavg: n = %lld < 1", (long long)n);
+    IONN_REQUIRE(G && eG && eW && gavg_out, IONN_ERR_ARG, "dfp16_gavg: NULL argument");
+    IONN_REQUIRE(aligned(G, 2) && aligned(eG, 4) && aligned(eW, 4) && aligned(gavg_out, 8),
+                 IONN_ERR_ALIGN, "dfp16_gavg: misaligned pointer");
+    gavg_kernel<<<dim3(1), dim3(1024), 0, as_stream(stream)>>>(G, n, eG, eW, gavg_out);
+    return check_launch("dfp16_gavg");
+}
+
+}  // extern "C"

@@ -1,0 +1,121 @@
+// int8 x int8 -> int32 contractions of a Linear layer ("Integer On-Device
+// Training: Overview", sections 3-4 and 7; weight index W[oc*IC + ic] as on
+// the TiGrIS "Compilation Pipeline" page) on gfx950 matrix cores.
+//
+//   fwd   Y  = X  W^T : A = X  [M=B][K=IN]  (K-major), B = W [N=OUT][K=IN] (K-major)
+//   dgrad dX = dY W   : A = dY [M=B][K=OUT] (K-major), B = W [K=OUT][N=IN] (N-major)
+//   wgrad G  = dY^T X : A = dY [K=B][M=OUT] (M-major), B = X [K=B][N=IN]   (N-major)
+//
+// Large tile-aligned problems run 256x256x64 tiles (4 wavefronts, 128x128
+// each: per 64-deep step a workgroup stages 32 KiB in LDS and issues 256
+// MFMAs); anything else runs bounds-checked 64x64 tiles.  The epilogue fuses
+// dgrad's ReLU mask and the max-abs that feeds the NITI shift.
+#include "gemm_core.h"
+
+namespace ionn {
+namespace {
+
+using namespace gemm;
+
+template <class SA, class SB>
+void launch_linear(const SA &sa, const SB &sb, const Epi &ep, int M, int N, int K, bool fast,
+                   hipStream_t st) {
+    if (fast)
+        launch<256, 256, 64, 2, 2, false>(sa, sb, ep, M, N, K, 1, st);
+    else if (M >= 1024 && N >= 1024)
+        launch<256, 256, 64, 2, 2, true>(sa, sb, ep, M, N, K, 1, st);
+    else
+        launch<64, 64, 64, 2, 2, true>(sa, sb, ep, M, N, K, 1, st);
+}
+
+__global__ void zero_i32_kernel(int32_t *C, int64_t n) {
+    for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+         i += int64_t(gridDim.x) * blockDim.x)
+        C[i] = 0;
+}
+
+// Empty reduction (K == 0): C = 0, which leaves any max-abs unchanged.
+int zero_output(int32_t *C, int64_t n, hipStream_t st, const char *name) {
+    int64_t blocks = (n + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    zero_i32_kernel<<<dim3(unsigned(blocks)), dim3(256), 0, st>>>(C, n);
+    return check_launch(name);
+}
+
+bool dims_ok(int64_t B, int64_t IN, int64_t OUT) {
+    return B >= 0 && IN >= 0 && OUT >= 0 && B <= kMaxDim && IN <= kMaxDim && OUT <= kMaxDim;
+}
+
+bool tile_aligned(int M, int N, int K) { return M % 256 == 0 && N % 256 == 0 && K % 64 == 0; }
+
+}  // namespace
+}  // namespace ionn
+
+using namespace ionn;
+using namespace ionn::gemm;
+
+extern "C" {
+
+int int_linear_fwd(const int8_t *X, const int8_t *W, int32_t *Y, int64_t B, int64_t IN,
+                   int64_t OUT, uint32_t *absmax_Y, void *stream) {
+    clear_error();
+    IONN_REQUIRE(dims_ok(B, IN, OUT), IONN_ERR_SHAPE,
+                 "int_linear_fwd: sizes must be in [0, 2^31): B=%lld IN=%lld OUT=%lld",
+                 (long long)B, (long long)IN, (long long)OUT);
+    if (B == 0 || OUT == 0) return IONN_OK;
+    IONN_REQUIRE(Y && (IN == 0 || (X && W)), IONN_ERR_ARG, "int_linear_fwd: NULL tensor");
+    IONN_REQUIRE(aligned(Y, 4) && aligned(absmax_Y, 4), IONN_ERR_ALIGN,
+                 "int_linear_fwd: Y/absmax must be 4-byte aligned");
+    hipStream_t st = as_stream(stream);
+    if (IN == 0) return zero_output(Y, B * OUT, st, "int_linear_fwd");
+    const int M = int(B), N = int(OUT), K = int(IN);
+    SrcRowK sa{X, IN, M, K, aligned(X, 16) && IN % 16 == 0};
+    SrcRowK sb{W, IN, N, K, aligned(W, 16) && IN % 16 == 0};
+    Epi ep{Y, OUT, M, N, aligned(Y, 16) && OUT % 4 == 0, nullptr, absmax_Y, false};
+    launch_linear(sa, sb, ep, M, N, K, tile_aligned(M, N, K) && sa.vec && sb.vec && ep.vec, st);
+    return check_launch("int_linear_fwd");
+}
+
+int int_linear_dgrad(const int8_t *dY, const int8_t *W, const int8_t *relu_act, int32_t *dX,
+                     int64_t B, int64_t IN, int64_t OUT, uint32_t *absmax_dX, void *stream) {
+    clear_error();
+    IONN_REQUIRE(dims_ok(B, IN, OUT), IONN_ERR_SHAPE,
+                 "int_linear_dgrad: sizes must be in [0, 2^31): B=%lld IN=%lld OUT=%lld",
+                 (long long)B, (long long)IN, (long long)OUT);
+    if (B == 0 || IN == 0) return IONN_OK;
+    IONN_REQUIRE(dX && (OUT == 0 || (dY && W)), IONN_ERR_ARG, "int_linear_dgrad: NULL tensor");
+    IONN_REQUIRE(aligned(dX, 4) && aligned(absmax_dX, 4), IONN_ERR_ALIGN,
+                 "int_linear_dgrad: dX/absmax must be 4-byte aligned");
+    hipStream_t st = as_stream(stream);
+    if (OUT == 0) return zero_output(dX, B * IN, st, "int_linear_dgrad");
+    const int M = int(B), N = int(IN), K = int(OUT);
+    SrcRowK sa{dY, OUT, M, K, aligned(dY, 16) && OUT % 16 == 0};
+    SrcColK sb{W, IN, N, K, aligned(W, 4) && IN % 4 == 0};
+    Epi ep{dX, IN, M, N,
+           aligned(dX, 16) && IN % 4 == 0 && (relu_act == nullptr || aligned(relu_act, 4)),
+           relu_act, absmax_dX, false};
+    launch_linear(sa, sb, ep, M, N, K, tile_aligned(M, N, K) && sa.vec && sb.vec && ep.vec, st);
+    return check_launch("int_linear_dgrad");
+}
+
+int int_linear_wgrad(const int8_t *dY, const int8_t *X, int32_t *G, int64_t B, int64_t IN,
+                     int64_t OUT, uint32_t *absmax_G, void *stream) {
+    clear_error();
+    IONN_REQUIRE(dims_ok(B, IN, OUT), IONN_ERR_SHAPE,
+                 "int_linear_wgrad: sizes must be in [0, 2^31): B=%lld IN=%lld OUT=%lld",
+                 (long long)B, (long long)IN, (long long)OUT);
+    if (OUT == 0 || IN == 0) return IONN_OK;
+    IONN_REQUIRE(G && (B == 0 || (dY && X)), IONN_ERR_ARG, "int_linear_wgrad: NULL tensor");
+    IONN_REQUIRE(aligned(G, 4) && aligned(absmax_G, 4), IONN_ERR_ALIGN,
+                 "int_linear_wgrad: G/absmax must be 4-byte aligned");
+    hipStream_t st = as_stream(stream);
+    if (B == 0) return zero_output(G, OUT * IN, st, "int_linear_wgrad");
+    const int M = int(OUT), N = int(IN), K = int(B);
+    SrcColK sa{dY, OUT, M, K, aligned(dY, 4) && OUT % 4 == 0};
+    SrcColK sb{X, IN, N, K, aligned(X, 4) && IN % 4 == 0};
+    Epi ep{G, IN, M, N, aligned(G, 16) && IN % 4 == 0, nullptr, absmax_G, false};
+    launch_linear(sa, sb, ep, M, N, K, tile_aligned(M, N, K) && sa.vec && sb.vec && ep.vec, st);
+    return check_launch("int_linear_wgrad");
+}
+
+}  // extern "C"

@@ -1,0 +1,170 @@
+"""Thin Python binding of libionn.so: one function per C entry point, same
+names, same argument order.  Arguments are torch tensors on a ROCm device
+(PyTorch is used only for device memory and streams); this module only
+checks dtypes/shapes and passes raw pointers.  Every computation runs in the
+library's HIP kernels.  Outputs are caller-provided, as in the C ABI.
+"""
+import ctypes
+
+import torch
+
+from ._lib import ConvDesc, check, lib
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _p(t, dtype=None, numel=None, name="tensor"):
+    """Device pointer of a contiguous tensor (None -> NULL)."""
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: must be a device tensor (no CPU path exists)")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name}: needs at least {numel} elements, has {t.numel()}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+i8, i16, i32, u32 = torch.int8, torch.int16, torch.int32, torch.int32  # uint32 scalars held as int32
+
+
+def ionn_fill_u32(dst, value=0, stream=None):
+    check(lib().ionn_fill_u32(_p(dst, torch.int32, name="dst"), dst.numel(), value & 0xFFFFFFFF,
+                              _stream(stream)), "ionn_fill_u32")
+
+
+def ionn_absmax_i32(x, absmax, stream=None):
+    check(lib().ionn_absmax_i32(_p(x, i32, name="x"), x.numel(), _p(absmax, u32, 1, "absmax"),
+                                _stream(stream)), "ionn_absmax_i32")
+
+
+def int_linear_fwd(X, W, Y, absmax_Y=None, stream=None):
+    B, IN = X.shape
+    OUT = W.shape[0]
+    assert tuple(W.shape) == (OUT, IN) and tuple(Y.shape) == (B, OUT), "shape mismatch"
+    check(lib().int_linear_fwd(_p(X, i8, name="X"), _p(W, i8, name="W"), _p(Y, i32, name="Y"),
+                               B, IN, OUT, _p(absmax_Y, u32, 1, "absmax_Y"), _stream(stream)),
+          "int_linear_fwd")
+
+
+def int_linear_dgrad(dY, W, dX, relu_act=None, absmax_dX=None, stream=None):
+    B, OUT = dY.shape
+    IN = W.shape[1]
+    assert tuple(W.shape) == (OUT, IN) and tuple(dX.shape) == (B, IN), "shape mismatch"
+    if relu_act is not None:
+        assert tuple(relu_act.shape) == (B, IN), "relu_act shape mismatch"
+    check(lib().int_linear_dgrad(_p(dY, i8, name="dY"), _p(W, i8, name="W"),
+                                 _p(relu_act, i8, name="relu_act"), _p(dX, i32, name="dX"), B, IN,
+                                 OUT, _p(absmax_dX, u32, 1, "absmax_dX"), _stream(stream)),
+          "int_linear_dgrad")
+
+
+def int_linear_wgrad(dY, X, G, absmax_G=None, stream=None):
+    B, OUT = dY.shape
+    IN = X.shape[1]
+    assert tuple(X.shape) == (B, IN) and tuple(G.shape) == (OUT, IN), "shape mismatch"
+    check(lib().int_linear_wgrad(_p(dY, i8, name="dY"), _p(X, i8, name="X"), _p(G, i32, name="G"),
+                                 B, IN, OUT, _p(absmax_G, u32, 1, "absmax_G"), _stream(stream)),
+          "int_linear_wgrad")
+
+
+def niti_quantize(acc, absmax, target_bits, relu, out, shift_out=None, stream=None):
+    assert acc.numel() == out.numel()
+    check(lib().niti_quantize(_p(acc, i32, name="acc"), acc.numel(), _p(absmax, u32, 1, "absmax"),
+                              int(target_bits), int(bool(relu)), _p(out, i8, name="out"),
+                              _p(shift_out, i32, 1, "shift_out"), _stream(stream)),
+          "niti_quantize")
+
+
+def niti_quantize_update(G, absmax, target_bits, mu_weight, W, shifts_out=None, gq_out=None,
+                         stream=None):
+    assert G.numel() == W.numel()
+    check(lib().niti_quantize_update(_p(G, i32, name="G"), G.numel(), _p(absmax, u32, 1, "absmax"),
+                                     int(target_bits), int(mu_weight), _p(W, i8, name="W"),
+                                     _p(shifts_out, i32, 2, "shifts_out"),
+                                     _p(gq_out, i32, G.numel(), "gq_out"), _stream(stream)),
+          "niti_quantize_update")
+
+
+def int_output_error(out, labels, target_mag, e, absmax_e=None, stream=None):
+    B, C = out.shape
+    assert tuple(e.shape) == (B, C) and labels.numel() == B
+    check(lib().int_output_error(_p(out, i8, name="out"), _p(labels, i32, name="labels"), B, C,
+                                 int(target_mag), _p(e, i32, name="e"),
+                                 _p(absmax_e, u32, 1, "absmax_e"), _stream(stream)),
+          "int_output_error")
+
+
+def conv_desc(N, H, W, Cin, Cout, KH=3, KW=3, stride=1, pad=1, dilation=1, groups=1):
+    return ConvDesc(N, H, W, Cin, Cout, KH, KW, stride, pad, dilation, groups)
+
+
+def int_conv_fwd(X, Wt, Y, desc, absmax_Y=None, stream=None):
+    check(lib().int_conv_fwd(_p(X, i8, name="X"), _p(Wt, i8, name="W"), _p(Y, i32, name="Y"),
+                             ctypes.byref(desc), _p(absmax_Y, u32, 1, "absmax_Y"), _stream(stream)),
+          "int_conv_fwd")
+
+
+def int_conv_dgrad(dY, Wt, dX, desc, absmax_dX=None, stream=None):
+    check(lib().int_conv_dgrad(_p(dY, i8, name="dY"), _p(Wt, i8, name="W"), _p(dX, i32, name="dX"),
+                               ctypes.byref(desc), _p(absmax_dX, u32, 1, "absmax_dX"),
+                               _stream(stream)), "int_conv_dgrad")
+
+
+def int_conv_wgrad(dY, X, G, desc, absmax_G=None, stream=None):
+    check(lib().int_conv_wgrad(_p(dY, i8, name="dY"), _p(X, i8, name="X"), _p(G, i32, name="G"),
+                               ctypes.byref(desc), _p(absmax_G, u32, 1, "absmax_G"),
+                               _stream(stream)), "int_conv_wgrad")
+
+
+def dfp16_workspace_bytes(M, K, N, which):
+    return int(lib().dfp16_workspace_bytes(M, K, N, which))
+
+
+def _dfp(fn, name, A, eA, B, eB, out, eout, M, K, N, chunk, workspace, status_out, stream):
+    check(fn(_p(A, i16, name="A"), _p(eA, i32, 1, "eA"), _p(B, i16, name="B"),
+             _p(eB, i32, 1, "eB"), _p(out, i16, name="out"), _p(eout, i32, 1, "e_out"), M, K, N,
+             int(chunk), _p(workspace, None, name="workspace"),
+             workspace.numel() * workspace.element_size() if workspace is not None else 0,
+             _p(status_out, i32, 1, "status_out"), _stream(stream)), name)
+
+
+def dfp16_gemm_fwd(X, eX, W, eW, Y, eY, workspace, chunk=64, status_out=None, stream=None):
+    M, K = X.shape
+    N = W.shape[0]
+    assert tuple(W.shape) == (N, K) and tuple(Y.shape) == (M, N)
+    _dfp(lib().dfp16_gemm_fwd, "dfp16_gemm_fwd", X, eX, W, eW, Y, eY, M, K, N, chunk, workspace,
+         status_out, stream)
+
+
+def dfp16_gemm_dgrad(dY, edY, W, eW, dX, edX, workspace, chunk=64, status_out=None, stream=None):
+    M, N = dY.shape
+    K = W.shape[1]
+    assert tuple(W.shape) == (N, K) and tuple(dX.shape) == (M, K)
+    _dfp(lib().dfp16_gemm_dgrad, "dfp16_gemm_dgrad", dY, edY, W, eW, dX, edX, M, K, N, chunk,
+         workspace, status_out, stream)
+
+
+def dfp16_gemm_wgrad(dY, edY, X, eX, G, eG, workspace, chunk=64, status_out=None, stream=None):
+    M, N = dY.shape
+    K = X.shape[1]
+    assert tuple(X.shape) == (M, K) and tuple(G.shape) == (N, K)
+    _dfp(lib().dfp16_gemm_wgrad, "dfp16_gemm_wgrad", dY, edY, X, eX, G, eG, M, K, N, chunk,
+         workspace, status_out, stream)
+
+
+def dfp16_gavg(G, eG, eW, gavg_out, stream=None):
+    check(lib().dfp16_gavg(_p(G, i16, name="G"), _p(eG, i32, 1, "eG"), _p(eW, i32, 1, "eW"),
+                           G.numel(), _p(gavg_out, torch.float64, 1, "gavg_out"), _stream(stream)),
+          "dfp16_gavg")

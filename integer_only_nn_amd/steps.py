@@ -1,0 +1,215 @@
+"""Training steps as sequences of libionn calls on one stream.
+
+Nothing here computes: each function allocates device buffers (PyTorch is
+the allocator) and enqueues the library's kernels in the order the method
+gives.  Shift values stay on the device; they are read back only when a
+caller asks for them.
+
+Order of a step ("Integer On-Device Training: Overview", sections 3, 4, 6.2):
+forward (activations requantised with a dynamic NITI shift), the user loss
+writes the output delta, then the backward pass per layer from the last:
+delta propagation with the pre-update weights (ReLU mask, requantised to
+target_bits = 7) and the weight gradient followed by the NITI update.
+"""
+from dataclasses import dataclass, field
+from typing import List, Optional
+
+import torch
+
+from . import ops
+
+TB_WEIGHT = 8
+MU_WEIGHT = 2
+TB_DELTA = 7
+
+
+def _i32(*shape, device):
+    return torch.empty(shape, dtype=torch.int32, device=device)
+
+
+def _i8(*shape, device):
+    return torch.empty(shape, dtype=torch.int8, device=device)
+
+
+# ---------------------------------------------------------------------------
+# Single linear layer.
+# ---------------------------------------------------------------------------
+
+@dataclass
+class LinearStepBuffers:
+    """Device buffers of one linear-layer step (allocated once, reused)."""
+    Y: torch.Tensor
+    dX: torch.Tensor
+    G: torch.Tensor
+    delta: torch.Tensor
+    scal: torch.Tensor    # int32[8]: absmax Y, dX, G | shift delta | s, ws
+    gq: Optional[torch.Tensor] = None
+
+    @staticmethod
+    def make(B, IN, OUT, device, with_gq=False):
+        return LinearStepBuffers(_i32(B, OUT, device=device), _i32(B, IN, device=device),
+                                 _i32(OUT, IN, device=device), _i8(B, IN, device=device),
+                                 torch.zeros(8, dtype=torch.int32, device=device),
+                                 _i32(OUT, IN, device=device) if with_gq else None)
+
+
+def linear_step(X, W, dY, buf: LinearStepBuffers, requant_delta=True, tb_w=TB_WEIGHT,
+                mu=MU_WEIGHT, tb_d=TB_DELTA, stream=None):
+    """fwd (int32 Y + max) -> dgrad (int32 dX + max) [-> delta, 7 bits] ->
+    wgrad (int32 G + max) -> NITI update of W in place."""
+    B, IN = X.shape
+    OUT = W.shape[0]
+    s = buf.scal
+    ops.ionn_fill_u32(s[0:3], 0, stream=stream)
+    ops.int_linear_fwd(X, W, buf.Y, absmax_Y=s[0:1], stream=stream)
+    ops.int_linear_dgrad(dY, W, buf.dX, absmax_dX=s[1:2], stream=stream)
+    if requant_delta:
+        ops.niti_quantize(buf.dX, s[1:2], tb_d, False, buf.delta, shift_out=s[3:4], stream=stream)
+    ops.int_linear_wgrad(dY, X, buf.G, absmax_G=s[2:3], stream=stream)
+    ops.niti_quantize_update(buf.G, s[2:3], tb_w, mu, W, shifts_out=s[4:6], gq_out=buf.gq,
+                             stream=stream)
+
+
+# ---------------------------------------------------------------------------
+# Multi-layer perceptron (all layers trainable).
+# ---------------------------------------------------------------------------
+
+@dataclass
+class MLP:
+    Ws: List[torch.Tensor]
+    relu: List[bool]
+    B: int
+    acts: List[torch.Tensor] = field(default_factory=list)
+    z32: List[torch.Tensor] = field(default_factory=list)
+    d32: List[torch.Tensor] = field(default_factory=list)
+    deltas: List[torch.Tensor] = field(default_factory=list)
+    G: List[torch.Tensor] = field(default_factory=list)
+    e32: Optional[torch.Tensor] = None
+    # per step: [fwd max x L | err max | dgrad max x L | G max x L] (uint32)
+    # and shifts [fwd s x L | err s | dgrad s x L | (s, ws) x L]
+    maxes: Optional[torch.Tensor] = None
+    shifts: Optional[torch.Tensor] = None
+
+    @staticmethod
+    def make(Ws, B, relu=None):
+        L = len(Ws)
+        dev = Ws[0].device
+        m = MLP(list(Ws), relu if relu is not None else [l < L - 1 for l in range(L)], B)
+        sizes = [Ws[0].shape[1]] + [w.shape[0] for w in Ws]
+        m.acts = [None] + [_i8(B, sizes[l + 1], device=dev) for l in range(L)]
+        m.z32 = [_i32(B, sizes[l + 1], device=dev) for l in range(L)]
+        m.d32 = [_i32(B, sizes[l], device=dev) for l in range(L)]
+        m.deltas = [_i8(B, sizes[l], device=dev) for l in range(L + 1)]
+        m.G = [_i32(*w.shape, device=dev) for w in Ws]
+        m.e32 = _i32(B, sizes[-1], device=dev)
+        m.maxes = torch.zeros(3 * L + 1, dtype=torch.int32, device=dev)
+        m.shifts = torch.zeros(4 * L + 1, dtype=torch.int32, device=dev)
+        return m
+
+    def step(self, X, labels, target_mag=127, tb_w=TB_WEIGHT, mu=MU_WEIGHT, tb_a=TB_DELTA,
+             tb_d=TB_DELTA, stream=None):
+        L = len(self.Ws)
+        mx, sh = self.maxes, self.shifts
+        ops.ionn_fill_u32(mx, 0, stream=stream)
+        self.acts[0] = X
+        for l in range(L):
+            ops.int_linear_fwd(self.acts[l], self.Ws[l], self.z32[l], absmax_Y=mx[l:l + 1],
+                               stream=stream)
+            ops.niti_quantize(self.z32[l], mx[l:l + 1], tb_a, self.relu[l], self.acts[l + 1],
+                              shift_out=sh[l:l + 1], stream=stream)
+        ops.int_output_error(self.acts[L], labels, target_mag, self.e32, absmax_e=mx[L:L + 1],
+                             stream=stream)
+        ops.niti_quantize(self.e32, mx[L:L + 1], tb_d, False, self.deltas[L],
+                          shift_out=sh[L:L + 1], stream=stream)
+        for l in range(L - 1, -1, -1):
+            mask = self.acts[l] if (l >= 1 and self.relu[l - 1]) else None
+            dm = mx[L + 1 + l:L + 2 + l]
+            ops.int_linear_dgrad(self.deltas[l + 1], self.Ws[l], self.d32[l], relu_act=mask,
+                                 absmax_dX=dm, stream=stream)
+            ops.niti_quantize(self.d32[l], dm, tb_d, False, self.deltas[l],
+                              shift_out=sh[L + 1 + l:L + 2 + l], stream=stream)
+            gm = mx[2 * L + 1 + l:2 * L + 2 + l]
+            ops.int_linear_wgrad(self.deltas[l + 1], self.acts[l], self.G[l], absmax_G=gm,
+                                 stream=stream)
+            ops.niti_quantize_update(self.G[l], gm, tb_w, mu, self.Ws[l],
+                                     shifts_out=sh[2 * L + 1 + 2 * l:2 * L + 3 + 2 * l],
+                                     stream=stream)
+
+    def shift_record(self):
+        """Host copy of the last step's shifts in the oracle's record layout."""
+        L = len(self.Ws)
+        s = self.shifts.cpu().tolist()
+        return dict(s_fwd=s[:L], s_err=s[L], s_dgrad=s[L + 1:2 * L + 1],
+                    s_upd=[(s[2 * L + 1 + 2 * l], s[2 * L + 2 + 2 * l]) for l in range(L)])
+
+
+# ---------------------------------------------------------------------------
+# 3x3 conv layer.
+# ---------------------------------------------------------------------------
+
+@dataclass
+class ConvStepBuffers:
+    Y: torch.Tensor
+    y8: torch.Tensor
+    dX: torch.Tensor
+    dx8: torch.Tensor
+    G: torch.Tensor
+    scal: torch.Tensor   # [absmax Y, dX, G, s_y, s_dx, s, ws]
+    gq: Optional[torch.Tensor] = None
+
+    @staticmethod
+    def make(N, H, W, Cin, Cout, device, with_gq=False):
+        return ConvStepBuffers(_i32(N, H, W, Cout, device=device), _i8(N, H, W, Cout, device=device),
+                               _i32(N, H, W, Cin, device=device), _i8(N, H, W, Cin, device=device),
+                               _i32(Cout, 3, 3, Cin, device=device),
+                               torch.zeros(8, dtype=torch.int32, device=device),
+                               _i32(Cout, 3, 3, Cin, device=device) if with_gq else None)
+
+
+def conv_step(X, Wt, dY, buf: ConvStepBuffers, tb_a=TB_DELTA, tb_d=TB_DELTA, tb_w=TB_WEIGHT,
+              mu=MU_WEIGHT, stream=None):
+    N, H, W_, Cin = X.shape
+    Cout = Wt.shape[0]
+    d = ops.conv_desc(N, H, W_, Cin, Cout)
+    s = buf.scal
+    ops.ionn_fill_u32(s[0:3], 0, stream=stream)
+    ops.int_conv_fwd(X, Wt, buf.Y, d, absmax_Y=s[0:1], stream=stream)
+    ops.niti_quantize(buf.Y, s[0:1], tb_a, False, buf.y8, shift_out=s[3:4], stream=stream)
+    ops.int_conv_dgrad(dY, Wt, buf.dX, d, absmax_dX=s[1:2], stream=stream)
+    ops.niti_quantize(buf.dX, s[1:2], tb_d, False, buf.dx8, shift_out=s[4:5], stream=stream)
+    ops.int_conv_wgrad(dY, X, buf.G, d, absmax_G=s[2:3], stream=stream)
+    ops.niti_quantize_update(buf.G, s[2:3], tb_w, mu, Wt, shifts_out=s[5:7], gq_out=buf.gq,
+                             stream=stream)
+
+
+# ---------------------------------------------------------------------------
+# DFP-16 layer.
+# ---------------------------------------------------------------------------
+
+@dataclass
+class DfpStepBuffers:
+    Y: torch.Tensor
+    dX: torch.Tensor
+    G: torch.Tensor
+    ws: torch.Tensor          # one workspace, reused by the three contractions
+    exps: torch.Tensor        # int32[8]: eY, edX, eG, status x3
+    gavg: torch.Tensor        # float64[1]
+
+    @staticmethod
+    def make(M, K, N, device):
+        wsb = max(ops.dfp16_workspace_bytes(M, K, N, w) for w in range(3))
+        return DfpStepBuffers(torch.empty(M, N, dtype=torch.int16, device=device),
+                              torch.empty(M, K, dtype=torch.int16, device=device),
+                              torch.empty(N, K, dtype=torch.int16, device=device),
+                              torch.empty(wsb, dtype=torch.uint8, device=device),
+                              torch.zeros(8, dtype=torch.int32, device=device),
+                              torch.zeros(1, dtype=torch.float64, device=device))
+
+
+def dfp16_step(X, eX, W, eW, dY, edY, buf: DfpStepBuffers, stream=None):
+    """eX, eW, edY: device int32[1] exponents."""
+    e = buf.exps
+    ops.dfp16_gemm_fwd(X, eX, W, eW, buf.Y, e[0:1], buf.ws, status_out=e[3:4], stream=stream)
+    ops.dfp16_gemm_dgrad(dY, edY, W, eW, buf.dX, e[1:2], buf.ws, status_out=e[4:5], stream=stream)
+    ops.dfp16_gemm_wgrad(dY, edY, X, eX, buf.G, e[2:3], buf.ws, status_out=e[5:6], stream=stream)
+    ops.dfp16_gavg(buf.G, e[2:3], eW, buf.gavg, stream=stream)

@@ -1,0 +1,102 @@
+"""GPU parity: DFP-16 chunked contractions (int8-split on the matrix cores),
+down-conversion with its exponents, and Gavg against the oracle, bit-exact
+(Gavg as an IEEE double)."""
+import numpy as np
+import pytest
+import torch
+
+import ionn_synth
+import oracle
+from oracle import fast
+from oracle import steps as osteps
+from integer_only_nn_amd import ops, steps
+from gpu_helpers import dev, host, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _exp(v):
+    return torch.tensor([v], dtype=torch.int32, device=dev())
+
+
+def _run(d, M, K, N):
+    buf = steps.DfpStepBuffers.make(M, K, N, dev())
+    steps.dfp16_step(to_dev(d["X"]), _exp(d["eX"]), to_dev(d["W"]), _exp(d["eW"]), to_dev(d["dY"]),
+                     _exp(d["edY"]), buf)
+    return buf
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 1, 1), (3, 64, 5), (17, 40, 9), (128, 128, 128), (200, 256, 136),
+                                   (256, 320, 1024), (1000, 64, 48), (4096, 256, 256)])
+def test_dfp16_step_vs_oracle(M, K, N):
+    say("dfp16", M, K, N)
+    d = ionn_synth.dfp16_gemm(M=M, K=K, N=N, seed=M + K)
+    want = osteps.dfp16_step(d["X"], d["eX"], d["W"], d["eW"], d["dY"], d["edY"])
+    buf = _run(d, M, K, N)
+    np.testing.assert_array_equal(host(buf.Y), want["Y"])
+    np.testing.assert_array_equal(host(buf.dX), want["dX"])
+    np.testing.assert_array_equal(host(buf.G), want["G"])
+    e = host(buf.exps).tolist()
+    assert e[:3] == [want["eY"], want["edX"], want["eG"]] and e[3:6] == [0, 0, 0]
+    assert float(host(buf.gavg)[0]) == want["gavg"]
+
+
+def test_dfp16_golden_chunk_case():
+    c = dict(X=np.zeros((2, 128), np.int16), W=np.zeros((1, 128), np.int16))
+    c["X"][0, :] = 1000
+    c["X"][1, 0] = 7
+    c["W"][0, :64] = 3
+    c["W"][0, 64:] = -1
+    Y = torch.empty(2, 1, dtype=torch.int16, device=dev())
+    eY = _exp(0)
+    ws = torch.empty(ops.dfp16_workspace_bytes(2, 128, 1, 0), dtype=torch.uint8, device=dev())
+    ops.dfp16_gemm_fwd(to_dev(c["X"]), _exp(-10), to_dev(c["W"]), _exp(-12), Y, eY, ws)
+    assert host(Y)[:, 0].tolist() == [32000, 6] and int(host(eY)[0]) == -20
+
+
+def test_dfp16_extreme_mantissas():
+    """Values at +-32767 / -32768 exercise the high-digit range of the split."""
+    M, K, N = 64, 192, 32
+    rng = np.random.default_rng(3)
+    pick = np.array([-32768, -32767, 32767, 32640, 32639, -129, -128, 127, 128, 0, 1, -1], np.int16)
+    X = pick[rng.integers(0, len(pick), (M, K))]
+    W = pick[rng.integers(0, len(pick), (N, K))]
+    dY = pick[rng.integers(0, len(pick), (M, N))]
+    d = dict(X=X, W=W, dY=dY, eX=-30, eW=-30, edY=-30)
+    want = osteps.dfp16_step(X, -30, W, -30, dY, -30)
+    buf = _run(d, M, K, N)
+    np.testing.assert_array_equal(host(buf.Y), want["Y"])
+    np.testing.assert_array_equal(host(buf.dX), want["dX"])
+    np.testing.assert_array_equal(host(buf.G), want["G"])
+
+
+def test_dfp16_exponent_overflow_flagged():
+    X = np.full((16, 64), 30000, np.int16)
+    W = np.full((16, 64), 30000, np.int16)
+    Y = torch.empty(16, 16, dtype=torch.int16, device=dev())
+    eY, st = _exp(0), _exp(0)
+    ws = torch.empty(ops.dfp16_workspace_bytes(16, 64, 16, 0), dtype=torch.uint8, device=dev())
+    ops.dfp16_gemm_fwd(to_dev(X), _exp(120), to_dev(W), _exp(10), Y, eY, ws, status_out=st)
+    assert int(host(st)[0]) == 1
+
+
+def test_dfp16_workload_full():
+    """M=25088, K=256, N=1024: every output, exponent and Gavg against the
+    oracle (float64-product variant of the chunked contraction)."""
+    M, K, N = 25088, 256, 1024
+    say("generating DFP-16 inputs")
+    d = ionn_synth.dfp16_gemm()
+    buf = _run(d, M, K, N)
+    e = host(buf.exps).tolist()
+    assert e[3:6] == [0, 0, 0]
+    say("oracle: forward")
+    Yo, eY, _ = fast.dfp16_fwd(d["X"], d["eX"], d["W"], d["eW"])
+    np.testing.assert_array_equal(host(buf.Y), Yo)
+    say("oracle: dgrad")
+    dXo, edX, _ = fast.dfp16_dgrad(d["dY"], d["edY"], d["W"], d["eW"])
+    np.testing.assert_array_equal(host(buf.dX), dXo)
+    say("oracle: wgrad")
+    Go, eG, _ = fast.dfp16_wgrad(d["dY"], d["edY"], d["X"], d["eX"])
+    np.testing.assert_array_equal(host(buf.G), Go)
+    assert e[:3] == [eY, edX, eG]
+    assert float(host(buf.gavg)[0]) == oracle.gavg(Go, eG, d["eW"])

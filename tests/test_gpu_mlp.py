@@ -1,0 +1,35 @@
+"""GPU parity: the 784-256-128-10 int8 MLP trained for 10 NITI steps (batch
+256) against the oracle; every forward, error, dgrad and update shift of every
+step and the final weights must match bit for bit."""
+import numpy as np
+import pytest
+
+import ionn_synth
+from oracle import steps as osteps
+from integer_only_nn_amd import steps
+from gpu_helpers import dev, host, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("B,sizes,nsteps", [(256, (784, 256, 128, 10), 10), (37, (50, 33, 20, 10), 4),
+                                            (8, (64, 16, 10), 3)])
+def test_mlp_training_matches_oracle(B, sizes, nsteps):
+    d = ionn_synth.mlp(B=B, sizes=sizes, seed=0)
+    Wo, recs = osteps.mlp_train(d["X"], d["labels"], d["Ws"], nsteps)
+    m = steps.MLP.make([to_dev(w) for w in d["Ws"]], B)
+    X, lab = to_dev(d["X"]), to_dev(d["labels"])
+    for t in range(nsteps):
+        m.step(X, lab)
+        got = m.shift_record()
+        want = {k: recs[t][k] for k in ("s_fwd", "s_err", "s_dgrad", "s_upd")}
+        say("step", t, got)
+        assert got == want, f"step {t}"
+        if t == nsteps - 1:
+            for l in range(len(sizes) - 1):
+                np.testing.assert_array_equal(host(m.acts[l + 1]), recs[t]["acts"][l + 1])
+            for l in range(len(sizes)):
+                np.testing.assert_array_equal(host(m.deltas[l]), recs[t]["deltas"][l])
+    for l, w in enumerate(Wo):
+        np.testing.assert_array_equal(host(m.Ws[l]), w)
+    assert any((host(m.Ws[l]) != d["Ws"][l]).any() for l in range(len(Wo)))

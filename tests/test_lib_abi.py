@@ -1,0 +1,100 @@
+"""The C-ABI library loads and exports every function include/ionn.h
+declares, and its host-side argument checks reject bad calls before touching
+the GPU (these calls return without any HIP call, so they run without one)."""
+import ctypes
+
+import pytest
+
+from integer_only_nn_amd import _lib
+
+lib = _lib.lib()
+OK, ARG, SHAPE, RANGE, ALIGN, UNSUP, HIP, WS = range(8)
+
+
+def test_exports_every_header_function():
+    names = _lib.header_functions()
+    assert len(names) >= 19
+    for n in names:
+        assert hasattr(lib, n), f"libionn.so does not export {n}"
+        assert n in _lib.SIGNATURES, f"no ctypes signature for {n}"
+    assert set(_lib.SIGNATURES) == set(names)
+
+
+def test_status_strings_and_version():
+    assert lib.ionn_status_str(0) == b"ok"
+    assert b"workspace" in lib.ionn_status_str(WS)
+    assert lib.ionn_version().startswith(b"ionn")
+
+
+P = ctypes.c_void_p
+FAKE = P(0x1000)        # never dereferenced: every call below fails validation first
+FAKE_ODD = P(0x1001)
+
+
+def _err():
+    return lib.ionn_last_error().decode()
+
+
+def test_linear_validation():
+    assert lib.int_linear_fwd(FAKE, FAKE, FAKE, -1, 4, 4, None, None) == SHAPE
+    assert lib.int_linear_fwd(FAKE, FAKE, FAKE, 1 << 31, 4, 4, None, None) == SHAPE
+    assert lib.int_linear_fwd(None, FAKE, FAKE, 2, 4, 4, None, None) == ARG
+    assert "NULL" in _err()
+    assert lib.int_linear_fwd(FAKE, FAKE, FAKE_ODD, 2, 4, 4, None, None) == ALIGN
+    assert lib.int_linear_dgrad(FAKE, None, None, FAKE, 2, 4, 4, None, None) == ARG
+    assert lib.int_linear_wgrad(FAKE, FAKE, None, 2, 4, 4, None, None) == ARG
+    # empty outputs are a no-op, even with NULL tensors
+    assert lib.int_linear_fwd(None, None, None, 0, 4, 4, None, None) == OK
+    assert lib.int_linear_wgrad(None, None, None, 4, 0, 4, None, None) == OK
+
+
+def test_niti_validation():
+    assert lib.niti_quantize(FAKE, 8, None, 7, 0, FAKE, None, None) == ARG
+    assert lib.niti_quantize(FAKE, 8, FAKE, 0, 0, FAKE, None, None) == RANGE
+    assert lib.niti_quantize(FAKE, 8, FAKE, 32, 0, FAKE, None, None) == RANGE
+    assert lib.niti_quantize(FAKE, 8, FAKE, 7, 2, FAKE, None, None) == ARG
+    assert lib.niti_quantize(FAKE, -1, FAKE, 7, 0, FAKE, None, None) == SHAPE
+    assert lib.niti_quantize_update(FAKE, 8, FAKE, 8, -1, FAKE, None, None, None) == RANGE
+    assert lib.niti_quantize_update(FAKE, 8, FAKE, 8, 32, FAKE, None, None, None) == RANGE
+    assert lib.niti_quantize_update(FAKE_ODD, 8, FAKE, 8, 2, FAKE, None, None, None) == ALIGN
+    assert lib.int_output_error(FAKE, FAKE, 4, 10, 200, FAKE, None, None) == RANGE
+    assert lib.ionn_fill_u32(None, 4, 0, None) == ARG
+    assert lib.ionn_absmax_i32(FAKE, 4, None, None) == ARG
+
+
+def _desc(**kw):
+    d = dict(N=1, H=8, W=8, Cin=16, Cout=16, KH=3, KW=3, stride=1, pad=1, dilation=1, groups=1)
+    d.update(kw)
+    return _lib.ConvDesc(**d)
+
+
+@pytest.mark.parametrize("kw", [dict(KH=5, KW=5), dict(stride=2), dict(pad=0), dict(dilation=2),
+                                dict(groups=2), dict(Cin=8), dict(Cout=24)])
+def test_conv_refuses_unsupported_geometry(kw):
+    d = _desc(**kw)
+    for f in (lib.int_conv_fwd, lib.int_conv_dgrad, lib.int_conv_wgrad):
+        assert f(FAKE, FAKE, FAKE, ctypes.byref(d), None, None) == UNSUP
+    assert "3x3" in _err() or "multiples of 16" in _err()
+
+
+def test_conv_validation():
+    assert lib.int_conv_fwd(FAKE, FAKE, FAKE, None, None, None) == ARG
+    d = _desc(N=-1)
+    assert lib.int_conv_fwd(FAKE, FAKE, FAKE, ctypes.byref(d), None, None) == SHAPE
+    d = _desc()
+    assert lib.int_conv_fwd(FAKE_ODD, FAKE, FAKE, ctypes.byref(d), None, None) == ALIGN
+
+
+def test_dfp16_validation():
+    need = lib.dfp16_workspace_bytes(100, 64, 32, 0)
+    assert need >= 100 * 32 * 4
+    assert lib.dfp16_workspace_bytes(0, 64, 32, 0) == 0
+    assert lib.dfp16_workspace_bytes(4, 4, 4, 3) == 0
+    assert lib.dfp16_workspace_bytes(100, 64, 32, 2) > lib.dfp16_workspace_bytes(100, 64, 32, 0)
+    f = lib.dfp16_gemm_fwd
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 100, 64, 32, 32, FAKE, need, None, None) == RANGE
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 64, 32, 64, FAKE, need, None, None) == SHAPE
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 100, 64, 32, 64, FAKE, need - 1, None, None) == WS
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 100, 64, 32, 64, P(0x1010), need, None, None) == WS
+    assert f(None, FAKE, FAKE, FAKE, FAKE, FAKE, 100, 64, 32, 64, FAKE, need, None, None) == ARG
+    assert lib.dfp16_gavg(FAKE, FAKE, FAKE, 0, FAKE, None) == SHAPE
