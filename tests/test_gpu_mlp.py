@@ -12,9 +12,10 @@ from gpu_helpers import dev, host, say, to_dev
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("B,sizes,nsteps", [(256, (784, 256, 128, 10), 10), (37, (50, 33, 20, 10), 4),
-                                            (8, (64, 16, 10), 3)])
-def test_mlp_training_matches_oracle(B, sizes, nsteps):
+@pytest.mark.parametrize("B,sizes,nsteps,moves", [(256, (784, 256, 128, 10), 10, False),
+                                                  (37, (50, 33, 20, 10), 4, True),
+                                                  (8, (64, 16, 10), 3, True)])
+def test_mlp_training_matches_oracle(B, sizes, nsteps, moves):
     d = ionn_synth.mlp(B=B, sizes=sizes, seed=0)
     Wo, recs = osteps.mlp_train(d["X"], d["labels"], d["Ws"], nsteps)
     m = steps.MLP.make([to_dev(w) for w in d["Ws"]], B)
@@ -32,4 +33,8 @@ def test_mlp_training_matches_oracle(B, sizes, nsteps):
                 np.testing.assert_array_equal(host(m.deltas[l]), recs[t]["deltas"][l])
     for l, w in enumerate(Wo):
         np.testing.assert_array_equal(host(m.Ws[l]), w)
-    assert any((host(m.Ws[l]) != d["Ws"][l]).any() for l in range(len(Wo)))
+    # With the full-size MLP every weight shift is >= 9, so the NITI deltas
+    # round to 0 and the weights stay put (the oracle agrees); the small
+    # MLPs move their weights.
+    moved = any((host(m.Ws[l]) != d["Ws"][l]).any() for l in range(len(Wo)))
+    assert moved == moves
