@@ -37,6 +37,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="also run a read-only and a write-only streaming kernel over 256 MiB "
+                         "(scale for the HBM byte counters)")
     ap.add_argument("--cpu-sample-rows", type=int, default=512,
                     help="token rows of the workload the CPU oracle runs")
     return ap.parse_args()
@@ -225,6 +228,16 @@ def main():
         "ms_per_step_with_delta_requant": round(ms_req, 4),
         "shifts": {"s_delta": shifts[3], "s_weight": shifts[4], "ws": shifts[5]},
     }
+    if args.calibrate:
+        from integer_only_nn_amd import ops
+        cal = torch.ones(64 << 20, dtype=torch.int32, device="cuda:0")   # 256 MiB
+        am = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+        for _ in range(3):
+            ops.ionn_absmax_i32(cal, am)     # reads exactly 256 MiB
+            ops.ionn_fill_u32(cal, 0)        # writes exactly 256 MiB
+        torch.cuda.synchronize()
+        result["calibration"] = {"read_kernel": "absmax_kernel", "write_kernel": "fill_u32_kernel",
+                                 "bytes": 256 << 20}
     if not args.no_secondary:
         log("secondary: conv and DFP-16 steps")
         c_ms = bench_conv(torch, steps_mod, 10)

@@ -1,0 +1,326 @@
+// Fast path of the int8 Linear contractions: 256x256 output tiles, 128-deep
+// K steps, gfx950 direct-to-LDS loads and LDS transpose reads.
+//
+// C[m][n] = sum_k A(m,k) * B(k,n), int32 modulo 2^32.  Each operand is either
+//   K-major: element (r, k) at base[r * ld + k]   (contiguous along k), or
+//   M-major: element (r, k) at base[k * ld + r]   (contiguous along r).
+// Requires M, N multiples of 256, K a multiple of 256, 16-byte aligned bases,
+// ld a multiple of 16 and each operand below 2^31 bytes (the caller checks).
+//
+// Data movement.  Every operand tile goes HBM -> LDS with
+// buffer_load_dwordx4 ... lds (each instruction writes 64 lanes x 16 B = 1 KiB of
+// LDS contiguously and uses no VGPRs for data), double-buffered in two static
+// LDS stages of 64 KiB (A 32 KiB + B 32 KiB).  The loop is unrolled by two so
+// the two stages are distinct arrays: the compiler can then prove that the
+// loads in flight into one stage do not alias the reads of the other and
+// waits for them only where the algorithm needs to.
+//
+// LDS layouts (bank-conflict free for the 16-lane and 8-lane phases of
+// 128-bit reads and the 32-lane phases of 64-bit reads):
+//   K-major tile [256 rows][128 B]: 16-byte chunk c of row r is stored at
+//     chunk position c ^ fK(r & 15), fK(r) = (r >> 1) ^ ((r & 1) << 2).
+//     Fragment read: one ds_read_b128 per 16x64 fragment.
+//   M-major tile [128 k][256 B]: 16-byte chunk c of k-row k is stored at
+//     position c ^ fM(k), fM(k) = (k & 7) | (((k >> 4) & 1) << 3).
+//     Fragment read: two ds_read_b64_tr_b8.  Within each 16-lane group the
+//     instruction returns, to lane j, byte (j mod 8) of the 8-byte rows
+//     addressed by lanes 2b + j/8 (b = 0..7); pointing lane i at
+//     T[k0 + i/2][m0 + 8 (i mod 2)] therefore hands lane j the eight values
+//     T[k0 .. k0+7][m0 + j], which is the matrix-core fragment layout (row =
+//     lane mod 16, consecutive k) without any register shuffling.
+// Both swizzles depend only on lane bits and on compile-time indices, so every
+// address is a uniform (scalar) part plus one of a few per-lane offsets.
+//
+// Compute: 4 wavefronts in a 2x2 grid, 128x128 each (8x8 blocks of 16x16,
+// 256 int32 accumulators per lane held in AGPRs).  Per 64-deep slice a
+// wavefront reads 8 A and 8 B fragments and issues 64
+// v_mfma_i32_16x16x64_i8; both slices' fragment reads of a K step are issued
+// before its 128 MFMAs so the LDS latency of the second slice hides behind
+// the first.
+#pragma once
+
+#include "gemm_core.h"
+
+namespace ionn {
+namespace g256 {
+
+constexpr int BM = 256, BN = 256, BK = 128, NT = 256;
+constexpr int TILE_BYTES = BM * BK;  // 32 KiB per operand per stage
+
+__host__ __device__ constexpr int fK(int r) { return ((r >> 1) ^ ((r & 1) << 2)) & 7; }
+__host__ __device__ constexpr int fM(int k) { return (k & 7) | (((k >> 4) & 1) << 3); }
+
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) v2i lds_v2i;
+
+// One buffer_load_dwordx4 ... lds: every lane fetches 16 bytes at
+// rsrc.base + soff + voff and the wavefront writes them to LDS at m0 + 16 *
+// lane.  Issued through inline asm so the compiler does not track it: the
+// kernel orders these loads itself (each wavefront waits for vmcnt(0), then
+// all meet at s_barrier, before a stage is read), and a compiler that cannot
+// tell the two LDS stages apart would otherwise wait for the prefetch in
+// flight before every LDS read.
+__device__ __forceinline__ void dma16(v4i rsrc, uint32_t voff, uint32_t soff, uint32_t lds_addr) {
+    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, %3 offen lds"
+                 :
+                 : "v"(voff), "s"(rsrc), "s"(lds_addr), "s"(soff)
+                 : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const int8_t *p) {
+    return uint32_t(uintptr_t((__attribute__((address_space(3))) const int8_t *)(p)));
+}
+
+// This wavefront's share (8 of the 32 1-KiB load instructions) of one
+// operand tile.  The operand is one buffer resource (base and byte size in
+// SGPRs: an offset past the end reads zeros instead of faulting); each
+// instruction adds a uniform SGPR offset (row or k-row position of the
+// instruction, plus k0) to a per-lane 32-bit VGPR offset.  The instruction
+// index enters the swizzle only through its parity bits, so two (K-major) or
+// four (M-major) per-lane offsets serve all eight instructions.
+template <bool KMAJOR>
+struct TileSrc {
+    v4i rsrc;
+    int ld;
+    uint32_t wave_off;
+    uint32_t lane_off[4];
+    __device__ __forceinline__ void init(const int8_t *b, int ldv, uint32_t bytes, int r0, int wave,
+                                         int lane) {
+        const uint64_t a = uint64_t(uintptr_t(b));
+        rsrc = v4i{__builtin_amdgcn_readfirstlane(int(uint32_t(a))),
+                   __builtin_amdgcn_readfirstlane(int(uint32_t(a >> 32) & 0xffffu)),  // stride 0
+                   __builtin_amdgcn_readfirstlane(int(bytes)),                        // num_records
+                   0x00020000};                                                       // 32-bit data format
+        ld = ldv;
+        if (KMAJOR) {
+            // instruction q = 8*wave + qq covers rows 8q .. 8q+7; lane -> row 8q + lane/8,
+            // row & 15 = 8*(qq & 1) + lane/8
+            wave_off = uint32_t(r0 + 64 * wave) * uint32_t(ld);
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                const int r15 = 8 * p + (lane >> 3);
+                lane_off[p] = uint32_t((lane >> 3) * ld + 16 * ((lane & 7) ^ fK(r15)));
+            }
+        } else {
+            // instruction q = 8*wave + qq covers k-rows 4q .. 4q+3; lane -> k = 4q + lane/16;
+            // fM(k) depends on (qq & 1) and (qq >> 2) & 1
+            wave_off = uint32_t(32 * wave) * uint32_t(ld) + uint32_t(r0);
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const int qq = (p & 1) | ((p >> 1) << 2);
+                const int k = 4 * qq + (lane >> 4);
+                lane_off[p] = uint32_t((lane >> 4) * ld + 16 * ((lane & 15) ^ fM(k)));
+            }
+        }
+    }
+    __device__ __forceinline__ void issue(int k0, int8_t *dst, int wave) const {
+        const uint32_t d = lds_addr(dst) + uint32_t(wave * 8 * 1024);
+#pragma unroll
+        for (int qq = 0; qq < 8; ++qq) {
+            const uint32_t soff = KMAJOR ? wave_off + uint32_t(8 * qq * ld + k0)
+                                         : wave_off + uint32_t((k0 + 4 * qq) * ld);
+            const uint32_t voff = KMAJOR ? lane_off[qq & 1] : lane_off[(qq & 1) | (((qq >> 2) & 1) << 1)];
+            dma16(rsrc, voff, soff, d + uint32_t(qq * 1024));
+        }
+    }
+};
+
+// Fragment reader for one operand of one wavefront (rows rw .. rw+127 of the
+// tile): fragment i covers rows rw + 16 i .. +15, slice ks covers k
+// 64 ks .. 64 ks + 63 (lane group lane/16 takes 16 of them).
+template <bool KMAJOR>
+struct FragSrc {
+    uint32_t off[2];
+    __device__ __forceinline__ void init(int rw, int lane) {
+        if (KMAJOR) {
+            // row = rw + 16 i + (lane & 15); (rw + 16 i) & 15 == 0
+            const int r15 = lane & 15;
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+                off[ks] = uint32_t((rw + r15) * BK + 16 * ((ks * 4 + (lane >> 4)) ^ fK(r15)));
+        } else {
+            // k = 64 ks + 16 g + 8 h + i/2 (g = lane/16, i = lane & 15), so
+            // fM(k) = i/2 | (g & 1) << 3.  Fragment fi sits in chunk
+            // c = rw/16 + fi with rw/16 in {0, 8}, hence position
+            // c ^ fM(k) = (rw/16 ^ (g & 1) << 3) | (fi ^ i/2).
+            const int g = lane >> 4, i = lane & 15;
+            const int hi = (rw >> 4) ^ ((g & 1) << 3);
+            off[0] = uint32_t((16 * g + (i >> 1)) * BM + 16 * hi + 8 * (i & 1));
+            off[1] = uint32_t(16 * (i >> 1));  // 16 * (i/2), XORed with 16 * fi
+        }
+    }
+    __device__ __forceinline__ v4i read(const int8_t *tile, int fi, int ks) const {
+        if (KMAJOR) {
+            return *reinterpret_cast<const v4i *>(tile + off[ks] + fi * 16 * BK);
+        } else {
+            const uint32_t o = off[0] + ((uint32_t(16 * fi)) ^ off[1]);
+            v4i out;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int8_t *p = tile + o + (64 * ks + 8 * h) * BM;
+                const v2i v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i *)(p));
+                out[2 * h] = v.x;
+                out[2 * h + 1] = v.y;
+            }
+            return out;
+        }
+    }
+};
+
+// One 16-fragment set: A fragments 0..7 then B fragments 0..7 of one slice.
+template <bool A_KM, bool B_KM>
+struct Frags {
+    v4i a[8], b[8];
+    __device__ __forceinline__ void read(int idx, const int8_t *As, const int8_t *Bs,
+                                         const FragSrc<A_KM> &fa, const FragSrc<B_KM> &fb, int ks) {
+        if (idx < 8) a[idx] = fa.read(As, idx, ks);
+        else b[idx - 8] = fb.read(Bs, idx - 8, ks);
+    }
+};
+
+#define IONN_SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
+
+// The 8 MFMAs of column block j of one slice.
+template <bool A_KM, bool B_KM>
+__device__ __forceinline__ void mfma_col(const Frags<A_KM, B_KM> &f, int j, v4i (&acc)[8][8]) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
+}
+
+template <bool A_KM, bool B_KM>
+__global__ __launch_bounds__(NT, 1) void gemm256_kernel(const int8_t *__restrict__ A, int64_t lda,
+                                                        const int8_t *__restrict__ B, int64_t ldb,
+                                                        uint32_t a_bytes, uint32_t b_bytes,
+                                                        gemm::Epi ep, int M, int N, int K) {
+    __shared__ __attribute__((aligned(1024))) int8_t sA0[TILE_BYTES];
+    __shared__ __attribute__((aligned(1024))) int8_t sB0[TILE_BYTES];
+    __shared__ __attribute__((aligned(1024))) int8_t sA1[TILE_BYTES];
+    __shared__ __attribute__((aligned(1024))) int8_t sB1[TILE_BYTES];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    int tm, tn;
+    gemm::tile_coords(blockIdx.x, M / BM, N / BN, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+
+    TileSrc<A_KM> ta;
+    TileSrc<B_KM> tb;
+    ta.init(A, int(lda), a_bytes, m0, wave, lane);
+    tb.init(B, int(ldb), b_bytes, n0, wave, lane);
+    FragSrc<A_KM> fa;
+    FragSrc<B_KM> fb;
+    fa.init(wm * 128, lane);
+    fb.init(wn * 128, lane);
+
+    v4i acc[8][8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = v4i{0, 0, 0, 0};
+
+    Frags<A_KM, B_KM> X, Y;  // slice 0 / slice 1 fragments of the current step
+    const int nk = K / BK;   // even (checked by the caller)
+
+    // Prologue: step 0 -> stage 0, wait, step 1 -> stage 1, slice-0 fragments of step 0.
+    ta.issue(0, sA0, wave);
+    tb.issue(0, sB0, wave);
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    ta.issue(BK, sA1, wave);
+    tb.issue(BK, sB1, wave);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) X.read(r, sA0, sB0, fa, fb, 0);
+
+    // One K step held in stage (Ac, Bc); the next step's data sits in the
+    // other stage (An, Bn) once the barrier is passed.  Order:
+    //   slice-0 MFMAs, two slice-1 fragment reads after each 8 of them;
+    //   slice-1 MFMAs of columns 0..5;
+    //   wait for this wave's loads and LDS reads, barrier (every wave's loads of
+    //   the next step are in; nobody reads this stage any more);
+    //   loads of step + 2 into this stage, and the next step's slice-0
+    //   fragment reads, spread over the last 16 slice-1 MFMAs.
+    auto step = [&](const int8_t *Ac, const int8_t *Bc, const int8_t *An, const int8_t *Bn,
+                    int8_t *Adst, int8_t *Bdst, int kt) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            mfma_col(X, j, acc);
+            IONN_SCHED_FENCE();
+            Y.read(2 * j, Ac, Bc, fa, fb, 1);
+            Y.read(2 * j + 1, Ac, Bc, fa, fb, 1);
+            IONN_SCHED_FENCE();
+        }
+#pragma unroll
+        for (int j = 0; j < 6; ++j) {
+            mfma_col(Y, j, acc);
+            IONN_SCHED_FENCE();
+        }
+        __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+        __builtin_amdgcn_s_barrier();
+        IONN_SCHED_FENCE();
+        if (kt + 2 < nk) {
+            ta.issue((kt + 2) * BK, Adst, wave);
+            tb.issue((kt + 2) * BK, Bdst, wave);
+        }
+        IONN_SCHED_FENCE();
+        if (kt + 1 < nk) {
+#pragma unroll
+            for (int r = 0; r < 8; ++r) X.read(r, An, Bn, fa, fb, 0);
+        }
+        IONN_SCHED_FENCE();
+        mfma_col(Y, 6, acc);
+        IONN_SCHED_FENCE();
+        if (kt + 1 < nk) {
+#pragma unroll
+            for (int r = 8; r < 16; ++r) X.read(r, An, Bn, fa, fb, 0);
+        }
+        IONN_SCHED_FENCE();
+        mfma_col(Y, 7, acc);
+        IONN_SCHED_FENCE();
+    };
+
+    for (int kt = 0; kt < nk; kt += 2) {
+        step(sA0, sB0, sA1, sB1, sA0, sB0, kt);
+        step(sA1, sB1, sA0, sB0, sA1, sB1, kt + 1);
+    }
+
+    // ---- epilogue: lane holds C[m][n .. n+3], m = .. + lane % 16 ----
+    uint32_t amax = 0;
+    const int em = lane & 15, en = (lane >> 4) * 4;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int m = m0 + wm * 128 + i * 16 + em;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int n = n0 + wn * 128 + j * 16 + en;
+            v4i v = acc[i][j];
+            int32_t *cp = ep.C + int64_t(m) * ep.ldc + n;
+            if (ep.act) {
+                const uint32_t a = *reinterpret_cast<const uint32_t *>(ep.act + int64_t(m) * ep.ldc + n);
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    if (int8_t(uint8_t(a >> (8 * c))) <= 0) v[c] = 0;
+            }
+            *reinterpret_cast<v4i *>(cp) = v;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) amax = max(amax, abs_u32(v[c]));
+        }
+    }
+    if (ep.absmax) {
+        amax = wave_max_u32(amax);
+        if (lane == 0 && amax != 0) atomicMax(ep.absmax, amax);
+    }
+}
+
+template <bool A_KM, bool B_KM>
+void launch(const int8_t *A, int64_t lda, const int8_t *B, int64_t ldb, const gemm::Epi &ep, int M,
+            int N, int K, hipStream_t st) {
+    const uint32_t a_bytes = uint32_t((A_KM ? int64_t(M) : int64_t(K)) * lda);
+    const uint32_t b_bytes = uint32_t((B_KM ? int64_t(N) : int64_t(K)) * ldb);
+    gemm256_kernel<A_KM, B_KM><<<dim3((M / BM) * (N / BN)), dim3(NT), 0, st>>>(
+        A, lda, B, ldb, a_bytes, b_bytes, ep, M, N, K);
+}
+
+}  // namespace g256
+}  // namespace ionn

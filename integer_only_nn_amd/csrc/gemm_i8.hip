@@ -10,7 +10,7 @@
 // each: per 64-deep step a workgroup stages 32 KiB in LDS and issues 256
 // MFMAs); anything else runs bounds-checked 64x64 tiles.  The epilogue fuses
 // dgrad's ReLU mask and the max-abs that feeds the NITI shift.
-#include "gemm_core.h"
+#include "gemm256.h"
 
 namespace ionn {
 namespace {
@@ -48,6 +48,18 @@ bool dims_ok(int64_t B, int64_t IN, int64_t OUT) {
 
 bool tile_aligned(int M, int N, int K) { return M % 256 == 0 && N % 256 == 0 && K % 64 == 0; }
 
+// The 256x256x128 direct-to-LDS path: whole tiles (an even number of 128-deep
+// K steps), operands below 2^31 bytes (32-bit buffer offsets), 16-byte aligned operands
+// with row pitches that are multiples of 16, 16-byte aligned output rows.
+bool fast256(int M, int N, int K, const void *A, int64_t lda, const void *B, int64_t ldb,
+             const Epi &ep) {
+    return M % 256 == 0 && N % 256 == 0 && K % 256 == 0 && aligned(A, 16) && aligned(B, 16) &&
+           lda % 16 == 0 && ldb % 16 == 0 && aligned(ep.C, 16) && ep.ldc % 4 == 0 &&
+           (ep.act == nullptr || aligned(ep.act, 4)) && int64_t(M) * lda < (int64_t(1) << 31) &&
+           int64_t(K) * lda < (int64_t(1) << 31) && int64_t(N) * ldb < (int64_t(1) << 31) &&
+           int64_t(K) * ldb < (int64_t(1) << 31);
+}
+
 }  // namespace
 }  // namespace ionn
 
@@ -72,6 +84,10 @@ int int_linear_fwd(const int8_t *X, const int8_t *W, int32_t *Y, int64_t B, int6
     SrcRowK sa{X, IN, M, K, aligned(X, 16) && IN % 16 == 0};
     SrcRowK sb{W, IN, N, K, aligned(W, 16) && IN % 16 == 0};
     Epi ep{Y, OUT, M, N, aligned(Y, 16) && OUT % 4 == 0, nullptr, absmax_Y, false};
+    if (fast256(M, N, K, X, IN, W, IN, ep)) {
+        g256::launch<true, true>(X, IN, W, IN, ep, M, N, K, st);
+        return check_launch("int_linear_fwd");
+    }
     launch_linear(sa, sb, ep, M, N, K, tile_aligned(M, N, K) && sa.vec && sb.vec && ep.vec, st);
     return check_launch("int_linear_fwd");
 }
@@ -94,6 +110,10 @@ int int_linear_dgrad(const int8_t *dY, const int8_t *W, const int8_t *relu_act, 
     Epi ep{dX, IN, M, N,
            aligned(dX, 16) && IN % 4 == 0 && (relu_act == nullptr || aligned(relu_act, 4)),
            relu_act, absmax_dX, false};
+    if (fast256(M, N, K, dY, OUT, W, IN, ep)) {
+        g256::launch<true, false>(dY, OUT, W, IN, ep, M, N, K, st);
+        return check_launch("int_linear_dgrad");
+    }
     launch_linear(sa, sb, ep, M, N, K, tile_aligned(M, N, K) && sa.vec && sb.vec && ep.vec, st);
     return check_launch("int_linear_dgrad");
 }
@@ -114,6 +134,10 @@ int int_linear_wgrad(const int8_t *dY, const int8_t *X, int32_t *G, int64_t B, i
     SrcColK sa{dY, OUT, M, K, aligned(dY, 4) && OUT % 4 == 0};
     SrcColK sb{X, IN, N, K, aligned(X, 4) && IN % 4 == 0};
     Epi ep{G, IN, M, N, aligned(G, 16) && IN % 4 == 0, nullptr, absmax_G, false};
+    if (fast256(M, N, K, dY, OUT, X, IN, ep)) {
+        g256::launch<false, false>(dY, OUT, X, IN, ep, M, N, K, st);
+        return check_launch("int_linear_wgrad");
+    }
     launch_linear(sa, sb, ep, M, N, K, tile_aligned(M, N, K) && sa.vec && sb.vec && ep.vec, st);
     return check_launch("int_linear_wgrad");
 }
