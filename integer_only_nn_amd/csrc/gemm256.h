@@ -21,7 +21,7 @@
 //     chunk position c ^ fK(r & 15), fK(r) = (r >> 1) ^ ((r & 1) << 2).
 //     Fragment read: one ds_read_b128 per 16x64 fragment.
 //   M-major tile [128 k][256 B]: 16-byte chunk c of k-row k is stored at
-//     position c ^ fM(k), fM(k) = (k & 7) | (((k >> 4) & 1) << 3).
+//     position c ^ fM(k), fM(k) = (k & 7) | ((k & 1) << 3).
 //     Fragment read: two ds_read_b64_tr_b8.  Within each 16-lane group the
 //     instruction returns, to lane j, byte (j mod 8) of the 8-byte rows
 //     addressed by lanes 2b + j/8 (b = 0..7); pointing lane i at
@@ -31,12 +31,15 @@
 // Both swizzles depend only on lane bits and on compile-time indices, so every
 // address is a uniform (scalar) part plus one of a few per-lane offsets.
 //
-// Compute: 4 wavefronts in a 2x2 grid, 128x128 each (8x8 blocks of 16x16,
-// 256 int32 accumulators per lane held in AGPRs).  Per 64-deep slice a
-// wavefront reads 8 A and 8 B fragments and issues 64
-// v_mfma_i32_16x16x64_i8; both slices' fragment reads of a K step are issued
-// before its 128 MFMAs so the LDS latency of the second slice hides behind
-// the first.
+// Compute: 4 wavefronts in a 2x2 grid, 128x128 each: 4x4 blocks of 32x32 on
+// v_mfma_i32_32x32x32_i8 (256 int32 accumulators per lane, in AGPRs).  On
+// gfx950 this shape runs int8 at full rate; the 16x16x64 shape measures at
+// half of it.  A 128-deep K step is 4 slices of 32; per slice a wavefront
+// reads 4 A and 4 B fragments (16 bytes per lane each: row = lane % 32,
+// k = 16 (lane / 32) .. +15) and issues 16 MFMAs.  The next slice's fragments
+// are read while the current slice's MFMAs run; at the last slice the stage
+// barrier, the next loads and the next step's first fragments are tucked in
+// before its last MFMAs.
 #pragma once
 
 #include "gemm_core.h"
@@ -48,7 +51,7 @@ constexpr int BM = 256, BN = 256, BK = 128, NT = 256;
 constexpr int TILE_BYTES = BM * BK;  // 32 KiB per operand per stage
 
 __host__ __device__ constexpr int fK(int r) { return ((r >> 1) ^ ((r & 1) << 2)) & 7; }
-__host__ __device__ constexpr int fM(int k) { return (k & 7) | (((k >> 4) & 1) << 3); }
+__host__ __device__ constexpr int fM(int k) { return (k & 7) | ((k & 1) << 3); }
 
 typedef int v2i __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) v2i lds_v2i;
@@ -76,14 +79,14 @@ __device__ __forceinline__ uint32_t lds_addr(const int8_t *p) {
 // SGPRs: an offset past the end reads zeros instead of faulting); each
 // instruction adds a uniform SGPR offset (row or k-row position of the
 // instruction, plus k0) to a per-lane 32-bit VGPR offset.  The instruction
-// index enters the swizzle only through its parity bits, so two (K-major) or
-// four (M-major) per-lane offsets serve all eight instructions.
+// index enters the swizzle only through its parity, so two per-lane offsets
+// serve all eight instructions.
 template <bool KMAJOR>
 struct TileSrc {
     v4i rsrc;
     int ld;
     uint32_t wave_off;
-    uint32_t lane_off[4];
+    uint32_t lane_off[2];
     __device__ __forceinline__ void init(const int8_t *b, int ldv, uint32_t bytes, int r0, int wave,
                                          int lane) {
         const uint64_t a = uint64_t(uintptr_t(b));
@@ -103,12 +106,11 @@ struct TileSrc {
             }
         } else {
             // instruction q = 8*wave + qq covers k-rows 4q .. 4q+3; lane -> k = 4q + lane/16;
-            // fM(k) depends on (qq & 1) and (qq >> 2) & 1
+            // k & 7 = 4*(qq & 1) + lane/16, so fM(k) depends on qq & 1 only
             wave_off = uint32_t(32 * wave) * uint32_t(ld) + uint32_t(r0);
 #pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                const int qq = (p & 1) | ((p >> 1) << 2);
-                const int k = 4 * qq + (lane >> 4);
+            for (int p = 0; p < 2; ++p) {
+                const int k = 4 * p + (lane >> 4);
                 lane_off[p] = uint32_t((lane >> 4) * ld + 16 * ((lane & 15) ^ fM(k)));
             }
         }
@@ -119,45 +121,54 @@ struct TileSrc {
         for (int qq = 0; qq < 8; ++qq) {
             const uint32_t soff = KMAJOR ? wave_off + uint32_t(8 * qq * ld + k0)
                                          : wave_off + uint32_t((k0 + 4 * qq) * ld);
-            const uint32_t voff = KMAJOR ? lane_off[qq & 1] : lane_off[(qq & 1) | (((qq >> 2) & 1) << 1)];
+            const uint32_t voff = lane_off[qq & 1];
             dma16(rsrc, voff, soff, d + uint32_t(qq * 1024));
         }
     }
 };
 
 // Fragment reader for one operand of one wavefront (rows rw .. rw+127 of the
-// tile): fragment i covers rows rw + 16 i .. +15, slice ks covers k
-// 64 ks .. 64 ks + 63 (lane group lane/16 takes 16 of them).
+// tile): fragment fi covers rows rw + 32 fi .. +31, slice sl covers k
+// 32 sl .. 32 sl + 31; lane takes row lane % 32 and k 16 (lane / 32) .. +15.
 template <bool KMAJOR>
 struct FragSrc {
     uint32_t off[2];
     __device__ __forceinline__ void init(int rw, int lane) {
         if (KMAJOR) {
-            // row = rw + 16 i + (lane & 15); (rw + 16 i) & 15 == 0
+            // row = rw + 32 fi + (lane & 31), row & 15 = lane & 15;
+            // chunk = 2 sl + lane/32, position chunk ^ fK(row & 15).
+            // off[p]: slices with (sl & 1) == p; (2 sl) ^ f keeps bit 2 of 2 sl
+            // separate only through the XOR, so both parities are precomputed
+            // and slices 2, 3 add 4 chunks (64 bytes) XOR-free: chunk bits
+            // 0-1 come from (lane/32, sl & 1), bit 2 from sl >> 1.
             const int r15 = lane & 15;
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
-                off[ks] = uint32_t((rw + r15) * BK + 16 * ((ks * 4 + (lane >> 4)) ^ fK(r15)));
+            for (int p = 0; p < 2; ++p)
+                off[p] = uint32_t((rw + (lane & 31)) * BK + 16 * ((2 * p + (lane >> 5)) ^ fK(r15)));
         } else {
-            // k = 64 ks + 16 g + 8 h + i/2 (g = lane/16, i = lane & 15), so
-            // fM(k) = i/2 | (g & 1) << 3.  Fragment fi sits in chunk
-            // c = rw/16 + fi with rw/16 in {0, 8}, hence position
-            // c ^ fM(k) = (rw/16 ^ (g & 1) << 3) | (fi ^ i/2).
+            // 16-lane group g = lane / 16 reads m-chunk 2 fi + (g & 1) (+ rw/16)
+            // at k = 32 sl + 16 (g >> 1) + 8 h + i/2, i = lane & 15; k & 7 = i/2,
+            // so fM(k) = i/2 | (i/2 & 1) << 3 per lane and the position is
+            // (rw/16 + (g & 1) ^ fM) ^ 2 fi.
             const int g = lane >> 4, i = lane & 15;
-            const int hi = (rw >> 4) ^ ((g & 1) << 3);
-            off[0] = uint32_t((16 * g + (i >> 1)) * BM + 16 * hi + 8 * (i & 1));
-            off[1] = uint32_t(16 * (i >> 1));  // 16 * (i/2), XORed with 16 * fi
+            const int f = fM(i >> 1);
+            const int base_c = ((rw >> 4) + (g & 1)) ^ f;
+            off[0] = uint32_t((16 * (g >> 1) + (i >> 1)) * BM + 8 * (i & 1));
+            off[1] = uint32_t(16 * base_c);  // XORed with 32 * fi
         }
     }
-    __device__ __forceinline__ v4i read(const int8_t *tile, int fi, int ks) const {
+    __device__ __forceinline__ v4i read(const int8_t *tile, int fi, int sl) const {
         if (KMAJOR) {
-            return *reinterpret_cast<const v4i *>(tile + off[ks] + fi * 16 * BK);
+            // positions of slices 2, 3 = positions of slices 0, 1 with bit 2
+            // flipped: fK only uses bits 0-2, so flip via XOR on the offset
+            const uint32_t o = off[sl & 1] ^ uint32_t((sl >> 1) * 64);
+            return *reinterpret_cast<const v4i *>(tile + o + fi * 32 * BK);
         } else {
-            const uint32_t o = off[0] + ((uint32_t(16 * fi)) ^ off[1]);
+            const uint32_t o = off[0] + (off[1] ^ uint32_t(32 * fi));
             v4i out;
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-                const int8_t *p = tile + o + (64 * ks + 8 * h) * BM;
+                const int8_t *p = tile + o + (32 * sl + 8 * h) * BM;
                 const v2i v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i *)(p));
                 out[2 * h] = v.x;
                 out[2 * h + 1] = v.y;
@@ -167,25 +178,27 @@ struct FragSrc {
     }
 };
 
-// One 16-fragment set: A fragments 0..7 then B fragments 0..7 of one slice.
+// Fragments of one 32-deep slice: A blocks 0..3 then B blocks 0..3.
 template <bool A_KM, bool B_KM>
 struct Frags {
-    v4i a[8], b[8];
+    v4i a[4], b[4];
     __device__ __forceinline__ void read(int idx, const int8_t *As, const int8_t *Bs,
-                                         const FragSrc<A_KM> &fa, const FragSrc<B_KM> &fb, int ks) {
-        if (idx < 8) a[idx] = fa.read(As, idx, ks);
-        else b[idx - 8] = fb.read(Bs, idx - 8, ks);
+                                         const FragSrc<A_KM> &fa, const FragSrc<B_KM> &fb, int sl) {
+        if (idx < 4) a[idx] = fa.read(As, idx, sl);
+        else b[idx - 4] = fb.read(Bs, idx - 4, sl);
     }
 };
 
 #define IONN_SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
 
-// The 8 MFMAs of column block j of one slice.
+// The 4 MFMAs of column block j of one slice.  The B fragment goes first, so
+// the 32x32 result has n along its rows: lane holds m = lane % 32 and, for
+// q = 0..3, n = 8 q + 4 (lane / 32) .. +3.
 template <bool A_KM, bool B_KM>
-__device__ __forceinline__ void mfma_col(const Frags<A_KM, B_KM> &f, int j, v4i (&acc)[8][8]) {
+__device__ __forceinline__ void mfma_col(const Frags<A_KM, B_KM> &f, int j, v16i (&acc)[4][4]) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-        acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
+    for (int i = 0; i < 4; ++i)
+        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
 }
 
 template <bool A_KM, bool B_KM>
@@ -214,13 +227,13 @@ __global__ __launch_bounds__(NT, 1) void gemm256_kernel(const int8_t *__restrict
     fa.init(wm * 128, lane);
     fb.init(wn * 128, lane);
 
-    v4i acc[8][8];
+    v16i acc[4][4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = v4i{0, 0, 0, 0};
+        for (int j = 0; j < 4; ++j) acc[i][j] = v16i{};
 
-    Frags<A_KM, B_KM> X, Y;  // slice 0 / slice 1 fragments of the current step
+    Frags<A_KM, B_KM> F[2];  // fragments of the current / next slice
     const int nk = K / BK;   // even (checked by the caller)
 
     // Prologue: step 0 -> stage 0, wait, step 1 -> stage 1, slice-0 fragments of step 0.
@@ -231,31 +244,32 @@ __global__ __launch_bounds__(NT, 1) void gemm256_kernel(const int8_t *__restrict
     ta.issue(BK, sA1, wave);
     tb.issue(BK, sB1, wave);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) X.read(r, sA0, sB0, fa, fb, 0);
+    for (int r = 0; r < 8; ++r) F[0].read(r, sA0, sB0, fa, fb, 0);
 
     // One K step held in stage (Ac, Bc); the next step's data sits in the
-    // other stage (An, Bn) once the barrier is passed.  Order:
-    //   slice-0 MFMAs, two slice-1 fragment reads after each 8 of them;
-    //   slice-1 MFMAs of columns 0..5;
-    //   wait for this wave's loads and LDS reads, barrier (every wave's loads of
-    //   the next step are in; nobody reads this stage any more);
-    //   loads of step + 2 into this stage, and the next step's slice-0
-    //   fragment reads, spread over the last 16 slice-1 MFMAs.
+    // other stage (An, Bn) once the barrier is passed.  Slices 0..2: the
+    // slice's 16 MFMAs with the next slice's 8 fragment reads after each
+    // column.  Slice 3: columns 0, 1; then wait for this wave's loads and LDS
+    // reads and meet at the barrier (every wave's loads of the next step are
+    // in; nobody reads this stage any more); loads of step + 2 into this
+    // stage; the next step's slice-0 reads spread over columns 2, 3.
     auto step = [&](const int8_t *Ac, const int8_t *Bc, const int8_t *An, const int8_t *Bn,
                     int8_t *Adst, int8_t *Bdst, int kt) __attribute__((always_inline)) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            mfma_col(X, j, acc);
-            IONN_SCHED_FENCE();
-            Y.read(2 * j, Ac, Bc, fa, fb, 1);
-            Y.read(2 * j + 1, Ac, Bc, fa, fb, 1);
-            IONN_SCHED_FENCE();
-        }
+        for (int sl = 0; sl < 3; ++sl) {
 #pragma unroll
-        for (int j = 0; j < 6; ++j) {
-            mfma_col(Y, j, acc);
-            IONN_SCHED_FENCE();
+            for (int j = 0; j < 4; ++j) {
+                mfma_col(F[sl & 1], j, acc);
+                IONN_SCHED_FENCE();
+                F[(sl + 1) & 1].read(2 * j, Ac, Bc, fa, fb, sl + 1);
+                F[(sl + 1) & 1].read(2 * j + 1, Ac, Bc, fa, fb, sl + 1);
+                IONN_SCHED_FENCE();
+            }
         }
+        mfma_col(F[1], 0, acc);
+        IONN_SCHED_FENCE();
+        mfma_col(F[1], 1, acc);
+        IONN_SCHED_FENCE();
         __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
         __builtin_amdgcn_s_barrier();
         IONN_SCHED_FENCE();
@@ -266,17 +280,17 @@ __global__ __launch_bounds__(NT, 1) void gemm256_kernel(const int8_t *__restrict
         IONN_SCHED_FENCE();
         if (kt + 1 < nk) {
 #pragma unroll
-            for (int r = 0; r < 8; ++r) X.read(r, An, Bn, fa, fb, 0);
+            for (int r = 0; r < 4; ++r) F[0].read(r, An, Bn, fa, fb, 0);
         }
         IONN_SCHED_FENCE();
-        mfma_col(Y, 6, acc);
+        mfma_col(F[1], 2, acc);
         IONN_SCHED_FENCE();
         if (kt + 1 < nk) {
 #pragma unroll
-            for (int r = 8; r < 16; ++r) X.read(r, An, Bn, fa, fb, 0);
+            for (int r = 4; r < 8; ++r) F[0].read(r, An, Bn, fa, fb, 0);
         }
         IONN_SCHED_FENCE();
-        mfma_col(Y, 7, acc);
+        mfma_col(F[1], 3, acc);
         IONN_SCHED_FENCE();
     };
 
@@ -285,26 +299,30 @@ __global__ __launch_bounds__(NT, 1) void gemm256_kernel(const int8_t *__restrict
         step(sA1, sB1, sA0, sB0, sA1, sB1, kt + 1);
     }
 
-    // ---- epilogue: lane holds C[m][n .. n+3], m = .. + lane % 16 ----
+    // ---- epilogue: lane holds C[m][n .. n+3] for m = .. + lane % 32 and
+    // n = .. + 8 q + 4 (lane / 32), q = 0..3 ----
     uint32_t amax = 0;
-    const int em = lane & 15, en = (lane >> 4) * 4;
+    const int em = lane & 31, en = (lane >> 5) * 4;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int m = m0 + wm * 128 + i * 16 + em;
+    for (int i = 0; i < 4; ++i) {
+        const int m = m0 + wm * 128 + i * 32 + em;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int n = n0 + wn * 128 + j * 16 + en;
-            v4i v = acc[i][j];
-            int32_t *cp = ep.C + int64_t(m) * ep.ldc + n;
-            if (ep.act) {
-                const uint32_t a = *reinterpret_cast<const uint32_t *>(ep.act + int64_t(m) * ep.ldc + n);
+        for (int j = 0; j < 4; ++j) {
 #pragma unroll
-                for (int c = 0; c < 4; ++c)
-                    if (int8_t(uint8_t(a >> (8 * c))) <= 0) v[c] = 0;
+            for (int q = 0; q < 4; ++q) {
+                const int n = n0 + wn * 128 + j * 32 + 8 * q + en;
+                v4i v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+                int32_t *cp = ep.C + int64_t(m) * ep.ldc + n;
+                if (ep.act) {
+                    const uint32_t a = *reinterpret_cast<const uint32_t *>(ep.act + int64_t(m) * ep.ldc + n);
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        if (int8_t(uint8_t(a >> (8 * c))) <= 0) v[c] = 0;
+                }
+                *reinterpret_cast<v4i *>(cp) = v;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) amax = max(amax, abs_u32(v[c]));
             }
-            *reinterpret_cast<v4i *>(cp) = v;
-#pragma unroll
-            for (int c = 0; c < 4; ++c) amax = max(amax, abs_u32(v[c]));
         }
     }
     if (ep.absmax) {

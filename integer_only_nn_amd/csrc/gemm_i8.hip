@@ -6,10 +6,11 @@
 //   dgrad dX = dY W   : A = dY [M=B][K=OUT] (K-major), B = W [K=OUT][N=IN] (N-major)
 //   wgrad G  = dY^T X : A = dY [K=B][M=OUT] (M-major), B = X [K=B][N=IN]   (N-major)
 //
-// Large tile-aligned problems run 256x256x64 tiles (4 wavefronts, 128x128
-// each: per 64-deep step a workgroup stages 32 KiB in LDS and issues 256
-// MFMAs); anything else runs bounds-checked 64x64 tiles.  The epilogue fuses
-// dgrad's ReLU mask and the max-abs that feeds the NITI shift.
+// Tile-aligned problems take the 256x256x128 direct-to-LDS kernel of
+// gemm256.h (v_mfma_i32_32x32x32_i8); other large problems run 256x256x64
+// bounds-checked tiles of the generic mainloop (gemm_core.h), small ones
+// 64x64 tiles.  The epilogue fuses dgrad's ReLU mask and the max-abs that
+// feeds the NITI shift.
 #include "gemm256.h"
 
 namespace ionn {
