@@ -37,9 +37,13 @@
 // half of it.  A 128-deep K step is 4 slices of 32; per slice a wavefront
 // reads 4 A and 4 B fragments (16 bytes per lane each: row = lane % 32,
 // k = 16 (lane / 32) .. +15) and issues 16 MFMAs.  The next slice's fragments
-// are read while the current slice's MFMAs run; at the last slice the stage
-// barrier, the next loads and the next step's first fragments are tucked in
-// before its last MFMAs.
+// are read while the current slice's MFMAs run, and the next step's loads go
+// out over the first two slices: one memory instruction between consecutive
+// MFMAs, because a wavefront stalls on the issue of a load into LDS for
+// about as long as an MFMA takes, and a burst of them starves the matrix core
+// (measured: 16 loads issued back to back cost a third of the loop time).
+// At the last slice the stage barrier, the first loads of the step after
+// next and the next step's first fragments are tucked in before its last MFMAs.
 #pragma once
 
 #include "gemm_core.h"
@@ -67,6 +71,18 @@ __device__ __forceinline__ void dma16(v4i rsrc, uint32_t voff, uint32_t soff, ui
     asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, %3 offen lds"
                  :
                  : "v"(voff), "s"(rsrc), "s"(lds_addr), "s"(soff)
+                 : "memory", "m0");
+}
+
+// Two loads under one m0: the second lands 1 KiB further in LDS through the
+// instruction offset, which also adds 1 KiB to its global address, so the
+// caller passes that load's SGPR offset less 1 KiB.
+__device__ __forceinline__ void dma16x2(v4i rsrc, uint32_t voff0, uint32_t soff0, uint32_t voff1,
+                                        uint32_t soff1m, uint32_t lds_addr) {
+    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, %3 offen lds\n\t"
+                 "buffer_load_dwordx4 %4, %1, %5 offen offset:1024 lds"
+                 :
+                 : "v"(voff0), "s"(rsrc), "s"(lds_addr), "s"(soff0), "v"(voff1), "s"(soff1m)
                  : "memory", "m0");
 }
 
@@ -115,15 +131,26 @@ struct TileSrc {
             }
         }
     }
+    __device__ __forceinline__ uint32_t soff_of(int k0, int qq) const {
+        return KMAJOR ? wave_off + uint32_t(8 * qq * ld + k0) : wave_off + uint32_t((k0 + 4 * qq) * ld);
+    }
+    __device__ __forceinline__ uint32_t lds_of(int8_t *dst, int wave, int qq) const {
+        return lds_addr(dst) + uint32_t(wave * 8 * 1024 + qq * 1024);
+    }
+    // instruction qq
+    __device__ __forceinline__ void issue_one(int k0, int8_t *dst, int wave, int qq) const {
+        dma16(rsrc, lane_off[qq & 1], soff_of(k0, qq), lds_of(dst, wave, qq));
+    }
+    // instructions qq (even) and qq + 1 under one m0; soff_of(k0, qq + 1) >= 1 KiB
+    // because it includes at least 8 rows (or 4 k-rows) of a pitch >= 256
+    __device__ __forceinline__ void issue_two(int k0, int8_t *dst, int wave, int qq) const {
+        dma16x2(rsrc, lane_off[0], soff_of(k0, qq), lane_off[1], soff_of(k0, qq + 1) - 1024u,
+                lds_of(dst, wave, qq));
+    }
+    // all eight instructions
     __device__ __forceinline__ void issue(int k0, int8_t *dst, int wave) const {
-        const uint32_t d = lds_addr(dst) + uint32_t(wave * 8 * 1024);
 #pragma unroll
-        for (int qq = 0; qq < 8; ++qq) {
-            const uint32_t soff = KMAJOR ? wave_off + uint32_t(8 * qq * ld + k0)
-                                         : wave_off + uint32_t((k0 + 4 * qq) * ld);
-            const uint32_t voff = lane_off[qq & 1];
-            dma16(rsrc, voff, soff, d + uint32_t(qq * 1024));
-        }
+        for (int qq = 0; qq < 8; qq += 2) issue_two(k0, dst, wave, qq);
     }
 };
 
@@ -191,14 +218,22 @@ struct Frags {
 
 #define IONN_SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
 
-// The 4 MFMAs of column block j of one slice.  The B fragment goes first, so
-// the 32x32 result has n along its rows: lane holds m = lane % 32 and, for
-// q = 0..3, n = 8 q + 4 (lane / 32) .. +3.
+// Issue order of one slice: 16 MFMAs in 4 groups, and the next slice's 8
+// fragments read in the order a0 b0 a1 b1 a2 b2 b3 a3.  Group g needs only
+// fragments that are read early: group 0 uses a0 a1 b0 b1, group 1 adds a2
+// b2, group 2 adds b3 and group 3 a3, so the first MFMAs of a slice wait for
+// reads issued two groups earlier.
+constexpr int GI[16] = {0, 0, 1, 1, 0, 1, 2, 2, 2, 0, 1, 2, 3, 3, 3, 3};
+constexpr int GJ[16] = {0, 1, 0, 1, 2, 2, 0, 1, 2, 3, 3, 3, 0, 1, 2, 3};
+constexpr int RO[8] = {0, 4, 1, 5, 2, 6, 7, 3};
+
+// MFMA t of group g.  The B fragment goes first, so the 32x32 result has n
+// along its rows: lane holds m = lane % 32 and, for q = 0..3,
+// n = 8 q + 4 (lane / 32) .. +3.
 template <bool A_KM, bool B_KM>
-__device__ __forceinline__ void mfma_col(const Frags<A_KM, B_KM> &f, int j, v16i (&acc)[4][4]) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
+__device__ __forceinline__ void mfma_gt(const Frags<A_KM, B_KM> &f, int g, int t, v16i (&acc)[4][4]) {
+    const int i = GI[4 * g + t], j = GJ[4 * g + t];
+    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
 }
 
 template <bool A_KM, bool B_KM>
@@ -234,64 +269,90 @@ __global__ __launch_bounds__(NT, 1) void gemm256_kernel(const int8_t *__restrict
         for (int j = 0; j < 4; ++j) acc[i][j] = v16i{};
 
     Frags<A_KM, B_KM> F[2];  // fragments of the current / next slice
-    const int nk = K / BK;   // even (checked by the caller)
+    const int nk = K / BK;   // even and >= 2 (checked by the caller)
 
-    // Prologue: step 0 -> stage 0, wait, step 1 -> stage 1, slice-0 fragments of step 0.
+    // Load instruction q (0..15) of this wavefront's share of a step: q < 8
+    // are the A tile's, q >= 8 the B tile's; pairs (q, q+1), q even, share m0.
+    auto dma1 = [&](int q, int k0, int8_t *Ad, int8_t *Bd) __attribute__((always_inline)) {
+        if (q < 8) ta.issue_one(k0, Ad, wave, q);
+        else tb.issue_one(k0, Bd, wave, q - 8);
+    };
+    auto dma2 = [&](int q, int k0, int8_t *Ad, int8_t *Bd) __attribute__((always_inline)) {
+        if (q < 8) ta.issue_two(k0, Ad, wave, q);
+        else tb.issue_two(k0, Bd, wave, q - 8);
+    };
+
+    // Prologue: step 0 -> stage 0, wait, the first 4 loads of step 1 ->
+    // stage 1, then the slice-0 fragments of step 0.  No scalar load may be
+    // pending into the loop (it would force a full LDS wait at its head).
     ta.issue(0, sA0, wave);
     tb.issue(0, sB0, wave);
     __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
-    ta.issue(BK, sA1, wave);
-    tb.issue(BK, sB1, wave);
+    dma2(0, BK, sA1, sB1);
+    dma2(2, BK, sA1, sB1);
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
 #pragma unroll
-    for (int r = 0; r < 8; ++r) F[0].read(r, sA0, sB0, fa, fb, 0);
+    for (int r = 0; r < 8; ++r) F[0].read(RO[r], sA0, sB0, fa, fb, 0);
 
-    // One K step held in stage (Ac, Bc); the next step's data sits in the
-    // other stage (An, Bn) once the barrier is passed.  Slices 0..2: the
-    // slice's 16 MFMAs with the next slice's 8 fragment reads after each
-    // column.  Slice 3: columns 0, 1; then wait for this wave's loads and LDS
-    // reads and meet at the barrier (every wave's loads of the next step are
-    // in; nobody reads this stage any more); loads of step + 2 into this
-    // stage; the next step's slice-0 reads spread over columns 2, 3.
+    // One K step held in stage (Ac, Bc); stage (An, Bn) receives the next
+    // step.  Exactly one memory instruction (a fragment read, or one or two
+    // loads under one m0) sits between consecutive MFMAs, so no issue gap is
+    // longer than an MFMA and the matrix core never waits on the issue of a
+    // load.  Slices 0..2: the next slice's fragment reads, and over slices 0
+    // and 1 the remaining 12 loads of the next step (its first 4 went out at
+    // the end of the previous step).  Slice 3: groups 0, 1; wait for this
+    // wave's loads and reads and meet at the barrier (the next step's data is
+    // in, nobody reads this stage any more); then the first 4 loads of step
+    // + 2 into this stage and the next step's slice-0 reads, interleaved with
+    // groups 2, 3.  Reading the next stage on the last step reads stale LDS,
+    // which is harmless and keeps the schedule branch-free.
     auto step = [&](const int8_t *Ac, const int8_t *Bc, const int8_t *An, const int8_t *Bn,
                     int8_t *Adst, int8_t *Bdst, int kt) __attribute__((always_inline)) {
+        int8_t *Anw = const_cast<int8_t *>(An), *Bnw = const_cast<int8_t *>(Bn);
+        const bool more1 = kt + 1 < nk, more2 = kt + 2 < nk;
 #pragma unroll
         for (int sl = 0; sl < 3; ++sl) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                mfma_col(F[sl & 1], j, acc);
+            for (int g = 0; g < 4; ++g) {
+                const int c = 4 * sl + g;
+                mfma_gt(F[sl & 1], g, 0, acc);
                 IONN_SCHED_FENCE();
-                F[(sl + 1) & 1].read(2 * j, Ac, Bc, fa, fb, sl + 1);
-                F[(sl + 1) & 1].read(2 * j + 1, Ac, Bc, fa, fb, sl + 1);
+                F[(sl + 1) & 1].read(RO[2 * g], Ac, Bc, fa, fb, sl + 1);
+                IONN_SCHED_FENCE();
+                mfma_gt(F[sl & 1], g, 1, acc);
+                IONN_SCHED_FENCE();
+                if (c < 8 && more1) {
+                    if (c < 4) dma2(4 + 2 * c, (kt + 1) * BK, Anw, Bnw);
+                    else dma1(12 + (c - 4), (kt + 1) * BK, Anw, Bnw);
+                }
+                IONN_SCHED_FENCE();
+                mfma_gt(F[sl & 1], g, 2, acc);
+                IONN_SCHED_FENCE();
+                F[(sl + 1) & 1].read(RO[2 * g + 1], Ac, Bc, fa, fb, sl + 1);
+                IONN_SCHED_FENCE();
+                mfma_gt(F[sl & 1], g, 3, acc);
                 IONN_SCHED_FENCE();
             }
         }
-        mfma_col(F[1], 0, acc);
-        IONN_SCHED_FENCE();
-        mfma_col(F[1], 1, acc);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) mfma_gt(F[1], t >> 2, t & 3, acc);
         IONN_SCHED_FENCE();
         __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
         __builtin_amdgcn_s_barrier();
         IONN_SCHED_FENCE();
-        if (kt + 2 < nk) {
-            ta.issue((kt + 2) * BK, Adst, wave);
-            tb.issue((kt + 2) * BK, Bdst, wave);
-        }
-        IONN_SCHED_FENCE();
-        if (kt + 1 < nk) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) F[0].read(r, An, Bn, fa, fb, 0);
-        }
-        IONN_SCHED_FENCE();
-        mfma_col(F[1], 2, acc);
-        IONN_SCHED_FENCE();
-        if (kt + 1 < nk) {
+        for (int g = 2; g < 4; ++g) {
+            if (more2) dma2(2 * (g - 2), (kt + 2) * BK, Adst, Bdst);
+            IONN_SCHED_FENCE();
 #pragma unroll
-            for (int r = 4; r < 8; ++r) F[0].read(r, An, Bn, fa, fb, 0);
+            for (int t = 0; t < 4; ++t) {
+                mfma_gt(F[1], g, t, acc);
+                IONN_SCHED_FENCE();
+                F[0].read(RO[4 * (g - 2) + t], An, Bn, fa, fb, 0);
+                IONN_SCHED_FENCE();
+            }
         }
-        IONN_SCHED_FENCE();
-        mfma_col(F[1], 3, acc);
-        IONN_SCHED_FENCE();
     };
 
     for (int kt = 0; kt < nk; kt += 2) {
