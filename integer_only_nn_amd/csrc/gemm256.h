@@ -236,7 +236,7 @@ __device__ __forceinline__ void mfma_gt(const Frags<A_KM, B_KM> &f, int g, int t
     acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
 }
 
-template <bool A_KM, bool B_KM>
+template <bool A_KM, bool B_KM, bool RELU>
 __global__ __launch_bounds__(NT, 1) void gemm256_kernel(const int8_t *__restrict__ A, int64_t lda,
                                                         const int8_t *__restrict__ B, int64_t ldb,
                                                         uint32_t a_bytes, uint32_t b_bytes,
@@ -361,44 +361,57 @@ __global__ __launch_bounds__(NT, 1) void gemm256_kernel(const int8_t *__restrict
     }
 
     // ---- epilogue: lane holds C[m][n .. n+3] for m = .. + lane % 32 and
-    // n = .. + 8 q + 4 (lane / 32), q = 0..3 ----
-    uint32_t amax = 0;
+    // n = .. + 8 q + 4 (lane / 32), q = 0..3.  The max-abs is taken as the
+    // larger magnitude of the running max and min (v_max3 / v_min3 over pairs
+    // of values: one instruction per value instead of abs + max per value);
+    // |INT32_MIN| = 2^31 is exact in uint32.  Row pointers are formed once
+    // per 32-row block; column offsets are immediates. ----
+    int32_t vmax = INT32_MIN, vmin = INT32_MAX;
     const int em = lane & 31, en = (lane >> 5) * 4;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int m = m0 + wm * 128 + i * 32 + em;
+        const int64_t m = m0 + wm * 128 + i * 32 + em;
+        const int64_t nb = n0 + wn * 128 + en;
+        int32_t *row = ep.C + m * ep.ldc + nb;
+        const int8_t *arow = RELU ? ep.act + m * ep.ldc + nb : nullptr;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int n = n0 + wn * 128 + j * 32 + 8 * q + en;
+                const int dn = j * 32 + 8 * q;
                 v4i v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-                int32_t *cp = ep.C + int64_t(m) * ep.ldc + n;
-                if (ep.act) {
-                    const uint32_t a = *reinterpret_cast<const uint32_t *>(ep.act + int64_t(m) * ep.ldc + n);
+                if (RELU) {
+                    const uint32_t a = *reinterpret_cast<const uint32_t *>(arow + dn);
 #pragma unroll
                     for (int c = 0; c < 4; ++c)
                         if (int8_t(uint8_t(a >> (8 * c))) <= 0) v[c] = 0;
                 }
-                *reinterpret_cast<v4i *>(cp) = v;
-#pragma unroll
-                for (int c = 0; c < 4; ++c) amax = max(amax, abs_u32(v[c]));
+                *reinterpret_cast<v4i *>(row + dn) = v;
+                vmax = max(vmax, max(v[0], v[1]));
+                vmax = max(vmax, max(v[2], v[3]));
+                vmin = min(vmin, min(v[0], v[1]));
+                vmin = min(vmin, min(v[2], v[3]));
             }
         }
     }
     if (ep.absmax) {
+        uint32_t amax = max(abs_u32(vmax), abs_u32(vmin));
         amax = wave_max_u32(amax);
         if (lane == 0 && amax != 0) atomicMax(ep.absmax, amax);
     }
 }
 
+// ep.act selects the ReLU-masked epilogue (dgrad): C = 0 where act <= 0.
 template <bool A_KM, bool B_KM>
 void launch(const int8_t *A, int64_t lda, const int8_t *B, int64_t ldb, const gemm::Epi &ep, int M,
             int N, int K, hipStream_t st) {
     const uint32_t a_bytes = uint32_t((A_KM ? int64_t(M) : int64_t(K)) * lda);
     const uint32_t b_bytes = uint32_t((B_KM ? int64_t(N) : int64_t(K)) * ldb);
-    gemm256_kernel<A_KM, B_KM><<<dim3((M / BM) * (N / BN)), dim3(NT), 0, st>>>(
-        A, lda, B, ldb, a_bytes, b_bytes, ep, M, N, K);
+    const dim3 grid((M / BM) * (N / BN)), block(NT);
+    if (ep.act)
+        gemm256_kernel<A_KM, B_KM, true><<<grid, block, 0, st>>>(A, lda, B, ldb, a_bytes, b_bytes, ep, M, N, K);
+    else
+        gemm256_kernel<A_KM, B_KM, false><<<grid, block, 0, st>>>(A, lda, B, ldb, a_bytes, b_bytes, ep, M, N, K);
 }
 
 }  // namespace g256
