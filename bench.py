@@ -28,6 +28,7 @@ import time
 
 import numpy as np
 
+HERE = os.path.dirname(os.path.abspath(__file__))
 PEAK_INT8_TOPS = 5000.0     # MI355X dense int8 matrix peak (5.0 POP/s)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 T, IN, OUT = 8192, 4096, 4096
@@ -173,6 +174,35 @@ def bench_dfp16(torch, steps_mod, nsteps):
     return (time.perf_counter() - t0) * 1e3 / nsteps
 
 
+def _kernel_source_hash():
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(HERE, "integer_only_nn_amd", "csrc", "*"))):
+        h.update(os.path.basename(p).encode())
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM-side bytes per launch from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE summary, if it was taken on the kernel sources as they are
+    now (else {}: the counters describe an older kernel)."""
+    path = os.path.join(HERE, "profiles", "gemm256_linear_step_8192x4096x4096_hbm_traffic.txt")
+    if not os.path.exists(path):
+        return {}
+    out, src = {}, None
+    with open(path) as f:
+        for line in f:
+            parts = line.split()
+            if len(parts) == 2 and parts[0] == "source_sha256":
+                src = parts[1]
+            elif len(parts) == 3 and parts[0] == "traffic_bytes_per_launch":
+                out[parts[1]] = float(parts[2])
+    return out if src == _kernel_source_hash() else {}
+
+
 def cpu_baseline(rows):
     """The oracle (plain C, OpenMP) on a bounded sample of the large-linear
     step: `rows` token rows through fwd and dgrad, wgrad over `rows` tokens,
@@ -209,6 +239,7 @@ def main():
     dom = max(gemm, key=gemm.get)
     achieved = 2.0 * T * IN * OUT / (gemm[dom] * 1e-3) / 1e12
     upd_bytes = 6.0 * IN * OUT
+    traffic = measured_traffic()
     upd_gbs = upd_bytes / (per["update"] * 1e-3) / 1e9
     log(f"step {ms:.3f} ms  {tops:.1f} TOPS  per-kernel ms {per}")
 
@@ -233,10 +264,11 @@ def main():
         "ms_per_step_events_per_launch": round(ms_instr, 4),
         "roofline": {"bound": "mfma", "kernel": f"int_linear_{dom}", "achieved": round(achieved, 1),
                      "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_INT8_TOPS, 4),
-                     "traffic": None},
+                     "traffic": traffic.get(f"int_linear_{dom}")},
         "update_pass": {"bound": "hbm", "achieved": round(upd_gbs, 1), "peak": PEAK_HBM_GBS,
                         "unit": "GB/s", "frac": round(upd_gbs / PEAK_HBM_GBS, 4),
-                        "bytes_per_launch": upd_bytes},
+                        "bytes_per_launch": upd_bytes,
+                        "traffic": traffic.get("niti_quantize_update")},
         "ms_per_step_with_delta_requant": round(ms_req, 4),
         "shifts": {"s_delta": shifts[3], "s_weight": shifts[4], "ws": shifts[5]},
     }
