@@ -176,11 +176,21 @@ int int_conv_dgrad(const int8_t *dY, const int8_t *Wt, int32_t *dX,
                    const ionn_conv_desc *desc, uint32_t *absmax_dX,
                    void *stream);
 
+/* Device workspace (bytes) that lets int_conv_wgrad take its fast path for
+ * this geometry (64 input and 64 output channels, W up to about 100): one
+ * partial G per compute unit plus one per 16 of them.  0 when the geometry
+ * has no fast path (the call then needs no workspace). */
+size_t int_conv_wgrad_workspace_bytes(const ionn_conv_desc *desc);
+
 /* G[co,kh,kw,ci] = sum_{n,h,w} dY[n,h,w,co] * X[n,h+kh-1,w+kw-1,ci].
- * G: int32 [Cout][3][3][Cin] (written; the call clears it first). */
+ * G: int32 [Cout][3][3][Cin] (written).  workspace (nullable, device,
+ * 16-byte aligned, ws_bytes long, owned by the caller, clobbered): with at
+ * least int_conv_wgrad_workspace_bytes(desc) bytes, the gradient is
+ * computed as per-compute-unit partial sums reduced in two passes; without
+ * it, by a split-K product with integer atomics.  Same bits either way. */
 int int_conv_wgrad(const int8_t *dY, const int8_t *X, int32_t *G,
                    const ionn_conv_desc *desc, uint32_t *absmax_G,
-                   void *stream);
+                   void *workspace, size_t ws_bytes, void *stream);
 
 /* ------------------------------------------------------------------------ */
 /* DFP-16 shared-exponent contractions ([DFP] sections 3, 3.1, 4).           */

@@ -1,0 +1,443 @@
+// Fast path of the 3x3 / stride 1 / pad 1 convolution contractions for 64
+// input and 64 output channels ("Integer On-Device Training: Overview",
+// section 7: Conv2D layers; NHWC activations and OHWI weights as on the
+// TiGrIS "Compilation Pipeline" page), on v_mfma_i32_32x32x32_i8.
+//
+//   fwd    out[p][co] = sum_{tap, ci} in[p + off(tap)][ci] * W[co][tap][ci]
+//   dgrad  out[p][ci] = sum_{tap, co} in[p + off(tap)][co] * W[co][8 - tap][ci]
+//
+// off(tap) = (kh - 1, kw - 1) for tap = 3 kh + kw, zero outside the image.
+// dgrad is the same sum over the mirrored kernel (off(8 - tap) = -off(tap)),
+// so both run one kernel; only the weight fragments differ.
+//
+// A persistent workgroup per compute unit walks tiles of 256 consecutive
+// output pixels of one image.  For each tile the input rows it touches, plus
+// one row above and below, are staged in LDS as a zero-padded halo: (W + 2)
+// slots per row (the two outer slots stay zero), 80 bytes per slot (64
+// channels + 16 bytes of padding, which makes 16 consecutive slots hit 16
+// distinct 16-byte bank groups).  Rows outside the image are written as
+// zeros, so every tap of every pixel reads its operand at
+// slot(pixel) + dy (W + 2) + dx with no bounds test.  The 64 x 576 weight
+// matrix lives in registers for the whole kernel (36 16-byte fragments per
+// lane), so LDS serves only the pixel operand.  The next tile's halo is
+// loaded into registers while the current tile computes and written to the
+// other LDS buffer afterwards: one barrier per tile.
+//
+// Each wavefront owns 64 pixels x 64 channels (2 x 2 blocks of 32 x 32, 64
+// accumulators); K = 9 taps x 64 = 18 steps of 32.
+#pragma once
+
+#include "common.h"
+
+namespace ionn {
+namespace c3 {
+
+constexpr int C = 64;            // input and output channels of the fast path
+constexpr int TP = 256;          // output pixels per tile
+constexpr int NT = 256;          // threads per workgroup (4 wavefronts)
+constexpr int SLOT = 80;         // LDS bytes per halo slot
+constexpr int HALO_BYTES = 48 * 1024;
+constexpr int HALO_IT = 10;      // 16-byte halo chunks per thread and tile, at most
+constexpr int KS = 18;           // 576 / 32
+
+// Bytes of the halo of a 256-pixel tile: rows touched by 256 consecutive
+// pixels (at most ceil(255 / W) + 1) plus one above and one below.
+inline int64_t halo_bytes(int64_t W) {
+    const int64_t rows = (TP - 1 + W - 1) / W + 1 + 2;
+    return rows * (W + 2) * SLOT;
+}
+
+inline bool fits(int64_t W) {
+    return W >= 1 && halo_bytes(W) <= HALO_BYTES && ((TP - 1 + W - 1) / W + 3) * W * 4 <= int64_t(HALO_IT) * NT;
+}
+
+template <bool DGRAD>
+__global__ __launch_bounds__(NT, 1) void conv3x3_kernel(const int8_t *__restrict__ in,
+                                                        const int8_t *__restrict__ wgt,
+                                                        int32_t *__restrict__ out, int N, int H,
+                                                        int W, uint32_t *__restrict__ absmax) {
+    __shared__ __attribute__((aligned(16))) int8_t halo[2][HALO_BYTES];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int HW = H * W;
+    const int tpi = (HW + TP - 1) / TP;
+    const int ntiles = N * tpi;
+    const int W2 = W + 2;
+
+    // ---- weight fragments: wf[cb][ks] = 16 bytes of row (cb*32 + lane%32),
+    // k = ks*32 + 16*(lane/32) of the operand B[row][k] (k = tap*64 + channel).
+    v4i wf[2][KS];
+    if (!DGRAD) {
+        // B[co][tap*64 + ci] = W[co][tap][ci]: the weight rows as stored.
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                wf[cb][ks] = *reinterpret_cast<const v4i *>(wgt + (cb * 32 + (lane & 31)) * 576 + ks * 32 +
+                                                            16 * (lane >> 5));
+    } else {
+        // B[ci][tap*64 + co] = W[co][8 - tap][ci]: W is staged in LDS, transposed
+        // there by all threads (16 bytes of one B row per step), then read back
+        // as fragments (once per workgroup).
+        int8_t *stage = &halo[0][0], *bt = &halo[1][0];
+        for (int i = tid; i < 64 * 576 / 16; i += NT)
+            *reinterpret_cast<v4i *>(stage + 16 * i) = *reinterpret_cast<const v4i *>(wgt + 16 * i);
+        __syncthreads();
+        for (int q = tid; q < 64 * 576 / 16; q += NT) {
+            const int ci = q / 36, kc = q - ci * 36;
+            const int tap = kc >> 2, co0 = (kc & 3) * 16;
+            uint32_t w4[4] = {0, 0, 0, 0};
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+                w4[j >> 2] |= uint32_t(uint8_t(stage[(co0 + j) * 576 + (8 - tap) * 64 + ci])) << (8 * (j & 3));
+            *reinterpret_cast<v4i *>(bt + ci * 576 + tap * 64 + co0) =
+                v4i{int(w4[0]), int(w4[1]), int(w4[2]), int(w4[3])};
+        }
+        __syncthreads();
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                wf[cb][ks] = *reinterpret_cast<const v4i *>(bt + (cb * 32 + (lane & 31)) * 576 + ks * 32 +
+                                                            16 * (lane >> 5));
+        __syncthreads();
+    }
+
+    // ---- zero both halo buffers (the outer slots of every row stay zero)
+    for (int i = tid; i < 2 * HALO_BYTES / 16; i += NT)
+        reinterpret_cast<v4i *>(&halo[0][0])[i] = v4i{0, 0, 0, 0};
+
+    // This thread's halo chunks: q = tid + NT*i -> (row r, column w, 16-byte
+    // chunk cc) with q = (r * W + w) * 4 + cc; the same for every tile.
+    int hr[HALO_IT], hw4[HALO_IT];
+#pragma unroll
+    for (int i = 0; i < HALO_IT; ++i) {
+        const int q = tid + NT * i;
+        hr[i] = q / (4 * W);
+        hw4[i] = q - hr[i] * 4 * W;
+    }
+
+    // Halo of tile t into registers (zeros for rows outside the image and
+    // for chunks past the tile's rows).
+    v4i hv[HALO_IT];
+    auto fetch = [&](int t) __attribute__((always_inline)) {
+        const int n = t / tpi, p0 = (t - n * tpi) * TP;
+        const int valid = min(TP, HW - p0);
+        const int hf = p0 / W, hl = (p0 + valid - 1) / W;
+        const int nrows = hl - hf + 3;
+#pragma unroll
+        for (int i = 0; i < HALO_IT; ++i) {
+            const int h = hf - 1 + hr[i];
+            v4i v = {0, 0, 0, 0};
+            if (hr[i] < nrows && h >= 0 && h < H)
+                v = *reinterpret_cast<const v4i *>(in + ((int64_t(n) * H + h) * W) * C + int64_t(hw4[i]) * 16);
+            hv[i] = v;
+        }
+    };
+    auto put = [&](int t, int8_t *buf) __attribute__((always_inline)) {
+        const int n = t / tpi, p0 = (t - n * tpi) * TP;
+        const int valid = min(TP, HW - p0);
+        const int hf = p0 / W, hl = (p0 + valid - 1) / W;
+        const int nrows = hl - hf + 3;
+#pragma unroll
+        for (int i = 0; i < HALO_IT; ++i) {
+            if (hr[i] < nrows) {
+                const int w = hw4[i] >> 2, cc = hw4[i] & 3;
+                *reinterpret_cast<v4i *>(buf + (hr[i] * W2 + w + 1) * SLOT + cc * 16) = hv[i];
+            }
+        }
+    };
+
+    int t = blockIdx.x;
+    if (t < ntiles) fetch(t);
+    __syncthreads();  // zeroing done before the first halo lands
+    if (t < ntiles) put(t, halo[0]);
+    __syncthreads();
+
+    int32_t vmax = INT32_MIN, vmin = INT32_MAX;
+    int b = 0;
+    for (; t < ntiles; t += gridDim.x, b ^= 1) {
+        const int tn = t + gridDim.x;
+        if (tn < ntiles) fetch(tn);
+
+        const int n = t / tpi, p0 = (t - n * tpi) * TP;
+        const int valid = min(TP, HW - p0);
+        const int hf = p0 / W;
+        const int8_t *buf = halo[b];
+
+        // LDS byte offset of each of this lane's two pixels (centre tap), or
+        // -1 past the tile's valid pixels.
+        int poff[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int pl = (2 * wave + j) * 32 + (lane & 31);
+            if (pl < valid) {
+                const int p = p0 + pl, h = p / W, w = p - h * W;
+                poff[j] = ((h - hf + 1) * W2 + w + 1) * SLOT + 16 * (lane >> 5);
+            } else {
+                poff[j] = -1;
+            }
+        }
+        // operand fragment of pixel block j at step ks: tap ks/2, channel chunk
+        // 2 (ks & 1) + lane/32; a lane past the valid pixels reads slot 0 (zero)
+        auto afrag = [&](int j, int ks) __attribute__((always_inline)) {
+            const int tap = ks >> 1, dy = tap / 3 - 1, dx = tap % 3 - 1;
+            const int o = poff[j] >= 0 ? poff[j] + (dy * W2 + dx) * SLOT + 32 * (ks & 1) : 0;
+            return *reinterpret_cast<const v4i *>(buf + o);
+        };
+
+        v16i acc[2][2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb) acc[j][cb] = v16i{};
+        v4i a[2][2];
+        a[0][0] = afrag(0, 0);
+        a[0][1] = afrag(1, 0);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const int c = ks & 1;
+            if (ks + 1 < KS) {
+                a[c ^ 1][0] = afrag(0, ks + 1);
+                a[c ^ 1][1] = afrag(1, ks + 1);
+            }
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int cb = 0; cb < 2; ++cb)
+                    acc[j][cb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(wf[cb][ks], a[c][j], acc[j][cb], 0, 0, 0);
+        }
+
+        // epilogue: lane holds out[p][co .. co+3], p = block pixel lane % 32,
+        // co = cb*32 + 8 q + 4 (lane / 32)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int pl = (2 * wave + j) * 32 + (lane & 31);
+            if (pl < valid) {
+                int32_t *row = out + (int64_t(n) * HW + p0 + pl) * C + 4 * (lane >> 5);
+#pragma unroll
+                for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const v4i v = {acc[j][cb][4 * q], acc[j][cb][4 * q + 1], acc[j][cb][4 * q + 2],
+                                       acc[j][cb][4 * q + 3]};
+                        *reinterpret_cast<v4i *>(row + cb * 32 + 8 * q) = v;
+                        vmax = max(vmax, max(max(v[0], v[1]), max(v[2], v[3])));
+                        vmin = min(vmin, min(min(v[0], v[1]), min(v[2], v[3])));
+                    }
+            }
+        }
+
+        if (tn < ntiles) put(tn, halo[b ^ 1]);
+        __syncthreads();
+    }
+
+    if (absmax) {
+        uint32_t amax = vmax >= vmin ? max(abs_u32(vmax), abs_u32(vmin)) : 0u;
+        amax = wave_max_u32(amax);
+        if (lane == 0 && amax != 0) atomicMax(absmax, amax);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Weight gradient, 64 -> 64 channels:
+//   G[co][tap*64 + ci] = sum_p dY[p][co] * X[p + off(tap)][ci]
+// as C = A B^T with A = dY^T (64 x pixels) and B = im2col(X) (576 x pixels),
+// K = pixels.  Persistent workgroups walk the same 256-pixel tiles as the
+// forward kernel; each keeps a partial G (64 x 576) in its accumulators over
+// all its tiles and writes it once to a workspace row; two reduction passes
+// of 16 rows each sum the rows into G (no atomics, so the result is
+// deterministic; integer sums are exact in any order anyway).
+//
+// Both operands have their contraction index (pixels) as the outer
+// dimension, so fragments come out of LDS with ds_read_b64_tr_b8: lane i of
+// each 16-lane group addresses row k0 + i/2 (a pixel), 8 bytes at column
+// m0 + 8 (i mod 2), and lane j receives column m0 + j of rows k0..k0+7.  The
+// dY tile sits in LDS as [pixel][80 bytes]; the X operand is read from the
+// zero-padded halo through a per-tile table of each pixel's slot.
+// Wavefront w owns n-blocks [nb0, nb0 + nn) = {0..4, 5..9, 10..13, 14..17}
+// of the 18 32-wide blocks of (tap, ci), for both 32-row blocks of co.
+// ---------------------------------------------------------------------------
+constexpr int WNB = 5;                      // n-blocks per wavefront, at most
+constexpr int DY_BYTES = TP * SLOT;         // one dY tile in LDS
+constexpr int GSZ = 64 * 576;               // elements of G
+
+inline int64_t wgrad_rows(int cus) { return cus + (cus + 15) / 16; }
+
+__device__ __forceinline__ v4i tr_frag(const int8_t *base0, const int8_t *base1) {
+    typedef int v2i_ __attribute__((ext_vector_type(2)));
+    typedef __attribute__((address_space(3))) v2i_ lds_v2i_;
+    const v2i_ x = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i_ *)(base0));
+    const v2i_ y = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i_ *)(base1));
+    return v4i{x.x, x.y, y.x, y.y};
+}
+
+__global__ __launch_bounds__(NT, 1) void conv3x3_wgrad_kernel(const int8_t *__restrict__ dY,
+                                                              const int8_t *__restrict__ X,
+                                                              int32_t *__restrict__ part, int N,
+                                                              int H, int W) {
+    __shared__ __attribute__((aligned(16))) int8_t sdy[2][DY_BYTES];
+    __shared__ __attribute__((aligned(16))) int8_t halo[2][HALO_BYTES];
+    __shared__ int sslot[2][TP];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int HW = H * W;
+    const int tpi = (HW + TP - 1) / TP;
+    const int ntiles = N * tpi;
+    const int W2 = W + 2;
+    const int nb0 = wave < 2 ? 5 * wave : 10 + 4 * (wave - 2);
+    const int nn = wave < 2 ? 5 : 4;
+
+    for (int i = tid; i < 2 * HALO_BYTES / 16; i += NT)
+        reinterpret_cast<v4i *>(&halo[0][0])[i] = v4i{0, 0, 0, 0};
+
+    int hr[HALO_IT], hw4[HALO_IT];
+#pragma unroll
+    for (int i = 0; i < HALO_IT; ++i) {
+        const int q = tid + NT * i;
+        hr[i] = q / (4 * W);
+        hw4[i] = q - hr[i] * 4 * W;
+    }
+
+    // Registers in flight for the next tile: 4 dY chunks, the halo chunks,
+    // and this thread's pixel slot.
+    v4i dv[4], hv[HALO_IT];
+    int myslot = 0;
+    auto fetch = [&](int t) __attribute__((always_inline)) {
+        const int n = t / tpi, p0 = (t - n * tpi) * TP;
+        const int valid = min(TP, HW - p0);
+        const int hf = p0 / W, hl = (p0 + valid - 1) / W;
+        const int nrows = hl - hf + 3;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int q = tid + NT * i, pl = q >> 2, cc = q & 3;
+            v4i v = {0, 0, 0, 0};
+            if (pl < valid)
+                v = *reinterpret_cast<const v4i *>(dY + (int64_t(n) * HW + p0 + pl) * C + 16 * cc);
+            dv[i] = v;
+        }
+#pragma unroll
+        for (int i = 0; i < HALO_IT; ++i) {
+            const int h = hf - 1 + hr[i];
+            v4i v = {0, 0, 0, 0};
+            if (hr[i] < nrows && h >= 0 && h < H)
+                v = *reinterpret_cast<const v4i *>(X + ((int64_t(n) * H + h) * W) * C + int64_t(hw4[i]) * 16);
+            hv[i] = v;
+        }
+        if (tid < valid) {
+            const int p = p0 + tid, h = p / W, w = p - h * W;
+            myslot = (h - hf + 1) * W2 + w + 1;
+        } else {
+            myslot = W2 + 1;  // any slot whose 3x3 neighbourhood is inside the halo; dY is 0 there
+        }
+    };
+    auto put = [&](int t, int bb) __attribute__((always_inline)) {
+        const int n = t / tpi, p0 = (t - n * tpi) * TP;
+        const int valid = min(TP, HW - p0);
+        const int hf = p0 / W, hl = (p0 + valid - 1) / W;
+        const int nrows = hl - hf + 3;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int q = tid + NT * i, pl = q >> 2, cc = q & 3;
+            *reinterpret_cast<v4i *>(&sdy[bb][pl * SLOT + 16 * cc]) = dv[i];
+        }
+#pragma unroll
+        for (int i = 0; i < HALO_IT; ++i) {
+            if (hr[i] < nrows) {
+                const int w = hw4[i] >> 2, cc = hw4[i] & 3;
+                *reinterpret_cast<v4i *>(&halo[bb][(hr[i] * W2 + w + 1) * SLOT + cc * 16]) = hv[i];
+            }
+        }
+        sslot[bb][tid] = myslot;
+    };
+
+    v16i acc[WNB][2];
+#pragma unroll
+    for (int j = 0; j < WNB; ++j)
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) acc[j][cb] = v16i{};
+
+    int t = blockIdx.x;
+    if (t < ntiles) fetch(t);
+    __syncthreads();
+    if (t < ntiles) put(t, 0);
+    __syncthreads();
+
+    // lane geometry of the transposing reads
+    const int g = lane >> 4, i16 = lane & 15;
+    const int prow = 16 * (g >> 1) + (i16 >> 1);     // pixel row within a 32-pixel step, h = 0
+    const int mcol = 16 * (g & 1) + 8 * (i16 & 1);   // column within a 32-wide block
+    int b = 0;
+    for (; t < ntiles; t += gridDim.x, b ^= 1) {
+        const int tn = t + gridDim.x;
+        if (tn < ntiles) fetch(tn);
+        const int8_t *ydb = sdy[b];
+        const int8_t *xb = halo[b];
+#pragma unroll 2
+        for (int kp = 0; kp < TP / 32; ++kp) {
+            const int r0 = kp * 32 + prow, r1 = r0 + 8;
+            const int s0 = sslot[b][r0], s1 = sslot[b][r1];
+            v4i a[2];
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb)
+                a[cb] = tr_frag(ydb + r0 * SLOT + cb * 32 + mcol, ydb + r1 * SLOT + cb * 32 + mcol);
+#pragma unroll
+            for (int j = 0; j < WNB; ++j) {
+                if (j < nn) {
+                    const int nb = nb0 + j, tap = nb >> 1;
+                    const int sh = (tap / 3 - 1) * W2 + (tap % 3 - 1);
+                    const int cix = (nb & 1) * 32 + mcol;
+                    const v4i bf = tr_frag(xb + (s0 + sh) * SLOT + cix, xb + (s1 + sh) * SLOT + cix);
+#pragma unroll
+                    for (int cb = 0; cb < 2; ++cb)
+                        acc[j][cb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bf, a[cb], acc[j][cb], 0, 0, 0);
+                }
+            }
+        }
+        if (tn < ntiles) put(tn, b ^ 1);
+        __syncthreads();
+    }
+
+    // partial G of this workgroup: lane holds co = cb*32 + lane%32 and
+    // n = (nb0 + j)*32 + 8 q + 4 (lane / 32) .. +3
+    int32_t *row = part + int64_t(blockIdx.x) * GSZ;
+#pragma unroll
+    for (int j = 0; j < WNB; ++j) {
+        if (j < nn) {
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb) {
+                int32_t *dst = row + (cb * 32 + (lane & 31)) * 576 + (nb0 + j) * 32 + 4 * (lane >> 5);
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    *reinterpret_cast<v4i *>(dst + 8 * q) =
+                        v4i{acc[j][cb][4 * q], acc[j][cb][4 * q + 1], acc[j][cb][4 * q + 2], acc[j][cb][4 * q + 3]};
+            }
+        }
+    }
+}
+
+// dst[g][e] = sum of src rows [16 g, min(16 g + 16, rows)) at element e (GSZ
+// elements per row); with absmax, dst is the final G and its max |G| is
+// max-combined into *absmax.
+__global__ __launch_bounds__(256) void conv3x3_wgrad_reduce(const int32_t *__restrict__ src, int rows,
+                                                            int32_t *__restrict__ dst,
+                                                            uint32_t *__restrict__ absmax) {
+    const int e = 4 * (blockIdx.x * 256 + threadIdx.x);  // GSZ / 1024 blocks along x
+    typedef unsigned v4u __attribute__((ext_vector_type(4)));  // sums wrap modulo 2^32
+    const int g = blockIdx.y;
+    const int r1 = min(16 * g + 16, rows);
+    v4u s = {0, 0, 0, 0};
+    for (int r = 16 * g; r < r1; ++r) s += *reinterpret_cast<const v4u *>(src + int64_t(r) * GSZ + e);
+    *reinterpret_cast<v4u *>(dst + int64_t(g) * GSZ + e) = s;
+    if (absmax) {
+        uint32_t m = max(max(abs_u32(int32_t(s.x)), abs_u32(int32_t(s.y))),
+                         max(abs_u32(int32_t(s.z)), abs_u32(int32_t(s.w))));
+        m = wave_max_u32(m);
+        if ((threadIdx.x & 63) == 0 && m != 0) atomicMax(absmax, m);
+    }
+}
+
+}  // namespace c3
+}  // namespace ionn

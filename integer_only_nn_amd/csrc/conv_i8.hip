@@ -17,6 +17,9 @@
 // modulo 2^32), so the split-K weight gradient is bit-identical to any
 // other summation order.
 #include "gemm_core.h"
+#include "conv3x3.h"
+
+#include <atomic>
 
 namespace ionn {
 
@@ -52,6 +55,31 @@ int check_desc(const ionn_conv_desc *d, const char *name) {
     return IONN_OK;
 }
 
+// Compute units of the current device (persistent grids).
+int device_cus() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+        v = 256;
+    cache[dev].store(v, std::memory_order_relaxed);
+    return v;
+}
+
+// The 64-channel halo-tiled kernel applies (see conv3x3.h).
+bool fast_c64(const ionn_conv_desc *d, const void *in, const void *w, const void *out) {
+    return d->Cin == 64 && d->Cout == 64 && c3::fits(d->W) && aligned(in, 16) && aligned(w, 16) &&
+           aligned(out, 16);
+}
+
+unsigned c3_grid(const ionn_conv_desc *d) {
+    const int64_t tiles = d->N * ((d->H * d->W + c3::TP - 1) / c3::TP);
+    const int64_t g = tiles < device_cus() ? tiles : device_cus();
+    return unsigned(g < 1 ? 1 : g);
+}
+
 }  // namespace
 }  // namespace ionn
 
@@ -72,6 +100,11 @@ int int_conv_fwd(const int8_t *X, const int8_t *Wt, int32_t *Y, const ionn_conv_
     hipStream_t st = as_stream(stream);
     if (Cin == 0) {
         zero_i32_kernel<<<dim3(4096), dim3(256), 0, st>>>(Y, int64_t(npix) * Cout);
+        return check_launch("int_conv_fwd");
+    }
+    if (fast_c64(desc, X, Wt, Y)) {
+        c3::conv3x3_kernel<false><<<dim3(c3_grid(desc)), dim3(c3::NT), 0, st>>>(
+            X, Wt, Y, int(desc->N), int(desc->H), int(desc->W), absmax_Y);
         return check_launch("int_conv_fwd");
     }
     const int M = npix, N = Cout, K = 9 * Cin;
@@ -99,6 +132,11 @@ int int_conv_dgrad(const int8_t *dY, const int8_t *Wt, int32_t *dX, const ionn_c
         zero_i32_kernel<<<dim3(4096), dim3(256), 0, st>>>(dX, int64_t(npix) * Cin);
         return check_launch("int_conv_dgrad");
     }
+    if (fast_c64(desc, dY, Wt, dX)) {
+        c3::conv3x3_kernel<true><<<dim3(c3_grid(desc)), dim3(c3::NT), 0, st>>>(
+            dY, Wt, dX, int(desc->N), int(desc->H), int(desc->W), absmax_dX);
+        return check_launch("int_conv_dgrad");
+    }
     const int M = npix, N = Cin, K = 9 * Cout;
     SrcIm2colK sa{dY, npix, int(desc->H), int(desc->W), Cout, -1};
     SrcConvWT sb{Wt, Cin, Cout};
@@ -110,8 +148,13 @@ int int_conv_dgrad(const int8_t *dY, const int8_t *Wt, int32_t *dX, const ionn_c
     return check_launch("int_conv_dgrad");
 }
 
+size_t int_conv_wgrad_workspace_bytes(const ionn_conv_desc *desc) {
+    if (desc == nullptr || desc->Cin != 64 || desc->Cout != 64 || !c3::fits(desc->W)) return 0;
+    return size_t(c3::wgrad_rows(device_cus())) * c3::GSZ * sizeof(int32_t);
+}
+
 int int_conv_wgrad(const int8_t *dY, const int8_t *X, int32_t *G, const ionn_conv_desc *desc,
-                   uint32_t *absmax_G, void *stream) {
+                   uint32_t *absmax_G, void *workspace, size_t ws_bytes, void *stream) {
     clear_error();
     if (int rc = check_desc(desc, "int_conv_wgrad")) return rc;
     const int npix = int(desc->N * desc->H * desc->W), Cin = int(desc->Cin), Cout = int(desc->Cout);
@@ -120,6 +163,25 @@ int int_conv_wgrad(const int8_t *dY, const int8_t *X, int32_t *G, const ionn_con
     IONN_REQUIRE(aligned(dY, 16) && aligned(X, 16) && aligned(G, 16) && aligned(absmax_G, 4),
                  IONN_ERR_ALIGN, "int_conv_wgrad: tensors must be 16-byte aligned");
     hipStream_t st = as_stream(stream);
+    if (npix > 0 && workspace != nullptr && fast_c64(desc, dY, X, G) && aligned(workspace, 16) &&
+        ws_bytes >= int_conv_wgrad_workspace_bytes(desc)) {
+        const unsigned P = c3_grid(desc);
+        int32_t *part = static_cast<int32_t *>(workspace);
+        c3::conv3x3_wgrad_kernel<<<dim3(P), dim3(c3::NT), 0, st>>>(dY, X, part, int(desc->N),
+                                                                    int(desc->H), int(desc->W));
+        if (int rc = check_launch("int_conv_wgrad")) return rc;
+        const int xb = c3::GSZ / 1024;
+        if (P > 16) {
+            const unsigned P2 = (P + 15) / 16;
+            int32_t *part2 = part + int64_t(P) * c3::GSZ;
+            c3::conv3x3_wgrad_reduce<<<dim3(xb, P2), dim3(256), 0, st>>>(part, int(P), part2, nullptr);
+            if (int rc = check_launch("int_conv_wgrad")) return rc;
+            c3::conv3x3_wgrad_reduce<<<dim3(xb, 1), dim3(256), 0, st>>>(part2, int(P2), G, absmax_G);
+        } else {
+            c3::conv3x3_wgrad_reduce<<<dim3(xb, 1), dim3(256), 0, st>>>(part, int(P), G, absmax_G);
+        }
+        return check_launch("int_conv_wgrad");
+    }
     const int M = Cout, N = 9 * Cin, K = npix;
     zero_i32_kernel<<<dim3(64), dim3(256), 0, st>>>(G, int64_t(M) * N);
     if (int rc = check_launch("int_conv_wgrad")) return rc;

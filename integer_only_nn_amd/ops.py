@@ -122,9 +122,15 @@ def int_conv_dgrad(dY, Wt, dX, desc, absmax_dX=None, stream=None):
                                _stream(stream)), "int_conv_dgrad")
 
 
-def int_conv_wgrad(dY, X, G, desc, absmax_G=None, stream=None):
+def int_conv_wgrad_workspace_bytes(desc):
+    return int(lib().int_conv_wgrad_workspace_bytes(ctypes.byref(desc)))
+
+
+def int_conv_wgrad(dY, X, G, desc, absmax_G=None, workspace=None, stream=None):
     check(lib().int_conv_wgrad(_p(dY, i8, name="dY"), _p(X, i8, name="X"), _p(G, i32, name="G"),
                                ctypes.byref(desc), _p(absmax_G, u32, 1, "absmax_G"),
+                               _p(workspace, None, name="workspace"),
+                               workspace.numel() * workspace.element_size() if workspace is not None else 0,
                                _stream(stream)), "int_conv_wgrad")
 
 

@@ -156,14 +156,17 @@ class ConvStepBuffers:
     G: torch.Tensor
     scal: torch.Tensor   # [absmax Y, dX, G, s_y, s_dx, s, ws]
     gq: Optional[torch.Tensor] = None
+    ws: Optional[torch.Tensor] = None   # weight-gradient workspace (None: no fast path)
 
     @staticmethod
     def make(N, H, W, Cin, Cout, device, with_gq=False):
+        wsb = ops.int_conv_wgrad_workspace_bytes(ops.conv_desc(N, H, W, Cin, Cout))
         return ConvStepBuffers(_i32(N, H, W, Cout, device=device), _i8(N, H, W, Cout, device=device),
                                _i32(N, H, W, Cin, device=device), _i8(N, H, W, Cin, device=device),
                                _i32(Cout, 3, 3, Cin, device=device),
                                torch.zeros(8, dtype=torch.int32, device=device),
-                               _i32(Cout, 3, 3, Cin, device=device) if with_gq else None)
+                               _i32(Cout, 3, 3, Cin, device=device) if with_gq else None,
+                               torch.empty(wsb, dtype=torch.uint8, device=device) if wsb else None)
 
 
 def conv_step(X, Wt, dY, buf: ConvStepBuffers, tb_a=TB_DELTA, tb_d=TB_DELTA, tb_w=TB_WEIGHT,
@@ -177,7 +180,7 @@ def conv_step(X, Wt, dY, buf: ConvStepBuffers, tb_a=TB_DELTA, tb_d=TB_DELTA, tb_
     ops.niti_quantize(buf.Y, s[0:1], tb_a, False, buf.y8, shift_out=s[3:4], stream=stream)
     ops.int_conv_dgrad(dY, Wt, buf.dX, d, absmax_dX=s[1:2], stream=stream)
     ops.niti_quantize(buf.dX, s[1:2], tb_d, False, buf.dx8, shift_out=s[4:5], stream=stream)
-    ops.int_conv_wgrad(dY, X, buf.G, d, absmax_G=s[2:3], stream=stream)
+    ops.int_conv_wgrad(dY, X, buf.G, d, absmax_G=s[2:3], workspace=buf.ws, stream=stream)
     ops.niti_quantize_update(buf.G, s[2:3], tb_w, mu, Wt, shifts_out=s[5:7], gq_out=buf.gq,
                              stream=stream)
 

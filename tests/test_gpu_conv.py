@@ -17,7 +17,13 @@ pytestmark = pytest.mark.gpu
 
 @pytest.mark.parametrize("N,H,W,Cin,Cout", [(1, 3, 3, 16, 16), (2, 9, 7, 16, 32), (1, 1, 1, 16, 16),
                                             (3, 17, 13, 32, 48), (2, 16, 16, 64, 64),
-                                            (4, 32, 32, 64, 64), (1, 5, 70, 48, 16)])
+                                            (4, 32, 32, 64, 64), (1, 5, 70, 48, 16),
+                                            # 64 -> 64 channels take the halo-tiled kernel:
+                                            # W = 1, 2 (many rows per tile), ragged last tiles,
+                                            # W = 100 (largest halo that fits), tiles > grid
+                                            (3, 5, 1, 64, 64), (2, 7, 2, 64, 64), (5, 13, 11, 64, 64),
+                                            (1, 100, 100, 64, 64), (2, 1, 57, 64, 64),
+                                            (40, 20, 20, 64, 64)])
 def test_conv_step_vs_oracle(N, H, W, Cin, Cout):
     say("conv", N, H, W, Cin, Cout)
     d = ionn_synth.conv3x3(N=N, H=H, W=W, Cin=Cin, Cout=Cout, seed=N * H + Cin)

@@ -72,9 +72,20 @@ def _desc(**kw):
                                 dict(groups=2), dict(Cin=8), dict(Cout=24)])
 def test_conv_refuses_unsupported_geometry(kw):
     d = _desc(**kw)
-    for f in (lib.int_conv_fwd, lib.int_conv_dgrad, lib.int_conv_wgrad):
+    for f in (lib.int_conv_fwd, lib.int_conv_dgrad):
         assert f(FAKE, FAKE, FAKE, ctypes.byref(d), None, None) == UNSUP
+    assert lib.int_conv_wgrad(FAKE, FAKE, FAKE, ctypes.byref(d), None, None, 0, None) == UNSUP
     assert "3x3" in _err() or "multiples of 16" in _err()
+
+
+def test_conv_wgrad_workspace_query():
+    """Workspace only for the 64-channel fast path (one partial G per compute
+    unit plus one per 16 of them, 64*576 int32 each); 0 otherwise."""
+    big = lib.int_conv_wgrad_workspace_bytes(ctypes.byref(_desc(Cin=64, Cout=64, W=56, H=56, N=128)))
+    assert big > 0 and big % (64 * 576 * 4) == 0
+    assert lib.int_conv_wgrad_workspace_bytes(ctypes.byref(_desc(Cin=64, Cout=32))) == 0
+    assert lib.int_conv_wgrad_workspace_bytes(ctypes.byref(_desc(Cin=64, Cout=64, W=4000))) == 0
+    assert lib.int_conv_wgrad_workspace_bytes(None) == 0
 
 
 def test_conv_validation():
