@@ -232,6 +232,228 @@ __global__ __launch_bounds__(WGM *WGN * 64) void dfp16_kernel(DfpArgs g) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Tile-aligned path on v_mfma_i32_32x32x32_i8 (full int8 rate on gfx950).
+//
+// 128 x 128 output tile per workgroup, 4 wavefronts of 64 x 64 (2 x 2 blocks
+// of 32 x 32); one 64-term chunk per K step, double-buffered in LDS as four
+// int8 digit planes (A hi/lo, B hi/lo).  A K-major operand lands as
+// [row][80 bytes] (16 consecutive rows hit 16 distinct bank groups) and is
+// read with ds_read_b128; an M-major operand (dgrad's W, wgrad's dY and X)
+// lands as [k][row + 16 bytes] and is read with two ds_read_b64_tr_b8 per
+// fragment, so no operand is ever transposed in memory.  The digit split
+// happens once per element on the way into LDS (v_perm_b32 picks the high
+// and low bytes of four int16 at a time).
+//
+// Per chunk and 32 x 32 block: 8 MFMAs give sum(ah bh), sum(ah bl + al bh)
+// and sum(al bl) over the 64 terms; the row sums of A' come from v_dot4 on
+// the A fragments (one value per lane), the column sums of B' from two MFMA
+// chains against an all-ones fragment (the 16 columns a lane holds).  Then
+// per element p = 65536 hh + 256 x + ll + 128 sum A' + 128 sum B' + 2^20
+// (mod 2^32) and acc += rhu(p, r): six VALU operations, which is the bound of
+// this kernel (the matrix cores idle a third of the time).
+// ---------------------------------------------------------------------------
+namespace d2 {
+
+typedef int v2i __attribute__((ext_vector_type(2)));
+constexpr int BM = 128, BN = 128, NT = 256;
+constexpr int KP = 80;            // K-major plane: bytes per row
+constexpr int MP = 128 + 16;      // M-major plane: bytes per k-row
+constexpr int PLANE = 128 * KP;   // >= 64 * MP
+constexpr int STAGE = 4 * PLANE;
+
+// hi / lo digit bytes of 4 int16 held in two dwords (lo digit = low byte - 128)
+__device__ __forceinline__ uint32_t hi4(uint32_t w0, uint32_t w1) { return __builtin_amdgcn_perm(w1, w0, 0x07050301u); }
+__device__ __forceinline__ uint32_t lo4(uint32_t w0, uint32_t w1) {
+    return __builtin_amdgcn_perm(w1, w0, 0x06040200u) ^ 0x80808080u;
+}
+
+// One operand tile (128 rows x 64 k of int16) global -> registers -> digit planes.
+template <bool KM>
+struct Ld {
+    v4i reg[4];
+    __device__ __forceinline__ void load(const int16_t *base, int64_t ld, int r0, int k0, int tid) {
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+            const int id = it * NT + tid;
+            const int16_t *p = KM ? base + int64_t(r0 + (id >> 3)) * ld + k0 + 8 * (id & 7)
+                                  : base + int64_t(k0 + (id >> 4)) * ld + r0 + 8 * (id & 15);
+            reg[it] = *reinterpret_cast<const v4i *>(p);
+        }
+    }
+    __device__ __forceinline__ void store(int8_t *hi, int8_t *lo, int tid) const {
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+            const int id = it * NT + tid;
+            const int off = KM ? (id >> 3) * KP + 8 * (id & 7) : (id >> 4) * MP + 8 * (id & 15);
+            const uint32_t w0 = reg[it].x, w1 = reg[it].y, w2 = reg[it].z, w3 = reg[it].w;
+            *reinterpret_cast<uint2 *>(hi + off) = make_uint2(hi4(w0, w1), hi4(w2, w3));
+            *reinterpret_cast<uint2 *>(lo + off) = make_uint2(lo4(w0, w1), lo4(w2, w3));
+        }
+    }
+};
+
+// Fragment of rows rb0 .. rb0+31, k = 32 kh + 16 (lane / 32) .. +15.
+template <bool KM>
+__device__ __forceinline__ v4i frag(const int8_t *plane, int rb0, int kh, int lane) {
+    if (KM) return *reinterpret_cast<const v4i *>(plane + (rb0 + (lane & 31)) * KP + 32 * kh + 16 * (lane >> 5));
+    typedef __attribute__((address_space(3))) v2i lds_v2i_t;
+    const int g = lane >> 4, i = lane & 15;
+    const int8_t *p = plane + (32 * kh + 16 * (g >> 1) + (i >> 1)) * MP + rb0 + 16 * (g & 1) + 8 * (i & 1);
+    const v2i x = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i_t *)(p));
+    const v2i y = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i_t *)(p + 8 * MP));
+    return v4i{x.x, x.y, y.x, y.y};
+}
+
+__device__ __forceinline__ int32_t dot16(v4i f) {  // sum of the 16 signed bytes
+    int32_t s = 0;
+    s = __builtin_amdgcn_sdot4(f.x, 0x01010101, s, false);
+    s = __builtin_amdgcn_sdot4(f.y, 0x01010101, s, false);
+    s = __builtin_amdgcn_sdot4(f.z, 0x01010101, s, false);
+    s = __builtin_amdgcn_sdot4(f.w, 0x01010101, s, false);
+    return s;
+}
+
+struct Args {
+    const int16_t *a, *b;
+    int64_t lda, ldb;
+    int32_t *acc;        // [M][N]
+    uint32_t *absmax;    // max-combined (non-atomic epilogue)
+    int M, N, L, r, split;
+    bool atomic;
+};
+
+template <bool A_KM, bool B_KM>
+__global__ __launch_bounds__(NT, 1) void dfp_kernel(Args g) {
+    __shared__ __attribute__((aligned(16))) int8_t lds[2 * STAGE];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int tiles_n = g.N / BN;
+    const int tm = blockIdx.x / tiles_n, tn = blockIdx.x - tm * tiles_n;
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int nch = g.L / 64;
+    const int c0 = int(int64_t(nch) * blockIdx.y / g.split);
+    const int c1 = int(int64_t(nch) * (blockIdx.y + 1) / g.split);
+
+    Ld<A_KM> la;
+    Ld<B_KM> lb;
+    v16i acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = v16i{};
+
+    if (c0 < c1) {
+        la.load(g.a, g.lda, m0, 64 * c0, tid);
+        lb.load(g.b, g.ldb, n0, 64 * c0, tid);
+        la.store(lds, lds + PLANE, tid);
+        lb.store(lds + 2 * PLANE, lds + 3 * PLANE, tid);
+    }
+    __syncthreads();
+
+    const v4i ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
+    const v16i zero16 = {};
+    const int r = g.r;
+    const uint32_t rm1 = r > 0 ? r - 1 : 0, rw = r > 0 ? 1 : 0;  // rounding bit (none for r = 0)
+    for (int c = c0; c < c1; ++c) {
+        const int8_t *st = lds + ((c - c0) & 1) * STAGE;
+        if (c + 1 < c1) {
+            la.load(g.a, g.lda, m0, 64 * (c + 1), tid);
+            lb.load(g.b, g.ldb, n0, 64 * (c + 1), tid);
+        }
+        v4i ah[2][2], al[2][2], bh[2][2], bl[2][2];
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                ah[i][kh] = frag<A_KM>(st, wm * 64 + 32 * i, kh, lane);
+                al[i][kh] = frag<A_KM>(st + PLANE, wm * 64 + 32 * i, kh, lane);
+                bh[i][kh] = frag<B_KM>(st + 2 * PLANE, wn * 64 + 32 * i, kh, lane);
+                bl[i][kh] = frag<B_KM>(st + 3 * PLANE, wn * 64 + 32 * i, kh, lane);
+            }
+        // 128 * sum(B') over the chunk for the 16 columns of each block; it
+        // seeds the low-digit MFMA chain, which then adds it for free
+        v16i ct[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            v16i sh = __builtin_amdgcn_mfma_i32_32x32x32_i8(bh[j][0], ones, zero16, 0, 0, 0);
+            sh = __builtin_amdgcn_mfma_i32_32x32x32_i8(bh[j][1], ones, sh, 0, 0, 0);
+            v16i sl = __builtin_amdgcn_mfma_i32_32x32x32_i8(bl[j][0], ones, zero16, 0, 0, 0);
+            sl = __builtin_amdgcn_mfma_i32_32x32x32_i8(bl[j][1], ones, sl, 0, 0, 0);
+#pragma unroll
+            for (int v = 0; v < 16; ++v) ct[j][v] = int32_t((uint32_t(sh[v]) << 15) + (uint32_t(sl[v]) << 7));
+        }
+        // 128 * sum(A') over the chunk + 2^20 for this lane's row of each block
+        // (lanes l and l + 32 hold the two 16-term halves of a row's k range)
+        uint32_t rt[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            int32_t sh = dot16(ah[i][0]) + dot16(ah[i][1]);
+            int32_t sl = dot16(al[i][0]) + dot16(al[i][1]);
+            sh += __shfl_xor(sh, 32, 64);
+            sl += __shfl_xor(sl, 32, 64);
+            rt[i] = (uint32_t(sh) << 15) + (uint32_t(sl) << 7) + (1u << 20);
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                v16i hh = __builtin_amdgcn_mfma_i32_32x32x32_i8(bh[j][0], ah[i][0], zero16, 0, 0, 0);
+                hh = __builtin_amdgcn_mfma_i32_32x32x32_i8(bh[j][1], ah[i][1], hh, 0, 0, 0);
+                v16i x = __builtin_amdgcn_mfma_i32_32x32x32_i8(bl[j][0], ah[i][0], zero16, 0, 0, 0);
+                x = __builtin_amdgcn_mfma_i32_32x32x32_i8(bh[j][0], al[i][0], x, 0, 0, 0);
+                x = __builtin_amdgcn_mfma_i32_32x32x32_i8(bl[j][1], ah[i][1], x, 0, 0, 0);
+                x = __builtin_amdgcn_mfma_i32_32x32x32_i8(bh[j][1], al[i][1], x, 0, 0, 0);
+                v16i ll = __builtin_amdgcn_mfma_i32_32x32x32_i8(bl[j][0], al[i][0], ct[j], 0, 0, 0);
+                ll = __builtin_amdgcn_mfma_i32_32x32x32_i8(bl[j][1], al[i][1], ll, 0, 0, 0);
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    // p mod 2^32, then acc += rhu(p, r) = (p >> r) + bit (r - 1) of p
+                    const uint32_t p = (uint32_t(hh[v]) << 16) + ((uint32_t(x[v]) << 8) + uint32_t(ll[v])) + rt[i];
+                    acc[i][j][v] = int32_t(uint32_t(acc[i][j][v]) + uint32_t(int32_t(p) >> r) +
+                                           __builtin_amdgcn_ubfe(p, rm1, rw));
+                }
+            }
+        if (c + 1 < c1) {
+            int8_t *nx = lds + ((c + 1 - c0) & 1) * STAGE;
+            la.store(nx, nx + PLANE, tid);
+            lb.store(nx + 2 * PLANE, nx + 3 * PLANE, tid);
+        }
+        __syncthreads();
+    }
+
+    // lane holds acc[m][n .. n+3] for m = block row lane % 32,
+    // n = block col 8 q + 4 (lane / 32)
+    uint32_t amax = 0;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int m = m0 + wm * 64 + 32 * i + (lane & 31);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int n = n0 + wn * 64 + 32 * j + 8 * q + 4 * (lane >> 5);
+                int32_t *cp = g.acc + int64_t(m) * g.N + n;
+                const v4i v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+                if (g.atomic) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) atomicAdd(cp + e, v[e]);
+                } else {
+                    *reinterpret_cast<v4i *>(cp) = v;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) amax = max(amax, abs_u32(v[e]));
+                }
+            }
+    }
+    if (!g.atomic && g.absmax) {
+        amax = wave_max_u32(amax);
+        if (lane == 0 && amax != 0) atomicMax(g.absmax, amax);
+    }
+}
+
+}  // namespace d2
+
 // out = sat16(rhu(acc, Rs)), Rs from the tensor max; exponent bookkeeping.
 __global__ __launch_bounds__(256) void downconvert_kernel(const int32_t *__restrict__ acc, int64_t n,
                                                           const uint32_t *__restrict__ absmax,
@@ -279,14 +501,18 @@ __global__ void zero_i32_kernel(int32_t *C, int64_t n) {
         C[i] = 0;
 }
 
-// Gavg: one workgroup sums |g| exactly in int64, then scales in double.
-__global__ __launch_bounds__(1024) void gavg_kernel(const int16_t *__restrict__ g, int64_t n,
-                                                    const int32_t *__restrict__ eg,
-                                                    const int32_t *__restrict__ ew,
-                                                    double *__restrict__ out) {
-    __shared__ int64_t part[16];
+// Gavg in three stream-ordered steps, exact: the output's 8 bytes first hold
+// the int64 sum of |g| (zeroed, then one atomic add per workgroup; integer
+// sums are order-free), then the last step turns the sum into
+// mean(|g|) * 2^(E_g - E_w) as a double.
+__global__ void gavg_zero_kernel(unsigned long long *acc) { *acc = 0ull; }
+
+__global__ __launch_bounds__(256) void gavg_sum_kernel(const int16_t *__restrict__ g, int64_t n,
+                                                       unsigned long long *__restrict__ acc) {
+    __shared__ int64_t part[4];
     int64_t s = 0;
-    for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
+    for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+         i += int64_t(gridDim.x) * blockDim.x) {
         const int32_t v = g[i];
         s += v < 0 ? -v : v;
     }
@@ -294,14 +520,19 @@ __global__ __launch_bounds__(1024) void gavg_kernel(const int16_t *__restrict__ 
     if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = s;
     __syncthreads();
     if (threadIdx.x == 0) {
-        int64_t tot = 0;
-        for (int w = 0; w < int(blockDim.x / 64); ++w) tot += part[w];
-        double v = double(tot) / double(n);
-        int e = *eg - *ew;
-        for (; e > 0; --e) v *= 2.0;
-        for (; e < 0; ++e) v *= 0.5;
-        *out = v;
+        const int64_t tot = part[0] + part[1] + part[2] + part[3];
+        if (tot) atomicAdd(acc, (unsigned long long)tot);
     }
+}
+
+__global__ void gavg_finish_kernel(double *out, int64_t n, const int32_t *__restrict__ eg,
+                                   const int32_t *__restrict__ ew) {
+    const int64_t tot = int64_t(*reinterpret_cast<const unsigned long long *>(out));
+    double v = double(tot) / double(n);
+    int e = *eg - *ew;
+    for (; e > 0; --e) v *= 2.0;
+    for (; e < 0; ++e) v *= 0.5;
+    *out = v;
 }
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -333,6 +564,36 @@ int contract(const Src16 &a, const Src16 &b, int M, int N, int L, int32_t *acc, 
     dim3 grid(tiles, g.split), block(256);
     if (even) dfp16_kernel<128, 128, 2, 2, false><<<grid, block, 0, st>>>(g);
     else dfp16_kernel<128, 128, 2, 2, true><<<grid, block, 0, st>>>(g);
+    if (int rc = check_launch("dfp16 contraction")) return rc;
+    if (g.atomic) return launch_absmax_i32(acc, int64_t(M) * N, absmax, st);
+    return IONN_OK;
+}
+
+// Tile-aligned contraction on the 32x32x32 path: acc[M][N] = sum_c rhu(p_c, r)
+// with A (M rows) and B (N rows) each K-major (element (row, k) at
+// base[row * ld + k]) or M-major (at base[k * ld + row]); reduction length L.
+bool fast2(int M, int N, int L, const void *a, int64_t lda, const void *b, int64_t ldb) {
+    return M % d2::BM == 0 && N % d2::BN == 0 && L % 64 == 0 && aligned(a, 16) && aligned(b, 16) &&
+           lda % 8 == 0 && ldb % 8 == 0;
+}
+
+template <bool A_KM, bool B_KM>
+int contract2(const int16_t *a, int64_t lda, const int16_t *b, int64_t ldb, int M, int N, int L,
+              int32_t *acc, uint32_t *absmax, hipStream_t st) {
+    d2::Args g{a, b, lda, ldb, acc, absmax, M, N, L, chunk_shift(L), 1, false};
+    const int tiles = (M / d2::BM) * (N / d2::BN);
+    const int nch = L / 64;
+    if (tiles < 256 && nch >= 8) {
+        int split = (256 + tiles - 1) / tiles;
+        if (split > nch / 4) split = nch / 4;
+        g.split = split < 1 ? 1 : split;
+    }
+    g.atomic = g.split > 1;
+    if (g.atomic) {
+        zero_i32_kernel<<<dim3(1024), dim3(256), 0, st>>>(acc, int64_t(M) * N);
+        if (int rc = check_launch("dfp16 contraction")) return rc;
+    }
+    d2::dfp_kernel<A_KM, B_KM><<<dim3(tiles, g.split), dim3(d2::NT), 0, st>>>(g);
     if (int rc = check_launch("dfp16 contraction")) return rc;
     if (g.atomic) return launch_absmax_i32(acc, int64_t(M) * N, absmax, st);
     return IONN_OK;
@@ -423,6 +684,10 @@ int dfp16_gemm_fwd(const int16_t *X, const int32_t *eX, const int16_t *W, const 
     Workspace w;
     ws_bytes(M, K, N, IONN_DFP16_FWD, &w, workspace);
     zero_i32_kernel<<<dim3(1), dim3(64), 0, st>>>(reinterpret_cast<int32_t *>(w.absmax), 1);
+    if (fast2(int(M), int(N), int(K), X, K, W, K)) {
+        if (int rc = contract2<true, true>(X, K, W, K, int(M), int(N), int(K), w.acc, w.absmax, st)) return rc;
+        return finish(w, M * N, eX, eW, chunk_shift(K), Y, eY, status_out, st);
+    }
     Src16 a{X, K, int(M), int(K), aligned(X, 16) && K % 8 == 0};
     Src16 b{W, K, int(N), int(K), aligned(W, 16) && K % 8 == 0};
     if (int rc = contract(a, b, int(M), int(N), int(K), w.acc, w.absmax, st)) return rc;
@@ -440,6 +705,10 @@ int dfp16_gemm_dgrad(const int16_t *dY, const int32_t *edY, const int16_t *W, co
     Workspace w;
     ws_bytes(M, K, N, IONN_DFP16_DGRAD, &w, workspace);
     zero_i32_kernel<<<dim3(1), dim3(64), 0, st>>>(reinterpret_cast<int32_t *>(w.absmax), 1);
+    if (fast2(int(M), int(K), int(N), dY, N, W, K)) {  // B = W seen M-major: (k, n) at W[n * K + k]
+        if (int rc = contract2<true, false>(dY, N, W, K, int(M), int(K), int(N), w.acc, w.absmax, st)) return rc;
+        return finish(w, M * K, edY, eW, chunk_shift(N), dX, edX, status_out, st);
+    }
     if (int rc = transpose16(W, w.t0, int(N), int(K), st)) return rc;  // W^T [K][N]
     Src16 a{dY, N, int(M), int(N), aligned(dY, 16) && N % 8 == 0};
     Src16 b{w.t0, N, int(K), int(N), N % 8 == 0};
@@ -458,6 +727,10 @@ int dfp16_gemm_wgrad(const int16_t *dY, const int32_t *edY, const int16_t *X, co
     Workspace w;
     ws_bytes(M, K, N, IONN_DFP16_WGRAD, &w, workspace);
     zero_i32_kernel<<<dim3(1), dim3(64), 0, st>>>(reinterpret_cast<int32_t *>(w.absmax), 1);
+    if (fast2(int(N), int(K), int(M), dY, N, X, K)) {  // A = dY, B = X, both M-major over m
+        if (int rc = contract2<false, false>(dY, N, X, K, int(N), int(K), int(M), w.acc, w.absmax, st)) return rc;
+        return finish(w, N * K, edY, eX, chunk_shift(M), G, eG, status_out, st);
+    }
     if (int rc = transpose16(dY, w.t0, int(M), int(N), st)) return rc;  // dY^T [N][M]
     if (int rc = transpose16(X, w.t1, int(M), int(K), st)) return rc;   // X^T  [K][M]
     Src16 a{w.t0, M, int(N), int(M), M % 8 == 0};
@@ -473,7 +746,13 @@ int dfp16_gavg(const int16_t *G, const int32_t *eG, const int32_t *eW, int64_t n
     IONN_REQUIRE(G && eG && eW && gavg_out, IONN_ERR_ARG, "dfp16_gavg: NULL argument");
     IONN_REQUIRE(aligned(G, 2) && aligned(eG, 4) && aligned(eW, 4) && aligned(gavg_out, 8),
                  IONN_ERR_ALIGN, "dfp16_gavg: misaligned pointer");
-    gavg_kernel<<<dim3(1), dim3(1024), 0, as_stream(stream)>>>(G, n, eG, eW, gavg_out);
+    hipStream_t st = as_stream(stream);
+    unsigned long long *acc = reinterpret_cast<unsigned long long *>(gavg_out);
+    gavg_zero_kernel<<<dim3(1), dim3(1), 0, st>>>(acc);
+    int64_t blocks = (n + 256 * 8 - 1) / (256 * 8);
+    if (blocks > 1024) blocks = 1024;
+    gavg_sum_kernel<<<dim3(unsigned(blocks)), dim3(256), 0, st>>>(G, n, acc);
+    gavg_finish_kernel<<<dim3(1), dim3(1), 0, st>>>(gavg_out, n, eG, eW);
     return check_launch("dfp16_gavg");
 }
 

@@ -27,6 +27,7 @@ def _run(d, M, K, N):
 
 
 @pytest.mark.parametrize("M,K,N", [(1, 1, 1), (3, 64, 5), (17, 40, 9), (128, 128, 128), (200, 256, 136),
+                                   (128, 64, 128), (640, 128, 384), (1024, 384, 128),
                                    (256, 320, 1024), (1000, 64, 48), (4096, 256, 256)])
 def test_dfp16_step_vs_oracle(M, K, N):
     say("dfp16", M, K, N)
@@ -54,9 +55,11 @@ def test_dfp16_golden_chunk_case():
     assert host(Y)[:, 0].tolist() == [32000, 6] and int(host(eY)[0]) == -20
 
 
-def test_dfp16_extreme_mantissas():
-    """Values at +-32767 / -32768 exercise the high-digit range of the split."""
-    M, K, N = 64, 192, 32
+@pytest.mark.parametrize("M,K,N", [(64, 192, 32), (256, 128, 128)])
+def test_dfp16_extreme_mantissas(M, K, N):
+    """Values at +-32767 / -32768 exercise the high-digit range of the split
+    (the second shape takes the tile-aligned 32x32x32 path in all three
+    contractions, the first the general one)."""
     rng = np.random.default_rng(3)
     pick = np.array([-32768, -32767, 32767, 32640, 32639, -129, -128, 127, 128, 0, 1, -1], np.int16)
     X = pick[rng.integers(0, len(pick), (M, K))]
