@@ -31,6 +31,7 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 PEAK_INT8_TOPS = 5000.0     # MI355X dense int8 matrix peak (5.0 POP/s)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PEAK_VALU_TOPS = 39.32      # 256 CUs x 4 SIMDs x 16 int32 lane-ops per cycle x 2.4 GHz
 T, IN, OUT = 8192, 4096, 4096
 
 
@@ -140,38 +141,83 @@ def bench_linear(torch, steps_mod, args):
     return ms, per, ms_req, shifts, ms_instr
 
 
+def _timed(torch, step, nsteps):
+    """Step time over nsteps (one event pair) and per-launch averages from a
+    second, event-bracketed run."""
+    for _ in range(5):
+        step(None)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(nsteps):
+        step(None)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / nsteps
+    tm = Timer(torch)
+    for _ in range(nsteps):
+        step(tm)
+    tm.mark(None)
+    torch.cuda.synchronize()
+    return ms, {k: float(np.mean(v)) for k, v in tm.per_name().items()}
+
+
 def bench_conv(torch, steps_mod, nsteps):
+    """The 128x56x56, 64 -> 64 channel conv NITI step, launch by launch as
+    steps.conv_step runs it."""
     import ionn_synth
+    from integer_only_nn_amd import ops
     dev = torch.device("cuda:0")
     d = ionn_synth.conv3x3()
     X, Wt, dY = (torch.from_numpy(d[k]).to(dev) for k in ("X", "W", "dY"))
     buf = steps_mod.ConvStepBuffers.make(128, 56, 56, 64, 64, dev)
-    for _ in range(3):
-        steps_mod.conv_step(X, Wt, dY, buf)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(nsteps):
-        steps_mod.conv_step(X, Wt, dY, buf)
-    torch.cuda.synchronize()
-    return (time.perf_counter() - t0) * 1e3 / nsteps
+    desc = ops.conv_desc(128, 56, 56, 64, 64)
+    s = buf.scal
+
+    def step(tm):
+        m = tm.mark if tm else (lambda n: None)
+        m("fill")
+        ops.ionn_fill_u32(s[0:3], 0)
+        m("fwd")
+        ops.int_conv_fwd(X, Wt, buf.Y, desc, absmax_Y=s[0:1])
+        m("requant_y")
+        ops.niti_quantize(buf.Y, s[0:1], 7, False, buf.y8, shift_out=s[3:4])
+        m("dgrad")
+        ops.int_conv_dgrad(dY, Wt, buf.dX, desc, absmax_dX=s[1:2])
+        m("requant_dx")
+        ops.niti_quantize(buf.dX, s[1:2], 7, False, buf.dx8, shift_out=s[4:5])
+        m("wgrad")
+        ops.int_conv_wgrad(dY, X, buf.G, desc, absmax_G=s[2:3], workspace=buf.ws)
+        m("update")
+        ops.niti_quantize_update(buf.G, s[2:3], 8, 2, Wt, shifts_out=s[5:7])
+    return _timed(torch, step, nsteps)
 
 
 def bench_dfp16(torch, steps_mod, nsteps):
+    """The DFP-16 step (fwd, dgrad, wgrad contractions with down-conversion,
+    then Gavg) on M=25088 K=256 N=1024."""
     import ionn_synth
+    from integer_only_nn_amd import ops
     dev = torch.device("cuda:0")
     d = ionn_synth.dfp16_gemm()
     X, W, dY = (torch.from_numpy(d[k]).to(dev) for k in ("X", "W", "dY"))
     e = lambda v: torch.tensor([v], dtype=torch.int32, device=dev)
     eX, eW, edY = e(d["eX"]), e(d["eW"]), e(d["edY"])
     buf = steps_mod.DfpStepBuffers.make(25088, 256, 1024, dev)
-    for _ in range(3):
-        steps_mod.dfp16_step(X, eX, W, eW, dY, edY, buf)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(nsteps):
-        steps_mod.dfp16_step(X, eX, W, eW, dY, edY, buf)
-    torch.cuda.synchronize()
-    return (time.perf_counter() - t0) * 1e3 / nsteps
+    ex = buf.exps
+
+    def step(tm):
+        m = tm.mark if tm else (lambda n: None)
+        m("fwd")
+        ops.dfp16_gemm_fwd(X, eX, W, eW, buf.Y, ex[0:1], buf.ws, status_out=ex[3:4])
+        m("dgrad")
+        ops.dfp16_gemm_dgrad(dY, edY, W, eW, buf.dX, ex[1:2], buf.ws, status_out=ex[4:5])
+        m("wgrad")
+        ops.dfp16_gemm_wgrad(dY, edY, X, eX, buf.G, ex[2:3], buf.ws, status_out=ex[5:6])
+        m("gavg")
+        ops.dfp16_gavg(buf.G, ex[2:3], eW, buf.gavg)
+    return _timed(torch, step, nsteps)
 
 
 def _kernel_source_hash():
@@ -284,17 +330,38 @@ def main():
                                  "bytes": 256 << 20}
     if not args.no_secondary:
         log("secondary: conv and DFP-16 steps")
-        c_ms = bench_conv(torch, steps_mod, 10)
-        f_ms = bench_dfp16(torch, steps_mod, 10)
+        c_ms, c_per = bench_conv(torch, steps_mod, 20)
+        f_ms, f_per = bench_dfp16(torch, steps_mod, 20)
         conv_ops = 3 * 2.0 * 128 * 56 * 56 * 64 * 9 * 64
         dfp_ops = 3 * 2.0 * 25088 * 256 * 1024
+        # conv contractions are HBM-bound: int8 image in, int32 result out
+        img = 128 * 56 * 56 * 64
+        conv_bytes = {"fwd": img + 4 * img, "dgrad": img + 4 * img, "wgrad": 2 * img + 4 * 64 * 9 * 64}
+        cdom = max(conv_bytes, key=lambda k: c_per[k])
+        cgbs = conv_bytes[cdom] / (c_per[cdom] * 1e-3) / 1e9
+        # DFP-16 contractions are VALU-bound: 6 int32 operations per output
+        # element per 64-term chunk (digit combination, rounding shift, add)
+        dfp_alu = {"fwd": 6.0 * 25088 * 1024 * (256 // 64), "dgrad": 6.0 * 25088 * 256 * (1024 // 64),
+                   "wgrad": 6.0 * 1024 * 256 * (25088 // 64)}
+        fdom = max(dfp_alu, key=lambda k: f_per[k])
+        falu = dfp_alu[fdom] / (f_per[fdom] * 1e-3) / 1e12
         result["secondary"] = {
             "conv3x3_step": {"shape": "N128 56x56 64->64 NHWC", "ms_per_step": round(c_ms, 4),
                              "TOPS": round(conv_ops / (c_ms * 1e-3) / 1e12, 2),
-                             "images_per_s": round(128 / (c_ms * 1e-3), 1)},
+                             "images_per_s": round(128 / (c_ms * 1e-3), 1),
+                             "kernel_ms": {k: round(v, 4) for k, v in c_per.items()},
+                             "roofline": {"bound": "hbm", "kernel": f"int_conv_{cdom}",
+                                          "achieved": round(cgbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                          "frac": round(cgbs / PEAK_HBM_GBS, 4),
+                                          "bytes_per_launch": conv_bytes[cdom]}},
             "dfp16_step": {"shape": "M25088 K256 N1024", "ms_per_step": round(f_ms, 4),
                            "int16_TOPS": round(dfp_ops / (f_ms * 1e-3) / 1e12, 2),
-                           "images_per_s": round(128 / (f_ms * 1e-3), 1)},
+                           "images_per_s": round(128 / (f_ms * 1e-3), 1),
+                           "kernel_ms": {k: round(v, 4) for k, v in f_per.items()},
+                           "roofline": {"bound": "alu", "kernel": f"dfp16_gemm_{fdom}",
+                                        "achieved": round(falu, 2), "peak": PEAK_VALU_TOPS,
+                                        "unit": "T int32 op/s", "frac": round(falu / PEAK_VALU_TOPS, 4),
+                                        "ops_per_launch": dfp_alu[fdom]}},
         }
     if not args.no_cpu_baseline:
         log("cpu baseline: oracle on a bounded sample")
