@@ -256,7 +256,7 @@ __global__ __launch_bounds__(WGM *WGN * 64) void dfp16_kernel(DfpArgs g) {
 namespace d2 {
 
 typedef int v2i __attribute__((ext_vector_type(2)));
-constexpr int BM = 128, BN = 128, NT = 256;
+constexpr int BM = 128, BN = 128, NT = 512;  // 8 wavefronts, 2 per SIMD
 constexpr int KP = 80;            // K-major plane: bytes per row
 constexpr int MP = 128 + 16;      // M-major plane: bytes per k-row
 constexpr int PLANE = 128 * KP;   // >= 64 * MP
@@ -271,10 +271,11 @@ __device__ __forceinline__ uint32_t lo4(uint32_t w0, uint32_t w1) {
 // One operand tile (128 rows x 64 k of int16) global -> registers -> digit planes.
 template <bool KM>
 struct Ld {
-    v4i reg[4];
+    static constexpr int IT = 128 * 64 / 8 / NT;  // 16-byte chunks per thread
+    v4i reg[IT];
     __device__ __forceinline__ void load(const int16_t *base, int64_t ld, int r0, int k0, int tid) {
 #pragma unroll
-        for (int it = 0; it < 4; ++it) {
+        for (int it = 0; it < IT; ++it) {
             const int id = it * NT + tid;
             const int16_t *p = KM ? base + int64_t(r0 + (id >> 3)) * ld + k0 + 8 * (id & 7)
                                   : base + int64_t(k0 + (id >> 4)) * ld + r0 + 8 * (id & 15);
@@ -283,7 +284,7 @@ struct Ld {
     }
     __device__ __forceinline__ void store(int8_t *hi, int8_t *lo, int tid) const {
 #pragma unroll
-        for (int it = 0; it < 4; ++it) {
+        for (int it = 0; it < IT; ++it) {
             const int id = it * NT + tid;
             const int off = KM ? (id >> 3) * KP + 8 * (id & 7) : (id >> 4) * MP + 8 * (id & 15);
             const uint32_t w0 = reg[it].x, w1 = reg[it].y, w2 = reg[it].z, w3 = reg[it].w;
@@ -317,139 +318,165 @@ __device__ __forceinline__ int32_t dot16(v4i f) {  // sum of the 16 signed bytes
 struct Args {
     const int16_t *a, *b;
     int64_t lda, ldb;
-    int32_t *acc;        // [M][N]
-    uint32_t *absmax;    // max-combined (non-atomic epilogue)
+    int32_t *acc;        // [M][N] (split == 1) or split partial tiles [split][M][N]
+    uint32_t *absmax;    // max-combined (split == 1)
     int M, N, L, r, split;
-    bool atomic;
 };
 
+// Persistent: workgroup w takes work units w, w + gridDim.x, ...; a unit is
+// one output tile and one range of chunks (a K split).  The chunk loop runs
+// across unit boundaries, so the first chunk of the next unit is loaded while
+// the last chunk of the current one computes and its result is stored.
 template <bool A_KM, bool B_KM>
 __global__ __launch_bounds__(NT, 1) void dfp_kernel(Args g) {
     __shared__ __attribute__((aligned(16))) int8_t lds[2 * STAGE];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave >> 1, wn = wave & 1;  // 32-row block wm of 4, 64-column half wn of 2
     const int tiles_n = g.N / BN;
-    const int tm = blockIdx.x / tiles_n, tn = blockIdx.x - tm * tiles_n;
-    const int m0 = tm * BM, n0 = tn * BN;
+    const int ntiles = (g.M / BM) * tiles_n;
+    const int nunits = ntiles * g.split;
     const int nch = g.L / 64;
-    const int c0 = int(int64_t(nch) * blockIdx.y / g.split);
-    const int c1 = int(int64_t(nch) * (blockIdx.y + 1) / g.split);
+
+    // unit u -> tile origin and chunk range
+    auto unit = [&](int u, int &m0, int &n0, int &c0, int &c1) __attribute__((always_inline)) {
+        const int t = u % ntiles, sp = u / ntiles;
+        const int tm = t / tiles_n;
+        m0 = tm * BM;
+        n0 = (t - tm * tiles_n) * BN;
+        c0 = int(int64_t(nch) * sp / g.split);
+        c1 = int(int64_t(nch) * (sp + 1) / g.split);
+    };
+
+    int u = blockIdx.x;
+    if (u >= nunits) return;
+    int m0, n0, c0, c1;
+    unit(u, m0, n0, c0, c1);
 
     Ld<A_KM> la;
     Ld<B_KM> lb;
-    v16i acc[2][2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = v16i{};
+    v16i acc[2];
+    acc[0] = v16i{};
+    acc[1] = v16i{};
+    uint32_t amax = 0;
 
-    if (c0 < c1) {
-        la.load(g.a, g.lda, m0, 64 * c0, tid);
-        lb.load(g.b, g.ldb, n0, 64 * c0, tid);
-        la.store(lds, lds + PLANE, tid);
-        lb.store(lds + 2 * PLANE, lds + 3 * PLANE, tid);
-    }
+    la.load(g.a, g.lda, m0, 64 * c0, tid);
+    lb.load(g.b, g.ldb, n0, 64 * c0, tid);
+    la.store(lds, lds + PLANE, tid);
+    lb.store(lds + 2 * PLANE, lds + 3 * PLANE, tid);
     __syncthreads();
 
     const v4i ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
     const v16i zero16 = {};
     const int r = g.r;
     const uint32_t rm1 = r > 0 ? r - 1 : 0, rw = r > 0 ? 1 : 0;  // rounding bit (none for r = 0)
-    for (int c = c0; c < c1; ++c) {
-        const int8_t *st = lds + ((c - c0) & 1) * STAGE;
-        if (c + 1 < c1) {
-            la.load(g.a, g.lda, m0, 64 * (c + 1), tid);
-            lb.load(g.b, g.ldb, n0, 64 * (c + 1), tid);
+    int c = c0, stage = 0;
+    while (true) {
+        // the work item after (u, c)
+        int nu = u, nm0 = m0, nn0 = n0, nc = c + 1, nc1 = c1;
+        bool more = true;
+        if (nc >= c1) {
+            nu = u + gridDim.x;
+            more = nu < nunits;
+            if (more) unit(nu, nm0, nn0, nc, nc1);
         }
-        v4i ah[2][2], al[2][2], bh[2][2], bl[2][2];
-#pragma unroll
-        for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                ah[i][kh] = frag<A_KM>(st, wm * 64 + 32 * i, kh, lane);
-                al[i][kh] = frag<A_KM>(st + PLANE, wm * 64 + 32 * i, kh, lane);
-                bh[i][kh] = frag<B_KM>(st + 2 * PLANE, wn * 64 + 32 * i, kh, lane);
-                bl[i][kh] = frag<B_KM>(st + 3 * PLANE, wn * 64 + 32 * i, kh, lane);
-            }
-        // 128 * sum(B') over the chunk for the 16 columns of each block; it
-        // seeds the low-digit MFMA chain, which then adds it for free
-        v16i ct[2];
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            v16i sh = __builtin_amdgcn_mfma_i32_32x32x32_i8(bh[j][0], ones, zero16, 0, 0, 0);
-            sh = __builtin_amdgcn_mfma_i32_32x32x32_i8(bh[j][1], ones, sh, 0, 0, 0);
-            v16i sl = __builtin_amdgcn_mfma_i32_32x32x32_i8(bl[j][0], ones, zero16, 0, 0, 0);
-            sl = __builtin_amdgcn_mfma_i32_32x32x32_i8(bl[j][1], ones, sl, 0, 0, 0);
-#pragma unroll
-            for (int v = 0; v < 16; ++v) ct[j][v] = int32_t((uint32_t(sh[v]) << 15) + (uint32_t(sl[v]) << 7));
+        if (more) {
+            la.load(g.a, g.lda, nm0, 64 * nc, tid);
+            lb.load(g.b, g.ldb, nn0, 64 * nc, tid);
         }
-        // 128 * sum(A') over the chunk + 2^20 for this lane's row of each block
-        // (lanes l and l + 32 hold the two 16-term halves of a row's k range)
-        uint32_t rt[2];
+        const int8_t *st = lds + stage * STAGE;
+        v4i ah[2], al[2], bh[2][2], bl[2][2];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            int32_t sh = dot16(ah[i][0]) + dot16(ah[i][1]);
-            int32_t sl = dot16(al[i][0]) + dot16(al[i][1]);
-            sh += __shfl_xor(sh, 32, 64);
-            sl += __shfl_xor(sl, 32, 64);
-            rt[i] = (uint32_t(sh) << 15) + (uint32_t(sl) << 7) + (1u << 20);
-        }
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int kh = 0; kh < 2; ++kh) {
+            ah[kh] = frag<A_KM>(st, 32 * wm, kh, lane);
+            al[kh] = frag<A_KM>(st + PLANE, 32 * wm, kh, lane);
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
-                v16i hh = __builtin_amdgcn_mfma_i32_32x32x32_i8(bh[j][0], ah[i][0], zero16, 0, 0, 0);
-                hh = __builtin_amdgcn_mfma_i32_32x32x32_i8(bh[j][1], ah[i][1], hh, 0, 0, 0);
-                v16i x = __builtin_amdgcn_mfma_i32_32x32x32_i8(bl[j][0], ah[i][0], zero16, 0, 0, 0);
-                x = __builtin_amdgcn_mfma_i32_32x32x32_i8(bh[j][0], al[i][0], x, 0, 0, 0);
-                x = __builtin_amdgcn_mfma_i32_32x32x32_i8(bl[j][1], ah[i][1], x, 0, 0, 0);
-                x = __builtin_amdgcn_mfma_i32_32x32x32_i8(bh[j][1], al[i][1], x, 0, 0, 0);
-                v16i ll = __builtin_amdgcn_mfma_i32_32x32x32_i8(bl[j][0], al[i][0], ct[j], 0, 0, 0);
-                ll = __builtin_amdgcn_mfma_i32_32x32x32_i8(bl[j][1], al[i][1], ll, 0, 0, 0);
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    // p mod 2^32, then acc += rhu(p, r) = (p >> r) + bit (r - 1) of p
-                    const uint32_t p = (uint32_t(hh[v]) << 16) + ((uint32_t(x[v]) << 8) + uint32_t(ll[v])) + rt[i];
-                    acc[i][j][v] = int32_t(uint32_t(acc[i][j][v]) + uint32_t(int32_t(p) >> r) +
-                                           __builtin_amdgcn_ubfe(p, rm1, rw));
-                }
+                bh[j][kh] = frag<B_KM>(st + 2 * PLANE, 64 * wn + 32 * j, kh, lane);
+                bl[j][kh] = frag<B_KM>(st + 3 * PLANE, 64 * wn + 32 * j, kh, lane);
             }
-        if (c + 1 < c1) {
-            int8_t *nx = lds + ((c + 1 - c0) & 1) * STAGE;
-            la.store(nx, nx + PLANE, tid);
-            lb.store(nx + 2 * PLANE, nx + 3 * PLANE, tid);
         }
-        __syncthreads();
-    }
-
-    // lane holds acc[m][n .. n+3] for m = block row lane % 32,
-    // n = block col 8 q + 4 (lane / 32)
-    uint32_t amax = 0;
+        // 128 * sum(A') over the chunk + 2^20 for this lane's row (lanes l and
+        // l + 32 hold the two 16-term halves of a row's k range)
+        int32_t sah = dot16(ah[0]) + dot16(ah[1]);
+        int32_t sal = dot16(al[0]) + dot16(al[1]);
+        sah += __shfl_xor(sah, 32, 64);
+        sal += __shfl_xor(sal, 32, 64);
+        const uint32_t rt = (uint32_t(sah) << 15) + (uint32_t(sal) << 7) + (1u << 20);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int m = m0 + wm * 64 + 32 * i + (lane & 31);
+        for (int j = 0; j < 2; ++j) {
+            // 128 * sum(B') for the block's 16 columns of this lane; it seeds
+            // the low-digit chain, which then adds it for free
+            v16i sh = __builtin_amdgcn_mfma_i32_32x32x32_i8(bh[j][0], ones, zero16, 0, 0, 0);
+            sh = __builtin_amdgcn_mfma_i32_32x32x32_i8(bh[j][1], ones, sh, 0, 0, 0);
+            v16i ll = __builtin_amdgcn_mfma_i32_32x32x32_i8(bl[j][0], ones, zero16, 0, 0, 0);
+            ll = __builtin_amdgcn_mfma_i32_32x32x32_i8(bl[j][1], ones, ll, 0, 0, 0);
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+            for (int v = 0; v < 16; ++v) ll[v] = int32_t(((uint32_t(sh[v]) << 8) + uint32_t(ll[v])) << 7);
+            v16i hh = __builtin_amdgcn_mfma_i32_32x32x32_i8(bh[j][0], ah[0], zero16, 0, 0, 0);
+            hh = __builtin_amdgcn_mfma_i32_32x32x32_i8(bh[j][1], ah[1], hh, 0, 0, 0);
+            v16i x = __builtin_amdgcn_mfma_i32_32x32x32_i8(bl[j][0], ah[0], zero16, 0, 0, 0);
+            x = __builtin_amdgcn_mfma_i32_32x32x32_i8(bh[j][0], al[0], x, 0, 0, 0);
+            x = __builtin_amdgcn_mfma_i32_32x32x32_i8(bl[j][1], ah[1], x, 0, 0, 0);
+            x = __builtin_amdgcn_mfma_i32_32x32x32_i8(bh[j][1], al[1], x, 0, 0, 0);
+            ll = __builtin_amdgcn_mfma_i32_32x32x32_i8(bl[j][0], al[0], ll, 0, 0, 0);
+            ll = __builtin_amdgcn_mfma_i32_32x32x32_i8(bl[j][1], al[1], ll, 0, 0, 0);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int n = n0 + wn * 64 + 32 * j + 8 * q + 4 * (lane >> 5);
-                int32_t *cp = g.acc + int64_t(m) * g.N + n;
-                const v4i v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-                if (g.atomic) {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) atomicAdd(cp + e, v[e]);
-                } else {
-                    *reinterpret_cast<v4i *>(cp) = v;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) amax = max(amax, abs_u32(v[e]));
-                }
+            for (int v = 0; v < 16; ++v) {
+                // p mod 2^32, then acc += rhu(p, r) = (p >> r) + bit (r - 1) of p
+                const uint32_t p = (uint32_t(hh[v]) << 16) + ((uint32_t(x[v]) << 8) + uint32_t(ll[v])) + rt;
+                acc[j][v] = int32_t(uint32_t(acc[j][v]) + uint32_t(int32_t(p) >> r) +
+                                    __builtin_amdgcn_ubfe(p, rm1, rw));
             }
+        }
+
+        if (c + 1 >= c1) {
+            // unit done: lane holds acc[m][n .. n+3] for m = row lane % 32 of the
+            // wave's block, n = block col 8 q + 4 (lane / 32)
+            const int m = m0 + 32 * wm + (lane & 31);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int n = n0 + 64 * wn + 32 * j + 8 * q + 4 * (lane >> 5);
+                    int32_t *cp = g.acc + (int64_t(u / ntiles) * g.M + m) * g.N + n;
+                    const v4i v = {acc[j][4 * q], acc[j][4 * q + 1], acc[j][4 * q + 2], acc[j][4 * q + 3]};
+                    *reinterpret_cast<v4i *>(cp) = v;
+                    if (g.split == 1) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) amax = max(amax, abs_u32(v[e]));
+                    }
+                }
+                acc[j] = v16i{};
+            }
+        }
+        if (!more) break;
+        int8_t *nx = lds + (stage ^ 1) * STAGE;
+        la.store(nx, nx + PLANE, tid);
+        lb.store(nx + 2 * PLANE, nx + 3 * PLANE, tid);
+        __syncthreads();
+        u = nu; m0 = nm0; n0 = nn0; c = nc; c1 = nc1; stage ^= 1;
     }
-    if (!g.atomic && g.absmax) {
+    if (g.split == 1 && g.absmax) {
         amax = wave_max_u32(amax);
         if (lane == 0 && amax != 0) atomicMax(g.absmax, amax);
     }
+}
+
+// acc[e] = sum over the split partial tiles (modulo 2^32), with the max |acc|.
+__global__ __launch_bounds__(256) void split_reduce(const int32_t *__restrict__ part, int split, int64_t n,
+                                                    int32_t *__restrict__ acc, uint32_t *__restrict__ absmax) {
+    typedef unsigned v4u __attribute__((ext_vector_type(4)));
+    uint32_t amax = 0;
+    for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; 4 * i < n; i += int64_t(gridDim.x) * blockDim.x) {
+        v4u s = {0, 0, 0, 0};
+        for (int p = 0; p < split; ++p) s += *reinterpret_cast<const v4u *>(part + int64_t(p) * n + 4 * i);
+        *reinterpret_cast<v4u *>(acc + 4 * i) = s;
+        amax = max(max(amax, max(abs_u32(int32_t(s.x)), abs_u32(int32_t(s.y)))),
+                   max(abs_u32(int32_t(s.z)), abs_u32(int32_t(s.w))));
+    }
+    amax = wave_max_u32(amax);
+    if ((threadIdx.x & 63) == 0 && amax != 0) atomicMax(absmax, amax);
 }
 
 }  // namespace d2
@@ -577,25 +604,38 @@ bool fast2(int M, int N, int L, const void *a, int64_t lda, const void *b, int64
            lda % 8 == 0 && ldb % 8 == 0;
 }
 
+// K splits of the tile-aligned path: enough work units to cover 256 compute
+// units when the output has few tiles, at least 4 chunks per unit.
+int split2(int64_t M, int64_t N, int64_t L) {
+    if (M % d2::BM || N % d2::BN || L % 64 || M < 1 || N < 1 || L < 1) return 1;
+    const int64_t tiles = (M / d2::BM) * (N / d2::BN), nch = L / 64;
+    if (tiles >= 256 || nch < 8) return 1;
+    int64_t split = (256 + tiles - 1) / tiles;
+    if (split > nch / 4) split = nch / 4;
+    return split < 1 ? 1 : int(split);
+}
+
 template <bool A_KM, bool B_KM>
 int contract2(const int16_t *a, int64_t lda, const int16_t *b, int64_t ldb, int M, int N, int L,
-              int32_t *acc, uint32_t *absmax, hipStream_t st) {
-    d2::Args g{a, b, lda, ldb, acc, absmax, M, N, L, chunk_shift(L), 1, false};
+              int32_t *acc, int32_t *part, uint32_t *absmax, hipStream_t st) {
+    const int split = split2(M, N, L);
+    d2::Args g{a, b, lda, ldb, split > 1 ? part : acc, absmax, M, N, L, chunk_shift(L), split};
     const int tiles = (M / d2::BM) * (N / d2::BN);
-    const int nch = L / 64;
-    if (tiles < 256 && nch >= 8) {
-        int split = (256 + tiles - 1) / tiles;
-        if (split > nch / 4) split = nch / 4;
-        g.split = split < 1 ? 1 : split;
-    }
-    g.atomic = g.split > 1;
-    if (g.atomic) {
-        zero_i32_kernel<<<dim3(1024), dim3(256), 0, st>>>(acc, int64_t(M) * N);
-        if (int rc = check_launch("dfp16 contraction")) return rc;
-    }
-    d2::dfp_kernel<A_KM, B_KM><<<dim3(tiles, g.split), dim3(d2::NT), 0, st>>>(g);
+    int cus = 256;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+        cus = 256;
+    const int units = tiles * split;
+    d2::dfp_kernel<A_KM, B_KM><<<dim3(units < cus ? units : cus), dim3(d2::NT), 0, st>>>(g);
     if (int rc = check_launch("dfp16 contraction")) return rc;
-    if (g.atomic) return launch_absmax_i32(acc, int64_t(M) * N, absmax, st);
+    if (split > 1) {
+        const int64_t n = int64_t(M) * N;
+        int64_t blocks = (n / 4 + 255) / 256;
+        if (blocks > 2048) blocks = 2048;
+        d2::split_reduce<<<dim3(unsigned(blocks)), dim3(256), 0, st>>>(part, split, n, acc, absmax);
+        return check_launch("dfp16 contraction");
+    }
     return IONN_OK;
 }
 
@@ -603,6 +643,7 @@ struct Workspace {
     int32_t *acc;
     uint32_t *absmax;
     int16_t *t0, *t1;
+    int32_t *part;  // split partial tiles of the tile-aligned path
 };
 
 size_t ws_bytes(int64_t M, int64_t K, int64_t N, int which, Workspace *w, void *base) {
@@ -615,6 +656,9 @@ size_t ws_bytes(int64_t M, int64_t K, int64_t N, int which, Workspace *w, void *
     };
     char *acc = take(size_t(out) * 4);
     char *am = take(4);
+    const int split = which == IONN_DFP16_FWD ? split2(M, N, K) : which == IONN_DFP16_DGRAD ? split2(M, K, N)
+                                                                                           : split2(N, K, M);
+    char *part = split > 1 ? take(size_t(split) * out * 4) : nullptr;
     char *t0 = nullptr, *t1 = nullptr;
     if (which == IONN_DFP16_DGRAD) t0 = take(size_t(N) * K * 2);           // W^T [K][N]
     if (which == IONN_DFP16_WGRAD) {
@@ -622,7 +666,8 @@ size_t ws_bytes(int64_t M, int64_t K, int64_t N, int which, Workspace *w, void *
         t1 = take(size_t(K) * M * 2);                                        // X^T  [K][M]
     }
     if (w) *w = Workspace{reinterpret_cast<int32_t *>(acc), reinterpret_cast<uint32_t *>(am),
-                          reinterpret_cast<int16_t *>(t0), reinterpret_cast<int16_t *>(t1)};
+                          reinterpret_cast<int16_t *>(t0), reinterpret_cast<int16_t *>(t1),
+                          reinterpret_cast<int32_t *>(part)};
     return off;
 }
 
@@ -685,7 +730,7 @@ int dfp16_gemm_fwd(const int16_t *X, const int32_t *eX, const int16_t *W, const 
     ws_bytes(M, K, N, IONN_DFP16_FWD, &w, workspace);
     zero_i32_kernel<<<dim3(1), dim3(64), 0, st>>>(reinterpret_cast<int32_t *>(w.absmax), 1);
     if (fast2(int(M), int(N), int(K), X, K, W, K)) {
-        if (int rc = contract2<true, true>(X, K, W, K, int(M), int(N), int(K), w.acc, w.absmax, st)) return rc;
+        if (int rc = contract2<true, true>(X, K, W, K, int(M), int(N), int(K), w.acc, w.part, w.absmax, st)) return rc;
         return finish(w, M * N, eX, eW, chunk_shift(K), Y, eY, status_out, st);
     }
     Src16 a{X, K, int(M), int(K), aligned(X, 16) && K % 8 == 0};
@@ -706,7 +751,7 @@ int dfp16_gemm_dgrad(const int16_t *dY, const int32_t *edY, const int16_t *W, co
     ws_bytes(M, K, N, IONN_DFP16_DGRAD, &w, workspace);
     zero_i32_kernel<<<dim3(1), dim3(64), 0, st>>>(reinterpret_cast<int32_t *>(w.absmax), 1);
     if (fast2(int(M), int(K), int(N), dY, N, W, K)) {  // B = W seen M-major: (k, n) at W[n * K + k]
-        if (int rc = contract2<true, false>(dY, N, W, K, int(M), int(K), int(N), w.acc, w.absmax, st)) return rc;
+        if (int rc = contract2<true, false>(dY, N, W, K, int(M), int(K), int(N), w.acc, w.part, w.absmax, st)) return rc;
         return finish(w, M * K, edY, eW, chunk_shift(N), dX, edX, status_out, st);
     }
     if (int rc = transpose16(W, w.t0, int(N), int(K), st)) return rc;  // W^T [K][N]
@@ -728,7 +773,7 @@ int dfp16_gemm_wgrad(const int16_t *dY, const int32_t *edY, const int16_t *X, co
     ws_bytes(M, K, N, IONN_DFP16_WGRAD, &w, workspace);
     zero_i32_kernel<<<dim3(1), dim3(64), 0, st>>>(reinterpret_cast<int32_t *>(w.absmax), 1);
     if (fast2(int(N), int(K), int(M), dY, N, X, K)) {  // A = dY, B = X, both M-major over m
-        if (int rc = contract2<false, false>(dY, N, X, K, int(N), int(K), int(M), w.acc, w.absmax, st)) return rc;
+        if (int rc = contract2<false, false>(dY, N, X, K, int(N), int(K), int(M), w.acc, w.part, w.absmax, st)) return rc;
         return finish(w, N * K, edY, eX, chunk_shift(M), G, eG, status_out, st);
     }
     if (int rc = transpose16(dY, w.t0, int(M), int(N), st)) return rc;  // dY^T [N][M]
