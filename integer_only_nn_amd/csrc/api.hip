@@ -35,7 +35,7 @@ __global__ void fill_u32_kernel(uint32_t *__restrict__ dst, int64_t n, uint32_t 
 
 // Max-abs reduction, max-combined into *absmax: 16 elements per thread per
 // iteration through 16-byte loads when x is 16-byte aligned, a wavefront
-// reduction, then one atomicMax per wavefront (order-independent).
+// reduction, then at most one atomicMax per wavefront (order-independent).
 template <bool VEC>
 __global__ __launch_bounds__(256) void absmax_kernel(const int32_t *__restrict__ x, int64_t n,
                                                      uint32_t *__restrict__ absmax) {
@@ -55,7 +55,7 @@ __global__ __launch_bounds__(256) void absmax_kernel(const int32_t *__restrict__
         for (int64_t i = tid; i < n; i += nthreads) m = max(m, abs_u32(x[i]));
     }
     m = wave_max_u32(m);
-    if ((threadIdx.x & 63) == 0 && m != 0) atomicMax(absmax, m);
+    if ((threadIdx.x & 63) == 0) publish_max_u32(absmax, m);
 }
 
 int launch_absmax_i32(const int32_t *x, int64_t n, uint32_t *absmax, hipStream_t st) {

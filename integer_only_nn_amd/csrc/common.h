@@ -85,6 +85,16 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
     return v;
 }
 
+// Fold a wavefront's value v (already reduced over its lanes) into the
+// device-wide max at *absmax.  The atomic is skipped when the current value is
+// already at least v: the maximum only grows, so the result is the same, and
+// the many wavefronts of a grid do not queue on one address.
+__device__ __forceinline__ void publish_max_u32(uint32_t *absmax, uint32_t v) {
+    if (v == 0) return;
+    if (__hip_atomic_load(absmax, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= v) return;
+    atomicMax(absmax, v);
+}
+
 __device__ __forceinline__ int64_t wave_sum_i64(int64_t v) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);

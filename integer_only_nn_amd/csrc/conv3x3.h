@@ -236,7 +236,7 @@ __global__ __launch_bounds__(NT, 1) void conv3x3_kernel(const int8_t *__restrict
     if (absmax) {
         uint32_t amax = vmax >= vmin ? max(abs_u32(vmax), abs_u32(vmin)) : 0u;
         amax = wave_max_u32(amax);
-        if (lane == 0 && amax != 0) atomicMax(absmax, amax);
+        if (lane == 0) publish_max_u32(absmax, amax);
     }
 }
 
@@ -435,7 +435,7 @@ __global__ __launch_bounds__(256) void conv3x3_wgrad_reduce(const int32_t *__res
         uint32_t m = max(max(abs_u32(int32_t(s.x)), abs_u32(int32_t(s.y))),
                          max(abs_u32(int32_t(s.z)), abs_u32(int32_t(s.w))));
         m = wave_max_u32(m);
-        if ((threadIdx.x & 63) == 0 && m != 0) atomicMax(absmax, m);
+        if ((threadIdx.x & 63) == 0) publish_max_u32(absmax, m);
     }
 }
 

@@ -228,7 +228,7 @@ __global__ __launch_bounds__(WGM *WGN * 64) void dfp16_kernel(DfpArgs g) {
     }
     if (!g.atomic && g.absmax) {
         amax = wave_max_u32(amax);
-        if (lane == 0 && amax != 0) atomicMax(g.absmax, amax);
+        if (lane == 0) publish_max_u32(g.absmax, amax);
     }
 }
 
@@ -430,6 +430,13 @@ __global__ __launch_bounds__(NT, 1) void dfp_kernel(Args g) {
             }
         }
 
+        // the prefetched chunk goes to the other stage before the unit's
+        // stores are issued, so its wait does not include them
+        int8_t *nx = lds + (stage ^ 1) * STAGE;
+        if (more) {
+            la.store(nx, nx + PLANE, tid);
+            lb.store(nx + 2 * PLANE, nx + 3 * PLANE, tid);
+        }
         if (c + 1 >= c1) {
             // unit done: lane holds acc[m][n .. n+3] for m = row lane % 32 of the
             // wave's block, n = block col 8 q + 4 (lane / 32)
@@ -451,15 +458,12 @@ __global__ __launch_bounds__(NT, 1) void dfp_kernel(Args g) {
             }
         }
         if (!more) break;
-        int8_t *nx = lds + (stage ^ 1) * STAGE;
-        la.store(nx, nx + PLANE, tid);
-        lb.store(nx + 2 * PLANE, nx + 3 * PLANE, tid);
         __syncthreads();
         u = nu; m0 = nm0; n0 = nn0; c = nc; c1 = nc1; stage ^= 1;
     }
     if (g.split == 1 && g.absmax) {
         amax = wave_max_u32(amax);
-        if (lane == 0 && amax != 0) atomicMax(g.absmax, amax);
+        if (lane == 0) publish_max_u32(g.absmax, amax);
     }
 }
 
@@ -470,13 +474,14 @@ __global__ __launch_bounds__(256) void split_reduce(const int32_t *__restrict__ 
     uint32_t amax = 0;
     for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; 4 * i < n; i += int64_t(gridDim.x) * blockDim.x) {
         v4u s = {0, 0, 0, 0};
-        for (int p = 0; p < split; ++p) s += *reinterpret_cast<const v4u *>(part + int64_t(p) * n + 4 * i);
+#pragma unroll 8
+        for (int p = 0; p < split; ++p) s += __builtin_nontemporal_load(reinterpret_cast<const v4u *>(part + int64_t(p) * n + 4 * i));
         *reinterpret_cast<v4u *>(acc + 4 * i) = s;
         amax = max(max(amax, max(abs_u32(int32_t(s.x)), abs_u32(int32_t(s.y)))),
                    max(abs_u32(int32_t(s.z)), abs_u32(int32_t(s.w))));
     }
     amax = wave_max_u32(amax);
-    if ((threadIdx.x & 63) == 0 && amax != 0) atomicMax(absmax, amax);
+    if ((threadIdx.x & 63) == 0) publish_max_u32(absmax, amax);
 }
 
 }  // namespace d2
@@ -631,7 +636,9 @@ int contract2(const int16_t *a, int64_t lda, const int16_t *b, int64_t ldb, int 
     if (int rc = check_launch("dfp16 contraction")) return rc;
     if (split > 1) {
         const int64_t n = int64_t(M) * N;
-        int64_t blocks = (n / 4 + 255) / 256;
+        // four 16-byte groups per thread: fewer requests in flight than one
+        // group per thread, which measured twice as fast on 16 partials
+        int64_t blocks = (n / 4 + 1023) / 1024;
         if (blocks > 2048) blocks = 2048;
         d2::split_reduce<<<dim3(unsigned(blocks)), dim3(256), 0, st>>>(part, split, n, acc, absmax);
         return check_launch("dfp16 contraction");

@@ -397,7 +397,7 @@ __global__ __launch_bounds__(NT, 1) void gemm256_kernel(const int8_t *__restrict
     if (ep.absmax) {
         uint32_t amax = max(abs_u32(vmax), abs_u32(vmin));
         amax = wave_max_u32(amax);
-        if (lane == 0 && amax != 0) atomicMax(ep.absmax, amax);
+        if (lane == 0) publish_max_u32(ep.absmax, amax);
     }
 }
 

@@ -364,7 +364,7 @@ __device__ __forceinline__ void mainloop(const SA &sa, const SB &sb, const Epi &
     }
     if (ep.absmax && !ep.atomic) {
         amax = wave_max_u32(amax);
-        if (lane == 0 && amax != 0) atomicMax(ep.absmax, amax);
+        if (lane == 0) publish_max_u32(ep.absmax, amax);
     }
 }
 

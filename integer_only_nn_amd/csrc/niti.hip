@@ -135,7 +135,7 @@ __global__ __launch_bounds__(256) void output_error_kernel(const int8_t *__restr
     }
     if (absmax) {
         m = wave_max_u32(m);
-        if ((threadIdx.x & 63) == 0 && m != 0) atomicMax(absmax, m);
+        if ((threadIdx.x & 63) == 0) publish_max_u32(absmax, m);
     }
 }
 
