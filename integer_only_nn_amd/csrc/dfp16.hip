@@ -246,12 +246,13 @@ __global__ __launch_bounds__(WGM *WGN * 64) void dfp16_kernel(DfpArgs g) {
 // and low bytes of four int16 at a time).
 //
 // Per chunk and 32 x 32 block: 8 MFMAs give sum(ah bh), sum(ah bl + al bh)
-// and sum(al bl) over the 64 terms; the row sums of A' come from v_dot4 on
-// the A fragments (one value per lane), the column sums of B' from two MFMA
-// chains against an all-ones fragment (the 16 columns a lane holds).  Then
-// per element p = 65536 hh + 256 x + ll + 128 sum A' + 128 sum B' + 2^20
-// (mod 2^32) and acc += rhu(p, r): six VALU operations, which is the bound of
-// this kernel (the matrix cores idle a third of the time).
+// and sum(al bl) over the 64 terms.  The row sums of A' and the column sums
+// of B' come from v_dot4 on the fragments (a fragment row is one row or
+// column, so each is one value per lane); the column sums then pass through
+// a small per-wave LDS row to the lanes that hold those columns in the MFMA
+// result.  Per element p = 65536 hh + 256 x + ll + 128 sum A' + 128 sum B' +
+// 2^20 (mod 2^32) and acc += rhu(p, r): six VALU operations, the bound of
+// this kernel.
 // ---------------------------------------------------------------------------
 namespace d2 {
 
@@ -306,13 +307,26 @@ __device__ __forceinline__ v4i frag(const int8_t *plane, int rb0, int kh, int la
     return v4i{x.x, x.y, y.x, y.y};
 }
 
-__device__ __forceinline__ int32_t dot16(v4i f) {  // sum of the 16 signed bytes
-    int32_t s = 0;
+__device__ __forceinline__ int32_t dot16(v4i f, int32_t s) {  // s + sum of the 16 signed bytes
     s = __builtin_amdgcn_sdot4(f.x, 0x01010101, s, false);
     s = __builtin_amdgcn_sdot4(f.y, 0x01010101, s, false);
     s = __builtin_amdgcn_sdot4(f.z, 0x01010101, s, false);
     s = __builtin_amdgcn_sdot4(f.w, 0x01010101, s, false);
     return s;
+}
+
+// v + (the same value in lane l ^ 32)
+__device__ __forceinline__ uint32_t add_half_swap(uint32_t v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return r[0] + r[1];
+}
+
+// Makes v opaque to the optimiser (no instruction): keeps (a << s) + v as one
+// v_lshl_add_u32 instead of letting the compiler fold v's adds into a v_add3
+// and leave the shift on its own.
+__device__ __forceinline__ uint32_t opaque(uint32_t v) {
+    asm volatile("" : "+v"(v));
+    return v;
 }
 
 struct Args {
@@ -330,6 +344,7 @@ struct Args {
 template <bool A_KM, bool B_KM>
 __global__ __launch_bounds__(NT, 1) void dfp_kernel(Args g) {
     __shared__ __attribute__((aligned(16))) int8_t lds[2 * STAGE];
+    __shared__ __attribute__((aligned(16))) uint32_t csum[NT / 64][64];  // per wave: 128 * sum(B') of its 64 columns
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;  // 32-row block wm of 4, 64-column half wn of 2
@@ -366,7 +381,6 @@ __global__ __launch_bounds__(NT, 1) void dfp_kernel(Args g) {
     lb.store(lds + 2 * PLANE, lds + 3 * PLANE, tid);
     __syncthreads();
 
-    const v4i ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
     const v16i zero16 = {};
     const int r = g.r;
     const uint32_t rm1 = r > 0 ? r - 1 : 0, rw = r > 0 ? 1 : 0;  // rounding bit (none for r = 0)
@@ -396,35 +410,40 @@ __global__ __launch_bounds__(NT, 1) void dfp_kernel(Args g) {
                 bl[j][kh] = frag<B_KM>(st + 3 * PLANE, 64 * wn + 32 * j, kh, lane);
             }
         }
-        // 128 * sum(A') over the chunk + 2^20 for this lane's row (lanes l and
-        // l + 32 hold the two 16-term halves of a row's k range)
-        int32_t sah = dot16(ah[0]) + dot16(ah[1]);
-        int32_t sal = dot16(al[0]) + dot16(al[1]);
-        sah += __shfl_xor(sah, 32, 64);
-        sal += __shfl_xor(sal, 32, 64);
-        const uint32_t rt = (uint32_t(sah) << 15) + (uint32_t(sal) << 7) + (1u << 20);
+        // Sums over the chunk's 64 terms (lanes l and l + 32 hold the two
+        // 16-term halves of a fragment row): 128 * sum(A') + 2^20 for this
+        // lane's row, and 128 * sum(B') for column 32 j + lane % 32 of the
+        // wave's half, which goes through the wave's own LDS row to reach the
+        // lanes that hold that column in the MFMA result layout.
+        // (256 sum(hi digits) + sum(lo digits)) over the lane's 32 terms
+        const uint32_t sa = dot16(al[1], dot16(al[0], int32_t(uint32_t(dot16(ah[1], dot16(ah[0], 0))) << 8)));
+        const uint32_t rt = (add_half_swap(sa) << 7) + (1u << 20);
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            // 128 * sum(B') for the block's 16 columns of this lane; it seeds
-            // the low-digit chain, which then adds it for free
-            v16i sh = __builtin_amdgcn_mfma_i32_32x32x32_i8(bh[j][0], ones, zero16, 0, 0, 0);
-            sh = __builtin_amdgcn_mfma_i32_32x32x32_i8(bh[j][1], ones, sh, 0, 0, 0);
-            v16i ll = __builtin_amdgcn_mfma_i32_32x32x32_i8(bl[j][0], ones, zero16, 0, 0, 0);
-            ll = __builtin_amdgcn_mfma_i32_32x32x32_i8(bl[j][1], ones, ll, 0, 0, 0);
+            const uint32_t sb =
+                dot16(bl[j][1], dot16(bl[j][0], int32_t(uint32_t(dot16(bh[j][1], dot16(bh[j][0], 0))) << 8)));
+            const uint32_t cs = add_half_swap(sb);
+            if (lane < 32) csum[wave][32 * j + lane] = cs << 7;
+        }
 #pragma unroll
-            for (int v = 0; v < 16; ++v) ll[v] = int32_t(((uint32_t(sh[v]) << 8) + uint32_t(ll[v])) << 7);
+        for (int j = 0; j < 2; ++j) {
+            v4i cb[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                cb[q] = *reinterpret_cast<const v4i *>(&csum[wave][32 * j + 8 * q + 4 * (lane >> 5)]);
             v16i hh = __builtin_amdgcn_mfma_i32_32x32x32_i8(bh[j][0], ah[0], zero16, 0, 0, 0);
             hh = __builtin_amdgcn_mfma_i32_32x32x32_i8(bh[j][1], ah[1], hh, 0, 0, 0);
             v16i x = __builtin_amdgcn_mfma_i32_32x32x32_i8(bl[j][0], ah[0], zero16, 0, 0, 0);
             x = __builtin_amdgcn_mfma_i32_32x32x32_i8(bh[j][0], al[0], x, 0, 0, 0);
             x = __builtin_amdgcn_mfma_i32_32x32x32_i8(bl[j][1], ah[1], x, 0, 0, 0);
             x = __builtin_amdgcn_mfma_i32_32x32x32_i8(bh[j][1], al[1], x, 0, 0, 0);
-            ll = __builtin_amdgcn_mfma_i32_32x32x32_i8(bl[j][0], al[0], ll, 0, 0, 0);
+            v16i ll = __builtin_amdgcn_mfma_i32_32x32x32_i8(bl[j][0], al[0], zero16, 0, 0, 0);
             ll = __builtin_amdgcn_mfma_i32_32x32x32_i8(bl[j][1], al[1], ll, 0, 0, 0);
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 // p mod 2^32, then acc += rhu(p, r) = (p >> r) + bit (r - 1) of p
-                const uint32_t p = (uint32_t(hh[v]) << 16) + ((uint32_t(x[v]) << 8) + uint32_t(ll[v])) + rt;
+                const uint32_t t = opaque((uint32_t(x[v]) << 8) + uint32_t(ll[v]));
+                const uint32_t p = (uint32_t(hh[v]) << 16) + opaque(t + rt + uint32_t(cb[v >> 2][v & 3]));
                 acc[j][v] = int32_t(uint32_t(acc[j][v]) + uint32_t(int32_t(p) >> r) +
                                     __builtin_amdgcn_ubfe(p, rm1, rw));
             }
