@@ -13,18 +13,21 @@
 // A persistent workgroup per compute unit walks tiles of 256 consecutive
 // output pixels of one image.  For each tile the input rows it touches, plus
 // one row above and below, are staged in LDS as a zero-padded halo: (W + 2)
-// slots per row (the two outer slots stay zero), 80 bytes per slot (64
-// channels + 16 bytes of padding, which makes 16 consecutive slots hit 16
-// distinct 16-byte bank groups).  Rows outside the image are written as
-// zeros, so every tap of every pixel reads its operand at
-// slot(pixel) + dy (W + 2) + dx with no bounds test.  The 64 x 576 weight
-// matrix lives in registers for the whole kernel (36 16-byte fragments per
-// lane), so LDS serves only the pixel operand.  The next tile's halo is
-// loaded into registers while the current tile computes and written to the
-// other LDS buffer afterwards: one barrier per tile.
+// slots per row (the two outer slots are zero) and zero rows outside the
+// image, so every tap of every pixel reads its operand at
+// slot(pixel) + dy (W + 2) + dx with no bounds test.
 //
-// Each wavefront owns 64 pixels x 64 channels (2 x 2 blocks of 32 x 32, 64
-// accumulators); K = 9 taps x 64 = 18 steps of 32.
+// fwd / dgrad: the 64 x 576 weight matrix lives in registers for the whole
+// kernel (36 16-byte fragments per lane), so LDS serves only the pixel
+// operand.  Halos are loaded straight into LDS two tiles ahead, into one of
+// three buffers, with 64-byte slots whose 16-byte chunks are XOR-swizzled
+// against bank conflicts.  Eight wavefronts, two per SIMD so that one's
+// memory waits overlap the other's matrix work; each owns 32 pixels x 64
+// channels (two blocks of 32 x 32); K = 9 taps x 64 = 18 steps of 32.
+//
+// wgrad: 80-byte slots (64 channels + 16 bytes of padding, which makes 16
+// consecutive slots hit 16 distinct 16-byte bank groups), double-buffered
+// through registers.
 #pragma once
 
 #include "common.h"
@@ -32,12 +35,16 @@
 namespace ionn {
 namespace c3 {
 
+typedef int v2i __attribute__((ext_vector_type(2)));
+
 constexpr int C = 64;            // input and output channels of the fast path
 constexpr int TP = 256;          // output pixels per tile
-constexpr int NT = 256;          // threads per workgroup (4 wavefronts)
+constexpr int NT = 256;          // threads per workgroup of the weight-gradient kernel
+constexpr int NTF = 512;         // threads per workgroup of the fwd / dgrad kernel
 constexpr int SLOT = 80;         // LDS bytes per halo slot
 constexpr int HALO_BYTES = 48 * 1024;
-constexpr int HALO_IT = 10;      // 16-byte halo chunks per thread and tile, at most
+constexpr int HALO_IT = 10;      // 16-byte halo chunks per thread and tile, at most (NT threads)
+constexpr int HALO_ITF = HALO_IT * NT / NTF;  // the same with NTF threads
 constexpr int KS = 18;           // 576 / 32
 
 // Bytes of the halo of a 256-pixel tile: rows touched by 256 consecutive
@@ -51,12 +58,53 @@ inline bool fits(int64_t W) {
     return W >= 1 && halo_bytes(W) <= HALO_BYTES && ((TP - 1 + W - 1) / W + 3) * W * 4 <= int64_t(HALO_IT) * NT;
 }
 
+// ---- fwd / dgrad ---------------------------------------------------------
+// The halo of a tile is fetched straight into LDS (buffer_load ... lds, no
+// registers in between), two tiles ahead, into one of three buffers.  A halo
+// slot is 64 bytes (one pixel); 16-byte chunk c of slot s sits at chunk
+// position 4 s + (c ^ ((s >> 2) & 3)), so eight consecutive slots read at
+// one channel chunk land in eight distinct bank groups.  The loads go
+// through a buffer resource over the activation tensor: pad slots, rows
+// outside the image and rows past the tile get an offset beyond the end and
+// are filled with zeros by the load itself.
+constexpr int NB = 3;                          // halo buffers
+constexpr int HBUF = 48 * 1024;                // bytes per buffer
+constexpr int NI = HBUF / (NTF / 64) / 1024;   // 1 KiB loads per wavefront per tile (6)
+constexpr uint32_t OOB = 0x80000000u;          // an offset past the end of any tensor taken here
+
+// Halo rows of a 256-pixel tile: the rows it touches plus one above and below.
+inline int64_t halo_rows(int64_t W) { return (TP - 1 + W - 1) / W + 1 + 2; }
+
+// The fwd / dgrad fast path holds a tile's halo in one buffer and addresses
+// the int8 input (act_bytes) and the int32 output with 32-bit offsets.
+inline bool fits_fd(int64_t W, int64_t act_bytes) {
+    return W >= 1 && halo_rows(W) * (W + 2) * 64 <= HBUF && 4 * act_bytes < (int64_t(1) << 31);
+}
+
+__device__ __forceinline__ int chunk_pos(int s, int c) { return 4 * s + (c ^ ((s >> 2) & 3)); }
+
+// 64 lanes x 16 bytes from rsrc.base + voff into LDS at m0 + 16 * lane.  Not
+// visible to the compiler: the kernel waits for these loads itself.
+__device__ __forceinline__ void dma_lds16(v4i rsrc, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :
+                 : "v"(voff), "s"(rsrc), "s"(lds)
+                 : "memory", "m0");
+}
+
+// s_waitcnt vmcnt(n) alone (expcnt and lgkmcnt left at their maxima).
+template <int n>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(n >= 0 && n < 64, "vmcnt");
+    __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
+}
+
 template <bool DGRAD>
-__global__ __launch_bounds__(NT, 1) void conv3x3_kernel(const int8_t *__restrict__ in,
-                                                        const int8_t *__restrict__ wgt,
-                                                        int32_t *__restrict__ out, int N, int H,
-                                                        int W, uint32_t *__restrict__ absmax) {
-    __shared__ __attribute__((aligned(16))) int8_t halo[2][HALO_BYTES];
+__global__ __launch_bounds__(NTF, 1) void conv3x3_kernel(const int8_t *__restrict__ in,
+                                                         const int8_t *__restrict__ wgt,
+                                                         int32_t *__restrict__ out, int N, int H,
+                                                         int W, uint32_t *__restrict__ absmax) {
+    __shared__ __attribute__((aligned(1024))) int8_t halo[NB][HBUF];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -64,6 +112,7 @@ __global__ __launch_bounds__(NT, 1) void conv3x3_kernel(const int8_t *__restrict
     const int tpi = (HW + TP - 1) / TP;
     const int ntiles = N * tpi;
     const int W2 = W + 2;
+    const int G = gridDim.x;
 
     // ---- weight fragments: wf[cb][ks] = 16 bytes of row (cb*32 + lane%32),
     // k = ks*32 + 16*(lane/32) of the operand B[row][k] (k = tap*64 + channel).
@@ -77,161 +126,146 @@ __global__ __launch_bounds__(NT, 1) void conv3x3_kernel(const int8_t *__restrict
                 wf[cb][ks] = *reinterpret_cast<const v4i *>(wgt + (cb * 32 + (lane & 31)) * 576 + ks * 32 +
                                                             16 * (lane >> 5));
     } else {
-        // B[ci][tap*64 + co] = W[co][8 - tap][ci]: W is staged in LDS, transposed
-        // there by all threads (16 bytes of one B row per step), then read back
-        // as fragments (once per workgroup).
-        int8_t *stage = &halo[0][0], *bt = &halo[1][0];
-        for (int i = tid; i < 64 * 576 / 16; i += NT)
+        // B[ci][tap*64 + co] = W[co][8 - tap][ci].  W is staged in LDS as stored
+        // (rows of 576 bytes per co) and every fragment comes out with two
+        // ds_read_b64_tr_b8: lane i of a 16-lane group addresses co row
+        // co0 + i/2 at ci0 + 8 (i mod 2), and lane j receives
+        // W[co0 .. co0+7][8 - tap][ci0 + j], eight consecutive k of row ci0 + j.
+        typedef __attribute__((address_space(3))) v2i lds_v2i_t;
+        int8_t *stage = &halo[0][0];
+        for (int i = tid; i < 64 * 576 / 16; i += NTF)
             *reinterpret_cast<v4i *>(stage + 16 * i) = *reinterpret_cast<const v4i *>(wgt + 16 * i);
         __syncthreads();
-        for (int q = tid; q < 64 * 576 / 16; q += NT) {
-            const int ci = q / 36, kc = q - ci * 36;
-            const int tap = kc >> 2, co0 = (kc & 3) * 16;
-            uint32_t w4[4] = {0, 0, 0, 0};
-#pragma unroll
-            for (int j = 0; j < 16; ++j)
-                w4[j >> 2] |= uint32_t(uint8_t(stage[(co0 + j) * 576 + (8 - tap) * 64 + ci])) << (8 * (j & 3));
-            *reinterpret_cast<v4i *>(bt + ci * 576 + tap * 64 + co0) =
-                v4i{int(w4[0]), int(w4[1]), int(w4[2]), int(w4[3])};
-        }
-        __syncthreads();
+        const int g = lane >> 4, i = lane & 15;
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-                wf[cb][ks] = *reinterpret_cast<const v4i *>(bt + (cb * 32 + (lane & 31)) * 576 + ks * 32 +
-                                                            16 * (lane >> 5));
+            for (int ks = 0; ks < KS; ++ks) {
+                const int co = (ks & 1) * 32 + 16 * (g >> 1) + (i >> 1);
+                const int ci = cb * 32 + 16 * (g & 1) + 8 * (i & 1);
+                const int8_t *p = stage + co * 576 + (8 - (ks >> 1)) * 64 + ci;
+                const v2i x = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i_t *)(p));
+                const v2i y = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i_t *)(p + 8 * 576));
+                wf[cb][ks] = v4i{x.x, x.y, y.x, y.y};
+            }
         __syncthreads();
     }
 
-    // ---- zero both halo buffers (the outer slots of every row stay zero)
-    for (int i = tid; i < 2 * HALO_BYTES / 16; i += NT)
-        reinterpret_cast<v4i *>(&halo[0][0])[i] = v4i{0, 0, 0, 0};
+    // The weight loads are complete before the halo loads start, so that no
+    // wait inside the tile loop has to cover them.
+    wait_vm<0>();
 
-    // This thread's halo chunks: q = tid + NT*i -> (row r, column w, 16-byte
-    // chunk cc) with q = (r * W + w) * 4 + cc; the same for every tile.
-    int hr[HALO_IT], hw4[HALO_IT];
+    // Buffer resource over the input: offsets at or past its end read zeros.
+    const uint64_t abase = uint64_t(uintptr_t(in));
+    const v4i rsrc = {__builtin_amdgcn_readfirstlane(int(uint32_t(abase))),
+                      __builtin_amdgcn_readfirstlane(int(uint32_t(abase >> 32) & 0xffffu)),
+                      __builtin_amdgcn_readfirstlane(int(uint32_t(int64_t(N) * HW * C))),
+                      0x00020000};
+    // Load i of this wavefront fills chunk positions q = (8 i + wave) * 64 + lane:
+    // slot s = q / 4, halo row s / W2, column s % W2 - 1, channel chunk
+    // (q % 4) ^ ((s / 4) % 4); hoff = byte offset of that chunk within its
+    // image row, or -1 for the pad slots.
+    int hrow[NI], hoff[NI];
 #pragma unroll
-    for (int i = 0; i < HALO_IT; ++i) {
-        const int q = tid + NT * i;
-        hr[i] = q / (4 * W);
-        hw4[i] = q - hr[i] * 4 * W;
+    for (int i = 0; i < NI; ++i) {
+        const int q = (8 * i + wave) * 64 + lane, sl = q >> 2;
+        hrow[i] = sl / W2;
+        const int w = sl - hrow[i] * W2 - 1;
+        hoff[i] = (w >= 0 && w < W) ? w * 64 + 16 * ((q & 3) ^ ((sl >> 2) & 3)) : -1;
     }
+    // Halo of tile t into buffer bf; every wavefront issues exactly NI loads,
+    // also past the last tile (all zeros then), so the wait counts below hold.
+    auto fetch = [&](int t, int bf) __attribute__((always_inline)) {
+        int n = 0, hf = 0, nrows = 0;
+        if (t < ntiles) {
+            n = t / tpi;
+            const int p0 = (t - n * tpi) * TP, valid = min(TP, HW - p0);
+            hf = p0 / W;
+            nrows = (p0 + valid - 1) / W - hf + 3;
+        }
+        const uint32_t lds0 = uint32_t(uintptr_t((__attribute__((address_space(3))) const int8_t *)(&halo[bf][0])));
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int h = hf - 1 + hrow[i];
+            const bool ok = hrow[i] < nrows && hoff[i] >= 0 && h >= 0 && h < H;
+            const uint32_t voff = ok ? uint32_t((n * H + h) * W) * 64u + uint32_t(hoff[i]) : OOB;
+            dma_lds16(rsrc, voff, lds0 + uint32_t((8 * i + wave) * 1024));
+        }
+    };
 
-    // Halo of tile t into registers (zeros for rows outside the image and
-    // for chunks past the tile's rows).
-    v4i hv[HALO_IT];
-    auto fetch = [&](int t) __attribute__((always_inline)) {
-        const int n = t / tpi, p0 = (t - n * tpi) * TP;
-        const int valid = min(TP, HW - p0);
-        const int hf = p0 / W, hl = (p0 + valid - 1) / W;
-        const int nrows = hl - hf + 3;
-#pragma unroll
-        for (int i = 0; i < HALO_IT; ++i) {
-            const int h = hf - 1 + hr[i];
-            v4i v = {0, 0, 0, 0};
-            if (hr[i] < nrows && h >= 0 && h < H)
-                v = *reinterpret_cast<const v4i *>(in + ((int64_t(n) * H + h) * W) * C + int64_t(hw4[i]) * 16);
-            hv[i] = v;
-        }
-    };
-    auto put = [&](int t, int8_t *buf) __attribute__((always_inline)) {
-        const int n = t / tpi, p0 = (t - n * tpi) * TP;
-        const int valid = min(TP, HW - p0);
-        const int hf = p0 / W, hl = (p0 + valid - 1) / W;
-        const int nrows = hl - hf + 3;
-#pragma unroll
-        for (int i = 0; i < HALO_IT; ++i) {
-            if (hr[i] < nrows) {
-                const int w = hw4[i] >> 2, cc = hw4[i] & 3;
-                *reinterpret_cast<v4i *>(buf + (hr[i] * W2 + w + 1) * SLOT + cc * 16) = hv[i];
-            }
-        }
-    };
+    // Output through a buffer resource as well (see the epilogue).
+    const __amdgpu_buffer_rsrc_t orsrc =
+        __builtin_amdgcn_make_buffer_rsrc(out, 0, int(int64_t(N) * HW * C * 4), 0x00020000);
 
     int t = blockIdx.x;
-    if (t < ntiles) fetch(t);
-    __syncthreads();  // zeroing done before the first halo lands
-    if (t < ntiles) put(t, halo[0]);
-    __syncthreads();
+    fetch(t, 0);
+    fetch(t + G, 1);
 
     int32_t vmax = INT32_MIN, vmin = INT32_MAX;
     int b = 0;
-    for (; t < ntiles; t += gridDim.x, b ^= 1) {
-        const int tn = t + gridDim.x;
-        if (tn < ntiles) fetch(tn);
+    for (int k = 0; t < ntiles; t += G, ++k) {
+        // This tile's loads are done when at most the next tile's (NI) and the
+        // previous tile's stores (8) are still outstanding.
+        if (k == 0) wait_vm<NI>(); else wait_vm<NI + 8>();
+        __syncthreads();
+        fetch(t + 2 * G, b == 0 ? 2 : b - 1);
 
         const int n = t / tpi, p0 = (t - n * tpi) * TP;
         const int valid = min(TP, HW - p0);
         const int hf = p0 / W;
         const int8_t *buf = halo[b];
 
-        // LDS byte offset of each of this lane's two pixels (centre tap), or
-        // -1 past the tile's valid pixels.
-        int poff[2];
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int pl = (2 * wave + j) * 32 + (lane & 31);
-            if (pl < valid) {
-                const int p = p0 + pl, h = p / W, w = p - h * W;
-                poff[j] = ((h - hf + 1) * W2 + w + 1) * SLOT + 16 * (lane >> 5);
-            } else {
-                poff[j] = -1;
-            }
+        // centre slot of this lane's pixel; slot 0 (a pad, all zero) past the
+        // tile's valid pixels
+        const int pl = 32 * wave + (lane & 31);
+        int sc = -1;
+        if (pl < valid) {
+            const int p = p0 + pl, h = p / W, w = p - h * W;
+            sc = (h - hf + 1) * W2 + w + 1;
         }
-        // operand fragment of pixel block j at step ks: tap ks/2, channel chunk
-        // 2 (ks & 1) + lane/32; a lane past the valid pixels reads slot 0 (zero)
-        auto afrag = [&](int j, int ks) __attribute__((always_inline)) {
+        // operand fragment at step ks: tap ks/2, channel chunk 2 (ks & 1) + lane/32
+        auto afrag = [&](int ks) __attribute__((always_inline)) {
             const int tap = ks >> 1, dy = tap / 3 - 1, dx = tap % 3 - 1;
-            const int o = poff[j] >= 0 ? poff[j] + (dy * W2 + dx) * SLOT + 32 * (ks & 1) : 0;
-            return *reinterpret_cast<const v4i *>(buf + o);
+            const int sl = sc >= 0 ? sc + dy * W2 + dx : 0;
+            return *reinterpret_cast<const v4i *>(buf + 16 * chunk_pos(sl, 2 * (ks & 1) + (lane >> 5)));
         };
 
-        v16i acc[2][2];
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int cb = 0; cb < 2; ++cb) acc[j][cb] = v16i{};
-        v4i a[2][2];
-        a[0][0] = afrag(0, 0);
-        a[0][1] = afrag(1, 0);
+        v16i acc[2] = {v16i{}, v16i{}};
+        v4i a[2];
+        a[0] = afrag(0);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const int c = ks & 1;
-            if (ks + 1 < KS) {
-                a[c ^ 1][0] = afrag(0, ks + 1);
-                a[c ^ 1][1] = afrag(1, ks + 1);
-            }
+            if (ks + 1 < KS) a[c ^ 1] = afrag(ks + 1);
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
-#pragma unroll
-                for (int cb = 0; cb < 2; ++cb)
-                    acc[j][cb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(wf[cb][ks], a[c][j], acc[j][cb], 0, 0, 0);
+            for (int cb = 0; cb < 2; ++cb)
+                acc[cb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(wf[cb][ks], a[c], acc[cb], 0, 0, 0);
         }
 
-        // epilogue: lane holds out[p][co .. co+3], p = block pixel lane % 32,
-        // co = cb*32 + 8 q + 4 (lane / 32)
+        // epilogue: lane holds out[p][co .. co+3], p = pixel pl,
+        // co = cb*32 + 8 q + 4 (lane / 32); a lane past the valid pixels
+        // stores to an offset beyond the end (dropped), so every wavefront
+        // issues exactly eight stores per tile
+        const uint32_t obase = pl < valid ? uint32_t(((n * HW + p0 + pl) * C + 4 * (lane >> 5)) * 4) : OOB;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int pl = (2 * wave + j) * 32 + (lane & 31);
-            if (pl < valid) {
-                int32_t *row = out + (int64_t(n) * HW + p0 + pl) * C + 4 * (lane >> 5);
+        for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
-                for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const v4i v = {acc[j][cb][4 * q], acc[j][cb][4 * q + 1], acc[j][cb][4 * q + 2],
-                                       acc[j][cb][4 * q + 3]};
-                        *reinterpret_cast<v4i *>(row + cb * 32 + 8 * q) = v;
-                        vmax = max(vmax, max(max(v[0], v[1]), max(v[2], v[3])));
-                        vmin = min(vmin, min(min(v[0], v[1]), min(v[2], v[3])));
-                    }
+            for (int q = 0; q < 4; ++q) {
+                const v4i v = {acc[cb][4 * q], acc[cb][4 * q + 1], acc[cb][4 * q + 2], acc[cb][4 * q + 3]};
+                __builtin_amdgcn_raw_buffer_store_b128(v, orsrc, int(obase + uint32_t((cb * 32 + 8 * q) * 4)), 0, 0);
             }
+        if (pl < valid) {
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+                for (int v = 0; v < 16; v += 2) {
+                    vmax = max(vmax, max(acc[cb][v], acc[cb][v + 1]));
+                    vmin = min(vmin, min(acc[cb][v], acc[cb][v + 1]));
+                }
         }
-
-        if (tn < ntiles) put(tn, halo[b ^ 1]);
-        __syncthreads();
+        b = b == 2 ? 0 : b + 1;
     }
+    wait_vm<0>();  // the zero-fill loads past the last tile land before the workgroup ends
 
     if (absmax) {
         uint32_t amax = vmax >= vmin ? max(abs_u32(vmax), abs_u32(vmin)) : 0u;

@@ -74,6 +74,12 @@ bool fast_c64(const ionn_conv_desc *d, const void *in, const void *w, const void
            aligned(out, 16);
 }
 
+// fwd / dgrad fast path: 64 -> 64 channels, the halo in one LDS buffer and
+// 32-bit byte offsets into the input and the int32 output.
+bool fast_c64_fd(const ionn_conv_desc *d, const void *in, const void *w, const void *out) {
+    return fast_c64(d, in, w, out) && c3::fits_fd(d->W, d->N * d->H * d->W * 64);
+}
+
 unsigned c3_grid(const ionn_conv_desc *d) {
     const int64_t tiles = d->N * ((d->H * d->W + c3::TP - 1) / c3::TP);
     const int64_t g = tiles < device_cus() ? tiles : device_cus();
@@ -102,8 +108,8 @@ int int_conv_fwd(const int8_t *X, const int8_t *Wt, int32_t *Y, const ionn_conv_
         zero_i32_kernel<<<dim3(4096), dim3(256), 0, st>>>(Y, int64_t(npix) * Cout);
         return check_launch("int_conv_fwd");
     }
-    if (fast_c64(desc, X, Wt, Y)) {
-        c3::conv3x3_kernel<false><<<dim3(c3_grid(desc)), dim3(c3::NT), 0, st>>>(
+    if (fast_c64_fd(desc, X, Wt, Y)) {
+        c3::conv3x3_kernel<false><<<dim3(c3_grid(desc)), dim3(c3::NTF), 0, st>>>(
             X, Wt, Y, int(desc->N), int(desc->H), int(desc->W), absmax_Y);
         return check_launch("int_conv_fwd");
     }
@@ -132,8 +138,8 @@ int int_conv_dgrad(const int8_t *dY, const int8_t *Wt, int32_t *dX, const ionn_c
         zero_i32_kernel<<<dim3(4096), dim3(256), 0, st>>>(dX, int64_t(npix) * Cin);
         return check_launch("int_conv_dgrad");
     }
-    if (fast_c64(desc, dY, Wt, dX)) {
-        c3::conv3x3_kernel<true><<<dim3(c3_grid(desc)), dim3(c3::NT), 0, st>>>(
+    if (fast_c64_fd(desc, dY, Wt, dX)) {
+        c3::conv3x3_kernel<true><<<dim3(c3_grid(desc)), dim3(c3::NTF), 0, st>>>(
             dY, Wt, dX, int(desc->N), int(desc->H), int(desc->W), absmax_dX);
         return check_launch("int_conv_dgrad");
     }

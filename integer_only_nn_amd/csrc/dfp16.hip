@@ -423,7 +423,7 @@ __global__ __launch_bounds__(NT, 1) void dfp_kernel(Args g) {
             const uint32_t sb =
                 dot16(bl[j][1], dot16(bl[j][0], int32_t(uint32_t(dot16(bh[j][1], dot16(bh[j][0], 0))) << 8)));
             const uint32_t cs = add_half_swap(sb);
-            if (lane < 32) csum[wave][32 * j + lane] = cs << 7;
+            csum[wave][32 * j + (lane & 31)] = cs << 7;  // lanes l and l + 32 hold the same value
         }
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
