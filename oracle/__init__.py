@@ -55,6 +55,9 @@ def _declare(L):
         "ora_linear_wgrad_at": (ctypes.c_int32, [_P, _P, _I64, _I64, _I64, _I64, _I64]),
         "ora_relu_mask": (None, [_P, _P, _I64]),
         "ora_output_error": (None, [_P, _P, _I64, _I64, _I, _P]),
+        "ora_oss_requant": (None, [_P, _P, _P, _P, _I64, _I64, _I, _P]),
+        "ora_bias_grad": (None, [_P, _I64, _I64, _P]),
+        "ora_niti_update_i32": (None, [_P, _P, _I64, _I, _I, _P, _P, _P]),
         "ora_conv_fwd": (_I64, [_P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I, _I, _I]),
         "ora_conv_dgrad": (_I64, [_P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I, _I, _I]),
         "ora_conv_wgrad": (_I64, [_P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I, _I, _I]),
@@ -158,6 +161,39 @@ def niti_update(G: np.ndarray, W: np.ndarray, target_bits: int, mu_weight: int):
     lib().ora_niti_update(_c(G, np.int32), _c(Wn, np.int8), G.size, int(target_bits),
                           int(mu_weight), _c(gq, np.int32), ctypes.byref(s), ctypes.byref(ws))
     return Wn, gq, s.value, ws.value
+
+
+# ---- offsets (bias) and OSS requantisation -------------------------------
+
+def oss_requant(acc, offset, mult, k, relu=False):
+    """int8 [M][C] = clip(floor(((acc + offset) mod 2^32) * mult / 2^k)) per channel."""
+    M, C = acc.shape
+    assert offset.shape == (C,) and mult.shape == (C,) and k.shape == (C,)
+    out = np.empty((M, C), np.int8)
+    lib().ora_oss_requant(_c(acc, np.int32), _c(offset, np.int32), _c(mult, np.int32),
+                          _c(k, np.int8), M, C, int(bool(relu)), _c(out, np.int8))
+    return out
+
+
+def bias_grad(d):
+    """int32 [C] column sums of the int8 error rows d [M][C]."""
+    M, C = d.shape
+    gb = np.empty(C, np.int32)
+    lib().ora_bias_grad(_c(d, np.int8), M, C, _c(gb, np.int32))
+    return gb
+
+
+def niti_update_i32(G, P, target_bits, mu):
+    """Return (P_new, Gq, shift, weight_shift); P is not modified."""
+    if G.shape != P.shape:
+        raise ValueError("G and P shapes differ")
+    Pn = np.ascontiguousarray(P, dtype=np.int32).copy()
+    gq = np.empty(G.shape, np.int32)
+    s = ctypes.c_int()
+    ws = ctypes.c_int()
+    lib().ora_niti_update_i32(_c(G, np.int32), _c(Pn, np.int32), G.size, int(target_bits),
+                              int(mu), _c(gq, np.int32), ctypes.byref(s), ctypes.byref(ws))
+    return Pn, gq, s.value, ws.value
 
 
 # ---- linear -------------------------------------------------------------

@@ -606,3 +606,63 @@ double ora_gavg(const int16_t *g, int64_t n, int e_g, int e_w)
     for (; e < 0; ++e) v *= 0.5;
     return v;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Offsets (bias) and the static OSS forward requantisation.                 */
+/* ------------------------------------------------------------------------ */
+
+/* floor(v / 2^k) for k in [0, 62], written with non-negative shifts only. */
+static int64_t floor_div_pow2(int64_t v, int k)
+{
+    const int64_t d = (int64_t)1 << k;
+    if (v >= 0) return v / d;
+    return -((-v + d - 1) / d);
+}
+
+/* [TI] section 8, Step 2: Add(offset) -> Mul(scale1 = mult) -> Mul(scale2 =
+ * 2^-k) -> Floor -> Clip, on the int32 accumulator of output channel c. */
+void ora_oss_requant(const int32_t *acc, const int32_t *offset, const int32_t *mult,
+                     const int8_t *k, int64_t M, int64_t C, int relu, int8_t *out)
+{
+    const int64_t lo = relu ? 0 : -128;
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t c = 0; c < C; ++c) {
+            const int32_t t = u32_to_i32((uint32_t)acc[m * C + c] + (uint32_t)offset[c]);
+            int64_t y = floor_div_pow2((int64_t)t * (int64_t)mult[c], k[c]);
+            if (y < lo) y = lo;
+            if (y > 127) y = 127;
+            out[m * C + c] = (int8_t)y;
+        }
+}
+
+/* The offset's gradient: the output error summed over the rows (batch, and
+ * pixels for a convolution). */
+void ora_bias_grad(const int8_t *d, int64_t M, int64_t C, int32_t *gb)
+{
+    for (int64_t c = 0; c < C; ++c) {
+        uint32_t s = 0;
+        for (int64_t m = 0; m < M; ++m) s += (uint32_t)(int32_t)d[m * C + c];
+        gb[c] = u32_to_i32(s);
+    }
+}
+
+/* [TI] section 3 steps 1-5 on int32 parameters; the final clamp is to the
+ * int32 range instead of int8. */
+void ora_niti_update_i32(const int32_t *G, int32_t *P, int64_t n, int target_bits,
+                         int mu, int32_t *gq_out, int *shift_out, int *weight_shift_out)
+{
+    int s = ora_niti_shift(ora_absmax_i32(G, n), target_bits);
+    int ws = s - mu;
+    if (ws < 0) ws = 0;
+    for (int64_t j = 0; j < n; ++j) {
+        int32_t gq = ora_rhu(G[j], s);
+        int32_t d = ora_rhu(gq, ws);
+        int64_t v = (int64_t)P[j] - (int64_t)d;
+        if (v < -2147483648LL) v = -2147483648LL;
+        if (v > 2147483647LL) v = 2147483647LL;
+        if (gq_out) gq_out[j] = gq;
+        P[j] = (int32_t)v;
+    }
+    if (shift_out) *shift_out = s;
+    if (weight_shift_out) *weight_shift_out = ws;
+}

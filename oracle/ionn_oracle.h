@@ -136,6 +136,26 @@ int ora_dfp16_wgrad(const int16_t *dY, int edY, const int16_t *X, int eX,
 /* Gavg = mean(|g|) * 2^(e_g - e_w)   ([APT] Equation 4, epsilon = 2^e_w). */
 double ora_gavg(const int16_t *g, int64_t n, int e_g, int e_w);
 
+/* ---- Offsets (bias) and the static OSS forward requantisation ([TI]
+ * section 7 "INT_LAYERS": int32 offsets updated by the backward pass, int8
+ * per-filter right shifts k and multipliers mult; section 8, "PC-Side Steps",
+ * Step 2: the OSS chain Add(offset) -> Mul(scale1) -> Mul(scale2) -> Floor
+ * -> Clip) ---- */
+/* out[m][c] = clip(floor(t * mult[c] / 2^k[c]), lo, 127) with
+ * t = acc[m][c] + offset[c] modulo 2^32 (int32, as the accumulator), the
+ * product exact in int64, lo = 0 if relu else -128 (reading U23).
+ * k[c] in [0, 62]. */
+void ora_oss_requant(const int32_t *acc, const int32_t *offset, const int32_t *mult,
+                     const int8_t *k, int64_t M, int64_t C, int relu, int8_t *out);
+/* gb[c] = sum_m d[m][c] over the int8 output error rows, modulo 2^32
+ * (reading U24: the offset's gradient is the error summed over the batch,
+ * as G is summed over it). */
+void ora_bias_grad(const int8_t *d, int64_t M, int64_t C, int32_t *gb);
+/* NITI update of int32 parameters (the offsets): the steps of
+ * ora_niti_update with P = sat32(P - d) (reading U25). */
+void ora_niti_update_i32(const int32_t *G, int32_t *P, int64_t n, int target_bits,
+                         int mu, int32_t *gq_out, int *shift_out, int *weight_shift_out);
+
 #ifdef __cplusplus
 }
 #endif
