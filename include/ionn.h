@@ -247,6 +247,44 @@ int dfp16_gemm_wgrad(const int16_t *dY, const int32_t *edY, const int16_t *X,
 int dfp16_gavg(const int16_t *G, const int32_t *eG, const int32_t *eW,
                int64_t n, double *gavg_out, void *stream);
 
+/* ------------------------------------------------------------------------ */
+/* Per-channel offsets (bias) and the static OSS requantisation ([TI]        */
+/* section 7: every layer carries mutable int32 offsets, updated by the      */
+/* backward pass, and per-filter right shifts k with multipliers mult;       */
+/* section 8, PC-side Step 2: the chain Add(offset) -> Mul(scale1) ->        */
+/* Mul(scale2) -> Floor -> Clip).  Channels are the last dimension: C        */
+/* output channels of a Linear layer or of an NHWC convolution output, with  */
+/* M = rows (batch, times pixels for a convolution).                         */
+/* ------------------------------------------------------------------------ */
+
+/* out[m][c] = clip(floor(t * mult[c] / 2^k[c]), lo, 127),
+ *   t = acc[m][c] + offset[c] modulo 2^32 (the int32 accumulator's add),
+ *   the product exact in 64 bits, lo = 0 if relu (the *_RELU layer types)
+ *   else -128.
+ * acc: int32 [M][C]; offset, mult: int32 [C]; k: int8 [C], each in [0, 62]
+ * (other values give unspecified outputs, no fault); out: int8 [M][C]
+ * (written).  M, C >= 0, M * C < 2^31; relu in {0, 1}. */
+int ionn_oss_requant(const int32_t *acc, const int32_t *offset,
+                     const int32_t *mult, const int8_t *k, int64_t M,
+                     int64_t C, int relu, int8_t *out, void *stream);
+
+/* Gradient of the offsets: gb[c] = sum_m d[m][c] modulo 2^32, over the int8
+ * output error d[M][C] that also feeds dgrad and wgrad.  gb: int32 [C],
+ * overwritten (the call clears it first).  M, C >= 0, M * C < 2^31. */
+int ionn_bias_grad(const int8_t *d, int64_t M, int64_t C, int32_t *gb,
+                   void *stream);
+
+/* NITI update of int32 parameters (the offsets), in place on P: the steps of
+ * niti_quantize_update with the last one P[j] = sat32(P[j] - d) (clamped to
+ * the int32 range).  *absmax must hold max |G| (e.g. from ionn_absmax_i32).
+ * shifts_out (nullable, device int32[2]) receives {s, ws}; gq_out (nullable,
+ * device int32[n]) receives Gq.  n >= 0; target_bits in [1, 31]; mu in
+ * [0, 31]. */
+int niti_quantize_update_i32(const int32_t *G, int64_t n,
+                             const uint32_t *absmax, int target_bits, int mu,
+                             int32_t *P, int32_t *shifts_out, int32_t *gq_out,
+                             void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -1,0 +1,242 @@
+// Per-channel int32 offsets (bias) and the static OSS forward
+// requantisation ("Integer On-Device Training: Overview", section 7: each
+// INT_LAYERS entry carries mutable int32 offsets, updated by the backward
+// pass, and per-filter right shifts k with multipliers mult; section 8,
+// PC-side Step 2: the OSS chain Add(offset) -> Mul(scale1) -> Mul(scale2) ->
+// Floor -> Clip), plus the offsets' gradient and their NITI update
+// (section 3, steps 1-5).
+//
+// OSS and the update are HBM-bound streams with the mapping of the NITI
+// quantiser: instruction c of a wavefront reads int32 elements
+// c*256 + 4*lane .. +3 (1 KiB contiguous per instruction).  The offset
+// gradient sums int8 columns: a lane owns 16 columns (16 bytes of a row), a
+// workgroup 1 KiB of every row of its row range, and workgroup sums are
+// combined with integer atomics (exact in any order).
+#include "common.h"
+
+namespace ionn {
+namespace {
+
+constexpr int kInstr = 8;                  // 1 KiB loads per wavefront and iteration
+constexpr int64_t kChunk = 256 * kInstr;   // int32 elements per wavefront and iteration
+
+unsigned stream_blocks(int64_t n) {
+    int64_t b = (n + 4 * kChunk - 1) / (4 * kChunk);
+    if (b < 1) b = 1;
+    if (b > 2048) b = 2048;
+    return unsigned(b);
+}
+
+// One OSS element: t = acc + offset modulo 2^32 (the int32 accumulator),
+// t * mult exact in 64 bits (|t * mult| <= 2^62), floor division by 2^k
+// (arithmetic shift), clip to [lo, 127].
+__device__ __forceinline__ int32_t oss1(int32_t acc, int32_t off, int32_t mult, int k, int32_t lo) {
+    const int32_t t = int32_t(uint32_t(acc) + uint32_t(off));
+    const int64_t y = (int64_t(t) * int64_t(mult)) >> (k & 63);  // k in [0, 62]; & 63 keeps any byte a defined shift
+    return y < lo ? lo : (y > 127 ? 127 : int32_t(y));
+}
+
+__device__ __forceinline__ uint32_t pack4(int32_t a, int32_t b, int32_t c, int32_t d) {
+    return (uint32_t(a) & 0xffu) | ((uint32_t(b) & 0xffu) << 8) | ((uint32_t(c) & 0xffu) << 16) |
+           (uint32_t(d) << 24);
+}
+
+// VEC: C % 4 == 0, acc / offset / mult 16-byte aligned, out / k 4-byte
+// aligned, so the four elements of a lane's 16 bytes share one row and
+// their parameters are four consecutive entries.
+template <bool VEC, bool RELU>
+__global__ __launch_bounds__(256) void oss_kernel(const int32_t *__restrict__ acc, int64_t n, int64_t C,
+                                                  const int32_t *__restrict__ offset,
+                                                  const int32_t *__restrict__ mult,
+                                                  const int8_t *__restrict__ k,
+                                                  int8_t *__restrict__ out) {
+    constexpr int32_t lo = RELU ? 0 : -128;
+    const int64_t tid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    const int64_t nthreads = int64_t(gridDim.x) * blockDim.x;
+    int64_t done = 0;
+    if (VEC) {
+        const int lane = threadIdx.x & 63;
+        const int64_t wave = tid >> 6, nwaves = nthreads >> 6;
+        const int64_t nfull = n / kChunk * kChunk;
+        const uint32_t Cu = uint32_t(C);
+        for (int64_t base = wave * kChunk; base < nfull; base += nwaves * kChunk) {
+            v4i a[kInstr];
+#pragma unroll
+            for (int c = 0; c < kInstr; ++c)
+                a[c] = __builtin_nontemporal_load(reinterpret_cast<const v4i *>(acc + base + c * 256 + 4 * lane));
+            const uint32_t ch0 = uint32_t((base + 4 * lane) % C);
+#pragma unroll
+            for (int c = 0; c < kInstr; ++c) {
+                const uint32_t ch = (ch0 + uint32_t(c * 256)) % Cu;
+                const v4i o = *reinterpret_cast<const v4i *>(offset + ch);
+                const v4i m = *reinterpret_cast<const v4i *>(mult + ch);
+                const uint32_t kk = *reinterpret_cast<const uint32_t *>(k + ch);
+                *reinterpret_cast<uint32_t *>(out + base + c * 256 + 4 * lane) =
+                    pack4(oss1(a[c].x, o.x, m.x, int(kk & 0xffu), lo),
+                          oss1(a[c].y, o.y, m.y, int((kk >> 8) & 0xffu), lo),
+                          oss1(a[c].z, o.z, m.z, int((kk >> 16) & 0xffu), lo),
+                          oss1(a[c].w, o.w, m.w, int(kk >> 24), lo));
+            }
+        }
+        done = nfull;
+    }
+    for (int64_t j = done + tid; j < n; j += nthreads) {
+        const int64_t ch = j % C;
+        out[j] = int8_t(oss1(acc[j], offset[ch], mult[ch], int(k[ch]), lo));
+    }
+}
+
+// gb[c] += sum of d[r][c] over rows r of this workgroup's range.  VEC: a
+// lane owns columns 16 cg .. 16 cg + 15 (C % 16 == 0, d 16-byte aligned);
+// the four wavefronts take every fourth row.  Otherwise a lane owns one
+// column.
+template <bool VEC>
+__global__ __launch_bounds__(256) void bias_grad_kernel(const int8_t *__restrict__ d, int64_t M, int64_t C,
+                                                        int64_t rows_per_block, int32_t *__restrict__ gb) {
+    constexpr int W = VEC ? 16 : 1;  // columns per lane
+    __shared__ int32_t red[4][64][W + 1];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t c0 = (int64_t(blockIdx.x) * 64 + lane) * W;
+    const int64_t r0 = int64_t(blockIdx.y) * rows_per_block;
+    const int64_t r1 = min(M, r0 + rows_per_block);
+    int32_t s[W];
+#pragma unroll
+    for (int e = 0; e < W; ++e) s[e] = 0;
+    if (c0 < C) {
+        if (VEC) {
+            int64_t r = r0 + wave;
+            for (; r + 12 < r1; r += 16) {
+                v4i w[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) w[u] = *reinterpret_cast<const v4i *>(d + (r + 4 * u) * C + c0);
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+#pragma unroll
+                    for (int e = 0; e < W; ++e)
+                        s[e] += int32_t(int8_t(uint8_t(uint32_t(w[u][e >> 2]) >> (8 * (e & 3)))));
+            }
+            for (; r < r1; r += 4) {
+                const v4i w = *reinterpret_cast<const v4i *>(d + r * C + c0);
+#pragma unroll
+                for (int e = 0; e < W; ++e) s[e] += int32_t(int8_t(uint8_t(uint32_t(w[e >> 2]) >> (8 * (e & 3)))));
+            }
+        } else {
+            for (int64_t r = r0 + wave; r < r1; r += 4) s[0] += int32_t(d[r * C + c0]);
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < W; ++e) red[wave][lane][e] = s[e];
+    __syncthreads();
+    if (wave == 0 && c0 < C) {
+#pragma unroll
+        for (int e = 0; e < W; ++e) {
+            const int32_t t = int32_t(uint32_t(red[0][lane][e]) + uint32_t(red[1][lane][e]) +
+                                      uint32_t(red[2][lane][e]) + uint32_t(red[3][lane][e]));
+            if (t != 0 && c0 + e < C) atomicAdd(gb + c0 + e, t);
+        }
+    }
+}
+
+__global__ void zero_kernel(int32_t *p, int64_t n) {
+    for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += int64_t(gridDim.x) * blockDim.x)
+        p[i] = 0;
+}
+
+// P[j] = sat32(P[j] - rhu(rhu(G[j], s), ws)), s from *absmax.
+__global__ __launch_bounds__(256) void update_i32_kernel(const int32_t *__restrict__ G, int64_t n,
+                                                         const uint32_t *__restrict__ absmax, int target_bits,
+                                                         int mu, int32_t *__restrict__ P,
+                                                         int32_t *__restrict__ shifts_out,
+                                                         int32_t *__restrict__ gq_out) {
+    const int s = niti_shift(*absmax, target_bits);
+    const int ws = s > mu ? s - mu : 0;
+    const int64_t tid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (tid == 0 && shifts_out) {
+        shifts_out[0] = s;
+        shifts_out[1] = ws;
+    }
+    for (int64_t j = tid; j < n; j += int64_t(gridDim.x) * blockDim.x) {
+        const int32_t gq = rhu(G[j], s);
+        const int64_t v = int64_t(P[j]) - int64_t(rhu(gq, ws));
+        P[j] = v < INT32_MIN ? INT32_MIN : (v > INT32_MAX ? INT32_MAX : int32_t(v));
+        if (gq_out) gq_out[j] = gq;
+    }
+}
+
+}  // namespace
+}  // namespace ionn
+
+using namespace ionn;
+
+extern "C" {
+
+int ionn_oss_requant(const int32_t *acc, const int32_t *offset, const int32_t *mult, const int8_t *k,
+                     int64_t M, int64_t C, int relu, int8_t *out, void *stream) {
+    clear_error();
+    IONN_REQUIRE(M >= 0 && C >= 0 && M <= kMaxDim && C <= kMaxDim && M * C <= kMaxDim, IONN_ERR_SHAPE,
+                 "ionn_oss_requant: bad shape M=%lld C=%lld", (long long)M, (long long)C);
+    IONN_REQUIRE(relu == 0 || relu == 1, IONN_ERR_ARG, "ionn_oss_requant: relu = %d", relu);
+    if (M * C == 0) return IONN_OK;
+    IONN_REQUIRE(acc && offset && mult && k && out, IONN_ERR_ARG, "ionn_oss_requant: NULL argument");
+    IONN_REQUIRE(aligned(acc, 4) && aligned(offset, 4) && aligned(mult, 4), IONN_ERR_ALIGN,
+                 "ionn_oss_requant: int32 pointers must be 4-byte aligned");
+    const int64_t n = M * C;
+    const bool vec = C % 4 == 0 && aligned(acc, 16) && aligned(offset, 16) && aligned(mult, 16) &&
+                     aligned(k, 4) && aligned(out, 4);
+    dim3 grid(stream_blocks(n)), block(256);
+    hipStream_t st = as_stream(stream);
+    if (vec && relu) oss_kernel<true, true><<<grid, block, 0, st>>>(acc, n, C, offset, mult, k, out);
+    else if (vec) oss_kernel<true, false><<<grid, block, 0, st>>>(acc, n, C, offset, mult, k, out);
+    else if (relu) oss_kernel<false, true><<<grid, block, 0, st>>>(acc, n, C, offset, mult, k, out);
+    else oss_kernel<false, false><<<grid, block, 0, st>>>(acc, n, C, offset, mult, k, out);
+    return check_launch("ionn_oss_requant");
+}
+
+int ionn_bias_grad(const int8_t *d, int64_t M, int64_t C, int32_t *gb, void *stream) {
+    clear_error();
+    IONN_REQUIRE(M >= 0 && C >= 0 && M <= kMaxDim && C <= kMaxDim && M * C <= kMaxDim, IONN_ERR_SHAPE,
+                 "ionn_bias_grad: bad shape M=%lld C=%lld", (long long)M, (long long)C);
+    if (C == 0) return IONN_OK;
+    IONN_REQUIRE(gb != nullptr && (M == 0 || d != nullptr), IONN_ERR_ARG, "ionn_bias_grad: NULL argument");
+    IONN_REQUIRE(aligned(gb, 4), IONN_ERR_ALIGN, "ionn_bias_grad: gb must be 4-byte aligned");
+    hipStream_t st = as_stream(stream);
+    zero_kernel<<<dim3(unsigned((C + 255) / 256 < 1024 ? (C + 255) / 256 : 1024)), dim3(256), 0, st>>>(gb, C);
+    if (int rc = check_launch("ionn_bias_grad")) return rc;
+    if (M == 0) return IONN_OK;
+    const bool vec = C % 16 == 0 && aligned(d, 16);
+    const int64_t cols_per_block = vec ? 64 * 16 : 64;
+    const int64_t gx = (C + cols_per_block - 1) / cols_per_block;
+    // about 1024 workgroups in all, at least 64 rows each
+    int64_t gy = (1024 + gx - 1) / gx;
+    int64_t rows = (M + gy - 1) / gy;
+    if (rows < 64) rows = 64;
+    gy = (M + rows - 1) / rows;
+    IONN_REQUIRE(gx <= 0x7fffffff && gy <= 65535, IONN_ERR_SHAPE, "ionn_bias_grad: grid too large");
+    const dim3 grid{unsigned(gx), unsigned(gy), 1u}, block{256u, 1u, 1u};
+    if (vec) bias_grad_kernel<true><<<grid, block, 0, st>>>(d, M, C, rows, gb);
+    else bias_grad_kernel<false><<<grid, block, 0, st>>>(d, M, C, rows, gb);
+    return check_launch("ionn_bias_grad");
+}
+
+int niti_quantize_update_i32(const int32_t *G, int64_t n, const uint32_t *absmax, int target_bits, int mu,
+                             int32_t *P, int32_t *shifts_out, int32_t *gq_out, void *stream) {
+    clear_error();
+    IONN_REQUIRE(n >= 0, IONN_ERR_SHAPE, "niti_quantize_update_i32: n = %lld < 0", (long long)n);
+    IONN_REQUIRE(absmax != nullptr, IONN_ERR_ARG, "niti_quantize_update_i32: absmax is NULL");
+    IONN_REQUIRE(n == 0 || (G != nullptr && P != nullptr), IONN_ERR_ARG,
+                 "niti_quantize_update_i32: G/P is NULL");
+    IONN_REQUIRE(target_bits >= 1 && target_bits <= 31, IONN_ERR_RANGE,
+                 "niti_quantize_update_i32: target_bits = %d outside [1, 31]", target_bits);
+    IONN_REQUIRE(mu >= 0 && mu <= 31, IONN_ERR_RANGE, "niti_quantize_update_i32: mu = %d outside [0, 31]", mu);
+    IONN_REQUIRE(aligned(G, 4) && aligned(P, 4) && aligned(absmax, 4) && aligned(shifts_out, 4) &&
+                     aligned(gq_out, 4),
+                 IONN_ERR_ALIGN, "niti_quantize_update_i32: int32 pointers must be 4-byte aligned");
+    int64_t blocks = (n + 255) / 256;
+    if (blocks < 1) blocks = 1;
+    if (blocks > 2048) blocks = 2048;
+    update_i32_kernel<<<dim3(unsigned(blocks)), dim3(256), 0, as_stream(stream)>>>(G, n, absmax, target_bits, mu, P,
+                                                                                   shifts_out, gq_out);
+    return check_launch("niti_quantize_update_i32");
+}
+
+}  // extern "C"

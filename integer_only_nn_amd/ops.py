@@ -97,6 +97,30 @@ def niti_quantize_update(G, absmax, target_bits, mu_weight, W, shifts_out=None, 
           "niti_quantize_update")
 
 
+def ionn_oss_requant(acc, offset, mult, k, out, relu=False, stream=None):
+    M, C = acc.shape
+    assert tuple(out.shape) == (M, C) and offset.numel() == C and mult.numel() == C and k.numel() == C
+    check(lib().ionn_oss_requant(_p(acc, i32, name="acc"), _p(offset, i32, name="offset"),
+                                 _p(mult, i32, name="mult"), _p(k, i8, name="k"), M, C, int(bool(relu)),
+                                 _p(out, i8, name="out"), _stream(stream)), "ionn_oss_requant")
+
+
+def ionn_bias_grad(d, gb, stream=None):
+    M, C = d.shape
+    assert gb.numel() == C
+    check(lib().ionn_bias_grad(_p(d, i8, name="d"), M, C, _p(gb, i32, name="gb"), _stream(stream)),
+          "ionn_bias_grad")
+
+
+def niti_quantize_update_i32(G, absmax, target_bits, mu, P, shifts_out=None, gq_out=None, stream=None):
+    assert G.numel() == P.numel()
+    check(lib().niti_quantize_update_i32(_p(G, i32, name="G"), G.numel(), _p(absmax, u32, 1, "absmax"),
+                                         int(target_bits), int(mu), _p(P, i32, name="P"),
+                                         _p(shifts_out, i32, 2, "shifts_out"),
+                                         _p(gq_out, i32, G.numel(), "gq_out"), _stream(stream)),
+          "niti_quantize_update_i32")
+
+
 def int_output_error(out, labels, target_mag, e, absmax_e=None, stream=None):
     B, C = out.shape
     assert tuple(e.shape) == (B, C) and labels.numel() == B
