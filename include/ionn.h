@@ -268,6 +268,22 @@ int ionn_oss_requant(const int32_t *acc, const int32_t *offset,
                      const int32_t *mult, const int8_t *k, int64_t M,
                      int64_t C, int relu, int8_t *out, void *stream);
 
+/* Forward of a Linear layer with its offsets and static OSS requantisation
+ * in one call: Y[b][o] = oss(sum_i X[b][i] * W[o][i]) with the per-output
+ * offset, mult and k of ionn_oss_requant (relu selects the *_RELU clip
+ * range).  X: int8 [B][IN]; W: int8 [OUT][IN]; Y: int8 [B][OUT] (written).
+ * Tile-aligned shapes (B, IN, OUT multiples of 256, IN > 0) with 16-byte
+ * aligned X, W, offset, mult and 4-byte aligned k, Y run as one kernel whose
+ * epilogue applies the chain to the int32 accumulators (no int32 tensor
+ * reaches memory); other shapes or alignments compute the int32 product in
+ * `workspace` (16-byte aligned, int_linear_fwd_oss_workspace_bytes bytes;
+ * IONN_ERR_WORKSPACE without it) and then run the OSS pass. */
+size_t int_linear_fwd_oss_workspace_bytes(int64_t B, int64_t IN, int64_t OUT);
+int int_linear_fwd_oss(const int8_t *X, const int8_t *W, const int32_t *offset,
+                       const int32_t *mult, const int8_t *k, int relu,
+                       int8_t *Y, int64_t B, int64_t IN, int64_t OUT,
+                       void *workspace, size_t workspace_bytes, void *stream);
+
 /* Gradient of the offsets: gb[c] = sum_m d[m][c] modulo 2^32, over the int8
  * output error d[M][C] that also feeds dgrad and wgrad.  gb: int32 [C],
  * overwritten (the call clears it first).  M, C >= 0, M * C < 2^31. */

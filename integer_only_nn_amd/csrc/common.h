@@ -75,6 +75,24 @@ __device__ __forceinline__ int32_t sat16(int32_t v) {
     return v < -32768 ? -32768 : (v > 32767 ? 32767 : v);
 }
 
+// One element of the static OSS requantisation ("Integer On-Device Training:
+// Overview", section 8, PC-side Step 2: Add(offset) -> Mul -> Mul -> Floor ->
+// Clip): t = acc + offset modulo 2^32 (the int32 accumulator), t * mult exact
+// in 64 bits (|t * mult| <= 2^62), floor division by 2^k as an arithmetic
+// shift (k in [0, 62]; & 63 keeps any byte a defined shift), clip to
+// [lo, 127].
+__device__ __forceinline__ int32_t oss_elem(int32_t acc, int32_t off, int32_t mult, int k, int32_t lo) {
+    const int32_t t = int32_t(uint32_t(acc) + uint32_t(off));
+    const int64_t y = (int64_t(t) * int64_t(mult)) >> (k & 63);
+    return y < lo ? lo : (y > 127 ? 127 : int32_t(y));
+}
+
+// Four int8 values (low bytes of a..d) in one dword, a lowest.
+__device__ __forceinline__ uint32_t pack4_u8(int32_t a, int32_t b, int32_t c, int32_t d) {
+    return (uint32_t(a) & 0xffu) | ((uint32_t(b) & 0xffu) << 8) | ((uint32_t(c) & 0xffu) << 16) |
+           (uint32_t(d) << 24);
+}
+
 // Max over the 64 lanes of a wavefront.
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 #pragma unroll

@@ -236,7 +236,7 @@ __device__ __forceinline__ void mfma_gt(const Frags<A_KM, B_KM> &f, int g, int t
     acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
 }
 
-template <bool A_KM, bool B_KM, bool RELU>
+template <bool A_KM, bool B_KM, bool RELU, bool OSS>
 __global__ __launch_bounds__(NT, 1) void gemm256_kernel(const int8_t *__restrict__ A, int64_t lda,
                                                         const int8_t *__restrict__ B, int64_t ldb,
                                                         uint32_t a_bytes, uint32_t b_bytes,
@@ -366,8 +366,35 @@ __global__ __launch_bounds__(NT, 1) void gemm256_kernel(const int8_t *__restrict
     // of values: one instruction per value instead of abs + max per value);
     // |INT32_MIN| = 2^31 is exact in uint32.  Row pointers are formed once
     // per 32-row block; column offsets are immediates. ----
-    int32_t vmax = INT32_MIN, vmin = INT32_MAX;
     const int em = lane & 31, en = (lane >> 5) * 4;
+    if (OSS) {
+        // static OSS: int8 out, four columns per dword; per-column parameters
+        // come from L1 (the same 16 column groups for every row block)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t m = m0 + wm * 128 + i * 32 + em;
+            const int64_t nb = n0 + wn * 128 + en;
+            int8_t *orow = ep.out8 + m * ep.ldc + nb;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int dn = j * 32 + 8 * q;
+                    const v4i o = *reinterpret_cast<const v4i *>(ep.oss_off + nb + dn);
+                    const v4i mu = *reinterpret_cast<const v4i *>(ep.oss_mult + nb + dn);
+                    const uint32_t kk = *reinterpret_cast<const uint32_t *>(ep.oss_k + nb + dn);
+                    const int lo = ep.oss_lo;
+                    *reinterpret_cast<uint32_t *>(orow + dn) =
+                        pack4_u8(oss_elem(acc[i][j][4 * q], o.x, mu.x, int(kk & 0xffu), lo),
+                                 oss_elem(acc[i][j][4 * q + 1], o.y, mu.y, int((kk >> 8) & 0xffu), lo),
+                                 oss_elem(acc[i][j][4 * q + 2], o.z, mu.z, int((kk >> 16) & 0xffu), lo),
+                                 oss_elem(acc[i][j][4 * q + 3], o.w, mu.w, int(kk >> 24), lo));
+                }
+            }
+        }
+        return;
+    }
+    int32_t vmax = INT32_MIN, vmin = INT32_MAX;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int64_t m = m0 + wm * 128 + i * 32 + em;
@@ -401,17 +428,20 @@ __global__ __launch_bounds__(NT, 1) void gemm256_kernel(const int8_t *__restrict
     }
 }
 
-// ep.act selects the ReLU-masked epilogue (dgrad): C = 0 where act <= 0.
+// ep.out8 selects the static OSS epilogue (int8 out, C unused); ep.act the
+// ReLU-masked one (dgrad): C = 0 where act <= 0.
 template <bool A_KM, bool B_KM>
 void launch(const int8_t *A, int64_t lda, const int8_t *B, int64_t ldb, const gemm::Epi &ep, int M,
             int N, int K, hipStream_t st) {
     const uint32_t a_bytes = uint32_t((A_KM ? int64_t(M) : int64_t(K)) * lda);
     const uint32_t b_bytes = uint32_t((B_KM ? int64_t(N) : int64_t(K)) * ldb);
     const dim3 grid((M / BM) * (N / BN)), block(NT);
-    if (ep.act)
-        gemm256_kernel<A_KM, B_KM, true><<<grid, block, 0, st>>>(A, lda, B, ldb, a_bytes, b_bytes, ep, M, N, K);
+    if (ep.out8)
+        gemm256_kernel<A_KM, B_KM, false, true><<<grid, block, 0, st>>>(A, lda, B, ldb, a_bytes, b_bytes, ep, M, N, K);
+    else if (ep.act)
+        gemm256_kernel<A_KM, B_KM, true, false><<<grid, block, 0, st>>>(A, lda, B, ldb, a_bytes, b_bytes, ep, M, N, K);
     else
-        gemm256_kernel<A_KM, B_KM, false><<<grid, block, 0, st>>>(A, lda, B, ldb, a_bytes, b_bytes, ep, M, N, K);
+        gemm256_kernel<A_KM, B_KM, false, false><<<grid, block, 0, st>>>(A, lda, B, ldb, a_bytes, b_bytes, ep, M, N, K);
 }
 
 }  // namespace g256

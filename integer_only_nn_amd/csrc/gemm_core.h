@@ -229,6 +229,12 @@ struct Epi {
     const int8_t *act;   // ReLU-mask source with C's layout (nullable)
     uint32_t *absmax;    // max-combined (nullable)
     bool atomic;         // split-K: atomicAdd into C (absmax handled separately)
+    // static OSS epilogue (256x256 path only): int8 out8[m][n] =
+    // oss_elem(C[m][n], oss_off[n], oss_mult[n], oss_k[n], oss_lo); C is not written
+    int8_t *out8;
+    const int32_t *oss_off, *oss_mult;
+    const int8_t *oss_k;
+    int oss_lo;
 };
 
 // Tile index remap: workgroups that are resident on one XCD at the same time

@@ -93,6 +93,46 @@ int int_linear_fwd(const int8_t *X, const int8_t *W, int32_t *Y, int64_t B, int6
     return check_launch("int_linear_fwd");
 }
 
+size_t int_linear_fwd_oss_workspace_bytes(int64_t B, int64_t IN, int64_t OUT) {
+    if (!dims_ok(B, IN, OUT)) return 0;
+    const bool tile = B % 256 == 0 && OUT % 256 == 0 && IN % 256 == 0 && IN > 0;
+    return tile ? 0 : size_t(B * OUT) * sizeof(int32_t);
+}
+
+int int_linear_fwd_oss(const int8_t *X, const int8_t *W, const int32_t *offset, const int32_t *mult,
+                       const int8_t *k, int relu, int8_t *Y, int64_t B, int64_t IN, int64_t OUT,
+                       void *workspace, size_t workspace_bytes, void *stream) {
+    clear_error();
+    IONN_REQUIRE(dims_ok(B, IN, OUT), IONN_ERR_SHAPE,
+                 "int_linear_fwd_oss: sizes must be in [0, 2^31): B=%lld IN=%lld OUT=%lld",
+                 (long long)B, (long long)IN, (long long)OUT);
+    IONN_REQUIRE(relu == 0 || relu == 1, IONN_ERR_ARG, "int_linear_fwd_oss: relu = %d", relu);
+    if (B == 0 || OUT == 0) return IONN_OK;
+    IONN_REQUIRE(Y && offset && mult && k && (IN == 0 || (X && W)), IONN_ERR_ARG,
+                 "int_linear_fwd_oss: NULL tensor");
+    IONN_REQUIRE(aligned(offset, 4) && aligned(mult, 4), IONN_ERR_ALIGN,
+                 "int_linear_fwd_oss: offset/mult must be 4-byte aligned");
+    hipStream_t st = as_stream(stream);
+    const int M = int(B), N = int(OUT), K = int(IN);
+    Epi ep{nullptr, OUT, M, N, false, nullptr, nullptr, false,
+           Y, offset, mult, k, relu ? 0 : -128};
+    if (M % 256 == 0 && N % 256 == 0 && K % 256 == 0 && K > 0 && aligned(X, 16) && aligned(W, 16) &&
+        aligned(Y, 4) && aligned(offset, 16) && aligned(mult, 16) && aligned(k, 4) &&
+        int64_t(M) * K < (int64_t(1) << 31) && int64_t(N) * K < (int64_t(1) << 31)) {
+        g256::launch<true, true>(X, IN, W, IN, ep, M, N, K, st);
+        return check_launch("int_linear_fwd_oss");
+    }
+    // other shapes: the int32 product into the workspace, then the OSS pass
+    IONN_REQUIRE(workspace != nullptr && aligned(workspace, 16) &&
+                     workspace_bytes >= size_t(B * OUT) * sizeof(int32_t),
+                 IONN_ERR_WORKSPACE,
+                 "int_linear_fwd_oss: this shape or alignment needs a 16-byte aligned workspace of %zu bytes",
+                 size_t(B * OUT) * sizeof(int32_t));
+    int32_t *acc = static_cast<int32_t *>(workspace);
+    if (int rc = int_linear_fwd(X, W, acc, B, IN, OUT, nullptr, stream)) return rc;
+    return ionn_oss_requant(acc, offset, mult, k, B, OUT, relu, Y, stream);
+}
+
 int int_linear_dgrad(const int8_t *dY, const int8_t *W, const int8_t *relu_act, int32_t *dX,
                      int64_t B, int64_t IN, int64_t OUT, uint32_t *absmax_dX, void *stream) {
     clear_error();

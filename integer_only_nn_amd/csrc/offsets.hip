@@ -27,20 +27,6 @@ unsigned stream_blocks(int64_t n) {
     return unsigned(b);
 }
 
-// One OSS element: t = acc + offset modulo 2^32 (the int32 accumulator),
-// t * mult exact in 64 bits (|t * mult| <= 2^62), floor division by 2^k
-// (arithmetic shift), clip to [lo, 127].
-__device__ __forceinline__ int32_t oss1(int32_t acc, int32_t off, int32_t mult, int k, int32_t lo) {
-    const int32_t t = int32_t(uint32_t(acc) + uint32_t(off));
-    const int64_t y = (int64_t(t) * int64_t(mult)) >> (k & 63);  // k in [0, 62]; & 63 keeps any byte a defined shift
-    return y < lo ? lo : (y > 127 ? 127 : int32_t(y));
-}
-
-__device__ __forceinline__ uint32_t pack4(int32_t a, int32_t b, int32_t c, int32_t d) {
-    return (uint32_t(a) & 0xffu) | ((uint32_t(b) & 0xffu) << 8) | ((uint32_t(c) & 0xffu) << 16) |
-           (uint32_t(d) << 24);
-}
-
 // VEC: C % 4 == 0, acc / offset / mult 16-byte aligned, out / k 4-byte
 // aligned, so the four elements of a lane's 16 bytes share one row and
 // their parameters are four consecutive entries.
@@ -72,17 +58,17 @@ __global__ __launch_bounds__(256) void oss_kernel(const int32_t *__restrict__ ac
                 const v4i m = *reinterpret_cast<const v4i *>(mult + ch);
                 const uint32_t kk = *reinterpret_cast<const uint32_t *>(k + ch);
                 *reinterpret_cast<uint32_t *>(out + base + c * 256 + 4 * lane) =
-                    pack4(oss1(a[c].x, o.x, m.x, int(kk & 0xffu), lo),
-                          oss1(a[c].y, o.y, m.y, int((kk >> 8) & 0xffu), lo),
-                          oss1(a[c].z, o.z, m.z, int((kk >> 16) & 0xffu), lo),
-                          oss1(a[c].w, o.w, m.w, int(kk >> 24), lo));
+                    pack4_u8(oss_elem(a[c].x, o.x, m.x, int(kk & 0xffu), lo),
+                          oss_elem(a[c].y, o.y, m.y, int((kk >> 8) & 0xffu), lo),
+                          oss_elem(a[c].z, o.z, m.z, int((kk >> 16) & 0xffu), lo),
+                          oss_elem(a[c].w, o.w, m.w, int(kk >> 24), lo));
             }
         }
         done = nfull;
     }
     for (int64_t j = done + tid; j < n; j += nthreads) {
         const int64_t ch = j % C;
-        out[j] = int8_t(oss1(acc[j], offset[ch], mult[ch], int(k[ch]), lo));
+        out[j] = int8_t(oss_elem(acc[j], offset[ch], mult[ch], int(k[ch]), lo));
     }
 }
 

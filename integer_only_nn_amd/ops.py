@@ -105,6 +105,22 @@ def ionn_oss_requant(acc, offset, mult, k, out, relu=False, stream=None):
                                  _p(out, i8, name="out"), _stream(stream)), "ionn_oss_requant")
 
 
+def int_linear_fwd_oss_workspace_bytes(B, IN, OUT):
+    return int(lib().int_linear_fwd_oss_workspace_bytes(int(B), int(IN), int(OUT)))
+
+
+def int_linear_fwd_oss(X, W, offset, mult, k, Y, relu=False, workspace=None, stream=None):
+    B, IN = X.shape
+    OUT = W.shape[0]
+    assert tuple(W.shape) == (OUT, IN) and tuple(Y.shape) == (B, OUT), "shape mismatch"
+    assert offset.numel() == OUT and mult.numel() == OUT and k.numel() == OUT
+    check(lib().int_linear_fwd_oss(_p(X, i8, name="X"), _p(W, i8, name="W"), _p(offset, i32, name="offset"),
+                                   _p(mult, i32, name="mult"), _p(k, i8, name="k"), int(bool(relu)),
+                                   _p(Y, i8, name="Y"), B, IN, OUT, _p(workspace, None, name="workspace"),
+                                   workspace.numel() * workspace.element_size() if workspace is not None else 0,
+                                   _stream(stream)), "int_linear_fwd_oss")
+
+
 def ionn_bias_grad(d, gb, stream=None):
     M, C = d.shape
     assert gb.numel() == C
