@@ -220,6 +220,51 @@ def bench_dfp16(torch, steps_mod, nsteps):
     return _timed(torch, step, nsteps)
 
 
+def bench_offsets(torch, nsteps):
+    """Offsets (bias) and the static OSS chain on the large-linear workload:
+    the forward with the chain in the contraction's epilogue (int8 out), the
+    same as an int32 contraction plus the OSS pass, and the offsets' backward
+    (gradient over the 8192 error rows, its max, the int32 NITI update).
+    Per-channel parameters are seeded: offset U[-2^18, 2^18), mult
+    U[1, 2^11) with every seventh negated, k U[16, 22)."""
+    import ionn_synth
+    from integer_only_nn_amd import ops
+    dev = torch.device("cuda:0")
+    d = ionn_synth.large_linear()
+    X, W, dY = (torch.from_numpy(d[k]).to(dev) for k in ("X", "W", "dY"))
+    rng = np.random.default_rng(11)
+    off = rng.integers(-2**18, 2**18, OUT, dtype=np.int64).astype(np.int32)
+    mult = rng.integers(1, 2**11, OUT, dtype=np.int64).astype(np.int32)
+    mult[::7] *= -1
+    k = rng.integers(16, 22, OUT).astype(np.int8)
+    off, mult, k = (torch.from_numpy(a).to(dev) for a in (off, mult, k))
+    Y8 = torch.empty(T, OUT, dtype=torch.int8, device=dev)
+    acc = torch.empty(T, OUT, dtype=torch.int32, device=dev)
+    gb = torch.empty(OUT, dtype=torch.int32, device=dev)
+    gws = torch.empty(ops.ionn_bias_grad_workspace_bytes(T, OUT), dtype=torch.uint8, device=dev)
+    P = torch.zeros(OUT, dtype=torch.int32, device=dev)
+    am = torch.zeros(1, dtype=torch.int32, device=dev)
+    sh = torch.zeros(2, dtype=torch.int32, device=dev)
+
+    def step(tm):
+        m = tm.mark if tm else (lambda n: None)
+        m("fwd_oss_fused")
+        ops.int_linear_fwd_oss(X, W, off, mult, k, Y8)
+        m("fwd_int32")
+        ops.int_linear_fwd(X, W, acc)
+        m("oss_pass")
+        ops.ionn_oss_requant(acc, off, mult, k, Y8)
+        m("bias_grad")
+        ops.ionn_bias_grad(dY, gb, gws)
+        m("fill")
+        ops.ionn_fill_u32(am, 0)
+        m("absmax")
+        ops.ionn_absmax_i32(gb, am)
+        m("update_i32")
+        ops.niti_quantize_update_i32(gb, am, 8, 2, P, shifts_out=sh)
+    return _timed(torch, step, nsteps)
+
+
 def _kernel_source_hash():
     import glob
     import hashlib
@@ -329,7 +374,7 @@ def main():
         result["calibration"] = {"read_kernel": "absmax_kernel", "write_kernel": "fill_u32_kernel",
                                  "bytes": 256 << 20}
     if not args.no_secondary:
-        log("secondary: conv and DFP-16 steps")
+        log("secondary: conv and DFP-16 steps, offsets and OSS")
         c_ms, c_per = bench_conv(torch, steps_mod, 20)
         f_ms, f_per = bench_dfp16(torch, steps_mod, 20)
         conv_ops = 3 * 2.0 * 128 * 56 * 56 * 64 * 9 * 64
@@ -345,6 +390,23 @@ def main():
                    "wgrad": 6.0 * 1024 * 256 * (25088 // 64)}
         fdom = max(dfp_alu, key=lambda k: f_per[k])
         falu = dfp_alu[fdom] / (f_per[fdom] * 1e-3) / 1e12
+        o_ms, o_per = bench_offsets(torch, 20)
+        o_gemm = 2.0 * T * IN * OUT / (o_per["fwd_oss_fused"] * 1e-3) / 1e12
+        o_oss = 5.0 * T * OUT / (o_per["oss_pass"] * 1e-3) / 1e9
+        o_bg = 1.0 * T * OUT / (o_per["bias_grad"] * 1e-3) / 1e9
+        offsets = {"shape": f"T{T} IN{IN} OUT{OUT}",
+                   "kernel_ms": {k2: round(v, 4) for k2, v in o_per.items()},
+                   "fwd_with_oss_ms": {"fused": round(o_per["fwd_oss_fused"], 4),
+                                       "int32_then_oss_pass": round(o_per["fwd_int32"] + o_per["oss_pass"], 4)},
+                   "offset_backward_ms": round(o_per["bias_grad"] + o_per["fill"] + o_per["absmax"]
+                                               + o_per["update_i32"], 4),
+                   "roofline": {"bound": "mfma", "kernel": "int_linear_fwd_oss", "achieved": round(o_gemm, 1),
+                                "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s",
+                                "frac": round(o_gemm / PEAK_INT8_TOPS, 4)},
+                   "oss_pass": {"bound": "hbm", "achieved": round(o_oss, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                "frac": round(o_oss / PEAK_HBM_GBS, 4), "bytes_per_launch": 5.0 * T * OUT},
+                   "bias_grad": {"bound": "hbm", "achieved": round(o_bg, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                 "frac": round(o_bg / PEAK_HBM_GBS, 4), "bytes_per_launch": 1.0 * T * OUT}}
         result["secondary"] = {
             "conv3x3_step": {"shape": "N128 56x56 64->64 NHWC", "ms_per_step": round(c_ms, 4),
                              "TOPS": round(conv_ops / (c_ms * 1e-3) / 1e12, 2),
@@ -362,6 +424,7 @@ def main():
                                         "achieved": round(falu, 2), "peak": PEAK_VALU_TOPS,
                                         "unit": "T int32 op/s", "frac": round(falu / PEAK_VALU_TOPS, 4),
                                         "ops_per_launch": dfp_alu[fdom]}},
+            "offsets_oss": offsets,
         }
     if not args.no_cpu_baseline:
         log("cpu baseline: oracle on a bounded sample")

@@ -286,9 +286,12 @@ int int_linear_fwd_oss(const int8_t *X, const int8_t *W, const int32_t *offset,
 
 /* Gradient of the offsets: gb[c] = sum_m d[m][c] modulo 2^32, over the int8
  * output error d[M][C] that also feeds dgrad and wgrad.  gb: int32 [C],
- * overwritten (the call clears it first).  M, C >= 0, M * C < 2^31. */
+ * overwritten.  The row ranges' sums pass through `workspace` (4-byte
+ * aligned, ionn_bias_grad_workspace_bytes(M, C) bytes; IONN_ERR_WORKSPACE
+ * when NULL or smaller, except for M = 0).  M, C >= 0, M * C < 2^31. */
+size_t ionn_bias_grad_workspace_bytes(int64_t M, int64_t C);
 int ionn_bias_grad(const int8_t *d, int64_t M, int64_t C, int32_t *gb,
-                   void *stream);
+                   void *workspace, size_t workspace_bytes, void *stream);
 
 /* NITI update of int32 parameters (the offsets), in place on P: the steps of
  * niti_quantize_update with the last one P[j] = sat32(P[j] - d) (clamped to

@@ -10,8 +10,10 @@
 // quantiser: instruction c of a wavefront reads int32 elements
 // c*256 + 4*lane .. +3 (1 KiB contiguous per instruction).  The offset
 // gradient sums int8 columns: a lane owns 16 columns (16 bytes of a row), a
-// workgroup 1 KiB of every row of its row range, and workgroup sums are
-// combined with integer atomics (exact in any order).
+// workgroup 1 KiB of every row of its row range; the per-range sums go to a
+// workspace and a second pass adds them (integer atomics from every
+// workgroup queued on the same addresses and ran at a tenth of the
+// bandwidth).
 #include "common.h"
 
 namespace ionn {
@@ -72,15 +74,18 @@ __global__ __launch_bounds__(256) void oss_kernel(const int32_t *__restrict__ ac
     }
 }
 
-// gb[c] += sum of d[r][c] over rows r of this workgroup's range.  VEC: a
-// lane owns columns 16 cg .. 16 cg + 15 (C % 16 == 0, d 16-byte aligned);
-// the four wavefronts take every fourth row.  Otherwise a lane owns one
-// column.
+// Column sums of the int8 rows d[M][C] over row range y of the grid.  VEC: a
+// lane owns columns 16 cg .. 16 cg + 15 (C % 16 == 0, d 16-byte aligned),
+// a workgroup a 1 KiB strip of every row in its range, its eight wavefronts
+// every eighth row; otherwise a lane owns one column.  The workgroup's sums
+// go to part[y][c] (no atomics: the second pass adds the row ranges).
+constexpr int BG_WAVES = 8;
 template <bool VEC>
-__global__ __launch_bounds__(256) void bias_grad_kernel(const int8_t *__restrict__ d, int64_t M, int64_t C,
-                                                        int64_t rows_per_block, int32_t *__restrict__ gb) {
+__global__ __launch_bounds__(64 * BG_WAVES) void bias_grad_kernel(const int8_t *__restrict__ d, int64_t M,
+                                                                  int64_t C, int64_t rows_per_block,
+                                                                  int32_t *__restrict__ part) {
     constexpr int W = VEC ? 16 : 1;  // columns per lane
-    __shared__ int32_t red[4][64][W + 1];
+    __shared__ int32_t red[BG_WAVES][64][W + 1];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t c0 = (int64_t(blockIdx.x) * 64 + lane) * W;
     const int64_t r0 = int64_t(blockIdx.y) * rows_per_block;
@@ -91,23 +96,24 @@ __global__ __launch_bounds__(256) void bias_grad_kernel(const int8_t *__restrict
     if (c0 < C) {
         if (VEC) {
             int64_t r = r0 + wave;
-            for (; r + 12 < r1; r += 16) {
-                v4i w[4];
+            constexpr int U = 4, S = BG_WAVES;
+            for (; r + (U - 1) * S < r1; r += U * S) {
+                v4i w[U];
 #pragma unroll
-                for (int u = 0; u < 4; ++u) w[u] = *reinterpret_cast<const v4i *>(d + (r + 4 * u) * C + c0);
+                for (int u = 0; u < U; ++u) w[u] = *reinterpret_cast<const v4i *>(d + (r + u * S) * C + c0);
 #pragma unroll
-                for (int u = 0; u < 4; ++u)
+                for (int u = 0; u < U; ++u)
 #pragma unroll
                     for (int e = 0; e < W; ++e)
                         s[e] += int32_t(int8_t(uint8_t(uint32_t(w[u][e >> 2]) >> (8 * (e & 3)))));
             }
-            for (; r < r1; r += 4) {
+            for (; r < r1; r += S) {
                 const v4i w = *reinterpret_cast<const v4i *>(d + r * C + c0);
 #pragma unroll
                 for (int e = 0; e < W; ++e) s[e] += int32_t(int8_t(uint8_t(uint32_t(w[e >> 2]) >> (8 * (e & 3)))));
             }
         } else {
-            for (int64_t r = r0 + wave; r < r1; r += 4) s[0] += int32_t(d[r * C + c0]);
+            for (int64_t r = r0 + wave; r < r1; r += BG_WAVES) s[0] += int32_t(d[r * C + c0]);
         }
     }
 #pragma unroll
@@ -116,11 +122,44 @@ __global__ __launch_bounds__(256) void bias_grad_kernel(const int8_t *__restrict
     if (wave == 0 && c0 < C) {
 #pragma unroll
         for (int e = 0; e < W; ++e) {
-            const int32_t t = int32_t(uint32_t(red[0][lane][e]) + uint32_t(red[1][lane][e]) +
-                                      uint32_t(red[2][lane][e]) + uint32_t(red[3][lane][e]));
-            if (t != 0 && c0 + e < C) atomicAdd(gb + c0 + e, t);
+            uint32_t t = 0;
+#pragma unroll
+            for (int w = 0; w < BG_WAVES; ++w) t += uint32_t(red[w][lane][e]);
+            if (c0 + e < C) part[int64_t(blockIdx.y) * C + c0 + e] = int32_t(t);
         }
     }
+}
+
+// gb[c] = sum over the ny row ranges of part[y][c] (modulo 2^32).
+__global__ __launch_bounds__(256) void bias_grad_sum(const int32_t *__restrict__ part, int64_t ny, int64_t C,
+                                                     int32_t *__restrict__ gb) {
+    const int64_t c = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (c >= C) return;
+    uint32_t t = 0;
+#pragma unroll 8
+    for (int64_t y = 0; y < ny; ++y) t += uint32_t(part[y * C + c]);
+    gb[c] = int32_t(t);
+}
+
+// Row split of the offset gradient: about 256 workgroups of 1 KiB strips in
+// all, each with at least 64 rows; the workspace holds one int32 row of C
+// per range.  The split depends on M and C only, so the workspace query
+// holds for either layout.
+struct BgGrid {
+    int64_t gx, gy, rows;
+    bool vec;
+};
+BgGrid bg_grid(int64_t M, int64_t C, bool vec) {
+    BgGrid g;
+    g.vec = vec;
+    const int64_t strips = (C + 1023) / 1024;
+    g.gx = vec ? strips : (C + 63) / 64;
+    int64_t gy = (256 + strips - 1) / strips;
+    int64_t rows = (M + gy - 1) / gy;
+    if (rows < 64) rows = 64;
+    g.rows = rows;
+    g.gy = M > 0 ? (M + rows - 1) / rows : 0;
+    return g;
 }
 
 __global__ void zero_kernel(int32_t *p, int64_t n) {
@@ -178,7 +217,14 @@ int ionn_oss_requant(const int32_t *acc, const int32_t *offset, const int32_t *m
     return check_launch("ionn_oss_requant");
 }
 
-int ionn_bias_grad(const int8_t *d, int64_t M, int64_t C, int32_t *gb, void *stream) {
+size_t ionn_bias_grad_workspace_bytes(int64_t M, int64_t C) {
+    if (M < 0 || C < 0 || M > kMaxDim || C > kMaxDim || M * C > kMaxDim) return 0;
+    const BgGrid g = bg_grid(M, C, C % 16 == 0);
+    return size_t(g.gy * C) * sizeof(int32_t);
+}
+
+int ionn_bias_grad(const int8_t *d, int64_t M, int64_t C, int32_t *gb, void *workspace, size_t workspace_bytes,
+                   void *stream) {
     clear_error();
     IONN_REQUIRE(M >= 0 && C >= 0 && M <= kMaxDim && C <= kMaxDim && M * C <= kMaxDim, IONN_ERR_SHAPE,
                  "ionn_bias_grad: bad shape M=%lld C=%lld", (long long)M, (long long)C);
@@ -186,21 +232,21 @@ int ionn_bias_grad(const int8_t *d, int64_t M, int64_t C, int32_t *gb, void *str
     IONN_REQUIRE(gb != nullptr && (M == 0 || d != nullptr), IONN_ERR_ARG, "ionn_bias_grad: NULL argument");
     IONN_REQUIRE(aligned(gb, 4), IONN_ERR_ALIGN, "ionn_bias_grad: gb must be 4-byte aligned");
     hipStream_t st = as_stream(stream);
-    zero_kernel<<<dim3(unsigned((C + 255) / 256 < 1024 ? (C + 255) / 256 : 1024)), dim3(256), 0, st>>>(gb, C);
+    if (M == 0) {
+        zero_kernel<<<dim3(unsigned((C + 255) / 256 < 1024 ? (C + 255) / 256 : 1024)), dim3(256), 0, st>>>(gb, C);
+        return check_launch("ionn_bias_grad");
+    }
+    const BgGrid g = bg_grid(M, C, C % 16 == 0 && aligned(d, 16));
+    const size_t need = size_t(g.gy * C) * sizeof(int32_t);
+    IONN_REQUIRE(workspace != nullptr && aligned(workspace, 4) && workspace_bytes >= need, IONN_ERR_WORKSPACE,
+                 "ionn_bias_grad: needs a 4-byte aligned workspace of %zu bytes", need);
+    IONN_REQUIRE(g.gx <= 0x7fffffff && g.gy <= 65535, IONN_ERR_SHAPE, "ionn_bias_grad: grid too large");
+    int32_t *part = static_cast<int32_t *>(workspace);
+    const dim3 grid{unsigned(g.gx), unsigned(g.gy), 1u}, block{64u * BG_WAVES, 1u, 1u};
+    if (g.vec) bias_grad_kernel<true><<<grid, block, 0, st>>>(d, M, C, g.rows, part);
+    else bias_grad_kernel<false><<<grid, block, 0, st>>>(d, M, C, g.rows, part);
     if (int rc = check_launch("ionn_bias_grad")) return rc;
-    if (M == 0) return IONN_OK;
-    const bool vec = C % 16 == 0 && aligned(d, 16);
-    const int64_t cols_per_block = vec ? 64 * 16 : 64;
-    const int64_t gx = (C + cols_per_block - 1) / cols_per_block;
-    // about 1024 workgroups in all, at least 64 rows each
-    int64_t gy = (1024 + gx - 1) / gx;
-    int64_t rows = (M + gy - 1) / gy;
-    if (rows < 64) rows = 64;
-    gy = (M + rows - 1) / rows;
-    IONN_REQUIRE(gx <= 0x7fffffff && gy <= 65535, IONN_ERR_SHAPE, "ionn_bias_grad: grid too large");
-    const dim3 grid{unsigned(gx), unsigned(gy), 1u}, block{256u, 1u, 1u};
-    if (vec) bias_grad_kernel<true><<<grid, block, 0, st>>>(d, M, C, rows, gb);
-    else bias_grad_kernel<false><<<grid, block, 0, st>>>(d, M, C, rows, gb);
+    bias_grad_sum<<<dim3(unsigned((C + 255) / 256)), dim3(256), 0, st>>>(part, g.gy, C, gb);
     return check_launch("ionn_bias_grad");
 }
 

@@ -121,11 +121,17 @@ def int_linear_fwd_oss(X, W, offset, mult, k, Y, relu=False, workspace=None, str
                                    _stream(stream)), "int_linear_fwd_oss")
 
 
-def ionn_bias_grad(d, gb, stream=None):
+def ionn_bias_grad_workspace_bytes(M, C):
+    return int(lib().ionn_bias_grad_workspace_bytes(int(M), int(C)))
+
+
+def ionn_bias_grad(d, gb, workspace, stream=None):
     M, C = d.shape
     assert gb.numel() == C
-    check(lib().ionn_bias_grad(_p(d, i8, name="d"), M, C, _p(gb, i32, name="gb"), _stream(stream)),
-          "ionn_bias_grad")
+    check(lib().ionn_bias_grad(_p(d, i8, name="d"), M, C, _p(gb, i32, name="gb"),
+                               _p(workspace, None, name="workspace"),
+                               workspace.numel() * workspace.element_size() if workspace is not None else 0,
+                               _stream(stream)), "ionn_bias_grad")
 
 
 def niti_quantize_update_i32(G, absmax, target_bits, mu, P, shifts_out=None, gq_out=None, stream=None):

@@ -43,7 +43,8 @@ def _gpu_bias_grad(d, misalign=False):
     else:
         dd = to_dev(d)
     gb = torch.full((C,), 12345, dtype=torch.int32, device=dev())  # overwritten
-    ops.ionn_bias_grad(dd, gb)
+    ws = torch.empty(max(ops.ionn_bias_grad_workspace_bytes(M, C), 4), dtype=torch.uint8, device=dev())
+    ops.ionn_bias_grad(dd, gb, ws)
     return host(gb)
 
 
@@ -137,6 +138,18 @@ def test_bias_grad_parity(M, C):
         np.testing.assert_array_equal(_gpu_bias_grad(d, misalign=True), want)
 
 
+def test_bias_grad_needs_workspace():
+    from integer_only_nn_amd._lib import IonnError
+    d = torch.zeros((100, 64), dtype=torch.int8, device=dev())
+    gb = torch.empty(64, dtype=torch.int32, device=dev())
+    with pytest.raises(IonnError):
+        ops.ionn_bias_grad(d, gb, None)
+    n = ops.ionn_bias_grad_workspace_bytes(100, 64)
+    assert n >= 64 * 4
+    with pytest.raises(IonnError):
+        ops.ionn_bias_grad(d, gb, torch.empty(n - 4, dtype=torch.uint8, device=dev()))
+
+
 def test_bias_grad_extreme_columns():
     # every value -128 or 127 in whole columns: the largest sums of the shape
     M, C = 4099, 48
@@ -173,7 +186,8 @@ def test_offset_backward_chain():
     Pn, gq, s, ws = oracle.niti_update_i32(gb, P, 8, 2)
     dd, Pd = to_dev(d), to_dev(P)
     gbd = torch.empty(C, dtype=torch.int32, device=dev())
-    ops.ionn_bias_grad(dd, gbd)
+    gws = torch.empty(ops.ionn_bias_grad_workspace_bytes(M, C), dtype=torch.uint8, device=dev())
+    ops.ionn_bias_grad(dd, gbd, gws)
     am = torch.zeros(1, dtype=torch.int32, device=dev())
     ops.ionn_absmax_i32(gbd, am)
     sh = torch.zeros(2, dtype=torch.int32, device=dev())
