@@ -39,12 +39,11 @@ typedef int v2i __attribute__((ext_vector_type(2)));
 
 constexpr int C = 64;            // input and output channels of the fast path
 constexpr int TP = 256;          // output pixels per tile
-constexpr int NT = 256;          // threads per workgroup of the weight-gradient kernel
-constexpr int NTF = 512;         // threads per workgroup of the fwd / dgrad kernel
+constexpr int NTF = 512;         // threads per workgroup (eight wavefronts)
 constexpr int SLOT = 80;         // LDS bytes per halo slot
 constexpr int HALO_BYTES = 48 * 1024;
-constexpr int HALO_IT = 10;      // 16-byte halo chunks per thread and tile, at most (NT threads)
-constexpr int HALO_ITF = HALO_IT * NT / NTF;  // the same with NTF threads
+constexpr int HALO_CHUNKS = 2560;              // 16-byte halo chunks per tile, at most
+constexpr int HALO_ITF = HALO_CHUNKS / NTF;    // the same per thread
 constexpr int KS = 18;           // 576 / 32
 
 // Bytes of the halo of a 256-pixel tile: rows touched by 256 consecutive
@@ -55,7 +54,7 @@ inline int64_t halo_bytes(int64_t W) {
 }
 
 inline bool fits(int64_t W) {
-    return W >= 1 && halo_bytes(W) <= HALO_BYTES && ((TP - 1 + W - 1) / W + 3) * W * 4 <= int64_t(HALO_IT) * NT;
+    return W >= 1 && halo_bytes(W) <= HALO_BYTES && ((TP - 1 + W - 1) / W + 3) * W * 4 <= HALO_CHUNKS;
 }
 
 // ---- fwd / dgrad ---------------------------------------------------------
@@ -290,10 +289,13 @@ __global__ __launch_bounds__(NTF, 1) void conv3x3_kernel(const int8_t *__restric
 // m0 + 8 (i mod 2), and lane j receives column m0 + j of rows k0..k0+7.  The
 // dY tile sits in LDS as [pixel][80 bytes]; the X operand is read from the
 // zero-padded halo through a per-tile table of each pixel's slot.
-// Wavefront w owns n-blocks [nb0, nb0 + nn) = {0..4, 5..9, 10..13, 14..17}
-// of the 18 32-wide blocks of (tap, ci), for both 32-row blocks of co.
+// Eight wavefronts, two per SIMD, so that one's LDS waits overlap the
+// other's matrix work.  Wavefront w owns n-blocks [nb0, nb0 + nn) of the 18
+// 32-wide blocks of (tap, ci), for both 32-row blocks of co: three blocks
+// for w = 0, 1 and two for the others, so the SIMD pairs (w, w + 4) carry
+// 5, 5, 4 and 4 blocks.
 // ---------------------------------------------------------------------------
-constexpr int WNB = 5;                      // n-blocks per wavefront, at most
+constexpr int WNB = 3;                      // n-blocks per wavefront, at most
 constexpr int DY_BYTES = TP * SLOT;         // one dY tile in LDS
 constexpr int GSZ = 64 * 576;               // elements of G
 
@@ -307,7 +309,7 @@ __device__ __forceinline__ v4i tr_frag(const int8_t *base0, const int8_t *base1)
     return v4i{x.x, x.y, y.x, y.y};
 }
 
-__global__ __launch_bounds__(NT, 1) void conv3x3_wgrad_kernel(const int8_t *__restrict__ dY,
+__global__ __launch_bounds__(NTF, 1) void conv3x3_wgrad_kernel(const int8_t *__restrict__ dY,
                                                               const int8_t *__restrict__ X,
                                                               int32_t *__restrict__ part, int N,
                                                               int H, int W) {
@@ -321,23 +323,23 @@ __global__ __launch_bounds__(NT, 1) void conv3x3_wgrad_kernel(const int8_t *__re
     const int tpi = (HW + TP - 1) / TP;
     const int ntiles = N * tpi;
     const int W2 = W + 2;
-    const int nb0 = wave < 2 ? 5 * wave : 10 + 4 * (wave - 2);
-    const int nn = wave < 2 ? 5 : 4;
+    const int nb0 = wave < 2 ? 3 * wave : 6 + 2 * (wave - 2);
+    const int nn = wave < 2 ? 3 : 2;
 
-    for (int i = tid; i < 2 * HALO_BYTES / 16; i += NT)
+    for (int i = tid; i < 2 * HALO_BYTES / 16; i += NTF)
         reinterpret_cast<v4i *>(&halo[0][0])[i] = v4i{0, 0, 0, 0};
 
-    int hr[HALO_IT], hw4[HALO_IT];
+    int hr[HALO_ITF], hw4[HALO_ITF];
 #pragma unroll
-    for (int i = 0; i < HALO_IT; ++i) {
-        const int q = tid + NT * i;
+    for (int i = 0; i < HALO_ITF; ++i) {
+        const int q = tid + NTF * i;
         hr[i] = q / (4 * W);
         hw4[i] = q - hr[i] * 4 * W;
     }
 
-    // Registers in flight for the next tile: 4 dY chunks, the halo chunks,
-    // and this thread's pixel slot.
-    v4i dv[4], hv[HALO_IT];
+    // Registers in flight for the next tile: 2 dY chunks, the halo chunks,
+    // and (threads below TP) the slot of pixel tid.
+    v4i dv[2], hv[HALO_ITF];
     int myslot = 0;
     auto fetch = [&](int t) __attribute__((always_inline)) {
         const int n = t / tpi, p0 = (t - n * tpi) * TP;
@@ -345,15 +347,15 @@ __global__ __launch_bounds__(NT, 1) void conv3x3_wgrad_kernel(const int8_t *__re
         const int hf = p0 / W, hl = (p0 + valid - 1) / W;
         const int nrows = hl - hf + 3;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int q = tid + NT * i, pl = q >> 2, cc = q & 3;
+        for (int i = 0; i < 2; ++i) {
+            const int q = tid + NTF * i, pl = q >> 2, cc = q & 3;
             v4i v = {0, 0, 0, 0};
             if (pl < valid)
                 v = *reinterpret_cast<const v4i *>(dY + (int64_t(n) * HW + p0 + pl) * C + 16 * cc);
             dv[i] = v;
         }
 #pragma unroll
-        for (int i = 0; i < HALO_IT; ++i) {
+        for (int i = 0; i < HALO_ITF; ++i) {
             const int h = hf - 1 + hr[i];
             v4i v = {0, 0, 0, 0};
             if (hr[i] < nrows && h >= 0 && h < H)
@@ -373,18 +375,18 @@ __global__ __launch_bounds__(NT, 1) void conv3x3_wgrad_kernel(const int8_t *__re
         const int hf = p0 / W, hl = (p0 + valid - 1) / W;
         const int nrows = hl - hf + 3;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int q = tid + NT * i, pl = q >> 2, cc = q & 3;
+        for (int i = 0; i < 2; ++i) {
+            const int q = tid + NTF * i, pl = q >> 2, cc = q & 3;
             *reinterpret_cast<v4i *>(&sdy[bb][pl * SLOT + 16 * cc]) = dv[i];
         }
 #pragma unroll
-        for (int i = 0; i < HALO_IT; ++i) {
+        for (int i = 0; i < HALO_ITF; ++i) {
             if (hr[i] < nrows) {
                 const int w = hw4[i] >> 2, cc = hw4[i] & 3;
                 *reinterpret_cast<v4i *>(&halo[bb][(hr[i] * W2 + w + 1) * SLOT + cc * 16]) = hv[i];
             }
         }
-        sslot[bb][tid] = myslot;
+        if (tid < TP) sslot[bb][tid] = myslot;
     };
 
     v16i acc[WNB][2];

@@ -173,7 +173,7 @@ int int_conv_wgrad(const int8_t *dY, const int8_t *X, int32_t *G, const ionn_con
         ws_bytes >= int_conv_wgrad_workspace_bytes(desc)) {
         const unsigned P = c3_grid(desc);
         int32_t *part = static_cast<int32_t *>(workspace);
-        c3::conv3x3_wgrad_kernel<<<dim3(P), dim3(c3::NT), 0, st>>>(dY, X, part, int(desc->N),
+        c3::conv3x3_wgrad_kernel<<<dim3(P), dim3(c3::NTF), 0, st>>>(dY, X, part, int(desc->N),
                                                                     int(desc->H), int(desc->W));
         if (int rc = check_launch("int_conv_wgrad")) return rc;
         const int xb = c3::GSZ / 1024;
