@@ -152,11 +152,15 @@ int int_output_error(const int8_t *out, const int32_t *labels, int64_t B,
 
 /* ------------------------------------------------------------------------ */
 /* Conv2D contractions ([TI] section 7), NHWC / OHWI, cross-correlation.     */
-/* Supported geometry: KH = KW = 3, stride 1, pad 1, dilation 1, groups 1;   */
-/* anything else returns IONN_ERR_UNSUPPORTED (the page's export refuses     */
-/* grouped and dilated convolutions outright).  Output size = input size.   */
-/* N, H, W, Cin, Cout >= 0; Cin and Cout must be multiples of 16 (else       */
-/* IONN_ERR_UNSUPPORTED); every tensor must fit in 2^31 elements.            */
+/* Geometry: stride 1, dilation 1, groups 1 (anything else returns           */
+/* IONN_ERR_UNSUPPORTED; the page's export refuses grouped and dilated       */
+/* convolutions outright); KH, KW in [1, 1024]; zero padding P = pad in     */
+/* [0, 1024] (else IONN_ERR_RANGE).  Output Ho = H + 2P - KH + 1,             */
+/* Wo = W + 2P - KW + 1.  N, H, W, Cin, Cout >= 0; every tensor must hold    */
+/* fewer than 2^31 elements.  3x3 / pad 1 with Cin and Cout multiples of 16  */
+/* runs on the matrix cores and needs 16-byte aligned tensors; other         */
+/* geometries (e.g. the page's 16 x 2 "valid" filter bank) run on direct     */
+/* kernels and need 4-byte aligned int32 tensors only.                       */
 /* ------------------------------------------------------------------------ */
 
 typedef struct ionn_conv_desc {
@@ -164,14 +168,15 @@ typedef struct ionn_conv_desc {
     int32_t KH, KW, stride, pad, dilation, groups;
 } ionn_conv_desc;
 
-/* Y[n,h,w,co] = sum_{kh,kw,ci} X[n,h+kh-1,w+kw-1,ci] * Wt[co,kh,kw,ci]
+/* Y[n,h,w,co] = sum_{kh,kw,ci} X[n,h+kh-P,w+kw-P,ci] * Wt[co,kh,kw,ci]
  * (zero outside the image).  X: int8 [N][H][W][Cin]; Wt: int8
- * [Cout][3][3][Cin]; Y: int32 [N][H][W][Cout] (written). */
+ * [Cout][KH][KW][Cin]; Y: int32 [N][Ho][Wo][Cout] (written). */
 int int_conv_fwd(const int8_t *X, const int8_t *Wt, int32_t *Y,
                  const ionn_conv_desc *desc, uint32_t *absmax_Y, void *stream);
 
-/* dX[n,h,w,ci] = sum_{kh,kw,co} dY[n,h-kh+1,w-kw+1,co] * Wt[co,kh,kw,ci].
- * dY: int8 [N][H][W][Cout]; dX: int32 [N][H][W][Cin] (written). */
+/* dX[n,h,w,ci] = sum_{kh,kw,co} dY[n,h-kh+P,w-kw+P,co] * Wt[co,kh,kw,ci]
+ * (terms outside dY dropped).  dY: int8 [N][Ho][Wo][Cout]; dX: int32
+ * [N][H][W][Cin] (written). */
 int int_conv_dgrad(const int8_t *dY, const int8_t *Wt, int32_t *dX,
                    const ionn_conv_desc *desc, uint32_t *absmax_dX,
                    void *stream);
@@ -182,8 +187,8 @@ int int_conv_dgrad(const int8_t *dY, const int8_t *Wt, int32_t *dX,
  * has no fast path (the call then needs no workspace). */
 size_t int_conv_wgrad_workspace_bytes(const ionn_conv_desc *desc);
 
-/* G[co,kh,kw,ci] = sum_{n,h,w} dY[n,h,w,co] * X[n,h+kh-1,w+kw-1,ci].
- * G: int32 [Cout][3][3][Cin] (written).  workspace (nullable, device,
+/* G[co,kh,kw,ci] = sum_{n,h,w} dY[n,h,w,co] * X[n,h+kh-P,w+kw-P,ci] over the
+ * output positions (h, w) < (Ho, Wo).  G: int32 [Cout][KH][KW][Cin] (written).  workspace (nullable, device,
  * 16-byte aligned, ws_bytes long, owned by the caller, clobbered): with at
  * least int_conv_wgrad_workspace_bytes(desc) bytes, the gradient is
  * computed as per-compute-unit partial sums reduced in two passes; without

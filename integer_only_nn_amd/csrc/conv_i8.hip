@@ -16,6 +16,12 @@
 // zeros outside it.  Integer atomics are exact and order-free (sums are
 // modulo 2^32), so the split-K weight gradient is bit-identical to any
 // other summation order.
+//
+// Other geometries at stride 1 (any KH x KW, any zero padding P, any
+// channel counts; output Ho = H + 2P - KH + 1, Wo = W + 2P - KW + 1), such
+// as the 16 x 2 "valid" filter bank of the page's example network, run on
+// direct kernels: one thread per output element of fwd and dgrad, one per
+// weight element and pixel range of wgrad.  These are small-layer paths.
 #include "gemm_core.h"
 #include "conv3x3.h"
 
@@ -35,24 +41,141 @@ __global__ void zero_i32_kernel(int32_t *C, int64_t n) {
         C[i] = 0;
 }
 
+int64_t out_h(const ionn_conv_desc *d) { return d->H + 2 * int64_t(d->pad) - d->KH + 1; }
+int64_t out_w(const ionn_conv_desc *d) { return d->W + 2 * int64_t(d->pad) - d->KW + 1; }
+
 int check_desc(const ionn_conv_desc *d, const char *name) {
     IONN_REQUIRE(d != nullptr, IONN_ERR_ARG, "%s: desc is NULL", name);
     IONN_REQUIRE(d->N >= 0 && d->H >= 0 && d->W >= 0 && d->Cin >= 0 && d->Cout >= 0,
                  IONN_ERR_SHAPE, "%s: negative size", name);
-    IONN_REQUIRE(d->KH == 3 && d->KW == 3 && d->stride == 1 && d->pad == 1 && d->dilation == 1 &&
-                     d->groups == 1,
-                 IONN_ERR_UNSUPPORTED,
-                 "%s: only 3x3 kernels, stride 1, pad 1, dilation 1, groups 1 are implemented "
-                 "(got %dx%d s%d p%d d%d g%d)",
-                 name, d->KH, d->KW, d->stride, d->pad, d->dilation, d->groups);
-    IONN_REQUIRE(d->Cin % 16 == 0 && d->Cout % 16 == 0, IONN_ERR_UNSUPPORTED,
-                 "%s: Cin and Cout must be multiples of 16 (got %lld, %lld)", name,
-                 (long long)d->Cin, (long long)d->Cout);
-    const int64_t npix = d->N * d->H * d->W;
+    IONN_REQUIRE(d->stride == 1 && d->dilation == 1 && d->groups == 1, IONN_ERR_UNSUPPORTED,
+                 "%s: only stride 1, dilation 1, groups 1 are implemented (got s%d d%d g%d)", name,
+                 d->stride, d->dilation, d->groups);
+    IONN_REQUIRE(d->KH >= 1 && d->KW >= 1 && d->KH <= 1024 && d->KW <= 1024 && d->pad >= 0 &&
+                     d->pad <= 1024,
+                 IONN_ERR_RANGE, "%s: kernel %dx%d with pad %d (need KH, KW in [1, 1024], pad in [0, 1024])",
+                 name, d->KH, d->KW, d->pad);
+    const int64_t npix = d->N * d->H * d->W, Ho = out_h(d), Wo = out_w(d);
+    const int64_t nout = d->N * (Ho > 0 ? Ho : 0) * (Wo > 0 ? Wo : 0);
     IONN_REQUIRE(npix <= kMaxDim && npix * d->Cin <= kMaxDim && npix * d->Cout <= kMaxDim &&
-                     9 * d->Cin * d->Cout <= kMaxDim,
+                     nout * d->Cout <= kMaxDim && d->Cin * d->KH * d->KW <= kMaxDim &&
+                     d->Cout * d->KH * d->KW * d->Cin <= kMaxDim,
                  IONN_ERR_SHAPE, "%s: tensors must hold fewer than 2^31 elements", name);
     return IONN_OK;
+}
+
+// The 3 x 3 / pad 1 paths (implicit GEMM, and the 64-channel kernels): 16-byte
+// channel chunks, so Cin and Cout are multiples of 16 and tensors 16-byte aligned.
+bool geom33(const ionn_conv_desc *d) {
+    return d->KH == 3 && d->KW == 3 && d->pad == 1 && d->Cin % 16 == 0 && d->Cout % 16 == 0;
+}
+
+// ---- direct kernels for other geometries (stride 1) ----
+__global__ __launch_bounds__(256) void conv_direct_fwd(const int8_t *__restrict__ X, const int8_t *__restrict__ Wt,
+                                                       int32_t *__restrict__ Y, int H, int W, int Cin, int Cout,
+                                                       int KH, int KW, int P, int Ho, int Wo, int64_t n_out,
+                                                       uint32_t *__restrict__ absmax) {
+    uint32_t amax = 0;
+    for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n_out;
+         i += int64_t(gridDim.x) * blockDim.x) {
+        const int co = int(i % Cout);
+        int64_t t = i / Cout;
+        const int wo = int(t % Wo);
+        t /= Wo;
+        const int ho = int(t % Ho);
+        const int64_t n = t / Ho;
+        uint32_t acc = 0;
+        for (int kh = 0; kh < KH; ++kh) {
+            const int y = ho + kh - P;
+            if (y < 0 || y >= H) continue;
+            for (int kw = 0; kw < KW; ++kw) {
+                const int x = wo + kw - P;
+                if (x < 0 || x >= W) continue;
+                const int8_t *xp = X + ((n * H + y) * W + x) * Cin;
+                const int8_t *wp = Wt + ((int64_t(co) * KH + kh) * KW + kw) * Cin;
+                for (int ci = 0; ci < Cin; ++ci) acc += uint32_t(int32_t(xp[ci]) * int32_t(wp[ci]));
+            }
+        }
+        Y[i] = int32_t(acc);
+        amax = max(amax, abs_u32(int32_t(acc)));
+    }
+    if (absmax) {
+        amax = wave_max_u32(amax);
+        if ((threadIdx.x & 63) == 0) publish_max_u32(absmax, amax);
+    }
+}
+
+__global__ __launch_bounds__(256) void conv_direct_dgrad(const int8_t *__restrict__ dY,
+                                                         const int8_t *__restrict__ Wt, int32_t *__restrict__ dX,
+                                                         int H, int W, int Cin, int Cout, int KH, int KW, int P,
+                                                         int Ho, int Wo, int64_t n_in,
+                                                         uint32_t *__restrict__ absmax) {
+    uint32_t amax = 0;
+    for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n_in;
+         i += int64_t(gridDim.x) * blockDim.x) {
+        const int ci = int(i % Cin);
+        int64_t t = i / Cin;
+        const int w = int(t % W);
+        t /= W;
+        const int h = int(t % H);
+        const int64_t n = t / H;
+        uint32_t acc = 0;
+        for (int kh = 0; kh < KH; ++kh) {
+            const int y = h - kh + P;
+            if (y < 0 || y >= Ho) continue;
+            for (int kw = 0; kw < KW; ++kw) {
+                const int x = w - kw + P;
+                if (x < 0 || x >= Wo) continue;
+                const int8_t *dp = dY + ((n * Ho + y) * Wo + x) * Cout;
+                const int8_t *wp = Wt + (int64_t(kh) * KW + kw) * Cin + ci;
+                const int64_t wstride = int64_t(KH) * KW * Cin;
+                for (int co = 0; co < Cout; ++co) acc += uint32_t(int32_t(dp[co]) * int32_t(wp[co * wstride]));
+            }
+        }
+        dX[i] = int32_t(acc);
+        amax = max(amax, abs_u32(int32_t(acc)));
+    }
+    if (absmax) {
+        amax = wave_max_u32(amax);
+        if ((threadIdx.x & 63) == 0) publish_max_u32(absmax, amax);
+    }
+}
+
+// G (zeroed) += the sum over output rows [r0, r1) of range blockIdx.y, rows
+// being (n, ho) pairs; one thread per weight element.
+__global__ __launch_bounds__(256) void conv_direct_wgrad(const int8_t *__restrict__ dY,
+                                                         const int8_t *__restrict__ X, int32_t *__restrict__ G,
+                                                         int H, int W, int Cin, int Cout, int KH, int KW, int P,
+                                                         int Ho, int Wo, int64_t rows, int64_t rows_per,
+                                                         int64_t n_g) {
+    const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i >= n_g) return;
+    const int ci = int(i % Cin);
+    int64_t t = i / Cin;
+    const int kw = int(t % KW);
+    t /= KW;
+    const int kh = int(t % KH);
+    const int co = int(t / KH);
+    const int64_t r0 = int64_t(blockIdx.y) * rows_per, r1 = min(rows, r0 + rows_per);
+    uint32_t acc = 0;
+    for (int64_t r = r0; r < r1; ++r) {
+        const int64_t n = r / Ho;
+        const int ho = int(r - n * Ho);
+        const int y = ho + kh - P;
+        if (y < 0 || y >= H) continue;
+        for (int wo = 0; wo < Wo; ++wo) {
+            const int x = wo + kw - P;
+            if (x < 0 || x >= W) continue;
+            acc += uint32_t(int32_t(dY[((n * Ho + ho) * Wo + wo) * Cout + co]) *
+                            int32_t(X[((n * H + y) * W + x) * Cin + ci]));
+        }
+    }
+    if (acc) atomicAdd(G + i, int32_t(acc));
+}
+
+unsigned direct_blocks(int64_t n) {
+    int64_t b = (n + 255) / 256;
+    return unsigned(b < 1 ? 1 : (b > 4096 ? 4096 : b));
 }
 
 // Compute units of the current device (persistent grids).
@@ -70,8 +193,8 @@ int device_cus() {
 
 // The 64-channel halo-tiled kernel applies (see conv3x3.h).
 bool fast_c64(const ionn_conv_desc *d, const void *in, const void *w, const void *out) {
-    return d->Cin == 64 && d->Cout == 64 && c3::fits(d->W) && aligned(in, 16) && aligned(w, 16) &&
-           aligned(out, 16);
+    return geom33(d) && d->Cin == 64 && d->Cout == 64 && c3::fits(d->W) && aligned(in, 16) &&
+           aligned(w, 16) && aligned(out, 16);
 }
 
 // fwd / dgrad fast path: 64 -> 64 channels, the halo in one LDS buffer and
@@ -99,6 +222,17 @@ int int_conv_fwd(const int8_t *X, const int8_t *Wt, int32_t *Y, const ionn_conv_
     clear_error();
     if (int rc = check_desc(desc, "int_conv_fwd")) return rc;
     const int npix = int(desc->N * desc->H * desc->W), Cin = int(desc->Cin), Cout = int(desc->Cout);
+    if (!geom33(desc)) {
+        const int64_t Ho = out_h(desc), Wo = out_w(desc), n_out = desc->N * Ho * Wo * Cout;
+        if (Ho <= 0 || Wo <= 0 || n_out == 0) return IONN_OK;
+        IONN_REQUIRE(Y && (Cin == 0 || (X && Wt)), IONN_ERR_ARG, "int_conv_fwd: NULL tensor");
+        IONN_REQUIRE(aligned(Y, 4) && aligned(absmax_Y, 4), IONN_ERR_ALIGN,
+                     "int_conv_fwd: Y/absmax must be 4-byte aligned");
+        conv_direct_fwd<<<dim3(direct_blocks(n_out)), dim3(256), 0, as_stream(stream)>>>(
+            X, Wt, Y, int(desc->H), int(desc->W), Cin, Cout, desc->KH, desc->KW, desc->pad, int(Ho), int(Wo),
+            n_out, absmax_Y);
+        return check_launch("int_conv_fwd");
+    }
     if (npix == 0 || Cout == 0) return IONN_OK;
     IONN_REQUIRE(X && Wt && Y, IONN_ERR_ARG, "int_conv_fwd: NULL tensor");
     IONN_REQUIRE(aligned(X, 16) && aligned(Wt, 16) && aligned(Y, 16) && aligned(absmax_Y, 4),
@@ -129,6 +263,23 @@ int int_conv_dgrad(const int8_t *dY, const int8_t *Wt, int32_t *dX, const ionn_c
     clear_error();
     if (int rc = check_desc(desc, "int_conv_dgrad")) return rc;
     const int npix = int(desc->N * desc->H * desc->W), Cin = int(desc->Cin), Cout = int(desc->Cout);
+    if (!geom33(desc)) {
+        const int64_t Ho = out_h(desc), Wo = out_w(desc), n_in = int64_t(npix) * Cin;
+        if (n_in == 0) return IONN_OK;
+        const bool any_out = Ho > 0 && Wo > 0 && Cout > 0;
+        IONN_REQUIRE(dX && (!any_out || (dY && Wt)), IONN_ERR_ARG, "int_conv_dgrad: NULL tensor");
+        IONN_REQUIRE(aligned(dX, 4) && aligned(absmax_dX, 4), IONN_ERR_ALIGN,
+                     "int_conv_dgrad: dX/absmax must be 4-byte aligned");
+        hipStream_t st = as_stream(stream);
+        if (!any_out) {
+            zero_i32_kernel<<<dim3(direct_blocks(n_in)), dim3(256), 0, st>>>(dX, n_in);
+            return check_launch("int_conv_dgrad");
+        }
+        conv_direct_dgrad<<<dim3(direct_blocks(n_in)), dim3(256), 0, st>>>(
+            dY, Wt, dX, int(desc->H), int(desc->W), Cin, Cout, desc->KH, desc->KW, desc->pad, int(Ho), int(Wo),
+            n_in, absmax_dX);
+        return check_launch("int_conv_dgrad");
+    }
     if (npix == 0 || Cin == 0) return IONN_OK;
     IONN_REQUIRE(dY && Wt && dX, IONN_ERR_ARG, "int_conv_dgrad: NULL tensor");
     IONN_REQUIRE(aligned(dY, 16) && aligned(Wt, 16) && aligned(dX, 16) && aligned(absmax_dX, 4),
@@ -155,7 +306,7 @@ int int_conv_dgrad(const int8_t *dY, const int8_t *Wt, int32_t *dX, const ionn_c
 }
 
 size_t int_conv_wgrad_workspace_bytes(const ionn_conv_desc *desc) {
-    if (desc == nullptr || desc->Cin != 64 || desc->Cout != 64 || !c3::fits(desc->W)) return 0;
+    if (desc == nullptr || !geom33(desc) || desc->Cin != 64 || desc->Cout != 64 || !c3::fits(desc->W)) return 0;
     return size_t(c3::wgrad_rows(device_cus())) * c3::GSZ * sizeof(int32_t);
 }
 
@@ -165,6 +316,33 @@ int int_conv_wgrad(const int8_t *dY, const int8_t *X, int32_t *G, const ionn_con
     if (int rc = check_desc(desc, "int_conv_wgrad")) return rc;
     const int npix = int(desc->N * desc->H * desc->W), Cin = int(desc->Cin), Cout = int(desc->Cout);
     if (Cin == 0 || Cout == 0) return IONN_OK;
+    if (!geom33(desc)) {
+        const int64_t Ho = out_h(desc), Wo = out_w(desc);
+        const int64_t n_g = int64_t(Cout) * desc->KH * desc->KW * Cin;
+        const int64_t rows = (Ho > 0 && Wo > 0) ? desc->N * Ho : 0;
+        IONN_REQUIRE(G && (rows == 0 || (dY && X)), IONN_ERR_ARG, "int_conv_wgrad: NULL tensor");
+        IONN_REQUIRE(aligned(G, 4) && aligned(absmax_G, 4), IONN_ERR_ALIGN,
+                     "int_conv_wgrad: G/absmax must be 4-byte aligned");
+        hipStream_t st = as_stream(stream);
+        zero_i32_kernel<<<dim3(direct_blocks(n_g)), dim3(256), 0, st>>>(G, n_g);
+        if (int rc = check_launch("int_conv_wgrad")) return rc;
+        if (rows > 0) {
+            // enough (weight, row range) threads to fill the chip, ranges of at least 8 rows
+            const int64_t gx = (n_g + 255) / 256;
+            int64_t ry = (65536 + gx * 256 - 1) / (gx * 256);
+            int64_t per = (rows + ry - 1) / ry;
+            if (per < 8) per = 8;
+            ry = (rows + per - 1) / per;
+            IONN_REQUIRE(gx <= 0x7fffffff && ry <= 65535, IONN_ERR_SHAPE, "int_conv_wgrad: grid too large");
+            const dim3 grid{unsigned(gx), unsigned(ry), 1u};
+            conv_direct_wgrad<<<grid, dim3(256), 0, st>>>(dY, X, G, int(desc->H), int(desc->W), Cin, Cout,
+                                                          desc->KH, desc->KW, desc->pad, int(Ho), int(Wo), rows,
+                                                          per, n_g);
+            if (int rc = check_launch("int_conv_wgrad")) return rc;
+        }
+        if (absmax_G) return launch_absmax_i32(G, n_g, absmax_G, st);
+        return IONN_OK;
+    }
     IONN_REQUIRE(G && (npix == 0 || (dY && X)), IONN_ERR_ARG, "int_conv_wgrad: NULL tensor");
     IONN_REQUIRE(aligned(dY, 16) && aligned(X, 16) && aligned(G, 16) && aligned(absmax_G, 4),
                  IONN_ERR_ALIGN, "int_conv_wgrad: tensors must be 16-byte aligned");

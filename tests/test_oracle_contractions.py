@@ -162,6 +162,33 @@ def test_conv_vs_torch_float64(N, H, Wd, Cin, Cout, K, P):
         assert oracle.conv_wgrad_at(dY, X, K, K, P, co, kh, kw, ci) == G[co, kh, kw, ci]
 
 
+def _torch_conv_refs_rect(X, W, dY, P):
+    Xt = torch.from_numpy(X.astype(np.float64)).permute(0, 3, 1, 2).contiguous()
+    Wt = torch.from_numpy(W.astype(np.float64)).permute(0, 3, 1, 2).contiguous()
+    dYt = torch.from_numpy(dY.astype(np.float64)).permute(0, 3, 1, 2).contiguous()
+    Y = torch.nn.functional.conv2d(Xt, Wt, padding=P)
+    dX = torch.nn.grad.conv2d_input(Xt.shape, Wt, dYt, padding=P)
+    G = torch.nn.grad.conv2d_weight(Xt, Wt.shape, dYt, padding=P)
+    back = lambda t: t.permute(0, 2, 3, 1).contiguous().numpy().astype(np.int64)
+    return back(Y), back(dX), back(G)
+
+
+# rectangular kernels, including the 16 x 2 "valid" filter bank of the TI
+# page's arc-fault example network (input 64 x 2 x 1, 3 filters -> 49 x 1 x 3)
+@pytest.mark.parametrize("N,H,Wd,Cin,Cout,KH,KW,P", [(8, 64, 2, 1, 3, 16, 2, 0), (2, 5, 4, 3, 2, 1, 3, 1),
+                                                     (1, 9, 6, 2, 5, 4, 2, 1), (3, 7, 7, 4, 3, 5, 1, 0)])
+def test_conv_rectangular_vs_torch_float64(N, H, Wd, Cin, Cout, KH, KW, P):
+    rng = np.random.default_rng(H * 31 + KH * 7 + KW)
+    X = rng.integers(-128, 128, (N, H, Wd, Cin)).astype(np.int8)
+    W = rng.integers(-128, 128, (Cout, KH, KW, Cin)).astype(np.int8)
+    Ho, Wo = H + 2 * P - KH + 1, Wd + 2 * P - KW + 1
+    dY = rng.integers(-128, 128, (N, Ho, Wo, Cout)).astype(np.int8)
+    Yr, dXr, Gr = _torch_conv_refs_rect(X, W, dY, P)
+    np.testing.assert_array_equal(oracle.conv_fwd(X, W, P), Yr)
+    np.testing.assert_array_equal(oracle.conv_dgrad(dY, W, X.shape, P), dXr)
+    np.testing.assert_array_equal(oracle.conv_wgrad(dY, X, KH, KW, P), Gr)
+
+
 def test_conv_adjoint_and_1x1_equals_linear():
     d = ionn_synth.conv3x3(N=2, H=9, W=7, Cin=16, Cout=8, seed=4)
     X, W, dY = d["X"], d["W"], d["dY"][..., :8]
