@@ -11,7 +11,8 @@ Uniform integers: lo + (u mod (hi - lo + 1)).  Normals: Box-Muller on
 consecutive pairs, u1 = ((x0 >> 11) + 1) * 2^-53 in (0, 1],
 u2 = (x1 >> 11) * 2^-53, then sigma * z rounded half away from zero and
 clipped.  Stream ids: X=1, W=2, dY=3, labels=4, W1..W3=5..7, exponents of
-X/W/dY = 8..10.
+X/W/dY = 8..10; per layer l of a model, offsets / multipliers / shifts =
+20 + 3 l, 21 + 3 l, 22 + 3 l; target magnitudes = 40, 41.
 """
 import numpy as np
 
@@ -125,4 +126,32 @@ def dfp16_gemm(M=25088, K=256, N=1024, seed=0):
         W=normal_int(seed, SID_W, (N, K), 4000.0, -32768, 32767, dtype=np.int16),
         dY=normal_int(seed, SID_DY, (M, N), 4000.0, -32768, 32767, dtype=np.int16),
         eX=e(SID_EX), eW=e(SID_EW), edY=e(SID_EDY),
+    )
+
+
+def arc_fault(B=8, seed=0):
+    """The example network of the TI on-device training page (arc-fault
+    detection): input 64 x 2 x 1 int8, Conv 3 filters 16 x 2 valid + ReLU
+    (-> 49 x 1 x 3 = 147), Linear 160 + ReLU, Linear 2; batch 8.  Weights
+    ~ round(N(0, 25)) (conv) and round(N(0, 20)) (linear); int32 offsets
+    ~ U[-256, 255]; multipliers ~ U[1, 4]; per-filter right shifts
+    ~ U{8..10}; inputs ~ round(N(0, 40)); labels ~ U{0, 1}; per-class target
+    magnitudes ~ U[60, 100] (true class) and U[-100, -60] (other class)."""
+    shapes = [(3, 16, 2, 1), (160, 147), (2, 160)]
+    sigma = [25.0, 20.0, 20.0]
+    layers = []
+    for l, shp in enumerate(shapes):
+        C = shp[0]
+        layers.append(dict(
+            W=normal_int(seed, SID_W1 + l, shp, sigma[l], -128, 127),
+            offset=uniform_int(seed, 20 + 3 * l, (C,), -256, 255, dtype=np.int32),
+            mult=uniform_int(seed, 21 + 3 * l, (C,), 1, 4, dtype=np.int32),
+            k=uniform_int(seed, 22 + 3 * l, (C,), 8, 10, dtype=np.int8),
+        ))
+    return dict(
+        X=normal_int(seed, SID_X, (B, 64, 2, 1), 40.0, -128, 127),
+        labels=uniform_int(seed, SID_LABELS, (B,), 0, 1, dtype=np.int32),
+        layers=layers,
+        tmc=uniform_int(seed, 40, (2,), 60, 100),
+        tmw=uniform_int(seed, 41, (2,), -100, -60),
     )

@@ -56,6 +56,7 @@ def _declare(L):
         "ora_relu_mask": (None, [_P, _P, _I64]),
         "ora_output_error": (None, [_P, _P, _I64, _I64, _I, _P]),
         "ora_oss_requant": (None, [_P, _P, _P, _P, _I64, _I64, _I, _P]),
+        "ora_mse_grad_targets": (None, [_P, _P, _I64, _I64, _P, _P, _P]),
         "ora_bias_grad": (None, [_P, _I64, _I64, _P]),
         "ora_niti_update_i32": (None, [_P, _P, _I64, _I, _I, _P, _P, _P]),
         "ora_conv_fwd": (_I64, [_P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I, _I, _I]),
@@ -173,6 +174,15 @@ def oss_requant(acc, offset, mult, k, relu=False):
     lib().ora_oss_requant(_c(acc, np.int32), _c(offset, np.int32), _c(mult, np.int32),
                           _c(k, np.int8), M, C, int(bool(relu)), _c(out, np.int8))
     return out
+
+
+def mse_grad_targets(out, labels, tmc, tmw):
+    """int32 [B][C] = out - (c == label ? tmc[c] : tmw[c])."""
+    B, C = out.shape
+    g = np.empty((B, C), np.int32)
+    lib().ora_mse_grad_targets(_c(out, np.int8), _c(labels, np.int32), B, C, _c(tmc, np.int8),
+                               _c(tmw, np.int8), _c(g, np.int32))
+    return g
 
 
 def bias_grad(d):

@@ -666,3 +666,15 @@ void ora_niti_update_i32(const int32_t *G, int32_t *P, int64_t n, int target_bit
     if (shift_out) *shift_out = s;
     if (weight_shift_out) *weight_shift_out = ws;
 }
+
+/* [TI] section 8, Step 3: the MSE loss against per-class target magnitudes;
+ * its gradient with respect to the output. */
+void ora_mse_grad_targets(const int8_t *out, const int32_t *labels, int64_t B, int64_t C,
+                          const int8_t *tmc, const int8_t *tmw, int32_t *g)
+{
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t c = 0; c < C; ++c) {
+            const int32_t t = (c == (int64_t)labels[b]) ? (int32_t)tmc[c] : (int32_t)tmw[c];
+            g[b * C + c] = (int32_t)out[b * C + c] - t;
+        }
+}

@@ -136,6 +136,14 @@ int ora_dfp16_wgrad(const int16_t *dY, int edY, const int16_t *X, int eX,
 /* Gavg = mean(|g|) * 2^(e_g - e_w)   ([APT] Equation 4, epsilon = 2^e_w). */
 double ora_gavg(const int16_t *g, int64_t n, int e_g, int e_w);
 
+/* Gradient of the MSE loss against per-class target magnitudes ([TI]
+ * section 8, PC-side Step 3: TARGET_MAG_CORRECT[c] for the true class,
+ * TARGET_MAG_WRONG[c] for the others), the loss delta the backward pass
+ * reads (reading U27):
+ *   g[b][c] = out[b][c] - (c == labels[b] ? tmc[c] : tmw[c]). */
+void ora_mse_grad_targets(const int8_t *out, const int32_t *labels, int64_t B, int64_t C,
+                          const int8_t *tmc, const int8_t *tmw, int32_t *g);
+
 /* ---- Offsets (bias) and the static OSS forward requantisation ([TI]
  * section 7 "INT_LAYERS": int32 offsets updated by the backward pass, int8
  * per-filter right shifts k and multipliers mult; section 8, "PC-Side Steps",

@@ -14,9 +14,9 @@ Operations", sections 3.1 and 4 (DFP primitives, chunked accumulation);
 """
 import numpy as np
 
-from . import (conv_dgrad, conv_fwd, conv_wgrad, dfp16_dgrad, dfp16_fwd, dfp16_wgrad, gavg,
-               linear_dgrad, linear_fwd, linear_wgrad, niti_requant, niti_update, output_error,
-               relu_mask)
+from . import (bias_grad, conv_dgrad, conv_fwd, conv_wgrad, dfp16_dgrad, dfp16_fwd, dfp16_wgrad,
+               gavg, linear_dgrad, linear_fwd, linear_wgrad, niti_requant, niti_update,
+               niti_update_i32, oss_requant, output_error, mse_grad_targets, relu_mask)
 
 # Readings: weight-update target_bits = 8 and mu_weight = 2 for every layer
 # (U8); propagated deltas and requantised activations use target_bits = 7.
@@ -115,3 +115,94 @@ def dfp16_step(X, eX, W, eW, dY, edY, chunk=64):
     G, eG, accG = dfp16_wgrad(dY, edY, X, eX, chunk)
     return dict(Y=Y, eY=eY, accY=accY, dX=dX, edX=edX, accdX=accdX, G=G, eG=eG, accG=accG,
                 gavg=gavg(G, eG, eW))
+
+
+# ---------------------------------------------------------------------------
+# Model-level driver: the INT_LAYERS forward and backward of the TI page
+# (section 7: layer types Conv2D, Conv2D+ReLU, Linear, Linear+ReLU with int8
+# weights, int32 offsets and OSS shifts/multipliers; section 8: the OSS chain
+# and the per-class TARGET_MAG loss; section 3: NITI updates).  A layer is a
+# dict: kind "conv" or "linear", relu, for conv KH, KW, pad and the input
+# geometry H, W, Cin, Cout; for linear IN, OUT; and the parameters weight
+# (int8), offset (int32), mult (int32), k (int8).
+# Readings U26-U28 of the design notes.
+# ---------------------------------------------------------------------------
+
+def _as_rows(a, L):
+    """Activation a of a layer's input, as the layer reads it."""
+    if L["kind"] == "conv":
+        return a.reshape(-1, L["H"], L["W"], L["Cin"])
+    return a.reshape(a.shape[0], -1)
+
+
+def model_forward(layers, X):
+    """a_l = OSS(contraction(a_{l-1}, W_l); offset_l, mult_l, k_l, relu_l).
+    Returns the activations [X, a_1, ..., a_L] (int8, conv outputs NHWC)."""
+    acts = [X]
+    for L in layers:
+        a = _as_rows(acts[-1], L)
+        if L["kind"] == "conv":
+            z = conv_fwd(a, L["weight"], L["pad"])
+        else:
+            z = linear_fwd(a, L["weight"])
+        C = z.shape[-1]
+        y = oss_requant(z.reshape(-1, C), L["offset"], L["mult"], L["k"], relu=L["relu"])
+        acts.append(y.reshape(z.shape))
+    return acts
+
+
+def model_step(layers, X, labels, tmc, tmw, tb_d=TB_DELTA, tb_w=TB_WEIGHT, mu=MU_WEIGHT):
+    """One training step of the model (forward, the MSE gradient against the
+    per-class targets, backward with updates of every layer's W and offsets).
+
+    Backward, l = L..1, with delta_L = requant(out - target, tb_d):
+      gb_l = column sums of delta_l (rows: batch, times pixels for conv);
+      G_l = wgrad(delta_l, a_{l-1});
+      for l > 1: d = dgrad(delta_l, W_l) with the pre-update W_l, masked by
+        a_{l-1} > 0 when layer l-1 has a ReLU, delta_{l-1} = requant(d, tb_d);
+      W_l = NITI update(G_l), offset_l = NITI int32 update(gb_l).
+    The first layer's input gradient is not formed: nothing consumes it.
+    Returns (new layers, record of tensors and shifts)."""
+    acts = model_forward(layers, X)
+    e32 = mse_grad_targets(acts[-1].reshape(acts[-1].shape[0], -1), labels, tmc, tmw)
+    delta, s_err = niti_requant(e32, tb_d)
+    new = [dict(L) for L in layers]
+    rec = dict(acts=acts, e32=e32, s_err=s_err, deltas={len(layers): delta}, s_dgrad={}, s_w={},
+               s_b={}, G={}, gb={})
+    for l in range(len(layers) - 1, -1, -1):
+        L = layers[l]
+        a_in = _as_rows(acts[l], L)
+        if L["kind"] == "conv":
+            Ho = L["H"] + 2 * L["pad"] - L["KH"] + 1
+            Wo = L["W"] + 2 * L["pad"] - L["KW"] + 1
+            d_out = delta.reshape(-1, Ho, Wo, L["Cout"])
+            G = conv_wgrad(d_out, a_in, L["KH"], L["KW"], L["pad"])
+        else:
+            d_out = delta.reshape(delta.shape[0], -1)
+            G = linear_wgrad(d_out, a_in)
+        gb = bias_grad(d_out.reshape(-1, d_out.shape[-1]))
+        rec["G"][l], rec["gb"][l] = G, gb
+        if l > 0:
+            if L["kind"] == "conv":
+                d32 = conv_dgrad(d_out, L["weight"], a_in.shape, L["pad"])
+            else:
+                d32 = linear_dgrad(d_out, L["weight"])
+            if layers[l - 1]["relu"]:
+                d32 = relu_mask(d32, a_in)
+            delta, rec["s_dgrad"][l] = niti_requant(d32, tb_d)
+            rec["deltas"][l] = delta
+        new[l]["weight"], _, s, ws = niti_update(G, L["weight"], tb_w, mu)
+        rec["s_w"][l] = (s, ws)
+        new[l]["offset"], _, s, ws = niti_update_i32(gb, L["offset"], tb_w, mu)
+        rec["s_b"][l] = (s, ws)
+    return new, rec
+
+
+def arc_fault_layers(d):
+    """The arc-fault example network (ionn_synth.arc_fault) as model layers."""
+    prm = [dict(weight=q["W"], offset=q["offset"], mult=q["mult"], k=q["k"]) for q in d["layers"]]
+    return [
+        dict(kind="conv", relu=True, H=64, W=2, Cin=1, Cout=3, KH=16, KW=2, pad=0, **prm[0]),
+        dict(kind="linear", relu=True, IN=147, OUT=160, **prm[1]),
+        dict(kind="linear", relu=False, IN=160, OUT=2, **prm[2]),
+    ]
