@@ -309,6 +309,90 @@ int niti_quantize_update_i32(const int32_t *G, int64_t n,
                              int32_t *P, int32_t *shifts_out, int32_t *gq_out,
                              void *stream);
 
+/* ------------------------------------------------------------------------ */
+/* Model-level driver: the INT_LAYERS forward and backward ([TI] section 7:  */
+/* Conv2D, Conv2D+ReLU, Linear and Linear+ReLU layers with int8 weights,     */
+/* int32 offsets and per-filter OSS shifts / multipliers; section 8: the OSS */
+/* chain and the per-class TARGET_MAG loss; section 3: the NITI updates).    */
+/* A sequence of the calls above on one stream; the caller owns the layer    */
+/* parameters and one workspace, and the driver allocates nothing.           */
+/* ------------------------------------------------------------------------ */
+
+enum {
+    IONN_LAYER_CONV2D = 0,
+    IONN_LAYER_CONV2D_RELU = 1,
+    IONN_LAYER_LINEAR = 2,
+    IONN_LAYER_LINEAR_RELU = 3
+};
+#define IONN_MAX_LAYERS 64
+
+/* One layer.  Per sample it reads H x W x Cin int8 values (NHWC; a Linear
+ * layer has H = W = 1 and Cin = its input features) and writes, for a conv,
+ * Ho x Wo x Cout (stride 1, zero padding pad, Ho = H + 2 pad - KH + 1,
+ * Wo = W + 2 pad - KW + 1), for a Linear, Cout values.  Layer l + 1 must read
+ * as many values per sample as layer l writes (a conv output feeds a Linear
+ * as one NHWC row).  weight: int8 [Cout][KH][KW][Cin] or [Cout][Cin];
+ * offset, mult: int32 [Cout]; k: int8 [Cout] in [0, 62] (the OSS chain of
+ * ionn_oss_requant).  weight and offset are device tensors updated in place
+ * by ionn_model_backward. */
+typedef struct ionn_layer {
+    int32_t type;
+    int32_t KH, KW, pad;
+    int64_t H, W, Cin, Cout;
+    int8_t *weight;
+    int32_t *offset;
+    const int32_t *mult;
+    const int8_t *k;
+} ionn_layer;
+
+/* Gradient of the MSE loss against per-class target magnitudes ([TI]
+ * section 8, PC-side Step 3: TARGET_MAG_CORRECT[c] for the true class,
+ * TARGET_MAG_WRONG[c] for the others):
+ *   g[b][c] = out[b][c] - (c == labels[b] ? tmc[c] : tmw[c]).
+ * out: int8 [B][C]; labels: int32 [B] (values outside [0, C) match no class);
+ * tmc, tmw: int8 [C]; g: int32 [B][C] (written); absmax_g (nullable)
+ * max-combined. */
+int ionn_mse_grad_targets(const int8_t *out, const int32_t *labels, int64_t B,
+                          int64_t C, const int8_t *tmc, const int8_t *tmw,
+                          int32_t *g, uint32_t *absmax_g, void *stream);
+
+/* d[j] = 0 where act[j] <= 0 (the ReLU mask of [TI] section 4), in place;
+ * absmax_d (nullable) is max-combined with the masked values. */
+int ionn_relu_mask_i32(int32_t *d, const int8_t *act, int64_t n,
+                       uint32_t *absmax_d, void *stream);
+
+/* Device workspace of the driver for this model and batch (0 and an error
+ * message on an invalid model).  It holds every layer's activation between
+ * ionn_model_forward and ionn_model_backward. */
+size_t ionn_model_workspace_bytes(const ionn_layer *layers, int L, int64_t B);
+
+/* Forward of the L layers over the batch X (int8 [B][H0][W0][Cin0]): per
+ * layer the int32 contraction, then the OSS chain (ReLU clip for the *_RELU
+ * types) into the layer's int8 activation, kept in `workspace` (256-byte
+ * aligned, ionn_model_workspace_bytes bytes).  out (nullable): int8
+ * [B][last layer's outputs] receives a copy of the last activation. */
+int ionn_model_forward(const ionn_layer *layers, int L, const int8_t *X,
+                       int64_t B, int8_t *out, void *workspace,
+                       size_t workspace_bytes, void *stream);
+
+/* Backward of the last ionn_model_forward on the same X and workspace, and
+ * the updates: g = the MSE gradient of the last activation against the
+ * per-class targets (ionn_mse_grad_targets), delta = niti_quantize(g,
+ * tb_delta); for l = L..1: the offset gradient (ionn_bias_grad over the
+ * batch and, for a conv, its output pixels), wgrad, and for l > 1 dgrad with
+ * the pre-update weights, masked by layer l-1's activation > 0 when layer
+ * l-1 has a ReLU, requantised with tb_delta; then niti_quantize_update of the
+ * weights and niti_quantize_update_i32 of the offsets (tb_weight, mu).
+ * shifts_out (nullable, device int32[1 + 5 L]): [0] the error's shift, then
+ * per layer l at 1 + 5 l: the shift of the delta it propagates (-1 for the
+ * first layer, which propagates none), {s, ws} of its weight update and
+ * {s, ws} of its offset update. */
+int ionn_model_backward(const ionn_layer *layers, int L, const int8_t *X,
+                        int64_t B, const int32_t *labels, const int8_t *tmc,
+                        const int8_t *tmw, int tb_delta, int tb_weight, int mu,
+                        void *workspace, size_t workspace_bytes,
+                        int32_t *shifts_out, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

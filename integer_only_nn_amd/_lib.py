@@ -43,6 +43,11 @@ SIGNATURES = {
     "int_linear_fwd_oss_workspace_bytes": (ctypes.c_size_t, [_I64, _I64, _I64]),
     "int_linear_fwd_oss": (_I, [_P, _P, _P, _P, _P, _I, _P, _I64, _I64, _I64, _P, ctypes.c_size_t, _P]),
     "niti_quantize_update_i32": (_I, [_P, _I64, _P, _I, _I, _P, _P, _P, _P]),
+    "ionn_mse_grad_targets": (_I, [_P, _P, _I64, _I64, _P, _P, _P, _P, _P]),
+    "ionn_relu_mask_i32": (_I, [_P, _P, _I64, _P, _P]),
+    "ionn_model_workspace_bytes": (ctypes.c_size_t, [_P, _I, _I64]),
+    "ionn_model_forward": (_I, [_P, _I, _P, _I64, _P, _P, ctypes.c_size_t, _P]),
+    "ionn_model_backward": (_I, [_P, _I, _P, _I64, _P, _P, _P, _I, _I, _I, _P, ctypes.c_size_t, _P, _P]),
 }
 
 
@@ -52,6 +57,17 @@ class ConvDesc(ctypes.Structure):
                 ("Cin", ctypes.c_int64), ("Cout", ctypes.c_int64),
                 ("KH", ctypes.c_int32), ("KW", ctypes.c_int32), ("stride", ctypes.c_int32),
                 ("pad", ctypes.c_int32), ("dilation", ctypes.c_int32), ("groups", ctypes.c_int32)]
+
+
+class Layer(ctypes.Structure):
+    """Mirror of ionn_layer."""
+    _fields_ = [("type", ctypes.c_int32), ("KH", ctypes.c_int32), ("KW", ctypes.c_int32),
+                ("pad", ctypes.c_int32), ("H", ctypes.c_int64), ("W", ctypes.c_int64),
+                ("Cin", ctypes.c_int64), ("Cout", ctypes.c_int64), ("weight", ctypes.c_void_p),
+                ("offset", ctypes.c_void_p), ("mult", ctypes.c_void_p), ("k", ctypes.c_void_p)]
+
+
+LAYER_CONV2D, LAYER_CONV2D_RELU, LAYER_LINEAR, LAYER_LINEAR_RELU = 0, 1, 2, 3
 
 
 class IonnError(RuntimeError):

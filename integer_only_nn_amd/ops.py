@@ -143,6 +143,56 @@ def niti_quantize_update_i32(G, absmax, target_bits, mu, P, shifts_out=None, gq_
           "niti_quantize_update_i32")
 
 
+def ionn_mse_grad_targets(out, labels, tmc, tmw, g, absmax_g=None, stream=None):
+    B, C = out.shape
+    assert tuple(g.shape) == (B, C) and labels.numel() == B and tmc.numel() == C and tmw.numel() == C
+    check(lib().ionn_mse_grad_targets(_p(out, i8, name="out"), _p(labels, i32, name="labels"), B, C,
+                                      _p(tmc, i8, name="tmc"), _p(tmw, i8, name="tmw"), _p(g, i32, name="g"),
+                                      _p(absmax_g, u32, 1, "absmax_g"), _stream(stream)), "ionn_mse_grad_targets")
+
+
+def ionn_relu_mask_i32(d, act, absmax_d=None, stream=None):
+    assert d.numel() == act.numel()
+    check(lib().ionn_relu_mask_i32(_p(d, i32, name="d"), _p(act, i8, name="act"), d.numel(),
+                                   _p(absmax_d, u32, 1, "absmax_d"), _stream(stream)), "ionn_relu_mask_i32")
+
+
+def layer_array(layers):
+    """ctypes array of ionn_layer from dicts with type, KH, KW, pad, H, W, Cin,
+    Cout and device tensors weight (int8), offset (int32), mult (int32), k (int8)."""
+    from ._lib import Layer
+    arr = (Layer * len(layers))()
+    for i, L in enumerate(layers):
+        arr[i] = Layer(int(L["type"]), int(L.get("KH", 1)), int(L.get("KW", 1)), int(L.get("pad", 0)),
+                       int(L["H"]), int(L["W"]), int(L["Cin"]), int(L["Cout"]),
+                       _p(L["weight"], i8, name="weight"), _p(L["offset"], i32, name="offset"),
+                       _p(L["mult"], i32, name="mult"), _p(L["k"], i8, name="k"))
+    return arr
+
+
+def ionn_model_workspace_bytes(larr, B):
+    n = int(lib().ionn_model_workspace_bytes(larr, len(larr), int(B)))
+    if n == 0:
+        check(2, "ionn_model_workspace_bytes")
+    return n
+
+
+def ionn_model_forward(larr, X, workspace, out=None, stream=None):
+    check(lib().ionn_model_forward(larr, len(larr), _p(X, i8, name="X"), X.shape[0], _p(out, i8, name="out"),
+                                   _p(workspace, None, name="workspace"), workspace.numel() * workspace.element_size(),
+                                   _stream(stream)), "ionn_model_forward")
+
+
+def ionn_model_backward(larr, X, labels, tmc, tmw, workspace, tb_delta=7, tb_weight=8, mu=2, shifts_out=None,
+                        stream=None):
+    check(lib().ionn_model_backward(larr, len(larr), _p(X, i8, name="X"), X.shape[0],
+                                    _p(labels, i32, name="labels"), _p(tmc, i8, name="tmc"), _p(tmw, i8, name="tmw"),
+                                    int(tb_delta), int(tb_weight), int(mu), _p(workspace, None, name="workspace"),
+                                    workspace.numel() * workspace.element_size(),
+                                    _p(shifts_out, i32, 1 + 5 * len(larr), "shifts_out"), _stream(stream)),
+          "ionn_model_backward")
+
+
 def int_output_error(out, labels, target_mag, e, absmax_e=None, stream=None):
     B, C = out.shape
     assert tuple(e.shape) == (B, C) and labels.numel() == B

@@ -216,3 +216,46 @@ def dfp16_step(X, eX, W, eW, dY, edY, buf: DfpStepBuffers, stream=None):
     ops.dfp16_gemm_dgrad(dY, edY, W, eW, buf.dX, e[1:2], buf.ws, status_out=e[4:5], stream=stream)
     ops.dfp16_gemm_wgrad(dY, edY, X, eX, buf.G, e[2:3], buf.ws, status_out=e[5:6], stream=stream)
     ops.dfp16_gavg(buf.G, e[2:3], eW, buf.gavg, stream=stream)
+
+
+# ---------------------------------------------------------------------------
+# Model-level driver (ionn_model_forward / ionn_model_backward).
+# ---------------------------------------------------------------------------
+
+class Model:
+    """Device copy of a layer list and the driver's workspace.  Layers are
+    dicts: kind "conv" or "linear", relu, geometry (conv: H, W, Cin, Cout, KH,
+    KW, pad; linear: IN, OUT) and host arrays weight, offset, mult, k."""
+
+    def __init__(self, layers, B, device):
+        self.B = B
+        self.dev = []
+        for L in layers:
+            conv = L["kind"] == "conv"
+            t = (0 if conv else 2) + (1 if L["relu"] else 0)
+            geo = dict(H=L["H"], W=L["W"], Cin=L["Cin"], Cout=L["Cout"], KH=L["KH"], KW=L["KW"], pad=L["pad"]) \
+                if conv else dict(H=1, W=1, Cin=L["IN"], Cout=L["OUT"])
+            self.dev.append(dict(type=t, **geo,
+                                 weight=torch.from_numpy(L["weight"].copy()).to(device),
+                                 offset=torch.from_numpy(L["offset"].copy()).to(device),
+                                 mult=torch.from_numpy(L["mult"].copy()).to(device),
+                                 k=torch.from_numpy(L["k"].copy()).to(device)))
+        self.larr = ops.layer_array(self.dev)
+        n = ops.ionn_model_workspace_bytes(self.larr, B)
+        self.ws = torch.empty(n, dtype=torch.uint8, device=device)
+        self.shifts = torch.zeros(1 + 5 * len(layers), dtype=torch.int32, device=device)
+        last = self.dev[-1]
+        n_out = last["Cout"]
+        if last["type"] < 2:
+            n_out *= (last["H"] + 2 * last["pad"] - last["KH"] + 1) * (last["W"] + 2 * last["pad"] - last["KW"] + 1)
+        self.out = torch.empty(B, n_out, dtype=torch.int8, device=device)
+
+    def forward(self, X, stream=None):
+        ops.ionn_model_forward(self.larr, X, self.ws, out=self.out, stream=stream)
+
+    def backward(self, X, labels, tmc, tmw, stream=None):
+        ops.ionn_model_backward(self.larr, X, labels, tmc, tmw, self.ws, shifts_out=self.shifts, stream=stream)
+
+    def step(self, X, labels, tmc, tmw, stream=None):
+        self.forward(X, stream=stream)
+        self.backward(X, labels, tmc, tmw, stream=stream)

@@ -1,0 +1,82 @@
+"""GPU parity: the model-level driver (ionn_model_forward / backward, the
+INT_LAYERS forward and backward of the TI "Integer On-Device Training:
+Overview" page, sections 7 and 8) against the oracle's model step, bit-exact:
+the page's arc-fault example network (Conv 16x2 valid + ReLU, Linear 160 +
+ReLU, Linear 2, batch 8) over ten steps, a large batch of it, and a model of
+3x3 convolutions that exercises the conv dgrad mask."""
+import numpy as np
+import pytest
+import torch
+
+import ionn_synth
+import oracle
+from oracle import steps as osteps
+from integer_only_nn_amd import steps
+from gpu_helpers import dev, host, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _check_step(m, layers, X, labels, tmc, tmw, step_no):
+    new, rec = osteps.model_step(layers, X, labels, tmc, tmw)
+    m.step(to_dev(X), to_dev(labels), to_dev(tmc), to_dev(tmw))
+    L = len(layers)
+    np.testing.assert_array_equal(host(m.out), rec["acts"][-1].reshape(X.shape[0], -1),
+                                  err_msg=f"step {step_no}: output")
+    for l in range(L):
+        np.testing.assert_array_equal(host(m.dev[l]["weight"]), new[l]["weight"], err_msg=f"step {step_no} W{l}")
+        np.testing.assert_array_equal(host(m.dev[l]["offset"]), new[l]["offset"], err_msg=f"step {step_no} b{l}")
+    sh = host(m.shifts).tolist()
+    assert sh[0] == rec["s_err"]
+    for l in range(L):
+        want = [rec["s_dgrad"].get(l, -1), *rec["s_w"][l], *rec["s_b"][l]]
+        assert sh[1 + 5 * l:6 + 5 * l] == want, (step_no, l, sh, want)
+    return new
+
+
+def test_arc_fault_network_ten_steps():
+    d = ionn_synth.arc_fault()
+    layers = osteps.arc_fault_layers(d)
+    m = steps.Model(layers, 8, dev())
+    for i in range(10):
+        say("arc-fault step", i)
+        layers = _check_step(m, layers, d["X"], d["labels"], d["tmc"], d["tmw"], i)
+
+
+def test_arc_fault_network_large_batch():
+    B = 4096
+    d = ionn_synth.arc_fault(B=B, seed=3)
+    layers = osteps.arc_fault_layers(d)
+    m = steps.Model(layers, B, dev())
+    for i in range(3):
+        say("arc-fault B=4096 step", i)
+        layers = _check_step(m, layers, d["X"], d["labels"], d["tmc"], d["tmw"], i)
+
+
+def _conv_layer(rng, H, W, Cin, Cout, K, pad, relu):
+    return dict(kind="conv", relu=relu, H=H, W=W, Cin=Cin, Cout=Cout, KH=K, KW=K, pad=pad,
+                weight=np.clip(np.round(rng.normal(0, 12, (Cout, K, K, Cin))), -128, 127).astype(np.int8),
+                offset=rng.integers(-200, 200, Cout).astype(np.int32),
+                mult=rng.integers(1, 4, Cout).astype(np.int32),
+                k=rng.integers(9, 11, Cout).astype(np.int8))
+
+
+def test_conv_stack_model():
+    """3x3 / pad 1 convolutions of 16 channels (matrix-core path) after a 3x3
+    conv from 3 channels (direct path), then a Linear: every dgrad of a conv
+    is masked by the previous conv's ReLU."""
+    rng = np.random.default_rng(9)
+    B, H, W = 6, 10, 9
+    layers = [_conv_layer(rng, H, W, 3, 16, 3, 1, True), _conv_layer(rng, H, W, 16, 16, 3, 1, True),
+              _conv_layer(rng, H, W, 16, 16, 3, 1, True),
+              dict(kind="linear", relu=False, IN=H * W * 16, OUT=5,
+                   weight=np.clip(np.round(rng.normal(0, 10, (5, H * W * 16))), -128, 127).astype(np.int8),
+                   offset=rng.integers(-200, 200, 5).astype(np.int32),
+                   mult=rng.integers(1, 4, 5).astype(np.int32), k=rng.integers(10, 12, 5).astype(np.int8))]
+    X = rng.integers(-100, 100, (B, H, W, 3)).astype(np.int8)
+    labels = rng.integers(0, 5, B).astype(np.int32)
+    tmc, tmw = np.full(5, 80, np.int8), np.full(5, -50, np.int8)
+    m = steps.Model(layers, B, dev())
+    for i in range(3):
+        say("conv stack step", i)
+        layers = _check_step(m, layers, X, labels, tmc, tmw, i)
