@@ -265,6 +265,64 @@ def bench_offsets(torch, nsteps):
     return _timed(torch, step, nsteps)
 
 
+def bench_model(torch, nsteps):
+    """The example network of the on-device training page (arc-fault
+    detection: Conv 16x2 valid + ReLU, Linear 160 + ReLU, Linear 2) trained
+    by the library's model driver: whole steps (forward, MSE gradient,
+    backward, updates) at the page's batch of 8, eagerly and replayed from
+    one captured HIP graph, and at batch 65536."""
+    import ionn_synth
+    from integer_only_nn_amd import steps as st
+    dev = torch.device("cuda:0")
+    res = {}
+    for B in (8, 65536):
+        d = ionn_synth.arc_fault(B=B)
+        layers = _model_layers(d)
+        m = st.Model(layers, B, dev)
+        X, lab, tmc, tmw = (torch.from_numpy(np.ascontiguousarray(d[k])).to(dev)
+                            for k in ("X", "labels", "tmc", "tmw"))
+        for _ in range(5):
+            m.step(X, lab, tmc, tmw)
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(nsteps):
+            m.step(X, lab, tmc, tmw)
+        t1.record()
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / nsteps
+        r = {"ms_per_step": round(ms, 4), "samples_per_s": round(B / (ms * 1e-3), 1)}
+        if B == 8:
+            s = torch.cuda.Stream()
+            s.wait_stream(torch.cuda.current_stream())
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(s):
+                m.step(X, lab, tmc, tmw, stream=s.cuda_stream)   # warm the capture stream
+                torch.cuda.synchronize()
+                with torch.cuda.graph(g, stream=s):
+                    m.step(X, lab, tmc, tmw, stream=s.cuda_stream)
+            torch.cuda.synchronize()
+            t0.record()
+            for _ in range(nsteps):
+                g.replay()
+            t1.record()
+            torch.cuda.synchronize()
+            gms = t0.elapsed_time(t1) / nsteps
+            r["graph_ms_per_step"] = round(gms, 4)
+            r["graph_samples_per_s"] = round(B / (gms * 1e-3), 1)
+        res[f"batch_{B}"] = r
+    return res
+
+
+def _model_layers(d):
+    """The example network's layer dicts (geometry of the page, parameters
+    from ionn_synth.arc_fault)."""
+    prm = [dict(weight=q["W"], offset=q["offset"], mult=q["mult"], k=q["k"]) for q in d["layers"]]
+    return [dict(kind="conv", relu=True, H=64, W=2, Cin=1, Cout=3, KH=16, KW=2, pad=0, **prm[0]),
+            dict(kind="linear", relu=True, IN=147, OUT=160, **prm[1]),
+            dict(kind="linear", relu=False, IN=160, OUT=2, **prm[2])]
+
+
 def _kernel_source_hash():
     import glob
     import hashlib
@@ -374,7 +432,7 @@ def main():
         result["calibration"] = {"read_kernel": "absmax_kernel", "write_kernel": "fill_u32_kernel",
                                  "bytes": 256 << 20}
     if not args.no_secondary:
-        log("secondary: conv and DFP-16 steps, offsets and OSS")
+        log("secondary: conv and DFP-16 steps, offsets and OSS, the example network")
         c_ms, c_per = bench_conv(torch, steps_mod, 20)
         f_ms, f_per = bench_dfp16(torch, steps_mod, 20)
         conv_ops = 3 * 2.0 * 128 * 56 * 56 * 64 * 9 * 64
@@ -425,6 +483,8 @@ def main():
                                         "unit": "T int32 op/s", "frac": round(falu / PEAK_VALU_TOPS, 4),
                                         "ops_per_launch": dfp_alu[fdom]}},
             "offsets_oss": offsets,
+            "arc_fault_model": dict(shape="Conv 16x2 valid 1->3 + ReLU, Linear 147->160 + ReLU, Linear 160->2",
+                                    **bench_model(torch, 50)),
         }
     if not args.no_cpu_baseline:
         log("cpu baseline: oracle on a bounded sample")

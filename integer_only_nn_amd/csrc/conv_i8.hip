@@ -141,36 +141,61 @@ __global__ __launch_bounds__(256) void conv_direct_dgrad(const int8_t *__restric
     }
 }
 
-// G (zeroed) += the sum over output rows [r0, r1) of range blockIdx.y, rows
-// being (n, ho) pairs; one thread per weight element.
+// G (zeroed) += this workgroup's share of the sum over output rows, rows
+// being (n, ho) pairs.  Every thread of the workgroup works: thread t takes
+// weight element w = wc + t % NW (NW = min(n_g - wc, 256) for the weight
+// chunk wc) and every S-th row of the workgroup's range from t / NW on
+// (S = 256 / NW); the S partial sums of a weight meet in LDS and one atomic
+// per weight and workgroup adds them into G.
 __global__ __launch_bounds__(256) void conv_direct_wgrad(const int8_t *__restrict__ dY,
                                                          const int8_t *__restrict__ X, int32_t *__restrict__ G,
                                                          int H, int W, int Cin, int Cout, int KH, int KW, int P,
                                                          int Ho, int Wo, int64_t rows, int64_t rows_per,
                                                          int64_t n_g) {
-    const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (i >= n_g) return;
-    const int ci = int(i % Cin);
-    int64_t t = i / Cin;
-    const int kw = int(t % KW);
-    t /= KW;
-    const int kh = int(t % KH);
-    const int co = int(t / KH);
-    const int64_t r0 = int64_t(blockIdx.y) * rows_per, r1 = min(rows, r0 + rows_per);
-    uint32_t acc = 0;
-    for (int64_t r = r0; r < r1; ++r) {
-        const int64_t n = r / Ho;
-        const int ho = int(r - n * Ho);
-        const int y = ho + kh - P;
-        if (y < 0 || y >= H) continue;
-        for (int wo = 0; wo < Wo; ++wo) {
-            const int x = wo + kw - P;
-            if (x < 0 || x >= W) continue;
-            acc += uint32_t(int32_t(dY[((n * Ho + ho) * Wo + wo) * Cout + co]) *
-                            int32_t(X[((n * H + y) * W + x) * Cin + ci]));
+    __shared__ uint32_t red[256];
+    const int t = threadIdx.x;
+    const int64_t r0 = int64_t(blockIdx.x) * rows_per, r1 = min(rows, r0 + rows_per);
+    for (int64_t wc = 0; wc < n_g; wc += 256) {
+        const int NW = int(min<int64_t>(n_g - wc, 256));
+        const int S = 256 / NW;
+        const int wl = t % NW, sub = t / NW;
+        uint32_t acc = 0;
+        if (sub < S) {
+            const int64_t i = wc + wl;
+            const int ci = int(i % Cin);
+            int64_t q = i / Cin;
+            const int kw = int(q % KW);
+            q /= KW;
+            const int kh = int(q % KH);
+            const int co = int(q / KH);
+            int64_t n = (r0 + sub) / Ho;
+            int ho = int(r0 + sub - n * Ho);
+            for (int64_t r = r0 + sub; r < r1; r += S) {
+                const int y = ho + kh - P;
+                if (y >= 0 && y < H) {
+                    const int8_t *dp = dY + ((n * Ho + ho) * Wo) * Cout + co;
+                    const int8_t *xp = X + ((n * H + y) * W) * Cin + ci;
+                    for (int wo = 0; wo < Wo; ++wo) {
+                        const int x = wo + kw - P;
+                        if (x >= 0 && x < W) acc += uint32_t(int32_t(dp[int64_t(wo) * Cout]) * int32_t(xp[int64_t(x) * Cin]));
+                    }
+                }
+                ho += S;
+                while (ho >= Ho) {
+                    ho -= Ho;
+                    ++n;
+                }
+            }
         }
+        red[t] = acc;
+        __syncthreads();
+        if (t < NW) {
+            uint32_t v = 0;
+            for (int k = 0; k < S; ++k) v += red[t + k * NW];
+            if (v) atomicAdd(G + wc + t, int32_t(v));
+        }
+        __syncthreads();
     }
-    if (acc) atomicAdd(G + i, int32_t(acc));
 }
 
 unsigned direct_blocks(int64_t n) {
@@ -327,17 +352,14 @@ int int_conv_wgrad(const int8_t *dY, const int8_t *X, int32_t *G, const ionn_con
         zero_i32_kernel<<<dim3(direct_blocks(n_g)), dim3(256), 0, st>>>(G, n_g);
         if (int rc = check_launch("int_conv_wgrad")) return rc;
         if (rows > 0) {
-            // enough (weight, row range) threads to fill the chip, ranges of at least 8 rows
-            const int64_t gx = (n_g + 255) / 256;
-            int64_t ry = (65536 + gx * 256 - 1) / (gx * 256);
-            int64_t per = (rows + ry - 1) / ry;
-            if (per < 8) per = 8;
-            ry = (rows + per - 1) / per;
-            IONN_REQUIRE(gx <= 0x7fffffff && ry <= 65535, IONN_ERR_SHAPE, "int_conv_wgrad: grid too large");
-            const dim3 grid{unsigned(gx), unsigned(ry), 1u};
-            conv_direct_wgrad<<<grid, dim3(256), 0, st>>>(dY, X, G, int(desc->H), int(desc->W), Cin, Cout,
-                                                          desc->KH, desc->KW, desc->pad, int(Ho), int(Wo), rows,
-                                                          per, n_g);
+            // up to 1024 workgroups of at least 16 output rows each
+            int64_t nb = (rows + 15) / 16;
+            if (nb > 1024) nb = 1024;
+            const int64_t per = (rows + nb - 1) / nb;
+            nb = (rows + per - 1) / per;
+            conv_direct_wgrad<<<dim3(unsigned(nb)), dim3(256), 0, st>>>(dY, X, G, int(desc->H), int(desc->W), Cin,
+                                                                      Cout, desc->KH, desc->KW, desc->pad, int(Ho),
+                                                                      int(Wo), rows, per, n_g);
             if (int rc = check_launch("int_conv_wgrad")) return rc;
         }
         if (absmax_G) return launch_absmax_i32(G, n_g, absmax_G, st);

@@ -14,6 +14,8 @@
 #include "gemm256.h"
 
 namespace ionn {
+
+int launch_absmax_i32(const int32_t *x, int64_t n, uint32_t *absmax, hipStream_t st);
 namespace {
 
 using namespace gemm;
@@ -178,6 +180,23 @@ int int_linear_wgrad(const int8_t *dY, const int8_t *X, int32_t *G, int64_t B, i
     if (fast256(M, N, K, dY, OUT, X, IN, ep)) {
         g256::launch<false, false>(dY, OUT, X, IN, ep, M, N, K, st);
         return check_launch("int_linear_wgrad");
+    }
+    // A small G over a long batch (a layer of a few hundred units trained on
+    // a large batch) has too few 64 x 64 tiles to fill the chip: split the
+    // batch over up to 32 ranges, add the ranges with integer atomics into
+    // the zeroed G (exact in any order), then take the max in its own pass.
+    const int tiles = ((M + 63) / 64) * ((N + 63) / 64);
+    const int ksteps = (K + 63) / 64;
+    if (tiles < 64 && ksteps >= 64) {
+        int split = (512 + tiles - 1) / tiles;
+        if (split > ksteps / 8) split = ksteps / 8;
+        if (split > 32) split = 32;
+        if (int rc = zero_output(G, OUT * IN, st, "int_linear_wgrad")) return rc;
+        Epi epa{G, IN, M, N, aligned(G, 16) && IN % 4 == 0, nullptr, nullptr, true};
+        launch<64, 64, 64, 2, 2, true>(sa, sb, epa, M, N, K, split, st);
+        if (int rc = check_launch("int_linear_wgrad")) return rc;
+        if (absmax_G) return launch_absmax_i32(G, OUT * IN, absmax_G, st);
+        return IONN_OK;
     }
     launch_linear(sa, sb, ep, M, N, K, tile_aligned(M, N, K) && sa.vec && sb.vec && ep.vec, st);
     return check_launch("int_linear_wgrad");
