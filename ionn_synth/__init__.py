@@ -155,3 +155,31 @@ def arc_fault(B=8, seed=0):
         tmc=uniform_int(seed, 40, (2,), 60, 100),
         tmw=uniform_int(seed, 41, (2,), -100, -60),
     )
+
+
+# Adaptive-precision workload: the weight-layer sizes of a CIFAR ResNet-20
+# (the network the adaptive precision page trains): a 3x3 conv 3 -> 16, six
+# 3x3 convs 16 -> 16, one 16 -> 32 and five 32 -> 32, one 32 -> 64 and five
+# 64 -> 64, and the 64 -> 10 classifier: 20 layers, 268,336 weights.
+RESNET20_SIZES = ([16 * 3 * 9] + [16 * 16 * 9] * 6 + [32 * 16 * 9] + [32 * 32 * 9] * 5
+                  + [64 * 32 * 9] + [64 * 64 * 9] * 5 + [10 * 64])
+SID_APT_W = 50          # + layer
+SID_APT_E = 120         # + layer: initial weight exponents
+SID_APT_G = 1 << 16     # + running gradient index
+
+
+def apt_weights(sizes=RESNET20_SIZES, k0=6, seed=0):
+    """Initial k0-bit weight mantissas per layer, round(N(0, 2^(k0-1) / 3))
+    clipped to the k0-bit range, and an exponent per layer ~ U{-12..-6}."""
+    lim = 1 << (k0 - 1)
+    Ws = [normal_int(seed, SID_APT_W + l, (n,), lim / 3.0, -lim, lim - 1, dtype=np.int16)
+          for l, n in enumerate(sizes)]
+    es = [int(uniform_int(seed, SID_APT_E + l, (1,), -12, -6, dtype=np.int32)[0])
+          for l in range(len(sizes))]
+    return Ws, es
+
+
+def apt_grad(index, n, sigma, seed=0):
+    """int16 gradient mantissas round(N(0, sigma)) clipped to the int16 range;
+    `index` numbers the draw (step and layer)."""
+    return normal_int(seed, SID_APT_G + int(index), (n,), float(sigma), -32768, 32767, dtype=np.int16)

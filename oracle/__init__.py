@@ -73,6 +73,11 @@ def _declare(L):
         "ora_dfp16_dgrad": (_I, [_P, _I, _P, _I, _P, _P, _P, _I64, _I64, _I64, _I]),
         "ora_dfp16_wgrad": (_I, [_P, _I, _P, _I, _P, _P, _P, _I64, _I64, _I64, _I]),
         "ora_gavg": (ctypes.c_double, [_P, _I64, _I, _I]),
+        "ora_sat_bits": (ctypes.c_int32, [_I64, _I]),
+        "ora_apt_update": (_I64, [_P, _I64, _I, _I, _P, _I, _I]),
+        "ora_apt_decide": (_I, [ctypes.c_double, ctypes.c_int32, _I, ctypes.c_double,
+                                ctypes.c_double, _I, _I]),
+        "ora_apt_rescale": (None, [_P, _I64, _I, _I]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -379,3 +384,30 @@ def dfp16_wgrad(dY, edY, X, eX, chunk=64):
 
 def gavg(g, e_g, e_w):
     return lib().ora_gavg(_c(g, np.int16), g.size, int(e_g), int(e_w))
+
+
+# ---- adaptive precision ([APT]) -------------------------------------------
+
+def sat_bits(v, k):
+    return lib().ora_sat_bits(int(v), int(k))
+
+
+def apt_update(W, k, e_w, G, e_g, lr_shift):
+    """k-bit weight update on the grid of eps = 2^e_w; returns (W', underflows)."""
+    if W.shape != G.shape:
+        raise ValueError("W and G must have the same shape")
+    out = np.array(W, dtype=np.int16, order="C", copy=True)
+    under = lib().ora_apt_update(_c(out, np.int16), out.size, int(k), int(e_w),
+                                 _c(G, np.int16), int(e_g), int(lr_shift))
+    return out, int(under)
+
+
+def apt_decide(gavg_sum, count, k, t_min, t_max, k_min, k_max):
+    return lib().ora_apt_decide(float(gavg_sum), int(count), int(k), float(t_min),
+                                float(t_max), int(k_min), int(k_max))
+
+
+def apt_rescale(W, k, dk):
+    out = np.array(W, dtype=np.int16, order="C", copy=True)
+    lib().ora_apt_rescale(_c(out, np.int16), out.size, int(k), int(dk))
+    return out

@@ -678,3 +678,72 @@ void ora_mse_grad_targets(const int8_t *out, const int32_t *labels, int64_t B, i
             g[b * C + c] = (int32_t)out[b * C + c] - t;
         }
 }
+
+/* ------------------------------------------------------------------------ */
+/* Adaptive precision ([APT]): a layer's weights are k-bit signed integers    */
+/* m with one shared exponent e, so one step of the grid is eps = 2^e         */
+/* (Equation 2, reading U29); the update of Equation 1 lands on that grid     */
+/* (Equation 3, reading U30); Algorithm 1 moves k by one bit per epoch.       */
+/* ------------------------------------------------------------------------ */
+
+/* Saturate to the signed k-bit range [-2^(k-1), 2^(k-1) - 1], k in [1, 32]. */
+int32_t ora_sat_bits(int64_t v, int k)
+{
+    const int64_t hi = ((int64_t)1 << (k - 1)) - 1;
+    const int64_t lo = -((int64_t)1 << (k - 1));
+    if (v > hi) return (int32_t)hi;
+    if (v < lo) return (int32_t)lo;
+    return (int32_t)v;
+}
+
+/* The change of one weight in units of eps for W <- W - lr * g, with
+ * lr = 2^-lr_shift, g = g_m * 2^e_g and eps = 2^e_w:  g_m * 2^-sigma,
+ * sigma = e_w + lr_shift - e_g.  When sigma > 0 the change is rounded to
+ * the grid half-up (a change under half a step is lost: quantisation
+ * underflow); when sigma < 0 it is exact.  |g_m| < 2^15, so a shift past 40
+ * either way gives the same final weight as any larger one. */
+static int64_t apt_change(int32_t g, int64_t sigma)
+{
+    if (sigma >= 0) return sigma > 40 ? 0 : (int64_t)ora_rhu(g, (int)sigma);
+    if (sigma < -40) sigma = -40;
+    return (int64_t)g * ((int64_t)1 << (-sigma));
+}
+
+/* In place: W[j] = sat_k(W[j] - change(G[j])).  Returns how many nonzero
+ * gradients changed nothing (underflowed). */
+int64_t ora_apt_update(int16_t *W, int64_t n, int k, int e_w, const int16_t *G, int e_g,
+                       int lr_shift)
+{
+    const int64_t sigma = (int64_t)e_w + (int64_t)lr_shift - (int64_t)e_g;
+    int64_t under = 0;
+    for (int64_t j = 0; j < n; ++j) {
+        const int64_t u = apt_change(G[j], sigma);
+        if (u == 0 && G[j] != 0) ++under;
+        W[j] = (int16_t)ora_sat_bits((int64_t)W[j] - u, k);
+    }
+    return under;
+}
+
+/* Algorithm 1 for one layer (reading U33): the mean of the epoch's Gavg
+ * samples against the limits; +1 raises k, -1 lowers it, 0 keeps it.  A
+ * layer without samples keeps its precision. */
+int ora_apt_decide(double gavg_sum, int32_t count, int k, double t_min, double t_max,
+                   int k_min, int k_max)
+{
+    if (count <= 0) return 0;
+    const double mean = gavg_sum / (double)count;
+    if (mean < t_min && k < k_max) return 1;
+    if (mean > t_max && k > k_min) return -1;
+    return 0;
+}
+
+/* The weights at the new precision, same range (reading U33): one more bit
+ * halves eps, so m -> 2m (exact) and e -> e - 1; one bit less doubles it,
+ * so m -> sat_{k-1}(rhu(m, 1)) and e -> e + 1. */
+void ora_apt_rescale(int16_t *W, int64_t n, int k, int dk)
+{
+    for (int64_t j = 0; j < n; ++j) {
+        if (dk > 0) W[j] = (int16_t)ora_sat_bits(2 * (int64_t)W[j], k + 1);
+        else if (dk < 0) W[j] = (int16_t)ora_sat_bits(ora_rhu(W[j], 1), k - 1);
+    }
+}

@@ -164,6 +164,19 @@ void ora_bias_grad(const int8_t *d, int64_t M, int64_t C, int32_t *gb);
 void ora_niti_update_i32(const int32_t *G, int32_t *P, int64_t n, int target_bits,
                          int mu, int32_t *gq_out, int *shift_out, int *weight_shift_out);
 
+/* ---- Adaptive precision ([APT] Equations 1-4, Algorithms 1 and 2) ---- */
+/* k-bit weights m with shared exponent e_w (eps = 2^e_w), k in [2, 16]. */
+int32_t ora_sat_bits(int64_t v, int k);
+/* W <- sat_k(W - change), change = g_m * 2^(e_g - lr_shift - e_w) rounded
+ * half-up to the grid (reading U30).  Returns the underflow count. */
+int64_t ora_apt_update(int16_t *W, int64_t n, int k, int e_w, const int16_t *G, int e_g,
+                       int lr_shift);
+/* Algorithm 1 on the epoch's summed Gavg samples: +1, 0 or -1 (reading U33). */
+int ora_apt_decide(double gavg_sum, int32_t count, int k, double t_min, double t_max,
+                   int k_min, int k_max);
+/* The weights at precision k + dk, dk in {-1, 0, +1}, same range. */
+void ora_apt_rescale(int16_t *W, int64_t n, int k, int dk);
+
 #ifdef __cplusplus
 }
 #endif
