@@ -314,6 +314,92 @@ def bench_model(torch, nsteps):
     return res
 
 
+def _graph_ms(torch, fn, reps, nreplay=20):
+    """Average time of one fn(stream) call, from a HIP graph holding `reps`
+    back-to-back calls replayed `nreplay` times (no host gaps between the
+    launches, unlike an eager loop whose per-call Python cost exceeds a
+    short kernel)."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        fn(s.cuda_stream)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            for _ in range(reps):
+                fn(s.cuda_stream)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(nreplay):
+        g.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / (nreplay * reps)
+
+
+def bench_apt(torch, nsteps):
+    """Adaptive per-layer precision: the k-bit update of one 4096 x 4096
+    layer (16.8 M int16 weights; reads W and G, writes W: 6 algorithmic bytes
+    per weight) plain and with Gavg sampling; the update of all 20 weight
+    layers of a ResNet-20 in one launch, per training step; and the move of
+    all 20 layers' precision between epochs (every layer raised or lowered
+    by one bit, so each rescale pass does real work).  Kernel times come
+    from graph replays of back-to-back calls; the eager per-call times
+    (HIP events around each call) are reported beside them."""
+    import ionn_synth
+    from integer_only_nn_amd import steps as st
+    dev = torch.device("cuda:0")
+    n = IN * OUT
+    W, _ = ionn_synth.apt_weights([n], k0=12, seed=3)
+    big = st.AptLayers(W, [12], [-10], dev)
+    Gb = [torch.from_numpy(ionn_synth.apt_grad(9, n, 3000.0, seed=3)).to(dev)]
+    egb = torch.tensor([-22], dtype=torch.int32, device=dev)
+    sizes = ionn_synth.RESNET20_SIZES
+    Ws, es = ionn_synth.apt_weights(sizes, k0=6)
+    rn = st.AptLayers(Ws, [6] * len(sizes), es, dev)
+    Gr = [torch.from_numpy(ionn_synth.apt_grad(l, m, 500.0)).to(dev) for l, m in enumerate(sizes)]
+    egr = torch.full((len(sizes),), -14, dtype=torch.int32, device=dev)
+    big.bind_grads(Gb)
+    rn.bind_grads(Gr)
+    flip = [0]
+
+    def step(tm):
+        m = tm.mark if tm else (lambda name: None)
+        m("update_16M")
+        big.step(None, egb, 6)
+        m("update_16M_sampling")
+        big.step(None, egb, 6, sample=True)
+        m("resnet20_update")
+        rn.step(None, egr, 3)
+        m("resnet20_update_sampling")
+        rn.step(None, egr, 3, sample=True)
+        m("set_sums")
+        flip[0] ^= 1
+        rn.gsum.fill_(0.0 if flip[0] else 1e9)   # below T_min: raise; far above T_max: lower
+        m("resnet20_adjust")
+        rn.end_epoch(1.0, 100.0, 2, 16)
+    _, per = _timed(torch, step, nsteps)
+    g = {"update_16M": _graph_ms(torch, lambda s: big.step(None, egb, 6, stream=s), 10),
+         "update_16M_sampling": _graph_ms(torch, lambda s: big.step(None, egb, 6, sample=True, stream=s), 10),
+         "resnet20_update": _graph_ms(torch, lambda s: rn.step(None, egr, 3, stream=s), 10),
+         "resnet20_update_sampling": _graph_ms(torch, lambda s: rn.step(None, egr, 3, sample=True, stream=s), 10)}
+    gbs = 6.0 * n / (g["update_16M"] * 1e-3) / 1e9
+    r4 = lambda v: round(v, 4)
+    return {"layer_16M": {"shape": "4096 x 4096 int16 weights, k = 12",
+                          "update_ms": r4(g["update_16M"]), "update_sampling_ms": r4(g["update_16M_sampling"]),
+                          "eager_update_ms": r4(per["update_16M"]),
+                          "roofline": {"bound": "hbm", "kernel": "apt_update", "achieved": round(gbs, 1),
+                                       "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                                       "bytes_per_launch": 6.0 * n}},
+            "resnet20": {"layers": len(sizes), "weights": sum(sizes),
+                         "update_ms": r4(g["resnet20_update"]), "update_sampling_ms": r4(g["resnet20_update_sampling"]),
+                         "eager_update_ms": r4(per["resnet20_update"]),
+                         "eager_adjust_ms": r4(per["resnet20_adjust"])}}
+
+
 def _model_layers(d):
     """The example network's layer dicts (geometry of the page, parameters
     from ionn_synth.arc_fault)."""
@@ -485,6 +571,7 @@ def main():
             "offsets_oss": offsets,
             "arc_fault_model": dict(shape="Conv 16x2 valid 1->3 + ReLU, Linear 147->160 + ReLU, Linear 160->2",
                                     **bench_model(torch, 50)),
+            "adaptive_precision": bench_apt(torch, 20),
         }
     if not args.no_cpu_baseline:
         log("cpu baseline: oracle on a bounded sample")

@@ -393,6 +393,58 @@ int ionn_model_backward(const ionn_layer *layers, int L, const int8_t *X,
                         void *workspace, size_t workspace_bytes,
                         int32_t *shifts_out, void *stream);
 
+/* ------------------------------------------------------------------------ */
+/* Adaptive per-layer precision ([APT]: the weight resolution epsilon of a   */
+/* k-bit tensor, Equation 2; the update of Equation 1 on that grid,          */
+/* Equation 3; Gavg, Equation 4; the policy of Algorithm 1 applied between   */
+/* epochs as Algorithm 2 lays out).                                          */
+/*                                                                          */
+/* Layer l holds k[l]-bit signed weight mantissas W[l] (int16 storage, the  */
+/* k-bit range [-2^(k-1), 2^(k-1) - 1]) with one shared exponent e_w[l]: a  */
+/* weight is m * 2^e_w and one grid step is epsilon = 2^e_w.  k, e_w, the   */
+/* gradient exponents e_g and the per-epoch Gavg sums are DEVICE int32 /    */
+/* double arrays of L entries, so steps and epochs chain on the stream      */
+/* without a host synchronisation.  W, G and n are HOST arrays of L device  */
+/* pointers and sizes (2-byte aligned; 16-byte aligned tensors take the     */
+/* vector path).  1 <= L <= IONN_MAX_LAYERS, 1 <= n[l] <= 2^36.  A k[l]     */
+/* outside [2, 16] is read as the nearest bound.                             */
+/* ------------------------------------------------------------------------ */
+
+/* Workspace (bytes, 8-byte aligned) a sampling apt_update needs for these
+ * layer sizes; 0 on invalid sizes. */
+size_t apt_workspace_bytes(int L, const int64_t *n);
+
+/* One step's update of every layer, in place on W:
+ *   W[l][j] = sat_k(W[l][j] - c),  c = rhu(G[l][j], sigma) if sigma >= 0,
+ *                                  c = G[l][j] * 2^-sigma   otherwise,
+ *   sigma = e_w[l] + lr_shift - e_g[l]
+ * i.e. W - lr * g with lr = 2^-lr_shift and g = G * 2^e_g, rounded to the
+ * layer's grid (a change under half a step is lost: quantisation underflow).
+ * G: int16 [n[l]] (a DFP-16 weight gradient, e.g. from dfp16_gemm_wgrad).
+ * lr_shift in [0, 62].  Sampling: when gavg_sum (double [L]) and gavg_count
+ * (int32 [L]) are given, every layer's Gavg of this gradient,
+ * mean(|G|) * 2^(e_g - e_w) (as dfp16_gavg), is added to gavg_sum[l] and
+ * gavg_count[l] grows by one; that needs `workspace`
+ * (apt_workspace_bytes(L, n) bytes); both NULL: no sampling, no workspace. */
+int apt_update(int L, int16_t *const *W, const int16_t *const *G,
+               const int64_t *n, const int32_t *k, const int32_t *e_w,
+               const int32_t *e_g, int lr_shift, double *gavg_sum,
+               int32_t *gavg_count, void *workspace, size_t workspace_bytes,
+               void *stream);
+
+/* Between epochs, per layer (Algorithm 1 on the mean of the epoch's
+ * samples, gavg_sum[l] / gavg_count[l]; no samples: no change):
+ *   mean < t_min and k < k_max:  k += 1, e_w -= 1, m -> 2m
+ *   mean > t_max and k > k_min:  k -= 1, e_w += 1, m -> sat_{k-1}(rhu(m, 1))
+ * (the range stays, the grid step halves or doubles); then gavg_sum and
+ * gavg_count are cleared.  dk_out (nullable, device int32 [L]) receives
+ * each layer's change.  2 <= k_min <= k_max <= 16; t_min <= t_max (t_max
+ * may be +inf: never lower).  No workspace. */
+int apt_adjust(int L, int16_t *const *W, const int64_t *n, int32_t *k,
+               int32_t *e_w, double *gavg_sum, int32_t *gavg_count,
+               double t_min, double t_max, int k_min, int k_max,
+               int32_t *dk_out, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -37,6 +37,9 @@ SIGNATURES = {
     "dfp16_gemm_dgrad": (_I, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P, ctypes.c_size_t, _P, _P]),
     "dfp16_gemm_wgrad": (_I, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P, ctypes.c_size_t, _P, _P]),
     "dfp16_gavg": (_I, [_P, _P, _P, _I64, _P, _P]),
+    "apt_workspace_bytes": (ctypes.c_size_t, [_I, _P]),
+    "apt_update": (_I, [_I, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, ctypes.c_size_t, _P]),
+    "apt_adjust": (_I, [_I, _P, _P, _P, _P, _P, _P, ctypes.c_double, ctypes.c_double, _I, _I, _P, _P]),
     "ionn_oss_requant": (_I, [_P, _P, _P, _P, _I64, _I64, _I, _P, _P]),
     "ionn_bias_grad_workspace_bytes": (ctypes.c_size_t, [_I64, _I64]),
     "ionn_bias_grad": (_I, [_P, _I64, _I64, _P, _P, ctypes.c_size_t, _P]),

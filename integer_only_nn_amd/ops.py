@@ -270,3 +270,40 @@ def dfp16_gavg(G, eG, eW, gavg_out, stream=None):
     check(lib().dfp16_gavg(_p(G, i16, name="G"), _p(eG, i32, 1, "eG"), _p(eW, i32, 1, "eW"),
                            G.numel(), _p(gavg_out, torch.float64, 1, "gavg_out"), _stream(stream)),
           "dfp16_gavg")
+
+
+# ---- adaptive per-layer precision -------------------------------------------
+
+def _ptr_array(ts, dtype, name):
+    return (ctypes.c_void_p * len(ts))(*[_p(t, dtype, name=f"{name}[{l}]").value for l, t in enumerate(ts)])
+
+
+def _sizes(ts):
+    return (ctypes.c_int64 * len(ts))(*[t.numel() for t in ts])
+
+
+def apt_workspace_bytes(sizes):
+    return lib().apt_workspace_bytes(len(sizes), (ctypes.c_int64 * len(sizes))(*[int(n) for n in sizes]))
+
+
+def apt_update(Ws, Gs, k, e_w, e_g, lr_shift, gavg_sum=None, gavg_count=None, workspace=None, stream=None):
+    """One step's k-bit update of every layer (lists of int16 device tensors);
+    k, e_w, e_g: int32 [L]; gavg_sum (float64 [L]) and gavg_count (int32 [L])
+    given together make it a sampling step."""
+    L = len(Ws)
+    if len(Gs) != L or any(w.numel() != g.numel() for w, g in zip(Ws, Gs)):
+        raise ValueError("Ws and Gs must pair up with equal sizes")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    check(lib().apt_update(L, _ptr_array(Ws, i16, "W"), _ptr_array(Gs, i16, "G"), _sizes(Ws),
+                           _p(k, i32, L, "k"), _p(e_w, i32, L, "e_w"), _p(e_g, i32, L, "e_g"), int(lr_shift),
+                           _p(gavg_sum, torch.float64, L, "gavg_sum"), _p(gavg_count, i32, L, "gavg_count"),
+                           _p(workspace, name="workspace"), ws_bytes, _stream(stream)), "apt_update")
+
+
+def apt_adjust(Ws, k, e_w, gavg_sum, gavg_count, t_min, t_max, k_min=2, k_max=16, dk_out=None, stream=None):
+    """Between epochs: one bit more or less per layer on its mean Gavg."""
+    L = len(Ws)
+    check(lib().apt_adjust(L, _ptr_array(Ws, i16, "W"), _sizes(Ws), _p(k, i32, L, "k"), _p(e_w, i32, L, "e_w"),
+                           _p(gavg_sum, torch.float64, L, "gavg_sum"), _p(gavg_count, i32, L, "gavg_count"),
+                           float(t_min), float(t_max), int(k_min), int(k_max), _p(dk_out, i32, L, "dk_out"),
+                           _stream(stream)), "apt_adjust")

@@ -259,3 +259,58 @@ class Model:
     def step(self, X, labels, tmc, tmw, stream=None):
         self.forward(X, stream=stream)
         self.backward(X, labels, tmc, tmw, stream=stream)
+
+
+# ---------------------------------------------------------------------------
+# Adaptive per-layer precision (apt_update / apt_adjust).
+# ---------------------------------------------------------------------------
+
+class AptLayers:
+    """Device state of adaptive per-layer precision over L int16 weight
+    tensors: their precisions k, weight exponents e_w and the epoch's Gavg
+    sums and counts, plus the workspace a sampling step needs.  The host
+    never reads the state back unless asked to.  The ctypes argument arrays
+    are built once (bind_grads for the gradient buffers), so a step costs
+    one library call."""
+
+    def __init__(self, Ws, ks, es, device):
+        self.W = [torch.from_numpy(w.copy()).to(device) for w in Ws]
+        L = len(self.W)
+        self.k = torch.tensor(list(ks), dtype=torch.int32, device=device)
+        self.e_w = torch.tensor(list(es), dtype=torch.int32, device=device)
+        self.gsum = torch.zeros(L, dtype=torch.float64, device=device)
+        self.gcnt = torch.zeros(L, dtype=torch.int32, device=device)
+        self.dk = torch.zeros(L, dtype=torch.int32, device=device)
+        self.ws = torch.empty(max(ops.apt_workspace_bytes([w.numel() for w in self.W]), 8),
+                              dtype=torch.uint8, device=device)
+        self._Wp = ops._ptr_array(self.W, torch.int16, "W")
+        self._n = ops._sizes(self.W)
+        self._G = None
+
+    def bind_grads(self, Gs):
+        """Fix the gradient buffers (int16 device tensors, one per layer) that
+        step() reads when it is given none."""
+        if len(Gs) != len(self.W) or any(g.numel() != w.numel() for g, w in zip(Gs, self.W)):
+            raise ValueError("one gradient per layer, of the layer's size")
+        self._G = (list(Gs), ops._ptr_array(Gs, torch.int16, "G"))
+
+    def step(self, Gs, e_g, lr_shift, sample=False, stream=None):
+        """One update of every layer with gradients Gs (int16 device tensors;
+        None: the bound buffers) and their exponents e_g (int32 device [L])."""
+        if Gs is not None:
+            self.bind_grads(Gs)
+        if self._G is None:
+            raise ValueError("no gradient buffers")
+        L = len(self.W)
+        ops.check(ops.lib().apt_update(
+            L, self._Wp, self._G[1], self._n, ops._p(self.k), ops._p(self.e_w), ops._p(e_g, torch.int32, L, "e_g"),
+            int(lr_shift), ops._p(self.gsum) if sample else None, ops._p(self.gcnt) if sample else None,
+            ops._p(self.ws) if sample else None, self.ws.numel() if sample else 0, ops._stream(stream)),
+            "apt_update")
+
+    def end_epoch(self, t_min, t_max, k_min=2, k_max=16, stream=None):
+        L = len(self.W)
+        ops.check(ops.lib().apt_adjust(
+            L, self._Wp, self._n, ops._p(self.k), ops._p(self.e_w), ops._p(self.gsum), ops._p(self.gcnt),
+            float(t_min), float(t_max), int(k_min), int(k_max), ops._p(self.dk), ops._stream(stream)),
+            "apt_adjust")

@@ -117,3 +117,39 @@ def test_dfp16_validation():
     assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 100, 64, 32, 64, P(0x1010), need, None, None) == WS
     assert f(None, FAKE, FAKE, FAKE, FAKE, FAKE, 100, 64, 32, 64, FAKE, need, None, None) == ARG
     assert lib.dfp16_gavg(FAKE, FAKE, FAKE, 0, FAKE, None) == SHAPE
+
+
+def test_apt_validation():
+    arrP = lambda *ps: (ctypes.c_void_p * len(ps))(*ps)
+    arrN = lambda *ns: (ctypes.c_int64 * len(ns))(*ns)
+    W, G, N = arrP(0x1000, 0x2000), arrP(0x3000, 0x4000), arrN(100, 9000)
+    # apt_update(L, W, G, n, k, e_w, e_g, lr_shift, gsum, gcnt, ws, ws_bytes, stream)
+    assert lib.apt_update(0, W, G, N, FAKE, FAKE, FAKE, 3, None, None, None, 0, None) == SHAPE
+    assert lib.apt_update(65, W, G, N, FAKE, FAKE, FAKE, 3, None, None, None, 0, None) == SHAPE
+    assert lib.apt_update(2, W, None, N, FAKE, FAKE, FAKE, 3, None, None, None, 0, None) == ARG
+    assert lib.apt_update(2, W, G, arrN(100, 0), FAKE, FAKE, FAKE, 3, None, None, None, 0, None) == SHAPE
+    assert lib.apt_update(2, W, G, arrN(100, 1 << 37), FAKE, FAKE, FAKE, 3, None, None, None, 0, None) == SHAPE
+    assert lib.apt_update(2, arrP(0x1000, None), G, N, FAKE, FAKE, FAKE, 3, None, None, None, 0, None) == ARG
+    assert lib.apt_update(2, arrP(0x1000, 0x2001), G, N, FAKE, FAKE, FAKE, 3, None, None, None, 0, None) == ALIGN
+    assert lib.apt_update(2, W, G, N, None, FAKE, FAKE, 3, None, None, None, 0, None) == ARG
+    assert lib.apt_update(2, W, G, N, FAKE_ODD, FAKE, FAKE, 3, None, None, None, 0, None) == ALIGN
+    assert lib.apt_update(2, W, G, N, FAKE, FAKE, FAKE, -1, None, None, None, 0, None) == RANGE
+    assert lib.apt_update(2, W, G, N, FAKE, FAKE, FAKE, 63, None, None, None, 0, None) == RANGE
+    assert lib.apt_update(2, W, G, N, FAKE, FAKE, FAKE, 3, FAKE, None, None, 0, None) == ARG
+    need = lib.apt_workspace_bytes(2, N)
+    assert need == 8 * (1 + 5)   # 2048 weights per workgroup: one for 100, five for 9000
+    assert lib.apt_update(2, W, G, N, FAKE, FAKE, FAKE, 3, FAKE, FAKE, None, 0, None) == WS
+    assert lib.apt_update(2, W, G, N, FAKE, FAKE, FAKE, 3, FAKE, FAKE, FAKE, need - 8, None) == WS
+    assert "workspace" in _err()
+    assert lib.apt_workspace_bytes(0, N) == 0 and lib.apt_workspace_bytes(2, arrN(1, -1)) == 0
+    # apt_adjust(L, W, n, k, e_w, gsum, gcnt, t_min, t_max, k_min, k_max, dk_out, stream)
+    adj = lambda L=2, w=W, n=N, k=FAKE, tmin=1.0, tmax=2.0, kmin=2, kmax=16, dk=None: lib.apt_adjust(
+        L, w, n, k, FAKE, FAKE, FAKE, tmin, tmax, kmin, kmax, dk, None)
+    assert adj(L=0) == SHAPE
+    assert adj(k=None) == ARG
+    assert adj(k=FAKE_ODD) == ALIGN
+    assert adj(dk=FAKE_ODD) == ALIGN
+    assert adj(kmin=1) == RANGE and adj(kmax=17) == RANGE and adj(kmin=9, kmax=8) == RANGE
+    assert adj(tmin=3.0, tmax=2.0) == RANGE
+    assert adj(tmin=float("nan")) == RANGE
+    assert adj(n=arrN(5, 0)) == SHAPE
