@@ -78,6 +78,14 @@ def _declare(L):
         "ora_apt_decide": (_I, [ctypes.c_double, ctypes.c_int32, _I, ctypes.c_double,
                                 ctypes.c_double, _I, _I]),
         "ora_apt_rescale": (None, [_P, _I64, _I, _I]),
+        "ora_f32_floor_log2": (_I, [ctypes.c_float]),
+        "ora_dfp_from_f32": (_I, [_P, _I64, _I, _P, _P]),
+        "ora_dfp_from_f32_blocked": (_I, [_P, _I64, _I64, _I, _I, _P, _P]),
+        "ora_dfp_to_f32": (None, [_P, _I64, _I, _P]),
+        "ora_scale_f32": (ctypes.c_float, [ctypes.c_float, _I]),
+        "ora_dfp_contract_f32": (_I64, [_P, _I64, _I64, _P, _I64, _I64, _I64, _I64, _I64, _I, _I, _I, _I, _P]),
+        "ora_dfp_fwd_f32_blocked": (_I64, [_P, _P, _P, _P, _I64, _I64, _I64, _I, _I, _P]),
+        "ora_dfp16_sgd": (_I, [_P, _P, _I64, ctypes.c_float, _P, _P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -411,3 +419,89 @@ def apt_rescale(W, k, dk):
     out = np.array(W, dtype=np.int16, order="C", copy=True)
     lib().ora_apt_rescale(_c(out, np.int16), out.size, int(k), int(dk))
     return out
+
+
+# ---- DFP as the DFP page runs it (FP32 partials, conversions, Blocked-DFP) ----
+
+def f32_floor_log2(m):
+    return lib().ora_f32_floor_log2(float(m))
+
+
+def dfp_from_f32(x, P=16):
+    """float32 array -> (int16 mantissas, exponent, status)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, np.int16)
+    e = ctypes.c_int()
+    st = lib().ora_dfp_from_f32(_c(x, np.float32), x.size, int(P), _c(out, np.int16), ctypes.byref(e))
+    return out, e.value, st
+
+
+def dfp_from_f32_blocked(x, B=64, P=16):
+    """float32 [rows][K] -> (int16 [rows][K], int32 exponents [rows][ceil(K/B)], status)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    rows, K = x.shape
+    nb = (K + B - 1) // B
+    out = np.empty(x.shape, np.int16)
+    e = np.empty((rows, nb), np.int32)
+    st = lib().ora_dfp_from_f32_blocked(_c(x, np.float32), rows, K, int(B), int(P), _c(out, np.int16),
+                                        _c(e, np.int32))
+    return out, e, st
+
+
+def dfp_to_f32(I, e):
+    out = np.empty(I.shape, np.float32)
+    lib().ora_dfp_to_f32(_c(I, np.int16), I.size, int(e), _c(out, np.float32))
+    return out
+
+
+def scale_f32(v, e):
+    return lib().ora_scale_f32(float(v), int(e))
+
+
+def _f32_role(A, sam, sak, B, sbk, sbn, M, N, L, input_shift, eA, eB, S):
+    out = np.empty((M, N), np.float32)
+    w = lib().ora_dfp_contract_f32(_c(A, np.int16), sam, sak, _c(B, np.int16), sbk, sbn, M, N, L,
+                                   int(input_shift), int(eA), int(eB), int(S), _c(out, np.float32))
+    return out, int(w)
+
+
+def dfp16_fwd_f32(X, eX, W, eW, S=1, input_shift=1):
+    """Y [M][N] float32 = X [M][K] . W [N][K]^T with FP32 chunk partials; returns (Y, wraps)."""
+    M, K = X.shape
+    N = W.shape[0]
+    return _f32_role(X, K, 1, W, 1, K, M, N, K, input_shift, eX, eW, S)
+
+
+def dfp16_dgrad_f32(dY, edY, W, eW, S=1, input_shift=1):
+    """dX [M][K] float32 = dY [M][N] . W [N][K]."""
+    M, N = dY.shape
+    K = W.shape[1]
+    return _f32_role(dY, N, 1, W, K, 1, M, K, N, input_shift, edY, eW, S)
+
+
+def dfp16_wgrad_f32(dY, edY, X, eX, S=1, input_shift=1):
+    """G [N][K] float32 = dY [M][N]^T . X [M][K]."""
+    M, N = dY.shape
+    K = X.shape[1]
+    return _f32_role(dY, 1, N, X, K, 1, N, K, M, input_shift, edY, eX, S)
+
+
+def dfp16_fwd_f32_blocked(X, eX, W, eW, S=1, input_shift=1):
+    """Y [M][N] float32 from Blocked-DFP X (exponents [M][K/64]) and W ([N][K/64])."""
+    M, K = X.shape
+    N = W.shape[0]
+    out = np.empty((M, N), np.float32)
+    w = lib().ora_dfp_fwd_f32_blocked(_c(X, np.int16), _c(eX, np.int32), _c(W, np.int16), _c(eW, np.int32),
+                                      M, K, N, int(input_shift), int(S), _c(out, np.float32))
+    return out, int(w)
+
+
+def dfp16_sgd(W32, G32, lr):
+    """FP32 master update and its DFP-16 copy: returns (W32', W16, eW, status)."""
+    W = np.array(W32, dtype=np.float32, copy=True)
+    G = np.ascontiguousarray(G32, dtype=np.float32)
+    W16 = np.empty(W.shape, np.int16)
+    e = ctypes.c_int()
+    st = lib().ora_dfp16_sgd(_c(W, np.float32), _c(G, np.float32), W.size, float(lr), _c(W16, np.int16),
+                             ctypes.byref(e))
+    return W, W16, e.value, st

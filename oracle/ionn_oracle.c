@@ -747,3 +747,211 @@ void ora_apt_rescale(int16_t *W, int64_t n, int k, int dk)
         else if (dk < 0) W[j] = (int16_t)ora_sat_bits(ora_rhu(W[j], 1), k - 1);
     }
 }
+
+/* ------------------------------------------------------------------------ */
+/* DFP as the DFP page runs it ([DFP] 3.1: float -> DFP conversion by the    */
+/* exponent of the absolute maximum, and back; 4 "Handling overflows": int32 */
+/* chunk partials converted to FP32, scaled by 2^(E_inp + E_wt) and summed   */
+/* into an FP32 output, with the input shifted by one bit; 3: Blocked-DFP,   */
+/* several exponents per tensor).  Readings U34-U38.                         */
+/* ------------------------------------------------------------------------ */
+
+static uint32_t f32_bits(float x)
+{
+    union { float f; uint32_t u; } v;
+    v.f = x;
+    return v.u;
+}
+
+/* 2^e as a double, e in [-1022, 1023], by repeated exact doubling/halving. */
+static double pow2d(int e)
+{
+    double v = 1.0;
+    for (; e > 0; --e) v *= 2.0;
+    for (; e < 0; ++e) v *= 0.5;
+    return v;
+}
+
+/* floor(log2 m) of a finite m > 0, read from the IEEE single fields. */
+int ora_f32_floor_log2(float m)
+{
+    const uint32_t u = f32_bits(m) & 0x7fffffffu;
+    const int ex = (int)(u >> 23);
+    if (ex > 0) return ex - 127;
+    return -150 + ora_bitlen_u32(u & 0x7fffffu);   /* subnormal: mantissa * 2^-149 */
+}
+
+/* Round a double with |v| < 2^52 to the nearest integer, ties to even. */
+static int64_t rne_i64(double v)
+{
+    int64_t t = (int64_t)v;            /* toward zero, exact for |v| < 2^52 */
+    double f = v - (double)t;          /* exact: the fraction, sign of v */
+    if (f > 0.5 || (f == 0.5 && (t & 1))) ++t;
+    else if (f < -0.5 || (f == -0.5 && (t & 1))) --t;
+    return t;
+}
+
+/* One element of a P-bit DFP tensor with shared exponent E:
+ * sat_P(round_to_nearest_even(x / 2^E)), the division exact in double. */
+static int32_t dfp_elem(float x, int E, int P)
+{
+    const double v = (double)x * pow2d(-E);
+    return ora_sat_bits(rne_i64(v), P);
+}
+
+/* Shared exponent of a P-bit tensor whose max |x| is m (reading U34):
+ * m = f * 2^q with f in [1, 2) gives E = q - (P - 2), so that m / 2^E lies in
+ * [2^(P-2), 2^(P-1)); 0 for m = 0. */
+static int dfp_exponent(float m, int P)
+{
+    return m > 0.0f ? ora_f32_floor_log2(m) - (P - 2) : 0;
+}
+
+/* Float -> DFP-P (P in [2, 16]) over n values with one exponent.  Returns 0,
+ * 1 when the exponent leaves the signed 8-bit range (still written), 2 when
+ * a value is not finite (outputs then unspecified). */
+int ora_dfp_from_f32(const float *x, int64_t n, int P, int16_t *out, int *e_out)
+{
+    float m = 0.0f;
+    for (int64_t j = 0; j < n; ++j) {
+        const float a = x[j] < 0.0f ? -x[j] : x[j];
+        if (!(a <= 3.402823466e38f)) return 2;       /* inf or NaN */
+        if (a > m) m = a;
+    }
+    const int E = dfp_exponent(m, P);
+    for (int64_t j = 0; j < n; ++j) out[j] = (int16_t)dfp_elem(x[j], E, P);
+    *e_out = E;
+    return (E < -128 || E > 127) ? 1 : 0;
+}
+
+/* Blocked-DFP: rows of K values, each split into blocks of B consecutive
+ * values (the last one shorter when B does not divide K), one exponent per
+ * block: e_out[r * nb + b], nb = ceil(K / B).  Returns as ora_dfp_from_f32
+ * (1 when any exponent leaves the 8-bit range). */
+int ora_dfp_from_f32_blocked(const float *x, int64_t rows, int64_t K, int B, int P,
+                             int16_t *out, int32_t *e_out)
+{
+    const int64_t nb = (K + B - 1) / B;
+    int st = 0;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t b = 0; b < nb; ++b) {
+            const int64_t k0 = b * B, k1 = (k0 + B < K) ? k0 + B : K;
+            int e = 0;
+            const int s = ora_dfp_from_f32(x + r * K + k0, k1 - k0, P, out + r * K + k0, &e);
+            if (s == 2) return 2;
+            if (s == 1) st = 1;
+            e_out[r * nb + b] = e;
+        }
+    return st;
+}
+
+/* DFP -> float: out = I * 2^e rounded once to single (exact whenever the
+ * value is a normal single). */
+void ora_dfp_to_f32(const int16_t *I, int64_t n, int e, float *out)
+{
+    const double s = pow2d(e);
+    for (int64_t j = 0; j < n; ++j) out[j] = (float)((double)I[j] * s);
+}
+
+/* fl(v * 2^e): the exact product in double, rounded once to single. */
+float ora_scale_f32(float v, int e)
+{
+    return (float)((double)v * pow2d(e));
+}
+
+/* Chunk ranges of the FP32 accumulation: range s of S covers chunks
+ * [floor(nch * s / S), floor(nch * (s + 1) / S)). */
+static int64_t range_start(int64_t nch, int S, int s)
+{
+    return nch * s / S;
+}
+
+/* The FP32-partial contraction (reading U35), per output (m, n):
+ *   A'(m,k) = rhu(A(m,k), input_shift)   (the input shifted by one bit)
+ *   p_c     = sum over chunk c of A'(m,k) * B(k,n)     (int32, modulo 2^32)
+ *   part_s  = 0 + float(p_c0) + float(p_c0+1) + ...    (single, in order)
+ *   total   = 0 + part_0 + part_1 + ... + part_{S-1}   (single, in order)
+ *   out     = fl(total * 2^(eA + input_shift + eB))
+ * with A(m,k) = A[m*sam + k*sak], B(k,n) = B[k*sbk + n*sbn], 64-term chunks.
+ * Returns the number of chunk partials whose exact value left int32. */
+int64_t ora_dfp_contract_f32(const int16_t *A, int64_t sam, int64_t sak,
+                             const int16_t *B, int64_t sbk, int64_t sbn, int64_t M,
+                             int64_t N, int64_t L, int input_shift, int eA, int eB,
+                             int S, float *out)
+{
+    const int64_t nch = (L + 63) / 64;
+    const int e = eA + input_shift + eB;
+    int64_t wraps = 0;
+#pragma omp parallel for schedule(static) reduction(+ : wraps)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            float total = 0.0f;
+            for (int s = 0; s < S; ++s) {
+                float part = 0.0f;
+                for (int64_t c = range_start(nch, S, s); c < range_start(nch, S, s + 1); ++c) {
+                    uint32_t p = 0;
+                    int64_t exact = 0;
+                    for (int64_t k = 64 * c; k < 64 * c + 64 && k < L; ++k) {
+                        const int32_t a = ora_rhu(A[m * sam + k * sak], input_shift);
+                        const int32_t b = B[k * sbk + n * sbn];
+                        p += (uint32_t)(a * b);
+                        exact += (int64_t)a * b;
+                    }
+                    wraps += !exact_in_i32(exact);
+                    part = part + (float)u32_to_i32(p);
+                }
+                total = total + part;
+            }
+            out[m * N + n] = ora_scale_f32(total, e);
+        }
+    return wraps;
+}
+
+/* The forward contraction on Blocked-DFP operands whose blocks are the
+ * 64-term chunks (reading U37): X [M][K] with exponents eX[m][c], W [N][K]
+ * with eW[n][c]; every chunk's term is scaled on its own,
+ *   t_c = fl(float(p_c) * 2^(eX[m][c] + input_shift + eW[n][c])),
+ * and the terms are summed as in ora_dfp_contract_f32 (S ranges in order). */
+int64_t ora_dfp_fwd_f32_blocked(const int16_t *X, const int32_t *eX, const int16_t *W,
+                                const int32_t *eW, int64_t M, int64_t K, int64_t N,
+                                int input_shift, int S, float *out)
+{
+    const int64_t nch = (K + 63) / 64;
+    int64_t wraps = 0;
+#pragma omp parallel for schedule(static) reduction(+ : wraps)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            float total = 0.0f;
+            for (int s = 0; s < S; ++s) {
+                float part = 0.0f;
+                for (int64_t c = range_start(nch, S, s); c < range_start(nch, S, s + 1); ++c) {
+                    uint32_t p = 0;
+                    int64_t exact = 0;
+                    for (int64_t k = 64 * c; k < 64 * c + 64 && k < K; ++k) {
+                        const int32_t a = ora_rhu(X[m * K + k], input_shift);
+                        const int32_t b = W[n * K + k];
+                        p += (uint32_t)(a * b);
+                        exact += (int64_t)a * b;
+                    }
+                    wraps += !exact_in_i32(exact);
+                    const int e = eX[m * nch + c] + input_shift + eW[n * nch + c];
+                    part = part + ora_scale_f32((float)u32_to_i32(p), e);
+                }
+                total = total + part;
+            }
+            out[m * N + n] = total;
+        }
+    return wraps;
+}
+
+/* The weight update of the DFP pipeline (reading U38): FP32 master weights
+ * W32[j] = fl(W32[j] - fl(lr * G32[j])) (two roundings, no fused multiply-
+ * add), then the DFP-16 copy the next forward reads. */
+int ora_dfp16_sgd(float *W32, const float *G32, int64_t n, float lr, int16_t *W16, int *eW)
+{
+    for (int64_t j = 0; j < n; ++j) {
+        const float t = lr * G32[j];
+        W32[j] = W32[j] - t;
+    }
+    return ora_dfp_from_f32(W32, n, 16, W16, eW);
+}

@@ -177,6 +177,23 @@ int ora_apt_decide(double gavg_sum, int32_t count, int k, double t_min, double t
 /* The weights at precision k + dk, dk in {-1, 0, +1}, same range. */
 void ora_apt_rescale(int16_t *W, int64_t n, int k, int dk);
 
+/* ---- DFP as the DFP page runs it ([DFP] 3.1 conversions, 4 FP32 partials
+ * with the 1-bit input shift, 3 Blocked-DFP; readings U34-U38) ---- */
+int     ora_f32_floor_log2(float m);
+int     ora_dfp_from_f32(const float *x, int64_t n, int P, int16_t *out, int *e_out);
+int     ora_dfp_from_f32_blocked(const float *x, int64_t rows, int64_t K, int B, int P,
+                                 int16_t *out, int32_t *e_out);
+void    ora_dfp_to_f32(const int16_t *I, int64_t n, int e, float *out);
+float   ora_scale_f32(float v, int e);
+int64_t ora_dfp_contract_f32(const int16_t *A, int64_t sam, int64_t sak,
+                             const int16_t *B, int64_t sbk, int64_t sbn, int64_t M,
+                             int64_t N, int64_t L, int input_shift, int eA, int eB,
+                             int S, float *out);
+int64_t ora_dfp_fwd_f32_blocked(const int16_t *X, const int32_t *eX, const int16_t *W,
+                                const int32_t *eW, int64_t M, int64_t K, int64_t N,
+                                int input_shift, int S, float *out);
+int     ora_dfp16_sgd(float *W32, const float *G32, int64_t n, float lr, int16_t *W16, int *eW);
+
 #ifdef __cplusplus
 }
 #endif
