@@ -220,6 +220,48 @@ def bench_dfp16(torch, steps_mod, nsteps):
     return _timed(torch, step, nsteps)
 
 
+def bench_dfp16_paper(torch, nsteps):
+    """The DFP-16 layer (M=25088, K=256, N=1024) stepped as the DFP page
+    runs it: FP32 input, weights and incoming gradient converted to DFP-16
+    (shared exponent from the absolute maximum), the three contractions
+    with FP32 chunk partials and the one-bit input shift, the FP32 output
+    re-quantised for the next layer, and the FP32 weight update with its
+    DFP-16 copy."""
+    from integer_only_nn_amd import ops
+    dev = torch.device("cuda:0")
+    M, K, N = 25088, 256, 1024
+    g = torch.Generator(device="cpu").manual_seed(5)
+    X32 = (torch.randn(M, K, generator=g) * 2.0).to(dev)
+    W32 = (torch.randn(N, K, generator=g) * 0.05).to(dev)
+    dY32 = (torch.randn(M, N, generator=g) * 1e-3).to(dev)
+    i16 = lambda *shape: torch.empty(*shape, dtype=torch.int16, device=dev)
+    f32 = lambda *shape: torch.empty(*shape, dtype=torch.float32, device=dev)
+    ex = torch.zeros(8, dtype=torch.int32, device=dev)       # eX, eW, edY, eY, status
+    X16, W16, dY16, Y16 = i16(M, K), i16(N, K), i16(M, N), i16(M, N)
+    Y, dX, G = f32(M, N), f32(M, K), f32(N, K)
+    cws = torch.empty(ops.dfp_convert_workspace_bytes(), dtype=torch.uint8, device=dev)
+    ws = torch.empty(max(ops.dfp16_f32_workspace_bytes(M, K, N, w) for w in range(3)), dtype=torch.uint8, device=dev)
+
+    def step(tm):
+        m = tm.mark if tm else (lambda name: None)
+        m("to_dfp_inputs")
+        ops.dfp_from_f32(X32, X16, ex[0:1], cws)
+        ops.dfp_from_f32(dY32, dY16, ex[2:3], cws)
+        m("to_dfp_weights")
+        ops.dfp_from_f32(W32, W16, ex[1:2], cws)
+        m("fwd")
+        ops.dfp16_gemm_fwd_f32(X16, ex[0:1], W16, ex[1:2], Y, ws)
+        m("requant_y")
+        ops.dfp_from_f32(Y, Y16, ex[3:4], cws)
+        m("dgrad")
+        ops.dfp16_gemm_dgrad_f32(dY16, ex[2:3], W16, ex[1:2], dX, ws)
+        m("wgrad")
+        ops.dfp16_gemm_wgrad_f32(dY16, ex[2:3], X16, ex[0:1], G, ws)
+        m("sgd_update")
+        ops.dfp16_sgd_update(W32, G, 1e-4, W16, ex[1:2], cws)
+    return _timed(torch, step, nsteps)
+
+
 def bench_offsets(torch, nsteps):
     """Offsets (bias) and the static OSS chain on the large-linear workload:
     the forward with the chain in the contraction's epilogue (int8 out), the
@@ -534,6 +576,11 @@ def main():
                    "wgrad": 6.0 * 1024 * 256 * (25088 // 64)}
         fdom = max(dfp_alu, key=lambda k: f_per[k])
         falu = dfp_alu[fdom] / (f_per[fdom] * 1e-3) / 1e12
+        p_ms, p_per = bench_dfp16_paper(torch, 20)
+        # the same VALU bound: per output element and 64-term chunk the digit
+        # combination, one int32 -> FP32 conversion and one FP32 addition
+        pdom = max(("fwd", "dgrad", "wgrad"), key=lambda k: p_per[k])
+        palu = dfp_alu[pdom] / (p_per[pdom] * 1e-3) / 1e12
         o_ms, o_per = bench_offsets(torch, 20)
         o_gemm = 2.0 * T * IN * OUT / (o_per["fwd_oss_fused"] * 1e-3) / 1e12
         o_oss = 5.0 * T * OUT / (o_per["oss_pass"] * 1e-3) / 1e9
@@ -568,6 +615,14 @@ def main():
                                         "achieved": round(falu, 2), "peak": PEAK_VALU_TOPS,
                                         "unit": "T int32 op/s", "frac": round(falu / PEAK_VALU_TOPS, 4),
                                         "ops_per_launch": dfp_alu[fdom]}},
+            "dfp16_paper_step": {"shape": "M25088 K256 N1024, FP32 chunk partials, 1-bit input shift",
+                                 "ms_per_step": round(p_ms, 4),
+                                 "int16_TOPS": round(dfp_ops / (p_ms * 1e-3) / 1e12, 2),
+                                 "kernel_ms": {k: round(v, 4) for k, v in p_per.items()},
+                                 "roofline": {"bound": "alu", "kernel": f"dfp16_gemm_{pdom}_f32",
+                                              "achieved": round(palu, 2), "peak": PEAK_VALU_TOPS,
+                                              "unit": "T int32 op/s", "frac": round(palu / PEAK_VALU_TOPS, 4),
+                                              "ops_per_launch": dfp_alu[pdom]}},
             "offsets_oss": offsets,
             "arc_fault_model": dict(shape="Conv 16x2 valid 1->3 + ReLU, Linear 147->160 + ReLU, Linear 160->2",
                                     **bench_model(torch, 50)),

@@ -253,6 +253,83 @@ int dfp16_gavg(const int16_t *G, const int32_t *eG, const int32_t *eW,
                int64_t n, double *gavg_out, void *stream);
 
 /* ------------------------------------------------------------------------ */
+/* DFP as the DFP page runs it ([DFP] 3.1: float -> DFP conversion with the   */
+/* shared exponent from the exponent of the absolute maximum; 4 "Handling    */
+/* overflows": int32 partials of short chains converted to FP32, scaled by    */
+/* 2^(E_inp + E_wt) and accumulated into an FP32 output, the input shifted by */
+/* one bit; 3: Blocked-DFP, several exponents per tensor; 4: the operations   */
+/* around the integer kernels, the weight update among them, in floating      */
+/* point).  Exponents are device int32.                                       */
+/* ------------------------------------------------------------------------ */
+
+/* The FP32-partial contractions: the roles and layouts of dfp16_gemm_*, with
+ * an FP32 output instead of the down-converted DFP-16 one.  Per output:
+ *   A' = rhu(A, input_shift)   (A is the data operand: X for fwd, dY for
+ *                               dgrad and wgrad; input_shift 0 or 1)
+ *   p_c = the 64-term chunk partials of A' . B   (int32, modulo 2^32)
+ *   the chunks fall into S consecutive ranges, range s covering chunks
+ *   [floor(n_c s / S), floor(n_c (s + 1) / S)); each range is summed in FP32
+ *   in chunk order starting from 0 (every float(p_c) and every addition
+ *   rounded to nearest even), the range sums are added in order to 0, and
+ *   out = fl(total * 2^(eA + input_shift + eB)) with one rounding.
+ * S = nsplit, or dfp16_f32_splits(M, K, N, which) when nsplit = 0 (a
+ * function of the shape alone); 1 <= nsplit <= n_c.  The order is part of
+ * the result: the same S gives the same bits on any path.  out: float,
+ * 16-byte aligned.  workspace: dfp16_f32_workspace_bytes(M, K, N, which,
+ * nsplit) bytes, 256-byte aligned (split partials, operand transposes). */
+int dfp16_f32_splits(int64_t M, int64_t K, int64_t N, int which);
+size_t dfp16_f32_workspace_bytes(int64_t M, int64_t K, int64_t N, int which,
+                                 int nsplit);
+int dfp16_gemm_fwd_f32(const int16_t *X, const int32_t *eX, const int16_t *W,
+                       const int32_t *eW, float *Y, int64_t M, int64_t K,
+                       int64_t N, int input_shift, int nsplit, void *workspace,
+                       size_t workspace_bytes, void *stream);
+int dfp16_gemm_dgrad_f32(const int16_t *dY, const int32_t *edY,
+                         const int16_t *W, const int32_t *eW, float *dX,
+                         int64_t M, int64_t K, int64_t N, int input_shift,
+                         int nsplit, void *workspace, size_t workspace_bytes,
+                         void *stream);
+int dfp16_gemm_wgrad_f32(const int16_t *dY, const int32_t *edY,
+                         const int16_t *X, const int32_t *eX, float *G,
+                         int64_t M, int64_t K, int64_t N, int input_shift,
+                         int nsplit, void *workspace, size_t workspace_bytes,
+                         void *stream);
+
+/* Workspace bytes of dfp_from_f32 and dfp16_sgd_update (4-byte aligned). */
+size_t dfp_convert_workspace_bytes(void);
+
+/* FP32 -> DFP-P, P in [2, 16]: max |x| = f * 2^q (f in [1, 2)) gives
+ * E = q - (P - 2) (0 for an all-zero x) and out = sat_P(round_to_nearest_even
+ * (x / 2^E)).  x: float [n], 16-byte aligned; out: int16 [n], 8-byte aligned;
+ * e_out: device int32; status_out (nullable): 0, 1 when E leaves the signed
+ * 8-bit range (E still written), 2 when x holds a NaN or infinity (outputs
+ * then unspecified). */
+int dfp_from_f32(const float *x, int64_t n, int P, int16_t *out,
+                 int32_t *e_out, int32_t *status_out, void *workspace,
+                 size_t workspace_bytes, void *stream);
+
+/* DFP -> FP32: out = fl(I * 2^e), one rounding (exact for normal results). */
+int dfp_to_f32(const int16_t *I, int64_t n, const int32_t *e, float *out,
+               void *stream);
+
+/* Blocked-DFP: x [rows][K] float; every row is cut into blocks of B values
+ * (the last one shorter when B does not divide K) and each block is
+ * converted as dfp_from_f32 does with its own exponent,
+ * e_out[r * ceil(K / B) + b].  status_out (nullable): the largest status of
+ * any block. */
+int dfp_from_f32_blocked(const float *x, int64_t rows, int64_t K, int B, int P,
+                         int16_t *out, int32_t *e_out, int32_t *status_out,
+                         void *stream);
+
+/* The weight update of the DFP pipeline: FP32 master weights
+ * W32 = fl(W32 - fl(lr * G32)) (two roundings, never fused), then their
+ * DFP-16 copy W16 / eW (as dfp_from_f32 with P = 16) for the next forward.
+ * W32, G32: float [n], 16-byte aligned; W16: int16 [n], 8-byte aligned. */
+int dfp16_sgd_update(float *W32, const float *G32, int64_t n, float lr,
+                     int16_t *W16, int32_t *eW, int32_t *status_out,
+                     void *workspace, size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------ */
 /* Per-channel offsets (bias) and the static OSS requantisation ([TI]        */
 /* section 7: every layer carries mutable int32 offsets, updated by the      */
 /* backward pass, and per-filter right shifts k with multipliers mult;       */

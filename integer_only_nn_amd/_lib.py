@@ -37,6 +37,16 @@ SIGNATURES = {
     "dfp16_gemm_dgrad": (_I, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P, ctypes.c_size_t, _P, _P]),
     "dfp16_gemm_wgrad": (_I, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P, ctypes.c_size_t, _P, _P]),
     "dfp16_gavg": (_I, [_P, _P, _P, _I64, _P, _P]),
+    "dfp16_f32_splits": (_I, [_I64, _I64, _I64, _I]),
+    "dfp16_f32_workspace_bytes": (ctypes.c_size_t, [_I64, _I64, _I64, _I, _I]),
+    "dfp16_gemm_fwd_f32": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _I, _P, ctypes.c_size_t, _P]),
+    "dfp16_gemm_dgrad_f32": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _I, _P, ctypes.c_size_t, _P]),
+    "dfp16_gemm_wgrad_f32": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _I, _P, ctypes.c_size_t, _P]),
+    "dfp_convert_workspace_bytes": (ctypes.c_size_t, []),
+    "dfp_from_f32": (_I, [_P, _I64, _I, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "dfp_to_f32": (_I, [_P, _I64, _P, _P, _P]),
+    "dfp_from_f32_blocked": (_I, [_P, _I64, _I64, _I, _I, _P, _P, _P, _P]),
+    "dfp16_sgd_update": (_I, [_P, _P, _I64, ctypes.c_float, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "apt_workspace_bytes": (ctypes.c_size_t, [_I, _P]),
     "apt_update": (_I, [_I, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, ctypes.c_size_t, _P]),
     "apt_adjust": (_I, [_I, _P, _P, _P, _P, _P, _P, ctypes.c_double, ctypes.c_double, _I, _I, _P, _P]),

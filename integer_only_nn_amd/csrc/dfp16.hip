@@ -32,6 +32,26 @@ namespace {
 constexpr int kChunk = 64;
 constexpr int kPad = 16;
 
+// fl(v * 2^e), one rounding: the product is exact in double (e clamped to
+// the double range, where a larger |e| gives the same single result).
+__device__ __forceinline__ float scale_f32(float v, int e) {
+    e = e < -1022 ? -1022 : (e > 1023 ? 1023 : e);
+    return float(double(v) * __longlong_as_double(int64_t(e + 1023) << 52));
+}
+
+// rhu(a, 1) of 8 int16 held in a v4i (the input shifted by one bit):
+// (a >> 1) + (a & 1) in every 16-bit half, which cannot carry across.
+__device__ __forceinline__ v4i rhu1_x8(v4i r) {
+    typedef short v2s __attribute__((ext_vector_type(2)));
+    int w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const v2s a = __builtin_bit_cast(v2s, w[q]);
+        w[q] = __builtin_bit_cast(int, v2s((a >> 1) + (a & 1)));
+    }
+    return v4i{w[0], w[1], w[2], w[3]};
+}
+
 // Split 8 int16 (4 dwords) into 8 high bytes and 8 flipped low bytes.
 __device__ __forceinline__ void split8(v4i w, uint32_t &h0, uint32_t &h1, uint32_t &l0,
                                        uint32_t &l1) {
@@ -81,6 +101,10 @@ struct Loader16 {
             reg[it] = v;
         }
     }
+    __device__ __forceinline__ void rhu1() {
+#pragma unroll
+        for (int it = 0; it < kPer; ++it) reg[it] = rhu1_x8(reg[it]);
+    }
     __device__ __forceinline__ void store(int8_t *hi, int8_t *lo, int tid) const {
 #pragma unroll
         for (int it = 0; it < kPer; ++it) {
@@ -104,9 +128,14 @@ struct DfpArgs {
     int r;               // per-chunk shift
     int split;           // K splits (gridDim.y)
     bool atomic;         // accumulate with atomicAdd (split > 1)
+    // FP32 form: acc holds floats, [split][M][N] partial sums when split > 1
+    // (no atomics: the splits are added in order afterwards), else the
+    // result scaled by 2^(*ea + shift + *eb)
+    int shift;
+    const int32_t *ea, *eb;
 };
 
-template <int BM, int BN, int WGM, int WGN, bool EDGE>
+template <int BM, int BN, int WGM, int WGN, bool EDGE, bool F32>
 __global__ __launch_bounds__(WGM *WGN * 64) void dfp16_kernel(DfpArgs g) {
     constexpr int NT = WGM * WGN * 64;
     constexpr int WTM = BM / WGM, WTN = BN / WGN;
@@ -136,6 +165,7 @@ __global__ __launch_bounds__(WGM *WGN * 64) void dfp16_kernel(DfpArgs g) {
     if (c_begin < c_end) {
         la.load(g.a, m0, c_begin * kChunk, tid);
         lb.load(g.b, n0, c_begin * kChunk, tid);
+        if (F32 && g.shift) la.rhu1();
         la.store(lds, lds + PLANE_A, tid);
         lb.store(lds + 2 * PLANE_A, lds + 2 * PLANE_A + PLANE_B, tid);
     }
@@ -187,12 +217,16 @@ __global__ __launch_bounds__(WGM *WGN * 64) void dfp16_kernel(DfpArgs g) {
                 for (int v = 0; v < 4; ++v) {
                     const uint32_t p = (uint32_t(hh[v]) << 16) + (uint32_t(x[v]) << 8) +
                                        uint32_t(ll[v]) + uint32_t(rt[i].x) + ct[v];
-                    acc[i][j][v] += rhu(int32_t(p), r);
+                    if (F32)
+                        acc[i][j][v] = __float_as_int(__fadd_rn(__int_as_float(acc[i][j][v]), float(int32_t(p))));
+                    else
+                        acc[i][j][v] += rhu(int32_t(p), r);
                 }
             }
         }
         if (c + 1 < c_end) {
             int8_t *nxt = lds + (cur ^ 1) * STAGE;
+            if (F32 && g.shift) la.rhu1();
             la.store(nxt, nxt + PLANE_A, tid);
             lb.store(nxt + 2 * PLANE_A, nxt + 2 * PLANE_A + PLANE_B, tid);
         }
@@ -201,6 +235,24 @@ __global__ __launch_bounds__(WGM *WGN * 64) void dfp16_kernel(DfpArgs g) {
 
     uint32_t amax = 0;
     const int em = lane & 15, en = (lane >> 4) * 4;
+    if (F32) {
+        const int e = g.split == 1 ? *g.ea + g.shift + *g.eb : 0;
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int m = m0 + wm * WTM + i * 16 + em;
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int n = n0 + wn * WTN + j * 16 + en;
+                float *cp = reinterpret_cast<float *>(g.acc) + (int64_t(blockIdx.y) * g.M + m) * g.N + n;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const float f = __int_as_float(acc[i][j][v]);
+                    if (m < g.M && n + v < g.N) cp[v] = g.split == 1 ? scale_f32(f, e) : f;
+                }
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
         const int m = m0 + wm * WTM + i * 16 + em;
@@ -283,6 +335,10 @@ struct Ld {
             reg[it] = *reinterpret_cast<const v4i *>(p);
         }
     }
+    __device__ __forceinline__ void rhu1() {
+#pragma unroll
+        for (int it = 0; it < IT; ++it) reg[it] = rhu1_x8(reg[it]);
+    }
     __device__ __forceinline__ void store(int8_t *hi, int8_t *lo, int tid) const {
 #pragma unroll
         for (int it = 0; it < IT; ++it) {
@@ -335,13 +391,18 @@ struct Args {
     int32_t *acc;        // [M][N] (split == 1) or split partial tiles [split][M][N]
     uint32_t *absmax;    // max-combined (split == 1)
     int M, N, L, r, split;
+    // FP32 form only: A's one-bit shift and the exponents of the final
+    // scaling 2^(*ea + shift + *eb) (split == 1; acc then holds floats)
+    int shift;
+    const int32_t *ea, *eb;
 };
+
 
 // Persistent: workgroup w takes work units w, w + gridDim.x, ...; a unit is
 // one output tile and one range of chunks (a K split).  The chunk loop runs
 // across unit boundaries, so the first chunk of the next unit is loaded while
 // the last chunk of the current one computes and its result is stored.
-template <bool A_KM, bool B_KM>
+template <bool A_KM, bool B_KM, bool F32>
 __global__ __launch_bounds__(NT, 1) void dfp_kernel(Args g) {
     __shared__ __attribute__((aligned(16))) int8_t lds[2 * STAGE];
     __shared__ __attribute__((aligned(16))) uint32_t csum[NT / 64][64];  // per wave: 128 * sum(B') of its 64 columns
@@ -377,6 +438,7 @@ __global__ __launch_bounds__(NT, 1) void dfp_kernel(Args g) {
 
     la.load(g.a, g.lda, m0, 64 * c0, tid);
     lb.load(g.b, g.ldb, n0, 64 * c0, tid);
+    if (F32 && g.shift) la.rhu1();
     la.store(lds, lds + PLANE, tid);
     lb.store(lds + 2 * PLANE, lds + 3 * PLANE, tid);
     __syncthreads();
@@ -441,11 +503,15 @@ __global__ __launch_bounds__(NT, 1) void dfp_kernel(Args g) {
             ll = __builtin_amdgcn_mfma_i32_32x32x32_i8(bl[j][1], al[1], ll, 0, 0, 0);
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                // p mod 2^32, then acc += rhu(p, r) = (p >> r) + bit (r - 1) of p
+                // p mod 2^32, then acc += rhu(p, r) = (p >> r) + bit (r - 1) of p;
+                // FP32 form: acc = fl(acc + fl(float(p)))
                 const uint32_t t = opaque((uint32_t(x[v]) << 8) + uint32_t(ll[v]));
                 const uint32_t p = (uint32_t(hh[v]) << 16) + opaque(t + rt + uint32_t(cb[v >> 2][v & 3]));
-                acc[j][v] = int32_t(uint32_t(acc[j][v]) + uint32_t(int32_t(p) >> r) +
-                                    __builtin_amdgcn_ubfe(p, rm1, rw));
+                if (F32)
+                    acc[j][v] = __float_as_int(__fadd_rn(__int_as_float(acc[j][v]), float(int32_t(p))));
+                else
+                    acc[j][v] = int32_t(uint32_t(acc[j][v]) + uint32_t(int32_t(p) >> r) +
+                                        __builtin_amdgcn_ubfe(p, rm1, rw));
             }
         }
 
@@ -453,6 +519,7 @@ __global__ __launch_bounds__(NT, 1) void dfp_kernel(Args g) {
         // stores are issued, so its wait does not include them
         int8_t *nx = lds + (stage ^ 1) * STAGE;
         if (more) {
+            if (F32 && g.shift) la.rhu1();
             la.store(nx, nx + PLANE, tid);
             lb.store(nx + 2 * PLANE, nx + 3 * PLANE, tid);
         }
@@ -466,9 +533,14 @@ __global__ __launch_bounds__(NT, 1) void dfp_kernel(Args g) {
                 for (int q = 0; q < 4; ++q) {
                     const int n = n0 + 64 * wn + 32 * j + 8 * q + 4 * (lane >> 5);
                     int32_t *cp = g.acc + (int64_t(u / ntiles) * g.M + m) * g.N + n;
-                    const v4i v = {acc[j][4 * q], acc[j][4 * q + 1], acc[j][4 * q + 2], acc[j][4 * q + 3]};
+                    v4i v = {acc[j][4 * q], acc[j][4 * q + 1], acc[j][4 * q + 2], acc[j][4 * q + 3]};
+                    if (F32 && g.split == 1) {
+                        const int e = *g.ea + g.shift + *g.eb;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) v[i] = __float_as_int(scale_f32(__int_as_float(v[i]), e));
+                    }
                     *reinterpret_cast<v4i *>(cp) = v;
-                    if (g.split == 1) {
+                    if (!F32 && g.split == 1) {
 #pragma unroll
                         for (int e = 0; e < 4; ++e) amax = max(amax, abs_u32(v[e]));
                     }
@@ -480,9 +552,23 @@ __global__ __launch_bounds__(NT, 1) void dfp_kernel(Args g) {
         __syncthreads();
         u = nu; m0 = nm0; n0 = nn0; c = nc; c1 = nc1; stage ^= 1;
     }
-    if (g.split == 1 && g.absmax) {
+    if (!F32 && g.split == 1 && g.absmax) {
         amax = wave_max_u32(amax);
         if (lane == 0) publish_max_u32(g.absmax, amax);
+    }
+}
+
+// FP32 form: out[e] = fl(total * 2^(*ea + shift + *eb)) with total the split
+// partial sums added in split order to 0.
+__global__ __launch_bounds__(256) void split_reduce_f32(const float *__restrict__ part, int split, int64_t n,
+                                                        float *__restrict__ out, const int32_t *__restrict__ ea,
+                                                        int shift, const int32_t *__restrict__ eb) {
+    const int e = *ea + shift + *eb;
+    const int64_t nt = int64_t(gridDim.x) * blockDim.x;
+    for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += nt) {
+        float s = 0.0f;
+        for (int p = 0; p < split; ++p) s = __fadd_rn(s, __builtin_nontemporal_load(part + int64_t(p) * n + i));
+        out[i] = scale_f32(s, e);
     }
 }
 
@@ -598,7 +684,7 @@ int chunk_shift(int64_t L) {
 // acc[M][N] = sum_c rhu(p_c, r) for A [M][L], B [N][L] (K-major int16).
 int contract(const Src16 &a, const Src16 &b, int M, int N, int L, int32_t *acc, uint32_t *absmax,
              hipStream_t st) {
-    DfpArgs g{a, b, acc, absmax, M, N, L, chunk_shift(L), 1, false};
+    DfpArgs g{a, b, acc, absmax, M, N, L, chunk_shift(L), 1, false, 0, nullptr, nullptr};
     const int tiles = ((M + 127) / 128) * ((N + 127) / 128);
     const int nchunks = (L + kChunk - 1) / kChunk;
     if (tiles < 512 && nchunks >= 16) {
@@ -613,8 +699,8 @@ int contract(const Src16 &a, const Src16 &b, int M, int N, int L, int32_t *acc, 
     }
     const bool even = M % 128 == 0 && N % 128 == 0 && L % kChunk == 0 && a.vec && b.vec;
     dim3 grid(tiles, g.split), block(256);
-    if (even) dfp16_kernel<128, 128, 2, 2, false><<<grid, block, 0, st>>>(g);
-    else dfp16_kernel<128, 128, 2, 2, true><<<grid, block, 0, st>>>(g);
+    if (even) dfp16_kernel<128, 128, 2, 2, false, false><<<grid, block, 0, st>>>(g);
+    else dfp16_kernel<128, 128, 2, 2, true, false><<<grid, block, 0, st>>>(g);
     if (int rc = check_launch("dfp16 contraction")) return rc;
     if (g.atomic) return launch_absmax_i32(acc, int64_t(M) * N, absmax, st);
     return IONN_OK;
@@ -643,7 +729,7 @@ template <bool A_KM, bool B_KM>
 int contract2(const int16_t *a, int64_t lda, const int16_t *b, int64_t ldb, int M, int N, int L,
               int32_t *acc, int32_t *part, uint32_t *absmax, hipStream_t st) {
     const int split = split2(M, N, L);
-    d2::Args g{a, b, lda, ldb, split > 1 ? part : acc, absmax, M, N, L, chunk_shift(L), split};
+    d2::Args g{a, b, lda, ldb, split > 1 ? part : acc, absmax, M, N, L, chunk_shift(L), split, 0, nullptr, nullptr};
     const int tiles = (M / d2::BM) * (N / d2::BN);
     int cus = 256;
     int dev = 0;
@@ -651,7 +737,7 @@ int contract2(const int16_t *a, int64_t lda, const int16_t *b, int64_t ldb, int 
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
         cus = 256;
     const int units = tiles * split;
-    d2::dfp_kernel<A_KM, B_KM><<<dim3(units < cus ? units : cus), dim3(d2::NT), 0, st>>>(g);
+    d2::dfp_kernel<A_KM, B_KM, false><<<dim3(units < cus ? units : cus), dim3(d2::NT), 0, st>>>(g);
     if (int rc = check_launch("dfp16 contraction")) return rc;
     if (split > 1) {
         const int64_t n = int64_t(M) * N;
@@ -711,6 +797,115 @@ int finish(const Workspace &w, int64_t n, const int32_t *ea, const int32_t *eb, 
     downconvert_kernel<<<dim3(unsigned(blocks)), dim3(256), 0, st>>>(w.acc, n, w.absmax, ea, eb, r,
                                                                     out, e_out, status);
     return check_launch("dfp16 down-conversion");
+}
+
+// ---------------------------------------------------------------------------
+// FP32 form: chunk partials summed in FP32 over S consecutive chunk ranges,
+// the ranges added in order, the total scaled by 2^(eA + shift + eB).
+// ---------------------------------------------------------------------------
+
+// Default range count: a function of the shape alone (so the result never
+// depends on which kernel runs), equal to split2 on tile-aligned shapes.
+int split_f32(int64_t M, int64_t N, int64_t L) {
+    const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128), nch = (L + 63) / 64;
+    if (tiles >= 256 || nch < 8) return 1;
+    int64_t s = (256 + tiles - 1) / tiles;
+    if (s > nch / 4) s = nch / 4;
+    return s < 1 ? 1 : int(s);
+}
+
+// Output rows, output columns and reduction length of a role.
+void role_dims(int64_t M, int64_t K, int64_t N, int which, int64_t &R, int64_t &C, int64_t &L) {
+    if (which == IONN_DFP16_FWD) { R = M; C = N; L = K; }
+    else if (which == IONN_DFP16_DGRAD) { R = M; C = K; L = N; }
+    else { R = N; C = K; L = M; }
+}
+
+struct WsF32 {
+    float *part;
+    int16_t *t0, *t1;
+};
+
+size_t ws_f32_bytes(int64_t M, int64_t K, int64_t N, int which, int S, WsF32 *w, void *base) {
+    int64_t R, C, L;
+    role_dims(M, K, N, which, R, C, L);
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t o = off;
+        off += align256(bytes);
+        return base ? static_cast<char *>(base) + o : nullptr;
+    };
+    char *part = S > 1 ? take(size_t(S) * R * C * 4) : nullptr;
+    char *t0 = nullptr, *t1 = nullptr;
+    if (which == IONN_DFP16_DGRAD) t0 = take(size_t(N) * K * 2);
+    if (which == IONN_DFP16_WGRAD) {
+        t0 = take(size_t(N) * M * 2);
+        t1 = take(size_t(K) * M * 2);
+    }
+    if (w) *w = WsF32{reinterpret_cast<float *>(part), reinterpret_cast<int16_t *>(t0),
+                      reinterpret_cast<int16_t *>(t1)};
+    return off ? off : 256;
+}
+
+template <bool A_KM, bool B_KM>
+int contract2_f32(const int16_t *a, int64_t lda, const int16_t *b, int64_t ldb, int M, int N, int L, int S,
+                  int shift, const int32_t *ea, const int32_t *eb, float *out, float *part, hipStream_t st) {
+    d2::Args g{a, b, lda, ldb, reinterpret_cast<int32_t *>(S > 1 ? part : out), nullptr, M, N, L, 0, S,
+               shift, ea, eb};
+    const int tiles = (M / d2::BM) * (N / d2::BN);
+    int cus = 256, dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+        cus = 256;
+    const int units = tiles * S;
+    d2::dfp_kernel<A_KM, B_KM, true><<<dim3(units < cus ? units : cus), dim3(d2::NT), 0, st>>>(g);
+    return check_launch("dfp16 FP32 contraction");
+}
+
+int contract_f32(const Src16 &a, const Src16 &b, int M, int N, int L, int S, int shift, const int32_t *ea,
+                 const int32_t *eb, float *out, float *part, hipStream_t st) {
+    DfpArgs g{a, b, reinterpret_cast<int32_t *>(S > 1 ? part : out), nullptr, M, N, L, 0, S, false,
+              shift, ea, eb};
+    // 64 x 64 tiles: the FP32 accumulators of a 128 x 128 tile spill here
+    const int tiles = ((M + 63) / 64) * ((N + 63) / 64);
+    const bool even = M % 64 == 0 && N % 64 == 0 && L % kChunk == 0 && a.vec && b.vec;
+    dim3 grid(tiles, S), block(256);
+    if (even) dfp16_kernel<64, 64, 2, 2, false, true><<<grid, block, 0, st>>>(g);
+    else dfp16_kernel<64, 64, 2, 2, true, true><<<grid, block, 0, st>>>(g);
+    return check_launch("dfp16 FP32 contraction");
+}
+
+int reduce_f32(const float *part, int S, int64_t n, float *out, const int32_t *ea, int shift, const int32_t *eb,
+               hipStream_t st) {
+    if (S <= 1) return IONN_OK;
+    int64_t blocks = (n + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    d2::split_reduce_f32<<<dim3(unsigned(blocks)), dim3(256), 0, st>>>(part, S, n, out, ea, shift, eb);
+    return check_launch("dfp16 FP32 split sum");
+}
+
+int check_f32(const void *A, const int32_t *eA, const void *B, const int32_t *eB, const float *out, int64_t M,
+              int64_t K, int64_t N, int input_shift, int nsplit, void *ws, size_t ws_size, int which,
+              const char *name, int &S) {
+    IONN_REQUIRE(M >= 1 && K >= 1 && N >= 1 && M <= kMaxDim && K <= kMaxDim && N <= kMaxDim &&
+                     M * N <= kMaxDim && M * K <= kMaxDim && N * K <= kMaxDim,
+                 IONN_ERR_SHAPE, "%s: sizes must be >= 1 with every tensor below 2^31 elements", name);
+    IONN_REQUIRE(A && eA && B && eB && out, IONN_ERR_ARG, "%s: NULL argument", name);
+    IONN_REQUIRE(input_shift == 0 || input_shift == 1, IONN_ERR_RANGE, "%s: input_shift = %d (0 or 1)", name,
+                 input_shift);
+    int64_t R, C, L;
+    role_dims(M, K, N, which, R, C, L);
+    const int64_t nch = (L + kChunk - 1) / kChunk;
+    IONN_REQUIRE(nsplit >= 0 && nsplit <= nch && nsplit <= 4096, IONN_ERR_RANGE,
+                 "%s: nsplit = %d outside [0, %lld]", name, nsplit, (long long)(nch < 4096 ? nch : 4096));
+    S = nsplit ? nsplit : split_f32(R, C, L);
+    IONN_REQUIRE(S * R * C <= (int64_t(1) << 40), IONN_ERR_SHAPE, "%s: split partials too large", name);
+    const size_t need = ws_f32_bytes(M, K, N, which, S, nullptr, nullptr);
+    IONN_REQUIRE(ws != nullptr && aligned(ws, 256) && ws_size >= need, IONN_ERR_WORKSPACE,
+                 "%s: workspace must be 256-byte aligned and hold %zu bytes", name, need);
+    IONN_REQUIRE(aligned(A, 2) && aligned(B, 2) && aligned(out, 16) && aligned(eA, 4) && aligned(eB, 4),
+                 IONN_ERR_ALIGN, "%s: misaligned pointer (out needs 16 bytes)", name);
+    return IONN_OK;
 }
 
 int check_common(const void *A, const int32_t *eA, const void *B, const int32_t *eB, void *out,
@@ -808,6 +1003,91 @@ int dfp16_gemm_wgrad(const int16_t *dY, const int32_t *edY, const int16_t *X, co
     Src16 b{w.t1, M, int(K), int(M), M % 8 == 0};
     if (int rc = contract(a, b, int(N), int(K), int(M), w.acc, w.absmax, st)) return rc;
     return finish(w, N * K, edY, eX, chunk_shift(M), G, eG, status_out, st);
+}
+
+int dfp16_f32_splits(int64_t M, int64_t K, int64_t N, int which) {
+    if (M < 1 || K < 1 || N < 1 || which < 0 || which > 2) return 0;
+    int64_t R, C, L;
+    role_dims(M, K, N, which, R, C, L);
+    return split_f32(R, C, L);
+}
+
+size_t dfp16_f32_workspace_bytes(int64_t M, int64_t K, int64_t N, int which, int nsplit) {
+    if (M < 1 || K < 1 || N < 1 || which < 0 || which > 2 || nsplit < 0) return 0;
+    const int S = nsplit ? nsplit : dfp16_f32_splits(M, K, N, which);
+    return ws_f32_bytes(M, K, N, which, S, nullptr, nullptr);
+}
+
+int dfp16_gemm_fwd_f32(const int16_t *X, const int32_t *eX, const int16_t *W, const int32_t *eW, float *Y,
+                       int64_t M, int64_t K, int64_t N, int input_shift, int nsplit, void *workspace,
+                       size_t workspace_bytes, void *stream) {
+    clear_error();
+    int S = 1;
+    if (int rc = check_f32(X, eX, W, eW, Y, M, K, N, input_shift, nsplit, workspace, workspace_bytes,
+                           IONN_DFP16_FWD, "dfp16_gemm_fwd_f32", S))
+        return rc;
+    hipStream_t st = as_stream(stream);
+    WsF32 w;
+    ws_f32_bytes(M, K, N, IONN_DFP16_FWD, S, &w, workspace);
+    if (fast2(int(M), int(N), int(K), X, K, W, K)) {
+        if (int rc = contract2_f32<true, true>(X, K, W, K, int(M), int(N), int(K), S, input_shift, eX, eW, Y,
+                                               w.part, st))
+            return rc;
+    } else {
+        Src16 a{X, K, int(M), int(K), aligned(X, 16) && K % 8 == 0};
+        Src16 b{W, K, int(N), int(K), aligned(W, 16) && K % 8 == 0};
+        if (int rc = contract_f32(a, b, int(M), int(N), int(K), S, input_shift, eX, eW, Y, w.part, st)) return rc;
+    }
+    return reduce_f32(w.part, S, M * N, Y, eX, input_shift, eW, st);
+}
+
+int dfp16_gemm_dgrad_f32(const int16_t *dY, const int32_t *edY, const int16_t *W, const int32_t *eW, float *dX,
+                         int64_t M, int64_t K, int64_t N, int input_shift, int nsplit, void *workspace,
+                         size_t workspace_bytes, void *stream) {
+    clear_error();
+    int S = 1;
+    if (int rc = check_f32(dY, edY, W, eW, dX, M, K, N, input_shift, nsplit, workspace, workspace_bytes,
+                           IONN_DFP16_DGRAD, "dfp16_gemm_dgrad_f32", S))
+        return rc;
+    hipStream_t st = as_stream(stream);
+    WsF32 w;
+    ws_f32_bytes(M, K, N, IONN_DFP16_DGRAD, S, &w, workspace);
+    if (fast2(int(M), int(K), int(N), dY, N, W, K)) {
+        if (int rc = contract2_f32<true, false>(dY, N, W, K, int(M), int(K), int(N), S, input_shift, edY, eW, dX,
+                                                w.part, st))
+            return rc;
+    } else {
+        if (int rc = transpose16(W, w.t0, int(N), int(K), st)) return rc;
+        Src16 a{dY, N, int(M), int(N), aligned(dY, 16) && N % 8 == 0};
+        Src16 b{w.t0, N, int(K), int(N), N % 8 == 0};
+        if (int rc = contract_f32(a, b, int(M), int(K), int(N), S, input_shift, edY, eW, dX, w.part, st)) return rc;
+    }
+    return reduce_f32(w.part, S, M * K, dX, edY, input_shift, eW, st);
+}
+
+int dfp16_gemm_wgrad_f32(const int16_t *dY, const int32_t *edY, const int16_t *X, const int32_t *eX, float *G,
+                         int64_t M, int64_t K, int64_t N, int input_shift, int nsplit, void *workspace,
+                         size_t workspace_bytes, void *stream) {
+    clear_error();
+    int S = 1;
+    if (int rc = check_f32(dY, edY, X, eX, G, M, K, N, input_shift, nsplit, workspace, workspace_bytes,
+                           IONN_DFP16_WGRAD, "dfp16_gemm_wgrad_f32", S))
+        return rc;
+    hipStream_t st = as_stream(stream);
+    WsF32 w;
+    ws_f32_bytes(M, K, N, IONN_DFP16_WGRAD, S, &w, workspace);
+    if (fast2(int(N), int(K), int(M), dY, N, X, K)) {
+        if (int rc = contract2_f32<false, false>(dY, N, X, K, int(N), int(K), int(M), S, input_shift, edY, eX, G,
+                                                 w.part, st))
+            return rc;
+    } else {
+        if (int rc = transpose16(dY, w.t0, int(M), int(N), st)) return rc;
+        if (int rc = transpose16(X, w.t1, int(M), int(K), st)) return rc;
+        Src16 a{w.t0, M, int(N), int(M), M % 8 == 0};
+        Src16 b{w.t1, M, int(K), int(M), M % 8 == 0};
+        if (int rc = contract_f32(a, b, int(N), int(K), int(M), S, input_shift, edY, eX, G, w.part, st)) return rc;
+    }
+    return reduce_f32(w.part, S, N * K, G, edY, input_shift, eX, st);
 }
 
 int dfp16_gavg(const int16_t *G, const int32_t *eG, const int32_t *eW, int64_t n, double *gavg_out,

@@ -266,6 +266,85 @@ def dfp16_gemm_wgrad(dY, edY, X, eX, G, eG, workspace, chunk=64, status_out=None
          workspace, status_out, stream)
 
 
+# ---- DFP as the DFP page runs it: FP32 partials, conversions, SGD -----------
+
+f32 = torch.float32
+
+
+def dfp16_f32_splits(M, K, N, which):
+    return int(lib().dfp16_f32_splits(M, K, N, which))
+
+
+def dfp16_f32_workspace_bytes(M, K, N, which, nsplit=0):
+    return int(lib().dfp16_f32_workspace_bytes(M, K, N, which, nsplit))
+
+
+def _dfp_f32(fn, name, A, eA, B, eB, out, M, K, N, input_shift, nsplit, workspace, stream):
+    check(fn(_p(A, i16, name="A"), _p(eA, i32, 1, "eA"), _p(B, i16, name="B"), _p(eB, i32, 1, "eB"),
+             _p(out, f32, name="out"), M, K, N, int(input_shift), int(nsplit), _p(workspace, None, name="workspace"),
+             workspace.numel() * workspace.element_size() if workspace is not None else 0, _stream(stream)), name)
+
+
+def dfp16_gemm_fwd_f32(X, eX, W, eW, Y, workspace, input_shift=1, nsplit=0, stream=None):
+    M, K = X.shape
+    N = W.shape[0]
+    assert tuple(W.shape) == (N, K) and tuple(Y.shape) == (M, N)
+    _dfp_f32(lib().dfp16_gemm_fwd_f32, "dfp16_gemm_fwd_f32", X, eX, W, eW, Y, M, K, N, input_shift, nsplit,
+             workspace, stream)
+
+
+def dfp16_gemm_dgrad_f32(dY, edY, W, eW, dX, workspace, input_shift=1, nsplit=0, stream=None):
+    M, N = dY.shape
+    K = W.shape[1]
+    assert tuple(W.shape) == (N, K) and tuple(dX.shape) == (M, K)
+    _dfp_f32(lib().dfp16_gemm_dgrad_f32, "dfp16_gemm_dgrad_f32", dY, edY, W, eW, dX, M, K, N, input_shift, nsplit,
+             workspace, stream)
+
+
+def dfp16_gemm_wgrad_f32(dY, edY, X, eX, G, workspace, input_shift=1, nsplit=0, stream=None):
+    M, N = dY.shape
+    K = X.shape[1]
+    assert tuple(X.shape) == (M, K) and tuple(G.shape) == (N, K)
+    _dfp_f32(lib().dfp16_gemm_wgrad_f32, "dfp16_gemm_wgrad_f32", dY, edY, X, eX, G, M, K, N, input_shift, nsplit,
+             workspace, stream)
+
+
+def dfp_convert_workspace_bytes():
+    return int(lib().dfp_convert_workspace_bytes())
+
+
+def dfp_from_f32(x, out, e_out, workspace, P=16, status_out=None, stream=None):
+    assert x.numel() == out.numel()
+    check(lib().dfp_from_f32(_p(x, f32, name="x"), x.numel(), int(P), _p(out, i16, name="out"),
+                             _p(e_out, i32, 1, "e_out"), _p(status_out, i32, 1, "status_out"),
+                             _p(workspace, None, name="workspace"),
+                             workspace.numel() * workspace.element_size(), _stream(stream)), "dfp_from_f32")
+
+
+def dfp_to_f32(I, e, out, stream=None):
+    assert I.numel() == out.numel()
+    check(lib().dfp_to_f32(_p(I, i16, name="I"), I.numel(), _p(e, i32, 1, "e"), _p(out, f32, name="out"),
+                           _stream(stream)), "dfp_to_f32")
+
+
+def dfp_from_f32_blocked(x, out, e_out, B=64, P=16, status_out=None, stream=None):
+    rows, K = x.shape
+    nb = (K + B - 1) // B
+    assert tuple(out.shape) == (rows, K) and e_out.numel() >= rows * nb
+    check(lib().dfp_from_f32_blocked(_p(x, f32, name="x"), rows, K, int(B), int(P), _p(out, i16, name="out"),
+                                     _p(e_out, i32, rows * nb, "e_out"), _p(status_out, i32, 1, "status_out"),
+                                     _stream(stream)), "dfp_from_f32_blocked")
+
+
+def dfp16_sgd_update(W32, G32, lr, W16, eW, workspace, status_out=None, stream=None):
+    n = W32.numel()
+    assert G32.numel() == n and W16.numel() == n
+    check(lib().dfp16_sgd_update(_p(W32, f32, name="W32"), _p(G32, f32, name="G32"), n, float(lr),
+                                 _p(W16, i16, name="W16"), _p(eW, i32, 1, "eW"), _p(status_out, i32, 1, "status_out"),
+                                 _p(workspace, None, name="workspace"), workspace.numel() * workspace.element_size(),
+                                 _stream(stream)), "dfp16_sgd_update")
+
+
 def dfp16_gavg(G, eG, eW, gavg_out, stream=None):
     check(lib().dfp16_gavg(_p(G, i16, name="G"), _p(eG, i32, 1, "eG"), _p(eW, i32, 1, "eW"),
                            G.numel(), _p(gavg_out, torch.float64, 1, "gavg_out"), _stream(stream)),

@@ -86,6 +86,8 @@ def _declare(L):
         "ora_dfp_contract_f32": (_I64, [_P, _I64, _I64, _P, _I64, _I64, _I64, _I64, _I64, _I, _I, _I, _I, _P]),
         "ora_dfp_fwd_f32_blocked": (_I64, [_P, _P, _P, _P, _I64, _I64, _I64, _I, _I, _P]),
         "ora_dfp16_sgd": (_I, [_P, _P, _I64, ctypes.c_float, _P, _P]),
+        "ora_dfp_contract_f32_at": (ctypes.c_float, [_P, _I64, _I64, _P, _I64, _I64, _I64, _I, _I, _I, _I,
+                                                     _I64, _I64]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -505,3 +507,20 @@ def dfp16_sgd(W32, G32, lr):
     st = lib().ora_dfp16_sgd(_c(W, np.float32), _c(G, np.float32), W.size, float(lr), _c(W16, np.int16),
                              ctypes.byref(e))
     return W, W16, e.value, st
+
+
+def dfp16_f32_at(role, A, eA, B, eB, m, n, S=1, input_shift=1):
+    """One output (row m, column n) of dfp16_{fwd,dgrad,wgrad}_f32."""
+    if role == "fwd":      # A = X [M][K], B = W [N][K]
+        K = A.shape[1]
+        args = (A, K, 1, B, 1, K, K)
+    elif role == "dgrad":  # A = dY [M][N], B = W [N][K]
+        N, K = B.shape
+        args = (A, N, 1, B, K, 1, N)
+    else:                  # A = dY [M][N], B = X [M][K]; output [N][K]
+        M, N = A.shape
+        K = B.shape[1]
+        args = (A, 1, N, B, K, 1, M)
+    a, sam, sak, b, sbk, sbn, L = args
+    return lib().ora_dfp_contract_f32_at(_c(a, np.int16), sam, sak, _c(b, np.int16), sbk, sbn, L,
+                                         int(input_shift), int(eA), int(eB), int(S), int(m), int(n))

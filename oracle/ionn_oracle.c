@@ -845,18 +845,25 @@ int ora_dfp_from_f32_blocked(const float *x, int64_t rows, int64_t K, int B, int
     return st;
 }
 
+/* Exponent sums beyond the double range: clamped to [-1022, 1023], where
+ * every single-precision result is already 0 or infinite (reading U35). */
+static int clamp_exp(int e)
+{
+    return e < -1022 ? -1022 : (e > 1023 ? 1023 : e);
+}
+
 /* DFP -> float: out = I * 2^e rounded once to single (exact whenever the
  * value is a normal single). */
 void ora_dfp_to_f32(const int16_t *I, int64_t n, int e, float *out)
 {
-    const double s = pow2d(e);
+    const double s = pow2d(clamp_exp(e));
     for (int64_t j = 0; j < n; ++j) out[j] = (float)((double)I[j] * s);
 }
 
 /* fl(v * 2^e): the exact product in double, rounded once to single. */
 float ora_scale_f32(float v, int e)
 {
-    return (float)((double)v * pow2d(e));
+    return (float)((double)v * pow2d(clamp_exp(e)));
 }
 
 /* Chunk ranges of the FP32 accumulation: range s of S covers chunks
@@ -954,4 +961,24 @@ int ora_dfp16_sgd(float *W32, const float *G32, int64_t n, float lr, int16_t *W1
         W32[j] = W32[j] - t;
     }
     return ora_dfp_from_f32(W32, n, 16, W16, eW);
+}
+
+/* One output of ora_dfp_contract_f32 (for sampled checks at full size). */
+float ora_dfp_contract_f32_at(const int16_t *A, int64_t sam, int64_t sak, const int16_t *B,
+                              int64_t sbk, int64_t sbn, int64_t L, int input_shift, int eA,
+                              int eB, int S, int64_t m, int64_t n)
+{
+    const int64_t nch = (L + 63) / 64;
+    float total = 0.0f;
+    for (int s = 0; s < S; ++s) {
+        float part = 0.0f;
+        for (int64_t c = range_start(nch, S, s); c < range_start(nch, S, s + 1); ++c) {
+            uint32_t p = 0;
+            for (int64_t k = 64 * c; k < 64 * c + 64 && k < L; ++k)
+                p += (uint32_t)(ora_rhu(A[m * sam + k * sak], input_shift) * (int32_t)B[k * sbk + n * sbn]);
+            part = part + (float)u32_to_i32(p);
+        }
+        total = total + part;
+    }
+    return ora_scale_f32(total, eA + input_shift + eB);
 }

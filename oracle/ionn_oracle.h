@@ -193,6 +193,9 @@ int64_t ora_dfp_fwd_f32_blocked(const int16_t *X, const int32_t *eX, const int16
                                 const int32_t *eW, int64_t M, int64_t K, int64_t N,
                                 int input_shift, int S, float *out);
 int     ora_dfp16_sgd(float *W32, const float *G32, int64_t n, float lr, int16_t *W16, int *eW);
+float   ora_dfp_contract_f32_at(const int16_t *A, int64_t sam, int64_t sak, const int16_t *B,
+                                int64_t sbk, int64_t sbn, int64_t L, int input_shift, int eA,
+                                int eB, int S, int64_t m, int64_t n);
 
 #ifdef __cplusplus
 }

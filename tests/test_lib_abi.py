@@ -153,3 +153,32 @@ def test_apt_validation():
     assert adj(tmin=3.0, tmax=2.0) == RANGE
     assert adj(tmin=float("nan")) == RANGE
     assert adj(n=arrN(5, 0)) == SHAPE
+
+
+def test_dfp_paper_form_validation():
+    ws = lib.dfp16_f32_workspace_bytes(256, 256, 256, 0, 0)
+    assert ws >= 256 and lib.dfp16_f32_workspace_bytes(0, 1, 1, 0, 0) == 0
+    # the default range count depends on the shape only
+    assert lib.dfp16_f32_splits(25088, 256, 1024, 0) == 1
+    assert lib.dfp16_f32_splits(25088, 256, 1024, 2) > 1        # wgrad: 8 tiles over 392 chunks
+    assert lib.dfp16_f32_splits(0, 256, 1024, 2) == 0
+    call = lambda M=256, K=256, N=256, shift=1, ns=0, w=ws, out=FAKE: lib.dfp16_gemm_fwd_f32(
+        FAKE, FAKE, FAKE, FAKE, out, M, K, N, shift, ns, FAKE, w, None)
+    assert call(M=0) == SHAPE
+    assert call(shift=2) == RANGE
+    assert call(ns=-1) == RANGE and call(ns=5) == RANGE          # 4 chunks
+    assert call(ns=4, w=0) == WS
+    assert call(out=P(0x1008)) == ALIGN
+    assert lib.dfp16_gemm_dgrad_f32(None, FAKE, FAKE, FAKE, FAKE, 8, 8, 8, 1, 0, FAKE, 1 << 20, None) == ARG
+    assert lib.dfp16_gemm_wgrad_f32(FAKE, FAKE, FAKE, FAKE, FAKE, 8, 8, 8, 1, 0, FAKE, 10, None) == WS
+    cw = lib.dfp_convert_workspace_bytes()
+    assert lib.dfp_from_f32(FAKE, 0, 16, FAKE, FAKE, None, FAKE, cw, None) == SHAPE
+    assert lib.dfp_from_f32(FAKE, 8, 1, FAKE, FAKE, None, FAKE, cw, None) == RANGE
+    assert lib.dfp_from_f32(FAKE, 8, 17, FAKE, FAKE, None, FAKE, cw, None) == RANGE
+    assert lib.dfp_from_f32(P(0x1004), 8, 16, FAKE, FAKE, None, FAKE, cw, None) == ALIGN
+    assert lib.dfp_from_f32(FAKE, 8, 16, FAKE, FAKE, None, None, cw, None) == WS
+    assert lib.dfp_to_f32(FAKE, 8, None, FAKE, None) == ARG
+    assert lib.dfp_from_f32_blocked(FAKE, 4, 100, 0, 16, FAKE, FAKE, None, None) == RANGE
+    assert lib.dfp_from_f32_blocked(FAKE, 0, 100, 64, 16, FAKE, FAKE, None, None) == SHAPE
+    assert lib.dfp16_sgd_update(FAKE, P(0x1004), 8, ctypes.c_float(0.1), FAKE, FAKE, None, FAKE, cw, None) == ALIGN
+    assert lib.dfp16_sgd_update(FAKE, FAKE, 8, ctypes.c_float(0.1), FAKE, FAKE, None, FAKE, 0, None) == WS
