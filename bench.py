@@ -226,7 +226,8 @@ def bench_dfp16_paper(torch, nsteps):
     (shared exponent from the absolute maximum), the three contractions
     with FP32 chunk partials and the one-bit input shift, the FP32 output
     re-quantised for the next layer, and the FP32 weight update with its
-    DFP-16 copy."""
+    DFP-16 copy.  The forward on Blocked-DFP operands (exponent per 64
+    values) is timed beside it."""
     from integer_only_nn_amd import ops
     dev = torch.device("cuda:0")
     M, K, N = 25088, 256, 1024
@@ -241,6 +242,9 @@ def bench_dfp16_paper(torch, nsteps):
     Y, dX, G = f32(M, N), f32(M, K), f32(N, K)
     cws = torch.empty(ops.dfp_convert_workspace_bytes(), dtype=torch.uint8, device=dev)
     ws = torch.empty(max(ops.dfp16_f32_workspace_bytes(M, K, N, w) for w in range(3)), dtype=torch.uint8, device=dev)
+    Xb, Wb = i16(M, K), i16(N, K)
+    eXb = torch.empty(M * (K // 64), dtype=torch.int32, device=dev)
+    eWb = torch.empty(N * (K // 64), dtype=torch.int32, device=dev)
 
     def step(tm):
         m = tm.mark if tm else (lambda name: None)
@@ -259,7 +263,16 @@ def bench_dfp16_paper(torch, nsteps):
         ops.dfp16_gemm_wgrad_f32(dY16, ex[2:3], X16, ex[0:1], G, ws)
         m("sgd_update")
         ops.dfp16_sgd_update(W32, G, 1e-4, W16, ex[1:2], cws)
-    return _timed(torch, step, nsteps)
+        # the Blocked-DFP variant of the forward (one exponent per 64 values)
+        m("to_blocked")
+        ops.dfp_from_f32_blocked(X32, Xb, eXb)
+        ops.dfp_from_f32_blocked(W32, Wb, eWb)
+        m("fwd_blocked")
+        ops.dfp16_gemm_fwd_f32_blocked(Xb, eXb, Wb, eWb, Y, ws)
+    ms, per = _timed(torch, step, nsteps)
+    # the step proper: conversions, the three contractions, re-quantisation
+    # and the update (the blocked variant is timed beside it, not in it)
+    return ms - per["to_blocked"] - per["fwd_blocked"], per
 
 
 def bench_offsets(torch, nsteps):

@@ -295,6 +295,19 @@ int dfp16_gemm_wgrad_f32(const int16_t *dY, const int32_t *edY,
                          int nsplit, void *workspace, size_t workspace_bytes,
                          void *stream);
 
+/* The forward contraction on Blocked-DFP operands whose blocks are the
+ * 64-term chunks: X [M][K] with exponents eX[m * nch + c], W [N][K] with
+ * eW[n * nch + c] (device int32, nch = ceil(K / 64); dfp_from_f32_blocked
+ * with B = 64 writes this layout).  Each chunk's term is scaled on its own,
+ * t_c = fl(float(p_c) * 2^(eX[m][c] + input_shift + eW[n][c])) (one
+ * rounding), and the terms are summed in the order of dfp16_gemm_fwd_f32;
+ * the output is not scaled again.  Workspace as dfp16_gemm_fwd_f32. */
+int dfp16_gemm_fwd_f32_blocked(const int16_t *X, const int32_t *eX,
+                               const int16_t *W, const int32_t *eW, float *Y,
+                               int64_t M, int64_t K, int64_t N, int input_shift,
+                               int nsplit, void *workspace,
+                               size_t workspace_bytes, void *stream);
+
 /* Workspace bytes of dfp_from_f32 and dfp16_sgd_update (4-byte aligned). */
 size_t dfp_convert_workspace_bytes(void);
 

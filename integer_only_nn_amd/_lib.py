@@ -42,6 +42,7 @@ SIGNATURES = {
     "dfp16_gemm_fwd_f32": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _I, _P, ctypes.c_size_t, _P]),
     "dfp16_gemm_dgrad_f32": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _I, _P, ctypes.c_size_t, _P]),
     "dfp16_gemm_wgrad_f32": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _I, _P, ctypes.c_size_t, _P]),
+    "dfp16_gemm_fwd_f32_blocked": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _I, _P, ctypes.c_size_t, _P]),
     "dfp_convert_workspace_bytes": (ctypes.c_size_t, []),
     "dfp_from_f32": (_I, [_P, _I64, _I, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "dfp_to_f32": (_I, [_P, _I64, _P, _P, _P]),

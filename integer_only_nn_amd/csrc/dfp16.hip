@@ -133,9 +133,12 @@ struct DfpArgs {
     // result scaled by 2^(*ea + shift + *eb)
     int shift;
     const int32_t *ea, *eb;
+    // Blocked-DFP form: exponents bea[m * nch + c], beb[n * nch + c]
+    const int32_t *bea, *beb;
+    int nch;
 };
 
-template <int BM, int BN, int WGM, int WGN, bool EDGE, bool F32>
+template <int BM, int BN, int WGM, int WGN, bool EDGE, bool F32, bool BLK = false>
 __global__ __launch_bounds__(WGM *WGN * 64) void dfp16_kernel(DfpArgs g) {
     constexpr int NT = WGM * WGN * 64;
     constexpr int WTM = BM / WGM, WTN = BN / WGN;
@@ -196,6 +199,21 @@ __global__ __launch_bounds__(WGM *WGN * 64) void dfp16_kernel(DfpArgs g) {
             const uint32_t ra = (uint32_t(sh.x) << 8) + uint32_t(sl.x);
             rt[i].x = int(ra * 128u + (1u << 20));
         }
+        int32_t eai[FM], ebv[FN][4];
+        if (BLK) {  // this chunk's exponents of the lane's rows and columns
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                const int m = m0 + wm * WTM + i * 16 + (lane & 15);
+                eai[i] = m < g.M ? g.bea[int64_t(m) * g.nch + c] + g.shift : 0;
+            }
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int n = n0 + wn * WTN + j * 16 + (lane >> 4) * 4 + v;
+                    ebv[j][v] = n < g.N ? g.beb[int64_t(n) * g.nch + c] : 0;
+                }
+        }
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
             const int off = (wn * WTN + j * 16 + frow) * ROW + fk;
@@ -217,7 +235,11 @@ __global__ __launch_bounds__(WGM *WGN * 64) void dfp16_kernel(DfpArgs g) {
                 for (int v = 0; v < 4; ++v) {
                     const uint32_t p = (uint32_t(hh[v]) << 16) + (uint32_t(x[v]) << 8) +
                                        uint32_t(ll[v]) + uint32_t(rt[i].x) + ct[v];
-                    if (F32)
+                    if (BLK)
+                        acc[i][j][v] = __float_as_int(__fadd_rn(
+                            __int_as_float(acc[i][j][v]),
+                            __builtin_amdgcn_ldexpf(float(int32_t(p)), eai[i] + ebv[j][v])));
+                    else if (F32)
                         acc[i][j][v] = __float_as_int(__fadd_rn(__int_as_float(acc[i][j][v]), float(int32_t(p))));
                     else
                         acc[i][j][v] += rhu(int32_t(p), r);
@@ -236,7 +258,7 @@ __global__ __launch_bounds__(WGM *WGN * 64) void dfp16_kernel(DfpArgs g) {
     uint32_t amax = 0;
     const int em = lane & 15, en = (lane >> 4) * 4;
     if (F32) {
-        const int e = g.split == 1 ? *g.ea + g.shift + *g.eb : 0;
+        const int e = !BLK && g.split == 1 ? *g.ea + g.shift + *g.eb : 0;
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
             const int m = m0 + wm * WTM + i * 16 + em;
@@ -247,7 +269,7 @@ __global__ __launch_bounds__(WGM *WGN * 64) void dfp16_kernel(DfpArgs g) {
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
                     const float f = __int_as_float(acc[i][j][v]);
-                    if (m < g.M && n + v < g.N) cp[v] = g.split == 1 ? scale_f32(f, e) : f;
+                    if (m < g.M && n + v < g.N) cp[v] = !BLK && g.split == 1 ? scale_f32(f, e) : f;
                 }
             }
         }
@@ -395,6 +417,11 @@ struct Args {
     // scaling 2^(*ea + shift + *eb) (split == 1; acc then holds floats)
     int shift;
     const int32_t *ea, *eb;
+    // Blocked-DFP form: one exponent per row and 64-term chunk,
+    // bea[m * nch + c] and beb[n * nch + c]; each chunk's term is scaled on
+    // its own and the output is not scaled again
+    const int32_t *bea, *beb;
+    int nch;
 };
 
 
@@ -402,9 +429,13 @@ struct Args {
 // one output tile and one range of chunks (a K split).  The chunk loop runs
 // across unit boundaries, so the first chunk of the next unit is loaded while
 // the last chunk of the current one computes and its result is stored.
-template <bool A_KM, bool B_KM, bool F32>
+template <bool A_KM, bool B_KM, bool F32, bool BLK = false>
 __global__ __launch_bounds__(NT, 1) void dfp_kernel(Args g) {
+    static_assert(F32 || !BLK, "the blocked form accumulates in FP32");
     __shared__ __attribute__((aligned(16))) int8_t lds[2 * STAGE];
+    // Blocked form, per stage: the chunk's exponents of the tile's 128 rows
+    // of A, then of its 128 rows of B
+    __shared__ __attribute__((aligned(16))) int32_t bexp[BLK ? 2 : 1][BLK ? 256 : 4];
     __shared__ __attribute__((aligned(16))) uint32_t csum[NT / 64][64];  // per wave: 128 * sum(B') of its 64 columns
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -436,8 +467,17 @@ __global__ __launch_bounds__(NT, 1) void dfp_kernel(Args g) {
     acc[1] = v16i{};
     uint32_t amax = 0;
 
+    int32_t ereg = 0;
+    auto eload = [&](int em0, int en0, int ec) __attribute__((always_inline)) {
+        if (tid < 128) ereg = g.bea[int64_t(em0 + tid) * g.nch + ec];
+        else if (tid < 256) ereg = g.beb[int64_t(en0 + tid - 128) * g.nch + ec];
+    };
     la.load(g.a, g.lda, m0, 64 * c0, tid);
     lb.load(g.b, g.ldb, n0, 64 * c0, tid);
+    if (BLK) {
+        eload(m0, n0, c0);
+        if (tid < 256) bexp[0][tid] = ereg;
+    }
     if (F32 && g.shift) la.rhu1();
     la.store(lds, lds + PLANE, tid);
     lb.store(lds + 2 * PLANE, lds + 3 * PLANE, tid);
@@ -459,6 +499,7 @@ __global__ __launch_bounds__(NT, 1) void dfp_kernel(Args g) {
         if (more) {
             la.load(g.a, g.lda, nm0, 64 * nc, tid);
             lb.load(g.b, g.ldb, nn0, 64 * nc, tid);
+            if (BLK) eload(nm0, nn0, nc);
         }
         const int8_t *st = lds + stage * STAGE;
         v4i ah[2], al[2], bh[2][2], bl[2][2];
@@ -487,12 +528,17 @@ __global__ __launch_bounds__(NT, 1) void dfp_kernel(Args g) {
             const uint32_t cs = add_half_swap(sb);
             csum[wave][32 * j + (lane & 31)] = cs << 7;  // lanes l and l + 32 hold the same value
         }
+        const int32_t ea_lane = BLK ? bexp[BLK ? stage : 0][32 * wm + (lane & 31)] + g.shift : 0;
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            v4i cb[4];
+            v4i cb[4], eb[4];
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
+            for (int q = 0; q < 4; ++q) {
                 cb[q] = *reinterpret_cast<const v4i *>(&csum[wave][32 * j + 8 * q + 4 * (lane >> 5)]);
+                if (BLK)
+                    eb[q] = *reinterpret_cast<const v4i *>(
+                        &bexp[BLK ? stage : 0][128 + 64 * wn + 32 * j + 8 * q + 4 * (lane >> 5)]);
+            }
             v16i hh = __builtin_amdgcn_mfma_i32_32x32x32_i8(bh[j][0], ah[0], zero16, 0, 0, 0);
             hh = __builtin_amdgcn_mfma_i32_32x32x32_i8(bh[j][1], ah[1], hh, 0, 0, 0);
             v16i x = __builtin_amdgcn_mfma_i32_32x32x32_i8(bl[j][0], ah[0], zero16, 0, 0, 0);
@@ -507,7 +553,11 @@ __global__ __launch_bounds__(NT, 1) void dfp_kernel(Args g) {
                 // FP32 form: acc = fl(acc + fl(float(p)))
                 const uint32_t t = opaque((uint32_t(x[v]) << 8) + uint32_t(ll[v]));
                 const uint32_t p = (uint32_t(hh[v]) << 16) + opaque(t + rt + uint32_t(cb[v >> 2][v & 3]));
-                if (F32)
+                if (BLK)  // the chunk's term scaled on its own (v_ldexp_f32: one rounding)
+                    acc[j][v] = __float_as_int(__fadd_rn(
+                        __int_as_float(acc[j][v]),
+                        __builtin_amdgcn_ldexpf(float(int32_t(p)), ea_lane + eb[v >> 2][v & 3])));
+                else if (F32)
                     acc[j][v] = __float_as_int(__fadd_rn(__int_as_float(acc[j][v]), float(int32_t(p))));
                 else
                     acc[j][v] = int32_t(uint32_t(acc[j][v]) + uint32_t(int32_t(p) >> r) +
@@ -522,6 +572,7 @@ __global__ __launch_bounds__(NT, 1) void dfp_kernel(Args g) {
             if (F32 && g.shift) la.rhu1();
             la.store(nx, nx + PLANE, tid);
             lb.store(nx + 2 * PLANE, nx + 3 * PLANE, tid);
+            if (BLK && tid < 256) bexp[BLK ? stage ^ 1 : 0][tid] = ereg;
         }
         if (c + 1 >= c1) {
             // unit done: lane holds acc[m][n .. n+3] for m = row lane % 32 of the
@@ -534,7 +585,7 @@ __global__ __launch_bounds__(NT, 1) void dfp_kernel(Args g) {
                     const int n = n0 + 64 * wn + 32 * j + 8 * q + 4 * (lane >> 5);
                     int32_t *cp = g.acc + (int64_t(u / ntiles) * g.M + m) * g.N + n;
                     v4i v = {acc[j][4 * q], acc[j][4 * q + 1], acc[j][4 * q + 2], acc[j][4 * q + 3]};
-                    if (F32 && g.split == 1) {
+                    if (F32 && !BLK && g.split == 1) {
                         const int e = *g.ea + g.shift + *g.eb;
 #pragma unroll
                         for (int i = 0; i < 4; ++i) v[i] = __float_as_int(scale_f32(__int_as_float(v[i]), e));
@@ -563,7 +614,7 @@ __global__ __launch_bounds__(NT, 1) void dfp_kernel(Args g) {
 __global__ __launch_bounds__(256) void split_reduce_f32(const float *__restrict__ part, int split, int64_t n,
                                                         float *__restrict__ out, const int32_t *__restrict__ ea,
                                                         int shift, const int32_t *__restrict__ eb) {
-    const int e = *ea + shift + *eb;
+    const int e = ea ? *ea + shift + *eb : 0;  // no exponents: the blocked form, already scaled
     const int64_t nt = int64_t(gridDim.x) * blockDim.x;
     for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += nt) {
         float s = 0.0f;
@@ -1088,6 +1139,44 @@ int dfp16_gemm_wgrad_f32(const int16_t *dY, const int32_t *edY, const int16_t *X
         if (int rc = contract_f32(a, b, int(N), int(K), int(M), S, input_shift, edY, eX, G, w.part, st)) return rc;
     }
     return reduce_f32(w.part, S, N * K, G, edY, input_shift, eX, st);
+}
+
+int dfp16_gemm_fwd_f32_blocked(const int16_t *X, const int32_t *eX, const int16_t *W, const int32_t *eW, float *Y,
+                               int64_t M, int64_t K, int64_t N, int input_shift, int nsplit, void *workspace,
+                               size_t workspace_bytes, void *stream) {
+    clear_error();
+    int S = 1;
+    if (int rc = check_f32(X, eX, W, eW, Y, M, K, N, input_shift, nsplit, workspace, workspace_bytes,
+                           IONN_DFP16_FWD, "dfp16_gemm_fwd_f32_blocked", S))
+        return rc;
+    hipStream_t st = as_stream(stream);
+    WsF32 w;
+    ws_f32_bytes(M, K, N, IONN_DFP16_FWD, S, &w, workspace);
+    const int nch = int((K + kChunk - 1) / kChunk);
+    float *dst = S > 1 ? w.part : Y;
+    if (fast2(int(M), int(N), int(K), X, K, W, K)) {
+        d2::Args g{X, W, K, K, reinterpret_cast<int32_t *>(dst), nullptr, int(M), int(N), int(K), 0, S,
+                   input_shift, nullptr, nullptr, eX, eW, nch};
+        const int tiles = int(M / d2::BM) * int(N / d2::BN);
+        int cus = 256, dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+            cus = 256;
+        const int units = tiles * S;
+        d2::dfp_kernel<true, true, true, true><<<dim3(units < cus ? units : cus), dim3(d2::NT), 0, st>>>(g);
+    } else {
+        Src16 a{X, K, int(M), int(K), aligned(X, 16) && K % 8 == 0};
+        Src16 b{W, K, int(N), int(K), aligned(W, 16) && K % 8 == 0};
+        DfpArgs g{a, b, reinterpret_cast<int32_t *>(dst), nullptr, int(M), int(N), int(K), 0, S, false,
+                  input_shift, nullptr, nullptr, eX, eW, nch};
+        const int tiles = int((M + 63) / 64) * int((N + 63) / 64);
+        const bool even = M % 64 == 0 && N % 64 == 0 && K % kChunk == 0 && a.vec && b.vec;
+        dim3 grid(tiles, S), block(256);
+        if (even) dfp16_kernel<64, 64, 2, 2, false, true, true><<<grid, block, 0, st>>>(g);
+        else dfp16_kernel<64, 64, 2, 2, true, true, true><<<grid, block, 0, st>>>(g);
+    }
+    if (int rc = check_launch("dfp16_gemm_fwd_f32_blocked")) return rc;
+    return reduce_f32(w.part, S, M * N, Y, nullptr, 0, nullptr, st);
 }
 
 int dfp16_gavg(const int16_t *G, const int32_t *eG, const int32_t *eW, int64_t n, double *gavg_out,

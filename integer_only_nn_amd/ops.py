@@ -309,6 +309,19 @@ def dfp16_gemm_wgrad_f32(dY, edY, X, eX, G, workspace, input_shift=1, nsplit=0, 
              workspace, stream)
 
 
+def dfp16_gemm_fwd_f32_blocked(X, eX, W, eW, Y, workspace, input_shift=1, nsplit=0, stream=None):
+    """eX: int32 [M][ceil(K/64)], eW: int32 [N][ceil(K/64)] (device)."""
+    M, K = X.shape
+    N = W.shape[0]
+    nch = (K + 63) // 64
+    assert tuple(W.shape) == (N, K) and tuple(Y.shape) == (M, N)
+    check(lib().dfp16_gemm_fwd_f32_blocked(
+        _p(X, i16, name="X"), _p(eX, i32, M * nch, "eX"), _p(W, i16, name="W"), _p(eW, i32, N * nch, "eW"),
+        _p(Y, f32, name="Y"), M, K, N, int(input_shift), int(nsplit), _p(workspace, None, name="workspace"),
+        workspace.numel() * workspace.element_size() if workspace is not None else 0, _stream(stream)),
+        "dfp16_gemm_fwd_f32_blocked")
+
+
 def dfp_convert_workspace_bytes():
     return int(lib().dfp_convert_workspace_bytes())
 

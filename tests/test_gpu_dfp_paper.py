@@ -253,3 +253,56 @@ def test_paper_step_chain():
     _same_f32(host(Wd32), W2, "W32")
     np.testing.assert_array_equal(host(Wd), W16)
     assert int(host(eWd)[0]) == eW2
+
+
+# ---- Blocked-DFP forward -------------------------------------------------------
+
+@pytest.mark.parametrize("M,K,N", [(128, 256, 128), (256, 1024, 384), (100, 130, 70), (1, 64, 1), (640, 256, 256),
+                                   (128, 4096, 128)])
+def test_blocked_fwd_parity(M, K, N):
+    """Float tensors with rows of very different scales, converted to
+    Blocked-DFP (64-value blocks), then the blocked forward contraction."""
+    rng = np.random.default_rng(M + K + N)
+    X32 = (rng.standard_normal((M, K)) * 10.0 ** rng.integers(-3, 3, (M, 1))).astype(np.float32)
+    W32 = (rng.standard_normal((N, K)) * 10.0 ** rng.integers(-3, 1, (1, K))).astype(np.float32)
+    Xb, eX, _ = oracle.dfp_from_f32_blocked(X32)
+    Wb, eW, _ = oracle.dfp_from_f32_blocked(W32)
+    nch = (K + 63) // 64
+    default = ops.dfp16_f32_splits(M, K, N, FWD)
+    for shift, nsplit in ((1, 0), (0, 1), (1, min(3, nch))):
+        S = nsplit or default
+        say("blocked", M, K, N, shift, S)
+        want, _ = oracle.dfp16_fwd_f32_blocked(Xb, eX, Wb, eW, S=S, input_shift=shift)
+        Y = torch.full((M, N), float("nan"), dtype=torch.float32, device=dev())
+        ws = torch.empty(ops.dfp16_f32_workspace_bytes(M, K, N, FWD, nsplit), dtype=torch.uint8, device=dev())
+        ops.dfp16_gemm_fwd_f32_blocked(to_dev(Xb), to_dev(eX), to_dev(Wb), to_dev(eW), Y, ws,
+                                       input_shift=shift, nsplit=nsplit)
+        _same_f32(host(Y), want, f"S={S} shift={shift}")
+
+
+def test_blocked_fwd_from_device_conversion_and_subnormal_terms():
+    """The blocked conversion on the device feeding the blocked forward;
+    block exponents low enough that chunk terms land in the subnormal range
+    (where v_ldexp_f32 rounds them once, as the oracle does)."""
+    M, K, N = 256, 512, 128
+    rng = np.random.default_rng(77)
+    X32 = (rng.standard_normal((M, K)) * 1e-20).astype(np.float32)
+    W32 = (rng.standard_normal((N, K)) * 1e-19).astype(np.float32)
+    X32[: M // 2, 64:128] *= 1e15   # half the rows keep only tiny blocks
+    Xd = torch.empty((M, K), dtype=torch.int16, device=dev())
+    Wd = torch.empty((N, K), dtype=torch.int16, device=dev())
+    eXd = torch.empty(M * (K // 64), dtype=torch.int32, device=dev())
+    eWd = torch.empty(N * (K // 64), dtype=torch.int32, device=dev())
+    ops.dfp_from_f32_blocked(to_dev(X32), Xd, eXd)
+    ops.dfp_from_f32_blocked(to_dev(W32), Wd, eWd)
+    Xb, eX, _ = oracle.dfp_from_f32_blocked(X32)
+    Wb, eW, _ = oracle.dfp_from_f32_blocked(W32)
+    np.testing.assert_array_equal(host(Xd), Xb)
+    np.testing.assert_array_equal(host(eXd).reshape(eX.shape), eX)
+    assert (eX.astype(np.int64)[:, :, None] + eW.astype(np.int64).T[None] + 1).min() < -150   # subnormal terms occur
+    want, _ = oracle.dfp16_fwd_f32_blocked(Xb, eX, Wb, eW, S=ops.dfp16_f32_splits(M, K, N, FWD))
+    Y = torch.empty((M, N), dtype=torch.float32, device=dev())
+    ws = torch.empty(ops.dfp16_f32_workspace_bytes(M, K, N, FWD), dtype=torch.uint8, device=dev())
+    ops.dfp16_gemm_fwd_f32_blocked(Xd, eXd, Wd, eWd, Y, ws)
+    _same_f32(host(Y), want, "blocked subnormal")
+    assert (np.abs(want) < 2.0 ** -126).any() and (want != 0).any()
