@@ -198,6 +198,204 @@ __global__ __launch_bounds__(256) void conv_direct_wgrad(const int8_t *__restric
     }
 }
 
+// ---- small samples: whole samples staged in LDS ----
+//
+// When one sample's input and output (and the filter bank) are a few KB, as
+// in the page's example network (64 x 2 input, 16 x 2 filters), a workgroup
+// copies SPB whole samples from HBM into LDS with wide loads and computes
+// from there: every input byte is read from HBM once per workgroup instead
+// of once per output that touches it, and the byte gathers hit LDS.
+
+constexpr int kSmallLds = 32768;                 // LDS bytes per workgroup
+constexpr int kSmallMaxBytes = 4096;             // per-sample input and output bytes
+constexpr int kSmallMaxW = 16384;                // filter bank bytes
+constexpr int kSmallMaxG = 1024;                 // weights held by one workgroup's wgrad
+
+struct SmallGeo {
+    int H, W, Cin, Cout, KH, KW, P, Ho, Wo;
+    int in_b, out_b, w_b;                        // bytes per sample in / out, filter bank
+    int spb;                                     // samples per group
+};
+
+__device__ __forceinline__ void copy_to_lds(int8_t *dst, const int8_t *src, int nbytes) {
+    if (((reinterpret_cast<uintptr_t>(src) | uintptr_t(nbytes)) & 15) == 0) {
+        for (int i = threadIdx.x; i < nbytes / 16; i += blockDim.x)
+            reinterpret_cast<uint4 *>(dst)[i] = reinterpret_cast<const uint4 *>(src)[i];
+    } else {
+        for (int i = threadIdx.x; i < nbytes; i += blockDim.x) dst[i] = src[i];
+    }
+}
+
+__device__ __forceinline__ int round16(int x) { return (x + 15) & ~15; }
+
+// Y for groups of g.spb samples, one output element per thread and step.
+__global__ __launch_bounds__(256) void conv_small_fwd(const int8_t *__restrict__ X, const int8_t *__restrict__ Wt,
+                                                      int32_t *__restrict__ Y, int64_t N, SmallGeo g,
+                                                      uint32_t *__restrict__ absmax) {
+    __shared__ __attribute__((aligned(16))) int8_t lds[kSmallLds];
+    int8_t *ws = lds, *xs = lds + round16(g.w_b);
+    copy_to_lds(ws, Wt, g.w_b);
+    uint32_t amax = 0;
+    for (int64_t n0 = int64_t(blockIdx.x) * g.spb; n0 < N; n0 += int64_t(gridDim.x) * g.spb) {
+        const int ns = int(N - n0 < g.spb ? N - n0 : g.spb);
+        __syncthreads();  // the previous group's reads are done
+        copy_to_lds(xs, X + n0 * g.in_b, ns * g.in_b);
+        __syncthreads();
+        const int nout = ns * g.out_b;
+        for (int o = threadIdx.x; o < nout; o += blockDim.x) {
+            const int sm = o / g.out_b, r = o - sm * g.out_b;
+            const int co = r % g.Cout, t = r / g.Cout, wo = t % g.Wo, ho = t / g.Wo;
+            const int8_t *xsm = xs + sm * g.in_b;
+            uint32_t acc = 0;
+            for (int kh = 0; kh < g.KH; ++kh) {
+                const int y = ho + kh - g.P;
+                if (y < 0 || y >= g.H) continue;
+                for (int kw = 0; kw < g.KW; ++kw) {
+                    const int x = wo + kw - g.P;
+                    if (x < 0 || x >= g.W) continue;
+                    const int8_t *xp = xsm + (y * g.W + x) * g.Cin;
+                    const int8_t *wp = ws + ((co * g.KH + kh) * g.KW + kw) * g.Cin;
+                    for (int ci = 0; ci < g.Cin; ++ci) acc += uint32_t(int32_t(xp[ci]) * int32_t(wp[ci]));
+                }
+            }
+            Y[n0 * g.out_b + o] = int32_t(acc);
+            amax = max(amax, abs_u32(int32_t(acc)));
+        }
+    }
+    if (absmax) {
+        amax = wave_max_u32(amax);
+        if ((threadIdx.x & 63) == 0) publish_max_u32(absmax, amax);
+    }
+}
+
+// dX for groups of samples: the output error staged, one input element per
+// thread and step.
+__global__ __launch_bounds__(256) void conv_small_dgrad(const int8_t *__restrict__ dY, const int8_t *__restrict__ Wt,
+                                                        int32_t *__restrict__ dX, int64_t N, SmallGeo g,
+                                                        uint32_t *__restrict__ absmax) {
+    __shared__ __attribute__((aligned(16))) int8_t lds[kSmallLds];
+    int8_t *ws = lds, *ds = lds + round16(g.w_b);
+    copy_to_lds(ws, Wt, g.w_b);
+    uint32_t amax = 0;
+    const int wstride = g.KH * g.KW * g.Cin;
+    for (int64_t n0 = int64_t(blockIdx.x) * g.spb; n0 < N; n0 += int64_t(gridDim.x) * g.spb) {
+        const int ns = int(N - n0 < g.spb ? N - n0 : g.spb);
+        __syncthreads();
+        copy_to_lds(ds, dY + n0 * g.out_b, ns * g.out_b);
+        __syncthreads();
+        const int nin = ns * g.in_b;
+        for (int o = threadIdx.x; o < nin; o += blockDim.x) {
+            const int sm = o / g.in_b, r = o - sm * g.in_b;
+            const int ci = r % g.Cin, t = r / g.Cin, w = t % g.W, h = t / g.W;
+            const int8_t *dsm = ds + sm * g.out_b;
+            uint32_t acc = 0;
+            for (int kh = 0; kh < g.KH; ++kh) {
+                const int y = h - kh + g.P;
+                if (y < 0 || y >= g.Ho) continue;
+                for (int kw = 0; kw < g.KW; ++kw) {
+                    const int x = w - kw + g.P;
+                    if (x < 0 || x >= g.Wo) continue;
+                    const int8_t *dp = dsm + (y * g.Wo + x) * g.Cout;
+                    const int8_t *wp = ws + (kh * g.KW + kw) * g.Cin + ci;
+                    for (int co = 0; co < g.Cout; ++co) acc += uint32_t(int32_t(dp[co]) * int32_t(wp[co * wstride]));
+                }
+            }
+            dX[n0 * g.in_b + o] = int32_t(acc);
+            amax = max(amax, abs_u32(int32_t(acc)));
+        }
+    }
+    if (absmax) {
+        amax = wave_max_u32(amax);
+        if ((threadIdx.x & 63) == 0) publish_max_u32(absmax, amax);
+    }
+}
+
+// G (zeroed) += this workgroup's samples.  Thread t holds weights
+// w = t % NW + 256 j... of a chunk layout like conv_direct_wgrad: weight
+// chunk c covers [256 c, 256 c + 256), thread t takes weight t % NW of it
+// and every S-th sample of the group from t / NW on; sums stay in
+// registers across groups, meet in LDS at the end, one atomic per weight.
+__global__ __launch_bounds__(256) void conv_small_wgrad(const int8_t *__restrict__ dY, const int8_t *__restrict__ X,
+                                                        int32_t *__restrict__ G, int64_t N, SmallGeo g, int n_g) {
+    __shared__ __attribute__((aligned(16))) int8_t lds[kSmallLds];
+    __shared__ uint32_t red[256];
+    int8_t *xs = lds, *ds = lds + round16(g.spb * g.in_b);
+    const int t = threadIdx.x;
+    constexpr int MAXC = kSmallMaxG / 256;
+    uint32_t acc[MAXC] = {};
+    for (int64_t n0 = int64_t(blockIdx.x) * g.spb; n0 < N; n0 += int64_t(gridDim.x) * g.spb) {
+        const int ns = int(N - n0 < g.spb ? N - n0 : g.spb);
+        __syncthreads();
+        copy_to_lds(xs, X + n0 * g.in_b, ns * g.in_b);
+        copy_to_lds(ds, dY + n0 * g.out_b, ns * g.out_b);
+        __syncthreads();
+#pragma unroll
+        for (int c = 0; c < MAXC; ++c) {
+            const int wc = 256 * c;
+            if (wc >= n_g) break;
+            const int NW = n_g - wc < 256 ? n_g - wc : 256, S = 256 / NW;
+            const int wl = t % NW, sub = t / NW;
+            if (sub >= S) continue;
+            const int i = wc + wl;
+            const int ci = i % g.Cin, q = i / g.Cin, kw = q % g.KW, q2 = q / g.KW, kh = q2 % g.KH, co = q2 / g.KH;
+            uint32_t a = 0;
+            for (int sm = sub; sm < ns; sm += S) {
+                const int8_t *dsm = ds + sm * g.out_b + co, *xsm = xs + sm * g.in_b + ci;
+                for (int ho = 0; ho < g.Ho; ++ho) {
+                    const int y = ho + kh - g.P;
+                    if (y < 0 || y >= g.H) continue;
+                    for (int wo = 0; wo < g.Wo; ++wo) {
+                        const int x = wo + kw - g.P;
+                        if (x >= 0 && x < g.W)
+                            a += uint32_t(int32_t(dsm[(ho * g.Wo + wo) * g.Cout]) * int32_t(xsm[(y * g.W + x) * g.Cin]));
+                    }
+                }
+            }
+            acc[c] += a;
+        }
+    }
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c) {
+        const int wc = 256 * c;
+        if (wc >= n_g) break;
+        const int NW = n_g - wc < 256 ? n_g - wc : 256, S = 256 / NW;
+        __syncthreads();
+        red[t] = t / NW < S ? acc[c] : 0u;
+        __syncthreads();
+        if (t < NW) {
+            uint32_t v = 0;
+            for (int k = 0; k < S; ++k) v += red[t + k * NW];
+            if (v) atomicAdd(G + wc + t, int32_t(v));
+        }
+    }
+}
+
+// The small-sample geometry of a descriptor, or spb = 0 when it does not fit.
+SmallGeo small_geo(const ionn_conv_desc *d, int which) {
+    SmallGeo g{};
+    const int64_t Ho = d->H + 2 * int64_t(d->pad) - d->KH + 1, Wo = d->W + 2 * int64_t(d->pad) - d->KW + 1;
+    const int64_t in_b = d->H * d->W * d->Cin, out_b = Ho * Wo * d->Cout;
+    const int64_t w_b = d->Cout * d->KH * d->KW * d->Cin;
+    if (Ho <= 0 || Wo <= 0 || in_b < 1 || out_b < 1 || in_b > kSmallMaxBytes || out_b > kSmallMaxBytes ||
+        w_b > kSmallMaxW)
+        return g;
+    int64_t per = which == 0 ? in_b : which == 1 ? out_b : in_b + out_b + 32;   // staged bytes per sample
+    const int64_t room = which == 2 ? kSmallLds - 16 : kSmallLds - ((w_b + 15) & ~15);
+    if (which == 2 && w_b > kSmallMaxG) return g;
+    int64_t spb = room / per;
+    if (spb > 64) spb = 64;
+    if (spb < 1) return g;
+    g = SmallGeo{int(d->H), int(d->W), int(d->Cin), int(d->Cout), d->KH, d->KW, d->pad, int(Ho), int(Wo),
+                 int(in_b), int(out_b), int(w_b), int(spb)};
+    return g;
+}
+
+unsigned small_blocks(int64_t N, int spb, int64_t cap) {
+    int64_t b = (N + spb - 1) / spb;
+    if (b > cap) b = cap;
+    return unsigned(b < 1 ? 1 : b);
+}
+
 unsigned direct_blocks(int64_t n) {
     int64_t b = (n + 255) / 256;
     return unsigned(b < 1 ? 1 : (b > 4096 ? 4096 : b));
@@ -253,6 +451,12 @@ int int_conv_fwd(const int8_t *X, const int8_t *Wt, int32_t *Y, const ionn_conv_
         IONN_REQUIRE(Y && (Cin == 0 || (X && Wt)), IONN_ERR_ARG, "int_conv_fwd: NULL tensor");
         IONN_REQUIRE(aligned(Y, 4) && aligned(absmax_Y, 4), IONN_ERR_ALIGN,
                      "int_conv_fwd: Y/absmax must be 4-byte aligned");
+        const SmallGeo sg = small_geo(desc, 0);
+        if (sg.spb > 0 && Cin > 0) {
+            conv_small_fwd<<<dim3(small_blocks(desc->N, sg.spb, 2048)), dim3(256), 0, as_stream(stream)>>>(
+                X, Wt, Y, desc->N, sg, absmax_Y);
+            return check_launch("int_conv_fwd");
+        }
         conv_direct_fwd<<<dim3(direct_blocks(n_out)), dim3(256), 0, as_stream(stream)>>>(
             X, Wt, Y, int(desc->H), int(desc->W), Cin, Cout, desc->KH, desc->KW, desc->pad, int(Ho), int(Wo),
             n_out, absmax_Y);
@@ -298,6 +502,12 @@ int int_conv_dgrad(const int8_t *dY, const int8_t *Wt, int32_t *dX, const ionn_c
         hipStream_t st = as_stream(stream);
         if (!any_out) {
             zero_i32_kernel<<<dim3(direct_blocks(n_in)), dim3(256), 0, st>>>(dX, n_in);
+            return check_launch("int_conv_dgrad");
+        }
+        const SmallGeo sg = small_geo(desc, 1);
+        if (sg.spb > 0) {
+            conv_small_dgrad<<<dim3(small_blocks(desc->N, sg.spb, 2048)), dim3(256), 0, st>>>(dY, Wt, dX, desc->N,
+                                                                                              sg, absmax_dX);
             return check_launch("int_conv_dgrad");
         }
         conv_direct_dgrad<<<dim3(direct_blocks(n_in)), dim3(256), 0, st>>>(
@@ -351,7 +561,12 @@ int int_conv_wgrad(const int8_t *dY, const int8_t *X, int32_t *G, const ionn_con
         hipStream_t st = as_stream(stream);
         zero_i32_kernel<<<dim3(direct_blocks(n_g)), dim3(256), 0, st>>>(G, n_g);
         if (int rc = check_launch("int_conv_wgrad")) return rc;
-        if (rows > 0) {
+        const SmallGeo sg = small_geo(desc, 2);
+        if (rows > 0 && sg.spb > 0) {
+            conv_small_wgrad<<<dim3(small_blocks(desc->N, sg.spb, 1024)), dim3(256), 0, st>>>(dY, X, G, desc->N, sg,
+                                                                                              int(n_g));
+            if (int rc = check_launch("int_conv_wgrad")) return rc;
+        } else if (rows > 0) {
             // up to 1024 workgroups of at least 16 output rows each
             int64_t nb = (rows + 15) / 16;
             if (nb > 1024) nb = 1024;

@@ -1,7 +1,8 @@
 """GPU parity: stride-1 conv contractions of other geometries (any KH x KW,
-zero padding, any channel counts) on the direct kernels, including the 16 x 2
-"valid" filter bank of the TI page's arc-fault example network, against the
-oracle, bit-exact with every max-abs."""
+zero padding, any channel counts) on the direct kernels and on the kernels
+that stage whole small samples in LDS, including the 16 x 2 "valid" filter
+bank of the TI page's arc-fault example network, against the oracle,
+bit-exact with every max-abs."""
 import numpy as np
 import pytest
 import torch
@@ -16,7 +17,11 @@ GEOMS = [(8, 64, 2, 1, 3, 16, 2, 0),     # the page's example: 64x2x1 -> 49x1x3
          (2, 5, 4, 3, 2, 1, 3, 1), (1, 9, 6, 2, 5, 4, 2, 1), (3, 7, 7, 4, 3, 5, 1, 0),
          (2, 10, 10, 3, 8, 3, 3, 1),     # 3x3 / pad 1 with 3 input channels
          (4, 8, 8, 16, 16, 1, 1, 0),     # 1x1
-         (16, 28, 28, 8, 16, 5, 5, 2),
+         (16, 28, 28, 8, 16, 5, 5, 2),   # 6 KB per sample: the direct kernels
+         (2, 40, 40, 4, 8, 3, 3, 1),     # the direct kernels again
+         (1000, 64, 2, 1, 3, 16, 2, 0),  # the example network's layer, a ragged last sample group
+         (6, 10, 10, 8, 12, 3, 3, 1),    # 864 weights: four weight chunks in the staged wgrad
+         (5, 12, 12, 8, 16, 3, 3, 0),    # 1152 weights: staged fwd/dgrad, direct wgrad
          (1, 1, 1, 1, 1, 1, 1, 0)]
 
 
