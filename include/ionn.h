@@ -181,6 +181,29 @@ int int_conv_dgrad(const int8_t *dY, const int8_t *Wt, int32_t *dX,
                    const ionn_conv_desc *desc, uint32_t *absmax_dX,
                    void *stream);
 
+/* The forward contraction with the NITI requantisation of its result fused
+ * in ("Integer On-Device Training: Overview", section 3, steps 1-3 and the
+ * ReLU of the Conv2D layer, section 7): Y8 = sat8(rhu(Y, s)), then
+ * max(Y8, 0) if relu, with s = max(0, bitlen(max|Y|) - target_bits) and Y
+ * the int32 sum of int_conv_fwd.  Y is never stored: the contraction runs
+ * twice, first for max|Y| only, then for the int8 output.  Y8: int8
+ * [N][H][W][Cout] (written).  absmax_Y (device, 4-byte aligned, required):
+ * must hold 0 on entry (ionn_fill_u32); receives max|Y|.  shift_out
+ * (nullable, device): receives s.  Only 3x3 / stride 1 / pad 1 with 64 input
+ * and 64 output channels and a width whose halo fits (as the int32 fast
+ * path); other geometries return IONN_ERR_UNSUPPORTED and take int_conv_fwd and
+ * niti_quantize.  X and Wt 16-byte aligned, Y8 4-byte aligned. */
+int int_conv_fwd_requant(const int8_t *X, const int8_t *Wt, int8_t *Y8,
+                         const ionn_conv_desc *desc, int target_bits, int relu,
+                         uint32_t *absmax_Y, int32_t *shift_out, void *stream);
+
+/* The same for delta propagation (section 3, the propagated-delta note:
+ * target_bits = 7): dX8 = sat8(rhu(dX, s)) with dX the int32 sum of
+ * int_conv_dgrad, computed twice and never stored. */
+int int_conv_dgrad_requant(const int8_t *dY, const int8_t *Wt, int8_t *dX8,
+                           const ionn_conv_desc *desc, int target_bits,
+                           uint32_t *absmax_dX, int32_t *shift_out, void *stream);
+
 /* Device workspace (bytes) that lets int_conv_wgrad take its fast path for
  * this geometry (64 input and 64 output channels, W up to about 100): one
  * partial G per compute unit plus one per 16 of them.  0 when the geometry

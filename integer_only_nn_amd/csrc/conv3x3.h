@@ -98,11 +98,21 @@ __device__ __forceinline__ void wait_vm() {
     __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
 }
 
-template <bool DGRAD>
+// What the epilogue does with the int32 accumulators.
+enum Mode : int {
+    STORE32 = 0,  // store them (int32 out) and max-combine max|acc| into *absmax
+    MAXONLY = 1,  // only max-combine max|acc| into *absmax (no output)
+    REQUANT = 2,  // store int8 sat8(rhu(acc, s)) (ReLU optional), s from the
+                  // finished *absmax and target_bits; block 0 writes s
+};
+
+template <bool DGRAD, int MODE = STORE32>
 __global__ __launch_bounds__(NTF, 1) void conv3x3_kernel(const int8_t *__restrict__ in,
                                                          const int8_t *__restrict__ wgt,
-                                                         int32_t *__restrict__ out, int N, int H,
-                                                         int W, uint32_t *__restrict__ absmax) {
+                                                         void *__restrict__ out_any, int N, int H,
+                                                         int W, uint32_t *__restrict__ absmax,
+                                                         int target_bits = 0, int relu = 0,
+                                                         int32_t *__restrict__ shift_out = nullptr) {
     __shared__ __attribute__((aligned(1024))) int8_t halo[NB][HBUF];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -192,9 +202,17 @@ __global__ __launch_bounds__(NTF, 1) void conv3x3_kernel(const int8_t *__restric
         }
     };
 
-    // Output through a buffer resource as well (see the epilogue).
+    // Output through a buffer resource as well (see the epilogue): int32 or,
+    // requantised, int8 elements.
+    constexpr int OB = MODE == REQUANT ? 1 : 4;
     const __amdgpu_buffer_rsrc_t orsrc =
-        __builtin_amdgcn_make_buffer_rsrc(out, 0, int(int64_t(N) * HW * C * 4), 0x00020000);
+        __builtin_amdgcn_make_buffer_rsrc(out_any, 0, int(int64_t(N) * HW * C * OB), 0x00020000);
+    // requantisation shift from the finished max |acc| (NITI steps 2-3)
+    int rs = 0;
+    if (MODE == REQUANT) {
+        rs = __builtin_amdgcn_readfirstlane(niti_shift(*absmax, target_bits));
+        if (blockIdx.x == 0 && tid == 0 && shift_out) *shift_out = rs;
+    }
 
     int t = blockIdx.x;
     fetch(t, 0);
@@ -204,8 +222,8 @@ __global__ __launch_bounds__(NTF, 1) void conv3x3_kernel(const int8_t *__restric
     int b = 0;
     for (int k = 0; t < ntiles; t += G, ++k) {
         // This tile's loads are done when at most the next tile's (NI) and the
-        // previous tile's stores (8) are still outstanding.
-        if (k == 0) wait_vm<NI>(); else wait_vm<NI + 8>();
+        // previous tile's stores (8, none without output) are still outstanding.
+        if (k == 0 || MODE == MAXONLY) wait_vm<NI>(); else wait_vm<NI + 8>();
         __syncthreads();
         fetch(t + 2 * G, b == 0 ? 2 : b - 1);
 
@@ -245,15 +263,32 @@ __global__ __launch_bounds__(NTF, 1) void conv3x3_kernel(const int8_t *__restric
         // co = cb*32 + 8 q + 4 (lane / 32); a lane past the valid pixels
         // stores to an offset beyond the end (dropped), so every wavefront
         // issues exactly eight stores per tile
-        const uint32_t obase = pl < valid ? uint32_t(((n * HW + p0 + pl) * C + 4 * (lane >> 5)) * 4) : OOB;
+        const uint32_t obase = pl < valid ? uint32_t(((n * HW + p0 + pl) * C + 4 * (lane >> 5)) * OB) : OOB;
+        if (MODE == STORE32) {
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb)
+            for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const v4i v = {acc[cb][4 * q], acc[cb][4 * q + 1], acc[cb][4 * q + 2], acc[cb][4 * q + 3]};
-                __builtin_amdgcn_raw_buffer_store_b128(v, orsrc, int(obase + uint32_t((cb * 32 + 8 * q) * 4)), 0, 0);
-            }
-        if (pl < valid) {
+                for (int q = 0; q < 4; ++q) {
+                    const v4i v = {acc[cb][4 * q], acc[cb][4 * q + 1], acc[cb][4 * q + 2], acc[cb][4 * q + 3]};
+                    __builtin_amdgcn_raw_buffer_store_b128(v, orsrc, int(obase + uint32_t((cb * 32 + 8 * q) * 4)), 0, 0);
+                }
+        } else if (MODE == REQUANT) {
+            // out = sat8(rhu(acc, s)), then max(out, 0) with ReLU; four
+            // channels per dword
+            auto rq = [&](int32_t v) __attribute__((always_inline)) {
+                const int32_t q8 = sat8(rhu(v, rs));
+                return relu ? max(q8, 0) : q8;
+            };
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint32_t w = pack4_u8(rq(acc[cb][4 * q]), rq(acc[cb][4 * q + 1]), rq(acc[cb][4 * q + 2]),
+                                                rq(acc[cb][4 * q + 3]));
+                    __builtin_amdgcn_raw_buffer_store_b32(w, orsrc, int(obase + uint32_t(cb * 32 + 8 * q)), 0, 0);
+                }
+        }
+        if (MODE != REQUANT && pl < valid) {
 #pragma unroll
             for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
@@ -266,7 +301,7 @@ __global__ __launch_bounds__(NTF, 1) void conv3x3_kernel(const int8_t *__restric
     }
     wait_vm<0>();  // the zero-fill loads past the last tile land before the workgroup ends
 
-    if (absmax) {
+    if (MODE != REQUANT && absmax) {
         uint32_t amax = vmax >= vmin ? max(abs_u32(vmax), abs_u32(vmin)) : 0u;
         amax = wave_max_u32(amax);
         if (lane == 0) publish_max_u32(absmax, amax);

@@ -438,6 +438,40 @@ unsigned c3_grid(const ionn_conv_desc *d) {
 using namespace ionn;
 using namespace ionn::gemm;
 
+// Two passes of the 64-channel halo-tiled kernel with the NITI requantisation
+// fused: max |acc| only, then the contraction again with int8 output.  The
+// int32 accumulator is never stored.
+template <bool DGRAD>
+int conv_requant(const int8_t *in, const int8_t *Wt, int8_t *out8, const ionn_conv_desc *desc,
+                 int target_bits, int relu, uint32_t *absmax, int32_t *shift_out, void *stream,
+                 const char *name) {
+    clear_error();
+    if (int rc = check_desc(desc, name)) return rc;
+    IONN_REQUIRE(geom33(desc) && desc->Cin == 64 && desc->Cout == 64 && c3::fits_fd(desc->W, desc->N * desc->H * desc->W * 64),
+                 IONN_ERR_UNSUPPORTED,
+                 "%s: fused path needs 3x3 / stride 1 / pad 1, 64 -> 64 channels and a width whose halo fits "
+                 "(use the int32 contraction and niti_quantize otherwise)", name);
+    IONN_REQUIRE(target_bits >= 1 && target_bits <= 31, IONN_ERR_RANGE, "%s: target_bits = %d outside [1, 31]",
+                 name, target_bits);
+    IONN_REQUIRE(relu == 0 || relu == 1, IONN_ERR_ARG, "%s: relu = %d", name, relu);
+    IONN_REQUIRE(absmax != nullptr, IONN_ERR_ARG, "%s: absmax is NULL", name);
+    const int64_t npix = desc->N * desc->H * desc->W;
+    IONN_REQUIRE(npix == 0 || (in && Wt && out8), IONN_ERR_ARG, "%s: NULL tensor", name);
+    IONN_REQUIRE(aligned(in, 16) && aligned(Wt, 16) && aligned(out8, 4) && aligned(absmax, 4) &&
+                     aligned(shift_out, 4),
+                 IONN_ERR_ALIGN, "%s: in/W must be 16-byte, out/absmax/shift 4-byte aligned", name);
+    hipStream_t st = as_stream(stream);
+    if (npix == 0)  // max |acc| = 0, so s = 0
+        return shift_out ? ionn_fill_u32(reinterpret_cast<uint32_t *>(shift_out), 1, 0, stream) : IONN_OK;
+    const dim3 grid(c3_grid(desc)), block(c3::NTF);
+    const int N = int(desc->N), H = int(desc->H), W = int(desc->W);
+    c3::conv3x3_kernel<DGRAD, c3::MAXONLY><<<grid, block, 0, st>>>(in, Wt, nullptr, N, H, W, absmax);
+    if (int rc = check_launch(name)) return rc;
+    c3::conv3x3_kernel<DGRAD, c3::REQUANT><<<grid, block, 0, st>>>(in, Wt, out8, N, H, W, absmax, target_bits,
+                                                                   relu, shift_out);
+    return check_launch(name);
+}
+
 extern "C" {
 
 int int_conv_fwd(const int8_t *X, const int8_t *Wt, int32_t *Y, const ionn_conv_desc *desc,
@@ -538,6 +572,18 @@ int int_conv_dgrad(const int8_t *dY, const int8_t *Wt, int32_t *dX, const ionn_c
     else
         launch<256, 64, 64, 4, 1, true>(sa, sb, ep, M, N, K, 1, st);
     return check_launch("int_conv_dgrad");
+}
+
+int int_conv_fwd_requant(const int8_t *X, const int8_t *Wt, int8_t *Y8, const ionn_conv_desc *desc,
+                         int target_bits, int relu, uint32_t *absmax_Y, int32_t *shift_out, void *stream) {
+    return conv_requant<false>(X, Wt, Y8, desc, target_bits, relu, absmax_Y, shift_out, stream,
+                               "int_conv_fwd_requant");
+}
+
+int int_conv_dgrad_requant(const int8_t *dY, const int8_t *Wt, int8_t *dX8, const ionn_conv_desc *desc,
+                           int target_bits, uint32_t *absmax_dX, int32_t *shift_out, void *stream) {
+    return conv_requant<true>(dY, Wt, dX8, desc, target_bits, 0, absmax_dX, shift_out, stream,
+                              "int_conv_dgrad_requant");
 }
 
 size_t int_conv_wgrad_workspace_bytes(const ionn_conv_desc *desc) {

@@ -185,6 +185,24 @@ def conv_step(X, Wt, dY, buf: ConvStepBuffers, tb_a=TB_DELTA, tb_d=TB_DELTA, tb_
                              stream=stream)
 
 
+def conv_step_fused(X, Wt, dY, buf: ConvStepBuffers, tb_a=TB_DELTA, tb_d=TB_DELTA, tb_w=TB_WEIGHT,
+                    mu=MU_WEIGHT, stream=None):
+    """The same step with the requantisation fused into the contractions
+    (64 -> 64 channels): y8, dx8, G, the update and every shift as in
+    conv_step; buf.Y and buf.dX are not written (the int32 sums are never
+    stored)."""
+    N, H, W_, Cin = X.shape
+    Cout = Wt.shape[0]
+    d = ops.conv_desc(N, H, W_, Cin, Cout)
+    s = buf.scal
+    ops.ionn_fill_u32(s[0:3], 0, stream=stream)
+    ops.int_conv_fwd_requant(X, Wt, buf.y8, d, tb_a, False, s[0:1], shift_out=s[3:4], stream=stream)
+    ops.int_conv_dgrad_requant(dY, Wt, buf.dx8, d, tb_d, s[1:2], shift_out=s[4:5], stream=stream)
+    ops.int_conv_wgrad(dY, X, buf.G, d, absmax_G=s[2:3], workspace=buf.ws, stream=stream)
+    ops.niti_quantize_update(buf.G, s[2:3], tb_w, mu, Wt, shifts_out=s[5:7], gq_out=buf.gq,
+                             stream=stream)
+
+
 # ---------------------------------------------------------------------------
 # DFP-16 layer.
 # ---------------------------------------------------------------------------

@@ -72,3 +72,108 @@ def test_conv_workload_full():
     assert (sc[2], sc[5], sc[6]) == (oracle.absmax(Go), s, ws)
     np.testing.assert_array_equal(host(buf.gq), gqo)
     np.testing.assert_array_equal(host(Wt), Wo)
+
+
+# ---------------------------------------------------------------------------
+# The requantisation fused into the 64 -> 64 contractions (two passes, the
+# int32 sums never stored): y8 / dx8 and every shift against the oracle.
+# ---------------------------------------------------------------------------
+
+FAST64 = [(2, 16, 16), (4, 32, 32), (3, 5, 3), (2, 7, 2), (5, 13, 11), (1, 100, 100), (2, 1, 57),
+          (40, 20, 20)]
+
+
+@pytest.mark.parametrize("N,H,W", FAST64)
+def test_conv_step_fused_vs_oracle(N, H, W):
+    say("conv fused", N, H, W)
+    d = ionn_synth.conv3x3(N=N, H=H, W=W, Cin=64, Cout=64, seed=N * H + 64)
+    want = osteps.conv_step(d["X"], d["W"], d["dY"])
+    Wt = to_dev(d["W"])
+    buf = steps.ConvStepBuffers.make(N, H, W, 64, 64, dev(), with_gq=True)
+    steps.conv_step_fused(to_dev(d["X"]), Wt, to_dev(d["dY"]), buf)
+    for k, t in (("y8", buf.y8), ("dx8", buf.dx8), ("G", buf.G), ("Gq", buf.gq)):
+        np.testing.assert_array_equal(host(t), want[k], err_msg=k)
+    np.testing.assert_array_equal(host(Wt), want["W_new"])
+    sc = host(buf.scal).astype(np.int64) & 0xFFFFFFFF
+    assert (sc[0], sc[1]) == (oracle.absmax(want["Y32"]), oracle.absmax(want["dX32"]))
+    assert sc[3:7].tolist() == [want["s_y"], want["s_dx"], want["s"], want["ws"]]
+
+
+@pytest.mark.parametrize("relu", [0, 1])
+@pytest.mark.parametrize("tb", [1, 7, 12, 31])
+def test_conv_fwd_requant_target_bits_relu(tb, relu):
+    """Any target_bits (s = 0 at 31: the sums are returned clamped) and the
+    Conv2D layer's ReLU, on a ragged 9x7 image pair."""
+    N, H, W = 2, 9, 7
+    d = ionn_synth.conv3x3(N=N, H=H, W=W, Cin=64, Cout=64, seed=tb + 10 * relu)
+    Y = oracle.conv_fwd(d["X"], d["W"])
+    y8, s = oracle.niti_requant(Y, tb, bool(relu))
+    out = torch.empty(N, H, W, 64, dtype=torch.int8, device=dev())
+    scal = torch.zeros(2, dtype=torch.int32, device=dev())
+    ops.int_conv_fwd_requant(to_dev(d["X"]), to_dev(d["W"]), out, ops.conv_desc(N, H, W, 64, 64), tb, relu,
+                             scal[0:1], shift_out=scal[1:2])
+    np.testing.assert_array_equal(host(out), y8)
+    assert host(scal).tolist() == [oracle.absmax(Y), s]
+    # delta propagation through the same path
+    dX = oracle.conv_dgrad(d["dY"], d["W"], d["X"].shape)
+    dx8, sd = oracle.niti_requant(dX, tb)
+    out2 = torch.empty(N, H, W, 64, dtype=torch.int8, device=dev())
+    scal.zero_()
+    ops.int_conv_dgrad_requant(to_dev(d["dY"]), to_dev(d["W"]), out2, ops.conv_desc(N, H, W, 64, 64), tb,
+                               scal[0:1], shift_out=scal[1:2])
+    np.testing.assert_array_equal(host(out2), dx8)
+    assert host(scal).tolist() == [oracle.absmax(dX), sd]
+
+
+def test_conv_requant_refusals_and_empty():
+    from integer_only_nn_amd._lib import IonnError
+    # width 1: the halo of a 256-pixel tile does not fit, no fused path
+    x1 = torch.zeros(3, 5, 1, 64, dtype=torch.int8, device=dev())
+    w1 = torch.zeros(64, 3, 3, 64, dtype=torch.int8, device=dev())
+    o1 = torch.zeros(3, 5, 1, 64, dtype=torch.int8, device=dev())
+    s1 = torch.zeros(2, dtype=torch.int32, device=dev())
+    with pytest.raises(IonnError) as e:
+        ops.int_conv_fwd_requant(x1, w1, o1, ops.conv_desc(3, 5, 1, 64, 64), 7, 0, s1[0:1])
+    assert e.value.status == 5
+    x = torch.zeros(1, 4, 4, 32, dtype=torch.int8, device=dev())
+    w = torch.zeros(64, 3, 3, 32, dtype=torch.int8, device=dev())
+    o = torch.zeros(1, 4, 4, 64, dtype=torch.int8, device=dev())
+    scal = torch.zeros(2, dtype=torch.int32, device=dev())
+    with pytest.raises(IonnError) as e:   # 32 input channels: no fused path
+        ops.int_conv_fwd_requant(x, w, o, ops.conv_desc(1, 4, 4, 32, 64), 7, 0, scal[0:1])
+    assert e.value.status == 5
+    x64 = torch.zeros(1, 4, 4, 64, dtype=torch.int8, device=dev())
+    w64 = torch.zeros(64, 3, 3, 64, dtype=torch.int8, device=dev())
+    with pytest.raises(IonnError) as e:
+        ops.int_conv_fwd_requant(x64, w64, o, ops.conv_desc(1, 4, 4, 64, 64), 0, 0, scal[0:1])
+    assert e.value.status == 3
+    # no pixels: nothing to contract, s = 0 is written
+    scal.fill_(9)
+    scal[0] = 0
+    ops.int_conv_fwd_requant(x64, w64, o, ops.conv_desc(0, 4, 4, 64, 64), 7, 0, scal[0:1], shift_out=scal[1:2])
+    assert host(scal).tolist() == [0, 0]
+
+
+def test_conv_fused_workload_full():
+    """128x56x56x64 -> 64 through the fused path: y8, dx8 and their shifts
+    against the oracle (float64-product variant), and the same bytes as the
+    int32-then-requantise path."""
+    say("generating conv inputs")
+    d = ionn_synth.conv3x3()
+    X, W, dY = d["X"], d["W"], d["dY"]
+    N, H, Wd, C = X.shape
+    Wt = to_dev(W)
+    buf = steps.ConvStepBuffers.make(N, H, Wd, C, 64, dev())
+    steps.conv_step_fused(to_dev(X), Wt, to_dev(dY), buf)
+    sc = host(buf.scal).astype(np.int64) & 0xFFFFFFFF
+    say("oracle: forward")
+    Yo = fast.conv_fwd(X, W)
+    y8, s_y = oracle.niti_requant(Yo, 7)
+    np.testing.assert_array_equal(host(buf.y8), y8)
+    assert (sc[0], sc[3]) == (oracle.absmax(Yo), s_y)
+    del Yo, y8
+    say("oracle: dgrad")
+    dXo = fast.conv_dgrad(dY, W, X.shape)
+    dx8, s_dx = oracle.niti_requant(dXo, 7)
+    np.testing.assert_array_equal(host(buf.dx8), dx8)
+    assert (sc[1], sc[4]) == (oracle.absmax(dXo), s_dx)
