@@ -534,8 +534,10 @@ def cpu_baseline(rows):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported by this build "
-              "(the per-GPU step is the unit; see the sharding notes in DESIGN.md)", file=sys.stderr)
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported: the step is "
+              "timed on one GPU at its full per-GPU shape (a data-parallel split over tokens would "
+              "reduce-scatter the int32 weight gradient and max-combine every per-tensor maximum)",
+              file=sys.stderr)
         sys.exit(2)
     import torch
     from integer_only_nn_amd import lib, steps as steps_mod
