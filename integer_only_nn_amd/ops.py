@@ -206,21 +206,30 @@ def conv_desc(N, H, W, Cin, Cout, KH=3, KW=3, stride=1, pad=1, dilation=1, group
     return ConvDesc(N, H, W, Cin, Cout, KH, KW, stride, pad, dilation, groups)
 
 
+def _conv_numels(desc):
+    """Elements of X [N][H][W][Cin], W [Cout][KH][KW][Cin] and the output
+    [N][Ho][Wo][Cout] (Ho = H + 2 pad - KH + 1, stride 1) that a call with
+    this descriptor touches."""
+    ho = max(desc.H + 2 * desc.pad - desc.KH + 1, 0)
+    wo = max(desc.W + 2 * desc.pad - desc.KW + 1, 0)
+    return (desc.N * desc.H * desc.W * desc.Cin, desc.Cout * desc.KH * desc.KW * desc.Cin,
+            desc.N * ho * wo * desc.Cout)
+
+
 def int_conv_fwd(X, Wt, Y, desc, absmax_Y=None, stream=None):
-    check(lib().int_conv_fwd(_p(X, i8, name="X"), _p(Wt, i8, name="W"), _p(Y, i32, name="Y"),
+    nx, nw, ny = _conv_numels(desc)
+    check(lib().int_conv_fwd(_p(X, i8, nx, "X"), _p(Wt, i8, nw, "W"), _p(Y, i32, ny, "Y"),
                              ctypes.byref(desc), _p(absmax_Y, u32, 1, "absmax_Y"), _stream(stream)),
           "int_conv_fwd")
 
 
 def int_conv_dgrad(dY, Wt, dX, desc, absmax_dX=None, stream=None):
-    check(lib().int_conv_dgrad(_p(dY, i8, name="dY"), _p(Wt, i8, name="W"), _p(dX, i32, name="dX"),
+    nx, nw, ny = _conv_numels(desc)
+    check(lib().int_conv_dgrad(_p(dY, i8, ny, "dY"), _p(Wt, i8, nw, "W"), _p(dX, i32, nx, "dX"),
                                ctypes.byref(desc), _p(absmax_dX, u32, 1, "absmax_dX"),
                                _stream(stream)), "int_conv_dgrad")
 
 
-def _conv_numels(desc):
-    npix = desc.N * desc.H * desc.W
-    return npix * desc.Cin, desc.Cout * desc.KH * desc.KW * desc.Cin, npix * desc.Cout
 
 
 def int_conv_fwd_requant(X, Wt, Y8, desc, target_bits, relu, absmax_Y, shift_out=None, stream=None):
@@ -244,7 +253,8 @@ def int_conv_wgrad_workspace_bytes(desc):
 
 
 def int_conv_wgrad(dY, X, G, desc, absmax_G=None, workspace=None, stream=None):
-    check(lib().int_conv_wgrad(_p(dY, i8, name="dY"), _p(X, i8, name="X"), _p(G, i32, name="G"),
+    nx, nw, ny = _conv_numels(desc)
+    check(lib().int_conv_wgrad(_p(dY, i8, ny, "dY"), _p(X, i8, nx, "X"), _p(G, i32, nw, "G"),
                                ctypes.byref(desc), _p(absmax_G, u32, 1, "absmax_G"),
                                _p(workspace, None, name="workspace"),
                                workspace.numel() * workspace.element_size() if workspace is not None else 0,
