@@ -80,3 +80,36 @@ def test_conv_stack_model():
     for i in range(3):
         say("conv stack step", i)
         layers = _check_step(m, layers, X, labels, tmc, tmw, i)
+
+
+@pytest.mark.parametrize("B", [1, 3, 33, 100])
+def test_arc_fault_network_batches(B):
+    """Batches on both sides of the one-workgroup path's size limit (about
+    4M multiply-adds per step: B = 1, 3, 33 take it, B = 100 the
+    multi-kernel driver)."""
+    d = ionn_synth.arc_fault(B=B, seed=B)
+    layers = osteps.arc_fault_layers(d)
+    m = steps.Model(layers, B, dev())
+    for i in range(3):
+        say("arc-fault B", B, "step", i)
+        layers = _check_step(m, layers, d["X"], d["labels"], d["tmc"], d["tmw"], i)
+
+
+def test_conv_stack_model_small():
+    """The 3x3 conv stack at a size the one-workgroup path takes: padded
+    convolutions, the masked conv dgrad and a flattening Linear."""
+    rng = np.random.default_rng(11)
+    B, H, W = 2, 6, 5
+    layers = [_conv_layer(rng, H, W, 3, 16, 3, 1, True), _conv_layer(rng, H, W, 16, 16, 3, 1, True),
+              _conv_layer(rng, H, W, 16, 16, 3, 1, False),
+              dict(kind="linear", relu=True, IN=H * W * 16, OUT=7,
+                   weight=np.clip(np.round(rng.normal(0, 10, (7, H * W * 16))), -128, 127).astype(np.int8),
+                   offset=rng.integers(-200, 200, 7).astype(np.int32),
+                   mult=rng.integers(1, 4, 7).astype(np.int32), k=rng.integers(10, 12, 7).astype(np.int8))]
+    X = rng.integers(-100, 100, (B, H, W, 3)).astype(np.int8)
+    labels = np.array([2, 9], np.int32)   # 9 matches no class
+    tmc, tmw = np.full(7, 70, np.int8), np.full(7, -40, np.int8)
+    m = steps.Model(layers, B, dev())
+    for i in range(3):
+        say("small conv stack step", i)
+        layers = _check_step(m, layers, X, labels, tmc, tmw, i)
