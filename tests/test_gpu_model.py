@@ -113,3 +113,34 @@ def test_conv_stack_model_small():
     for i in range(3):
         say("small conv stack step", i)
         layers = _check_step(m, layers, X, labels, tmc, tmw, i)
+
+
+def _mlp(rng, dims, relus):
+    layers = []
+    for i in range(len(dims) - 1):
+        n_in, n_out = dims[i], dims[i + 1]
+        layers.append(dict(kind="linear", relu=relus[i], IN=n_in, OUT=n_out,
+                           weight=np.clip(np.round(rng.normal(0, 25, (n_out, n_in))), -128, 127).astype(np.int8),
+                           offset=rng.integers(-300, 300, n_out).astype(np.int32),
+                           mult=rng.integers(1, 5, n_out).astype(np.int32),
+                           k=rng.integers(6, 10, n_out).astype(np.int8)))
+    return layers
+
+
+@pytest.mark.parametrize("L", [8, 9])
+def test_deep_mlp_layer_limit(L):
+    """Ragged widths, ReLU on some layers only: eight layers run in one
+    workgroup, nine on the multi-kernel path; both bit-exact, every shift."""
+    rng = np.random.default_rng(40 + L)
+    dims = [37, 23, 64, 5, 17, 33, 9, 40, 3, 11][:L + 1]
+    relus = [True, False, True, True, False, True, True, False, True][:L]
+    layers = _mlp(rng, dims, relus)
+    B = 4
+    X = rng.integers(-128, 128, (B, dims[0])).astype(np.int8)
+    C = dims[-1]
+    labels = np.array([0, C - 1, 1, C + 3], np.int32)   # the last matches no class
+    tmc, tmw = np.full(C, 90, np.int8), np.full(C, -20, np.int8)
+    m = steps.Model(layers, B, dev())
+    for i in range(3):
+        say(f"deep MLP L={L} step", i)
+        layers = _check_step(m, layers, X, labels, tmc, tmw, i)
