@@ -499,7 +499,11 @@ int ionn_model_forward(const ionn_layer *layers, int L, const int8_t *X,
  * shifts_out (nullable, device int32[1 + 5 L]): [0] the error's shift, then
  * per layer l at 1 + 5 l: the shift of the delta it propagates (-1 for the
  * first layer, which propagates none), {s, ws} of its weight update and
- * {s, ws} of its offset update. */
+ * {s, ws} of its offset update.
+ * Models of at most 8 layers and 2^22 multiply-adds per step whose layers'
+ * operands fit in LDS run the forward and the backward as one workgroup each
+ * (same bits); others run the sequence above as separate launches.  Either
+ * way the calls are stream-ordered and allocate nothing. */
 int ionn_model_backward(const ionn_layer *layers, int L, const int8_t *X,
                         int64_t B, const int32_t *labels, const int8_t *tmc,
                         const int8_t *tmw, int tb_delta, int tb_weight, int mu,
