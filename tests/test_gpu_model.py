@@ -144,3 +144,33 @@ def test_deep_mlp_layer_limit(L):
     for i in range(3):
         say(f"deep MLP L={L} step", i)
         layers = _check_step(m, layers, X, labels, tmc, tmw, i)
+
+
+@pytest.mark.parametrize("B", [8, 100])
+def test_model_step_replayed_from_graph(B):
+    """A whole training step captured in one HIP graph and replayed three
+    times, with eager work and synchronisations between the replays: each
+    replay matches the oracle's next step (B = 8: the one-workgroup kernels;
+    B = 100: the multi-kernel driver)."""
+    d = ionn_synth.arc_fault(B=B, seed=50 + B)
+    layers = osteps.arc_fault_layers(d)
+    m = steps.Model(layers, B, dev())
+    X, lab, tmc, tmw = (to_dev(d[k]) for k in ("X", "labels", "tmc", "tmw"))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        m.step(X, lab, tmc, tmw, stream=s.cuda_stream)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        say("graph replay", rep, "B", B)
+        g.replay()
+        torch.cuda.synchronize()
+        new, rec = osteps.model_step(layers, d["X"], d["labels"], d["tmc"], d["tmw"])
+        np.testing.assert_array_equal(host(m.out), rec["acts"][-1].reshape(B, -1), err_msg=f"replay {rep}: output")
+        for l in range(len(layers)):
+            np.testing.assert_array_equal(host(m.dev[l]["weight"]), new[l]["weight"], err_msg=f"replay {rep} W{l}")
+            np.testing.assert_array_equal(host(m.dev[l]["offset"]), new[l]["offset"], err_msg=f"replay {rep} b{l}")
+        assert host(m.shifts).tolist()[0] == rec["s_err"]
+        layers = new
+        torch.zeros(1000, device=dev()).add_(1.0)   # unrelated eager work between replays
