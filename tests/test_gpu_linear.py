@@ -130,3 +130,33 @@ def test_large_linear_step_full():
     assert (sc[4], sc[5]) == (s, ws)
     np.testing.assert_array_equal(host(buf.gq), gqo)
     np.testing.assert_array_equal(host(Wd), Wo)
+
+
+def test_linear_step_replayed_from_graph():
+    """The training step (fill, fwd, dgrad, delta, wgrad, update) captured in
+    one HIP graph and replayed three times at a ragged size, with eager work
+    between replays: the fill kernel resets the maxima on every replay and
+    each replay matches the oracle's step on the weights it left."""
+    d = ionn_synth.single_linear(B=300, IN=520, OUT=264, seed=21)
+    X, W, dY = d["X"], d["W"], d["dY"]
+    Wd = to_dev(W)
+    Xd, dYd = to_dev(X), to_dev(dY)
+    buf = steps.LinearStepBuffers.make(300, 520, 264, dev(), with_gq=True)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        steps.linear_step(Xd, Wd, dYd, buf, stream=s.cuda_stream)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        say("linear step graph replay", rep)
+        g.replay()
+        torch.cuda.synchronize()
+        want = osteps.linear_step(X, W, dY)
+        np.testing.assert_array_equal(host(buf.delta), want["delta"], err_msg=f"replay {rep}: delta")
+        np.testing.assert_array_equal(host(buf.gq), want["Gq"], err_msg=f"replay {rep}: Gq")
+        np.testing.assert_array_equal(host(Wd), want["W_new"], err_msg=f"replay {rep}: W")
+        sc = host(buf.scal).tolist()
+        assert sc[3] == want["s_d"] and (sc[4], sc[5]) == (want["s"], want["ws"]), (rep, sc)
+        W = want["W_new"]
+        torch.zeros(1000, device=dev()).add_(1.0)   # unrelated eager work between replays
