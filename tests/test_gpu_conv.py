@@ -177,3 +177,35 @@ def test_conv_fused_workload_full():
     dx8, s_dx = oracle.niti_requant(dXo, 7)
     np.testing.assert_array_equal(host(buf.dx8), dx8)
     assert (sc[1], sc[4]) == (oracle.absmax(dXo), s_dx)
+
+
+def test_conv_step_fused_replayed_from_graph():
+    """The fused conv step captured in one HIP graph and replayed three
+    times (ragged 13x11 images), with eager work between replays: the maxima
+    restart from the fill kernel each time, the requantising passes read the
+    finished maxima, and every replay matches the oracle's step on the
+    weights the previous one left."""
+    N, H, W = 3, 13, 11
+    d = ionn_synth.conv3x3(N=N, H=H, W=W, Cin=64, Cout=64, seed=77)
+    X, Wt0, dY = d["X"], d["W"], d["dY"]
+    Wt = to_dev(Wt0)
+    Xd, dYd = to_dev(X), to_dev(dY)
+    buf = steps.ConvStepBuffers.make(N, H, W, 64, 64, dev(), with_gq=True)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        steps.conv_step_fused(Xd, Wt, dYd, buf, stream=s.cuda_stream)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        say("conv fused graph replay", rep)
+        g.replay()
+        torch.cuda.synchronize()
+        want = osteps.conv_step(X, Wt0, dY)
+        for k, t in (("y8", buf.y8), ("dx8", buf.dx8), ("Gq", buf.gq)):
+            np.testing.assert_array_equal(host(t), want[k], err_msg=f"replay {rep}: {k}")
+        np.testing.assert_array_equal(host(Wt), want["W_new"], err_msg=f"replay {rep}: W")
+        sc = host(buf.scal).astype(np.int64) & 0xFFFFFFFF
+        assert sc[3:7].tolist() == [want["s_y"], want["s_dx"], want["s"], want["ws"]], (rep, sc)
+        Wt0 = want["W_new"]
+        torch.zeros(1000, device=dev()).add_(1.0)   # unrelated eager work between replays
