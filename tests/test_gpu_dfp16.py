@@ -103,3 +103,34 @@ def test_dfp16_workload_full():
     np.testing.assert_array_equal(host(buf.G), Go)
     assert e[:3] == [eY, edX, eG]
     assert float(host(buf.gavg)[0]) == oracle.gavg(Go, eG, d["eW"])
+
+
+@pytest.mark.parametrize("M,K,N", [(640, 128, 384), (256, 320, 1024)])
+def test_dfp16_step_replayed_from_graph(M, K, N):
+    """The DFP-16 step (three contractions with their K splits and
+    reductions, the down-conversions, Gavg) captured in one HIP graph and
+    replayed three times; the outputs are overwritten between replays, so
+    each replay has to rebuild every value, exponent and status."""
+    d = ionn_synth.dfp16_gemm(M=M, K=K, N=N, seed=M + 3 * K)
+    want = osteps.dfp16_step(d["X"], d["eX"], d["W"], d["eW"], d["dY"], d["edY"])
+    buf = steps.DfpStepBuffers.make(M, K, N, dev())
+    args = (to_dev(d["X"]), _exp(d["eX"]), to_dev(d["W"]), _exp(d["eW"]), to_dev(d["dY"]), _exp(d["edY"]))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        steps.dfp16_step(*args, buf, stream=s.cuda_stream)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        say("dfp16 graph replay", rep, M, K, N)
+        for t, v in ((buf.Y, 123), (buf.dX, -5), (buf.G, 77), (buf.exps, -7), (buf.gavg, -1.0)):
+            t.fill_(v)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host(buf.Y), want["Y"], err_msg=f"replay {rep}: Y")
+        np.testing.assert_array_equal(host(buf.dX), want["dX"], err_msg=f"replay {rep}: dX")
+        np.testing.assert_array_equal(host(buf.G), want["G"], err_msg=f"replay {rep}: G")
+        e = host(buf.exps).tolist()
+        assert e[:3] == [want["eY"], want["edX"], want["eG"]] and e[3:6] == [0, 0, 0], (rep, e)
+        assert float(host(buf.gavg)[0]) == want["gavg"]
