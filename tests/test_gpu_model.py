@@ -174,3 +174,35 @@ def test_model_step_replayed_from_graph(B):
         assert host(m.shifts).tolist()[0] == rec["s_err"]
         layers = new
         torch.zeros(1000, device=dev()).add_(1.0)   # unrelated eager work between replays
+
+
+@pytest.mark.parametrize("B", [2, 40, 64])
+def test_rectangular_padded_conv_model(B):
+    """Rectangular kernels with and without padding (1x3 pad 1 grows the
+    height by two rows, 2x2 valid shrinks both), odd channel counts, both
+    paths (B = 2 and 40 one workgroup; B = 64 multi-kernel: the second
+    layer's 64*7*4*5 input gradients exceed the 8192 kept in LDS)."""
+    rng = np.random.default_rng(90 + B)
+    H, W = 5, 4
+
+    def conv(H, W, Cin, Cout, KH, KW, pad, relu):
+        return dict(kind="conv", relu=relu, H=H, W=W, Cin=Cin, Cout=Cout, KH=KH, KW=KW, pad=pad,
+                    weight=np.clip(np.round(rng.normal(0, 20, (Cout, KH, KW, Cin))), -128, 127).astype(np.int8),
+                    offset=rng.integers(-200, 200, Cout).astype(np.int32),
+                    mult=rng.integers(1, 4, Cout).astype(np.int32), k=rng.integers(6, 9, Cout).astype(np.int8))
+
+    l0 = conv(H, W, 3, 5, 1, 3, 1, True)            # -> (H + 2) x W x 5
+    l1 = conv(H + 2, W, 5, 4, 2, 2, 0, True)        # -> (H + 1) x (W - 1) x 4
+    n_in = (H + 1) * (W - 1) * 4
+    l2 = dict(kind="linear", relu=False, IN=n_in, OUT=6,
+              weight=np.clip(np.round(rng.normal(0, 15, (6, n_in))), -128, 127).astype(np.int8),
+              offset=rng.integers(-200, 200, 6).astype(np.int32),
+              mult=rng.integers(1, 4, 6).astype(np.int32), k=rng.integers(6, 9, 6).astype(np.int8))
+    layers = [l0, l1, l2]
+    X = rng.integers(-128, 128, (B, H, W, 3)).astype(np.int8)
+    labels = rng.integers(0, 7, B).astype(np.int32)   # 6 matches no class
+    tmc, tmw = np.full(6, 100, np.int8), np.full(6, -30, np.int8)
+    m = steps.Model(layers, B, dev())
+    for i in range(3):
+        say("rectangular conv model B", B, "step", i)
+        layers = _check_step(m, layers, X, labels, tmc, tmw, i)
