@@ -7,18 +7,27 @@ int8 x int8 -> int32, with the fused max-abs) and the NITI update of the
 16.8M weights.  Throughput counts 2*M*N*K ops per contraction (824.6 G int8
 ops per step); requantisation and update ALU work is not counted.  Inputs are
 seeded synthetic tensors with the workload's distributions, resident in HBM
-before the timed region.  The reported step time comes from K steps with one
-HIP event pair around all of them.  A second run of K steps brackets every
-launch with HIP events on the stream it runs on and gives the per-kernel
-averages (the roofline figure); an event between two kernels makes the first
-end with a system-scope release, so these steps run slightly slower.
+before the timed region.
 
-Also reported: the oracle (plain C, CPU) timed on a bounded sample of the
-same workload on this host, and secondary measurements of the conv and DFP-16
-steps.
+Timing protocol: --warmup W steps, then untimed steps until the clocks have
+left their idle state (at least --settle-s seconds and two consecutive K-step
+windows within 1%; the first K-step window after the W steps is reported
+beside it), then K steps between one HIP event pair (the reported step time),
+K steps with an event pair each (median and minimum), and K steps with every
+launch bracketed by events (per-kernel averages, the roofline figure; an
+event between two kernels makes the first end with a system-scope release,
+so these steps run slightly slower).  Socket power, the power-limit
+residency and the graphics clock are read from the driver's metrics over a
+few seconds of back-to-back steps.  The NITI update is also timed on its
+own, with the last-level cache flushed before every launch and warm.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-secondary]
-       [--no-cpu-baseline]
+Also reported: the single-layer and MLP workloads (latency-bound), the
+oracle (plain C, CPU) timed on bounded samples of the large step on this
+host with every thread and with one, and secondary measurements of the conv,
+DFP-16, offsets, model-driver and adaptive-precision paths.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--settle-s S]
+       [--power-window-s P] [--no-secondary] [--no-cpu-baseline]
 """
 import argparse
 import json
@@ -39,14 +48,23 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--settle-s", type=float, default=0.5,
+                    help="after the --warmup steps, keep stepping (untimed) for at least this long and "
+                         "until two consecutive K-step windows agree within 1%%: the clocks leave their "
+                         "idle state over the first tens of milliseconds")
+    ap.add_argument("--power-window-s", type=float, default=3.2,
+                    help="seconds of back-to-back steps over which socket power, power-limit residency "
+                         "and the graphics clock are read (0: skip)")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate", action="store_true",
                     help="also run a read-only and a write-only streaming kernel over 256 MiB "
                          "(scale for the HBM byte counters)")
-    ap.add_argument("--cpu-sample-rows", type=int, default=1536,
-                    help="token rows of the workload the CPU oracle runs")
+    ap.add_argument("--cpu-sample-rows", type=int, default=1024,
+                    help="token rows of the workload the CPU oracle runs on all host threads")
+    ap.add_argument("--cpu-sample-rows-1t", type=int, default=64,
+                    help="token rows of the workload the CPU oracle runs on one thread")
     return ap.parse_args()
 
 
@@ -75,7 +93,149 @@ class Timer:
         return out
 
 
-def bench_linear(torch, steps_mod, args):
+class PowerMonitor:
+    """Socket power, power-limit residency and graphics clock of the GPU from
+    the driver's metrics table (amdsmi).  The table is refreshed about once a
+    second; its energy accumulator, firmware timestamp (10 ns units), PPT
+    (package power tracking) residency and accumulation counter (1 ms units)
+    are exact between two refreshes, so averages are taken over whole
+    refresh intervals.  Unavailable (None) when amdsmi cannot read the
+    device."""
+
+    def __init__(self, torch):
+        self.h = None
+        self.err = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            hs = amdsmi.amdsmi_get_processor_handles()
+            want = None
+            try:
+                p = torch.cuda.get_device_properties(0)
+                want = "%04x:%02x:%02x" % (getattr(p, "pci_domain_id", 0), p.pci_bus_id, p.pci_device_id)
+            except Exception:
+                pass
+            for h in hs:
+                if want is None or amdsmi.amdsmi_get_gpu_device_bdf(h).lower().startswith(want):
+                    self.h = h
+                    break
+            if self.h is None and len(hs) == 1:
+                self.h = hs[0]
+            self.amdsmi = amdsmi
+            if self.h is None:
+                self.err = f"no amdsmi handle matches the device ({want})"
+        except Exception as e:   # no amdsmi, no permission: report the reason
+            self.err = repr(e)
+
+    def read(self):
+        m = self.amdsmi.amdsmi_get_gpu_metrics_info(self.h)
+        clks = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, int) and c > 0]
+        return dict(t=time.perf_counter(), fw=m.get("firmware_timestamp"), energy=m.get("energy_accumulator"),
+                    acc=m.get("accumulation_counter"), ppt=m.get("ppt_residency_acc"),
+                    clk=float(np.mean(clks)) if clks else None, clks=clks,
+                    power=m.get("current_socket_power"))
+
+    def static(self):
+        out = {}
+        try:
+            cap = self.amdsmi.amdsmi_get_power_cap_info(self.h)
+            out["power_cap_w"] = round(cap["power_cap"] / 1e6, 1)
+        except Exception as e:
+            out["power_cap_w"] = None
+            out["power_cap_error"] = repr(e)
+        try:
+            ci = self.amdsmi.amdsmi_get_clock_info(self.h, self.amdsmi.AmdSmiClkType.GFX)
+            out["gfxclk_max_mhz"] = ci.get("max_clk")
+        except Exception:
+            out["gfxclk_max_mhz"] = None
+        try:
+            out["energy_resolution_uj"] = float(self.amdsmi.amdsmi_get_energy_count(self.h)["counter_resolution"])
+        except Exception:
+            out["energy_resolution_uj"] = 15.3
+        return out
+
+    def window(self, step, torch, seconds):
+        """Run step() back to back for `seconds` while sampling the metrics
+        table every 2 ms; average power (energy / firmware time), PPT
+        residency and the graphics clock over the refresh intervals that lie
+        wholly inside the stepping."""
+        import threading
+        st = self.static()
+        samples, stop = [], threading.Event()
+
+        def sampler():
+            while not stop.is_set():
+                try:
+                    samples.append(self.read())
+                except Exception:
+                    pass
+                time.sleep(0.002)
+
+        th = threading.Thread(target=sampler, daemon=True)
+        torch.cuda.synchronize()
+        th.start()
+        t0 = time.perf_counter()
+        n = 0
+        while time.perf_counter() - t0 < seconds:
+            for _ in range(25):
+                step()
+            n += 25
+            torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        stop.set()
+        th.join()
+        # refreshes: samples whose firmware timestamp changed, inside [t0, t1]
+        ref, last = [], None
+        for s in samples:
+            if s["fw"] is not None and s["fw"] != last:
+                if t0 + 0.05 < s["t"] < t1:
+                    ref.append(s)
+                last = s["fw"]
+        out = dict(st, window_s=round(t1 - t0, 3), steps=n, refreshes=len(ref),
+                   source="amdsmi gpu_metrics: energy accumulator over firmware time, PPT residency "
+                          "over the accumulation counter, current_gfxclks (8 XCDs) at each refresh")
+        if len(ref) >= 2:
+            a, b = ref[0], ref[-1]
+            dt = (b["fw"] - a["fw"]) * 1e-8
+            out["avg_socket_power_w"] = round((b["energy"] - a["energy"]) * st["energy_resolution_uj"] * 1e-6 / dt, 1)
+            out["ppt_limited_frac"] = round((b["ppt"] - a["ppt"]) / max(1, b["acc"] - a["acc"]), 3)
+            clks = [r["clk"] for r in ref[1:] if r["clk"]]
+            out["gfxclk_mhz_mean"] = round(float(np.mean(clks)), 1) if clks else None
+            out["gfxclk_mhz_per_xcd"] = ref[-1]["clks"]
+            out["interval_s"] = round(dt, 3)
+        try:
+            # the driver's per-limiter residencies (percent of time), for the
+            # reasons the clock sat below its maximum
+            v = self.amdsmi.amdsmi_get_violation_status(self.h)
+            out["violation_pct"] = {k: v[k] for k in ("per_ppt_pwr", "per_socket_thrm", "per_vr_thrm",
+                                                      "per_hbm_thrm", "per_prochot_thrm",
+                                                      "per_gfx_clk_below_host_limit") if k in v}
+        except Exception as e:
+            out["violation_pct"] = {"error": repr(e)}
+        return out
+
+
+def settle(torch, step, k, min_s, max_s=5.0, tol=0.01):
+    """Untimed steps until at least min_s seconds have passed and two
+    consecutive windows of k steps agree within tol (at most max_s).
+    Returns (steps run, seconds, window times in ms/step)."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wins, n = [], 0
+    t0 = time.perf_counter()
+    while True:
+        e0.record()
+        for _ in range(k):
+            step()
+        e1.record()
+        torch.cuda.synchronize()
+        n += k
+        wins.append(e0.elapsed_time(e1) / k)
+        el = time.perf_counter() - t0
+        if el >= max_s or (el >= min_s and len(wins) >= 2 and abs(wins[-1] - wins[-2]) <= tol * wins[-2]):
+            return n, el, wins
+
+
+def bench_linear(torch, steps_mod, args, pm):
     from integer_only_nn_amd import ops
     import ionn_synth
     dev = torch.device("cuda:0")
@@ -86,6 +246,12 @@ def bench_linear(torch, steps_mod, args):
     dY = torch.from_numpy(d["dY"]).to(dev)
     buf = steps_mod.LinearStepBuffers.make(T, IN, OUT, dev)
     s = buf.scal
+    res = {}
+    if pm.h is not None:
+        try:
+            res["idle_gfxclk_mhz"] = pm.read()["clk"]
+        except Exception:
+            pass
 
     def step(tm=None):
         m = tm.mark if tm else (lambda n: None)
@@ -100,17 +266,39 @@ def bench_linear(torch, steps_mod, args):
         m("update")
         ops.niti_quantize_update(buf.G, s[2:3], 8, 2, W, shifts_out=s[4:6])
 
-    for _ in range(args.warmup):
-        step()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0.record()
-    for _ in range(args.steps):
+
+    def timed(nsteps):
+        torch.cuda.synchronize()
+        t0.record()
+        for _ in range(nsteps):
+            step()
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / nsteps
+
+    for _ in range(args.warmup):
         step()
-    t1.record()
+    # the first K-step window right after the warm-up steps, from idle clocks
+    res["first_window_ms_per_step"] = timed(args.steps)
+    n_set, s_set, wins = settle(torch, step, args.steps, args.settle_s)
+    res["settle"] = {"steps": n_set, "seconds": round(s_set, 3),
+                     "first_windows_ms_per_step": [round(w, 4) for w in wins[:6]],
+                     "last_windows_ms_per_step": [round(w, 4) for w in wins[-2:]]}
+    res["ms"] = timed(args.steps)
+
+    # per-step times (an event pair per step) for the median and the minimum
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / args.steps
+    ev[0].record()
+    for i in range(args.steps):
+        step()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    per_step = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
+    res["per_step_ms"] = {"median": float(np.median(per_step)), "min": float(np.min(per_step)),
+                          "max": float(np.max(per_step))}
 
     # the same steps with every launch bracketed by events: per-kernel averages
     tm = Timer(torch)
@@ -121,8 +309,54 @@ def bench_linear(torch, steps_mod, args):
     tm.mark(None)
     t1.record()
     torch.cuda.synchronize()
-    ms_instr = t0.elapsed_time(t1) / args.steps
-    per = {k: float(np.mean(v)) for k, v in tm.per_name().items()}
+    res["ms_instr"] = t0.elapsed_time(t1) / args.steps
+    res["per"] = {k: float(np.mean(v)) for k, v in tm.per_name().items()}
+
+    # each contraction timed inside the step by one event pair around it
+    # alone (the other launches run unbracketed), and back to back on its own
+    def only(name, e_a, e_b):
+        def st_():
+            ops.ionn_fill_u32(s[0:3], 0)
+            if name == "fwd":
+                e_a.record()
+            ops.int_linear_fwd(X, W, buf.Y, absmax_Y=s[0:1])
+            if name == "fwd":
+                e_b.record()
+            elif name == "dgrad":
+                e_a.record()
+            ops.int_linear_dgrad(dY, W, buf.dX, absmax_dX=s[1:2])
+            if name == "dgrad":
+                e_b.record()
+            elif name == "wgrad":
+                e_a.record()
+            ops.int_linear_wgrad(dY, X, buf.G, absmax_G=s[2:3])
+            if name == "wgrad":
+                e_b.record()
+            ops.niti_quantize_update(buf.G, s[2:3], 8, 2, W, shifts_out=s[4:6])
+        return st_
+    launch = {"fwd": lambda: ops.int_linear_fwd(X, W, buf.Y, absmax_Y=s[0:1]),
+              "dgrad": lambda: ops.int_linear_dgrad(dY, W, buf.dX, absmax_dX=s[1:2]),
+              "wgrad": lambda: ops.int_linear_wgrad(dY, X, buf.G, absmax_G=s[2:3]),
+              "update": lambda: ops.niti_quantize_update(buf.G, s[2:3], 8, 2, W, shifts_out=s[4:6])}
+    in_step, b2b = {}, {}
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for name in ("fwd", "dgrad", "wgrad"):
+        torch.cuda.synchronize()
+        for a, b in evs:
+            only(name, a, b)()
+        torch.cuda.synchronize()
+        in_step[name] = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    for name, fn in launch.items():
+        fn()
+        t0.record()
+        for _ in range(args.steps):
+            fn()
+        t1.record()
+        torch.cuda.synchronize()
+        b2b[name] = t0.elapsed_time(t1) / args.steps
+    res["kernel_in_step"] = in_step
+    res["kernel_back_to_back"] = b2b
 
     # the same step with the propagated delta requantised to 7 bits (untimed above)
     def step_req():
@@ -136,9 +370,160 @@ def bench_linear(torch, steps_mod, args):
         step_req()
     t1.record()
     torch.cuda.synchronize()
-    ms_req = t0.elapsed_time(t1) / args.steps
-    shifts = buf.scal.cpu().tolist()
-    return ms, per, ms_req, shifts, ms_instr
+    res["ms_req"] = t0.elapsed_time(t1) / args.steps
+    res["shifts"] = buf.scal.cpu().tolist()
+
+    # power and clock over a few seconds of back-to-back steps
+    if args.power_window_s > 0 and pm.h is not None:
+        try:
+            res["power"] = pm.window(step, torch, args.power_window_s)
+        except Exception as e:
+            res["power"] = {"error": repr(e)}
+
+    # the NITI update on its own: G cold (the 256 MB last-level cache flushed
+    # by a 1 GiB pass before every launch: a write pass, as the measurement
+    # protocol states, and a read-only pass, which leaves no dirty lines to
+    # write back during the update) and warm (launched back to back)
+    flush = torch.empty(256 << 20, dtype=torch.int32, device=dev)    # 1 GiB
+    fam = torch.zeros(1, dtype=torch.int32, device=dev)
+    ops.ionn_fill_u32(flush, 1)
+    upd = {}
+    for kind in ("write", "read"):
+        torch.cuda.synchronize()
+        for a, b in evs:
+            if kind == "write":
+                ops.ionn_fill_u32(flush, 0)
+            else:
+                ops.ionn_absmax_i32(flush, fam)
+            a.record()
+            launch["update"]()
+            b.record()
+        torch.cuda.synchronize()
+        ts = [a.elapsed_time(b) for a, b in evs]
+        upd[kind] = {"median_ms": float(np.median(ts)), "min_ms": float(np.min(ts))}
+    upd["warm"] = {"median_ms": b2b["update"], "min_ms": b2b["update"]}
+    del flush
+    res["update_alone"] = upd
+    return res
+
+
+def bench_small(torch, nsteps):
+    """The two latency-bound workloads: the single int8 linear layer (batch
+    16, 64 -> 32, one NITI step) and the 784-256-128-10 MLP trained for 10
+    steps at batch 256, each eagerly (one library call per launch) and
+    replayed from one captured HIP graph.  The MLP's weights are restored
+    from their seeded values before every 10-step run, outside the timed
+    region."""
+    import ionn_synth
+    from integer_only_nn_amd import steps as st
+    dev = torch.device("cuda:0")
+    to = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    out = {}
+
+    d = ionn_synth.single_linear()
+    X, W0, dY = to(d["X"]), to(d["W"]), to(d["dY"])
+    W = W0.clone()
+    buf = st.LinearStepBuffers.make(16, 64, 32, dev)
+
+    def one(stream=None):
+        st.linear_step(X, W, dY, buf, stream=stream)
+
+    def eager_ms(fn, reps):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    def graph_ms(fn, reps, nreplay=20):
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(s):
+            fn(s.cuda_stream)
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g, stream=s):
+                for _ in range(reps):
+                    fn(s.cuda_stream)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(nreplay):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / (nreplay * reps)
+
+    ems = eager_ms(one, nsteps)
+    gms = graph_ms(one, 10)
+    ops1 = 3 * 2.0 * 16 * 64 * 32
+    out["single_linear_16x64x32"] = {
+        "us_per_step": round(ems * 1e3, 2), "graph_us_per_step": round(gms * 1e3, 2),
+        "GOPS": round(ops1 / (ems * 1e-3) / 1e9, 3), "graph_GOPS": round(ops1 / (gms * 1e-3) / 1e9, 3),
+        "launches_per_step": 6, "note": "W evolves from step to step; the kernels' work does not depend on it"}
+
+    m = ionn_synth.mlp()
+    Ws0 = [to(w) for w in m["Ws"]]
+    Ws = [w.clone() for w in Ws0]
+    Xm, lab = to(m["X"]), to(m["labels"].astype(np.int32))
+    net = st.MLP.make(Ws, 256)
+
+    def ten(stream=None):
+        for _ in range(10):
+            net.step(Xm, lab, stream=stream)
+
+    def restore():
+        for w, w0 in zip(Ws, Ws0):
+            w.copy_(w0)
+
+    ten()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(nsteps):
+        restore()
+        torch.cuda.synchronize()
+        e0.record()
+        ten()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    t_eager = float(np.median(ts))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        ten(s.cuda_stream)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            ten(s.cuda_stream)
+    torch.cuda.synchronize()
+    tg = []
+    for _ in range(nsteps):
+        restore()
+        torch.cuda.synchronize()
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        tg.append(e0.elapsed_time(e1))
+    t_graph = float(np.median(tg))
+    sizes = (784, 256, 128, 10)
+    ops_step = 2.0 * 256 * sum(a * b for a, b in zip(sizes[:-1], sizes[1:])) * 3
+    out["mlp_784_256_128_10_b256_10steps"] = {
+        "ms_10_steps": round(t_eager, 4), "samples_per_s": round(2560 / (t_eager * 1e-3), 1),
+        "graph_ms_10_steps": round(t_graph, 4), "graph_samples_per_s": round(2560 / (t_graph * 1e-3), 1),
+        "TOPS": round(10 * ops_step / (t_eager * 1e-3) / 1e12, 4),
+        "graph_TOPS": round(10 * ops_step / (t_graph * 1e-3) / 1e12, 4),
+        "launches_per_step": 1 + 2 * 3 + 2 + 4 * 3,
+        "note": "median of runs; weights restored to their seeded values before each 10-step run, "
+                "outside the timed region"}
+    return out
 
 
 def _timed(torch, step, nsteps):
@@ -513,22 +898,42 @@ def measured_traffic():
     return out if src == _kernel_source_hash() else {}
 
 
-def cpu_baseline(rows):
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(rows, threads=None):
     """The oracle (plain C, OpenMP) on a bounded sample of the large-linear
     step: `rows` token rows through fwd and dgrad, wgrad over `rows` tokens,
-    then the NITI update of all 16.8M weights.  Returns TOPS for the sample."""
+    then the NITI update of all 16.8M weights.  threads=None: the oracle's
+    default (every host thread).  Returns (TOPS of the sample, seconds,
+    threads used)."""
     import oracle
     import ionn_synth
     d = ionn_synth.large_linear(T=rows, IN=IN, OUT=OUT)
     X, W, dY = d["X"], d["W"], d["dY"]
-    t0 = time.perf_counter()
-    oracle.linear_fwd(X, W)
-    oracle.linear_dgrad(dY, W)
-    G = oracle.linear_wgrad(dY, X)
-    oracle.niti_update(G, W, 8, 2)
-    dt = time.perf_counter() - t0
+    prev = oracle.get_threads()
+    if threads is not None:
+        oracle.set_threads(threads)
+    try:
+        used = oracle.get_threads()
+        t0 = time.perf_counter()
+        oracle.linear_fwd(X, W)
+        oracle.linear_dgrad(dY, W)
+        G = oracle.linear_wgrad(dY, X)
+        oracle.niti_update(G, W, 8, 2)
+        dt = time.perf_counter() - t0
+    finally:
+        oracle.set_threads(prev)
     ops_done = 3 * 2.0 * rows * IN * OUT
-    return ops_done / dt / 1e12, dt, oracle.get_threads()
+    return ops_done / dt / 1e12, dt, used
 
 
 def main():
@@ -543,17 +948,40 @@ def main():
     from integer_only_nn_amd import lib, steps as steps_mod
     lib()  # fail loudly if the HIP library is missing
     assert torch.cuda.is_available(), "no ROCm device visible"
+    pm = PowerMonitor(torch)
 
-    ms, per, ms_req, shifts, ms_instr = bench_linear(torch, steps_mod, args)
+    L = bench_linear(torch, steps_mod, args, pm)
+    ms, per = L["ms"], L["per"]
     ops_step = 3 * 2.0 * T * IN * OUT
     tops = ops_step / (ms * 1e-3) / 1e12
-    gemm = {k: per[k] for k in ("fwd", "dgrad", "wgrad")}
+    # the roofline kernel: the slowest contraction, timed inside the step by
+    # one event pair around it alone (per-launch brackets on every kernel
+    # slow the step down; they only give the breakdown in kernel_ms)
+    gemm = dict(L["kernel_in_step"])
     dom = max(gemm, key=gemm.get)
     achieved = 2.0 * T * IN * OUT / (gemm[dom] * 1e-3) / 1e12
+    b2b = L["kernel_back_to_back"]
     upd_bytes = 6.0 * IN * OUT
     traffic = measured_traffic()
     upd_gbs = upd_bytes / (per["update"] * 1e-3) / 1e9
+    gbs = lambda t_ms: round(upd_bytes / (t_ms * 1e-3) / 1e9, 1)
+    ua = L["update_alone"]
     log(f"step {ms:.3f} ms  {tops:.1f} TOPS  per-kernel ms {per}")
+    shifts = L["shifts"]
+    power = L.get("power") or {"error": pm.err}
+    roof = {"bound": "mfma", "kernel": f"int_linear_{dom}", "achieved": round(achieved, 1),
+            "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_INT8_TOPS, 4),
+            "traffic": traffic.get(f"int_linear_{dom}"),
+            "duration_ms": round(gemm[dom], 4),
+            "duration_source": "HIP events around this kernel alone inside each timed step (the "
+                               "interval also holds the system-scope release the end event forces)",
+            "achieved_back_to_back": round(2.0 * T * IN * OUT / (b2b[dom] * 1e-3) / 1e12, 1)}
+    clk = power.get("gfxclk_mhz_mean")
+    if clk:
+        # the same peak at the graphics clock the power limit held during the
+        # steps (matrix rate scales with the clock)
+        roof["peak_at_measured_clock"] = round(PEAK_INT8_TOPS * clk / 2400.0, 1)
+        roof["frac_at_measured_clock"] = round(achieved / roof["peak_at_measured_clock"], 4)
 
     result = {
         "metric": "INT8 training-step TOPS (fwd+dgrad+wgrad+NITI update), % of INT8 MFMA peak",
@@ -572,18 +1000,33 @@ def main():
                    "out": OUT, "target_bits_weight": 8, "mu_weight": 2, "parallelism": "none"},
         "pct_of_int8_peak": round(100.0 * tops / PEAK_INT8_TOPS, 2),
         "tokens_per_s": round(T / (ms * 1e-3), 1),
+        "per_step_ms": {k: round(v, 4) for k, v in L["per_step_ms"].items()},
+        "warmup_protocol": {"warmup_steps": args.warmup, "settle": L["settle"],
+                            "first_window_after_warmup_ms_per_step": round(L["first_window_ms_per_step"], 4),
+                            "idle_gfxclk_mhz": L.get("idle_gfxclk_mhz")},
         "kernel_ms": {k: round(v, 4) for k, v in per.items()},
-        "ms_per_step_events_per_launch": round(ms_instr, 4),
-        "roofline": {"bound": "mfma", "kernel": f"int_linear_{dom}", "achieved": round(achieved, 1),
-                     "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_INT8_TOPS, 4),
-                     "traffic": traffic.get(f"int_linear_{dom}")},
+        "ms_per_step_events_per_launch": round(L["ms_instr"], 4),
+        "kernel_ms_in_step": {k: round(v, 4) for k, v in L["kernel_in_step"].items()},
+        "kernel_ms_back_to_back": {k: round(v, 4) for k, v in L["kernel_back_to_back"].items()},
+        "roofline": roof,
+        "clock_power": power,
         "update_pass": {"bound": "hbm", "achieved": round(upd_gbs, 1), "peak": PEAK_HBM_GBS,
                         "unit": "GB/s", "frac": round(upd_gbs / PEAK_HBM_GBS, 4),
                         "bytes_per_launch": upd_bytes,
-                        "traffic": traffic.get("niti_quantize_update")},
-        "ms_per_step_with_delta_requant": round(ms_req, 4),
+                        "in_step_event_interval_ms": round(per["update"], 4),
+                        "alone": {k: {"median_ms": round(v["median_ms"], 4), "min_ms": round(v["min_ms"], 4),
+                                      "GBps": gbs(v["median_ms"]),
+                                      "frac": round(gbs(v["median_ms"]) / PEAK_HBM_GBS, 4)}
+                                  for k, v in ua.items()},
+                        "alone_note": "write / read: the last-level cache flushed before every launch by a "
+                                      "1 GiB write (resp. read-only) pass; warm: launched back to back",
+                        "traffic": traffic.get("niti_quantize_update"),
+                        "traffic_source": "profiles/ FETCH_SIZE + WRITE_SIZE summary of the committed "
+                                          "kernels (null when the sources changed since)"},
+        "ms_per_step_with_delta_requant": round(L["ms_req"], 4),
         "shifts": {"s_delta": shifts[3], "s_weight": shifts[4], "ws": shifts[5]},
     }
+    result["small_workloads"] = bench_small(torch, 20)
     if args.calibrate:
         from integer_only_nn_amd import ops
         cal = torch.ones(64 << 20, dtype=torch.int32, device="cuda:0")   # 256 MiB
@@ -615,6 +1058,10 @@ def main():
         # element per 64-term chunk (digit combination, rounding shift, add)
         dfp_alu = {"fwd": 6.0 * 25088 * 1024 * (256 // 64), "dgrad": 6.0 * 25088 * 256 * (1024 // 64),
                    "wgrad": 6.0 * 1024 * 256 * (25088 // 64)}
+        # the method's own work: 2*M*N*K int16 multiply-adds per contraction,
+        # each 4 int8 digit products on the matrix cores (every role has the
+        # same M*N*K); the VALU view of the epilogue is kept beside it
+        dfp_i8 = 4 * 2.0 * 25088 * 256 * 1024
         fdom = max(dfp_alu, key=lambda k: f_per[k])
         falu = dfp_alu[fdom] / (f_per[fdom] * 1e-3) / 1e12
         p_ms, p_per = bench_dfp16_paper(torch, 20)
@@ -659,31 +1106,47 @@ def main():
                            "int16_TOPS": round(dfp_ops / (f_ms * 1e-3) / 1e12, 2),
                            "images_per_s": round(128 / (f_ms * 1e-3), 1),
                            "kernel_ms": {k: round(v, 4) for k, v in f_per.items()},
-                           "roofline": {"bound": "alu", "kernel": f"dfp16_gemm_{fdom}",
-                                        "achieved": round(falu, 2), "peak": PEAK_VALU_TOPS,
-                                        "unit": "T int32 op/s", "frac": round(falu / PEAK_VALU_TOPS, 4),
-                                        "ops_per_launch": dfp_alu[fdom]}},
+                           "roofline": {"bound": "mfma", "kernel": f"dfp16_gemm_{fdom}",
+                                        "achieved": round(dfp_i8 / (f_per[fdom] * 1e-3) / 1e12, 1),
+                                        "peak": PEAK_INT8_TOPS, "unit": "TOPS (int8 digit products)",
+                                        "frac": round(dfp_i8 / (f_per[fdom] * 1e-3) / 1e12 / PEAK_INT8_TOPS, 4),
+                                        "ops_per_launch": dfp_i8,
+                                        "work": "2*M*N*K int16 multiply-adds = 4 int8 digit products each"},
+                           "roofline_valu": {"bound": "alu", "kernel": f"dfp16_gemm_{fdom}",
+                                             "achieved": round(falu, 2), "peak": PEAK_VALU_TOPS,
+                                             "unit": "T int32 op/s", "frac": round(falu / PEAK_VALU_TOPS, 4),
+                                             "ops_per_launch": dfp_alu[fdom],
+                                             "work": "the kernel's epilogue: 6 int32 ops per output per chunk"}},
             "dfp16_paper_step": {"shape": "M25088 K256 N1024, FP32 chunk partials, 1-bit input shift",
                                  "ms_per_step": round(p_ms, 4),
                                  "int16_TOPS": round(dfp_ops / (p_ms * 1e-3) / 1e12, 2),
                                  "kernel_ms": {k: round(v, 4) for k, v in p_per.items()},
-                                 "roofline": {"bound": "alu", "kernel": f"dfp16_gemm_{pdom}_f32",
-                                              "achieved": round(palu, 2), "peak": PEAK_VALU_TOPS,
-                                              "unit": "T int32 op/s", "frac": round(palu / PEAK_VALU_TOPS, 4),
-                                              "ops_per_launch": dfp_alu[pdom]}},
+                                 "roofline": {"bound": "mfma", "kernel": f"dfp16_gemm_{pdom}_f32",
+                                              "achieved": round(dfp_i8 / (p_per[pdom] * 1e-3) / 1e12, 1),
+                                              "peak": PEAK_INT8_TOPS, "unit": "TOPS (int8 digit products)",
+                                              "frac": round(dfp_i8 / (p_per[pdom] * 1e-3) / 1e12 / PEAK_INT8_TOPS, 4),
+                                              "ops_per_launch": dfp_i8},
+                                 "roofline_valu": {"bound": "alu", "kernel": f"dfp16_gemm_{pdom}_f32",
+                                                   "achieved": round(palu, 2), "peak": PEAK_VALU_TOPS,
+                                                   "unit": "T int32 op/s", "frac": round(palu / PEAK_VALU_TOPS, 4),
+                                                   "ops_per_launch": dfp_alu[pdom]}},
             "offsets_oss": offsets,
             "arc_fault_model": dict(shape="Conv 16x2 valid 1->3 + ReLU, Linear 147->160 + ReLU, Linear 160->2",
                                     **bench_model(torch, 50)),
             "adaptive_precision": bench_apt(torch, 20),
         }
     if not args.no_cpu_baseline:
-        log("cpu baseline: oracle on a bounded sample")
+        log("cpu baseline: oracle on bounded samples, all host threads then one thread")
         ctops, dt, threads = cpu_baseline(args.cpu_sample_rows)
+        ctops1, dt1, _ = cpu_baseline(args.cpu_sample_rows_1t, threads=1)
+        sample = lambda r, t: (f"{r} of {T} token rows through fwd, dgrad and wgrad "
+                               f"(3 x 2 x {r} x {IN} x {OUT} ops) plus the full 16.8M-weight update; {t:.1f} s")
         result["cpu_baseline"] = {
-            "value": round(ctops, 4), "unit": "TOPS", "cores": threads, "kind": "oracle",
-            "sample": f"{args.cpu_sample_rows} of {T} token rows through fwd, dgrad and wgrad "
-                      f"(3 x 2 x {args.cpu_sample_rows} x {IN} x {OUT} ops) plus the full "
-                      f"16.8M-weight update; {dt:.1f} s"}
+            "value": round(ctops, 5), "unit": "TOPS", "cores": threads, "kind": "oracle",
+            "sample": sample(args.cpu_sample_rows, dt), "cpu_model": _cpu_model(),
+            "host_threads": os.cpu_count(),
+            "one_thread": {"value": round(ctops1, 5), "unit": "TOPS", "cores": 1,
+                           "sample": sample(args.cpu_sample_rows_1t, dt1)}}
     print(json.dumps(result), flush=True)
 
 
