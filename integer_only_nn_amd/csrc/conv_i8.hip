@@ -25,6 +25,8 @@
 #include "gemm_core.h"
 #include "conv3x3.h"
 
+#include <initializer_list>
+
 #include <atomic>
 
 namespace ionn {
@@ -55,11 +57,25 @@ int check_desc(const ionn_conv_desc *d, const char *name) {
                      d->pad <= 1024,
                  IONN_ERR_RANGE, "%s: kernel %dx%d with pad %d (need KH, KW in [1, 1024], pad in [0, 1024])",
                  name, d->KH, d->KW, d->pad);
-    const int64_t npix = d->N * d->H * d->W, Ho = out_h(d), Wo = out_w(d);
-    const int64_t nout = d->N * (Ho > 0 ? Ho : 0) * (Wo > 0 ? Wo : 0);
-    IONN_REQUIRE(npix <= kMaxDim && npix * d->Cin <= kMaxDim && npix * d->Cout <= kMaxDim &&
-                     nout * d->Cout <= kMaxDim && d->Cin * d->KH * d->KW <= kMaxDim &&
-                     d->Cout * d->KH * d->KW * d->Cin <= kMaxDim,
+    // Every size on its own first, then each product one factor at a time
+    // (a <= kMaxDim / b before a * b), so no intermediate can overflow.
+    IONN_REQUIRE(d->N <= kMaxDim && d->H <= kMaxDim && d->W <= kMaxDim && d->Cin <= kMaxDim &&
+                     d->Cout <= kMaxDim,
+                 IONN_ERR_SHAPE, "%s: every size must be below 2^31", name);
+    const int64_t Ho = out_h(d), Wo = out_w(d);
+    IONN_REQUIRE(Ho <= kMaxDim && Wo <= kMaxDim, IONN_ERR_SHAPE, "%s: output size out of range", name);
+    auto fits = [](std::initializer_list<int64_t> f) {
+        int64_t p = 1;
+        for (int64_t v : f) {
+            if (v <= 0) return true;  // an empty tensor
+            if (p > kMaxDim / v) return false;
+            p *= v;
+        }
+        return p <= kMaxDim;
+    };
+    IONN_REQUIRE(fits({d->N, d->H, d->W, d->Cin}) && fits({d->N, d->H, d->W, d->Cout}) &&
+                     fits({d->N, Ho, Wo, d->Cout}) && fits({d->N, Ho, Wo, d->Cin}) &&
+                     fits({int64_t(d->KH), int64_t(d->KW), d->Cin, d->Cout}),
                  IONN_ERR_SHAPE, "%s: tensors must hold fewer than 2^31 elements", name);
     return IONN_OK;
 }

@@ -84,6 +84,7 @@ class MLP:
     d32: List[torch.Tensor] = field(default_factory=list)
     deltas: List[torch.Tensor] = field(default_factory=list)
     G: List[torch.Tensor] = field(default_factory=list)
+    Gq: Optional[List[torch.Tensor]] = None   # with_gq: each layer's Gq of the last step
     e32: Optional[torch.Tensor] = None
     # per step: [fwd max x L | err max | dgrad max x L | G max x L] (uint32)
     # and shifts [fwd s x L | err s | dgrad s x L | (s, ws) x L]
@@ -91,10 +92,12 @@ class MLP:
     shifts: Optional[torch.Tensor] = None
 
     @staticmethod
-    def make(Ws, B, relu=None):
+    def make(Ws, B, relu=None, with_gq=False):
         L = len(Ws)
         dev = Ws[0].device
         m = MLP(list(Ws), relu if relu is not None else [l < L - 1 for l in range(L)], B)
+        if with_gq:
+            m.Gq = [_i32(*w.shape, device=dev) for w in Ws]
         sizes = [Ws[0].shape[1]] + [w.shape[0] for w in Ws]
         m.acts = [None] + [_i8(B, sizes[l + 1], device=dev) for l in range(L)]
         m.z32 = [_i32(B, sizes[l + 1], device=dev) for l in range(L)]
@@ -133,6 +136,7 @@ class MLP:
                                  stream=stream)
             ops.niti_quantize_update(self.G[l], gm, tb_w, mu, self.Ws[l],
                                      shifts_out=sh[2 * L + 1 + 2 * l:2 * L + 3 + 2 * l],
+                                     gq_out=self.Gq[l] if self.Gq is not None else None,
                                      stream=stream)
 
     def shift_record(self):

@@ -67,7 +67,6 @@ def _declare(L):
         "ora_conv_wgrad_at": (ctypes.c_int32, [_P, _P] + [_I64] * 5 + [_I] * 3 + [_I64] * 4),
         "ora_dfp_chunk_shift": (_I, [_I64, _I]),
         "ora_dfp_contract": (_I64, [_P, _I64, _I64, _P, _I64, _I64, _I64, _I64, _I64, _I, _P]),
-        "ora_dfp_contract_at": (ctypes.c_int32, [_P, _I64, _I64, _P, _I64, _I64, _I64, _I, _I64, _I64]),
         "ora_dfp_downconvert": (_I, [_P, _I64, _P]),
         "ora_dfp16_fwd": (_I, [_P, _I, _P, _I, _P, _P, _P, _I64, _I64, _I64, _I]),
         "ora_dfp16_dgrad": (_I, [_P, _I, _P, _I, _P, _P, _P, _I64, _I64, _I64, _I]),
@@ -349,11 +348,6 @@ def dfp_contract(A, sam, sak, B, sbk, sbn, M, N, L, chunk=64, return_wraps=False
     return (acc, w) if return_wraps else acc
 
 
-def dfp_contract_at(A, sam, sak, B, sbk, sbn, L, m, n, chunk=64):
-    return lib().ora_dfp_contract_at(_c(A, np.int16), sam, sak, _c(B, np.int16), sbk, sbn, L,
-                                     int(chunk), int(m), int(n))
-
-
 def dfp_downconvert(acc):
     out = np.empty(acc.shape, np.int16)
     rs = lib().ora_dfp_downconvert(_c(acc, np.int32), acc.size, _c(out, np.int16))
@@ -507,6 +501,21 @@ def dfp16_sgd(W32, G32, lr):
     st = lib().ora_dfp16_sgd(_c(W, np.float32), _c(G, np.float32), W.size, float(lr), _c(W16, np.int16),
                              ctypes.byref(e))
     return W, W16, e.value, st
+
+
+def dfp16_default_splits(M, K, N, role):
+    """The default number S of chunk ranges of the FP32 accumulation for a
+    shape (reading U35 of the design notes: the order is a function of the
+    shape alone).  With R x C outputs of the role in 128 x 128 tiles and n_c
+    chunks of 64 along its reduction: S = 1 when there are at least 256 tiles
+    or fewer than 8 chunks; otherwise S = min(ceil(256 / tiles),
+    floor(n_c / 4)), at least 1."""
+    R, C, L = {"fwd": (M, N, K), "dgrad": (M, K, N), "wgrad": (N, K, M)}[role]
+    tiles = -(-R // 128) * -(-C // 128)
+    nch = -(-L // 64)
+    if tiles >= 256 or nch < 8:
+        return 1
+    return max(1, min(-(-256 // tiles), nch // 4))
 
 
 def dfp16_f32_at(role, A, eA, B, eB, m, n, S=1, input_shift=1):

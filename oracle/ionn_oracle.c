@@ -502,21 +502,6 @@ int ora_dfp_chunk_shift(int64_t L, int chunk)
     return nc <= 1 ? 0 : ora_ceil_log2(nc);
 }
 
-int32_t ora_dfp_contract_at(const int16_t *A, int64_t sam, int64_t sak,
-                            const int16_t *B, int64_t sbk, int64_t sbn,
-                            int64_t L, int chunk, int64_t m, int64_t n)
-{
-    int r = ora_dfp_chunk_shift(L, chunk);
-    uint32_t acc = 0;
-    for (int64_t k0 = 0; k0 < L; k0 += chunk) {
-        uint32_t p = 0;
-        for (int64_t k = k0; k < k0 + chunk && k < L; ++k)
-            p += (uint32_t)((int32_t)A[m * sam + k * sak] * (int32_t)B[k * sbk + n * sbn]);
-        acc += (uint32_t)ora_rhu(u32_to_i32(p), r);
-    }
-    return u32_to_i32(acc);
-}
-
 int64_t ora_dfp_contract(const int16_t *A, int64_t sam, int64_t sak,
                          const int16_t *B, int64_t sbk, int64_t sbn, int64_t M,
                          int64_t N, int64_t L, int chunk, int32_t *acc_out)

@@ -116,9 +116,6 @@ int     ora_dfp_chunk_shift(int64_t L, int chunk);
 int64_t ora_dfp_contract(const int16_t *A, int64_t sam, int64_t sak,
                          const int16_t *B, int64_t sbk, int64_t sbn, int64_t M,
                          int64_t N, int64_t L, int chunk, int32_t *acc);
-int32_t ora_dfp_contract_at(const int16_t *A, int64_t sam, int64_t sak,
-                            const int16_t *B, int64_t sbk, int64_t sbn,
-                            int64_t L, int chunk, int64_t m, int64_t n);
 /* Down-conversion: Rs = max(0, bitlen(max|acc|) - 15); out = sat16(rhu(acc, Rs)).
  * Returns Rs. */
 int ora_dfp_downconvert(const int32_t *acc, int64_t n, int16_t *out);

@@ -68,6 +68,8 @@ def mlp_step(X, labels, Ws, relu_layers=None, target_mag=127, tb_w=TB_WEIGHT, mu
     new_W = list(Ws)
     s_dgrad = [None] * L
     s_upd = [None] * L
+    Gs = [None] * L
+    Gqs = [None] * L
     deltas = [None] * (L + 1)
     deltas[L] = delta
     for l in range(L - 1, -1, -1):
@@ -75,11 +77,11 @@ def mlp_step(X, labels, Ws, relu_layers=None, target_mag=127, tb_w=TB_WEIGHT, mu
         if l >= 1 and relu_layers[l - 1]:
             d32 = relu_mask(d32, acts[l])
         deltas[l], s_dgrad[l] = niti_requant(d32, tb_d)
-        G = linear_wgrad(deltas[l + 1], acts[l])
-        new_W[l], _, s, ws = niti_update(G, Ws[l], tb_w, mu)
+        Gs[l] = linear_wgrad(deltas[l + 1], acts[l])
+        new_W[l], Gqs[l], s, ws = niti_update(Gs[l], Ws[l], tb_w, mu)
         s_upd[l] = (s, ws)
     rec = dict(acts=acts, s_fwd=s_fwd, e32=e32, s_err=s_err, deltas=deltas, s_dgrad=s_dgrad,
-               s_upd=s_upd)
+               s_upd=s_upd, G=Gs, Gq=Gqs)
     return new_W, rec
 
 

@@ -119,6 +119,14 @@ def _gpu_f32(which, A, eA, B, eB, M, K, N, shift, nsplit, misalign=False):
     return host(out)
 
 
+def _default_S(M, K, N, which):
+    """The default FP32 range count, from the oracle's statement of the rule;
+    the library must use the same one."""
+    S = oracle.dfp16_default_splits(M, K, N, {FWD: "fwd", DGRAD: "dgrad", WGRAD: "wgrad"}[which])
+    assert ops.dfp16_f32_splits(M, K, N, which) == S, (M, K, N, which)
+    return S
+
+
 def _ora_f32(which, A, eA, B, eB, S, shift):
     fn = {FWD: oracle.dfp16_fwd_f32, DGRAD: oracle.dfp16_dgrad_f32, WGRAD: oracle.dfp16_wgrad_f32}[which]
     return fn(A, eA, B, eB, S=S, input_shift=shift)[0]
@@ -147,7 +155,7 @@ def test_f32_contraction_parity(M, K, N, which):
     A, eA, B, eB = _operands(which, M, K, N, seed=M + K + N + which)
     L = {FWD: K, DGRAD: N, WGRAD: M}[which]
     nch = (L + 63) // 64
-    default = ops.dfp16_f32_splits(M, K, N, which)
+    default = _default_S(M, K, N, which)
     for shift, nsplit in ((1, 0), (0, 0), (1, 1), (1, nch), (1, min(3, nch))):
         S = nsplit or default
         say("f32", which, M, K, N, shift, nsplit, S)
@@ -159,7 +167,7 @@ def test_f32_contraction_parity(M, K, N, which):
 def test_f32_contraction_unaligned_operands(which):
     M, K, N = 256, 256, 128
     A, eA, B, eB = _operands(which, M, K, N, seed=9 + which)
-    S = ops.dfp16_f32_splits(M, K, N, which)
+    S = _default_S(M, K, N, which)
     _same_f32(_gpu_f32(which, A, eA, B, eB, M, K, N, 1, 0, misalign=True), _ora_f32(which, A, eA, B, eB, S, 1))
 
 
@@ -177,7 +185,7 @@ def test_f32_contraction_full_size_sampled(which):
     times: 4096 sampled outputs (and whole rows) against the oracle."""
     M, K, N = 25088, 256, 1024
     A, eA, B, eB = _operands(which, M, K, N, seed=0)
-    S = ops.dfp16_f32_splits(M, K, N, which)
+    S = _default_S(M, K, N, which)
     got = _gpu_f32(which, A, eA, B, eB, M, K, N, 1, 0)
     R, C = got.shape
     rng = np.random.default_rng(which)
@@ -220,10 +228,10 @@ def test_paper_step_chain():
     Xo, eX, _ = oracle.dfp_from_f32(X32)
     Wo, eW, _ = oracle.dfp_from_f32(W32)
     dYo, edY, _ = oracle.dfp_from_f32(dY32)
-    Y = oracle.dfp16_fwd_f32(Xo, eX, Wo, eW, S=ops.dfp16_f32_splits(M, K, N, FWD))[0]
+    Y = oracle.dfp16_fwd_f32(Xo, eX, Wo, eW, S=_default_S(M, K, N, FWD))[0]
     Yo, eY, _ = oracle.dfp_from_f32(Y)
-    dX = oracle.dfp16_dgrad_f32(dYo, edY, Wo, eW, S=ops.dfp16_f32_splits(M, K, N, DGRAD))[0]
-    G = oracle.dfp16_wgrad_f32(dYo, edY, Xo, eX, S=ops.dfp16_f32_splits(M, K, N, WGRAD))[0]
+    dX = oracle.dfp16_dgrad_f32(dYo, edY, Wo, eW, S=_default_S(M, K, N, DGRAD))[0]
+    G = oracle.dfp16_wgrad_f32(dYo, edY, Xo, eX, S=_default_S(M, K, N, WGRAD))[0]
     W2, W16, eW2, _ = oracle.dfp16_sgd(W32, G, 0.01)
 
     cws = _cws()
@@ -268,7 +276,7 @@ def test_blocked_fwd_parity(M, K, N):
     Xb, eX, _ = oracle.dfp_from_f32_blocked(X32)
     Wb, eW, _ = oracle.dfp_from_f32_blocked(W32)
     nch = (K + 63) // 64
-    default = ops.dfp16_f32_splits(M, K, N, FWD)
+    default = _default_S(M, K, N, FWD)
     for shift, nsplit in ((1, 0), (0, 1), (1, min(3, nch))):
         S = nsplit or default
         say("blocked", M, K, N, shift, S)
@@ -300,7 +308,7 @@ def test_blocked_fwd_from_device_conversion_and_subnormal_terms():
     np.testing.assert_array_equal(host(Xd), Xb)
     np.testing.assert_array_equal(host(eXd).reshape(eX.shape), eX)
     assert (eX.astype(np.int64)[:, :, None] + eW.astype(np.int64).T[None] + 1).min() < -150   # subnormal terms occur
-    want, _ = oracle.dfp16_fwd_f32_blocked(Xb, eX, Wb, eW, S=ops.dfp16_f32_splits(M, K, N, FWD))
+    want, _ = oracle.dfp16_fwd_f32_blocked(Xb, eX, Wb, eW, S=_default_S(M, K, N, FWD))
     Y = torch.empty((M, N), dtype=torch.float32, device=dev())
     ws = torch.empty(ops.dfp16_f32_workspace_bytes(M, K, N, FWD), dtype=torch.uint8, device=dev())
     ops.dfp16_gemm_fwd_f32_blocked(Xd, eXd, Wd, eWd, Y, ws)

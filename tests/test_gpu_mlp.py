@@ -18,7 +18,7 @@ pytestmark = pytest.mark.gpu
 def test_mlp_training_matches_oracle(B, sizes, nsteps, moves):
     d = ionn_synth.mlp(B=B, sizes=sizes, seed=0)
     Wo, recs = osteps.mlp_train(d["X"], d["labels"], d["Ws"], nsteps)
-    m = steps.MLP.make([to_dev(w) for w in d["Ws"]], B)
+    m = steps.MLP.make([to_dev(w) for w in d["Ws"]], B, with_gq=True)
     X, lab = to_dev(d["X"]), to_dev(d["labels"])
     for t in range(nsteps):
         m.step(X, lab)
@@ -26,6 +26,12 @@ def test_mlp_training_matches_oracle(B, sizes, nsteps, moves):
         want = {k: recs[t][k] for k in ("s_fwd", "s_err", "s_dgrad", "s_upd")}
         say("step", t, got)
         assert got == want, f"step {t}"
+        # every layer's weight gradient and its quantised form, every step:
+        # at full size the weights cannot move (each weight shift >= 9), so
+        # the update is checked through G and Gq
+        for l in range(len(sizes) - 1):
+            np.testing.assert_array_equal(host(m.G[l]), recs[t]["G"][l], err_msg=f"step {t} G{l}")
+            np.testing.assert_array_equal(host(m.Gq[l]), recs[t]["Gq"][l], err_msg=f"step {t} Gq{l}")
         if t == nsteps - 1:
             for l in range(len(sizes) - 1):
                 np.testing.assert_array_equal(host(m.acts[l + 1]), recs[t]["acts"][l + 1])

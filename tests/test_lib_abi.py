@@ -102,6 +102,16 @@ def test_conv_validation():
     assert lib.int_conv_fwd(FAKE, FAKE, FAKE, ctypes.byref(d), None, None) == SHAPE
     d = _desc()
     assert lib.int_conv_fwd(FAKE_ODD, FAKE, FAKE, ctypes.byref(d), None, None) == ALIGN
+    # descriptors whose element counts overflow 64 bits when multiplied out
+    # (2^20 x 2^20 x 2^20 x 2^20) or wrap to a small value are refused, not
+    # accepted as empty
+    for kw in (dict(N=1 << 20, H=1 << 20, W=1 << 20, Cin=1 << 20, Cout=16),
+               dict(N=1 << 40, H=1 << 24, W=1 << 24, Cin=16, Cout=16),
+               dict(N=1 << 31, H=1, W=1, Cin=1, Cout=1),
+               dict(N=1 << 16, H=1 << 16, W=1, Cin=16, Cout=16)):
+        d = _desc(**kw)
+        for f in (lib.int_conv_fwd, lib.int_conv_dgrad):
+            assert f(FAKE, FAKE, FAKE, ctypes.byref(d), None, None) == SHAPE, kw
 
 
 def test_dfp16_validation():

@@ -257,3 +257,21 @@ def test_linear_step_config1_properties():
     assert r["ws"] == max(0, r["s"] - 2)
     assert r["s_d"] == oracle.niti_shift(oracle.absmax(r["dX32"]), 7)
     assert (r["W_new"] != d["W"]).any()   # the small config moves the weights
+
+
+@pytest.mark.parametrize("case", ["STEP-1", "STEP-2"])
+def test_conv_step_golden(case):
+    """The oracle's whole conv step (forward + requantisation, dgrad +
+    requantisation, wgrad + NITI update) on hand-worked cases."""
+    from oracle import steps as osteps
+    with open(os.path.join(GOLD, "conv_step_cases.json")) as f:
+        c = json.load(f)[case]
+    img = lambda k: np.array(c[k], np.int8).reshape(1, 3, 3, 1)
+    W = np.array(c["W"], np.int8).reshape(1, 3, 3, 1)
+    r = osteps.conv_step(img("X"), W, img("dY"))
+    np.testing.assert_array_equal(r["y8"].reshape(3, 3), c["y8"])
+    np.testing.assert_array_equal(r["dx8"].reshape(3, 3), c["dx8"])
+    np.testing.assert_array_equal(r["G"].reshape(3, 3), c["G"])
+    np.testing.assert_array_equal(r["Gq"].reshape(3, 3), c["Gq"])
+    np.testing.assert_array_equal(r["W_new"].reshape(3, 3), c["W_new"])
+    assert (r["s_y"], r["s_dx"], r["s"], r["ws"]) == (c["s_y"], c["s_dx"], c["s"], c["ws"])

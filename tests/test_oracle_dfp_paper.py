@@ -259,3 +259,44 @@ def test_sgd_update_and_copy():
     t = Fraction(float(lr)) * Fraction(float(g))
     t32 = Fraction(_f32(float(t)))
     assert Fraction(float(W2[0])) == Fraction(_f32(float(Fraction(float(w)) - t32)))
+
+
+# ---- the single-output form and the default order ---------------------------
+
+@pytest.mark.parametrize("role", ["fwd", "dgrad", "wgrad"])
+def test_f32_single_output_equals_full_contraction(role):
+    """dfp16_f32_at (the full-size sampled checker) against the whole-tensor
+    contraction, every output of ragged shapes, for several range counts and
+    both input shifts: a wrong stride, operand role or range bound in either
+    fails here."""
+    rng = np.random.default_rng({"fwd": 1, "dgrad": 2, "wgrad": 3}[role])
+    full = {"fwd": oracle.dfp16_fwd_f32, "dgrad": oracle.dfp16_dgrad_f32, "wgrad": oracle.dfp16_wgrad_f32}[role]
+    for M, K, N in ((37, 200, 29), (5, 64, 3), (70, 131, 66)):
+        X = rng.integers(-32768, 32768, (M, K)).astype(np.int16)
+        W = rng.integers(-32768, 32768, (N, K)).astype(np.int16)
+        dY = rng.integers(-32768, 32768, (M, N)).astype(np.int16)
+        A, B = {"fwd": (X, W), "dgrad": (dY, W), "wgrad": (dY, X)}[role]
+        L = {"fwd": K, "dgrad": N, "wgrad": M}[role]
+        nch = -(-L // 64)
+        for S in sorted({1, 2, 3, nch} & set(range(1, nch + 1))):
+            for shift in (0, 1):
+                want, _ = full(A, -30, B, -21, S=S, input_shift=shift)
+                R, C = want.shape
+                got = np.array([[oracle.dfp16_f32_at(role, A, -30, B, -21, r, c, S=S, input_shift=shift)
+                                 for c in range(C)] for r in range(R)], np.float32)
+                np.testing.assert_array_equal(got.view(np.uint32), want.view(np.uint32),
+                                              err_msg=f"{role} {M}x{K}x{N} S={S} shift={shift}")
+
+
+def test_default_split_rule_hand_worked():
+    """The default range count (a function of the shape, reading U35) on
+    hand-worked shapes: the DFP-16 layer M 25088, K 256, N 1024 has 1568
+    forward tiles and 392 dgrad tiles (S = 1) and 16 wgrad tiles over 392
+    chunks (S = min(ceil(256 / 16), 392 // 4) = 16)."""
+    rule = oracle.dfp16_default_splits
+    assert [rule(25088, 256, 1024, r) for r in ("fwd", "dgrad", "wgrad")] == [1, 1, 16]
+    assert rule(128, 64, 128, "wgrad") == 1                 # one chunk: nothing to split
+    assert rule(640, 1024, 128, "fwd") == 4                 # 5 tiles, 16 chunks: min(52, 4)
+    assert rule(64, 4096, 64, "fwd") == 16                  # 1 tile, 64 chunks: min(256, 16)
+    assert rule(256, 512, 384, "fwd") == 2                  # 6 tiles, 8 chunks: min(43, 2)
+    assert rule(256, 512, 384, "dgrad") == 1                # 8 tiles, 6 chunks (< 8)
