@@ -411,6 +411,22 @@ size_t ionn_bias_grad_workspace_bytes(int64_t M, int64_t C);
 int ionn_bias_grad(const int8_t *d, int64_t M, int64_t C, int32_t *gb,
                    void *workspace, size_t workspace_bytes, void *stream);
 
+/* ionn_bias_grad for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same result, with the row-range sums held in a 2 MiB device array of
+ * the library instead of a caller workspace.  Allocates nothing and calls
+ * no allocating routine; each GPU the library runs on holds one such array
+ * until the process ends.  Shapes whose sums need more than 2 MiB
+ * (ionn_bias_grad_workspace_bytes(M, C) > 2 MiB) return IONN_ERR_SHAPE and
+ * enqueue nothing.  All calls on one GPU share its array: calls that
+ * overlap on one GPU (two streams, two threads) race and give unspecified
+ * gb; calls ordered on a stream are independent (every entry a call reads
+ * it has written first).  The stream's device must be the current device or
+ * the stream must belong to it; the array's address is looked up once per
+ * device (IONN_ERR_HIP if that lookup fails). */
+int ionn_bias_grad_noalloc(const int8_t *d, int64_t M, int64_t C, int32_t *gb,
+                           void *stream);
+
 /* NITI update of int32 parameters (the offsets), in place on P: the steps of
  * niti_quantize_update with the last one P[j] = sat32(P[j] - d) (clamped to
  * the int32 range).  *absmax must hold max |G| (e.g. from ionn_absmax_i32).

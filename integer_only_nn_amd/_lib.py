@@ -56,6 +56,7 @@ SIGNATURES = {
     "ionn_oss_requant": (_I, [_P, _P, _P, _P, _I64, _I64, _I, _P, _P]),
     "ionn_bias_grad_workspace_bytes": (ctypes.c_size_t, [_I64, _I64]),
     "ionn_bias_grad": (_I, [_P, _I64, _I64, _P, _P, ctypes.c_size_t, _P]),
+    "ionn_bias_grad_noalloc": (_I, [_P, _I64, _I64, _P, _P]),
     "int_linear_fwd_oss_workspace_bytes": (ctypes.c_size_t, [_I64, _I64, _I64]),
     "int_linear_fwd_oss": (_I, [_P, _P, _P, _P, _P, _I, _P, _I64, _I64, _I64, _P, ctypes.c_size_t, _P]),
     "niti_quantize_update_i32": (_I, [_P, _I64, _P, _I, _I, _P, _P, _P, _P]),

@@ -16,10 +16,16 @@
 // bandwidth).
 #include "common.h"
 
+#include <mutex>
+
 namespace ionn {
 namespace {
 
 constexpr int kInstr = 8;                  // 1 KiB loads per wavefront and iteration
+// Size of the allocation-free offset gradient's device scratch (2 MiB: the
+// row-range sums of up to 2^19 columns x ranges).
+constexpr size_t kBgScratchBytes = size_t(2) << 20;
+constexpr size_t kBgScratchInts = kBgScratchBytes / sizeof(int32_t);
 constexpr int64_t kChunk = 256 * kInstr;   // int32 elements per wavefront and iteration
 
 unsigned stream_blocks(int64_t n) {
@@ -191,6 +197,62 @@ __global__ __launch_bounds__(256) void update_i32_kernel(const int32_t *__restri
 }  // namespace
 }  // namespace ionn
 
+// Device scratch of ionn_bias_grad_noalloc: the row-range sums of the offset
+// gradient, for callers that cannot allocate.  One copy per GPU, held until
+// the process ends.  In host code `scratch` only names the symbol; its
+// device address comes from hipGetSymbolAddress (bg_scratch) and is what
+// the kernels receive.
+static __device__ __align__(256) int32_t scratch[ionn::kBgScratchInts];
+
+namespace ionn {
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+int32_t *g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on the GPU that owns `st` (the current
+// device for the null stream), looked up once per device with that device
+// current.
+int bg_scratch(hipStream_t st, int32_t **out) {
+    int dev = -1;
+    hipError_t e = st ? hipStreamGetDevice(st, &dev) : hipGetDevice(&dev);
+    IONN_REQUIRE(e == hipSuccess && dev >= 0 && dev < kMaxDevices, IONN_ERR_HIP,
+                 "ionn_bias_grad_noalloc: cannot tell the stream's device (%s)", hipGetErrorString(e));
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        int cur = -1;
+        IONN_REQUIRE(hipGetDevice(&cur) == hipSuccess, IONN_ERR_HIP, "ionn_bias_grad_noalloc: hipGetDevice failed");
+        if (cur != dev) IONN_REQUIRE(hipSetDevice(dev) == hipSuccess, IONN_ERR_HIP, "ionn_bias_grad_noalloc: hipSetDevice failed");
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev) (void)hipSetDevice(cur);
+        IONN_REQUIRE(e == hipSuccess && p != nullptr, IONN_ERR_HIP,
+                     "ionn_bias_grad_noalloc: hipGetSymbolAddress(scratch) failed on device %d (%s)", dev,
+                     hipGetErrorString(e));
+        g_scratch_ptr[dev] = static_cast<int32_t *>(p);
+    }
+    *out = g_scratch_ptr[dev];
+    return IONN_OK;
+}
+
+// Both offset-gradient entry points: the row-range sums into part (every
+// entry part[y][c], y < g.gy, c < C, is written before it is read, so the
+// buffer needs no clearing), then their sum into gb.
+int bias_grad_launch(const int8_t *d, int64_t M, int64_t C, int32_t *gb, const BgGrid &g, int32_t *part,
+                     hipStream_t st, const char *name) {
+    IONN_REQUIRE(g.gx <= 0x7fffffff && g.gy <= 65535, IONN_ERR_SHAPE, "%s: grid too large", name);
+    const dim3 grid{unsigned(g.gx), unsigned(g.gy), 1u}, block{64u * BG_WAVES, 1u, 1u};
+    if (g.vec) bias_grad_kernel<true><<<grid, block, 0, st>>>(d, M, C, g.rows, part);
+    else bias_grad_kernel<false><<<grid, block, 0, st>>>(d, M, C, g.rows, part);
+    if (int rc = check_launch(name)) return rc;
+    bias_grad_sum<<<dim3(unsigned((C + 255) / 256)), dim3(256), 0, st>>>(part, g.gy, C, gb);
+    return check_launch(name);
+}
+
+}  // namespace
+}  // namespace ionn
+
 using namespace ionn;
 
 extern "C" {
@@ -240,14 +302,31 @@ int ionn_bias_grad(const int8_t *d, int64_t M, int64_t C, int32_t *gb, void *wor
     const size_t need = size_t(g.gy * C) * sizeof(int32_t);
     IONN_REQUIRE(workspace != nullptr && aligned(workspace, 4) && workspace_bytes >= need, IONN_ERR_WORKSPACE,
                  "ionn_bias_grad: needs a 4-byte aligned workspace of %zu bytes", need);
-    IONN_REQUIRE(g.gx <= 0x7fffffff && g.gy <= 65535, IONN_ERR_SHAPE, "ionn_bias_grad: grid too large");
-    int32_t *part = static_cast<int32_t *>(workspace);
-    const dim3 grid{unsigned(g.gx), unsigned(g.gy), 1u}, block{64u * BG_WAVES, 1u, 1u};
-    if (g.vec) bias_grad_kernel<true><<<grid, block, 0, st>>>(d, M, C, g.rows, part);
-    else bias_grad_kernel<false><<<grid, block, 0, st>>>(d, M, C, g.rows, part);
-    if (int rc = check_launch("ionn_bias_grad")) return rc;
-    bias_grad_sum<<<dim3(unsigned((C + 255) / 256)), dim3(256), 0, st>>>(part, g.gy, C, gb);
-    return check_launch("ionn_bias_grad");
+    return bias_grad_launch(d, M, C, gb, g, static_cast<int32_t *>(workspace), st, "ionn_bias_grad");
+}
+
+int ionn_bias_grad_noalloc(const int8_t *d, int64_t M, int64_t C, int32_t *gb, void *stream) {
+    clear_error();
+    IONN_REQUIRE(M >= 0 && C >= 0 && M <= kMaxDim && C <= kMaxDim && M * C <= kMaxDim, IONN_ERR_SHAPE,
+                 "ionn_bias_grad_noalloc: bad shape M=%lld C=%lld", (long long)M, (long long)C);
+    if (C == 0) return IONN_OK;
+    IONN_REQUIRE(gb != nullptr && (M == 0 || d != nullptr), IONN_ERR_ARG,
+                 "ionn_bias_grad_noalloc: NULL argument");
+    IONN_REQUIRE(aligned(gb, 4), IONN_ERR_ALIGN, "ionn_bias_grad_noalloc: gb must be 4-byte aligned");
+    hipStream_t st = as_stream(stream);
+    if (M == 0) {
+        zero_kernel<<<dim3(unsigned((C + 255) / 256 < 1024 ? (C + 255) / 256 : 1024)), dim3(256), 0, st>>>(gb, C);
+        return check_launch("ionn_bias_grad_noalloc");
+    }
+    const BgGrid g = bg_grid(M, C, C % 16 == 0 && aligned(d, 16));
+    const size_t need = size_t(g.gy * C) * sizeof(int32_t);
+    IONN_REQUIRE(need <= kBgScratchBytes, IONN_ERR_SHAPE,
+                 "ionn_bias_grad_noalloc: M=%lld C=%lld needs %zu bytes of row-range sums, more than the "
+                 "%zu-byte device scratch (use ionn_bias_grad with a workspace)",
+                 (long long)M, (long long)C, need, kBgScratchBytes);
+    int32_t *part = nullptr;
+    if (int rc = bg_scratch(st, &part)) return rc;
+    return bias_grad_launch(d, M, C, gb, g, part, st, "ionn_bias_grad_noalloc");
 }
 
 int niti_quantize_update_i32(const int32_t *G, int64_t n, const uint32_t *absmax, int target_bits, int mu,

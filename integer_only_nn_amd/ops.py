@@ -125,6 +125,13 @@ def ionn_bias_grad_workspace_bytes(M, C):
     return int(lib().ionn_bias_grad_workspace_bytes(int(M), int(C)))
 
 
+def ionn_bias_grad_noalloc(d, gb, stream=None):
+    M, C = d.shape
+    assert gb.numel() == C
+    check(lib().ionn_bias_grad_noalloc(_p(d, i8, name="d"), M, C, _p(gb, i32, name="gb"), _stream(stream)),
+          "ionn_bias_grad_noalloc")
+
+
 def ionn_bias_grad(d, gb, workspace, stream=None):
     M, C = d.shape
     assert gb.numel() == C

@@ -192,3 +192,15 @@ def test_dfp_paper_form_validation():
     assert lib.dfp_from_f32_blocked(FAKE, 0, 100, 64, 16, FAKE, FAKE, None, None) == SHAPE
     assert lib.dfp16_sgd_update(FAKE, P(0x1004), 8, ctypes.c_float(0.1), FAKE, FAKE, None, FAKE, cw, None) == ALIGN
     assert lib.dfp16_sgd_update(FAKE, FAKE, 8, ctypes.c_float(0.1), FAKE, FAKE, None, FAKE, 0, None) == WS
+
+
+def test_bias_grad_noalloc_refuses_sizes_beyond_its_scratch():
+    # 64 rows x 2^20 columns need 4 MiB of row-range sums, over the 2 MiB
+    # device scratch: refused before any HIP call
+    assert lib.ionn_bias_grad_workspace_bytes(64, 1 << 20) > 2 << 20
+    assert lib.ionn_bias_grad_noalloc(FAKE, 64, 1 << 20, FAKE, None) == SHAPE
+    assert "scratch" in _err()
+    assert lib.ionn_bias_grad_noalloc(FAKE, -1, 16, FAKE, None) == SHAPE
+    assert lib.ionn_bias_grad_noalloc(None, 4, 16, FAKE, None) == ARG
+    assert lib.ionn_bias_grad_noalloc(FAKE, 4, 16, FAKE_ODD, None) == ALIGN
+    assert lib.ionn_bias_grad_noalloc(None, 4, 0, None, None) == OK
