@@ -185,24 +185,38 @@ int int_conv_dgrad(const int8_t *dY, const int8_t *Wt, int32_t *dX,
  * in ("Integer On-Device Training: Overview", section 3, steps 1-3 and the
  * ReLU of the Conv2D layer, section 7): Y8 = sat8(rhu(Y, s)), then
  * max(Y8, 0) if relu, with s = max(0, bitlen(max|Y|) - target_bits) and Y
- * the int32 sum of int_conv_fwd.  Y is never stored: the contraction runs
- * twice, first for max|Y| only, then for the int8 output.  Y8: int8
- * [N][H][W][Cout] (written).  absmax_Y (device, 4-byte aligned, required):
- * must hold 0 on entry (ionn_fill_u32); receives max|Y|.  shift_out
- * (nullable, device): receives s.  Only 3x3 / stride 1 / pad 1 with 64 input
- * and 64 output channels and a width whose halo fits (as the int32 fast
- * path); other geometries return IONN_ERR_UNSUPPORTED and take int_conv_fwd and
- * niti_quantize.  X and Wt 16-byte aligned, Y8 4-byte aligned. */
+ * the int32 sum of int_conv_fwd.  Y is never stored.
+ *  - With a workspace (int_conv_requant_workspace_bytes(desc) bytes, 16-byte
+ *    aligned, clobbered; IONN_ERR_WORKSPACE if smaller) and target_bits <= 7:
+ *    one contraction pass stores, per block of 32 pixels x 64 channels,
+ *    f = asr(Y, s_b) as int8 with the block's own shift s_b (it always fits
+ *    int8) and bit s_b - 1 of every Y (its rounding bit) in the workspace;
+ *    a streaming pass over Y8 then applies the tensor's shift s >= s_b:
+ *    rhu(Y, s) = f + bit when s = s_b, rhu(f, s - s_b) otherwise.  Y8 must
+ *    then be 16-byte aligned.
+ *  - Without one (workspace NULL), or with target_bits > 7: the contraction
+ *    runs twice, first for max|Y| only, then for the int8 output.
+ * Same bits either way.  Y8: int8 [N][H][W][Cout] (written).  absmax_Y
+ * (device, 4-byte aligned, required): must hold 0 on entry (ionn_fill_u32);
+ * receives max|Y|.  shift_out (nullable, device): receives s.  Only 3x3 /
+ * stride 1 / pad 1 with 64 input and 64 output channels and a width whose
+ * halo fits (as the int32 fast path); other geometries return
+ * IONN_ERR_UNSUPPORTED and take int_conv_fwd and niti_quantize.  X and Wt
+ * 16-byte aligned, Y8 4-byte aligned. */
+size_t int_conv_requant_workspace_bytes(const ionn_conv_desc *desc);
 int int_conv_fwd_requant(const int8_t *X, const int8_t *Wt, int8_t *Y8,
                          const ionn_conv_desc *desc, int target_bits, int relu,
-                         uint32_t *absmax_Y, int32_t *shift_out, void *stream);
+                         uint32_t *absmax_Y, int32_t *shift_out,
+                         void *workspace, size_t workspace_bytes, void *stream);
 
 /* The same for delta propagation (section 3, the propagated-delta note:
  * target_bits = 7): dX8 = sat8(rhu(dX, s)) with dX the int32 sum of
- * int_conv_dgrad, computed twice and never stored. */
+ * int_conv_dgrad, never stored; one pass plus the streaming pass with a
+ * workspace, two contraction passes without. */
 int int_conv_dgrad_requant(const int8_t *dY, const int8_t *Wt, int8_t *dX8,
                            const ionn_conv_desc *desc, int target_bits,
-                           uint32_t *absmax_dX, int32_t *shift_out, void *stream);
+                           uint32_t *absmax_dX, int32_t *shift_out,
+                           void *workspace, size_t workspace_bytes, void *stream);
 
 /* Device workspace (bytes) that lets int_conv_wgrad take its fast path for
  * this geometry (64 input and 64 output channels, W up to about 100): one

@@ -30,8 +30,9 @@ SIGNATURES = {
     "int_output_error": (_I, [_P, _P, _I64, _I64, _I, _P, _P, _P]),
     "int_conv_fwd": (_I, [_P, _P, _P, _P, _P, _P]),
     "int_conv_dgrad": (_I, [_P, _P, _P, _P, _P, _P]),
-    "int_conv_fwd_requant": (_I, [_P, _P, _P, _P, _I, _I, _P, _P, _P]),
-    "int_conv_dgrad_requant": (_I, [_P, _P, _P, _P, _I, _P, _P, _P]),
+    "int_conv_requant_workspace_bytes": (ctypes.c_size_t, [_P]),
+    "int_conv_fwd_requant": (_I, [_P, _P, _P, _P, _I, _I, _P, _P, _P, ctypes.c_size_t, _P]),
+    "int_conv_dgrad_requant": (_I, [_P, _P, _P, _P, _I, _P, _P, _P, ctypes.c_size_t, _P]),
     "int_conv_wgrad_workspace_bytes": (ctypes.c_size_t, [_P]),
     "int_conv_wgrad": (_I, [_P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "dfp16_workspace_bytes": (ctypes.c_size_t, [_I64, _I64, _I64, _I]),

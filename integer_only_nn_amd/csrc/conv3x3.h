@@ -104,7 +104,29 @@ enum Mode : int {
     MAXONLY = 1,  // only max-combine max|acc| into *absmax (no output)
     REQUANT = 2,  // store int8 sat8(rhu(acc, s)) (ReLU optional), s from the
                   // finished *absmax and target_bits; block 0 writes s
+    PARTIAL = 3,  // one pass of the requantisation (target_bits <= 7): each
+                  // wavefront's 32 x 64 block is stored as int8
+                  // f = asr(acc, s_b) with its own shift s_b = max(0,
+                  // bitlen(max |acc| of the block) - target_bits), which
+                  // always fits int8, plus bit s_b - 1 of every acc (the
+                  // rounding bit) and s_b; max |acc| is max-combined into
+                  // *absmax.  conv3x3_requant_fix then finishes every value
+                  // with the tensor's shift s >= s_b:
+                  // rhu(acc, s) = f + bit when s = s_b, rhu(f, s - s_b) else.
 };
+
+// Weight row loaded by fragment lane i (0..31) of a 32-channel block in
+// PARTIAL mode: output row i of the 32 x 32 product is channel
+// 16 ((i >> 2) & 1) + 4 (i >> 3) + (i & 3), so the 16 values a lane holds
+// (rows 8 q + 4 (lane / 32) + j, q, j = 0..3) are the 16 consecutive
+// channels 16 (lane / 32) .. + 15 of the block and leave in one 16-byte store.
+__host__ __device__ constexpr int part_row(int i) { return 16 * ((i >> 2) & 1) + 4 * (i >> 3) + (i & 3); }
+
+// Vector-memory stores per wavefront and tile of each mode (the halo waits
+// count them).
+__host__ __device__ constexpr int stores_per_tile(int mode) {
+    return mode == MAXONLY ? 0 : (mode == PARTIAL ? 4 : 8);
+}
 
 template <bool DGRAD, int MODE = STORE32>
 __global__ __launch_bounds__(NTF, 1) void conv3x3_kernel(const int8_t *__restrict__ in,
@@ -112,7 +134,9 @@ __global__ __launch_bounds__(NTF, 1) void conv3x3_kernel(const int8_t *__restric
                                                          void *__restrict__ out_any, int N, int H,
                                                          int W, uint32_t *__restrict__ absmax,
                                                          int target_bits = 0, int relu = 0,
-                                                         int32_t *__restrict__ shift_out = nullptr) {
+                                                         int32_t *__restrict__ shift_out = nullptr,
+                                                         uint32_t *__restrict__ bits_out = nullptr,
+                                                         int32_t *__restrict__ shifts_blk = nullptr) {
     __shared__ __attribute__((aligned(1024))) int8_t halo[NB][HBUF];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -132,8 +156,9 @@ __global__ __launch_bounds__(NTF, 1) void conv3x3_kernel(const int8_t *__restric
         for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
-                wf[cb][ks] = *reinterpret_cast<const v4i *>(wgt + (cb * 32 + (lane & 31)) * 576 + ks * 32 +
-                                                            16 * (lane >> 5));
+                wf[cb][ks] = *reinterpret_cast<const v4i *>(
+                    wgt + (cb * 32 + (MODE == PARTIAL ? part_row(lane & 31) : (lane & 31))) * 576 + ks * 32 +
+                    16 * (lane >> 5));
     } else {
         // B[ci][tap*64 + co] = W[co][8 - tap][ci].  W is staged in LDS as stored
         // (rows of 576 bytes per co) and every fragment comes out with two
@@ -142,8 +167,19 @@ __global__ __launch_bounds__(NTF, 1) void conv3x3_kernel(const int8_t *__restric
         // W[co0 .. co0+7][8 - tap][ci0 + j], eight consecutive k of row ci0 + j.
         typedef __attribute__((address_space(3))) v2i lds_v2i_t;
         int8_t *stage = &halo[0][0];
-        for (int i = tid; i < 64 * 576 / 16; i += NTF)
-            *reinterpret_cast<v4i *>(stage + 16 * i) = *reinterpret_cast<const v4i *>(wgt + 16 * i);
+        if (MODE == PARTIAL) {
+            // the channels of every 32-byte block in the order part_row
+            // reads them: staged dword b holds channel dword 4 (b & 1) + b / 2
+            for (int i = tid; i < 64 * 576 / 32; i += NTF) {
+                const v4i x = *reinterpret_cast<const v4i *>(wgt + 32 * i);
+                const v4i y = *reinterpret_cast<const v4i *>(wgt + 32 * i + 16);
+                *reinterpret_cast<v4i *>(stage + 32 * i) = v4i{x[0], y[0], x[1], y[1]};
+                *reinterpret_cast<v4i *>(stage + 32 * i + 16) = v4i{x[2], y[2], x[3], y[3]};
+            }
+        } else {
+            for (int i = tid; i < 64 * 576 / 16; i += NTF)
+                *reinterpret_cast<v4i *>(stage + 16 * i) = *reinterpret_cast<const v4i *>(wgt + 16 * i);
+        }
         __syncthreads();
         const int g = lane >> 4, i = lane & 15;
 #pragma unroll
@@ -204,7 +240,7 @@ __global__ __launch_bounds__(NTF, 1) void conv3x3_kernel(const int8_t *__restric
 
     // Output through a buffer resource as well (see the epilogue): int32 or,
     // requantised, int8 elements.
-    constexpr int OB = MODE == REQUANT ? 1 : 4;
+    constexpr int OB = MODE == REQUANT || MODE == PARTIAL ? 1 : 4;
     const __amdgpu_buffer_rsrc_t orsrc =
         __builtin_amdgcn_make_buffer_rsrc(out_any, 0, int(int64_t(N) * HW * C * OB), 0x00020000);
     // requantisation shift from the finished max |acc| (NITI steps 2-3)
@@ -213,6 +249,14 @@ __global__ __launch_bounds__(NTF, 1) void conv3x3_kernel(const int8_t *__restric
         rs = __builtin_amdgcn_readfirstlane(niti_shift(*absmax, target_bits));
         if (blockIdx.x == 0 && tid == 0 && shift_out) *shift_out = rs;
     }
+
+    // PARTIAL side outputs: one rounding-bit word per lane and one shift per
+    // wavefront and tile
+    const __amdgpu_buffer_rsrc_t brsrc =
+        __builtin_amdgcn_make_buffer_rsrc(bits_out, 0, MODE == PARTIAL ? ntiles * 8 * 64 * 4 : 0, 0x00020000);
+    const __amdgpu_buffer_rsrc_t srsrc =
+        __builtin_amdgcn_make_buffer_rsrc(shifts_blk, 0, MODE == PARTIAL ? ntiles * 8 * 4 : 0, 0x00020000);
+    uint32_t gmax = 0;
 
     int t = blockIdx.x;
     fetch(t, 0);
@@ -223,7 +267,7 @@ __global__ __launch_bounds__(NTF, 1) void conv3x3_kernel(const int8_t *__restric
     for (int k = 0; t < ntiles; t += G, ++k) {
         // This tile's loads are done when at most the next tile's (NI) and the
         // previous tile's stores (8, none without output) are still outstanding.
-        if (k == 0 || MODE == MAXONLY) wait_vm<NI>(); else wait_vm<NI + 8>();
+        if (k == 0) wait_vm<NI>(); else wait_vm<NI + stores_per_tile(MODE)>();
         __syncthreads();
         fetch(t + 2 * G, b == 0 ? 2 : b - 1);
 
@@ -287,8 +331,43 @@ __global__ __launch_bounds__(NTF, 1) void conv3x3_kernel(const int8_t *__restric
                                                 rq(acc[cb][4 * q + 3]));
                     __builtin_amdgcn_raw_buffer_store_b32(w, orsrc, int(obase + uint32_t(cb * 32 + 8 * q)), 0, 0);
                 }
+        } else if (MODE == PARTIAL) {
+            // this wavefront's max |acc| over its valid pixels, its shift, and
+            // the int8 f = asr(acc, sb) with the rounding bits
+            int32_t bmax = INT32_MIN, bmin = INT32_MAX;
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+                for (int v = 0; v < 16; v += 2) {
+                    bmax = max(bmax, max(acc[cb][v], acc[cb][v + 1]));
+                    bmin = min(bmin, min(acc[cb][v], acc[cb][v + 1]));
+                }
+            const uint32_t bm = wave_max_u32(pl < valid ? max(abs_u32(bmax), abs_u32(bmin)) : 0u);
+            gmax = max(gmax, bm);
+            const int sb = __builtin_amdgcn_readfirstlane(niti_shift(bm, target_bits));
+            const int sh1 = sb > 0 ? sb - 1 : 0;
+            const uint32_t one = sb > 0 ? 1u : 0u;
+            uint32_t bits = 0;
+            const uint32_t ob = pl < valid ? uint32_t((n * HW + p0 + pl) * C + 16 * (lane >> 5)) : OOB;
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb) {
+                v4i f;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    f[q] = int(pack4_u8(acc[cb][4 * q] >> sb, acc[cb][4 * q + 1] >> sb, acc[cb][4 * q + 2] >> sb,
+                                        acc[cb][4 * q + 3] >> sb));
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        bits |= ((uint32_t(acc[cb][4 * q + j]) >> sh1) & one) << (16 * cb + 4 * q + j);
+                }
+                __builtin_amdgcn_raw_buffer_store_b128(f, orsrc, int(ob + uint32_t(32 * cb)), 0, 0);
+            }
+            const int blk = t * 8 + wave;
+            __builtin_amdgcn_raw_buffer_store_b32(bits, brsrc, int(uint32_t(blk * 64 + lane) * 4u), 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(uint32_t(sb), srsrc, int(lane == 0 ? uint32_t(blk) * 4u : OOB),
+                                                  0, 0);
         }
-        if (MODE != REQUANT && pl < valid) {
+        if (MODE != REQUANT && MODE != PARTIAL && pl < valid) {
 #pragma unroll
             for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
@@ -301,10 +380,48 @@ __global__ __launch_bounds__(NTF, 1) void conv3x3_kernel(const int8_t *__restric
     }
     wait_vm<0>();  // the zero-fill loads past the last tile land before the workgroup ends
 
-    if (MODE != REQUANT && absmax) {
+    if (MODE == PARTIAL) {
+        if (lane == 0) publish_max_u32(absmax, gmax);
+    } else if (MODE != REQUANT && absmax) {
         uint32_t amax = vmax >= vmin ? max(abs_u32(vmax), abs_u32(vmin)) : 0u;
         amax = wave_max_u32(amax);
         if (lane == 0) publish_max_u32(absmax, amax);
+    }
+}
+
+// Finishes a PARTIAL pass: every 16 bytes of the int8 tensor (pixel P,
+// channels 16 q4 .. + 15) take their block's shift sb and rounding bits and
+// become sat8(rhu(acc, s)) (then max(., 0) with relu), s = the tensor's
+// shift from the finished *absmax; block 0 writes s.  In place.  A pixel's
+// block is (tile, wavefront) = (n tpi + p / 256, (p / 32) % 8) and its lane
+// p % 32 (channels 0-15, 32-47) or p % 32 + 32 (16-31, 48-63).
+__global__ __launch_bounds__(256) void conv3x3_requant_fix(int8_t *__restrict__ y8,
+                                                           const uint32_t *__restrict__ bits,
+                                                           const int32_t *__restrict__ shifts_blk,
+                                                           const uint32_t *__restrict__ absmax, int target_bits,
+                                                           int relu, uint32_t HW, uint32_t tpi, uint32_t nchunks,
+                                                           int32_t *__restrict__ shift_out) {
+    const int s = niti_shift(*absmax, target_bits);
+    if (blockIdx.x == 0 && threadIdx.x == 0 && shift_out) *shift_out = s;
+    for (uint32_t c = blockIdx.x * 256u + threadIdx.x; c < nchunks; c += gridDim.x * 256u) {
+        const uint32_t P = c >> 2, q4 = c & 3u;
+        const uint32_t n = P / HW, p = P - n * HW;
+        const uint32_t blk = (n * tpi + (p >> 8)) * 8u + ((p >> 5) & 7u);
+        const uint32_t w = bits[blk * 64u + (p & 31u) + 32u * (q4 & 1u)] >> (16u * (q4 >> 1));
+        const int d = s - shifts_blk[blk];
+        v4i v = *reinterpret_cast<const v4i *>(y8 + 16ull * c);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            int32_t o[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int32_t f = int32_t(int8_t(uint8_t(uint32_t(v[q]) >> (8 * j))));
+                int32_t r = d == 0 ? sat8(f + int32_t((w >> (4 * q + j)) & 1u)) : rhu(f, d);
+                o[j] = relu ? max(r, 0) : r;
+            }
+            v[q] = int(pack4_u8(o[0], o[1], o[2], o[3]));
+        }
+        *reinterpret_cast<v4i *>(y8 + 16ull * c) = v;
     }
 }
 

@@ -454,13 +454,23 @@ unsigned c3_grid(const ionn_conv_desc *d) {
 using namespace ionn;
 using namespace ionn::gemm;
 
-// Two passes of the 64-channel halo-tiled kernel with the NITI requantisation
-// fused: max |acc| only, then the contraction again with int8 output.  The
-// int32 accumulator is never stored.
+// Workspace of the one-pass fused requantisation: a rounding-bit word per
+// lane and a shift per wavefront, for every tile.
+size_t requant_ws_bytes(const ionn_conv_desc *d) {
+    const int64_t tiles = d->N * ((d->H * d->W + c3::TP - 1) / c3::TP);
+    return size_t(tiles) * 8 * (64 * 4 + 4);
+}
+
+// The 64-channel halo-tiled kernel with the NITI requantisation fused; the
+// int32 accumulator is never stored.  With a workspace and target_bits <= 7:
+// one contraction pass storing each wavefront block's int8 asr(acc, s_b)
+// with its rounding bits, then a streaming pass that applies the tensor's
+// shift (conv3x3.h, PARTIAL).  Otherwise two contraction passes: max |acc|
+// only, then the contraction again with int8 output.
 template <bool DGRAD>
 int conv_requant(const int8_t *in, const int8_t *Wt, int8_t *out8, const ionn_conv_desc *desc,
-                 int target_bits, int relu, uint32_t *absmax, int32_t *shift_out, void *stream,
-                 const char *name) {
+                 int target_bits, int relu, uint32_t *absmax, int32_t *shift_out, void *workspace,
+                 size_t workspace_bytes, void *stream, const char *name) {
     clear_error();
     if (int rc = check_desc(desc, name)) return rc;
     IONN_REQUIRE(geom33(desc) && desc->Cin == 64 && desc->Cout == 64 && c3::fits_fd(desc->W, desc->N * desc->H * desc->W * 64),
@@ -481,6 +491,25 @@ int conv_requant(const int8_t *in, const int8_t *Wt, int8_t *out8, const ionn_co
         return shift_out ? ionn_fill_u32(reinterpret_cast<uint32_t *>(shift_out), 1, 0, stream) : IONN_OK;
     const dim3 grid(c3_grid(desc)), block(c3::NTF);
     const int N = int(desc->N), H = int(desc->H), W = int(desc->W);
+    if (workspace != nullptr && target_bits <= 7) {
+        const size_t need = requant_ws_bytes(desc);
+        IONN_REQUIRE(workspace_bytes >= need && aligned(workspace, 16) && aligned(out8, 16), IONN_ERR_WORKSPACE,
+                     "%s: the one-pass path needs a 16-byte aligned workspace of %zu bytes and a 16-byte aligned "
+                     "output", name, need);
+        const int64_t tiles = desc->N * ((desc->H * desc->W + c3::TP - 1) / c3::TP);
+        uint32_t *bits = static_cast<uint32_t *>(workspace);
+        int32_t *sblk = reinterpret_cast<int32_t *>(bits + tiles * 8 * 64);
+        c3::conv3x3_kernel<DGRAD, c3::PARTIAL><<<grid, block, 0, st>>>(in, Wt, out8, N, H, W, absmax, target_bits,
+                                                                       relu, nullptr, bits, sblk);
+        if (int rc = check_launch(name)) return rc;
+        const int64_t nchunks = npix * 4;
+        int64_t fb = (nchunks + 255) / 256;
+        if (fb > 2048) fb = 2048;
+        c3::conv3x3_requant_fix<<<dim3(unsigned(fb)), dim3(256), 0, st>>>(
+            out8, bits, sblk, absmax, target_bits, relu, uint32_t(desc->H * desc->W),
+            uint32_t((desc->H * desc->W + c3::TP - 1) / c3::TP), uint32_t(nchunks), shift_out);
+        return check_launch(name);
+    }
     c3::conv3x3_kernel<DGRAD, c3::MAXONLY><<<grid, block, 0, st>>>(in, Wt, nullptr, N, H, W, absmax);
     if (int rc = check_launch(name)) return rc;
     c3::conv3x3_kernel<DGRAD, c3::REQUANT><<<grid, block, 0, st>>>(in, Wt, out8, N, H, W, absmax, target_bits,
@@ -590,16 +619,28 @@ int int_conv_dgrad(const int8_t *dY, const int8_t *Wt, int32_t *dX, const ionn_c
     return check_launch("int_conv_dgrad");
 }
 
+size_t int_conv_requant_workspace_bytes(const ionn_conv_desc *desc) {
+    if (desc == nullptr || desc->N < 0 || desc->H < 0 || desc->W < 0 || desc->N > kMaxDim ||
+        desc->H > kMaxDim || desc->W > kMaxDim || desc->stride != 1 || desc->dilation != 1 ||
+        desc->groups != 1 || !geom33(desc) || desc->Cin != 64 || desc->Cout != 64 ||
+        desc->H * desc->W > kMaxDim / (desc->N > 0 ? desc->N : 1) ||
+        !c3::fits_fd(desc->W, desc->N * desc->H * desc->W * 64))
+        return 0;
+    return requant_ws_bytes(desc);
+}
+
 int int_conv_fwd_requant(const int8_t *X, const int8_t *Wt, int8_t *Y8, const ionn_conv_desc *desc,
-                         int target_bits, int relu, uint32_t *absmax_Y, int32_t *shift_out, void *stream) {
-    return conv_requant<false>(X, Wt, Y8, desc, target_bits, relu, absmax_Y, shift_out, stream,
-                               "int_conv_fwd_requant");
+                         int target_bits, int relu, uint32_t *absmax_Y, int32_t *shift_out, void *workspace,
+                         size_t workspace_bytes, void *stream) {
+    return conv_requant<false>(X, Wt, Y8, desc, target_bits, relu, absmax_Y, shift_out, workspace,
+                               workspace_bytes, stream, "int_conv_fwd_requant");
 }
 
 int int_conv_dgrad_requant(const int8_t *dY, const int8_t *Wt, int8_t *dX8, const ionn_conv_desc *desc,
-                           int target_bits, uint32_t *absmax_dX, int32_t *shift_out, void *stream) {
-    return conv_requant<true>(dY, Wt, dX8, desc, target_bits, 0, absmax_dX, shift_out, stream,
-                              "int_conv_dgrad_requant");
+                           int target_bits, uint32_t *absmax_dX, int32_t *shift_out, void *workspace,
+                           size_t workspace_bytes, void *stream) {
+    return conv_requant<true>(dY, Wt, dX8, desc, target_bits, 0, absmax_dX, shift_out, workspace,
+                              workspace_bytes, stream, "int_conv_dgrad_requant");
 }
 
 size_t int_conv_wgrad_workspace_bytes(const ionn_conv_desc *desc) {

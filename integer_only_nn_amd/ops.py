@@ -239,19 +239,30 @@ def int_conv_dgrad(dY, Wt, dX, desc, absmax_dX=None, stream=None):
 
 
 
-def int_conv_fwd_requant(X, Wt, Y8, desc, target_bits, relu, absmax_Y, shift_out=None, stream=None):
+def int_conv_requant_workspace_bytes(desc):
+    return int(lib().int_conv_requant_workspace_bytes(ctypes.byref(desc)))
+
+
+def _ws(workspace):
+    return (_p(workspace, None, name="workspace"),
+            workspace.numel() * workspace.element_size() if workspace is not None else 0)
+
+
+def int_conv_fwd_requant(X, Wt, Y8, desc, target_bits, relu, absmax_Y, shift_out=None, workspace=None,
+                         stream=None):
     nx, nw, ny = _conv_numels(desc)
     check(lib().int_conv_fwd_requant(_p(X, i8, nx, "X"), _p(Wt, i8, nw, "W"), _p(Y8, i8, ny, "Y8"),
                                      ctypes.byref(desc), int(target_bits), int(bool(relu)),
                                      _p(absmax_Y, u32, 1, "absmax_Y"), _p(shift_out, i32, 1, "shift_out"),
-                                     _stream(stream)), "int_conv_fwd_requant")
+                                     *_ws(workspace), _stream(stream)), "int_conv_fwd_requant")
 
 
-def int_conv_dgrad_requant(dY, Wt, dX8, desc, target_bits, absmax_dX, shift_out=None, stream=None):
+def int_conv_dgrad_requant(dY, Wt, dX8, desc, target_bits, absmax_dX, shift_out=None, workspace=None,
+                           stream=None):
     nx, nw, ny = _conv_numels(desc)
     check(lib().int_conv_dgrad_requant(_p(dY, i8, ny, "dY"), _p(Wt, i8, nw, "W"), _p(dX8, i8, nx, "dX8"),
                                        ctypes.byref(desc), int(target_bits), _p(absmax_dX, u32, 1, "absmax_dX"),
-                                       _p(shift_out, i32, 1, "shift_out"), _stream(stream)),
+                                       _p(shift_out, i32, 1, "shift_out"), *_ws(workspace), _stream(stream)),
           "int_conv_dgrad_requant")
 
 

@@ -161,16 +161,20 @@ class ConvStepBuffers:
     scal: torch.Tensor   # [absmax Y, dX, G, s_y, s_dx, s, ws]
     gq: Optional[torch.Tensor] = None
     ws: Optional[torch.Tensor] = None   # weight-gradient workspace (None: no fast path)
+    rws: Optional[torch.Tensor] = None  # one-pass requantisation workspace (None: two passes)
 
     @staticmethod
-    def make(N, H, W, Cin, Cout, device, with_gq=False):
-        wsb = ops.int_conv_wgrad_workspace_bytes(ops.conv_desc(N, H, W, Cin, Cout))
+    def make(N, H, W, Cin, Cout, device, with_gq=False, one_pass=True):
+        d = ops.conv_desc(N, H, W, Cin, Cout)
+        wsb = ops.int_conv_wgrad_workspace_bytes(d)
+        rwb = ops.int_conv_requant_workspace_bytes(d) if one_pass else 0
         return ConvStepBuffers(_i32(N, H, W, Cout, device=device), _i8(N, H, W, Cout, device=device),
                                _i32(N, H, W, Cin, device=device), _i8(N, H, W, Cin, device=device),
                                _i32(Cout, 3, 3, Cin, device=device),
                                torch.zeros(8, dtype=torch.int32, device=device),
                                _i32(Cout, 3, 3, Cin, device=device) if with_gq else None,
-                               torch.empty(wsb, dtype=torch.uint8, device=device) if wsb else None)
+                               torch.empty(wsb, dtype=torch.uint8, device=device) if wsb else None,
+                               torch.empty(rwb, dtype=torch.uint8, device=device) if rwb else None)
 
 
 def conv_step(X, Wt, dY, buf: ConvStepBuffers, tb_a=TB_DELTA, tb_d=TB_DELTA, tb_w=TB_WEIGHT,
@@ -194,14 +198,17 @@ def conv_step_fused(X, Wt, dY, buf: ConvStepBuffers, tb_a=TB_DELTA, tb_d=TB_DELT
     """The same step with the requantisation fused into the contractions
     (64 -> 64 channels): y8, dx8, G, the update and every shift as in
     conv_step; buf.Y and buf.dX are not written (the int32 sums are never
-    stored)."""
+    stored).  With buf.rws each requantising contraction is one pass plus a
+    streaming pass over its int8 output, else two contraction passes."""
     N, H, W_, Cin = X.shape
     Cout = Wt.shape[0]
     d = ops.conv_desc(N, H, W_, Cin, Cout)
     s = buf.scal
     ops.ionn_fill_u32(s[0:3], 0, stream=stream)
-    ops.int_conv_fwd_requant(X, Wt, buf.y8, d, tb_a, False, s[0:1], shift_out=s[3:4], stream=stream)
-    ops.int_conv_dgrad_requant(dY, Wt, buf.dx8, d, tb_d, s[1:2], shift_out=s[4:5], stream=stream)
+    ops.int_conv_fwd_requant(X, Wt, buf.y8, d, tb_a, False, s[0:1], shift_out=s[3:4], workspace=buf.rws,
+                             stream=stream)
+    ops.int_conv_dgrad_requant(dY, Wt, buf.dx8, d, tb_d, s[1:2], shift_out=s[4:5], workspace=buf.rws,
+                               stream=stream)
     ops.int_conv_wgrad(dY, X, buf.G, d, absmax_G=s[2:3], workspace=buf.ws, stream=stream)
     ops.niti_quantize_update(buf.G, s[2:3], tb_w, mu, Wt, shifts_out=s[5:7], gq_out=buf.gq,
                              stream=stream)

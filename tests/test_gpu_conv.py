@@ -75,21 +75,25 @@ def test_conv_workload_full():
 
 
 # ---------------------------------------------------------------------------
-# The requantisation fused into the 64 -> 64 contractions (two passes, the
-# int32 sums never stored): y8 / dx8 and every shift against the oracle.
+# The requantisation fused into the 64 -> 64 contractions (the int32 sums
+# never stored), on both paths: one contraction pass plus the streaming pass
+# (with the workspace) and two contraction passes (without): y8 / dx8 and
+# every shift against the oracle.
 # ---------------------------------------------------------------------------
 
 FAST64 = [(2, 16, 16), (4, 32, 32), (3, 5, 3), (2, 7, 2), (5, 13, 11), (1, 100, 100), (2, 1, 57),
           (40, 20, 20)]
 
 
+@pytest.mark.parametrize("one_pass", [True, False])
 @pytest.mark.parametrize("N,H,W", FAST64)
-def test_conv_step_fused_vs_oracle(N, H, W):
-    say("conv fused", N, H, W)
+def test_conv_step_fused_vs_oracle(N, H, W, one_pass):
+    say("conv fused", N, H, W, "one pass" if one_pass else "two passes")
     d = ionn_synth.conv3x3(N=N, H=H, W=W, Cin=64, Cout=64, seed=N * H + 64)
     want = osteps.conv_step(d["X"], d["W"], d["dY"])
     Wt = to_dev(d["W"])
-    buf = steps.ConvStepBuffers.make(N, H, W, 64, 64, dev(), with_gq=True)
+    buf = steps.ConvStepBuffers.make(N, H, W, 64, 64, dev(), with_gq=True, one_pass=one_pass)
+    assert (buf.rws is not None) == one_pass
     steps.conv_step_fused(to_dev(d["X"]), Wt, to_dev(d["dY"]), buf)
     for k, t in (("y8", buf.y8), ("dx8", buf.dx8), ("G", buf.G), ("Gq", buf.gq)):
         np.testing.assert_array_equal(host(t), want[k], err_msg=k)
@@ -99,19 +103,24 @@ def test_conv_step_fused_vs_oracle(N, H, W):
     assert sc[3:7].tolist() == [want["s_y"], want["s_dx"], want["s"], want["ws"]]
 
 
+@pytest.mark.parametrize("one_pass", [True, False])
 @pytest.mark.parametrize("relu", [0, 1])
-@pytest.mark.parametrize("tb", [1, 7, 12, 31])
-def test_conv_fwd_requant_target_bits_relu(tb, relu):
-    """Any target_bits (s = 0 at 31: the sums are returned clamped) and the
-    Conv2D layer's ReLU, on a ragged 9x7 image pair."""
+@pytest.mark.parametrize("tb", [1, 2, 5, 7, 12, 31])
+def test_conv_fwd_requant_target_bits_relu(tb, relu, one_pass):
+    """Any target_bits (s = 0 at 31: the sums are returned clamped; above 7
+    the one-pass request runs two passes) and the Conv2D layer's ReLU, on a
+    ragged 9x7 image pair."""
     N, H, W = 2, 9, 7
+    desc = ops.conv_desc(N, H, W, 64, 64)
+    ws = torch.empty(ops.int_conv_requant_workspace_bytes(desc), dtype=torch.uint8, device=dev()) \
+        if one_pass else None
     d = ionn_synth.conv3x3(N=N, H=H, W=W, Cin=64, Cout=64, seed=tb + 10 * relu)
     Y = oracle.conv_fwd(d["X"], d["W"])
     y8, s = oracle.niti_requant(Y, tb, bool(relu))
     out = torch.empty(N, H, W, 64, dtype=torch.int8, device=dev())
     scal = torch.zeros(2, dtype=torch.int32, device=dev())
-    ops.int_conv_fwd_requant(to_dev(d["X"]), to_dev(d["W"]), out, ops.conv_desc(N, H, W, 64, 64), tb, relu,
-                             scal[0:1], shift_out=scal[1:2])
+    ops.int_conv_fwd_requant(to_dev(d["X"]), to_dev(d["W"]), out, desc, tb, relu,
+                             scal[0:1], shift_out=scal[1:2], workspace=ws)
     np.testing.assert_array_equal(host(out), y8)
     assert host(scal).tolist() == [oracle.absmax(Y), s]
     # delta propagation through the same path
@@ -119,10 +128,43 @@ def test_conv_fwd_requant_target_bits_relu(tb, relu):
     dx8, sd = oracle.niti_requant(dX, tb)
     out2 = torch.empty(N, H, W, 64, dtype=torch.int8, device=dev())
     scal.zero_()
-    ops.int_conv_dgrad_requant(to_dev(d["dY"]), to_dev(d["W"]), out2, ops.conv_desc(N, H, W, 64, 64), tb,
-                               scal[0:1], shift_out=scal[1:2])
+    ops.int_conv_dgrad_requant(to_dev(d["dY"]), to_dev(d["W"]), out2, desc, tb,
+                               scal[0:1], shift_out=scal[1:2], workspace=ws)
     np.testing.assert_array_equal(host(out2), dx8)
     assert host(scal).tolist() == [oracle.absmax(dX), sd]
+
+
+@pytest.mark.parametrize("case", ["zeros", "one_hot", "small", "large"])
+def test_conv_requant_one_pass_edge_values(case):
+    """The one-pass path where the block shifts differ from the tensor's:
+    all-zero images (every shift 0), a single non-zero pixel (one block at
+    the tensor's shift, every other block far below it), values that never
+    need a shift, and the largest sums the int8 ranges allow."""
+    N, H, W = 2, 17, 15
+    rng = np.random.default_rng({"zeros": 1, "one_hot": 2, "small": 3, "large": 4}[case])
+    Wt = np.clip(np.round(rng.normal(0, 15, (64, 3, 3, 64))), -128, 127).astype(np.int8)
+    X = np.zeros((N, H, W, 64), np.int8)
+    if case == "one_hot":
+        X[1, 8, 7, :] = 127
+    elif case == "small":
+        X = rng.integers(-1, 2, (N, H, W, 64)).astype(np.int8)
+        Wt = rng.integers(-1, 2, (64, 3, 3, 64)).astype(np.int8)
+    elif case == "large":
+        X[:] = -128
+        X[0, ::2, ::3, :] = 127
+        Wt[:] = -128
+    desc = ops.conv_desc(N, H, W, 64, 64)
+    ws = torch.empty(ops.int_conv_requant_workspace_bytes(desc), dtype=torch.uint8, device=dev())
+    ws.fill_(0xA5)   # stale workspace contents must not matter
+    for relu in (0, 1):
+        Y = oracle.conv_fwd(X, Wt)
+        y8, s = oracle.niti_requant(Y, 7, bool(relu))
+        out = torch.full((N, H, W, 64), 99, dtype=torch.int8, device=dev())
+        scal = torch.zeros(2, dtype=torch.int32, device=dev())
+        ops.int_conv_fwd_requant(to_dev(X), to_dev(Wt), out, desc, 7, relu, scal[0:1], shift_out=scal[1:2],
+                                 workspace=ws)
+        np.testing.assert_array_equal(host(out), y8, err_msg=f"{case} relu={relu}")
+        assert host(scal).tolist() == [oracle.absmax(Y), s]
 
 
 def test_conv_requant_refusals_and_empty():
@@ -147,6 +189,12 @@ def test_conv_requant_refusals_and_empty():
     with pytest.raises(IonnError) as e:
         ops.int_conv_fwd_requant(x64, w64, o, ops.conv_desc(1, 4, 4, 64, 64), 0, 0, scal[0:1])
     assert e.value.status == 3
+    # a workspace smaller than the one-pass path needs is refused
+    d4 = ops.conv_desc(1, 4, 4, 64, 64)
+    small = torch.empty(ops.int_conv_requant_workspace_bytes(d4) - 16, dtype=torch.uint8, device=dev())
+    with pytest.raises(IonnError) as e:
+        ops.int_conv_fwd_requant(x64, w64, o, d4, 7, 0, scal[0:1], workspace=small)
+    assert e.value.status == 7
     # no pixels: nothing to contract, s = 0 is written
     scal.fill_(9)
     scal[0] = 0
@@ -177,6 +225,12 @@ def test_conv_fused_workload_full():
     dx8, s_dx = oracle.niti_requant(dXo, 7)
     np.testing.assert_array_equal(host(buf.dx8), dx8)
     assert (sc[1], sc[4]) == (oracle.absmax(dXo), s_dx)
+    # the two-pass path gives the same bytes at full size
+    buf2 = steps.ConvStepBuffers.make(N, H, Wd, C, 64, dev(), one_pass=False)
+    steps.conv_step_fused(to_dev(X), to_dev(W), to_dev(dY), buf2)
+    np.testing.assert_array_equal(host(buf2.y8), host(buf.y8))
+    np.testing.assert_array_equal(host(buf2.dx8), host(buf.dx8))
+    assert host(buf2.scal)[[0, 1, 3, 4]].tolist() == host(buf.scal)[[0, 1, 3, 4]].tolist()
 
 
 def test_conv_step_fused_replayed_from_graph():
