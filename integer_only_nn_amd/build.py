@@ -32,12 +32,20 @@ def _headers():
     return glob.glob(os.path.join(CSRC, "*.h")) + glob.glob(os.path.join(INCLUDE, "*.h"))
 
 
+# Per-file code-generation options.  conv_pipe.hip keeps its matrix-core
+# accumulators in VGPRs and its weight operand in AGPRs (the VGPR form of the
+# MFMA instructions).
+FILE_FLAGS = {
+    "conv_pipe.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def _compile(src, force):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     deps = [src] + _headers()
     if not force and os.path.exists(obj) and os.path.getmtime(obj) >= max(map(os.path.getmtime, deps)):
         return obj
-    cmd = [HIPCC] + CFLAGS + ["-c", src, "-o", obj + ".tmp"]
+    cmd = [HIPCC] + CFLAGS + FILE_FLAGS.get(os.path.basename(src), []) + ["-c", src, "-o", obj + ".tmp"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")

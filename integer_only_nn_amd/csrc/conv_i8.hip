@@ -24,6 +24,7 @@
 // weight element and pixel range of wgrad.  These are small-layer paths.
 #include "gemm_core.h"
 #include "conv3x3.h"
+#include "conv_pipe.h"
 
 #include <initializer_list>
 
@@ -491,6 +492,9 @@ int conv_requant(const int8_t *in, const int8_t *Wt, int8_t *out8, const ionn_co
         return shift_out ? ionn_fill_u32(reinterpret_cast<uint32_t *>(shift_out), 1, 0, stream) : IONN_OK;
     const dim3 grid(c3_grid(desc)), block(c3::NTF);
     const int N = int(desc->N), H = int(desc->H), W = int(desc->W);
+    // the pipelined kernel when its halo fits (80-byte slots), else the
+    // eight-wavefront one (64-byte slots)
+    const bool pipe = c3::pipe_fits(desc->W, npix * 64);
     if (workspace != nullptr && target_bits <= 7) {
         const size_t need = requant_ws_bytes(desc);
         IONN_REQUIRE(workspace_bytes >= need && aligned(workspace, 16) && aligned(out8, 16), IONN_ERR_WORKSPACE,
@@ -499,8 +503,12 @@ int conv_requant(const int8_t *in, const int8_t *Wt, int8_t *out8, const ionn_co
         const int64_t tiles = desc->N * ((desc->H * desc->W + c3::TP - 1) / c3::TP);
         uint32_t *bits = static_cast<uint32_t *>(workspace);
         int32_t *sblk = reinterpret_cast<int32_t *>(bits + tiles * 8 * 64);
-        c3::conv3x3_kernel<DGRAD, c3::PARTIAL><<<grid, block, 0, st>>>(in, Wt, out8, N, H, W, absmax, target_bits,
-                                                                       relu, nullptr, bits, sblk);
+        if (pipe)
+            c3::launch_pipe(DGRAD, c3::PARTIAL, in, Wt, out8, N, H, W, absmax, target_bits, relu, nullptr, bits,
+                            sblk, grid.x, st);
+        else
+            c3::conv3x3_kernel<DGRAD, c3::PARTIAL><<<grid, block, 0, st>>>(in, Wt, out8, N, H, W, absmax,
+                                                                           target_bits, relu, nullptr, bits, sblk);
         if (int rc = check_launch(name)) return rc;
         const int64_t nchunks = npix * 4;
         int64_t fb = (nchunks + 255) / 256;
@@ -508,6 +516,14 @@ int conv_requant(const int8_t *in, const int8_t *Wt, int8_t *out8, const ionn_co
         c3::conv3x3_requant_fix<<<dim3(unsigned(fb)), dim3(256), 0, st>>>(
             out8, bits, sblk, absmax, target_bits, relu, uint32_t(desc->H * desc->W),
             uint32_t((desc->H * desc->W + c3::TP - 1) / c3::TP), uint32_t(nchunks), shift_out);
+        return check_launch(name);
+    }
+    if (pipe) {
+        c3::launch_pipe(DGRAD, c3::MAXONLY, in, Wt, nullptr, N, H, W, absmax, 0, 0, nullptr, nullptr, nullptr,
+                        grid.x, st);
+        if (int rc = check_launch(name)) return rc;
+        c3::launch_pipe(DGRAD, c3::REQUANT, in, Wt, out8, N, H, W, absmax, target_bits, relu, shift_out, nullptr,
+                        nullptr, grid.x, st);
         return check_launch(name);
     }
     c3::conv3x3_kernel<DGRAD, c3::MAXONLY><<<grid, block, 0, st>>>(in, Wt, nullptr, N, H, W, absmax);
