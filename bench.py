@@ -252,19 +252,24 @@ def bench_linear(torch, steps_mod, args, pm):
             res["idle_gfxclk_mhz"] = pm.read()["clk"]
         except Exception:
             pass
+    # the maxima alternate between two scalar sets: each step's update
+    # clears the set the next step max-combines into (no fill launch per
+    # step); sets[ph] is the current step's
+    sets = (s[8:11], s[12:15])
+    ph = [0]
 
     def step(tm=None):
         m = tm.mark if tm else (lambda n: None)
-        m("fill")
-        ops.ionn_fill_u32(s[0:3], 0)
+        cur, nxt = sets[ph[0]], sets[ph[0] ^ 1]
+        ph[0] ^= 1
         m("fwd")
-        ops.int_linear_fwd(X, W, buf.Y, absmax_Y=s[0:1])
+        ops.int_linear_fwd(X, W, buf.Y, absmax_Y=cur[0:1])
         m("dgrad")
-        ops.int_linear_dgrad(dY, W, buf.dX, absmax_dX=s[1:2])
+        ops.int_linear_dgrad(dY, W, buf.dX, absmax_dX=cur[1:2])
         m("wgrad")
-        ops.int_linear_wgrad(dY, X, buf.G, absmax_G=s[2:3])
+        ops.int_linear_wgrad(dY, X, buf.G, absmax_G=cur[2:3])
         m("update")
-        ops.niti_quantize_update(buf.G, s[2:3], 8, 2, W, shifts_out=s[4:6])
+        ops.niti_quantize_update_clear(buf.G, cur[2:3], 8, 2, W, nxt, shifts_out=s[4:6])
 
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
@@ -316,24 +321,27 @@ def bench_linear(torch, steps_mod, args, pm):
     # alone (the other launches run unbracketed), and back to back on its own
     def only(name, e_a, e_b):
         def st_():
-            ops.ionn_fill_u32(s[0:3], 0)
+            cur, nxt = sets[ph[0]], sets[ph[0] ^ 1]
+            ph[0] ^= 1
             if name == "fwd":
                 e_a.record()
-            ops.int_linear_fwd(X, W, buf.Y, absmax_Y=s[0:1])
+            ops.int_linear_fwd(X, W, buf.Y, absmax_Y=cur[0:1])
             if name == "fwd":
                 e_b.record()
             elif name == "dgrad":
                 e_a.record()
-            ops.int_linear_dgrad(dY, W, buf.dX, absmax_dX=s[1:2])
+            ops.int_linear_dgrad(dY, W, buf.dX, absmax_dX=cur[1:2])
             if name == "dgrad":
                 e_b.record()
             elif name == "wgrad":
                 e_a.record()
-            ops.int_linear_wgrad(dY, X, buf.G, absmax_G=s[2:3])
+            ops.int_linear_wgrad(dY, X, buf.G, absmax_G=cur[2:3])
             if name == "wgrad":
                 e_b.record()
-            ops.niti_quantize_update(buf.G, s[2:3], 8, 2, W, shifts_out=s[4:6])
+            ops.niti_quantize_update_clear(buf.G, cur[2:3], 8, 2, W, nxt, shifts_out=s[4:6])
         return st_
+    # kernels launched back to back on their own (maxima into the spare
+    # set s[0:3], which no step reads)
     launch = {"fwd": lambda: ops.int_linear_fwd(X, W, buf.Y, absmax_Y=s[0:1]),
               "dgrad": lambda: ops.int_linear_dgrad(dY, W, buf.dX, absmax_dX=s[1:2]),
               "wgrad": lambda: ops.int_linear_wgrad(dY, X, buf.G, absmax_G=s[2:3]),
@@ -360,8 +368,9 @@ def bench_linear(torch, steps_mod, args, pm):
 
     # the same step with the propagated delta requantised to 7 bits (untimed above)
     def step_req():
+        cur = sets[ph[0]]
         step()
-        ops.niti_quantize(buf.dX, s[1:2], 7, False, buf.delta, shift_out=s[3:4])
+        ops.niti_quantize(buf.dX, cur[1:2], 7, False, buf.delta, shift_out=s[3:4])
     for _ in range(2):
         step_req()
     torch.cuda.synchronize()
@@ -372,6 +381,9 @@ def bench_linear(torch, steps_mod, args, pm):
     torch.cuda.synchronize()
     res["ms_req"] = t0.elapsed_time(t1) / args.steps
     res["shifts"] = buf.scal.cpu().tolist()
+    # max |Y|, |dX|, |G| of the last step (the tests compare them with the
+    # oracle's for this workload)
+    res["last_maxima"] = [int(v) & 0xFFFFFFFF for v in sets[ph[0] ^ 1].cpu().tolist()]
 
     # power and clock over a few seconds of back-to-back steps
     if args.power_window_s > 0 and pm.h is not None:
@@ -1026,6 +1038,7 @@ def main():
                                           "kernels (null when the sources changed since)"},
         "ms_per_step_with_delta_requant": round(L["ms_req"], 4),
         "shifts": {"s_delta": shifts[3], "s_weight": shifts[4], "ws": shifts[5]},
+        "maxima_last_step": L["last_maxima"],
     }
     result["small_workloads"] = bench_small(torch, 20)
     if args.calibrate:

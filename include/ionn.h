@@ -139,6 +139,19 @@ int niti_quantize_update(const int32_t *G, int64_t n, const uint32_t *absmax,
                          int target_bits, int mu_weight, int8_t *W,
                          int32_t *shifts_out, int32_t *gq_out, void *stream);
 
+/* niti_quantize_update, which also sets clear[0 .. n_clear) to 0 (device
+ * uint32, 0 <= n_clear <= 256, must not overlap *absmax).  For a training
+ * loop that alternates two sets of max-combined scalars: the update of one
+ * step clears the set the next step max-combines into, so no separate fill
+ * precedes each step (a HIP graph then captures an even number of steps).
+ * Nothing reads clear in the call; the clearing happens before the kernel
+ * ends, so the next call on the stream sees zeros. */
+int niti_quantize_update_clear(const int32_t *G, int64_t n,
+                               const uint32_t *absmax, int target_bits,
+                               int mu_weight, int8_t *W, int32_t *shifts_out,
+                               int32_t *gq_out, uint32_t *clear,
+                               int64_t n_clear, void *stream);
+
 /* Output error of a classifier whose loss pushes the true class toward a
  * target magnitude and the others toward 0 ([TI] sections 4 and 6.2: user
  * loss writes the delta for the backward pass):

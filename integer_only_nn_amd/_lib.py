@@ -27,6 +27,7 @@ SIGNATURES = {
     "int_linear_wgrad": (_I, [_P, _P, _P, _I64, _I64, _I64, _P, _P]),
     "niti_quantize": (_I, [_P, _I64, _P, _I, _I, _P, _P, _P]),
     "niti_quantize_update": (_I, [_P, _I64, _P, _I, _I, _P, _P, _P, _P]),
+    "niti_quantize_update_clear": (_I, [_P, _I64, _P, _I, _I, _P, _P, _P, _P, _I64, _P]),
     "int_output_error": (_I, [_P, _P, _I64, _I64, _I, _P, _P, _P]),
     "int_conv_fwd": (_I, [_P, _P, _P, _P, _P, _P]),
     "int_conv_dgrad": (_I, [_P, _P, _P, _P, _P, _P]),

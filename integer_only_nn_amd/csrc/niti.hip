@@ -66,13 +66,17 @@ __global__ __launch_bounds__(256) void quantize_kernel(const int32_t *__restrict
 }
 
 // W[j] = sat8(W[j] - rhu(rhu(G[j], s), ws)), s and ws from *absmax.
+// clear[0 .. n_clear) = 0 as well (block 0; n_clear <= 256; the host checks
+// that clear does not overlap absmax, which every block reads).
 template <bool VEC, bool GQ>
 __global__ __launch_bounds__(256) void update_kernel(const int32_t *__restrict__ G, int64_t n,
                                                      const uint32_t *__restrict__ absmax,
                                                      int target_bits, int mu_weight,
                                                      int8_t *__restrict__ W,
                                                      int32_t *__restrict__ shifts_out,
-                                                     int32_t *__restrict__ gq_out) {
+                                                     int32_t *__restrict__ gq_out,
+                                                     uint32_t *__restrict__ clear = nullptr,
+                                                     int n_clear = 0) {
     const int s = niti_shift(*absmax, target_bits);
     const int ws = s - mu_weight > 0 ? s - mu_weight : 0;
     const int64_t tid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -81,6 +85,7 @@ __global__ __launch_bounds__(256) void update_kernel(const int32_t *__restrict__
         shifts_out[0] = s;
         shifts_out[1] = ws;
     }
+    if (tid < n_clear) clear[tid] = 0u;
     int64_t done = 0;
     if (VEC) {
         const int lane = threadIdx.x & 63;
@@ -198,6 +203,38 @@ int niti_quantize_update(const int32_t *G, int64_t n, const uint32_t *absmax, in
     else if (gq_out) update_kernel<false, true><<<grid, block, 0, st>>>(G, n, absmax, target_bits, mu_weight, W, shifts_out, gq_out);
     else update_kernel<false, false><<<grid, block, 0, st>>>(G, n, absmax, target_bits, mu_weight, W, shifts_out, gq_out);
     return check_launch("niti_quantize_update");
+}
+
+int niti_quantize_update_clear(const int32_t *G, int64_t n, const uint32_t *absmax, int target_bits,
+                               int mu_weight, int8_t *W, int32_t *shifts_out, int32_t *gq_out,
+                               uint32_t *clear, int64_t n_clear, void *stream) {
+    clear_error();
+    IONN_REQUIRE(n >= 0, IONN_ERR_SHAPE, "niti_quantize_update_clear: n = %lld < 0", (long long)n);
+    IONN_REQUIRE(absmax != nullptr, IONN_ERR_ARG, "niti_quantize_update_clear: absmax is NULL");
+    IONN_REQUIRE(n == 0 || (G != nullptr && W != nullptr), IONN_ERR_ARG,
+                 "niti_quantize_update_clear: G/W is NULL");
+    IONN_REQUIRE(target_bits >= 1 && target_bits <= 31, IONN_ERR_RANGE,
+                 "niti_quantize_update_clear: target_bits = %d outside [1, 31]", target_bits);
+    IONN_REQUIRE(mu_weight >= 0 && mu_weight <= 31, IONN_ERR_RANGE,
+                 "niti_quantize_update_clear: mu_weight = %d outside [0, 31]", mu_weight);
+    IONN_REQUIRE(n_clear >= 0 && n_clear <= 256 && (n_clear == 0 || clear != nullptr), IONN_ERR_ARG,
+                 "niti_quantize_update_clear: n_clear = %lld (need 0..256 and a clear pointer)",
+                 (long long)n_clear);
+    const uintptr_t a = uintptr_t(absmax), c0 = uintptr_t(clear), c1 = c0 + uintptr_t(4 * n_clear);
+    IONN_REQUIRE(n_clear == 0 || a + 4 <= c0 || a >= c1, IONN_ERR_ARG,
+                 "niti_quantize_update_clear: clear overlaps absmax");
+    IONN_REQUIRE(aligned(G, 4) && aligned(absmax, 4) && aligned(shifts_out, 4) && aligned(gq_out, 4) &&
+                     aligned(clear, 4),
+                 IONN_ERR_ALIGN, "niti_quantize_update_clear: int32 pointers must be 4-byte aligned");
+    const bool vec = aligned(G, 16) && aligned(W, 4) && aligned(gq_out, 16);
+    dim3 grid(stream_blocks(n)), block(256);
+    hipStream_t st = as_stream(stream);
+    const int nc = int(n_clear);
+    if (vec && gq_out) update_kernel<true, true><<<grid, block, 0, st>>>(G, n, absmax, target_bits, mu_weight, W, shifts_out, gq_out, clear, nc);
+    else if (vec) update_kernel<true, false><<<grid, block, 0, st>>>(G, n, absmax, target_bits, mu_weight, W, shifts_out, gq_out, clear, nc);
+    else if (gq_out) update_kernel<false, true><<<grid, block, 0, st>>>(G, n, absmax, target_bits, mu_weight, W, shifts_out, gq_out, clear, nc);
+    else update_kernel<false, false><<<grid, block, 0, st>>>(G, n, absmax, target_bits, mu_weight, W, shifts_out, gq_out, clear, nc);
+    return check_launch("niti_quantize_update_clear");
 }
 
 int int_output_error(const int8_t *out, const int32_t *labels, int64_t B, int64_t C,

@@ -97,6 +97,18 @@ def niti_quantize_update(G, absmax, target_bits, mu_weight, W, shifts_out=None, 
           "niti_quantize_update")
 
 
+def niti_quantize_update_clear(G, absmax, target_bits, mu_weight, W, clear, shifts_out=None, gq_out=None,
+                               stream=None):
+    assert G.numel() == W.numel()
+    check(lib().niti_quantize_update_clear(_p(G, i32, name="G"), G.numel(), _p(absmax, u32, 1, "absmax"),
+                                           int(target_bits), int(mu_weight), _p(W, i8, name="W"),
+                                           _p(shifts_out, i32, 2, "shifts_out"),
+                                           _p(gq_out, i32, G.numel(), "gq_out"),
+                                           _p(clear, u32, None, "clear"), clear.numel() if clear is not None else 0,
+                                           _stream(stream)),
+          "niti_quantize_update_clear")
+
+
 def ionn_oss_requant(acc, offset, mult, k, out, relu=False, stream=None):
     M, C = acc.shape
     assert tuple(out.shape) == (M, C) and offset.numel() == C and mult.numel() == C and k.numel() == C

@@ -37,37 +37,64 @@ def _i8(*shape, device):
 
 @dataclass
 class LinearStepBuffers:
-    """Device buffers of one linear-layer step (allocated once, reused)."""
+    """Device buffers of one linear-layer step (allocated once, reused).
+
+    scal, int32[16]: [0:3] the max |Y|, |dX|, |G| of the last step, [3] the
+    delta's shift, [4:6] the update's s, ws; [8:11] and [12:15] the two sets
+    the maxima are max-combined into when steps alternate (alternate=True):
+    each step's update clears the set the next step uses, so no fill kernel
+    runs per step; the maxima of the step just taken are then in set
+    `maxima()`."""
     Y: torch.Tensor
     dX: torch.Tensor
     G: torch.Tensor
     delta: torch.Tensor
-    scal: torch.Tensor    # int32[8]: absmax Y, dX, G | shift delta | s, ws
+    scal: torch.Tensor
     gq: Optional[torch.Tensor] = None
+    alternate: bool = False
+    phase: int = 0
 
     @staticmethod
-    def make(B, IN, OUT, device, with_gq=False):
+    def make(B, IN, OUT, device, with_gq=False, alternate=False):
         return LinearStepBuffers(_i32(B, OUT, device=device), _i32(B, IN, device=device),
                                  _i32(OUT, IN, device=device), _i8(B, IN, device=device),
-                                 torch.zeros(8, dtype=torch.int32, device=device),
-                                 _i32(OUT, IN, device=device) if with_gq else None)
+                                 torch.zeros(16, dtype=torch.int32, device=device),
+                                 _i32(OUT, IN, device=device) if with_gq else None, alternate)
+
+    def maxima(self):
+        """The max |Y|, |dX|, |G| scalars of the last step (device view)."""
+        if not self.alternate:
+            return self.scal[0:3]
+        o = 8 if self.phase == 1 else 12
+        return self.scal[o:o + 3]
 
 
 def linear_step(X, W, dY, buf: LinearStepBuffers, requant_delta=True, tb_w=TB_WEIGHT,
                 mu=MU_WEIGHT, tb_d=TB_DELTA, stream=None):
     """fwd (int32 Y + max) -> dgrad (int32 dX + max) [-> delta, 7 bits] ->
-    wgrad (int32 G + max) -> NITI update of W in place."""
-    B, IN = X.shape
-    OUT = W.shape[0]
+    wgrad (int32 G + max) -> NITI update of W in place.  With
+    buf.alternate the maxima go to one of two scalar sets and the update
+    clears the other, instead of a fill before the step (a captured HIP
+    graph must then hold an even number of steps)."""
     s = buf.scal
-    ops.ionn_fill_u32(s[0:3], 0, stream=stream)
-    ops.int_linear_fwd(X, W, buf.Y, absmax_Y=s[0:1], stream=stream)
-    ops.int_linear_dgrad(dY, W, buf.dX, absmax_dX=s[1:2], stream=stream)
+    if buf.alternate:
+        m = s[8:11] if buf.phase == 0 else s[12:15]
+        nxt = s[12:15] if buf.phase == 0 else s[8:11]
+        buf.phase ^= 1
+    else:
+        m, nxt = s[0:3], None
+        ops.ionn_fill_u32(m, 0, stream=stream)
+    ops.int_linear_fwd(X, W, buf.Y, absmax_Y=m[0:1], stream=stream)
+    ops.int_linear_dgrad(dY, W, buf.dX, absmax_dX=m[1:2], stream=stream)
     if requant_delta:
-        ops.niti_quantize(buf.dX, s[1:2], tb_d, False, buf.delta, shift_out=s[3:4], stream=stream)
-    ops.int_linear_wgrad(dY, X, buf.G, absmax_G=s[2:3], stream=stream)
-    ops.niti_quantize_update(buf.G, s[2:3], tb_w, mu, W, shifts_out=s[4:6], gq_out=buf.gq,
-                             stream=stream)
+        ops.niti_quantize(buf.dX, m[1:2], tb_d, False, buf.delta, shift_out=s[3:4], stream=stream)
+    ops.int_linear_wgrad(dY, X, buf.G, absmax_G=m[2:3], stream=stream)
+    if nxt is None:
+        ops.niti_quantize_update(buf.G, m[2:3], tb_w, mu, W, shifts_out=s[4:6], gq_out=buf.gq,
+                                 stream=stream)
+    else:
+        ops.niti_quantize_update_clear(buf.G, m[2:3], tb_w, mu, W, nxt, shifts_out=s[4:6], gq_out=buf.gq,
+                                       stream=stream)
 
 
 # ---------------------------------------------------------------------------

@@ -160,3 +160,54 @@ def test_linear_step_replayed_from_graph():
         assert sc[3] == want["s_d"] and (sc[4], sc[5]) == (want["s"], want["ws"]), (rep, sc)
         W = want["W_new"]
         torch.zeros(1000, device=dev()).add_(1.0)   # unrelated eager work between replays
+
+
+@pytest.mark.parametrize("B,IN,OUT", [(300, 520, 264), (256, 256, 256), (16, 64, 32)])
+def test_linear_steps_alternating_scalar_sets(B, IN, OUT):
+    """Steps whose update clears the next step's max-combined scalars
+    (niti_quantize_update_clear) instead of a fill before each step: five
+    consecutive steps against the oracle's, every maximum and shift."""
+    d = ionn_synth.single_linear(B=B, IN=IN, OUT=OUT, seed=B + IN)
+    X, W, dY = d["X"], d["W"], d["dY"]
+    Wd, Xd, dYd = to_dev(W), to_dev(X), to_dev(dY)
+    buf = steps.LinearStepBuffers.make(B, IN, OUT, dev(), with_gq=True, alternate=True)
+    buf.scal[8:15].fill_(12345)    # stale values: the first step's set must not be used unless cleared
+    buf.scal[8:11].zero_()
+    for t in range(5):
+        steps.linear_step(Xd, Wd, dYd, buf)
+        want = osteps.linear_step(X, W, dY)
+        np.testing.assert_array_equal(host(buf.gq), want["Gq"], err_msg=f"step {t}: Gq")
+        np.testing.assert_array_equal(host(Wd), want["W_new"], err_msg=f"step {t}: W")
+        m = host(buf.maxima()).astype(np.int64) & 0xFFFFFFFF
+        assert m.tolist() == [oracle.absmax(want["Y32"]), oracle.absmax(want["dX32"]), oracle.absmax(want["G"])], t
+        sc = host(buf.scal).tolist()
+        assert sc[3] == want["s_d"] and (sc[4], sc[5]) == (want["s"], want["ws"]), (t, sc)
+        W = want["W_new"]
+
+
+def test_linear_steps_alternating_replayed_from_graph():
+    """Two alternating steps captured in one HIP graph, replayed three times
+    with eager work between replays: each replay is two oracle steps."""
+    d = ionn_synth.single_linear(B=300, IN=520, OUT=264, seed=33)
+    X, W, dY = d["X"], d["W"], d["dY"]
+    Wd, Xd, dYd = to_dev(W), to_dev(X), to_dev(dY)
+    buf = steps.LinearStepBuffers.make(300, 520, 264, dev(), with_gq=True, alternate=True)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        steps.linear_step(Xd, Wd, dYd, buf, stream=s.cuda_stream)
+        steps.linear_step(Xd, Wd, dYd, buf, stream=s.cuda_stream)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        say("alternating linear steps graph replay", rep)
+        g.replay()
+        torch.cuda.synchronize()
+        want = osteps.linear_step(X, W, dY)
+        want = osteps.linear_step(X, want["W_new"], dY)
+        np.testing.assert_array_equal(host(Wd), want["W_new"], err_msg=f"replay {rep}: W")
+        np.testing.assert_array_equal(host(buf.gq), want["Gq"], err_msg=f"replay {rep}: Gq")
+        m = host(buf.scal[12:15]).astype(np.int64) & 0xFFFFFFFF   # the second step's set
+        assert m.tolist() == [oracle.absmax(want["Y32"]), oracle.absmax(want["dX32"]), oracle.absmax(want["G"])]
+        W = want["W_new"]
+        torch.zeros(1000, device=dev()).add_(1.0)

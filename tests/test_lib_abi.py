@@ -204,3 +204,14 @@ def test_bias_grad_noalloc_refuses_sizes_beyond_its_scratch():
     assert lib.ionn_bias_grad_noalloc(None, 4, 16, FAKE, None) == ARG
     assert lib.ionn_bias_grad_noalloc(FAKE, 4, 16, FAKE_ODD, None) == ALIGN
     assert lib.ionn_bias_grad_noalloc(None, 4, 0, None, None) == OK
+
+
+def test_update_clear_validation():
+    f = lib.niti_quantize_update_clear
+    # clear overlapping absmax, n_clear out of range, NULL clear with a count
+    assert f(FAKE, 8, P(0x2000), 8, 2, FAKE, None, None, P(0x2000), 3, None) == ARG
+    assert f(FAKE, 8, P(0x2004), 8, 2, FAKE, None, None, P(0x2000), 3, None) == ARG
+    assert f(FAKE, 8, P(0x2000), 8, 2, FAKE, None, None, P(0x3000), 257, None) == ARG
+    assert f(FAKE, 8, P(0x2000), 8, 2, FAKE, None, None, None, 2, None) == ARG
+    assert f(FAKE, 8, P(0x2000), 8, 2, FAKE, None, None, P(0x3002), 2, None) == ALIGN
+    assert f(FAKE, 8, P(0x2000), 0, 2, FAKE, None, None, P(0x3000), 2, None) == RANGE
