@@ -422,6 +422,15 @@ struct Args {
     // its own and the output is not scaled again
     const int32_t *bea, *beb;
     int nch;
+    // Block-shift int16 form (integer, split == 1): each wavefront's 32 x 64
+    // block of acc gets its own shift s_b = max(0, bitlen(max |acc|) - 15);
+    // out16 [M][N] receives asr(acc, s_b), bits the rounding bits (bit
+    // 16 j + v of word blk * 64 + lane for value v of column block j), shifts
+    // s_b of block blk = tile * 8 + wave, slots max |acc| of each workgroup
+    int16_t *out16;
+    uint32_t *bits;
+    int32_t *shifts;
+    uint32_t *slots;
 };
 
 
@@ -429,9 +438,10 @@ struct Args {
 // one output tile and one range of chunks (a K split).  The chunk loop runs
 // across unit boundaries, so the first chunk of the next unit is loaded while
 // the last chunk of the current one computes and its result is stored.
-template <bool A_KM, bool B_KM, bool F32, bool BLK = false>
+template <bool A_KM, bool B_KM, bool F32, bool BLK = false, bool B16 = false>
 __global__ __launch_bounds__(NT, 1) void dfp_kernel(Args g) {
     static_assert(F32 || !BLK, "the blocked form accumulates in FP32");
+    static_assert(!(F32 && B16), "the block-shift form is integer");
     __shared__ __attribute__((aligned(16))) int8_t lds[2 * STAGE];
     // Blocked form, per stage: the chunk's exponents of the tile's 128 rows
     // of A, then of its 128 rows of B
@@ -574,7 +584,46 @@ __global__ __launch_bounds__(NT, 1) void dfp_kernel(Args g) {
             lb.store(nx + 2 * PLANE, nx + 3 * PLANE, tid);
             if (BLK && tid < 256) bexp[BLK ? stage ^ 1 : 0][tid] = ereg;
         }
-        if (c + 1 >= c1) {
+        if (B16 && c + 1 >= c1) {
+            // unit done, block-shift form: the shift of the wave's block, then
+            // int16 asr(acc, s_b); lanes l and l + 32 trade halves so that each
+            // stores 8 consecutive columns (16 bytes)
+            uint32_t bm = 0;
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) bm = max(bm, abs_u32(acc[j][v]));
+            bm = wave_max_u32(bm);
+            amax = max(amax, bm);
+            const int sb = niti_shift(bm, 15);
+            const uint32_t sm1 = sb > 0 ? sb - 1 : 0, sw = sb > 0 ? 1 : 0;
+            const int blk = ((m0 / BM) * tiles_n + n0 / BN) * 8 + wave;
+            const int m = m0 + 32 * wm + (lane & 31);
+            uint32_t bw = 0;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                uint32_t pk[8];  // int16 pairs, two words per column group q
+#pragma unroll
+                for (int v = 0; v < 16; v += 2) {
+                    bw |= __builtin_amdgcn_ubfe(uint32_t(acc[j][v]), sm1, sw) << (16 * j + v);
+                    bw |= __builtin_amdgcn_ubfe(uint32_t(acc[j][v + 1]), sm1, sw) << (16 * j + v + 1);
+                    pk[v >> 1] = __builtin_amdgcn_perm(uint32_t(acc[j][v + 1] >> sb), uint32_t(acc[j][v] >> sb),
+                                                       0x05040100u);
+                }
+#pragma unroll
+                for (int pq = 0; pq < 2; ++pq) {
+                    const auto s0 = __builtin_amdgcn_permlane32_swap(pk[4 * pq], pk[4 * pq + 2], false, false);
+                    const auto s1 = __builtin_amdgcn_permlane32_swap(pk[4 * pq + 1], pk[4 * pq + 3], false, false);
+                    const int n = n0 + 64 * wn + 32 * j + 8 * (2 * pq + (lane >> 5));
+                    *reinterpret_cast<v4i *>(g.out16 + int64_t(m) * g.N + n) =
+                        v4i{int(s0[0]), int(s1[0]), int(s0[1]), int(s1[1])};
+                }
+                acc[j] = v16i{};
+            }
+            g.bits[int64_t(blk) * 64 + lane] = bw;
+            if (lane == 0) g.shifts[blk] = sb;
+        }
+        if (!B16 && c + 1 >= c1) {
             // unit done: lane holds acc[m][n .. n+3] for m = row lane % 32 of the
             // wave's block, n = block col 8 q + 4 (lane / 32)
             const int m = m0 + 32 * wm + (lane & 31);
@@ -603,7 +652,16 @@ __global__ __launch_bounds__(NT, 1) void dfp_kernel(Args g) {
         __syncthreads();
         u = nu; m0 = nm0; n0 = nn0; c = nc; c1 = nc1; stage ^= 1;
     }
-    if (!F32 && g.split == 1 && g.absmax) {
+    if (B16) {  // the workgroup's max |acc| to its slot (the loop has no reader of csum left)
+        if (lane == 0) csum[wave][0] = amax;
+        __syncthreads();
+        if (tid == 0) {
+            uint32_t mx = 0;
+#pragma unroll
+            for (int w = 0; w < NT / 64; ++w) mx = max(mx, csum[w][0]);
+            g.slots[blockIdx.x] = mx;
+        }
+    } else if (!F32 && g.split == 1 && g.absmax) {
         amax = wave_max_u32(amax);
         if (lane == 0) publish_max_u32(g.absmax, amax);
     }
@@ -623,10 +681,12 @@ __global__ __launch_bounds__(256) void split_reduce_f32(const float *__restrict_
     }
 }
 
-// acc[e] = sum over the split partial tiles (modulo 2^32), with the max |acc|.
+// acc[e] = sum over the split partial tiles (modulo 2^32), with the max |acc|
+// of each workgroup in slots[blockIdx.x].
 __global__ __launch_bounds__(256) void split_reduce(const int32_t *__restrict__ part, int split, int64_t n,
-                                                    int32_t *__restrict__ acc, uint32_t *__restrict__ absmax) {
+                                                    int32_t *__restrict__ acc, uint32_t *__restrict__ slots) {
     typedef unsigned v4u __attribute__((ext_vector_type(4)));
+    __shared__ uint32_t red[4];
     uint32_t amax = 0;
     for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; 4 * i < n; i += int64_t(gridDim.x) * blockDim.x) {
         v4u s = {0, 0, 0, 0};
@@ -637,20 +697,99 @@ __global__ __launch_bounds__(256) void split_reduce(const int32_t *__restrict__ 
                    max(abs_u32(int32_t(s.z)), abs_u32(int32_t(s.w))));
     }
     amax = wave_max_u32(amax);
-    if ((threadIdx.x & 63) == 0) publish_max_u32(absmax, amax);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
+    __syncthreads();
+    if (threadIdx.x == 0) slots[blockIdx.x] = max(max(red[0], red[1]), max(red[2], red[3]));
 }
 
 }  // namespace d2
 
-// out = sat16(rhu(acc, Rs)), Rs from the tensor max; exponent bookkeeping.
+// The max over nslots per-workgroup maxima, for every thread of a block of
+// at most 256 threads (1D or 2D; waves are taken in linear thread order).
+__device__ __forceinline__ uint32_t slots_max(const uint32_t *__restrict__ slots, int nslots) {
+    __shared__ uint32_t red[4];
+    const int t = threadIdx.y * blockDim.x + threadIdx.x, nt = blockDim.x * blockDim.y;
+    uint32_t mx = 0;
+    for (int i = t; i < nslots; i += nt) mx = max(mx, slots[i]);
+    mx = wave_max_u32(mx);
+    if ((t & 63) == 0) red[t >> 6] = mx;
+    __syncthreads();
+    const int nw = (nt + 63) >> 6;
+    uint32_t r = red[0];
+    for (int w = 1; w < nw; ++w) r = max(r, red[w]);
+    return r;
+}
+
+// Block-shift form, second pass (in place over out [M][N], tile-aligned):
+// with Rs = max(0, bitlen(max |acc|) - 15) from the workgroup maxima and s_b
+// the shift of the element's block, d = Rs - s_b >= 0 and
+//   rhu(acc, Rs) = sat16(f + bit)    for d = 0  (f = asr(acc, s_b), bit = bit s_b - 1 of acc)
+//                = rhu(f, d)          for d > 0  (the bits of acc below s_b cannot reach
+//                                                 the rounding position s_b + d - 1)
+// A thread takes 8 consecutive columns (16 bytes) of a row, as int16 pairs:
+// the pair arithmetic never carries across halves (|rhu(f, d)| <= 2^14; the
+// d = 0 sum saturates per half).  Threads (x, y) of a block cover column
+// groups x and rows y; exponent bookkeeping as in the two-pass form.
+__global__ __launch_bounds__(256) void block16_fix_kernel(int16_t *__restrict__ out, int M, int N,
+                                                          const uint32_t *__restrict__ bits,
+                                                          const int32_t *__restrict__ shifts,
+                                                          const uint32_t *__restrict__ slots, int nslots,
+                                                          const int32_t *__restrict__ ea,
+                                                          const int32_t *__restrict__ eb, int r,
+                                                          int32_t *__restrict__ e_out,
+                                                          int32_t *__restrict__ status) {
+    typedef short v2s __attribute__((ext_vector_type(2)));
+    const int rs = niti_shift(slots_max(slots, nslots), 15);
+    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0 && threadIdx.y == 0) {
+        const int e = *ea + *eb + r + rs;
+        *e_out = e;
+        if (status) *status = (e < -128 || e > 127) ? 1 : 0;
+    }
+    const uint32_t cpr = uint32_t(N) >> 3, tiles_n = uint32_t(N) >> 7;
+    const uint32_t c = blockIdx.x * blockDim.x + threadIdx.x;
+    if (c >= cpr) return;
+    const uint32_t n = c << 3;
+    const uint32_t pos = 16 * ((n >> 5) & 1) + 4 * ((n >> 3) & 3);
+    for (uint32_t m = blockIdx.y * blockDim.y + threadIdx.y; m < uint32_t(M); m += gridDim.y * blockDim.y) {
+        const uint32_t blk = ((m >> 7) * tiles_n + (n >> 7)) * 8 + ((m >> 5) & 3) * 2 + ((n >> 6) & 1);
+        const int d = rs - shifts[blk];
+        v4i *p = reinterpret_cast<v4i *>(out + int64_t(m) * N + n);
+        const v4i x = *p;
+        v4i y;
+        if (d == 0) {
+            // pair q of the 8 columns: bits 2 (q & 1) and 2 (q & 1) + 1 of the
+            // word of lane m % 32 (q < 2) or m % 32 + 32 (q >= 2)
+            const uint32_t b0 = bits[blk * 64 + (m & 31)] >> pos, b1 = bits[blk * 64 + 32 + (m & 31)] >> pos;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t bw = (q < 2 ? b0 : b1) >> (2 * (q & 1));
+                const v2s bit = __builtin_bit_cast(v2s, (bw & 1u) | ((bw & 2u) << 15));
+                const int xq = x[q];  // a scalar copy: bit_cast of a vector element reads element 0
+                y[q] = __builtin_bit_cast(int, __builtin_elementwise_add_sat(__builtin_bit_cast(v2s, xq), bit));
+            }
+        } else {
+            const v2s dv = {short(d), short(d)}, dm = {short(d - 1), short(d - 1)}, one = {1, 1};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int xq = x[q];
+                const v2s f = __builtin_bit_cast(v2s, xq);
+                y[q] = __builtin_bit_cast(int, v2s((f >> dv) + ((f >> dm) & one)));
+            }
+        }
+        *p = y;
+    }
+}
+
+// out = sat16(rhu(acc, Rs)), Rs from the tensor max (the max over nslots
+// partial maxima); exponent bookkeeping.
 __global__ __launch_bounds__(256) void downconvert_kernel(const int32_t *__restrict__ acc, int64_t n,
-                                                          const uint32_t *__restrict__ absmax,
+                                                          const uint32_t *__restrict__ slots, int nslots,
                                                           const int32_t *__restrict__ ea,
                                                           const int32_t *__restrict__ eb, int r,
                                                           int16_t *__restrict__ out,
                                                           int32_t *__restrict__ e_out,
                                                           int32_t *__restrict__ status) {
-    const int rs = niti_shift(*absmax, 15);
+    const int rs = niti_shift(slots_max(slots, nslots), 15);
     const int64_t tid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
     const int64_t nt = int64_t(gridDim.x) * blockDim.x;
     if (tid == 0) {
@@ -713,14 +852,62 @@ __global__ __launch_bounds__(256) void gavg_sum_kernel(const int16_t *__restrict
     }
 }
 
-__global__ void gavg_finish_kernel(double *out, int64_t n, const int32_t *__restrict__ eg,
-                                   const int32_t *__restrict__ ew) {
-    const int64_t tot = int64_t(*reinterpret_cast<const unsigned long long *>(out));
+// mean(|g|) * 2^(E_g - E_w) from the exact sum (one rounding in the
+// division; the power-of-two scaling is exact short of the double range).
+__device__ double gavg_value(int64_t tot, int64_t n, const int32_t *__restrict__ eg, const int32_t *__restrict__ ew) {
     double v = double(tot) / double(n);
     int e = *eg - *ew;
     for (; e > 0; --e) v *= 2.0;
     for (; e < 0; ++e) v *= 0.5;
-    *out = v;
+    return v;
+}
+
+__global__ void gavg_finish_kernel(double *out, int64_t n, const int32_t *__restrict__ eg,
+                                   const int32_t *__restrict__ ew) {
+    *out = gavg_value(int64_t(*reinterpret_cast<const unsigned long long *>(out)), n, eg, ew);
+}
+
+// The whole Gavg in one workgroup, for tensors small enough that one compute
+// unit streams them faster than three dependent launches complete.
+constexpr int64_t kGavgOneBlock = int64_t(1) << 21;
+
+__global__ __launch_bounds__(1024) void gavg_one_kernel(const int16_t *__restrict__ g, int64_t n, double *out,
+                                                        const int32_t *__restrict__ eg,
+                                                        const int32_t *__restrict__ ew) {
+    __shared__ int64_t part[16];
+    int64_t s = 0;
+    const int64_t n8 = n / 8;
+    const v4i *gv = reinterpret_cast<const v4i *>(g);
+    auto add8 = [&](const v4i w) {
+        int32_t t = 0;  // 8 magnitudes below 2^15 each
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int32_t lo = int32_t(uint32_t(w[q]) << 16) >> 16, hi = w[q] >> 16;
+            t += (lo < 0 ? -lo : lo) + (hi < 0 ? -hi : hi);
+        }
+        s += t;
+    };
+    int64_t i = threadIdx.x;
+    for (; i + 7 * 1024 < n8; i += 8 * 1024) {  // eight 16-byte loads in flight per thread
+        v4i w[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) w[k] = gv[i + k * 1024];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) add8(w[k]);
+    }
+    for (; i < n8; i += 1024) add8(gv[i]);
+    for (int64_t i = n8 * 8 + threadIdx.x; i < n; i += 1024) {
+        const int32_t v = g[i];
+        s += v < 0 ? -v : v;
+    }
+    s = wave_sum_i64(s);
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = s;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int64_t tot = 0;
+        for (int w = 0; w < 16; ++w) tot += part[w];
+        *out = gavg_value(tot, n, eg, ew);
+    }
 }
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -776,37 +963,18 @@ int split2(int64_t M, int64_t N, int64_t L) {
     return split < 1 ? 1 : int(split);
 }
 
-template <bool A_KM, bool B_KM>
-int contract2(const int16_t *a, int64_t lda, const int16_t *b, int64_t ldb, int M, int N, int L,
-              int32_t *acc, int32_t *part, uint32_t *absmax, hipStream_t st) {
-    const int split = split2(M, N, L);
-    d2::Args g{a, b, lda, ldb, split > 1 ? part : acc, absmax, M, N, L, chunk_shift(L), split, 0, nullptr, nullptr};
-    const int tiles = (M / d2::BM) * (N / d2::BN);
-    int cus = 256;
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
-        cus = 256;
-    const int units = tiles * split;
-    d2::dfp_kernel<A_KM, B_KM, false><<<dim3(units < cus ? units : cus), dim3(d2::NT), 0, st>>>(g);
-    if (int rc = check_launch("dfp16 contraction")) return rc;
-    if (split > 1) {
-        const int64_t n = int64_t(M) * N;
-        // four 16-byte groups per thread: fewer requests in flight than one
-        // group per thread, which measured twice as fast on 16 partials
-        int64_t blocks = (n / 4 + 1023) / 1024;
-        if (blocks > 2048) blocks = 2048;
-        d2::split_reduce<<<dim3(unsigned(blocks)), dim3(256), 0, st>>>(part, split, n, acc, absmax);
-        return check_launch("dfp16 contraction");
-    }
-    return IONN_OK;
-}
+// Workgroup maxima of the tile-aligned path (one per persistent workgroup
+// of the contraction, or per workgroup of the split sum).
+constexpr int kMaxSlots = 4096;
 
 struct Workspace {
     int32_t *acc;
     uint32_t *absmax;
     int16_t *t0, *t1;
-    int32_t *part;  // split partial tiles of the tile-aligned path
+    int32_t *part;     // split partial tiles of the tile-aligned path
+    uint32_t *bits;    // block-shift form: rounding bits, one word per lane and 32 x 64 block
+    int32_t *shifts;   // block-shift form: s_b per block
+    uint32_t *slots;   // workgroup maxima
 };
 
 size_t ws_bytes(int64_t M, int64_t K, int64_t N, int which, Workspace *w, void *base) {
@@ -828,10 +996,68 @@ size_t ws_bytes(int64_t M, int64_t K, int64_t N, int which, Workspace *w, void *
         t0 = take(size_t(N) * M * 2);                                        // dY^T [N][M]
         t1 = take(size_t(K) * M * 2);                                        // X^T  [K][M]
     }
+    char *bits = take(size_t((out + 7) / 8));           // 256 bytes per 2048-element block
+    char *shifts = take(size_t((out + 2047) / 2048) * 4);
+    char *slots = take(size_t(kMaxSlots) * 4);
     if (w) *w = Workspace{reinterpret_cast<int32_t *>(acc), reinterpret_cast<uint32_t *>(am),
                           reinterpret_cast<int16_t *>(t0), reinterpret_cast<int16_t *>(t1),
-                          reinterpret_cast<int32_t *>(part)};
+                          reinterpret_cast<int32_t *>(part), reinterpret_cast<uint32_t *>(bits),
+                          reinterpret_cast<int32_t *>(shifts), reinterpret_cast<uint32_t *>(slots)};
     return off;
+}
+
+// Tile-aligned contraction of an M x N output with reduction length L and
+// its down-conversion to out (int16) with the exponent bookkeeping.  Without
+// K splits the contraction writes the block-shift int16 form straight into
+// out and a second pass applies the tensor's shift in place; with K splits it
+// writes int32 partial tiles, the split sum forms acc and the down-conversion
+// reads it.  Either way the max |acc| travels through per-workgroup slots, so
+// nothing needs clearing first.
+template <bool A_KM, bool B_KM>
+int contract2(const int16_t *a, int64_t lda, const int16_t *b, int64_t ldb, int M, int N, int L,
+              const Workspace &w, const int32_t *ea, const int32_t *eb, int16_t *out, int32_t *e_out,
+              int32_t *status, hipStream_t st) {
+    const int split = split2(M, N, L);
+    const int r = chunk_shift(L);
+    d2::Args g{a, b, lda, ldb, split > 1 ? w.part : w.acc, nullptr, M, N, L, r, split, 0, nullptr, nullptr};
+    const int tiles = (M / d2::BM) * (N / d2::BN);
+    int cus = 256;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+        cus = 256;
+    const int units = tiles * split;
+    int grid = units < cus ? units : cus;
+    if (grid > kMaxSlots) grid = kMaxSlots;
+    const int64_t n = int64_t(M) * N;
+    if (split == 1) {
+        g.out16 = out;
+        g.bits = w.bits;
+        g.shifts = w.shifts;
+        g.slots = w.slots;
+        d2::dfp_kernel<A_KM, B_KM, false, false, true><<<dim3(grid), dim3(d2::NT), 0, st>>>(g);
+        if (int rc = check_launch("dfp16 contraction")) return rc;
+        const unsigned cpr = unsigned(N) / 8, bx = cpr < 256 ? cpr : 256, by = 256 / bx;
+        unsigned gy = (unsigned(M) + by - 1) / by;
+        if (gy > 4096) gy = 4096;
+        block16_fix_kernel<<<dim3((cpr + bx - 1) / bx, gy), dim3(bx, by), 0, st>>>(
+            out, M, N, w.bits, w.shifts, w.slots, grid, ea, eb, r, e_out, status);
+        return check_launch("dfp16 down-conversion");
+    }
+    d2::dfp_kernel<A_KM, B_KM, false><<<dim3(grid), dim3(d2::NT), 0, st>>>(g);
+    if (int rc = check_launch("dfp16 contraction")) return rc;
+    // four 16-byte groups per thread: fewer requests in flight than one
+    // group per thread, which measured twice as fast on 16 partials
+    int64_t blocks = (n / 4 + 1023) / 1024;
+    if (blocks > 2048) blocks = 2048;
+    d2::split_reduce<<<dim3(unsigned(blocks)), dim3(256), 0, st>>>(w.part, split, n, w.acc, w.slots);
+    if (int rc = check_launch("dfp16 contraction")) return rc;
+    int64_t dblocks = (n / 8 + 255) / 256;
+    if (dblocks < 1) dblocks = 1;
+    if (dblocks > 8192) dblocks = 8192;
+    downconvert_kernel<<<dim3(unsigned(dblocks)), dim3(256), 0, st>>>(w.acc, n, w.slots, int(blocks), ea, eb, r,
+                                                                     out, e_out, status);
+    return check_launch("dfp16 down-conversion");
 }
 
 int transpose16(const int16_t *src, int16_t *dst, int R, int C, hipStream_t st) {
@@ -845,7 +1071,7 @@ int finish(const Workspace &w, int64_t n, const int32_t *ea, const int32_t *eb, 
     int64_t blocks = (n / 8 + 255) / 256;
     if (blocks < 1) blocks = 1;
     if (blocks > 8192) blocks = 8192;
-    downconvert_kernel<<<dim3(unsigned(blocks)), dim3(256), 0, st>>>(w.acc, n, w.absmax, ea, eb, r,
+    downconvert_kernel<<<dim3(unsigned(blocks)), dim3(256), 0, st>>>(w.acc, n, w.absmax, 1, ea, eb, r,
                                                                     out, e_out, status);
     return check_launch("dfp16 down-conversion");
 }
@@ -1000,11 +1226,9 @@ int dfp16_gemm_fwd(const int16_t *X, const int32_t *eX, const int16_t *W, const 
     hipStream_t st = as_stream(stream);
     Workspace w;
     ws_bytes(M, K, N, IONN_DFP16_FWD, &w, workspace);
+    if (fast2(int(M), int(N), int(K), X, K, W, K))
+        return contract2<true, true>(X, K, W, K, int(M), int(N), int(K), w, eX, eW, Y, eY, status_out, st);
     zero_i32_kernel<<<dim3(1), dim3(64), 0, st>>>(reinterpret_cast<int32_t *>(w.absmax), 1);
-    if (fast2(int(M), int(N), int(K), X, K, W, K)) {
-        if (int rc = contract2<true, true>(X, K, W, K, int(M), int(N), int(K), w.acc, w.part, w.absmax, st)) return rc;
-        return finish(w, M * N, eX, eW, chunk_shift(K), Y, eY, status_out, st);
-    }
     Src16 a{X, K, int(M), int(K), aligned(X, 16) && K % 8 == 0};
     Src16 b{W, K, int(N), int(K), aligned(W, 16) && K % 8 == 0};
     if (int rc = contract(a, b, int(M), int(N), int(K), w.acc, w.absmax, st)) return rc;
@@ -1021,11 +1245,9 @@ int dfp16_gemm_dgrad(const int16_t *dY, const int32_t *edY, const int16_t *W, co
     hipStream_t st = as_stream(stream);
     Workspace w;
     ws_bytes(M, K, N, IONN_DFP16_DGRAD, &w, workspace);
+    if (fast2(int(M), int(K), int(N), dY, N, W, K))  // B = W seen M-major: (k, n) at W[n * K + k]
+        return contract2<true, false>(dY, N, W, K, int(M), int(K), int(N), w, edY, eW, dX, edX, status_out, st);
     zero_i32_kernel<<<dim3(1), dim3(64), 0, st>>>(reinterpret_cast<int32_t *>(w.absmax), 1);
-    if (fast2(int(M), int(K), int(N), dY, N, W, K)) {  // B = W seen M-major: (k, n) at W[n * K + k]
-        if (int rc = contract2<true, false>(dY, N, W, K, int(M), int(K), int(N), w.acc, w.part, w.absmax, st)) return rc;
-        return finish(w, M * K, edY, eW, chunk_shift(N), dX, edX, status_out, st);
-    }
     if (int rc = transpose16(W, w.t0, int(N), int(K), st)) return rc;  // W^T [K][N]
     Src16 a{dY, N, int(M), int(N), aligned(dY, 16) && N % 8 == 0};
     Src16 b{w.t0, N, int(K), int(N), N % 8 == 0};
@@ -1043,11 +1265,9 @@ int dfp16_gemm_wgrad(const int16_t *dY, const int32_t *edY, const int16_t *X, co
     hipStream_t st = as_stream(stream);
     Workspace w;
     ws_bytes(M, K, N, IONN_DFP16_WGRAD, &w, workspace);
+    if (fast2(int(N), int(K), int(M), dY, N, X, K))  // A = dY, B = X, both M-major over m
+        return contract2<false, false>(dY, N, X, K, int(N), int(K), int(M), w, edY, eX, G, eG, status_out, st);
     zero_i32_kernel<<<dim3(1), dim3(64), 0, st>>>(reinterpret_cast<int32_t *>(w.absmax), 1);
-    if (fast2(int(N), int(K), int(M), dY, N, X, K)) {  // A = dY, B = X, both M-major over m
-        if (int rc = contract2<false, false>(dY, N, X, K, int(N), int(K), int(M), w.acc, w.part, w.absmax, st)) return rc;
-        return finish(w, N * K, edY, eX, chunk_shift(M), G, eG, status_out, st);
-    }
     if (int rc = transpose16(dY, w.t0, int(M), int(N), st)) return rc;  // dY^T [N][M]
     if (int rc = transpose16(X, w.t1, int(M), int(K), st)) return rc;   // X^T  [K][M]
     Src16 a{w.t0, M, int(N), int(M), M % 8 == 0};
@@ -1187,6 +1407,10 @@ int dfp16_gavg(const int16_t *G, const int32_t *eG, const int32_t *eW, int64_t n
     IONN_REQUIRE(aligned(G, 2) && aligned(eG, 4) && aligned(eW, 4) && aligned(gavg_out, 8),
                  IONN_ERR_ALIGN, "dfp16_gavg: misaligned pointer");
     hipStream_t st = as_stream(stream);
+    if (n <= kGavgOneBlock && aligned(G, 16)) {
+        gavg_one_kernel<<<dim3(1), dim3(1024), 0, st>>>(G, n, gavg_out, eG, eW);
+        return check_launch("dfp16_gavg");
+    }
     unsigned long long *acc = reinterpret_cast<unsigned long long *>(gavg_out);
     gavg_zero_kernel<<<dim3(1), dim3(1), 0, st>>>(acc);
     int64_t blocks = (n + 256 * 8 - 1) / (256 * 8);

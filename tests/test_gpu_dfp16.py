@@ -28,7 +28,8 @@ def _run(d, M, K, N):
 
 @pytest.mark.parametrize("M,K,N", [(1, 1, 1), (3, 64, 5), (17, 40, 9), (128, 128, 128), (200, 256, 136),
                                    (128, 64, 128), (640, 128, 384), (1024, 384, 128),
-                                   (256, 320, 1024), (1000, 64, 48), (4096, 256, 256)])
+                                   (256, 320, 1024), (1000, 64, 48), (4096, 256, 256),
+                                   (2304, 128, 2048)])
 def test_dfp16_step_vs_oracle(M, K, N):
     say("dfp16", M, K, N)
     d = ionn_synth.dfp16_gemm(M=M, K=K, N=N, seed=M + K)
