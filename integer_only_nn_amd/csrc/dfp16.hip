@@ -4,17 +4,19 @@
 // Training for Resource Constrained Devices", Equation 4).
 //
 // gfx950 has no int16 matrix instruction, so each int16 mantissa is split
-// exactly into two int8 digits:  a = 256*ah + al + 128  with
-//   ah = a >> 8            (the signed high byte, in [-128, 127])
-//   al = (a & 255) - 128   (the low byte with its top bit flipped, in [-128, 127]).
-// For one 64-term chunk (k over the chunk, A' = a - 128, B' = b - 128):
+// exactly into two int8 digits: the signed high byte ah = a >> 8 and a low
+// digit al from the low byte.  The integer form takes al = 127 - (a & 255),
+// so a = 256 ah + 127 - al and every correction term of a 64-term chunk is an
+// int8 product against a fragment of -127 (see dfpi_kernel): the matrix
+// cores produce H, X2, L2 with p = 65536 H - 256 X2 + L2 (mod 2^32).  The
+// FP32 forms and the general-shape kernel take al = (a & 255) - 128, so
+// a = 256 ah + al + 128 and
 //   sum a*b = 65536*sum(ah*bh) + 256*sum(ah*bl + al*bh) + sum(al*bl)
 //             + 128*sum(A') + 128*sum(B') + 2^20                  (mod 2^32)
-// Four v_mfma_i32_16x16x64_i8 per 16x16 block give the digit products (the
-// two cross terms chained into one accumulator); the row sums of A' and column
-// sums of B' come from the same instruction against an all-ones fragment.
-// Zero padding (a = 0: ah = 0, al = -128) contributes exactly 0, so every chunk
-// is evaluated as a full 64-term chunk.
+// with the sums of A' = a - 128 and B' = b - 128 taken on the VALU or against
+// an all-ones fragment.  Both splits are exact for every int16, zero
+// included, so zero padding contributes exactly 0 and every chunk is
+// evaluated as a full 64-term chunk.
 //
 // Overflow management: each chunk's int32 partial p_c is shifted down by
 // r = ceil(log2(number of chunks)) with round-half-up before it joins the
@@ -337,10 +339,12 @@ constexpr int MP = 128 + 16;      // M-major plane: bytes per k-row
 constexpr int PLANE = 128 * KP;   // >= 64 * MP
 constexpr int STAGE = 4 * PLANE;
 
-// hi / lo digit bytes of 4 int16 held in two dwords (lo digit = low byte - 128)
+// hi / lo digit bytes of 4 int16 held in two dwords.  The lo digit is the
+// low byte with its top bit flipped (low - 128) for the FP32 forms, or with
+// its low 7 bits flipped (127 - low) for the integer form (lox selects).
 __device__ __forceinline__ uint32_t hi4(uint32_t w0, uint32_t w1) { return __builtin_amdgcn_perm(w1, w0, 0x07050301u); }
-__device__ __forceinline__ uint32_t lo4(uint32_t w0, uint32_t w1) {
-    return __builtin_amdgcn_perm(w1, w0, 0x06040200u) ^ 0x80808080u;
+__device__ __forceinline__ uint32_t lo4(uint32_t w0, uint32_t w1, uint32_t lox = 0x80808080u) {
+    return __builtin_amdgcn_perm(w1, w0, 0x06040200u) ^ lox;
 }
 
 // One operand tile (128 rows x 64 k of int16) global -> registers -> digit planes.
@@ -361,14 +365,14 @@ struct Ld {
 #pragma unroll
         for (int it = 0; it < IT; ++it) reg[it] = rhu1_x8(reg[it]);
     }
-    __device__ __forceinline__ void store(int8_t *hi, int8_t *lo, int tid) const {
+    __device__ __forceinline__ void store(int8_t *hi, int8_t *lo, int tid, uint32_t lox = 0x80808080u) const {
 #pragma unroll
         for (int it = 0; it < IT; ++it) {
             const int id = it * NT + tid;
             const int off = KM ? (id >> 3) * KP + 8 * (id & 7) : (id >> 4) * MP + 8 * (id & 15);
             const uint32_t w0 = reg[it].x, w1 = reg[it].y, w2 = reg[it].z, w3 = reg[it].w;
             *reinterpret_cast<uint2 *>(hi + off) = make_uint2(hi4(w0, w1), hi4(w2, w3));
-            *reinterpret_cast<uint2 *>(lo + off) = make_uint2(lo4(w0, w1), lo4(w2, w3));
+            *reinterpret_cast<uint2 *>(lo + off) = make_uint2(lo4(w0, w1, lox), lo4(w2, w3, lox));
         }
     }
 };
@@ -434,14 +438,14 @@ struct Args {
 };
 
 
-// Persistent: workgroup w takes work units w, w + gridDim.x, ...; a unit is
-// one output tile and one range of chunks (a K split).  The chunk loop runs
-// across unit boundaries, so the first chunk of the next unit is loaded while
-// the last chunk of the current one computes and its result is stored.
-template <bool A_KM, bool B_KM, bool F32, bool BLK = false, bool B16 = false>
+// FP32 forms (digits with lo = low byte - 128, corrections from the digit
+// sums on the VALU).  Persistent: workgroup w takes work units w,
+// w + gridDim.x, ...; a unit is one output tile and one range of chunks (a K
+// split).  The chunk loop runs across unit boundaries, so the first chunk of
+// the next unit is loaded while the last chunk of the current one computes and
+// its result is stored.
+template <bool A_KM, bool B_KM, bool BLK = false>
 __global__ __launch_bounds__(NT, 1) void dfp_kernel(Args g) {
-    static_assert(F32 || !BLK, "the blocked form accumulates in FP32");
-    static_assert(!(F32 && B16), "the block-shift form is integer");
     __shared__ __attribute__((aligned(16))) int8_t lds[2 * STAGE];
     // Blocked form, per stage: the chunk's exponents of the tile's 128 rows
     // of A, then of its 128 rows of B
@@ -475,7 +479,6 @@ __global__ __launch_bounds__(NT, 1) void dfp_kernel(Args g) {
     v16i acc[2];
     acc[0] = v16i{};
     acc[1] = v16i{};
-    uint32_t amax = 0;
 
     int32_t ereg = 0;
     auto eload = [&](int em0, int en0, int ec) __attribute__((always_inline)) {
@@ -488,14 +491,12 @@ __global__ __launch_bounds__(NT, 1) void dfp_kernel(Args g) {
         eload(m0, n0, c0);
         if (tid < 256) bexp[0][tid] = ereg;
     }
-    if (F32 && g.shift) la.rhu1();
+    if (g.shift) la.rhu1();
     la.store(lds, lds + PLANE, tid);
     lb.store(lds + 2 * PLANE, lds + 3 * PLANE, tid);
     __syncthreads();
 
     const v16i zero16 = {};
-    const int r = g.r;
-    const uint32_t rm1 = r > 0 ? r - 1 : 0, rw = r > 0 ? 1 : 0;  // rounding bit (none for r = 0)
     int c = c0, stage = 0;
     while (true) {
         // the work item after (u, c)
@@ -559,19 +560,15 @@ __global__ __launch_bounds__(NT, 1) void dfp_kernel(Args g) {
             ll = __builtin_amdgcn_mfma_i32_32x32x32_i8(bl[j][1], al[1], ll, 0, 0, 0);
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                // p mod 2^32, then acc += rhu(p, r) = (p >> r) + bit (r - 1) of p;
-                // FP32 form: acc = fl(acc + fl(float(p)))
+                // p mod 2^32, then acc = fl(acc + fl(float(p)))
                 const uint32_t t = opaque((uint32_t(x[v]) << 8) + uint32_t(ll[v]));
                 const uint32_t p = (uint32_t(hh[v]) << 16) + opaque(t + rt + uint32_t(cb[v >> 2][v & 3]));
                 if (BLK)  // the chunk's term scaled on its own (v_ldexp_f32: one rounding)
                     acc[j][v] = __float_as_int(__fadd_rn(
                         __int_as_float(acc[j][v]),
                         __builtin_amdgcn_ldexpf(float(int32_t(p)), ea_lane + eb[v >> 2][v & 3])));
-                else if (F32)
-                    acc[j][v] = __float_as_int(__fadd_rn(__int_as_float(acc[j][v]), float(int32_t(p))));
                 else
-                    acc[j][v] = int32_t(uint32_t(acc[j][v]) + uint32_t(int32_t(p) >> r) +
-                                        __builtin_amdgcn_ubfe(p, rm1, rw));
+                    acc[j][v] = __float_as_int(__fadd_rn(__int_as_float(acc[j][v]), float(int32_t(p))));
             }
         }
 
@@ -579,10 +576,158 @@ __global__ __launch_bounds__(NT, 1) void dfp_kernel(Args g) {
         // stores are issued, so its wait does not include them
         int8_t *nx = lds + (stage ^ 1) * STAGE;
         if (more) {
-            if (F32 && g.shift) la.rhu1();
+            if (g.shift) la.rhu1();
             la.store(nx, nx + PLANE, tid);
             lb.store(nx + 2 * PLANE, nx + 3 * PLANE, tid);
             if (BLK && tid < 256) bexp[BLK ? stage ^ 1 : 0][tid] = ereg;
+        }
+        if (c + 1 >= c1) {
+            // unit done: lane holds acc[m][n .. n+3] for m = row lane % 32 of the
+            // wave's block, n = block col 8 q + 4 (lane / 32)
+            const int m = m0 + 32 * wm + (lane & 31);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int n = n0 + 64 * wn + 32 * j + 8 * q + 4 * (lane >> 5);
+                    int32_t *cp = g.acc + (int64_t(u / ntiles) * g.M + m) * g.N + n;
+                    v4i v = {acc[j][4 * q], acc[j][4 * q + 1], acc[j][4 * q + 2], acc[j][4 * q + 3]};
+                    if (!BLK && g.split == 1) {
+                        const int e = *g.ea + g.shift + *g.eb;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) v[i] = __float_as_int(scale_f32(__int_as_float(v[i]), e));
+                    }
+                    *reinterpret_cast<v4i *>(cp) = v;
+                }
+                acc[j] = v16i{};
+            }
+        }
+        if (!more) break;
+        __syncthreads();
+        u = nu; m0 = nm0; n0 = nn0; c = nc; c1 = nc1; stage ^= 1;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Integer form, corrections on the matrix cores.  With the lo digit
+// al = 127 - (a & 255) (in [-128, 127]), a = 256 ah + 127 - al and per term
+//   a b = 65536 ah bh - 256 (ah bl + al bh - 127 ah - 127 bh)
+//         + (al bl - 127 al - 127 bl) + 127^2,
+// so over a 64-term chunk, with every correction an int8 product against a
+// fragment of -127:
+//   H  = 16 + sum ah bh
+//   X2 = 64 + sum (ah bl + al bh) + sum (-127) ah + sum (-127) bh
+//   L2 = 64 + sum al bl + sum (-127) al + sum (-127) bl
+//   p  = 65536 H - 256 X2 + L2                                  (mod 2^32)
+// (the constants 16, 64, 64 are the accumulators' starting values and sum to
+// 65536*16 - 256*64 + 64 = 64 * 127^2).  |X2| < 2^23, so L2 - 256 X2 is one
+// 24-bit multiply-add; |H| < 2^21.  Per output and chunk the VALU does 5
+// operations: the two of p, and acc += (p >> r) + bit (r - 1) of p.
+// ---------------------------------------------------------------------------
+template <bool A_KM, bool B_KM, bool B16>
+__global__ __launch_bounds__(NT, 1) void dfpi_kernel(Args g) {
+    __shared__ __attribute__((aligned(16))) int8_t lds[2 * STAGE];
+    __shared__ uint32_t wmax[NT / 64];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;  // 32-row block wm of 4, 64-column half wn of 2
+    const int tiles_n = g.N / BN;
+    const int ntiles = (g.M / BM) * tiles_n;
+    const int nunits = ntiles * g.split;
+    const int nch = g.L / 64;
+    constexpr uint32_t LOX = 0x7f7f7f7fu;
+
+    auto unit = [&](int u, int &m0, int &n0, int &c0, int &c1) __attribute__((always_inline)) {
+        const int t = u % ntiles, sp = u / ntiles;
+        const int tm = t / tiles_n;
+        m0 = tm * BM;
+        n0 = (t - tm * tiles_n) * BN;
+        c0 = int(int64_t(nch) * sp / g.split);
+        c1 = int(int64_t(nch) * (sp + 1) / g.split);
+    };
+
+    int u = blockIdx.x;
+    if (u >= nunits) return;
+    int m0, n0, c0, c1;
+    unit(u, m0, n0, c0, c1);
+
+    Ld<A_KM> la;
+    Ld<B_KM> lb;
+    v16i acc[2];
+    acc[0] = v16i{};
+    acc[1] = v16i{};
+    uint32_t amax = 0;
+    la.load(g.a, g.lda, m0, 64 * c0, tid);
+    lb.load(g.b, g.ldb, n0, 64 * c0, tid);
+    la.store(lds, lds + PLANE, tid, LOX);
+    lb.store(lds + 2 * PLANE, lds + 3 * PLANE, tid, LOX);
+    __syncthreads();
+
+    const v4i cm = {int(0x81818181u), int(0x81818181u), int(0x81818181u), int(0x81818181u)};  // -127 bytes
+    const v16i c16 = {16, 16, 16, 16, 16, 16, 16, 16, 16, 16, 16, 16, 16, 16, 16, 16};
+    const v16i c64 = {64, 64, 64, 64, 64, 64, 64, 64, 64, 64, 64, 64, 64, 64, 64, 64};
+    const int r = g.r;
+    const uint32_t rm1 = r > 0 ? r - 1 : 0, rw = r > 0 ? 1 : 0;  // rounding bit (none for r = 0)
+    // -256 kept opaque, so that L2 - 256 X2 stays one v_mad_i32_i24 instead
+    // of a shift and a subtraction
+    int m256 = -256;
+    asm volatile("" : "+s"(m256));
+    int c = c0, stage = 0;
+    while (true) {
+        int nu = u, nm0 = m0, nn0 = n0, nc = c + 1, nc1 = c1;
+        bool more = true;
+        if (nc >= c1) {
+            nu = u + gridDim.x;
+            more = nu < nunits;
+            if (more) unit(nu, nm0, nn0, nc, nc1);
+        }
+        if (more) {
+            la.load(g.a, g.lda, nm0, 64 * nc, tid);
+            lb.load(g.b, g.ldb, nn0, 64 * nc, tid);
+        }
+        const int8_t *st = lds + stage * STAGE;
+        v4i ah[2], al[2], bh[2][2], bl[2][2];
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) {
+            ah[kh] = frag<A_KM>(st, 32 * wm, kh, lane);
+            al[kh] = frag<A_KM>(st + PLANE, 32 * wm, kh, lane);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                bh[j][kh] = frag<B_KM>(st + 2 * PLANE, 64 * wn + 32 * j, kh, lane);
+                bl[j][kh] = frag<B_KM>(st + 3 * PLANE, 64 * wn + 32 * j, kh, lane);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            v16i h = __builtin_amdgcn_mfma_i32_32x32x32_i8(bh[j][0], ah[0], c16, 0, 0, 0);
+            v16i x = __builtin_amdgcn_mfma_i32_32x32x32_i8(bl[j][0], ah[0], c64, 0, 0, 0);
+            v16i l = __builtin_amdgcn_mfma_i32_32x32x32_i8(bl[j][0], al[0], c64, 0, 0, 0);
+            x = __builtin_amdgcn_mfma_i32_32x32x32_i8(bh[j][0], al[0], x, 0, 0, 0);
+            l = __builtin_amdgcn_mfma_i32_32x32x32_i8(cm, al[0], l, 0, 0, 0);
+            x = __builtin_amdgcn_mfma_i32_32x32x32_i8(cm, ah[0], x, 0, 0, 0);
+            h = __builtin_amdgcn_mfma_i32_32x32x32_i8(bh[j][1], ah[1], h, 0, 0, 0);
+            l = __builtin_amdgcn_mfma_i32_32x32x32_i8(bl[j][0], cm, l, 0, 0, 0);
+            x = __builtin_amdgcn_mfma_i32_32x32x32_i8(bh[j][0], cm, x, 0, 0, 0);
+            l = __builtin_amdgcn_mfma_i32_32x32x32_i8(bl[j][1], al[1], l, 0, 0, 0);
+            x = __builtin_amdgcn_mfma_i32_32x32x32_i8(bl[j][1], ah[1], x, 0, 0, 0);
+            l = __builtin_amdgcn_mfma_i32_32x32x32_i8(cm, al[1], l, 0, 0, 0);
+            x = __builtin_amdgcn_mfma_i32_32x32x32_i8(bh[j][1], al[1], x, 0, 0, 0);
+            l = __builtin_amdgcn_mfma_i32_32x32x32_i8(bl[j][1], cm, l, 0, 0, 0);
+            x = __builtin_amdgcn_mfma_i32_32x32x32_i8(cm, ah[1], x, 0, 0, 0);
+            x = __builtin_amdgcn_mfma_i32_32x32x32_i8(bh[j][1], cm, x, 0, 0, 0);
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const uint32_t p = (uint32_t(h[v]) << 16) + opaque(uint32_t(__mul24(x[v], m256) + l[v]));
+                acc[j][v] = int32_t(uint32_t(acc[j][v]) + uint32_t(int32_t(p) >> r) + __builtin_amdgcn_ubfe(p, rm1, rw));
+            }
+        }
+
+        // the prefetched chunk goes to the other stage before the unit's
+        // stores are issued, so its wait does not include them
+        int8_t *nx = lds + (stage ^ 1) * STAGE;
+        if (more) {
+            la.store(nx, nx + PLANE, tid, LOX);
+            lb.store(nx + 2 * PLANE, nx + 3 * PLANE, tid, LOX);
         }
         if (B16 && c + 1 >= c1) {
             // unit done, block-shift form: the shift of the wave's block, then
@@ -624,8 +769,8 @@ __global__ __launch_bounds__(NT, 1) void dfp_kernel(Args g) {
             if (lane == 0) g.shifts[blk] = sb;
         }
         if (!B16 && c + 1 >= c1) {
-            // unit done: lane holds acc[m][n .. n+3] for m = row lane % 32 of the
-            // wave's block, n = block col 8 q + 4 (lane / 32)
+            // unit done (K-split partial tiles): lane holds acc[m][n .. n+3] for
+            // m = row lane % 32 of the wave's block, n = block col 8 q + 4 (lane / 32)
             const int m = m0 + 32 * wm + (lane & 31);
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
@@ -633,17 +778,8 @@ __global__ __launch_bounds__(NT, 1) void dfp_kernel(Args g) {
                 for (int q = 0; q < 4; ++q) {
                     const int n = n0 + 64 * wn + 32 * j + 8 * q + 4 * (lane >> 5);
                     int32_t *cp = g.acc + (int64_t(u / ntiles) * g.M + m) * g.N + n;
-                    v4i v = {acc[j][4 * q], acc[j][4 * q + 1], acc[j][4 * q + 2], acc[j][4 * q + 3]};
-                    if (F32 && !BLK && g.split == 1) {
-                        const int e = *g.ea + g.shift + *g.eb;
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) v[i] = __float_as_int(scale_f32(__int_as_float(v[i]), e));
-                    }
-                    *reinterpret_cast<v4i *>(cp) = v;
-                    if (!F32 && g.split == 1) {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) amax = max(amax, abs_u32(v[e]));
-                    }
+                    *reinterpret_cast<v4i *>(cp) = v4i{acc[j][4 * q], acc[j][4 * q + 1], acc[j][4 * q + 2],
+                                                       acc[j][4 * q + 3]};
                 }
                 acc[j] = v16i{};
             }
@@ -652,20 +788,18 @@ __global__ __launch_bounds__(NT, 1) void dfp_kernel(Args g) {
         __syncthreads();
         u = nu; m0 = nm0; n0 = nn0; c = nc; c1 = nc1; stage ^= 1;
     }
-    if (B16) {  // the workgroup's max |acc| to its slot (the loop has no reader of csum left)
-        if (lane == 0) csum[wave][0] = amax;
+    if (B16) {  // the workgroup's max |acc| to its slot
+        if (lane == 0) wmax[wave] = amax;
         __syncthreads();
         if (tid == 0) {
             uint32_t mx = 0;
 #pragma unroll
-            for (int w = 0; w < NT / 64; ++w) mx = max(mx, csum[w][0]);
+            for (int w = 0; w < NT / 64; ++w) mx = max(mx, wmax[w]);
             g.slots[blockIdx.x] = mx;
         }
-    } else if (!F32 && g.split == 1 && g.absmax) {
-        amax = wave_max_u32(amax);
-        if (lane == 0) publish_max_u32(g.absmax, amax);
     }
 }
+
 
 // FP32 form: out[e] = fl(total * 2^(*ea + shift + *eb)) with total the split
 // partial sums added in split order to 0.
@@ -1035,7 +1169,7 @@ int contract2(const int16_t *a, int64_t lda, const int16_t *b, int64_t ldb, int 
         g.bits = w.bits;
         g.shifts = w.shifts;
         g.slots = w.slots;
-        d2::dfp_kernel<A_KM, B_KM, false, false, true><<<dim3(grid), dim3(d2::NT), 0, st>>>(g);
+        d2::dfpi_kernel<A_KM, B_KM, true><<<dim3(grid), dim3(d2::NT), 0, st>>>(g);
         if (int rc = check_launch("dfp16 contraction")) return rc;
         const unsigned cpr = unsigned(N) / 8, bx = cpr < 256 ? cpr : 256, by = 256 / bx;
         unsigned gy = (unsigned(M) + by - 1) / by;
@@ -1044,7 +1178,7 @@ int contract2(const int16_t *a, int64_t lda, const int16_t *b, int64_t ldb, int 
             out, M, N, w.bits, w.shifts, w.slots, grid, ea, eb, r, e_out, status);
         return check_launch("dfp16 down-conversion");
     }
-    d2::dfp_kernel<A_KM, B_KM, false><<<dim3(grid), dim3(d2::NT), 0, st>>>(g);
+    d2::dfpi_kernel<A_KM, B_KM, false><<<dim3(grid), dim3(d2::NT), 0, st>>>(g);
     if (int rc = check_launch("dfp16 contraction")) return rc;
     // four 16-byte groups per thread: fewer requests in flight than one
     // group per thread, which measured twice as fast on 16 partials
@@ -1135,7 +1269,7 @@ int contract2_f32(const int16_t *a, int64_t lda, const int16_t *b, int64_t ldb, 
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
         cus = 256;
     const int units = tiles * S;
-    d2::dfp_kernel<A_KM, B_KM, true><<<dim3(units < cus ? units : cus), dim3(d2::NT), 0, st>>>(g);
+    d2::dfp_kernel<A_KM, B_KM><<<dim3(units < cus ? units : cus), dim3(d2::NT), 0, st>>>(g);
     return check_launch("dfp16 FP32 contraction");
 }
 
@@ -1383,7 +1517,7 @@ int dfp16_gemm_fwd_f32_blocked(const int16_t *X, const int32_t *eX, const int16_
             hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
             cus = 256;
         const int units = tiles * S;
-        d2::dfp_kernel<true, true, true, true><<<dim3(units < cus ? units : cus), dim3(d2::NT), 0, st>>>(g);
+        d2::dfp_kernel<true, true, true><<<dim3(units < cus ? units : cus), dim3(d2::NT), 0, st>>>(g);
     } else {
         Src16 a{X, K, int(M), int(K), aligned(X, 16) && K % 8 == 0};
         Src16 b{W, K, int(N), int(K), aligned(W, 16) && K % 8 == 0};
