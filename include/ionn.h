@@ -110,6 +110,20 @@ int int_linear_dgrad(const int8_t *dY, const int8_t *W, const int8_t *relu_act,
 int int_linear_wgrad(const int8_t *dY, const int8_t *X, int32_t *G, int64_t B,
                      int64_t IN, int64_t OUT, uint32_t *absmax_G, void *stream);
 
+/* The same weight gradient with a caller-provided workspace, for a small G
+ * over a long batch (G within 32 blocks of 32 x 32, at most 256 per side,
+ * B >= 4096): each range of the batch leaves its partial G in the workspace
+ * and one pass sums them (modulo 2^32, so the result is the one above bit
+ * for bit) and takes the max, instead of adding into a cleared G with
+ * atomics.  int_linear_wgrad_workspace_bytes gives the bytes needed (0 when
+ * the shape does not take this path; then, or with dY / X not 4-byte
+ * aligned, the call is int_linear_wgrad).  workspace: device, 4-byte
+ * aligned, at least that many bytes, else IONN_ERR_WORKSPACE. */
+size_t int_linear_wgrad_workspace_bytes(int64_t B, int64_t IN, int64_t OUT);
+int int_linear_wgrad_ws(const int8_t *dY, const int8_t *X, int32_t *G, int64_t B,
+                        int64_t IN, int64_t OUT, uint32_t *absmax_G, void *workspace,
+                        size_t workspace_bytes, void *stream);
+
 /* ------------------------------------------------------------------------ */
 /* NITI quantiser and update ([TI] section 3, steps 1-5).                    */
 /* ------------------------------------------------------------------------ */

@@ -25,6 +25,8 @@ SIGNATURES = {
     "int_linear_fwd": (_I, [_P, _P, _P, _I64, _I64, _I64, _P, _P]),
     "int_linear_dgrad": (_I, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P]),
     "int_linear_wgrad": (_I, [_P, _P, _P, _I64, _I64, _I64, _P, _P]),
+    "int_linear_wgrad_workspace_bytes": (ctypes.c_size_t, [_I64, _I64, _I64]),
+    "int_linear_wgrad_ws": (_I, [_P, _P, _P, _I64, _I64, _I64, _P, _P, ctypes.c_size_t, _P]),
     "niti_quantize": (_I, [_P, _I64, _P, _I, _I, _P, _P, _P]),
     "niti_quantize_update": (_I, [_P, _I64, _P, _I, _I, _P, _P, _P, _P]),
     "niti_quantize_update_clear": (_I, [_P, _I64, _P, _I, _I, _P, _P, _P, _P, _I64, _P]),

@@ -245,6 +245,29 @@ __device__ __forceinline__ void copy_to_lds(int8_t *dst, const int8_t *src, int 
 
 __device__ __forceinline__ int round16(int x) { return (x + 15) & ~15; }
 
+// nbytes from src to LDS at dst + (src mod 4), whatever src's alignment:
+// aligned dwords (dst is 4-byte aligned; the copy's first dword starts at
+// dst, its leading src mod 4 bytes are not part of the data), the last,
+// partial dword by bytes so nothing past src + nbytes is read.  Returns the
+// offset (src mod 4) at which the data starts.
+__device__ __forceinline__ int copy_to_lds_u(int8_t *dst, const int8_t *src, int nbytes) {
+    const int off = int(reinterpret_cast<uintptr_t>(src) & 3);
+    const uint32_t *a = reinterpret_cast<const uint32_t *>(src - off);
+    const int end = off + nbytes, full = end / 4;  // dwords wholly inside [src - off, src + nbytes)
+    uint32_t *d = reinterpret_cast<uint32_t *>(dst);
+    int q = threadIdx.x;
+    for (; q + 3 * int(blockDim.x) < full; q += 4 * blockDim.x) {
+        uint32_t w[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) w[u] = a[q + u * blockDim.x];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) d[q + u * blockDim.x] = w[u];
+    }
+    for (; q < full; q += blockDim.x) d[q] = a[q];
+    if (threadIdx.x < uint32_t(end - 4 * full)) dst[4 * full + threadIdx.x] = src[4 * full + threadIdx.x - off];
+    return off;
+}
+
 // Y for groups of g.spb samples, one output element per thread and step.
 __global__ __launch_bounds__(256) void conv_small_fwd(const int8_t *__restrict__ X, const int8_t *__restrict__ Wt,
                                                       int32_t *__restrict__ Y, int64_t N, SmallGeo g,
@@ -388,6 +411,120 @@ __global__ __launch_bounds__(256) void conv_small_wgrad(const int8_t *__restrict
 }
 
 // The small-sample geometry of a descriptor, or spb = 0 when it does not fit.
+// Full-row windows (no padding and KW = W, so every window spans whole input
+// rows): output row ho of sample n reads the contiguous bytes
+// X[n][ho RB .. ho RB + L) with RB = W Cin and L = KH RB, and channel co's
+// filter is the contiguous Wt[co][0 .. L) (OHWI).  L is a multiple of 4.
+constexpr int kRowsMaxCout = 8;
+
+__device__ __forceinline__ bool rows_geo(const SmallGeo &g) { return g.P == 0 && g.KW == g.W; }
+
+// Y (int32, [n][ho][co]) for groups of g.spb staged samples: one (sample,
+// output row) per thread, its L / 4 window words read as two aligned LDS
+// dwords and v_alignbyte, one v_dot4 per word and channel.
+__global__ __launch_bounds__(256) void conv_rows_fwd(const int8_t *__restrict__ X, const int8_t *__restrict__ Wt,
+                                                     int32_t *__restrict__ Y, int64_t N, SmallGeo g,
+                                                     uint32_t *__restrict__ absmax) {
+    __shared__ __attribute__((aligned(16))) int8_t lds[kSmallLds];
+    int8_t *ws = lds, *xs = lds + round16(g.w_b);
+    copy_to_lds(ws, Wt, g.w_b);
+    const uint32_t *w32 = reinterpret_cast<const uint32_t *>(ws);
+    const int RB = g.W * g.Cin, LW = g.KH * RB / 4, Cout = g.Cout;
+    const int dsm = 256 / g.Ho, dho = 256 - dsm * g.Ho;  // (sample, row) step per 256 pairs
+    uint32_t amax = 0;
+    for (int64_t n0 = int64_t(blockIdx.x) * g.spb; n0 < N; n0 += int64_t(gridDim.x) * g.spb) {
+        const int ns = int(N - n0 < g.spb ? N - n0 : g.spb);
+        __syncthreads();
+        const int x0 = copy_to_lds_u(xs, X + n0 * g.in_b, ns * g.in_b);
+        __syncthreads();
+        int sm = int(threadIdx.x) / g.Ho, ho = int(threadIdx.x) - sm * g.Ho;
+        for (; sm < ns;) {
+            const int start = x0 + sm * g.in_b + ho * RB;
+            const uint32_t *d = reinterpret_cast<const uint32_t *>(xs + (start & ~3));
+            const uint32_t sh = uint32_t(start & 3);
+            int32_t acc[kRowsMaxCout];
+#pragma unroll
+            for (int co = 0; co < kRowsMaxCout; ++co) acc[co] = 0;
+            uint32_t lo = d[0];
+            for (int i = 0; i < LW; ++i) {
+                const uint32_t hi = d[i + 1];
+                const int w = int(__builtin_amdgcn_alignbyte(hi, lo, sh));  // window bytes 4i .. 4i + 3
+                lo = hi;
+#pragma unroll
+                for (int co = 0; co < kRowsMaxCout; ++co)
+                    if (co < Cout) acc[co] = __builtin_amdgcn_sdot4(w, int(w32[co * LW + i]), acc[co], false);
+            }
+            int32_t *yp = Y + ((n0 + sm) * g.Ho + ho) * Cout;
+#pragma unroll
+            for (int co = 0; co < kRowsMaxCout; ++co)
+                if (co < Cout) {
+                    yp[co] = acc[co];
+                    amax = max(amax, abs_u32(acc[co]));
+                }
+            sm += dsm;
+            ho += dho;
+            if (ho >= g.Ho) {
+                ho -= g.Ho;
+                ++sm;
+            }
+        }
+    }
+    if (absmax) {
+        amax = wave_max_u32(amax);
+        if ((threadIdx.x & 63) == 0) publish_max_u32(absmax, amax);
+    }
+}
+
+// G += (int32, OHWI, zeroed by the caller) over groups of staged samples:
+// thread slot s = (co, word jw) keeps the four sums of G[co][4 jw .. 4 jw + 3];
+// the 1024 / slots slices of a workgroup take every (1024 / slots)-th output
+// row and meet in LDS; the workgroup adds its sums with integer atomics
+// (exact in any order).
+constexpr int kRowsWgradThreads = 1024;
+
+__global__ __launch_bounds__(kRowsWgradThreads) void conv_rows_wgrad(const int8_t *__restrict__ dY,
+                                                                     const int8_t *__restrict__ X,
+                                                                     int32_t *__restrict__ G, int64_t N, SmallGeo g) {
+    __shared__ __attribute__((aligned(16))) int8_t lds[kSmallLds];
+    __shared__ uint32_t red[4][kRowsWgradThreads];
+    int8_t *xs = lds, *ds = lds + round16(g.spb * g.in_b + 16);
+    const int RB = g.W * g.Cin, LW = g.KH * RB / 4, L = 4 * LW;
+    const int slots = g.Cout * LW, S = kRowsWgradThreads / slots;
+    const int t = threadIdx.x, slot = t % slots, sub = t / slots;
+    const int co = slot / LW, jw = slot - co * LW;
+    uint32_t a[4] = {0, 0, 0, 0};
+    for (int64_t n0 = int64_t(blockIdx.x) * g.spb; n0 < N; n0 += int64_t(gridDim.x) * g.spb) {
+        const int ns = int(N - n0 < g.spb ? N - n0 : g.spb);
+        __syncthreads();
+        const int8_t *xsd = xs + copy_to_lds_u(xs, X + n0 * g.in_b, ns * g.in_b);
+        const int8_t *dsd = ds + copy_to_lds_u(ds, dY + n0 * g.out_b, ns * g.out_b);
+        __syncthreads();
+        if (sub < S) {
+            for (int sm = 0; sm < ns; ++sm) {
+                for (int ho = sub; ho < g.Ho; ho += S) {
+                    const int start = int(xsd - xs) + sm * g.in_b + ho * RB + 4 * jw;
+                    const uint32_t *d = reinterpret_cast<const uint32_t *>(xs + (start & ~3));
+                    const uint32_t w = __builtin_amdgcn_alignbyte(d[1], d[0], uint32_t(start & 3));
+                    const int32_t dy = dsd[(sm * g.Ho + ho) * g.Cout + co];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) a[e] += uint32_t(dy * int32_t(int8_t(uint8_t(w >> (8 * e)))));
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) red[e][t] = sub < S ? a[e] : 0u;
+    __syncthreads();
+    if (sub == 0 && slot < slots) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            uint32_t tot = 0;
+            for (int z = 0; z < S; ++z) tot += red[e][z * slots + slot];
+            if (tot) atomicAdd(G + co * L + 4 * jw + e, int32_t(tot));
+        }
+    }
+}
+
 SmallGeo small_geo(const ionn_conv_desc *d, int which) {
     SmallGeo g{};
     const int64_t Ho = d->H + 2 * int64_t(d->pad) - d->KH + 1, Wo = d->W + 2 * int64_t(d->pad) - d->KW + 1;
@@ -405,6 +542,15 @@ SmallGeo small_geo(const ionn_conv_desc *d, int which) {
     g = SmallGeo{int(d->H), int(d->W), int(d->Cin), int(d->Cout), d->KH, d->KW, d->pad, int(Ho), int(Wo),
                  int(in_b), int(out_b), int(w_b), int(spb)};
     return g;
+}
+
+// Whether the full-row-window kernels take the geometry: no padding, KW = W,
+// a window length L = KH W Cin that is a multiple of 4 (at most 1024 bytes),
+// at most 8 output channels and at most 256 (channel, window word) slots.
+bool rows_path(const ionn_conv_desc *d) {
+    const int64_t L = int64_t(d->KH) * d->W * d->Cin;
+    return d->pad == 0 && d->KW == d->W && L % 4 == 0 && L <= 1024 && d->Cout >= 1 &&
+           d->Cout <= kRowsMaxCout && d->Cout * (L / 4) <= 256;
 }
 
 unsigned small_blocks(int64_t N, int spb, int64_t cap) {
@@ -547,6 +693,14 @@ int int_conv_fwd(const int8_t *X, const int8_t *Wt, int32_t *Y, const ionn_conv_
         IONN_REQUIRE(aligned(Y, 4) && aligned(absmax_Y, 4), IONN_ERR_ALIGN,
                      "int_conv_fwd: Y/absmax must be 4-byte aligned");
         const SmallGeo sg = small_geo(desc, 0);
+        if (sg.spb > 0 && Cin > 0 && rows_path(desc)) {
+            // the window reads run up to 3 bytes past the staged samples
+            SmallGeo rg = sg;
+            while (rg.spb > 1 && ((rg.w_b + 15) & ~15) + int64_t(rg.spb) * rg.in_b + 16 > kSmallLds) --rg.spb;
+            conv_rows_fwd<<<dim3(small_blocks(desc->N, rg.spb, 2048)), dim3(256), 0, as_stream(stream)>>>(
+                X, Wt, Y, desc->N, rg, absmax_Y);
+            return check_launch("int_conv_fwd");
+        }
         if (sg.spb > 0 && Cin > 0) {
             conv_small_fwd<<<dim3(small_blocks(desc->N, sg.spb, 2048)), dim3(256), 0, as_stream(stream)>>>(
                 X, Wt, Y, desc->N, sg, absmax_Y);
@@ -681,7 +835,11 @@ int int_conv_wgrad(const int8_t *dY, const int8_t *X, int32_t *G, const ionn_con
         zero_i32_kernel<<<dim3(direct_blocks(n_g)), dim3(256), 0, st>>>(G, n_g);
         if (int rc = check_launch("int_conv_wgrad")) return rc;
         const SmallGeo sg = small_geo(desc, 2);
-        if (rows > 0 && sg.spb > 0) {
+        if (rows > 0 && sg.spb > 0 && rows_path(desc)) {
+            conv_rows_wgrad<<<dim3(small_blocks(desc->N, sg.spb, 256)), dim3(kRowsWgradThreads), 0, st>>>(
+                dY, X, G, desc->N, sg);
+            if (int rc = check_launch("int_conv_wgrad")) return rc;
+        } else if (rows > 0 && sg.spb > 0) {
             conv_small_wgrad<<<dim3(small_blocks(desc->N, sg.spb, 1024)), dim3(256), 0, st>>>(dY, X, G, desc->N, sg,
                                                                                               int(n_g));
             if (int rc = check_launch("int_conv_wgrad")) return rc;

@@ -12,6 +12,7 @@
 // 64x64 tiles.  The epilogue fuses dgrad's ReLU mask and the max-abs that
 // feeds the NITI shift.
 #include "gemm256.h"
+#include "wgrad_long.h"
 
 namespace ionn {
 
@@ -182,9 +183,18 @@ int int_linear_wgrad(const int8_t *dY, const int8_t *X, int32_t *G, int64_t B, i
         return check_launch("int_linear_wgrad");
     }
     // A small G over a long batch (a layer of a few hundred units trained on
-    // a large batch) has too few 64 x 64 tiles to fill the chip: split the
-    // batch over up to 32 ranges, add the ranges with integer atomics into
-    // the zeroed G (exact in any order), then take the max in its own pass.
+    // a large batch): batch ranges reduced by the matrix cores from row
+    // copies in LDS, added into the zeroed G with integer atomics (exact in
+    // any order), then the max in its own pass.
+    if (wl::wgrad_long_fits(K, M, N, dY, X)) {
+        if (int rc = zero_output(G, OUT * IN, st, "int_linear_wgrad")) return rc;
+        wl::wgrad_long_launch(dY, X, K, M, N, G, nullptr, st);
+        if (int rc = check_launch("int_linear_wgrad")) return rc;
+        if (absmax_G) return launch_absmax_i32(G, OUT * IN, absmax_G, st);
+        return IONN_OK;
+    }
+    // Otherwise too few 64 x 64 tiles to fill the chip: split the batch over
+    // up to 32 ranges of the generic kernel, with the same atomics.
     const int tiles = ((M + 63) / 64) * ((N + 63) / 64);
     const int ksteps = (K + 63) / 64;
     if (tiles < 64 && ksteps >= 64) {
@@ -200,6 +210,36 @@ int int_linear_wgrad(const int8_t *dY, const int8_t *X, int32_t *G, int64_t B, i
     }
     launch_linear(sa, sb, ep, M, N, K, tile_aligned(M, N, K) && sa.vec && sb.vec && ep.vec, st);
     return check_launch("int_linear_wgrad");
+}
+
+size_t int_linear_wgrad_workspace_bytes(int64_t B, int64_t IN, int64_t OUT) {
+    if (!dims_ok(B, IN, OUT) || !wl::wgrad_long_fits(B, OUT, IN, nullptr, nullptr)) return 0;
+    return size_t(wl::wgrad_long_groups(B)) * size_t(OUT * IN) * sizeof(int32_t);
+}
+
+int int_linear_wgrad_ws(const int8_t *dY, const int8_t *X, int32_t *G, int64_t B, int64_t IN, int64_t OUT,
+                        uint32_t *absmax_G, void *workspace, size_t workspace_bytes, void *stream) {
+    clear_error();
+    IONN_REQUIRE(dims_ok(B, IN, OUT), IONN_ERR_SHAPE,
+                 "int_linear_wgrad_ws: sizes must be in [0, 2^31): B=%lld IN=%lld OUT=%lld", (long long)B,
+                 (long long)IN, (long long)OUT);
+    const size_t need = int_linear_wgrad_workspace_bytes(B, IN, OUT);
+    if (need == 0 || OUT == 0 || IN == 0 || !wl::wgrad_long_fits(B, OUT, IN, dY, X))
+        return int_linear_wgrad(dY, X, G, B, IN, OUT, absmax_G, stream);
+    IONN_REQUIRE(G && dY && X, IONN_ERR_ARG, "int_linear_wgrad_ws: NULL tensor");
+    IONN_REQUIRE(aligned(G, 4) && aligned(absmax_G, 4), IONN_ERR_ALIGN,
+                 "int_linear_wgrad_ws: G/absmax must be 4-byte aligned");
+    IONN_REQUIRE(workspace != nullptr && aligned(workspace, 4) && workspace_bytes >= need, IONN_ERR_WORKSPACE,
+                 "int_linear_wgrad_ws: needs a 4-byte aligned workspace of %zu bytes", need);
+    hipStream_t st = as_stream(stream);
+    int32_t *part = static_cast<int32_t *>(workspace);
+    const int nw = wl::wgrad_long_launch(dY, X, B, int(OUT), int(IN), G, part, st);
+    if (int rc = check_launch("int_linear_wgrad_ws")) return rc;
+    const int64_t n = OUT * IN;
+    int64_t blocks = (n + 63) / 64;
+    if (blocks > 2048) blocks = 2048;
+    wl::wgrad_long_sum<<<dim3(unsigned(blocks)), dim3(256), 0, st>>>(part, nw, n, G, absmax_G);
+    return check_launch("int_linear_wgrad_ws");
 }
 
 }  // extern "C"

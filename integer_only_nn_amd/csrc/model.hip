@@ -93,8 +93,8 @@ struct Plan {
     int32_t *z32, *g32, *gb, *e32;
     int8_t *delta[2];
     uint32_t *scal;
-    void *bgws, *cws;
-    size_t bg_bytes, cw_bytes, z_bytes;
+    void *bgws, *cws, *lws;
+    size_t bg_bytes, cw_bytes, lw_bytes, z_bytes;
     size_t total;
 };
 
@@ -107,7 +107,7 @@ Plan plan(const ionn_layer *layers, int L, int64_t B, void *base) {
         return base ? static_cast<char *>(base) + o : nullptr;
     };
     int64_t max_io = 0, max_out = 0, max_w = 0, max_c = 0;
-    size_t bg = 0, cw = 0;
+    size_t bg = 0, cw = 0, lw = 0;
     for (int l = 0; l < L; ++l) {
         const ionn_layer &Ly = layers[l];
         max_io = max(max_io, max(in_size(Ly), out_size(Ly)));
@@ -118,6 +118,8 @@ Plan plan(const ionn_layer *layers, int L, int64_t B, void *base) {
         if (is_conv(Ly)) {
             const ionn_conv_desc d = desc_of(Ly, B);
             cw = max(cw, int_conv_wgrad_workspace_bytes(&d));
+        } else {
+            lw = max(lw, int_linear_wgrad_workspace_bytes(B, Ly.Cin, Ly.Cout));
         }
     }
     for (int l = 0; l < L; ++l) p.act[l] = reinterpret_cast<int8_t *>(take(size_t(B * out_size(layers[l]))));
@@ -133,6 +135,8 @@ Plan plan(const ionn_layer *layers, int L, int64_t B, void *base) {
     p.bgws = take(bg);
     p.cw_bytes = cw;
     p.cws = cw ? take(cw) : nullptr;
+    p.lw_bytes = lw;
+    p.lws = lw ? take(lw) : nullptr;
     p.total = off;
     return p;
 }
@@ -739,7 +743,8 @@ int ionn_model_backward(const ionn_layer *layers, int L, const int8_t *X, int64_
             const ionn_conv_desc d = desc_of(Ly, B);
             if (int rc = int_conv_wgrad(dl, a_in, p.g32, &d, am_g, p.cws, p.cw_bytes, stream)) return rc;
         } else {
-            if (int rc = int_linear_wgrad(dl, a_in, p.g32, B, Ly.Cin, Ly.Cout, am_g, stream)) return rc;
+            if (int rc = int_linear_wgrad_ws(dl, a_in, p.g32, B, Ly.Cin, Ly.Cout, am_g, p.lws, p.lw_bytes, stream))
+                return rc;
         }
         // propagated delta, with the pre-update weights
         if (l > 0) {

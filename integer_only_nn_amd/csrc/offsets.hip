@@ -136,6 +136,55 @@ __global__ __launch_bounds__(64 * BG_WAVES) void bias_grad_kernel(const int8_t *
     }
 }
 
+// Column sums of a narrow d[M][C] (C < 64, d 4-byte aligned): the M*C bytes
+// read as one flat array of dwords.  Thread t of the grid takes dwords t,
+// t + T, t + 2T, ... (T threads in all, 4T a multiple of C), so byte e of every
+// dword it reads lies in the same column (4t + e) mod C.  The thread's four
+// sums meet the workgroup's in LDS bins; the workgroup's row goes to
+// part[blockIdx.x][c].  Block 0 adds the last n mod 4 bytes.
+__global__ __launch_bounds__(256) void bias_grad_narrow(const int8_t *__restrict__ d, int64_t n, int C,
+                                                        int32_t *__restrict__ part) {
+    __shared__ uint32_t bins[64];
+    if (threadIdx.x < 64) bins[threadIdx.x] = 0;
+    __syncthreads();
+    const int64_t t = int64_t(blockIdx.x) * blockDim.x + threadIdx.x, T = int64_t(gridDim.x) * blockDim.x;
+    const uint32_t *w = reinterpret_cast<const uint32_t *>(d);
+    const int64_t nw = n / 4;
+    uint32_t s[4] = {0, 0, 0, 0};
+    auto add = [&](uint32_t x) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s[e] += uint32_t(int32_t(int8_t(uint8_t(x >> (8 * e)))));
+    };
+    int64_t i = t;
+    for (; i + 3 * T < nw; i += 4 * T) {  // four loads in flight
+        uint32_t x[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) x[u] = __builtin_nontemporal_load(w + i + u * T);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) add(x[u]);
+    }
+    for (; i < nw; i += T) add(w[i]);
+    const int c0 = int((4 * t) % C);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) atomicAdd(&bins[(c0 + e) % C], s[e]);
+    if (blockIdx.x == 0 && threadIdx.x == 0)
+        for (int64_t j = 4 * nw; j < n; ++j) atomicAdd(&bins[j % C], uint32_t(int32_t(d[j])));
+    __syncthreads();
+    if (int(threadIdx.x) < C) part[int64_t(blockIdx.x) * C + threadIdx.x] = int32_t(bins[threadIdx.x]);
+}
+
+// Workgroups of bias_grad_narrow: at most `cap` (the rows of partial sums the
+// workspace holds) and at most 256, a multiple of C / gcd(C, 1024) so that
+// the dword stride 4 * 256 * G is a multiple of C; 0 when no such count fits.
+int64_t narrow_blocks(int64_t C, int64_t cap) {
+    int64_t a = C, b = 1024;
+    while (b) { const int64_t r = a % b; a = b; b = r; }
+    const int64_t q = C / a;
+    int64_t g = cap < 256 ? cap : 256;
+    g -= g % q;
+    return g;
+}
+
 // gb[c] = sum over the ny row ranges of part[y][c] (modulo 2^32).
 __global__ __launch_bounds__(256) void bias_grad_sum(const int32_t *__restrict__ part, int64_t ny, int64_t C,
                                                      int32_t *__restrict__ gb) {
@@ -242,6 +291,16 @@ int bg_scratch(hipStream_t st, int32_t **out) {
 int bias_grad_launch(const int8_t *d, int64_t M, int64_t C, int32_t *gb, const BgGrid &g, int32_t *part,
                      hipStream_t st, const char *name) {
     IONN_REQUIRE(g.gx <= 0x7fffffff && g.gy <= 65535, IONN_ERR_SHAPE, "%s: grid too large", name);
+    if (C < 64 && C % 16 != 0 && aligned(d, 4) && M * C >= (int64_t(1) << 16)) {
+        // narrow rows: one lane per column would leave most lanes idle
+        const int64_t nb = narrow_blocks(C, g.gy);
+        if (nb >= 1) {
+            bias_grad_narrow<<<dim3(unsigned(nb)), dim3(256), 0, st>>>(d, M * C, int(C), part);
+            if (int rc = check_launch(name)) return rc;
+            bias_grad_sum<<<dim3(unsigned((C + 255) / 256)), dim3(256), 0, st>>>(part, nb, C, gb);
+            return check_launch(name);
+        }
+    }
     const dim3 grid{unsigned(g.gx), unsigned(g.gy), 1u}, block{64u * BG_WAVES, 1u, 1u};
     if (g.vec) bias_grad_kernel<true><<<grid, block, 0, st>>>(d, M, C, g.rows, part);
     else bias_grad_kernel<false><<<grid, block, 0, st>>>(d, M, C, g.rows, part);

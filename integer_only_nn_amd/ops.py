@@ -79,6 +79,21 @@ def int_linear_wgrad(dY, X, G, absmax_G=None, stream=None):
           "int_linear_wgrad")
 
 
+def int_linear_wgrad_workspace_bytes(B, IN, OUT):
+    return int(lib().int_linear_wgrad_workspace_bytes(int(B), int(IN), int(OUT)))
+
+
+def int_linear_wgrad_ws(dY, X, G, workspace, absmax_G=None, stream=None):
+    B, OUT = dY.shape
+    IN = X.shape[1]
+    assert tuple(X.shape) == (B, IN) and tuple(G.shape) == (OUT, IN), "shape mismatch"
+    check(lib().int_linear_wgrad_ws(_p(dY, i8, name="dY"), _p(X, i8, name="X"), _p(G, i32, name="G"),
+                                    B, IN, OUT, _p(absmax_G, u32, 1, "absmax_G"),
+                                    _p(workspace, None, name="workspace"),
+                                    workspace.numel() * workspace.element_size() if workspace is not None else 0,
+                                    _stream(stream)), "int_linear_wgrad_ws")
+
+
 def niti_quantize(acc, absmax, target_bits, relu, out, shift_out=None, stream=None):
     assert acc.numel() == out.numel()
     check(lib().niti_quantize(_p(acc, i32, name="acc"), acc.numel(), _p(absmax, u32, 1, "absmax"),

@@ -22,7 +22,11 @@ GEOMS = [(8, 64, 2, 1, 3, 16, 2, 0),     # the page's example: 64x2x1 -> 49x1x3
          (1000, 64, 2, 1, 3, 16, 2, 0),  # the example network's layer, a ragged last sample group
          (6, 10, 10, 8, 12, 3, 3, 1),    # 864 weights: four weight chunks in the staged wgrad
          (5, 12, 12, 8, 16, 3, 3, 0),    # 1152 weights: staged fwd/dgrad, direct wgrad
-         (1, 1, 1, 1, 1, 1, 1, 0)]
+         (1, 1, 1, 1, 1, 1, 1, 0),
+         # full-row windows (no padding, KW = W): the row kernels, with odd
+         # sample sizes, every channel count up to 8, and one channel past it
+         (7, 10, 3, 2, 5, 4, 3, 0), (3, 9, 1, 4, 8, 3, 1, 0), (4096, 64, 2, 1, 3, 16, 2, 0),
+         (2, 6, 2, 2, 9, 3, 2, 0), (5, 33, 2, 2, 1, 1, 2, 0)]
 
 
 def _u32(t):

@@ -51,6 +51,55 @@ def test_contractions_vs_oracle(B, IN, OUT):
     assert am == [oracle.absmax(Yo), oracle.absmax(dXo), oracle.absmax(Go)]
 
 
+# small G over a long batch: the LDS row-copy path (byte and dword copies,
+# one to 32 blocks of 32 x 32, ragged batch tails) and, past 32 blocks, the
+# generic split
+LONG_WGRAD = [(65536, 147, 160), (65536, 160, 2), (5000, 33, 7), (4097, 256, 128), (9000, 250, 130),
+              (20000, 64, 96)]
+
+
+@pytest.mark.parametrize("B,IN,OUT", LONG_WGRAD)
+def test_wgrad_long_batch(B, IN, OUT):
+    say("wgrad long", B, IN, OUT)
+    d = ionn_synth.single_linear(B=B, IN=IN, OUT=OUT, seed=B + 3 * IN + OUT)
+    X, dY = d["X"], d["dY"]
+    G = torch.empty(OUT, IN, dtype=torch.int32, device=dev())
+    am = torch.zeros(1, dtype=torch.int32, device=dev())
+    ops.int_linear_wgrad(to_dev(dY), to_dev(X), G, absmax_G=am)
+    want = fast.linear_wgrad(dY, X)
+    np.testing.assert_array_equal(host(G), want)
+    assert u32(am) == oracle.absmax(want)
+
+
+@pytest.mark.parametrize("B,IN,OUT", [(65536, 147, 160), (65536, 160, 2), (5000, 33, 7), (4097, 256, 128)])
+def test_wgrad_long_batch_workspace(B, IN, OUT):
+    # the partial-sums form gives the same G and max as the oracle; called
+    # twice in a row (the workspace is overwritten, never cleared)
+    say("wgrad long ws", B, IN, OUT)
+    ws = torch.empty(ops.int_linear_wgrad_workspace_bytes(B, IN, OUT), dtype=torch.uint8, device=dev())
+    assert ws.numel() > 0
+    for seed in (1, 2):
+        d = ionn_synth.single_linear(B=B, IN=IN, OUT=OUT, seed=seed * 7 + B + IN)
+        X, dY = d["X"], d["dY"]
+        G = torch.full((OUT, IN), 99, dtype=torch.int32, device=dev())
+        am = torch.zeros(1, dtype=torch.int32, device=dev())
+        ops.int_linear_wgrad_ws(to_dev(dY), to_dev(X), G, ws, absmax_G=am)
+        want = fast.linear_wgrad(dY, X)
+        np.testing.assert_array_equal(host(G), want)
+        assert u32(am) == oracle.absmax(want)
+
+
+def test_wgrad_long_batch_extremes():
+    # every product 16384 or -16256: the largest sums the long path meets
+    B, IN, OUT = 8192, 40, 24
+    X = np.full((B, IN), -128, np.int8)
+    X[:, ::3] = 127
+    dY = np.full((B, OUT), -128, np.int8)
+    G = torch.empty(OUT, IN, dtype=torch.int32, device=dev())
+    ops.int_linear_wgrad(to_dev(dY), to_dev(X), G)
+    np.testing.assert_array_equal(host(G), fast.linear_wgrad(dY, X))
+
+
 @pytest.mark.parametrize("B,IN,OUT", [(16, 64, 32), (256, 256, 128), (33, 100, 17), (1024, 1024, 256)])
 def test_dgrad_relu_mask(B, IN, OUT):
     d = ionn_synth.single_linear(B=B, IN=IN, OUT=OUT, seed=7)

@@ -124,7 +124,10 @@ def test_oss_unaligned_and_edges():
                          torch.empty((0, 8), dtype=torch.int8, device=dev()))
 
 
-BG_SHAPES = [(0, 5), (1, 1), (7, 33), (129, 64), (1000, 4096 + 16), (8192, 4096)]
+BG_SHAPES = [(0, 5), (1, 1), (7, 33), (129, 64), (1000, 4096 + 16), (8192, 4096),
+             # narrow rows (C < 64, not a multiple of 16): the flat-array path,
+             # with n mod 4 tail bytes, odd C and C sharing factors with 1024
+             (65537, 3), (65536, 2), (20000, 17), (6000, 48), (3211264, 3)]
 
 
 @pytest.mark.parametrize("M,C", BG_SHAPES)

@@ -48,6 +48,25 @@ def test_linear_validation():
     assert lib.int_linear_wgrad(None, None, None, 4, 0, 4, None, None) == OK
 
 
+def test_linear_wgrad_workspace_query_and_checks():
+    # a small G over a long batch takes the partial-sums path: groups of at
+    # least 512 rows, at most 128, times the G size
+    need = lib.int_linear_wgrad_workspace_bytes(65536, 147, 160)
+    assert need == 128 * 147 * 160 * 4
+    assert lib.int_linear_wgrad_workspace_bytes(5000, 33, 7) == 10 * 33 * 7 * 4
+    # short batches, large G, bad sizes: no workspace (the call is int_linear_wgrad)
+    assert lib.int_linear_wgrad_workspace_bytes(100, 64, 32) == 0
+    assert lib.int_linear_wgrad_workspace_bytes(65536, 512, 512) == 0
+    assert lib.int_linear_wgrad_workspace_bytes(-1, 4, 4) == 0
+    f = lib.int_linear_wgrad_ws
+    assert f(FAKE, FAKE, FAKE, 65536, 147, 160, None, None, need - 4, None) == WS
+    assert "workspace" in _err()
+    assert f(FAKE, FAKE, FAKE, 65536, 147, 160, None, FAKE_ODD, need, None) == WS
+    assert f(FAKE, FAKE, None, 65536, 147, 160, None, FAKE, need, None) == ARG
+    assert f(FAKE, FAKE, FAKE_ODD, 65536, 147, 160, None, FAKE, need, None) == ALIGN
+    assert f(FAKE, FAKE, FAKE, -1, 147, 160, None, FAKE, need, None) == SHAPE
+
+
 def test_niti_validation():
     assert lib.niti_quantize(FAKE, 8, None, 7, 0, FAKE, None, None) == ARG
     assert lib.niti_quantize(FAKE, 8, FAKE, 0, 0, FAKE, None, None) == RANGE
