@@ -246,9 +246,11 @@ int int_conv_dgrad_requant(const int8_t *dY, const int8_t *Wt, int8_t *dX8,
                            void *workspace, size_t workspace_bytes, void *stream);
 
 /* Device workspace (bytes) that lets int_conv_wgrad take its fast path for
- * this geometry (64 input and 64 output channels, W up to about 100): one
- * partial G per compute unit plus one per 16 of them.  0 when the geometry
- * has no fast path (the call then needs no workspace). */
+ * this geometry: for 64 input and 64 output channels (3x3, W up to about
+ * 100), one partial G per compute unit plus one per 16 of them; for a
+ * full-row-window filter (no padding, KW = W, KH*W*Cin a multiple of 4, at
+ * most 8 output channels), one partial G per workgroup (at most 1024).  0
+ * when the geometry has no fast path (the call then needs no workspace). */
 size_t int_conv_wgrad_workspace_bytes(const ionn_conv_desc *desc);
 
 /* G[co,kh,kw,ci] = sum_{n,h,w} dY[n,h,w,co] * X[n,h+kh-P,w+kw-P,ci] over the

@@ -23,6 +23,7 @@
 // direct kernels: one thread per output element of fwd and dgrad, one per
 // weight element and pixel range of wgrad.  These are small-layer paths.
 #include "gemm_core.h"
+#include "wgrad_long.h"
 #include "conv3x3.h"
 #include "conv_pipe.h"
 
@@ -475,7 +476,8 @@ __global__ __launch_bounds__(256) void conv_rows_fwd(const int8_t *__restrict__ 
     }
 }
 
-// G += (int32, OHWI, zeroed by the caller) over groups of staged samples:
+// G += (int32, OHWI, zeroed by the caller) over groups of staged samples, or
+// (part not null) each workgroup's sums to part[blockIdx.x][Cout L]:
 // thread slot s = (co, word jw) keeps the four sums of G[co][4 jw .. 4 jw + 3];
 // the 1024 / slots slices of a workgroup take every (1024 / slots)-th output
 // row and meet in LDS; the workgroup adds its sums with integer atomics
@@ -484,7 +486,8 @@ constexpr int kRowsWgradThreads = 1024;
 
 __global__ __launch_bounds__(kRowsWgradThreads) void conv_rows_wgrad(const int8_t *__restrict__ dY,
                                                                      const int8_t *__restrict__ X,
-                                                                     int32_t *__restrict__ G, int64_t N, SmallGeo g) {
+                                                                     int32_t *__restrict__ G, int64_t N, SmallGeo g,
+                                                                     int32_t *__restrict__ part) {
     __shared__ __attribute__((aligned(16))) int8_t lds[kSmallLds];
     __shared__ uint32_t red[4][kRowsWgradThreads];
     int8_t *xs = lds, *ds = lds + round16(g.spb * g.in_b + 16);
@@ -520,7 +523,10 @@ __global__ __launch_bounds__(kRowsWgradThreads) void conv_rows_wgrad(const int8_
         for (int e = 0; e < 4; ++e) {
             uint32_t tot = 0;
             for (int z = 0; z < S; ++z) tot += red[e][z * slots + slot];
-            if (tot) atomicAdd(G + co * L + 4 * jw + e, int32_t(tot));
+            if (part)
+                part[int64_t(blockIdx.x) * g.Cout * L + co * L + 4 * jw + e] = int32_t(tot);
+            else if (tot)
+                atomicAdd(G + co * L + 4 * jw + e, int32_t(tot));
         }
     }
 }
@@ -813,8 +819,23 @@ int int_conv_dgrad_requant(const int8_t *dY, const int8_t *Wt, int8_t *dX8, cons
                               workspace_bytes, stream, "int_conv_dgrad_requant");
 }
 
+// Workgroups of the full-row-window wgrad (one group of staged samples per
+// workgroup and step; at most 1024 with per-workgroup partials, 256 when they
+// add into G with atomics), or 0 when the geometry is not one.
+int64_t rows_wgrad_groups(const ionn_conv_desc *d, int64_t cap = 1024) {
+    if (geom33(d) || !rows_path(d)) return 0;
+    const int64_t Ho = out_h(d), Wo = out_w(d);
+    if (Ho <= 0 || Wo <= 0 || d->N <= 0) return 0;
+    const SmallGeo sg = small_geo(d, 2);
+    if (sg.spb <= 0) return 0;
+    return small_blocks(d->N, sg.spb, cap);
+}
+
 size_t int_conv_wgrad_workspace_bytes(const ionn_conv_desc *desc) {
-    if (desc == nullptr || !geom33(desc) || desc->Cin != 64 || desc->Cout != 64 || !c3::fits(desc->W)) return 0;
+    if (desc == nullptr) return 0;
+    if (const int64_t nb = rows_wgrad_groups(desc))
+        return size_t(nb) * size_t(desc->Cout * desc->KH * desc->KW * desc->Cin) * sizeof(int32_t);
+    if (!geom33(desc) || desc->Cin != 64 || desc->Cout != 64 || !c3::fits(desc->W)) return 0;
     return size_t(c3::wgrad_rows(device_cus())) * c3::GSZ * sizeof(int32_t);
 }
 
@@ -832,12 +853,24 @@ int int_conv_wgrad(const int8_t *dY, const int8_t *X, int32_t *G, const ionn_con
         IONN_REQUIRE(aligned(G, 4) && aligned(absmax_G, 4), IONN_ERR_ALIGN,
                      "int_conv_wgrad: G/absmax must be 4-byte aligned");
         hipStream_t st = as_stream(stream);
+        const SmallGeo sg = small_geo(desc, 2);
+        const int64_t rg = rows > 0 ? rows_wgrad_groups(desc) : 0;
+        if (rg > 0 && workspace != nullptr && aligned(workspace, 4) &&
+            ws_bytes >= size_t(rg) * size_t(n_g) * sizeof(int32_t)) {
+            // per-workgroup partials, summed with the max in one pass
+            int32_t *part = static_cast<int32_t *>(workspace);
+            conv_rows_wgrad<<<dim3(unsigned(rg)), dim3(kRowsWgradThreads), 0, st>>>(dY, X, G, desc->N, sg, part);
+            if (int rc = check_launch("int_conv_wgrad")) return rc;
+            int64_t blocks = (n_g + 63) / 64;
+            if (blocks > 2048) blocks = 2048;
+            wl::wgrad_long_sum<><<<dim3(unsigned(blocks)), dim3(256), 0, st>>>(part, int(rg), n_g, G, absmax_G);
+            return check_launch("int_conv_wgrad");
+        }
         zero_i32_kernel<<<dim3(direct_blocks(n_g)), dim3(256), 0, st>>>(G, n_g);
         if (int rc = check_launch("int_conv_wgrad")) return rc;
-        const SmallGeo sg = small_geo(desc, 2);
-        if (rows > 0 && sg.spb > 0 && rows_path(desc)) {
-            conv_rows_wgrad<<<dim3(small_blocks(desc->N, sg.spb, 256)), dim3(kRowsWgradThreads), 0, st>>>(
-                dY, X, G, desc->N, sg);
+        if (rg > 0) {
+            const int64_t ra = rows_wgrad_groups(desc, 256);
+            conv_rows_wgrad<<<dim3(unsigned(ra)), dim3(kRowsWgradThreads), 0, st>>>(dY, X, G, desc->N, sg, nullptr);
             if (int rc = check_launch("int_conv_wgrad")) return rc;
         } else if (rows > 0 && sg.spb > 0) {
             conv_small_wgrad<<<dim3(small_blocks(desc->N, sg.spb, 1024)), dim3(256), 0, st>>>(dY, X, G, desc->N, sg,

@@ -238,7 +238,7 @@ int int_linear_wgrad_ws(const int8_t *dY, const int8_t *X, int32_t *G, int64_t B
     const int64_t n = OUT * IN;
     int64_t blocks = (n + 63) / 64;
     if (blocks > 2048) blocks = 2048;
-    wl::wgrad_long_sum<<<dim3(unsigned(blocks)), dim3(256), 0, st>>>(part, nw, n, G, absmax_G);
+    wl::wgrad_long_sum<><<<dim3(unsigned(blocks)), dim3(256), 0, st>>>(part, nw, n, G, absmax_G);
     return check_launch("int_linear_wgrad_ws");
 }
 

@@ -15,6 +15,7 @@
 // workgroup queued on the same addresses and ran at a tenth of the
 // bandwidth).
 #include "common.h"
+#include "wgrad_long.h"
 
 #include <mutex>
 
@@ -185,16 +186,6 @@ int64_t narrow_blocks(int64_t C, int64_t cap) {
     return g;
 }
 
-// gb[c] = sum over the ny row ranges of part[y][c] (modulo 2^32).
-__global__ __launch_bounds__(256) void bias_grad_sum(const int32_t *__restrict__ part, int64_t ny, int64_t C,
-                                                     int32_t *__restrict__ gb) {
-    const int64_t c = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (c >= C) return;
-    uint32_t t = 0;
-#pragma unroll 8
-    for (int64_t y = 0; y < ny; ++y) t += uint32_t(part[y * C + c]);
-    gb[c] = int32_t(t);
-}
 
 // Row split of the offset gradient: about 256 workgroups of 1 KiB strips in
 // all, each with at least 64 rows; the workspace holds one int32 row of C
@@ -297,7 +288,7 @@ int bias_grad_launch(const int8_t *d, int64_t M, int64_t C, int32_t *gb, const B
         if (nb >= 1) {
             bias_grad_narrow<<<dim3(unsigned(nb)), dim3(256), 0, st>>>(d, M * C, int(C), part);
             if (int rc = check_launch(name)) return rc;
-            bias_grad_sum<<<dim3(unsigned((C + 255) / 256)), dim3(256), 0, st>>>(part, nb, C, gb);
+            wl::wgrad_long_sum<><<<dim3(unsigned((C + 63) / 64)), dim3(256), 0, st>>>(part, int(nb), C, gb, nullptr);
             return check_launch(name);
         }
     }
@@ -305,7 +296,9 @@ int bias_grad_launch(const int8_t *d, int64_t M, int64_t C, int32_t *gb, const B
     if (g.vec) bias_grad_kernel<true><<<grid, block, 0, st>>>(d, M, C, g.rows, part);
     else bias_grad_kernel<false><<<grid, block, 0, st>>>(d, M, C, g.rows, part);
     if (int rc = check_launch(name)) return rc;
-    bias_grad_sum<<<dim3(unsigned((C + 255) / 256)), dim3(256), 0, st>>>(part, g.gy, C, gb);
+    int64_t sb = (C + 63) / 64;
+    if (sb > 2048) sb = 2048;
+    wl::wgrad_long_sum<><<<dim3(unsigned(sb)), dim3(256), 0, st>>>(part, int(g.gy), C, gb, nullptr);
     return check_launch(name);
 }
 

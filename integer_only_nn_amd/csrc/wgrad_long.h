@@ -176,9 +176,11 @@ __global__ __launch_bounds__(NT) void wgrad_long_kernel(Args g) {
 // consecutive i: thread (slice z, group q) adds part[w][i .. i + 3] for
 // i = 64 b + 4 q and w = z, z + 16, ... (loads of eight partials in flight),
 // and the 16 slices meet in LDS.
+template <int SL = 16>
 __global__ __launch_bounds__(256) void wgrad_long_sum(const int32_t *__restrict__ part, int nw, int64_t n,
                                                       int32_t *__restrict__ G, uint32_t *__restrict__ absmax) {
-    __shared__ uint32_t red[16][64];
+    static_assert(SL == 16, "16 slices of 16 groups");
+    __shared__ uint32_t red[SL][64];
     const int q = threadIdx.x & 15, z = threadIdx.x >> 4;
     uint32_t amax = 0;
     for (int64_t i0 = int64_t(blockIdx.x) * 64; i0 < n; i0 += int64_t(gridDim.x) * 64) {

@@ -50,6 +50,14 @@ def test_conv_general_vs_oracle(N, H, W, Cin, Cout, KH, KW, P):
     ops.int_conv_fwd(Xd, Wd, Y, desc, absmax_Y=am[0:1])
     ops.int_conv_dgrad(dYd, Wd, dX, desc, absmax_dX=am[1:2])
     ops.int_conv_wgrad(dYd, Xd, G, desc, absmax_G=am[2:3])
+    nws = ops.int_conv_wgrad_workspace_bytes(desc)
+    if nws:  # the partial-sums form: the same G and max
+        G2 = torch.full_like(G, 7)
+        am2 = torch.zeros(1, dtype=torch.int32, device=dev())
+        ops.int_conv_wgrad(dYd, Xd, G2, desc, absmax_G=am2,
+                           workspace=torch.empty(nws, dtype=torch.uint8, device=dev()))
+        np.testing.assert_array_equal(host(G2), host(G))
+        assert _u32(am2) == _u32(am[2:3])
     Yo = oracle.conv_fwd(X, Wt, P)
     dXo = oracle.conv_dgrad(dY, Wt, X.shape, P)
     Go = oracle.conv_wgrad(dY, X, KH, KW, P)

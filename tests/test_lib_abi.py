@@ -105,14 +105,23 @@ def test_conv_refuses_bad_kernel_or_pad(kw):
 
 
 def test_conv_wgrad_workspace_query():
-    """Workspace only for the 64-channel fast path (one partial G per compute
-    unit plus one per 16 of them, 64*576 int32 each); 0 otherwise."""
+    """Workspace for the 64-channel fast path (one partial G per compute
+    unit plus one per 16 of them, 64*576 int32 each) and for full-row-window
+    filters; 0 otherwise."""
     big = lib.int_conv_wgrad_workspace_bytes(ctypes.byref(_desc(Cin=64, Cout=64, W=56, H=56, N=128)))
     assert big > 0 and big % (64 * 576 * 4) == 0
     assert lib.int_conv_wgrad_workspace_bytes(ctypes.byref(_desc(Cin=64, Cout=32))) == 0
     assert lib.int_conv_wgrad_workspace_bytes(ctypes.byref(_desc(Cin=64, Cout=64, W=4000))) == 0
     assert lib.int_conv_wgrad_workspace_bytes(ctypes.byref(_desc(Cin=64, Cout=64, KH=5, KW=5, pad=2))) == 0
     assert lib.int_conv_wgrad_workspace_bytes(None) == 0
+    # full-row-window filters (no padding, KW = W): one partial G per
+    # workgroup of up to 64 staged samples, at most 1024 workgroups
+    ex = _desc(N=65536, H=64, W=2, Cin=1, Cout=3, KH=16, KW=2, pad=0)
+    assert lib.int_conv_wgrad_workspace_bytes(ctypes.byref(ex)) == 1024 * 3 * 32 * 4
+    few = _desc(N=100, H=64, W=2, Cin=1, Cout=3, KH=16, KW=2, pad=0)
+    assert lib.int_conv_wgrad_workspace_bytes(ctypes.byref(few)) == 2 * 3 * 32 * 4
+    assert lib.int_conv_wgrad_workspace_bytes(ctypes.byref(_desc(N=100, H=64, W=2, Cin=1, Cout=9, KH=16, KW=2,
+                                                                 pad=0))) == 0
 
 
 def test_conv_validation():
