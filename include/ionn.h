@@ -575,8 +575,9 @@ int ionn_model_backward(const ionn_layer *layers, int L, const int8_t *X,
 /* Equation 3; Gavg, Equation 4; the policy of Algorithm 1 applied between   */
 /* epochs as Algorithm 2 lays out).                                          */
 /*                                                                          */
-/* Layer l holds k[l]-bit signed weight mantissas W[l] (int16 storage, the  */
-/* k-bit range [-2^(k-1), 2^(k-1) - 1]) with one shared exponent e_w[l]: a  */
+/* Layer l holds k[l]-bit signed weight mantissas W[l] (int16 storage, or   */
+/* int8 through the _mixed calls; the k-bit range [-2^(k-1), 2^(k-1) - 1]) */
+/* with one shared exponent e_w[l]: a                                       */
 /* weight is m * 2^e_w and one grid step is epsilon = 2^e_w.  k, e_w, the   */
 /* gradient exponents e_g and the per-epoch Gavg sums are DEVICE int32 /    */
 /* double arrays of L entries, so steps and epochs chain on the stream      */
@@ -620,6 +621,25 @@ int apt_adjust(int L, int16_t *const *W, const int64_t *n, int32_t *k,
                int32_t *e_w, double *gavg_sum, int32_t *gavg_count,
                double t_min, double t_max, int k_min, int k_max,
                int32_t *dk_out, void *stream);
+
+/* apt_update and apt_adjust over layers held at their own width, for the
+ * memory saving low precision brings ([APT] section on the memory of
+ * training): wbytes (HOST int32 [L]) gives each layer's bytes per weight,
+ * 2 (int16 mantissas, as above) or 1 (int8 mantissas; W[l] 1-byte aligned,
+ * 8-byte aligned for the vector path).  A layer held in int8 reads its k in
+ * [2, 8] (a k above 8 as 8) and apt_adjust never raises it past 8, so its
+ * mantissas always fit; the arithmetic is that of an int16 layer with the
+ * same k, bit for bit.  wbytes NULL: every layer int16.  A wbytes entry other
+ * than 1 or 2 is IONN_ERR_ARG. */
+int apt_update_mixed(int L, void *const *W, const int32_t *wbytes,
+                     const int16_t *const *G, const int64_t *n, const int32_t *k,
+                     const int32_t *e_w, const int32_t *e_g, int lr_shift,
+                     double *gavg_sum, int32_t *gavg_count, void *workspace,
+                     size_t workspace_bytes, void *stream);
+int apt_adjust_mixed(int L, void *const *W, const int32_t *wbytes, const int64_t *n,
+                     int32_t *k, int32_t *e_w, double *gavg_sum,
+                     int32_t *gavg_count, double t_min, double t_max, int k_min,
+                     int k_max, int32_t *dk_out, void *stream);
 
 #ifdef __cplusplus
 }

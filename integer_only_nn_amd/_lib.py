@@ -57,6 +57,8 @@ SIGNATURES = {
     "apt_workspace_bytes": (ctypes.c_size_t, [_I, _P]),
     "apt_update": (_I, [_I, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, ctypes.c_size_t, _P]),
     "apt_adjust": (_I, [_I, _P, _P, _P, _P, _P, _P, ctypes.c_double, ctypes.c_double, _I, _I, _P, _P]),
+    "apt_update_mixed": (_I, [_I, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, ctypes.c_size_t, _P]),
+    "apt_adjust_mixed": (_I, [_I, _P, _P, _P, _P, _P, _P, _P, ctypes.c_double, ctypes.c_double, _I, _I, _P, _P]),
     "ionn_oss_requant": (_I, [_P, _P, _P, _P, _I64, _I64, _I, _P, _P]),
     "ionn_bias_grad_workspace_bytes": (ctypes.c_size_t, [_I64, _I64]),
     "ionn_bias_grad": (_I, [_P, _I64, _I64, _P, _P, ctypes.c_size_t, _P]),

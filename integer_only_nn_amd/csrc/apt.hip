@@ -25,11 +25,12 @@ constexpr int kKMinBits = 2, kKMaxBits = 16;
 constexpr int64_t kMaxLayerElems = int64_t(1) << 36;    // sum |g| < 2^53 stays exact in a double
 
 struct Table {
-    int16_t *W[IONN_MAX_LAYERS];
+    void *W[IONN_MAX_LAYERS];            // int16 mantissas, or int8 for the layers in i8
     const int16_t *G[IONN_MAX_LAYERS];
     int64_t n[IONN_MAX_LAYERS];
     int32_t first[IONN_MAX_LAYERS + 1];  // first workgroup of each layer; first[L] = grid size
-    uint64_t vec;                        // bit l: layer l's W and G are 16-byte aligned
+    uint64_t vec;                        // bit l: layer l takes the vector path (aligned W and G)
+    uint64_t i8;                         // bit l: layer l's W is int8 (k held in [2, 8])
     int32_t L;
 };
 
@@ -39,8 +40,12 @@ __device__ __forceinline__ int layer_of(const Table &t, int b) {
     return l;
 }
 
-__device__ __forceinline__ int clamp_bits(int k) {
-    return k < kKMinBits ? kKMinBits : (k > kKMaxBits ? kKMaxBits : k);
+constexpr int kKMaxBits8 = 8;  // int8 storage holds at most 8-bit mantissas
+
+__device__ __forceinline__ int max_bits(const Table &t, int l) { return (t.i8 >> l) & 1 ? kKMaxBits8 : kKMaxBits; }
+
+__device__ __forceinline__ int clamp_bits(int k, int kmax) {
+    return k < kKMinBits ? kKMinBits : (k > kmax ? kmax : k);
 }
 
 // The change of a weight in grid steps for sigma = e_w + lr_shift - e_g,
@@ -102,13 +107,38 @@ __global__ __launch_bounds__(kThreads) void update_kernel(Table t, const int32_t
                                                           const int32_t *__restrict__ e_g, int lr_shift,
                                                           int64_t *__restrict__ part) {
     const int l = layer_of(t, blockIdx.x);
-    const Rule r = make_rule(clamp_bits(kbits[l]), e_w[l], e_g[l], lr_shift);
+    const Rule r = make_rule(clamp_bits(kbits[l], max_bits(t, l)), e_w[l], e_g[l], lr_shift);
     const int64_t n = t.n[l];
     const int64_t b0 = int64_t(int(blockIdx.x) - t.first[l]) * kBlockElems;
-    int16_t *__restrict__ W = t.W[l];
+    int16_t *__restrict__ W = static_cast<int16_t *>(t.W[l]);
+    int8_t *__restrict__ W8 = static_cast<int8_t *>(t.W[l]);
     const int16_t *__restrict__ G = t.G[l];
     int32_t asum = 0;
-    if ((t.vec >> l) & 1) {
+    if ((t.i8 >> l) & 1) {
+        // int8 weights: 8 per thread (8 bytes of W, 16 of G)
+        const int64_t e = b0 + int64_t(threadIdx.x) * 8;
+        if (((t.vec >> l) & 1) && e + 8 <= n) {
+            const uint2 w = *reinterpret_cast<const uint2 *>(W8 + e);
+            const v4i gv = __builtin_nontemporal_load(reinterpret_cast<const v4i *>(G + e));
+            const uint32_t gd[4] = {uint32_t(gv.x), uint32_t(gv.y), uint32_t(gv.z), uint32_t(gv.w)};
+            uint32_t o[2] = {0, 0};
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int32_t g = j & 1 ? hi16(gd[j >> 1]) : lo16(gd[j >> 1]);
+                const int32_t m = int32_t(int8_t(uint8_t((j < 4 ? w.x : w.y) >> (8 * (j & 3)))));
+                if (SAMPLE) asum += iabs(g);
+                o[j >> 2] |= (uint32_t(apply(r, m, g)) & 0xffu) << (8 * (j & 3));
+            }
+            *reinterpret_cast<uint2 *>(W8 + e) = make_uint2(o[0], o[1]);
+        } else {
+            const int64_t end = e + 8 < n ? e + 8 : n;
+            for (int64_t j = e; j < end; ++j) {
+                const int32_t g = G[j];
+                if (SAMPLE) asum += iabs(g);
+                W8[j] = int8_t(apply(r, W8[j], g));
+            }
+        }
+    } else if ((t.vec >> l) & 1) {
         v4i wv[kVecPerThread], gv[kVecPerThread];
 #pragma unroll
         for (int i = 0; i < kVecPerThread; ++i) {
@@ -214,8 +244,10 @@ __global__ __launch_bounds__(kThreads) void rescale_kernel(Table t, const int32_
                                                            const double *__restrict__ gavg_sum,
                                                            const int32_t *__restrict__ gavg_count, Policy p) {
     const int l = layer_of(t, blockIdx.x);
-    const int k = clamp_bits(kbits[l]);
-    const int dk = decide(gavg_sum[l], gavg_count[l], k, p.t_min, p.t_max, p.k_min, p.k_max);
+    const int kmax = max_bits(t, l);
+    const int k = clamp_bits(kbits[l], kmax);
+    const int dk = decide(gavg_sum[l], gavg_count[l], k, p.t_min, p.t_max, p.k_min,
+                          p.k_max < kmax ? p.k_max : kmax);
     if (dk == 0) return;
     const int kn = k + dk;
     const int32_t lo = -(int32_t(1) << (kn - 1)), hi = (int32_t(1) << (kn - 1)) - 1;
@@ -225,8 +257,12 @@ __global__ __launch_bounds__(kThreads) void rescale_kernel(Table t, const int32_
     };
     const int64_t n = t.n[l];
     const int64_t b0 = int64_t(int(blockIdx.x) - t.first[l]) * kBlockElems;
-    int16_t *__restrict__ W = t.W[l];
-    if ((t.vec >> l) & 1) {
+    int16_t *__restrict__ W = static_cast<int16_t *>(t.W[l]);
+    if ((t.i8 >> l) & 1) {
+        int8_t *__restrict__ W8 = static_cast<int8_t *>(t.W[l]);
+        const int64_t end = b0 + kBlockElems < n ? b0 + kBlockElems : n;
+        for (int64_t j = b0 + threadIdx.x; j < end; j += kThreads) W8[j] = int8_t(one(W8[j]));
+    } else if ((t.vec >> l) & 1) {
 #pragma unroll
         for (int i = 0; i < kVecPerThread; ++i) {
             const int64_t e = b0 + (int64_t(i) * kThreads + threadIdx.x) * 8;
@@ -249,12 +285,13 @@ __global__ __launch_bounds__(kThreads) void rescale_kernel(Table t, const int32_
 
 // After the rescale: the same decision moves k and the exponent, reports
 // the change, and clears the sums for the next epoch.
-__global__ void commit_kernel(int L, int32_t *kbits, int32_t *e_w, double *gavg_sum, int32_t *gavg_count,
-                              int32_t *dk_out, Policy p) {
+__global__ void commit_kernel(int L, uint64_t i8, int32_t *kbits, int32_t *e_w, double *gavg_sum,
+                              int32_t *gavg_count, int32_t *dk_out, Policy p) {
     const int l = blockIdx.x * blockDim.x + threadIdx.x;
     if (l >= L) return;
-    const int k = clamp_bits(kbits[l]);
-    const int dk = decide(gavg_sum[l], gavg_count[l], k, p.t_min, p.t_max, p.k_min, p.k_max);
+    const int kmax = (i8 >> l) & 1 ? kKMaxBits8 : kKMaxBits;
+    const int k = clamp_bits(kbits[l], kmax);
+    const int dk = decide(gavg_sum[l], gavg_count[l], k, p.t_min, p.t_max, p.k_min, p.k_max < kmax ? p.k_max : kmax);
     kbits[l] = k + dk;
     e_w[l] = e_w[l] - dk;
     gavg_sum[l] = 0.0;
@@ -263,7 +300,8 @@ __global__ void commit_kernel(int L, int32_t *kbits, int32_t *e_w, double *gavg_
 }
 
 // Fill the table from host arrays; returns 0 or an IONN_ERR_* code.
-int make_table(const char *who, int L, int16_t *const *W, const int16_t *const *G, const int64_t *n, Table &t) {
+int make_table(const char *who, int L, void *const *W, const int32_t *wbytes, const int16_t *const *G,
+               const int64_t *n, Table &t) {
     IONN_REQUIRE(L >= 1 && L <= IONN_MAX_LAYERS, IONN_ERR_SHAPE, "%s: L = %d outside [1, %d]", who, L,
                  IONN_MAX_LAYERS);
     IONN_REQUIRE(W && n, IONN_ERR_ARG, "%s: NULL layer array", who);
@@ -275,15 +313,19 @@ int make_table(const char *who, int L, int16_t *const *W, const int16_t *const *
                      (long long)n[l]);
         IONN_REQUIRE(W[l] != nullptr && (G == nullptr || G[l] != nullptr), IONN_ERR_ARG,
                      "%s: layer %d has a NULL tensor", who, l);
-        IONN_REQUIRE(aligned(W[l], 2) && (G == nullptr || aligned(G[l], 2)), IONN_ERR_ALIGN,
-                     "%s: layer %d tensors must be 2-byte aligned", who, l);
+        const int wb = wbytes ? wbytes[l] : 2;
+        IONN_REQUIRE(wb == 1 || wb == 2, IONN_ERR_ARG, "%s: layer %d has %d bytes per weight (1 or 2)", who, l,
+                     wb);
+        IONN_REQUIRE(aligned(W[l], size_t(wb)) && (G == nullptr || aligned(G[l], 2)), IONN_ERR_ALIGN,
+                     "%s: layer %d tensors must be aligned to their element size", who, l);
         t.W[l] = W[l];
+        if (wb == 1) t.i8 |= uint64_t(1) << l;
         t.G[l] = G ? G[l] : nullptr;
         t.n[l] = n[l];
         t.first[l] = int32_t(blocks);
         blocks += (n[l] + kBlockElems - 1) / kBlockElems;
         IONN_REQUIRE(blocks <= 0x7fffffff, IONN_ERR_SHAPE, "%s: too many weights", who);
-        if (aligned(W[l], 16) && (G == nullptr || aligned(G[l], 16))) t.vec |= uint64_t(1) << l;
+        if (aligned(W[l], wb == 1 ? 8 : 16) && (G == nullptr || aligned(G[l], 16))) t.vec |= uint64_t(1) << l;
     }
     t.first[L] = int32_t(blocks);
     return IONN_OK;
@@ -306,13 +348,13 @@ size_t apt_workspace_bytes(int L, const int64_t *n) {
     return size_t(blocks) * sizeof(int64_t);
 }
 
-int apt_update(int L, int16_t *const *W, const int16_t *const *G, const int64_t *n, const int32_t *k,
-               const int32_t *e_w, const int32_t *e_g, int lr_shift, double *gavg_sum, int32_t *gavg_count,
-               void *workspace, size_t workspace_bytes, void *stream) {
+int apt_update_mixed(int L, void *const *W, const int32_t *wbytes, const int16_t *const *G, const int64_t *n,
+                     const int32_t *k, const int32_t *e_w, const int32_t *e_g, int lr_shift, double *gavg_sum,
+                     int32_t *gavg_count, void *workspace, size_t workspace_bytes, void *stream) {
     clear_error();
     IONN_REQUIRE(G != nullptr, IONN_ERR_ARG, "apt_update: NULL gradient array");
     Table t;
-    if (int rc = make_table("apt_update", L, W, G, n, t)) return rc;
+    if (int rc = make_table("apt_update", L, W, wbytes, G, n, t)) return rc;
     IONN_REQUIRE(k && e_w && e_g, IONN_ERR_ARG, "apt_update: NULL k / e_w / e_g");
     IONN_REQUIRE(aligned(k, 4) && aligned(e_w, 4) && aligned(e_g, 4), IONN_ERR_ALIGN,
                  "apt_update: k / e_w / e_g must be 4-byte aligned");
@@ -338,12 +380,19 @@ int apt_update(int L, int16_t *const *W, const int16_t *const *G, const int64_t 
     return check_launch("apt_update");
 }
 
-int apt_adjust(int L, int16_t *const *W, const int64_t *n, int32_t *k, int32_t *e_w, double *gavg_sum,
-               int32_t *gavg_count, double t_min, double t_max, int k_min, int k_max, int32_t *dk_out,
-               void *stream) {
+int apt_update(int L, int16_t *const *W, const int16_t *const *G, const int64_t *n, const int32_t *k,
+               const int32_t *e_w, const int32_t *e_g, int lr_shift, double *gavg_sum, int32_t *gavg_count,
+               void *workspace, size_t workspace_bytes, void *stream) {
+    return apt_update_mixed(L, reinterpret_cast<void *const *>(W), nullptr, G, n, k, e_w, e_g, lr_shift, gavg_sum,
+                            gavg_count, workspace, workspace_bytes, stream);
+}
+
+int apt_adjust_mixed(int L, void *const *W, const int32_t *wbytes, const int64_t *n, int32_t *k, int32_t *e_w,
+                     double *gavg_sum, int32_t *gavg_count, double t_min, double t_max, int k_min, int k_max,
+                     int32_t *dk_out, void *stream) {
     clear_error();
     Table t;
-    if (int rc = make_table("apt_adjust", L, W, nullptr, n, t)) return rc;
+    if (int rc = make_table("apt_adjust", L, W, wbytes, nullptr, n, t)) return rc;
     IONN_REQUIRE(k && e_w && gavg_sum && gavg_count, IONN_ERR_ARG, "apt_adjust: NULL state array");
     IONN_REQUIRE(aligned(k, 4) && aligned(e_w, 4) && aligned(gavg_sum, 8) && aligned(gavg_count, 4) &&
                      aligned(dk_out, 4),
@@ -356,8 +405,15 @@ int apt_adjust(int L, int16_t *const *W, const int64_t *n, int32_t *k, int32_t *
     hipStream_t st = as_stream(stream);
     rescale_kernel<<<dim3(unsigned(t.first[L])), dim3(kThreads), 0, st>>>(t, k, gavg_sum, gavg_count, p);
     if (int rc = check_launch("apt_adjust")) return rc;
-    commit_kernel<<<dim3(1), dim3(64), 0, st>>>(L, k, e_w, gavg_sum, gavg_count, dk_out, p);
+    commit_kernel<<<dim3(1), dim3(64), 0, st>>>(L, t.i8, k, e_w, gavg_sum, gavg_count, dk_out, p);
     return check_launch("apt_adjust");
+}
+
+int apt_adjust(int L, int16_t *const *W, const int64_t *n, int32_t *k, int32_t *e_w, double *gavg_sum,
+               int32_t *gavg_count, double t_min, double t_max, int k_min, int k_max, int32_t *dk_out,
+               void *stream) {
+    return apt_adjust_mixed(L, reinterpret_cast<void *const *>(W), nullptr, n, k, e_w, gavg_sum, gavg_count, t_min,
+                            t_max, k_min, k_max, dk_out, stream);
 }
 
 }  // extern "C"

@@ -468,6 +468,37 @@ def apt_update(Ws, Gs, k, e_w, e_g, lr_shift, gavg_sum=None, gavg_count=None, wo
                            _p(workspace, name="workspace"), ws_bytes, _stream(stream)), "apt_update")
 
 
+def _wbytes(Ws):
+    """Host int32 array of bytes per weight (1 for int8 tensors, 2 for int16)."""
+    out = []
+    for l, w in enumerate(Ws):
+        if w.dtype not in (torch.int8, torch.int16):
+            raise TypeError(f"W[{l}] must be int8 or int16, not {w.dtype}")
+        out.append(1 if w.dtype == torch.int8 else 2)
+    return (ctypes.c_int32 * len(Ws))(*out)
+
+
+def apt_update_mixed(Ws, Gs, k, e_w, e_g, lr_shift, gavg_sum=None, gavg_count=None, workspace=None, stream=None):
+    """apt_update over layers held in int8 (k in [2, 8]) or int16."""
+    L = len(Ws)
+    if len(Gs) != L or any(w.numel() != g.numel() for w, g in zip(Ws, Gs)):
+        raise ValueError("Ws and Gs must pair up with equal sizes")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    check(lib().apt_update_mixed(L, _ptr_array(Ws, None, "W"), _wbytes(Ws), _ptr_array(Gs, i16, "G"), _sizes(Ws),
+                                 _p(k, i32, L, "k"), _p(e_w, i32, L, "e_w"), _p(e_g, i32, L, "e_g"), int(lr_shift),
+                                 _p(gavg_sum, torch.float64, L, "gavg_sum"), _p(gavg_count, i32, L, "gavg_count"),
+                                 _p(workspace, name="workspace"), ws_bytes, _stream(stream)), "apt_update_mixed")
+
+
+def apt_adjust_mixed(Ws, k, e_w, gavg_sum, gavg_count, t_min, t_max, k_min=2, k_max=16, dk_out=None, stream=None):
+    """apt_adjust over layers held in int8 (never raised past 8 bits) or int16."""
+    L = len(Ws)
+    check(lib().apt_adjust_mixed(L, _ptr_array(Ws, None, "W"), _wbytes(Ws), _sizes(Ws), _p(k, i32, L, "k"),
+                                 _p(e_w, i32, L, "e_w"), _p(gavg_sum, torch.float64, L, "gavg_sum"),
+                                 _p(gavg_count, i32, L, "gavg_count"), float(t_min), float(t_max), int(k_min),
+                                 int(k_max), _p(dk_out, i32, L, "dk_out"), _stream(stream)), "apt_adjust_mixed")
+
+
 def apt_adjust(Ws, k, e_w, gavg_sum, gavg_count, t_min, t_max, k_min=2, k_max=16, dk_out=None, stream=None):
     """Between epochs: one bit more or less per layer on its mean Gavg."""
     L = len(Ws)

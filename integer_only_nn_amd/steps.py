@@ -14,6 +14,7 @@ target_bits = 7) and the weight gradient followed by the NITI update.
 from dataclasses import dataclass, field
 from typing import List, Optional
 
+import numpy as np
 import torch
 
 from . import ops
@@ -329,9 +330,18 @@ class AptLayers:
     are built once (bind_grads for the gradient buffers), so a step costs
     one library call."""
 
-    def __init__(self, Ws, ks, es, device):
-        self.W = [torch.from_numpy(w.copy()).to(device) for w in Ws]
+    def __init__(self, Ws, ks, es, device, int8_layers=()):
+        """int8_layers: indices of layers held in int8 (their k must be at
+        most 8 and stays there: half the memory of int16)."""
+        self.W = []
+        for l, w in enumerate(Ws):
+            if l in int8_layers:
+                if int(ks[l]) > 8 or w.min(initial=0) < -128 or w.max(initial=0) > 127:
+                    raise ValueError(f"layer {l}: int8 storage needs k <= 8 and mantissas in [-128, 127]")
+                w = w.astype(np.int8)
+            self.W.append(torch.from_numpy(np.ascontiguousarray(w).copy()).to(device))
         L = len(self.W)
+        self._mixed = bool(int8_layers)
         self.k = torch.tensor(list(ks), dtype=torch.int32, device=device)
         self.e_w = torch.tensor(list(es), dtype=torch.int32, device=device)
         self.gsum = torch.zeros(L, dtype=torch.float64, device=device)
@@ -339,7 +349,8 @@ class AptLayers:
         self.dk = torch.zeros(L, dtype=torch.int32, device=device)
         self.ws = torch.empty(max(ops.apt_workspace_bytes([w.numel() for w in self.W]), 8),
                               dtype=torch.uint8, device=device)
-        self._Wp = ops._ptr_array(self.W, torch.int16, "W")
+        self._Wp = ops._ptr_array(self.W, None, "W")
+        self._wb = ops._wbytes(self.W)
         self._n = ops._sizes(self.W)
         self._G = None
 
@@ -358,15 +369,19 @@ class AptLayers:
         if self._G is None:
             raise ValueError("no gradient buffers")
         L = len(self.W)
-        ops.check(ops.lib().apt_update(
-            L, self._Wp, self._G[1], self._n, ops._p(self.k), ops._p(self.e_w), ops._p(e_g, torch.int32, L, "e_g"),
-            int(lr_shift), ops._p(self.gsum) if sample else None, ops._p(self.gcnt) if sample else None,
-            ops._p(self.ws) if sample else None, self.ws.numel() if sample else 0, ops._stream(stream)),
-            "apt_update")
+        args = (self._G[1], self._n, ops._p(self.k), ops._p(self.e_w), ops._p(e_g, torch.int32, L, "e_g"),
+                int(lr_shift), ops._p(self.gsum) if sample else None, ops._p(self.gcnt) if sample else None,
+                ops._p(self.ws) if sample else None, self.ws.numel() if sample else 0, ops._stream(stream))
+        if self._mixed:
+            ops.check(ops.lib().apt_update_mixed(L, self._Wp, self._wb, *args), "apt_update_mixed")
+        else:
+            ops.check(ops.lib().apt_update(L, self._Wp, *args), "apt_update")
 
     def end_epoch(self, t_min, t_max, k_min=2, k_max=16, stream=None):
         L = len(self.W)
-        ops.check(ops.lib().apt_adjust(
-            L, self._Wp, self._n, ops._p(self.k), ops._p(self.e_w), ops._p(self.gsum), ops._p(self.gcnt),
-            float(t_min), float(t_max), int(k_min), int(k_max), ops._p(self.dk), ops._stream(stream)),
-            "apt_adjust")
+        args = (self._n, ops._p(self.k), ops._p(self.e_w), ops._p(self.gsum), ops._p(self.gcnt), float(t_min),
+                float(t_max), int(k_min), int(k_max), ops._p(self.dk), ops._stream(stream))
+        if self._mixed:
+            ops.check(ops.lib().apt_adjust_mixed(L, self._Wp, self._wb, *args), "apt_adjust_mixed")
+        else:
+            ops.check(ops.lib().apt_adjust(L, self._Wp, *args), "apt_adjust")

@@ -269,3 +269,99 @@ def test_update_replayed_from_graph():
             np.testing.assert_array_equal(host(st.W[l]), ostate[l]["W"], err_msg=f"replay {rep} layer {l}")
         assert host(st.gsum).tolist() == sums and host(st.gcnt).tolist() == counts
         torch.zeros(1000, device=dev()).add_(1.0)   # unrelated eager work between replays
+
+
+# ---- layers held in int8 (k <= 8): half the memory, the same arithmetic ----
+
+@pytest.mark.parametrize("sample", [False, True])
+def test_int8_storage_update_parity(sample):
+    """Layers of every size class held in int8 (odd sizes, ragged tails, a
+    1-byte misaligned tensor on the element path) mixed with int16 layers in
+    one launch: every weight equals the oracle's int16 result."""
+    sizes = [1, 7, 8, 4097, 8193, 65536 + 5, 3000]
+    seed = 17
+    Ws, ks = _layers(sizes, seed, kmax=8)
+    Gs = _grads(sizes, seed)
+    rng = np.random.default_rng(seed + 1)
+    e_w = [int(x) for x in rng.integers(-20, 0, len(sizes))]
+    e_g = [int(x) for x in rng.integers(-30, -5, len(sizes))]
+    i8 = (0, 1, 3, 5, 6)
+    st = AptLayers(Ws, ks, e_w, dev(), int8_layers=i8)
+    assert [w.element_size() for w in st.W] == [1 if l in i8 else 2 for l in range(len(sizes))]
+    # layer 6 held one byte off its allocation's alignment (element path)
+    buf = torch.empty(sizes[6] + 1, dtype=torch.int8, device=dev())
+    buf[1:] = st.W[6]
+    W6 = buf[1:]
+    Wd = st.W[:6] + [W6]
+    gsum = torch.zeros(len(sizes), dtype=torch.float64, device=dev())
+    gcnt = torch.zeros(len(sizes), dtype=torch.int32, device=dev())
+    ws = torch.empty(ops.apt_workspace_bytes(sizes), dtype=torch.uint8, device=dev())
+    ops.apt_update_mixed(Wd, [to_dev(g) for g in Gs], _i32(ks), _i32(e_w), _i32(e_g), 4,
+                         gsum if sample else None, gcnt if sample else None, ws if sample else None)
+    for l in range(len(sizes)):
+        want, _ = oracle.apt_update(Ws[l], ks[l], e_w[l], Gs[l], e_g[l], 4)
+        np.testing.assert_array_equal(host(Wd[l]).astype(np.int16), want, err_msg=f"layer {l}")
+    if sample:
+        assert host(gsum).tolist() == [0.0 + oracle.gavg(Gs[l], e_g[l], e_w[l]) for l in range(len(sizes))]
+
+
+def test_int8_storage_k_reads_and_stays_within_8():
+    """An int8 layer reads a k above 8 as 8, and the epoch policy never
+    raises it past 8 (it still lowers it); an int16 layer beside it rises."""
+    n = 5000
+    rng = np.random.default_rng(3)
+    W8 = rng.integers(-128, 128, n).astype(np.int16)
+    W16 = rng.integers(-128, 128, n).astype(np.int16)
+    G = ionn_synth.apt_grad(5, n, 500.0)
+    st = AptLayers([W8, W16], [8, 8], [-6, -6], dev(), int8_layers=(0,))
+    st.k.copy_(torch.tensor([12, 8], dtype=torch.int32))       # read as 8 for the int8 layer
+    st.step([to_dev(G), to_dev(G)], _i32([-12, -12]), 2)
+    want, _ = oracle.apt_update(W8, 8, -6, G, -12, 2)
+    np.testing.assert_array_equal(host(st.W[0]).astype(np.int16), want)
+    # a mean below T_min: the int16 layer gains a bit, the int8 one is held
+    st.k.copy_(torch.tensor([8, 8], dtype=torch.int32))
+    st.gsum.copy_(torch.tensor([0.01, 0.01], dtype=torch.float64))
+    st.gcnt.copy_(torch.tensor([1, 1], dtype=torch.int32))
+    before = [host(w).astype(np.int16) for w in st.W]
+    st.end_epoch(1.0, 50.0, 2, 16)
+    assert host(st.dk).tolist() == [0, 1] and host(st.k).tolist() == [8, 9]
+    np.testing.assert_array_equal(host(st.W[0]).astype(np.int16), before[0])
+    np.testing.assert_array_equal(host(st.W[1]), oracle.apt_rescale(before[1], 8, 1))
+    # a mean above T_max: the int8 layer loses a bit like any other
+    st.gsum.copy_(torch.tensor([500.0, 0.5], dtype=torch.float64))
+    st.gcnt.copy_(torch.tensor([1, 1], dtype=torch.int32))
+    st.end_epoch(1.0, 50.0, 2, 16)
+    assert host(st.dk).tolist()[0] == -1 and int(host(st.k)[0]) == 7
+    np.testing.assert_array_equal(host(st.W[0]).astype(np.int16), oracle.apt_rescale(before[0], 8, -1))
+
+
+def test_int8_storage_workflow_parity_resnet20():
+    """Algorithm 2 over a ResNet-20's 20 layers held in int8 (k from 6,
+    k_max 8): 3 epochs of 4 steps against the oracle run with k_max = 8; the
+    weights take half the bytes of the int16 layers."""
+    sizes = ionn_synth.RESNET20_SIZES
+    L = len(sizes)
+    Ws, es = ionn_synth.apt_weights(sizes, k0=6, seed=1)
+    sig = [30.0 * (1 + (l % 4) ** 3) for l in range(L)]
+    egs = [-13 - (l % 3) for l in range(L)]
+    ostate = oapt.new_state(Ws, [6] * L, es)
+    dstate = AptLayers(Ws, [6] * L, es, dev(), int8_layers=tuple(range(L)))
+    assert sum(w.numel() * w.element_size() for w in dstate.W) == sum(sizes)
+    eg = _i32(egs)
+    moved = 0
+    for ep in range(3):
+        sums, counts = [0.0] * L, [0] * L
+        for s in range(4):
+            grads = [(ionn_synth.apt_grad((ep * 8 + s) * L + l, sizes[l], sig[l]), egs[l]) for l in range(L)]
+            sample = s % 2 == 0
+            oapt.step(ostate, grads, 3, sums if sample else None, counts if sample else None)
+            dstate.step([to_dev(g) for g, _ in grads], eg, 3, sample=sample)
+        dks = oapt.adjust(ostate, sums, counts, 1.0, 30.0, 2, 8)
+        dstate.end_epoch(1.0, 30.0, 2, 16)   # the int8 layers stop at 8 by themselves
+        assert host(dstate.dk).tolist() == dks
+        assert host(dstate.k).tolist() == [s["k"] for s in ostate]
+        for l in range(L):
+            np.testing.assert_array_equal(host(dstate.W[l]).astype(np.int16), ostate[l]["W"],
+                                          err_msg=f"epoch {ep} layer {l}")
+        moved += sum(1 for d in dks if d)
+    assert moved > 0

@@ -193,6 +193,23 @@ def test_apt_validation():
     assert adj(n=arrN(5, 0)) == SHAPE
 
 
+def test_apt_mixed_width_validation():
+    arrP = lambda *ps: (ctypes.c_void_p * len(ps))(*ps)
+    arrN = lambda *ns: (ctypes.c_int64 * len(ns))(*ns)
+    arrB = lambda *bs: (ctypes.c_int32 * len(bs))(*bs)
+    W, G, N = arrP(0x1000, 0x2001), arrP(0x3000, 0x4000), arrN(100, 9000)
+    upd = lambda W_, wb: lib.apt_update_mixed(2, W_, wb, G, N, FAKE, FAKE, FAKE, 3, None, None, None, 0, None)
+    # bytes per weight must be 1 or 2
+    assert upd(W, arrB(2, 3)) == ARG and "bytes per weight" in _err()
+    assert upd(W, arrB(0, 1)) == ARG
+    # an int8 layer may sit at any byte; an int16 one needs 2-byte alignment
+    assert upd(arrP(0x1000, 0x2001), arrB(2, 2)) == ALIGN
+    assert upd(arrP(0x1001, 0x2001), arrB(1, 2)) == ALIGN
+    adj = lambda W_, wb: lib.apt_adjust_mixed(2, W_, wb, N, FAKE, FAKE, FAKE, FAKE, 1.0, 2.0, 2, 16, None, None)
+    assert adj(W, arrB(1, 4)) == ARG
+    assert adj(W, arrB(2, 2)) == ALIGN
+
+
 def test_dfp_paper_form_validation():
     ws = lib.dfp16_f32_workspace_bytes(256, 256, 256, 0, 0)
     assert ws >= 256 and lib.dfp16_f32_workspace_bytes(0, 1, 1, 0, 0) == 0
