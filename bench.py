@@ -829,10 +829,12 @@ def bench_apt(torch, nsteps):
     sizes = ionn_synth.RESNET20_SIZES
     Ws, es = ionn_synth.apt_weights(sizes, k0=6)
     rn = st.AptLayers(Ws, [6] * len(sizes), es, dev)
+    rn8 = st.AptLayers(Ws, [6] * len(sizes), es, dev, int8_layers=tuple(range(len(sizes))))
     Gr = [torch.from_numpy(ionn_synth.apt_grad(l, m, 500.0)).to(dev) for l, m in enumerate(sizes)]
     egr = torch.full((len(sizes),), -14, dtype=torch.int32, device=dev)
     big.bind_grads(Gb)
     rn.bind_grads(Gr)
+    rn8.bind_grads(Gr)
     flip = [0]
 
     def step(tm):
@@ -854,7 +856,8 @@ def bench_apt(torch, nsteps):
     g = {"update_16M": _graph_ms(torch, lambda s: big.step(None, egb, 6, stream=s), 10),
          "update_16M_sampling": _graph_ms(torch, lambda s: big.step(None, egb, 6, sample=True, stream=s), 10),
          "resnet20_update": _graph_ms(torch, lambda s: rn.step(None, egr, 3, stream=s), 10),
-         "resnet20_update_sampling": _graph_ms(torch, lambda s: rn.step(None, egr, 3, sample=True, stream=s), 10)}
+         "resnet20_update_sampling": _graph_ms(torch, lambda s: rn.step(None, egr, 3, sample=True, stream=s), 10),
+         "resnet20_int8_update": _graph_ms(torch, lambda s: rn8.step(None, egr, 3, stream=s), 10)}
     gbs = 6.0 * n / (g["update_16M"] * 1e-3) / 1e9
     r4 = lambda v: round(v, 4)
     return {"layer_16M": {"shape": "4096 x 4096 int16 weights, k = 12",
@@ -866,7 +869,11 @@ def bench_apt(torch, nsteps):
             "resnet20": {"layers": len(sizes), "weights": sum(sizes),
                          "update_ms": r4(g["resnet20_update"]), "update_sampling_ms": r4(g["resnet20_update_sampling"]),
                          "eager_update_ms": r4(per["resnet20_update"]),
-                         "eager_adjust_ms": r4(per["resnet20_adjust"])}}
+                         "eager_adjust_ms": r4(per["resnet20_adjust"]),
+                         "weight_bytes_int16": sum(w.numel() * w.element_size() for w in rn.W),
+                         "int8_storage": {"update_ms": r4(g["resnet20_int8_update"]),
+                                          "weight_bytes": sum(w.numel() * w.element_size() for w in rn8.W),
+                                          "note": "every layer held in int8 (k <= 8, never raised past 8)"}}}
 
 
 def _model_layers(d):
@@ -880,7 +887,7 @@ def _model_layers(d):
 
 # The translation units (and the headers they include) that build the
 # contraction and update kernels the traffic figures describe.
-TRAFFIC_SOURCES = ("common.h", "gemm_core.h", "gemm256.h", "gemm_i8.hip", "niti.hip")
+TRAFFIC_SOURCES = ("common.h", "gemm_core.h", "gemm256.h", "wgrad_long.h", "gemm_i8.hip", "niti.hip")
 
 
 def _kernel_source_hash():
