@@ -1075,10 +1075,11 @@ def main():
         conv_op1 = 2.0 * 128 * 56 * 56 * 64 * 9 * 64
         fdom_c = max(("fwd_requant", "dgrad_requant"), key=lambda k: cf_per[k])
         cf_tops = conv_op1 / (cf_per[fdom_c] * 1e-3) / 1e12
-        # DFP-16 contractions are VALU-bound: 6 int32 operations per output
-        # element per 64-term chunk (digit combination, rounding shift, add)
-        dfp_alu = {"fwd": 6.0 * 25088 * 1024 * (256 // 64), "dgrad": 6.0 * 25088 * 256 * (1024 // 64),
-                   "wgrad": 6.0 * 1024 * 256 * (25088 // 64)}
+        # VALU view of the DFP-16 contractions: 5 int32 operations per output
+        # element per 64-term chunk (digit combination mad_i24 + lshl_add,
+        # then the rounding shift, its rounding bit and the add)
+        dfp_alu = {"fwd": 5.0 * 25088 * 1024 * (256 // 64), "dgrad": 5.0 * 25088 * 256 * (1024 // 64),
+                   "wgrad": 5.0 * 1024 * 256 * (25088 // 64)}
         # the method's own work: 2*M*N*K int16 multiply-adds per contraction,
         # each 4 int8 digit products on the matrix cores (every role has the
         # same M*N*K); the VALU view of the epilogue is kept beside it
@@ -1086,8 +1087,9 @@ def main():
         fdom = max(dfp_alu, key=lambda k: f_per[k])
         falu = dfp_alu[fdom] / (f_per[fdom] * 1e-3) / 1e12
         p_ms, p_per = bench_dfp16_paper(torch, 20)
-        # the same VALU bound: per output element and 64-term chunk the digit
-        # combination, one int32 -> FP32 conversion and one FP32 addition
+        # the same count for the FP32 form: per output element and 64-term
+        # chunk three operations of digit combination, one int32 -> FP32
+        # conversion and one FP32 addition
         pdom = max(("fwd", "dgrad", "wgrad"), key=lambda k: p_per[k])
         palu = dfp_alu[pdom] / (p_per[pdom] * 1e-3) / 1e12
         o_ms, o_per = bench_offsets(torch, 20)
@@ -1137,7 +1139,7 @@ def main():
                                              "achieved": round(falu, 2), "peak": PEAK_VALU_TOPS,
                                              "unit": "T int32 op/s", "frac": round(falu / PEAK_VALU_TOPS, 4),
                                              "ops_per_launch": dfp_alu[fdom],
-                                             "work": "the kernel's epilogue: 6 int32 ops per output per chunk"}},
+                                             "work": "the kernel's per-chunk epilogue: 5 int32 ops per output per chunk"}},
             "dfp16_paper_step": {"shape": "M25088 K256 N1024, FP32 chunk partials, 1-bit input shift",
                                  "ms_per_step": round(p_ms, 4),
                                  "int16_TOPS": round(dfp_ops / (p_ms * 1e-3) / 1e12, 2),
