@@ -571,23 +571,31 @@ def bench_conv(torch, steps_mod, nsteps):
     buf = steps_mod.ConvStepBuffers.make(128, 56, 56, 64, 64, dev)
     desc = ops.conv_desc(128, 56, 56, 64, 64)
     s = buf.scal
+    # the maxima alternate between two scalar sets: each step's update
+    # clears the set the next step max-combines into (no fill launch)
+    sets = (s[8:11], s[12:15])
+    ph = [0]
+
+    def cur_next():
+        c, n = sets[ph[0]], sets[ph[0] ^ 1]
+        ph[0] ^= 1
+        return c, n
 
     def step(tm):
         m = tm.mark if tm else (lambda n: None)
-        m("fill")
-        ops.ionn_fill_u32(s[0:3], 0)
+        c, n = cur_next()
         m("fwd")
-        ops.int_conv_fwd(X, Wt, buf.Y, desc, absmax_Y=s[0:1])
+        ops.int_conv_fwd(X, Wt, buf.Y, desc, absmax_Y=c[0:1])
         m("requant_y")
-        ops.niti_quantize(buf.Y, s[0:1], 7, False, buf.y8, shift_out=s[3:4])
+        ops.niti_quantize(buf.Y, c[0:1], 7, False, buf.y8, shift_out=s[3:4])
         m("dgrad")
-        ops.int_conv_dgrad(dY, Wt, buf.dX, desc, absmax_dX=s[1:2])
+        ops.int_conv_dgrad(dY, Wt, buf.dX, desc, absmax_dX=c[1:2])
         m("requant_dx")
-        ops.niti_quantize(buf.dX, s[1:2], 7, False, buf.dx8, shift_out=s[4:5])
+        ops.niti_quantize(buf.dX, c[1:2], 7, False, buf.dx8, shift_out=s[4:5])
         m("wgrad")
-        ops.int_conv_wgrad(dY, X, buf.G, desc, absmax_G=s[2:3], workspace=buf.ws)
+        ops.int_conv_wgrad(dY, X, buf.G, desc, absmax_G=c[2:3], workspace=buf.ws)
         m("update")
-        ops.niti_quantize_update(buf.G, s[2:3], 8, 2, Wt, shifts_out=s[5:7])
+        ops.niti_quantize_update_clear(buf.G, c[2:3], 8, 2, Wt, n, shifts_out=s[5:7])
 
     def step_fused(tm):
         # the requantisation fused into the contractions (steps.conv_step_fused):
@@ -595,16 +603,15 @@ def bench_conv(torch, steps_mod, nsteps):
         # block's own shift with its rounding bits, a streaming pass applies
         # the tensor's shift; the int32 sums are never stored
         m = tm.mark if tm else (lambda n: None)
-        m("fill")
-        ops.ionn_fill_u32(s[0:3], 0)
+        c, n = cur_next()
         m("fwd_requant")
-        ops.int_conv_fwd_requant(X, Wt, buf.y8, desc, 7, False, s[0:1], shift_out=s[3:4], workspace=buf.rws)
+        ops.int_conv_fwd_requant(X, Wt, buf.y8, desc, 7, False, c[0:1], shift_out=s[3:4], workspace=buf.rws)
         m("dgrad_requant")
-        ops.int_conv_dgrad_requant(dY, Wt, buf.dx8, desc, 7, s[1:2], shift_out=s[4:5], workspace=buf.rws)
+        ops.int_conv_dgrad_requant(dY, Wt, buf.dx8, desc, 7, c[1:2], shift_out=s[4:5], workspace=buf.rws)
         m("wgrad")
-        ops.int_conv_wgrad(dY, X, buf.G, desc, absmax_G=s[2:3], workspace=buf.ws)
+        ops.int_conv_wgrad(dY, X, buf.G, desc, absmax_G=c[2:3], workspace=buf.ws)
         m("update")
-        ops.niti_quantize_update(buf.G, s[2:3], 8, 2, Wt, shifts_out=s[5:7])
+        ops.niti_quantize_update_clear(buf.G, c[2:3], 8, 2, Wt, n, shifts_out=s[5:7])
     return _timed(torch, step, nsteps), _timed(torch, step_fused, nsteps)
 
 

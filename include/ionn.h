@@ -247,7 +247,7 @@ int int_conv_dgrad_requant(const int8_t *dY, const int8_t *Wt, int8_t *dX8,
 
 /* Device workspace (bytes) that lets int_conv_wgrad take its fast path for
  * this geometry: for 64 input and 64 output channels (3x3, W up to about
- * 100), one partial G per compute unit plus one per 16 of them; for a
+ * 100), one partial G per compute unit; for a
  * full-row-window filter (no padding, KW = W, KH*W*Cin a multiple of 4, at
  * most 8 output channels), one partial G per workgroup (at most 1024).  0
  * when the geometry has no fast path (the call then needs no workspace). */

@@ -302,12 +302,22 @@ __global__ __launch_bounds__(NTF, 1) void conv3x3_kernel(const int8_t *__restric
 // shift from the finished *absmax; block 0 writes s.  In place.  A pixel's
 // block is (tile, wavefront) = (n tpi + p / 256, (p / 32) % 8) and its lane
 // p % 32 (channels 0-15, 32-47) or p % 32 + 32 (16-31, 48-63).
+//
+// Per dword of four int8 values f, with d = s - sb:
+//  - d = 0: f + bit, bytewise without carries between bytes (the low seven
+//    bits added, bit 7 restored by XOR); the only overflow, 127 + 1, shows
+//    as a byte whose sign turned on and is set back to 127;
+//  - d > 0: rhu(f, d) on int16 pairs (bytes 0, 2 and 1, 3 sign-extended in
+//    place), d taken as min(d, 8): for |f| <= 128 and d >= 8,
+//    f + 2^(d-1) lies in [0, 2^d), so the result is 0 at d = 8 as at any
+//    larger d; the results fit int8, so the low byte of each half is kept.
 __global__ __launch_bounds__(256) void conv3x3_requant_fix(int8_t *__restrict__ y8,
                                                            const uint32_t *__restrict__ bits,
                                                            const int32_t *__restrict__ shifts_blk,
                                                            const uint32_t *__restrict__ absmax, int target_bits,
                                                            int relu, uint32_t HW, uint32_t tpi, uint32_t nchunks,
                                                            int32_t *__restrict__ shift_out) {
+    typedef short v2s __attribute__((ext_vector_type(2)));
     const int s = niti_shift(*absmax, target_bits);
     if (blockIdx.x == 0 && threadIdx.x == 0 && shift_out) *shift_out = s;
     for (uint32_t c = blockIdx.x * 256u + threadIdx.x; c < nchunks; c += gridDim.x * 256u) {
@@ -317,16 +327,33 @@ __global__ __launch_bounds__(256) void conv3x3_requant_fix(int8_t *__restrict__ 
         const uint32_t w = bits[blk * 64u + (p & 31u) + 32u * (q4 & 1u)] >> (16u * (q4 >> 1));
         const int d = s - shifts_blk[blk];
         v4i v = *reinterpret_cast<const v4i *>(y8 + 16ull * c);
+        if (d == 0) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            int32_t o[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int32_t f = int32_t(int8_t(uint8_t(uint32_t(v[q]) >> (8 * j))));
-                int32_t r = d == 0 ? sat8(f + int32_t((w >> (4 * q + j)) & 1u)) : rhu(f, d);
-                o[j] = relu ? max(r, 0) : r;
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t f = uint32_t(v[q]);
+                // bits 4q .. 4q + 3 of w to bit 0 of bytes 0 .. 3
+                const uint32_t m = (((w >> (4 * q)) & 15u) * 0x00204081u) & 0x01010101u;
+                uint32_t r = ((f & 0x7f7f7f7fu) + m) ^ (f & 0x80808080u);
+                r -= (~f & r & 0x80808080u) >> 7;                      // 127 + 1 -> 127
+                if (relu) r &= ~(((r >> 7) & 0x01010101u) * 0xffu);   // negative bytes -> 0
+                v[q] = int(r);
             }
-            v[q] = int(pack4_u8(o[0], o[1], o[2], o[3]));
+        } else {
+            const short dd = short(d < 8 ? d : 8);
+            const v2s dv = {dd, dd}, half = {short(1 << (dd - 1)), short(1 << (dd - 1))}, zero = {0, 0};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t f = uint32_t(v[q]);
+                const v2s lo = __builtin_bit_cast(v2s, (f << 8) & 0xff00ff00u) >> v2s{8, 8};  // bytes 0, 2
+                const v2s hi = __builtin_bit_cast(v2s, f & 0xff00ff00u) >> v2s{8, 8};         // bytes 1, 3
+                v2s rl = (lo + half) >> dv, rh = (hi + half) >> dv;
+                if (relu) {
+                    rl = __builtin_elementwise_max(rl, zero);
+                    rh = __builtin_elementwise_max(rh, zero);
+                }
+                v[q] = int((__builtin_bit_cast(uint32_t, rl) & 0x00ff00ffu) |
+                           ((__builtin_bit_cast(uint32_t, rh) & 0x00ff00ffu) << 8));
+            }
         }
         *reinterpret_cast<v4i *>(y8 + 16ull * c) = v;
     }
@@ -338,8 +365,8 @@ __global__ __launch_bounds__(256) void conv3x3_requant_fix(int8_t *__restrict__ 
 // as C = A B^T with A = dY^T (64 x pixels) and B = im2col(X) (576 x pixels),
 // K = pixels.  Persistent workgroups walk the same 256-pixel tiles as the
 // forward kernel; each keeps a partial G (64 x 576) in its accumulators over
-// all its tiles and writes it once to a workspace row; two reduction passes
-// of 16 rows each sum the rows into G (no atomics, so the result is
+// all its tiles and writes it once to a workspace row; one pass sums the rows
+// into G with the max (wgrad_long.h, no atomics, so the result is
 // deterministic; integer sums are exact in any order anyway).
 //
 // Both operands have their contraction index (pixels) as the outer
@@ -358,7 +385,9 @@ constexpr int WNB = 3;                      // n-blocks per wavefront, at most
 constexpr int DY_BYTES = TP * SLOT;         // one dY tile in LDS
 constexpr int GSZ = 64 * 576;               // elements of G
 
-inline int64_t wgrad_rows(int cus) { return cus + (cus + 15) / 16; }
+// Workspace rows of the weight gradient: one partial G per workgroup, at most
+// one workgroup per compute unit.
+inline int64_t wgrad_rows(int cus) { return cus; }
 
 __device__ __forceinline__ v4i tr_frag(const int8_t *base0, const int8_t *base1) {
     typedef int v2i_ __attribute__((ext_vector_type(2)));
@@ -510,27 +539,6 @@ __global__ __launch_bounds__(NTF, 1) void conv3x3_wgrad_kernel(const int8_t *__r
                         v4i{acc[j][cb][4 * q], acc[j][cb][4 * q + 1], acc[j][cb][4 * q + 2], acc[j][cb][4 * q + 3]};
             }
         }
-    }
-}
-
-// dst[g][e] = sum of src rows [16 g, min(16 g + 16, rows)) at element e (GSZ
-// elements per row); with absmax, dst is the final G and its max |G| is
-// max-combined into *absmax.
-__global__ __launch_bounds__(256) void conv3x3_wgrad_reduce(const int32_t *__restrict__ src, int rows,
-                                                            int32_t *__restrict__ dst,
-                                                            uint32_t *__restrict__ absmax) {
-    const int e = 4 * (blockIdx.x * 256 + threadIdx.x);  // GSZ / 1024 blocks along x
-    typedef unsigned v4u __attribute__((ext_vector_type(4)));  // sums wrap modulo 2^32
-    const int g = blockIdx.y;
-    const int r1 = min(16 * g + 16, rows);
-    v4u s = {0, 0, 0, 0};
-    for (int r = 16 * g; r < r1; ++r) s += *reinterpret_cast<const v4u *>(src + int64_t(r) * GSZ + e);
-    *reinterpret_cast<v4u *>(dst + int64_t(g) * GSZ + e) = s;
-    if (absmax) {
-        uint32_t m = max(max(abs_u32(int32_t(s.x)), abs_u32(int32_t(s.y))),
-                         max(abs_u32(int32_t(s.z)), abs_u32(int32_t(s.w))));
-        m = wave_max_u32(m);
-        if ((threadIdx.x & 63) == 0) publish_max_u32(absmax, m);
     }
 }
 

@@ -901,16 +901,10 @@ int int_conv_wgrad(const int8_t *dY, const int8_t *X, int32_t *G, const ionn_con
         c3::conv3x3_wgrad_kernel<<<dim3(P), dim3(c3::NTF), 0, st>>>(dY, X, part, int(desc->N),
                                                                     int(desc->H), int(desc->W));
         if (int rc = check_launch("int_conv_wgrad")) return rc;
-        const int xb = c3::GSZ / 1024;
-        if (P > 16) {
-            const unsigned P2 = (P + 15) / 16;
-            int32_t *part2 = part + int64_t(P) * c3::GSZ;
-            c3::conv3x3_wgrad_reduce<<<dim3(xb, P2), dim3(256), 0, st>>>(part, int(P), part2, nullptr);
-            if (int rc = check_launch("int_conv_wgrad")) return rc;
-            c3::conv3x3_wgrad_reduce<<<dim3(xb, 1), dim3(256), 0, st>>>(part2, int(P2), G, absmax_G);
-        } else {
-            c3::conv3x3_wgrad_reduce<<<dim3(xb, 1), dim3(256), 0, st>>>(part, int(P), G, absmax_G);
-        }
+        // one pass over the P partial rows: 64 elements of G per workgroup,
+        // 16 slices of the rows each, with the max
+        wl::wgrad_long_sum<><<<dim3(unsigned(c3::GSZ / 64)), dim3(256), 0, st>>>(part, int(P), c3::GSZ, G,
+                                                                                 absmax_G);
         return check_launch("int_conv_wgrad");
     }
     const int M = Cout, N = 9 * Cin, K = npix;

@@ -901,7 +901,8 @@ __global__ __launch_bounds__(256) void block16_fix_kernel(int16_t *__restrict__ 
                 const int xq = x[q];  // a scalar copy: bit_cast of a vector element reads element 0
                 y[q] = __builtin_bit_cast(int, __builtin_elementwise_add_sat(__builtin_bit_cast(v2s, xq), bit));
             }
-        } else {
+        } else if (d < 16) {
+            // packed 16-bit shifts take their count modulo 16, so d < 16 here
             const v2s dv = {short(d), short(d)}, dm = {short(d - 1), short(d - 1)}, one = {1, 1};
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
@@ -909,6 +910,9 @@ __global__ __launch_bounds__(256) void block16_fix_kernel(int16_t *__restrict__ 
                 const v2s f = __builtin_bit_cast(v2s, xq);
                 y[q] = __builtin_bit_cast(int, v2s((f >> dv) + ((f >> dm) & one)));
             }
+        } else {
+            // |f| <= 2^15 and d >= 16: f + 2^(d-1) lies in [0, 2^d), so rhu(f, d) = 0
+            y = v4i{0, 0, 0, 0};
         }
         *p = y;
     }

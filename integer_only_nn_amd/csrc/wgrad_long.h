@@ -180,13 +180,32 @@ template <int SL = 16>
 __global__ __launch_bounds__(256) void wgrad_long_sum(const int32_t *__restrict__ part, int nw, int64_t n,
                                                       int32_t *__restrict__ G, uint32_t *__restrict__ absmax) {
     static_assert(SL == 16, "16 slices of 16 groups");
+    typedef unsigned v4u __attribute__((ext_vector_type(4)));  // sums wrap modulo 2^32
     __shared__ uint32_t red[SL][64];
     const int q = threadIdx.x & 15, z = threadIdx.x >> 4;
+    // whole 16-byte groups when every partial row starts 16-byte aligned
+    const bool vec = (n & 3) == 0 && (reinterpret_cast<uintptr_t>(part) & 15) == 0;
     uint32_t amax = 0;
     for (int64_t i0 = int64_t(blockIdx.x) * 64; i0 < n; i0 += int64_t(gridDim.x) * 64) {
         const int64_t i = i0 + 4 * q;
         uint32_t t[4] = {0, 0, 0, 0};
         int w = z;
+        if (vec && i0 + 64 <= n) {
+            v4u tv = {0, 0, 0, 0};
+            for (; w + 16 * 7 < nw; w += 16 * 8) {
+                v4u x[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) x[u] = *reinterpret_cast<const v4u *>(part + int64_t(w + 16 * u) * n + i);
+#pragma unroll
+                for (int u = 0; u < 8; ++u) tv += x[u];
+            }
+            for (; w < nw; w += 16) tv += *reinterpret_cast<const v4u *>(part + int64_t(w) * n + i);
+            t[0] = tv.x;
+            t[1] = tv.y;
+            t[2] = tv.z;
+            t[3] = tv.w;
+            w = nw;
+        }
         for (; w + 16 * 7 < nw; w += 16 * 8) {
             uint32_t x[8][4];
 #pragma unroll

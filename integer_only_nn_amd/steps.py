@@ -181,28 +181,66 @@ class MLP:
 
 @dataclass
 class ConvStepBuffers:
+    """Device buffers of one 3x3 conv step.
+
+    scal, int32[16]: [0:3] the max |Y|, |dX|, |G|, [3] s_y, [4] s_dx,
+    [5:7] the update's s, ws; [8:11] and [12:15] the two sets the maxima are
+    max-combined into when steps alternate (alternate=True): each step's
+    update clears the set the next step uses, so no fill kernel runs per
+    step; the maxima of the step just taken are then in set `maxima()`."""
     Y: torch.Tensor
     y8: torch.Tensor
     dX: torch.Tensor
     dx8: torch.Tensor
     G: torch.Tensor
-    scal: torch.Tensor   # [absmax Y, dX, G, s_y, s_dx, s, ws]
+    scal: torch.Tensor
     gq: Optional[torch.Tensor] = None
     ws: Optional[torch.Tensor] = None   # weight-gradient workspace (None: no fast path)
     rws: Optional[torch.Tensor] = None  # one-pass requantisation workspace (None: two passes)
+    alternate: bool = False
+    phase: int = 0
 
     @staticmethod
-    def make(N, H, W, Cin, Cout, device, with_gq=False, one_pass=True):
+    def make(N, H, W, Cin, Cout, device, with_gq=False, one_pass=True, alternate=False):
         d = ops.conv_desc(N, H, W, Cin, Cout)
         wsb = ops.int_conv_wgrad_workspace_bytes(d)
         rwb = ops.int_conv_requant_workspace_bytes(d) if one_pass else 0
         return ConvStepBuffers(_i32(N, H, W, Cout, device=device), _i8(N, H, W, Cout, device=device),
                                _i32(N, H, W, Cin, device=device), _i8(N, H, W, Cin, device=device),
                                _i32(Cout, 3, 3, Cin, device=device),
-                               torch.zeros(8, dtype=torch.int32, device=device),
+                               torch.zeros(16, dtype=torch.int32, device=device),
                                _i32(Cout, 3, 3, Cin, device=device) if with_gq else None,
                                torch.empty(wsb, dtype=torch.uint8, device=device) if wsb else None,
-                               torch.empty(rwb, dtype=torch.uint8, device=device) if rwb else None)
+                               torch.empty(rwb, dtype=torch.uint8, device=device) if rwb else None,
+                               alternate)
+
+    def maxima(self):
+        """The max |Y|, |dX|, |G| scalars of the last step (device view)."""
+        if not self.alternate:
+            return self.scal[0:3]
+        o = 8 if self.phase == 1 else 12
+        return self.scal[o:o + 3]
+
+    def _sets(self, stream):
+        """The maxima of this step and the set the update clears (None: a
+        fill kernel cleared this step's set)."""
+        s = self.scal
+        if not self.alternate:
+            ops.ionn_fill_u32(s[0:3], 0, stream=stream)
+            return s[0:3], None
+        m = s[8:11] if self.phase == 0 else s[12:15]
+        nxt = s[12:15] if self.phase == 0 else s[8:11]
+        self.phase ^= 1
+        return m, nxt
+
+
+def _conv_update(buf, m, nxt, tb_w, mu, Wt, stream):
+    s = buf.scal
+    if nxt is None:
+        ops.niti_quantize_update(buf.G, m[2:3], tb_w, mu, Wt, shifts_out=s[5:7], gq_out=buf.gq, stream=stream)
+    else:
+        ops.niti_quantize_update_clear(buf.G, m[2:3], tb_w, mu, Wt, nxt, shifts_out=s[5:7], gq_out=buf.gq,
+                                       stream=stream)
 
 
 def conv_step(X, Wt, dY, buf: ConvStepBuffers, tb_a=TB_DELTA, tb_d=TB_DELTA, tb_w=TB_WEIGHT,
@@ -211,14 +249,13 @@ def conv_step(X, Wt, dY, buf: ConvStepBuffers, tb_a=TB_DELTA, tb_d=TB_DELTA, tb_
     Cout = Wt.shape[0]
     d = ops.conv_desc(N, H, W_, Cin, Cout)
     s = buf.scal
-    ops.ionn_fill_u32(s[0:3], 0, stream=stream)
-    ops.int_conv_fwd(X, Wt, buf.Y, d, absmax_Y=s[0:1], stream=stream)
-    ops.niti_quantize(buf.Y, s[0:1], tb_a, False, buf.y8, shift_out=s[3:4], stream=stream)
-    ops.int_conv_dgrad(dY, Wt, buf.dX, d, absmax_dX=s[1:2], stream=stream)
-    ops.niti_quantize(buf.dX, s[1:2], tb_d, False, buf.dx8, shift_out=s[4:5], stream=stream)
-    ops.int_conv_wgrad(dY, X, buf.G, d, absmax_G=s[2:3], workspace=buf.ws, stream=stream)
-    ops.niti_quantize_update(buf.G, s[2:3], tb_w, mu, Wt, shifts_out=s[5:7], gq_out=buf.gq,
-                             stream=stream)
+    m, nxt = buf._sets(stream)
+    ops.int_conv_fwd(X, Wt, buf.Y, d, absmax_Y=m[0:1], stream=stream)
+    ops.niti_quantize(buf.Y, m[0:1], tb_a, False, buf.y8, shift_out=s[3:4], stream=stream)
+    ops.int_conv_dgrad(dY, Wt, buf.dX, d, absmax_dX=m[1:2], stream=stream)
+    ops.niti_quantize(buf.dX, m[1:2], tb_d, False, buf.dx8, shift_out=s[4:5], stream=stream)
+    ops.int_conv_wgrad(dY, X, buf.G, d, absmax_G=m[2:3], workspace=buf.ws, stream=stream)
+    _conv_update(buf, m, nxt, tb_w, mu, Wt, stream)
 
 
 def conv_step_fused(X, Wt, dY, buf: ConvStepBuffers, tb_a=TB_DELTA, tb_d=TB_DELTA, tb_w=TB_WEIGHT,
@@ -227,19 +264,20 @@ def conv_step_fused(X, Wt, dY, buf: ConvStepBuffers, tb_a=TB_DELTA, tb_d=TB_DELT
     (64 -> 64 channels): y8, dx8, G, the update and every shift as in
     conv_step; buf.Y and buf.dX are not written (the int32 sums are never
     stored).  With buf.rws each requantising contraction is one pass plus a
-    streaming pass over its int8 output, else two contraction passes."""
+    streaming pass over its int8 output, else two contraction passes.  With
+    buf.alternate no fill kernel runs (a captured HIP graph must then hold
+    an even number of steps)."""
     N, H, W_, Cin = X.shape
     Cout = Wt.shape[0]
     d = ops.conv_desc(N, H, W_, Cin, Cout)
     s = buf.scal
-    ops.ionn_fill_u32(s[0:3], 0, stream=stream)
-    ops.int_conv_fwd_requant(X, Wt, buf.y8, d, tb_a, False, s[0:1], shift_out=s[3:4], workspace=buf.rws,
+    m, nxt = buf._sets(stream)
+    ops.int_conv_fwd_requant(X, Wt, buf.y8, d, tb_a, False, m[0:1], shift_out=s[3:4], workspace=buf.rws,
                              stream=stream)
-    ops.int_conv_dgrad_requant(dY, Wt, buf.dx8, d, tb_d, s[1:2], shift_out=s[4:5], workspace=buf.rws,
+    ops.int_conv_dgrad_requant(dY, Wt, buf.dx8, d, tb_d, m[1:2], shift_out=s[4:5], workspace=buf.rws,
                                stream=stream)
-    ops.int_conv_wgrad(dY, X, buf.G, d, absmax_G=s[2:3], workspace=buf.ws, stream=stream)
-    ops.niti_quantize_update(buf.G, s[2:3], tb_w, mu, Wt, shifts_out=s[5:7], gq_out=buf.gq,
-                             stream=stream)
+    ops.int_conv_wgrad(dY, X, buf.G, d, absmax_G=m[2:3], workspace=buf.ws, stream=stream)
+    _conv_update(buf, m, nxt, tb_w, mu, Wt, stream)
 
 
 # ---------------------------------------------------------------------------

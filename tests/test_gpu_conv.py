@@ -103,6 +103,32 @@ def test_conv_step_fused_vs_oracle(N, H, W, one_pass):
     assert sc[3:7].tolist() == [want["s_y"], want["s_dx"], want["s"], want["ws"]]
 
 
+@pytest.mark.parametrize("fused", [True, False])
+def test_conv_steps_alternating_scalar_sets(fused):
+    """Five steps with the maxima alternating between two scalar sets (each
+    step's update clears the set the next one uses; no fill kernel), each
+    against the oracle's step on the weights the previous one left."""
+    N, H, W = 2, 10, 9
+    d = ionn_synth.conv3x3(N=N, H=H, W=W, Cin=64, Cout=64, seed=91)
+    X, Wt0, dY = d["X"], d["W"], d["dY"]
+    Wt, Xd, dYd = to_dev(Wt0), to_dev(X), to_dev(dY)
+    buf = steps.ConvStepBuffers.make(N, H, W, 64, 64, dev(), with_gq=True, alternate=True)
+    run = steps.conv_step_fused if fused else steps.conv_step
+    for k in range(5):
+        say("conv alternating step", k, "fused" if fused else "int32")
+        run(Xd, Wt, dYd, buf)
+        want = osteps.conv_step(X, Wt0, dY)
+        for name, t in (("y8", buf.y8), ("dx8", buf.dx8), ("G", buf.G), ("Gq", buf.gq)):
+            np.testing.assert_array_equal(host(t), want[name], err_msg=f"step {k}: {name}")
+        np.testing.assert_array_equal(host(Wt), want["W_new"], err_msg=f"step {k}: W")
+        mx = host(buf.maxima()).astype(np.int64) & 0xFFFFFFFF
+        assert mx.tolist() == [oracle.absmax(want["Y32"]), oracle.absmax(want["dX32"]),
+                               oracle.absmax(want["G"])], k
+        sc = host(buf.scal)
+        assert sc[3:7].tolist() == [want["s_y"], want["s_dx"], want["s"], want["ws"]], k
+        Wt0 = want["W_new"]
+
+
 @pytest.mark.parametrize("one_pass", [True, False])
 @pytest.mark.parametrize("relu", [0, 1])
 @pytest.mark.parametrize("tb", [1, 2, 5, 7, 12, 31])

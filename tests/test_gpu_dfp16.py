@@ -74,6 +74,36 @@ def test_dfp16_extreme_mantissas(M, K, N):
     np.testing.assert_array_equal(host(buf.G), want["G"])
 
 
+@pytest.mark.parametrize("M,K,N", [(256, 256, 128), (512, 128, 256)])
+def test_dfp16_blocks_far_below_the_tensor_shift(M, K, N):
+    """Row blocks of X and dY at scales from zero to full range.  Without K
+    splits the contractions store every 32-row block at its own shift, and
+    the in-place pass then moves each block by d = Rs - s_b: from 0 for the
+    full-range blocks past 16 for the all-zero ones (full-range products
+    wrap their chunks, so the tensor's maximum nears 2^31)."""
+    rng = np.random.default_rng(11)
+    scales = [0, 1, 3, 40, 300, 3000, 32767, 32767]
+
+    def rows(n, k):
+        a = np.zeros((n, k), np.int16)
+        for b in range(0, n, 32):
+            sc = scales[(b // 32) % len(scales)]
+            if sc:
+                a[b:b + 32] = rng.integers(-sc, sc + 1, (min(32, n - b), k))
+        return a
+
+    X, dY = rows(M, K), rows(M, N)
+    W = rng.integers(-32768, 32768, (N, K)).astype(np.int16)
+    d = dict(X=X, W=W, dY=dY, eX=-20, eW=-20, edY=-20)
+    want = osteps.dfp16_step(X, -20, W, -20, dY, -20)
+    buf = _run(d, M, K, N)
+    np.testing.assert_array_equal(host(buf.Y), want["Y"])
+    np.testing.assert_array_equal(host(buf.dX), want["dX"])
+    np.testing.assert_array_equal(host(buf.G), want["G"])
+    e = host(buf.exps).tolist()
+    assert e[:3] == [want["eY"], want["edX"], want["eG"]]
+
+
 def test_dfp16_exponent_overflow_flagged():
     X = np.full((16, 64), 30000, np.int16)
     W = np.full((16, 64), 30000, np.int16)

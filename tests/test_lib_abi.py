@@ -106,7 +106,7 @@ def test_conv_refuses_bad_kernel_or_pad(kw):
 
 def test_conv_wgrad_workspace_query():
     """Workspace for the 64-channel fast path (one partial G per compute
-    unit plus one per 16 of them, 64*576 int32 each) and for full-row-window
+    unit, 64*576 int32 each) and for full-row-window
     filters; 0 otherwise."""
     big = lib.int_conv_wgrad_workspace_bytes(ctypes.byref(_desc(Cin=64, Cout=64, W=56, H=56, N=128)))
     assert big > 0 and big % (64 * 576 * 4) == 0
