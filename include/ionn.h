@@ -111,8 +111,8 @@ int int_linear_wgrad(const int8_t *dY, const int8_t *X, int32_t *G, int64_t B,
                      int64_t IN, int64_t OUT, uint32_t *absmax_G, void *stream);
 
 /* The same weight gradient with a caller-provided workspace, for a small G
- * over a long batch (G within 32 blocks of 32 x 32, at most 256 per side,
- * B >= 4096): each range of the batch leaves its partial G in the workspace
+ * over a long batch (G within 32 blocks of 32 x 32, between 2 and 256 per
+ * side, B >= 4096): each range of the batch leaves its partial G in the workspace
  * and one pass sums them (modulo 2^32, so the result is the one above bit
  * for bit) and takes the max, instead of adding into a cleared G with
  * atomics.  int_linear_wgrad_workspace_bytes gives the bytes needed (0 when

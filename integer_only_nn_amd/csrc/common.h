@@ -6,6 +6,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
@@ -36,6 +37,19 @@ inline hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s);
 
 inline bool aligned(const void *p, size_t a) {
     return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0;
+}
+
+// Compute units of the current device (persistent grids), cached per device.
+inline int device_cus() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+        v = 256;
+    cache[dev].store(v, std::memory_order_relaxed);
+    return v;
 }
 
 constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;

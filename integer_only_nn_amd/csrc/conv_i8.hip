@@ -570,19 +570,6 @@ unsigned direct_blocks(int64_t n) {
     return unsigned(b < 1 ? 1 : (b > 4096 ? 4096 : b));
 }
 
-// Compute units of the current device (persistent grids).
-int device_cus() {
-    static std::atomic<int> cache[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    int v = cache[dev].load(std::memory_order_relaxed);
-    if (v > 0) return v;
-    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
-        v = 256;
-    cache[dev].store(v, std::memory_order_relaxed);
-    return v;
-}
-
 // The 64-channel halo-tiled kernel applies (see conv3x3.h).
 bool fast_c64(const ionn_conv_desc *d, const void *in, const void *w, const void *out) {
     return geom33(d) && d->Cin == 64 && d->Cout == 64 && c3::fits(d->W) && aligned(in, 16) &&
@@ -861,9 +848,7 @@ int int_conv_wgrad(const int8_t *dY, const int8_t *X, int32_t *G, const ionn_con
             int32_t *part = static_cast<int32_t *>(workspace);
             conv_rows_wgrad<<<dim3(unsigned(rg)), dim3(kRowsWgradThreads), 0, st>>>(dY, X, G, desc->N, sg, part);
             if (int rc = check_launch("int_conv_wgrad")) return rc;
-            int64_t blocks = (n_g + 63) / 64;
-            if (blocks > 2048) blocks = 2048;
-            wl::wgrad_long_sum<><<<dim3(unsigned(blocks)), dim3(256), 0, st>>>(part, int(rg), n_g, G, absmax_G);
+            wl::sum_partials(part, int(rg), n_g, G, absmax_G, st);
             return check_launch("int_conv_wgrad");
         }
         zero_i32_kernel<<<dim3(direct_blocks(n_g)), dim3(256), 0, st>>>(G, n_g);
@@ -901,10 +886,8 @@ int int_conv_wgrad(const int8_t *dY, const int8_t *X, int32_t *G, const ionn_con
         c3::conv3x3_wgrad_kernel<<<dim3(P), dim3(c3::NTF), 0, st>>>(dY, X, part, int(desc->N),
                                                                     int(desc->H), int(desc->W));
         if (int rc = check_launch("int_conv_wgrad")) return rc;
-        // one pass over the P partial rows: 64 elements of G per workgroup,
-        // 16 slices of the rows each, with the max
-        wl::wgrad_long_sum<><<<dim3(unsigned(c3::GSZ / 64)), dim3(256), 0, st>>>(part, int(P), c3::GSZ, G,
-                                                                                 absmax_G);
+        // one pass over the P partial rows, with the max
+        wl::sum_partials(part, int(P), c3::GSZ, G, absmax_G, st);
         return check_launch("int_conv_wgrad");
     }
     const int M = Cout, N = 9 * Cin, K = npix;

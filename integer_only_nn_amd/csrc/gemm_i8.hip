@@ -7,11 +7,13 @@
 //   wgrad G  = dY^T X : A = dY [K=B][M=OUT] (M-major), B = X [K=B][N=IN]   (N-major)
 //
 // Tile-aligned problems take the 256x256x128 direct-to-LDS kernel of
-// gemm256.h (v_mfma_i32_32x32x32_i8); other large problems run 256x256x64
-// bounds-checked tiles of the generic mainloop (gemm_core.h), small ones
-// 64x64 tiles.  The epilogue fuses dgrad's ReLU mask and the max-abs that
+// gemm256.h (v_mfma_i32_32x32x32_i8); a long batch through layers of at most
+// 160 inputs and outputs takes gemm_skinny.h; other large problems run
+// 256x256x64 bounds-checked tiles of the generic mainloop (gemm_core.h),
+// small ones 64x64 tiles.  The epilogue fuses dgrad's ReLU mask and the max-abs that
 // feeds the NITI shift.
 #include "gemm256.h"
+#include "gemm_skinny.h"
 #include "wgrad_long.h"
 
 namespace ionn {
@@ -92,6 +94,10 @@ int int_linear_fwd(const int8_t *X, const int8_t *W, int32_t *Y, int64_t B, int6
         g256::launch<true, true>(X, IN, W, IN, ep, M, N, K, st);
         return check_launch("int_linear_fwd");
     }
+    if (sk::skinny_fits(M, N, K, X, W, Y, nullptr)) {
+        sk::skinny_launch(false, X, W, Y, nullptr, absmax_Y, M, N, K, st);
+        return check_launch("int_linear_fwd");
+    }
     launch_linear(sa, sb, ep, M, N, K, tile_aligned(M, N, K) && sa.vec && sb.vec && ep.vec, st);
     return check_launch("int_linear_fwd");
 }
@@ -156,6 +162,10 @@ int int_linear_dgrad(const int8_t *dY, const int8_t *W, const int8_t *relu_act, 
            relu_act, absmax_dX, false};
     if (fast256(M, N, K, dY, OUT, W, IN, ep)) {
         g256::launch<true, false>(dY, OUT, W, IN, ep, M, N, K, st);
+        return check_launch("int_linear_dgrad");
+    }
+    if (sk::skinny_fits(M, N, K, dY, W, dX, relu_act)) {
+        sk::skinny_launch(true, dY, W, dX, relu_act, absmax_dX, M, N, K, st);
         return check_launch("int_linear_dgrad");
     }
     launch_linear(sa, sb, ep, M, N, K, tile_aligned(M, N, K) && sa.vec && sb.vec && ep.vec, st);
@@ -235,10 +245,7 @@ int int_linear_wgrad_ws(const int8_t *dY, const int8_t *X, int32_t *G, int64_t B
     int32_t *part = static_cast<int32_t *>(workspace);
     const int nw = wl::wgrad_long_launch(dY, X, B, int(OUT), int(IN), G, part, st);
     if (int rc = check_launch("int_linear_wgrad_ws")) return rc;
-    const int64_t n = OUT * IN;
-    int64_t blocks = (n + 63) / 64;
-    if (blocks > 2048) blocks = 2048;
-    wl::wgrad_long_sum<><<<dim3(unsigned(blocks)), dim3(256), 0, st>>>(part, nw, n, G, absmax_G);
+    wl::sum_partials(part, nw, OUT * IN, G, absmax_G, st);
     return check_launch("int_linear_wgrad_ws");
 }
 

@@ -288,7 +288,7 @@ int bias_grad_launch(const int8_t *d, int64_t M, int64_t C, int32_t *gb, const B
         if (nb >= 1) {
             bias_grad_narrow<<<dim3(unsigned(nb)), dim3(256), 0, st>>>(d, M * C, int(C), part);
             if (int rc = check_launch(name)) return rc;
-            wl::wgrad_long_sum<><<<dim3(unsigned((C + 63) / 64)), dim3(256), 0, st>>>(part, int(nb), C, gb, nullptr);
+            wl::sum_partials(part, int(nb), C, gb, nullptr, st);
             return check_launch(name);
         }
     }
@@ -296,9 +296,7 @@ int bias_grad_launch(const int8_t *d, int64_t M, int64_t C, int32_t *gb, const B
     if (g.vec) bias_grad_kernel<true><<<grid, block, 0, st>>>(d, M, C, g.rows, part);
     else bias_grad_kernel<false><<<grid, block, 0, st>>>(d, M, C, g.rows, part);
     if (int rc = check_launch(name)) return rc;
-    int64_t sb = (C + 63) / 64;
-    if (sb > 2048) sb = 2048;
-    wl::wgrad_long_sum<><<<dim3(unsigned(sb)), dim3(256), 0, st>>>(part, int(g.gy), C, gb, nullptr);
+    wl::sum_partials(part, int(g.gy), C, gb, nullptr, st);
     return check_launch(name);
 }
 

@@ -75,7 +75,7 @@ struct Stage {
             if (q < nd) {
                 if (VEC) {
                     *reinterpret_cast<uint32_t *>(st + r * P + c) = w[j];
-                } else {
+                } else {  // C >= 2: a dword spans at most two rows
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int cc = c + e, wrap = cc >= C;
@@ -172,63 +172,65 @@ __global__ __launch_bounds__(NT) void wgrad_long_kernel(Args g) {
 }
 
 // G[i] = sum over the nw workgroup partials part[w][i] (modulo 2^32), with
-// max |G| max-combined into *absmax (nullable).  A workgroup takes 64
-// consecutive i: thread (slice z, group q) adds part[w][i .. i + 3] for
-// i = 64 b + 4 q and w = z, z + 16, ... (loads of eight partials in flight),
-// and the 16 slices meet in LDS.
-template <int SL = 16>
+// max |G| max-combined into *absmax (nullable).  A workgroup step takes
+// E = 4 (256 / SL) consecutive i: thread (slice z, group q) adds
+// part[w][i .. i + 3] for i = i0 + 4 q and w = z, z + SL, ... (eight loads
+// in flight), and the SL slices meet in LDS.  More slices suit fewer
+// outputs over more partials (sum_partials picks SL).
+template <int SL>
 __global__ __launch_bounds__(256) void wgrad_long_sum(const int32_t *__restrict__ part, int nw, int64_t n,
                                                       int32_t *__restrict__ G, uint32_t *__restrict__ absmax) {
-    static_assert(SL == 16, "16 slices of 16 groups");
+    static_assert(SL == 16 || SL == 64, "16 or 64 slices");
+    constexpr int GR = 256 / SL, E = 4 * GR;
     typedef unsigned v4u __attribute__((ext_vector_type(4)));  // sums wrap modulo 2^32
-    __shared__ uint32_t red[SL][64];
-    const int q = threadIdx.x & 15, z = threadIdx.x >> 4;
+    __shared__ uint32_t red[SL][E];
+    const int q = threadIdx.x % GR, z = threadIdx.x / GR;
     // whole 16-byte groups when every partial row starts 16-byte aligned
     const bool vec = (n & 3) == 0 && (reinterpret_cast<uintptr_t>(part) & 15) == 0;
     uint32_t amax = 0;
-    for (int64_t i0 = int64_t(blockIdx.x) * 64; i0 < n; i0 += int64_t(gridDim.x) * 64) {
+    for (int64_t i0 = int64_t(blockIdx.x) * E; i0 < n; i0 += int64_t(gridDim.x) * E) {
         const int64_t i = i0 + 4 * q;
         uint32_t t[4] = {0, 0, 0, 0};
         int w = z;
-        if (vec && i0 + 64 <= n) {
+        if (vec && i0 + E <= n) {
             v4u tv = {0, 0, 0, 0};
-            for (; w + 16 * 7 < nw; w += 16 * 8) {
+            for (; w + SL * 7 < nw; w += SL * 8) {
                 v4u x[8];
 #pragma unroll
-                for (int u = 0; u < 8; ++u) x[u] = *reinterpret_cast<const v4u *>(part + int64_t(w + 16 * u) * n + i);
+                for (int u = 0; u < 8; ++u) x[u] = *reinterpret_cast<const v4u *>(part + int64_t(w + SL * u) * n + i);
 #pragma unroll
                 for (int u = 0; u < 8; ++u) tv += x[u];
             }
-            for (; w < nw; w += 16) tv += *reinterpret_cast<const v4u *>(part + int64_t(w) * n + i);
+            for (; w < nw; w += SL) tv += *reinterpret_cast<const v4u *>(part + int64_t(w) * n + i);
             t[0] = tv.x;
             t[1] = tv.y;
             t[2] = tv.z;
             t[3] = tv.w;
             w = nw;
         }
-        for (; w + 16 * 7 < nw; w += 16 * 8) {
+        for (; w + SL * 7 < nw; w += SL * 8) {
             uint32_t x[8][4];
 #pragma unroll
             for (int u = 0; u < 8; ++u)
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    x[u][e] = i + e < n ? uint32_t(part[int64_t(w + 16 * u) * n + i + e]) : 0u;
+                    x[u][e] = i + e < n ? uint32_t(part[int64_t(w + SL * u) * n + i + e]) : 0u;
 #pragma unroll
             for (int u = 0; u < 8; ++u)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) t[e] += x[u][e];
         }
-        for (; w < nw; w += 16)
+        for (; w < nw; w += SL)
 #pragma unroll
             for (int e = 0; e < 4; ++e) t[e] += i + e < n ? uint32_t(part[int64_t(w) * n + i + e]) : 0u;
         __syncthreads();
 #pragma unroll
         for (int e = 0; e < 4; ++e) red[z][4 * q + e] = t[e];
         __syncthreads();
-        if (threadIdx.x < 64 && i0 + threadIdx.x < n) {
+        if (threadIdx.x < E && i0 + threadIdx.x < n) {
             uint32_t tot = 0;
 #pragma unroll
-            for (int zz = 0; zz < 16; ++zz) tot += red[zz][threadIdx.x];
+            for (int zz = 0; zz < SL; ++zz) tot += red[zz][threadIdx.x];
             G[i0 + threadIdx.x] = int32_t(tot);
             amax = max(amax, abs_u32(int32_t(tot)));
         }
@@ -239,6 +241,22 @@ __global__ __launch_bounds__(256) void wgrad_long_sum(const int32_t *__restrict_
     }
 }
 
+// Launches the sum of nw partial rows of n elements into G (with the max
+// when absmax is not null), at most 2048 workgroups (each then loops):
+// 16 slices (256-byte segments of each partial row) unless the rows are too
+// short to give the compute units work, then 64 (64-byte segments; 32
+// slices measured slower than 16 on 36864-element rows).
+inline void sum_partials(const int32_t *part, int nw, int64_t n, int32_t *G, uint32_t *absmax, hipStream_t st) {
+    auto blocks = [n](int64_t e) {
+        const int64_t b = (n + e - 1) / e;
+        return unsigned(b < 1 ? 1 : (b > 2048 ? 2048 : b));
+    };
+    if (n >= 4096)
+        wgrad_long_sum<16><<<dim3(blocks(64)), dim3(256), 0, st>>>(part, nw, n, G, absmax);
+    else
+        wgrad_long_sum<64><<<dim3(blocks(16)), dim3(256), 0, st>>>(part, nw, n, G, absmax);
+}
+
 // Workgroups of a launch over a reduction of length K: at least 512 rows
 // each, at most 128.
 inline int64_t wgrad_long_groups(int64_t K) {
@@ -247,10 +265,11 @@ inline int64_t wgrad_long_groups(int64_t K) {
 }
 
 // Whether the kernel takes the shape: G within 32 blocks of 32 x 32, at most
-// 256 per side, and a reduction long enough to split.
+// 256 per side, at least 2 (a staged dword then spans at most two rows), and
+// a reduction long enough to split.
 inline bool wgrad_long_fits(int64_t K, int64_t M, int64_t N, const void *a, const void *b) {
     const int64_t mb = (M + 31) / 32, nb = (N + 31) / 32;
-    return M >= 1 && N >= 1 && mb <= MAXB && nb <= MAXB && mb * nb <= MAXBLK && K >= 4096 && aligned(a, 4) &&
+    return M >= 2 && N >= 2 && mb <= MAXB && nb <= MAXB && mb * nb <= MAXBLK && K >= 4096 && aligned(a, 4) &&
            aligned(b, 4) && K * (M > N ? M : N) < (int64_t(1) << 31);
 }
 

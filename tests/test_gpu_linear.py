@@ -51,11 +51,35 @@ def test_contractions_vs_oracle(B, IN, OUT):
     assert am == [oracle.absmax(Yo), oracle.absmax(dXo), oracle.absmax(Go)]
 
 
+# a long batch through narrow layers (N, K <= 160): the row-run staging
+# path of fwd and dgrad (rows of any byte length, fragments built with
+# v_alignbyte, bytes past K masked), ragged last stages, single columns
+SKINNY = [(65536, 147, 160), (65536, 160, 2), (65536, 2, 160), (4096, 160, 147), (4112, 147, 160),
+          (4096, 1, 1), (8192, 160, 160), (4096, 33, 31), (4128, 64, 96), (6000, 100, 5)]
+
+
+@pytest.mark.parametrize("B,IN,OUT", SKINNY)
+def test_skinny_contractions_vs_oracle(B, IN, OUT):
+    say("skinny", B, IN, OUT)
+    d = ionn_synth.single_linear(B=B, IN=IN, OUT=OUT, seed=B + 3 * IN + OUT)
+    X, W, dY = d["X"], d["W"], d["dY"]
+    act = ionn_synth.uniform_int(B + IN, 20, (B, IN), -128, 127)
+    Y, dX, G, am = _contract(X, W, dY, act=act)
+    Yo = oracle.linear_fwd(X, W)
+    dXo = oracle.relu_mask(oracle.linear_dgrad(dY, W), act)
+    Go = oracle.linear_wgrad(dY, X)
+    np.testing.assert_array_equal(Y, Yo)
+    np.testing.assert_array_equal(dX, dXo)
+    np.testing.assert_array_equal(G, Go)
+    assert am == [oracle.absmax(Yo), oracle.absmax(dXo), oracle.absmax(Go)]
+
+
 # small G over a long batch: the LDS row-copy path (byte and dword copies,
-# one to 32 blocks of 32 x 32, ragged batch tails) and, past 32 blocks, the
+# rows of 2 and 3 bytes whose dwords span two rows, one to 32 blocks of
+# 32 x 32, ragged batch tails) and, past 32 blocks or with 1-byte rows, the
 # generic split
 LONG_WGRAD = [(65536, 147, 160), (65536, 160, 2), (5000, 33, 7), (4097, 256, 128), (9000, 250, 130),
-              (20000, 64, 96)]
+              (20000, 64, 96), (4096, 1, 1), (5000, 1, 7), (4500, 3, 1), (4099, 2, 5)]
 
 
 @pytest.mark.parametrize("B,IN,OUT", LONG_WGRAD)
@@ -71,7 +95,8 @@ def test_wgrad_long_batch(B, IN, OUT):
     assert u32(am) == oracle.absmax(want)
 
 
-@pytest.mark.parametrize("B,IN,OUT", [(65536, 147, 160), (65536, 160, 2), (5000, 33, 7), (4097, 256, 128)])
+@pytest.mark.parametrize("B,IN,OUT", [(65536, 147, 160), (65536, 160, 2), (5000, 33, 7), (4097, 256, 128),
+                                   (5000, 2, 7), (4500, 3, 2)])
 def test_wgrad_long_batch_workspace(B, IN, OUT):
     # the partial-sums form gives the same G and max as the oracle; called
     # twice in a row (the workspace is overwritten, never cleared)
