@@ -50,10 +50,11 @@ def test_linear_validation():
 
 def test_linear_wgrad_workspace_query_and_checks():
     # a small G over a long batch takes the partial-sums path: groups of at
-    # least 512 rows, at most 128, times the G size
+    # least 256 rows, at most 256, times the G size
     need = lib.int_linear_wgrad_workspace_bytes(65536, 147, 160)
-    assert need == 128 * 147 * 160 * 4
-    assert lib.int_linear_wgrad_workspace_bytes(5000, 33, 7) == 10 * 33 * 7 * 4
+    assert need == 256 * 147 * 160 * 4
+    assert lib.int_linear_wgrad_workspace_bytes(5000, 33, 7) == 20 * 33 * 7 * 4
+    assert lib.int_linear_wgrad_workspace_bytes(200000, 33, 7) == 256 * 33 * 7 * 4
     # short batches, large G, bad sizes: no workspace (the call is int_linear_wgrad)
     assert lib.int_linear_wgrad_workspace_bytes(100, 64, 32) == 0
     assert lib.int_linear_wgrad_workspace_bytes(65536, 512, 512) == 0
