@@ -102,22 +102,41 @@ __global__ __launch_bounds__(64 * BG_WAVES) void bias_grad_kernel(const int8_t *
     for (int e = 0; e < W; ++e) s[e] = 0;
     if (c0 < C) {
         if (VEC) {
+            // bytes offset by 128 (x ^ 0x80 = x + 128, in [0, 255]) and added
+            // two columns per 32-bit add in 16-bit fields: even bytes of a
+            // dword in one word, odd bytes in another; a field holds the sum
+            // of up to 257 rows, so the fields go to the int32 sums (less 128
+            // per row) every 256 rows of the lane
+            constexpr int U = 8, S = BG_WAVES;
             int64_t r = r0 + wave;
-            constexpr int U = 4, S = BG_WAVES;
-            for (; r + (U - 1) * S < r1; r += U * S) {
-                v4i w[U];
+            while (r < r1) {
+                uint32_t fe[4] = {0, 0, 0, 0}, fo[4] = {0, 0, 0, 0};
+                const int64_t rend = min(r1, r + int64_t(256) * S);
+                int n = 0;
+                auto add = [&](const v4i &w) {
 #pragma unroll
-                for (int u = 0; u < U; ++u) w[u] = *reinterpret_cast<const v4i *>(d + (r + u * S) * C + c0);
+                    for (int q = 0; q < 4; ++q) {
+                        const uint32_t x = uint32_t(w[q]) ^ 0x80808080u;
+                        fe[q] += x & 0x00ff00ffu;
+                        fo[q] += (x >> 8) & 0x00ff00ffu;
+                    }
+                };
+                for (; r + (U - 1) * S < rend; r += U * S, n += U) {
+                    v4i w[U];
 #pragma unroll
-                for (int u = 0; u < U; ++u)
+                    for (int u = 0; u < U; ++u) w[u] = *reinterpret_cast<const v4i *>(d + (r + u * S) * C + c0);
 #pragma unroll
-                    for (int e = 0; e < W; ++e)
-                        s[e] += int32_t(int8_t(uint8_t(uint32_t(w[u][e >> 2]) >> (8 * (e & 3)))));
-            }
-            for (; r < r1; r += S) {
-                const v4i w = *reinterpret_cast<const v4i *>(d + r * C + c0);
+                    for (int u = 0; u < U; ++u) add(w[u]);
+                }
+                for (; r < rend; r += S, ++n) add(*reinterpret_cast<const v4i *>(d + r * C + c0));
+                const int32_t off = 128 * n;
 #pragma unroll
-                for (int e = 0; e < W; ++e) s[e] += int32_t(int8_t(uint8_t(uint32_t(w[e >> 2]) >> (8 * (e & 3)))));
+                for (int q = 0; q < 4; ++q) {
+                    s[4 * q] += int32_t(fe[q] & 0xffffu) - off;
+                    s[4 * q + 1] += int32_t(fo[q] & 0xffffu) - off;
+                    s[4 * q + 2] += int32_t(fe[q] >> 16) - off;
+                    s[4 * q + 3] += int32_t(fo[q] >> 16) - off;
+                }
             }
         } else {
             for (int64_t r = r0 + wave; r < r1; r += BG_WAVES) s[0] += int32_t(d[r * C + c0]);

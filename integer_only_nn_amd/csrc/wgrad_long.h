@@ -243,15 +243,15 @@ __global__ __launch_bounds__(256) void wgrad_long_sum(const int32_t *__restrict_
 
 // Launches the sum of nw partial rows of n elements into G (with the max
 // when absmax is not null), at most 2048 workgroups (each then loops):
-// 16 slices (256-byte segments of each partial row) unless the rows are too
-// short to give the compute units work, then 64 (64-byte segments; 32
-// slices measured slower than 16 on 36864-element rows).
+// 16 slices (256-byte segments of each partial row) when that still gives
+// 256 workgroups, else 64 (64-byte segments; 32 slices measured slower than
+// 16 on 36864-element rows).
 inline void sum_partials(const int32_t *part, int nw, int64_t n, int32_t *G, uint32_t *absmax, hipStream_t st) {
     auto blocks = [n](int64_t e) {
         const int64_t b = (n + e - 1) / e;
         return unsigned(b < 1 ? 1 : (b > 2048 ? 2048 : b));
     };
-    if (n >= 4096)
+    if (n >= 16384)
         wgrad_long_sum<16><<<dim3(blocks(64)), dim3(256), 0, st>>>(part, nw, n, G, absmax);
     else
         wgrad_long_sum<64><<<dim3(blocks(16)), dim3(256), 0, st>>>(part, nw, n, G, absmax);
