@@ -697,23 +697,26 @@ __global__ __launch_bounds__(NT, 1) void dfpi_kernel(Args g) {
                 bl[j][kh] = frag<B_KM>(st + 3 * PLANE, 64 * wn + 32 * j, kh, lane);
             }
         }
+        // the row corrections of A (sum (-127) ah, sum (-127) al over the
+        // chunk) are the same for both column blocks: formed once, with the
+        // starting value 64, and the start of both blocks' X2 and L2 chains
+        v16i rx = __builtin_amdgcn_mfma_i32_32x32x32_i8(cm, ah[0], c64, 0, 0, 0);
+        v16i rl = __builtin_amdgcn_mfma_i32_32x32x32_i8(cm, al[0], c64, 0, 0, 0);
+        rx = __builtin_amdgcn_mfma_i32_32x32x32_i8(cm, ah[1], rx, 0, 0, 0);
+        rl = __builtin_amdgcn_mfma_i32_32x32x32_i8(cm, al[1], rl, 0, 0, 0);
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             v16i h = __builtin_amdgcn_mfma_i32_32x32x32_i8(bh[j][0], ah[0], c16, 0, 0, 0);
-            v16i x = __builtin_amdgcn_mfma_i32_32x32x32_i8(bl[j][0], ah[0], c64, 0, 0, 0);
-            v16i l = __builtin_amdgcn_mfma_i32_32x32x32_i8(bl[j][0], al[0], c64, 0, 0, 0);
+            v16i x = __builtin_amdgcn_mfma_i32_32x32x32_i8(bl[j][0], ah[0], rx, 0, 0, 0);
+            v16i l = __builtin_amdgcn_mfma_i32_32x32x32_i8(bl[j][0], al[0], rl, 0, 0, 0);
             x = __builtin_amdgcn_mfma_i32_32x32x32_i8(bh[j][0], al[0], x, 0, 0, 0);
-            l = __builtin_amdgcn_mfma_i32_32x32x32_i8(cm, al[0], l, 0, 0, 0);
-            x = __builtin_amdgcn_mfma_i32_32x32x32_i8(cm, ah[0], x, 0, 0, 0);
             h = __builtin_amdgcn_mfma_i32_32x32x32_i8(bh[j][1], ah[1], h, 0, 0, 0);
             l = __builtin_amdgcn_mfma_i32_32x32x32_i8(bl[j][0], cm, l, 0, 0, 0);
             x = __builtin_amdgcn_mfma_i32_32x32x32_i8(bh[j][0], cm, x, 0, 0, 0);
             l = __builtin_amdgcn_mfma_i32_32x32x32_i8(bl[j][1], al[1], l, 0, 0, 0);
             x = __builtin_amdgcn_mfma_i32_32x32x32_i8(bl[j][1], ah[1], x, 0, 0, 0);
-            l = __builtin_amdgcn_mfma_i32_32x32x32_i8(cm, al[1], l, 0, 0, 0);
             x = __builtin_amdgcn_mfma_i32_32x32x32_i8(bh[j][1], al[1], x, 0, 0, 0);
             l = __builtin_amdgcn_mfma_i32_32x32x32_i8(bl[j][1], cm, l, 0, 0, 0);
-            x = __builtin_amdgcn_mfma_i32_32x32x32_i8(cm, ah[1], x, 0, 0, 0);
             x = __builtin_amdgcn_mfma_i32_32x32x32_i8(bh[j][1], cm, x, 0, 0, 0);
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
