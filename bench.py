@@ -894,7 +894,7 @@ def _model_layers(d):
 
 # The translation units (and the headers they include) that build the
 # contraction and update kernels the traffic figures describe.
-TRAFFIC_SOURCES = ("common.h", "gemm_core.h", "gemm256.h", "wgrad_long.h", "gemm_i8.hip", "niti.hip")
+TRAFFIC_SOURCES = ("common.h", "gemm_core.h", "gemm256.h", "gemm_skinny.h", "wgrad_long.h", "gemm_i8.hip", "niti.hip")
 
 
 def _kernel_source_hash():
