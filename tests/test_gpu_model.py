@@ -53,6 +53,20 @@ def test_arc_fault_network_large_batch():
         layers = _check_step(m, layers, d["X"], d["labels"], d["tmc"], d["tmw"], i)
 
 
+def test_arc_fault_network_bench_batch():
+    """The batch the benchmark times (65536): the narrow-layer contractions
+    over 512 stages on one workgroup per compute unit, the long-batch
+    weight gradients over 256 batch ranges, the full-row-window conv
+    kernels; two steps, every weight, offset, shift and output."""
+    B = 65536
+    d = ionn_synth.arc_fault(B=B, seed=5)
+    layers = osteps.arc_fault_layers(d)
+    m = steps.Model(layers, B, dev())
+    for i in range(2):
+        say("arc-fault B=65536 step", i)
+        layers = _check_step(m, layers, d["X"], d["labels"], d["tmc"], d["tmw"], i)
+
+
 def _conv_layer(rng, H, W, Cin, Cout, K, pad, relu):
     return dict(kind="conv", relu=relu, H=H, W=W, Cin=Cin, Cout=Cout, KH=K, KW=K, pad=pad,
                 weight=np.clip(np.round(rng.normal(0, 12, (Cout, K, K, Cin))), -128, 127).astype(np.int8),
