@@ -17,6 +17,7 @@
 #include "common.h"
 #include "wgrad_long.h"
 
+#include <algorithm>
 #include <mutex>
 
 namespace ionn {
@@ -75,8 +76,10 @@ __global__ __launch_bounds__(256) void oss_kernel(const int32_t *__restrict__ ac
         }
         done = nfull;
     }
-    for (int64_t j = done + tid; j < n; j += nthreads) {
-        const int64_t ch = j % C;
+    // n < 2^31: 32-bit element and channel indices
+    const uint32_t Cu = uint32_t(C);
+    for (uint32_t j = uint32_t(done + tid); j < uint32_t(n); j += uint32_t(nthreads)) {
+        const uint32_t ch = j % Cu;
         out[j] = int8_t(oss_elem(acc[j], offset[ch], mult[ch], int(k[ch]), lo));
     }
 }
@@ -339,7 +342,10 @@ int ionn_oss_requant(const int32_t *acc, const int32_t *offset, const int32_t *m
     const int64_t n = M * C;
     const bool vec = C % 4 == 0 && aligned(acc, 16) && aligned(offset, 16) && aligned(mult, 16) &&
                      aligned(k, 4) && aligned(out, 4);
-    dim3 grid(stream_blocks(n)), block(256);
+    // the element-wise form takes one element per lane (up to 2^21 of them
+    // in flight), the vector form 16 bytes per lane and instruction
+    const int64_t scalar_blocks = std::min<int64_t>((n + 255) / 256, 8192);
+    dim3 grid(vec ? stream_blocks(n) : unsigned(scalar_blocks)), block(256);
     hipStream_t st = as_stream(stream);
     if (vec && relu) oss_kernel<true, true><<<grid, block, 0, st>>>(acc, n, C, offset, mult, k, out);
     else if (vec) oss_kernel<true, false><<<grid, block, 0, st>>>(acc, n, C, offset, mult, k, out);
