@@ -41,29 +41,37 @@ struct Args {
     int M, N, K, nb, ks;  // nb = ceil(N / 32), ks = ceil(K / 32)
 };
 
+// A buffer offset past the end of every resource built here: loads from it
+// return 0 and stores to it are dropped, so lanes outside a tensor need no
+// branch (a lane-dependent branch around a load or store leaves the compiler
+// unable to count the memory operations in flight, and it then drains them
+// all before the next use of a loaded value).
+constexpr uint32_t OOB = 0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *p, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, int(bytes), 0x00020000);
+}
+
 // Rows m0 .. m0 + RS - 1 of A, RS K contiguous bytes from a multiple of 16
 // (m0 is a multiple of RS = 128, the base is 16-byte aligned): thread t holds
 // pieces t, t + NT, ... of 16 bytes.  M K is a multiple of 16, so a piece
-// lies wholly before or wholly past the end of A (then it is not loaded).
-__device__ __forceinline__ void stage_load(v4i (&v)[NQ], const int8_t *a, int K, int64_t m0, int M) {
+// lies wholly before or wholly past the end of A (then it reads as zeros).
+__device__ __forceinline__ void stage_load(v4i (&v)[NQ], __amdgpu_buffer_rsrc_t ar, int K, int64_t m0, int M) {
     const int64_t rows = M - m0 < RS ? M - m0 : RS;
-    const int nq = int(rows * K / 16);
-    const v4i *p = reinterpret_cast<const v4i *>(a + m0 * K);
+    const int nq = rows > 0 ? int(rows * K / 16) : 0;
+    const uint32_t base = uint32_t(m0 * K);
 #pragma unroll
     for (int j = 0; j < NQ; ++j) {
         const int q = int(threadIdx.x) + j * NT;
-        v[j] = q < nq ? p[q] : v4i{0, 0, 0, 0};
+        v[j] = __builtin_amdgcn_raw_buffer_load_b128(ar, int(q < nq ? base + 16u * uint32_t(q) : OOB), 0, 0);
     }
 }
 
-// The pieces to LDS as they lie in memory.
-__device__ __forceinline__ void stage_store(const v4i (&v)[NQ], int K, int8_t *st) {
-    const int nq = RS * K / 16;
+// The pieces to LDS as they lie in memory (all NQ NT pieces: those past the
+// stage's rows are zeros and stay inside the stage buffer).
+__device__ __forceinline__ void stage_store(const v4i (&v)[NQ], int8_t *st) {
 #pragma unroll
-    for (int j = 0; j < NQ; ++j) {
-        const int q = int(threadIdx.x) + j * NT;
-        if (q < nq) reinterpret_cast<v4i *>(st)[q] = v[j];
-    }
+    for (int j = 0; j < NQ; ++j) reinterpret_cast<v4i *>(st)[int(threadIdx.x) + j * NT] = v[j];
 }
 
 // Row r (of the stage), bytes c0 .. c0 + 15 of A from the stage as it lies
@@ -95,20 +103,21 @@ constexpr int NW = 32 * MAXB * 32 * MAXB / 4 / NT;  // dwords per thread, larges
 __device__ __forceinline__ void stage_w(int8_t *st, int8_t *lin, const int8_t *w, int rows, int cols) {
     const int t = int(threadIdx.x);
     const int n4 = rows * cols / 4, tail = rows * cols - 4 * n4;
-    const uint32_t *w32 = reinterpret_cast<const uint32_t *>(w);
+    const __amdgpu_buffer_rsrc_t wr = rsrc(w, int64_t(rows) * cols);
     uint32_t v[NW];
 #pragma unroll
     for (int j = 0; j < NW; ++j) {
         const int q = t + j * NT;
-        v[j] = q < n4 ? w32[q] : 0u;
+        v[j] = __builtin_amdgcn_raw_buffer_load_b32(wr, int(q < n4 ? 4u * uint32_t(q) : OOB), 0, 0);
     }
+    const uint8_t tb = __builtin_amdgcn_raw_buffer_load_b8(wr, int(t < tail ? uint32_t(4 * n4 + t) : OOB), 0, 0);
     uint32_t *l32 = reinterpret_cast<uint32_t *>(lin);
 #pragma unroll
     for (int j = 0; j < NW; ++j) {
         const int q = t + j * NT;
         if (q < n4) l32[q] = v[j];
     }
-    if (t < tail) lin[4 * n4 + t] = w[4 * n4 + t];
+    if (t < tail) lin[4 * n4 + t] = int8_t(tb);
     __syncthreads();
     const int dpr = (cols + 3) / 4;  // dwords per padded row
     const int items = rows * dpr;
@@ -133,21 +142,11 @@ __device__ __forceinline__ void stage_w(int8_t *st, int8_t *lin, const int8_t *w
     }
 }
 
-// The four mask bytes of values e0 .. e0 + 3 of a run of `valid` values
-// (past its end: any), as one word.
-__device__ __forceinline__ uint32_t mask_word(const int8_t *ab, int e0, int valid) {
-    if (e0 + 4 <= valid) return *reinterpret_cast<const uint32_t *>(ab + e0);
-    uint32_t a = 0x01010101u;
-    for (int e = 0; e < 4; ++e)
-        if (e0 + e < valid) a = (a & ~(0xffu << (8 * e))) | (uint32_t(uint8_t(ab[e0 + e])) << (8 * e));
-    return a;
-}
-
 // One workgroup per group of stages (persistent over m0 = RS (blockIdx.x +
 // i gridDim.x)).  B is staged once through LDS (fwd: rows n of K bytes;
 // dgrad: rows k of N bytes, read back transposed) into registers; the next
 // stage's dwords are in flight while the current one is contracted.
-template <bool BT>
+template <bool BT, bool N4>
 __global__ __launch_bounds__(NT, 1) void skinny_kernel(Args g) {
     typedef int v2i_ __attribute__((ext_vector_type(2)));
     typedef __attribute__((address_space(3))) v2i_ lds_v2i_t;
@@ -162,6 +161,7 @@ __global__ __launch_bounds__(NT, 1) void skinny_kernel(Args g) {
     // B staged over both buffers as one region of 32 MAXB rows of pitch PA
     // (fwd: rows n of K bytes; dgrad: rows k of N bytes), zero-padded
     static_assert(32 * MAXB * PA <= 2 * SA, "B fits the two stage buffers");
+    static_assert(NQ * NT * 16 <= SA, "a stage's pieces fit its buffer");
     int8_t *bst = &lds[0][0];
     for (int i = int(threadIdx.x); i < 2 * SA / 16; i += NT)
         reinterpret_cast<v4i *>(bst)[i] = v4i{0, 0, 0, 0};
@@ -170,8 +170,9 @@ __global__ __launch_bounds__(NT, 1) void skinny_kernel(Args g) {
     // overlaps B's staging
     const int64_t nstages = (int64_t(g.M) + RS - 1) / RS;
     int64_t sidx = blockIdx.x;
+    const __amdgpu_buffer_rsrc_t ar = rsrc(g.a, int64_t(g.M) * g.K);
     v4i v[NQ];
-    if (sidx < nstages) stage_load(v, g.a, g.K, sidx * RS, g.M);
+    if (sidx < nstages) stage_load(v, ar, g.K, sidx * RS, g.M);
     stage_w(bst, reinterpret_cast<int8_t *>(out_lds), g.w, BT ? g.K : g.N, BT ? g.N : g.K);
     __syncthreads();
     v4i bf[MAXB][MAXB];  // [column block][k step]
@@ -201,23 +202,60 @@ __global__ __launch_bounds__(NT, 1) void skinny_kernel(Args g) {
     int buf = 0;
     uint32_t amax = 0;
     while (sidx < nstages) {
-        stage_store(v, g.K, lds[buf]);
+        stage_store(v, lds[buf]);
         __syncthreads();
         const int64_t m0 = sidx * RS;
         const int64_t nxt = sidx + gridDim.x;
-        if (nxt < nstages) stage_load(v, g.a, g.K, nxt * RS, g.M);
+        // (past the last stage the loads read zeros: no branch around them)
+        stage_load(v, ar, g.K, nxt * RS, g.M);
         // the wavefront's block of C: rows mb .. mb + 31, one contiguous run
         // of `valid` values; its mask words are fetched now, used at the end
         const int64_t mb = m0 + 32 * wave;
         const int64_t brows = g.M - mb < 32 ? g.M - mb : 32;
         const int valid = brows > 0 ? int(brows) * g.N : 0;
         const int8_t *ab = g.act ? g.act + mb * g.N : nullptr;
+        // (whole words in one pass, so that no lane takes a path of byte
+        // loads: the compiler then waits for each word by count, where a
+        // per-lane choice between a word and its bytes made it drain every
+        // load and store before each of the 20 stores below; ab is 4-byte
+        // aligned, as act is and 32 N is a multiple of 4)
+        // Every path issues the same loads (none without a mask: an empty
+        // resource), so that the compiler's count of the memory operations
+        // after the next stage's loads is exact, not the least over the paths.
+        const __amdgpu_buffer_rsrc_t mr = g.act ? rsrc(g.act, int64_t(g.M) * g.N) : rsrc(g.a, 0);
+        const bool masked = g.act != nullptr;
         uint32_t mk[NP];
+        uint32_t tb = 0;
+        if (N4) {
+            // word (j, q): the mask bytes of row lane % 32, columns
+            // n = 32 j + 8 q + 4 (lane / 32) .. + 3, which the lane stores
+            // (past the block's rows or N: read as 0, never stored)
+            const int r = lane & 31;
+            const uint32_t rb = uint32_t((mb + r) * g.N);
 #pragma unroll
-        for (int i = 0; i < NP; ++i) {
-            const int e0 = 4 * (lane + 64 * i);
-            mk[i] = (ab && e0 < valid) ? mask_word(ab, e0, valid) : 0x01010101u;
+            for (int j = 0; j < MAXB; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int n = 32 * j + 8 * q + 4 * (lane >> 5);
+                    mk[4 * j + q] = __builtin_amdgcn_raw_buffer_load_b32(
+                        mr, int(j < nb && n < g.N && r < brows ? rb + uint32_t(n) : OOB), 0, 0);
+                }
+        } else {
+            // word i: the mask bytes of values 4 p .. 4 p + 3 of the run,
+            // p = lane + 64 i, when the run holds all four; of the word the
+            // run ends inside (a last block of brows N values, not a multiple
+            // of 4), value e goes to lane e (tb)
+            const uint32_t rb = uint32_t(mb * g.N);
+#pragma unroll
+            for (int i = 0; i < NP; ++i) {
+                const int e0 = 4 * (lane + 64 * i);
+                mk[i] = __builtin_amdgcn_raw_buffer_load_b32(mr, int(e0 + 4 <= valid ? rb + uint32_t(e0) : OOB), 0, 0);
+            }
+            const int wq = valid >> 2;
+            tb = __builtin_amdgcn_raw_buffer_load_b8(
+                mr, int(lane < (valid & 3) ? rb + uint32_t(4 * wq + lane) : OOB), 0, 0);
         }
+
         v16i acc[MAXB];
 #pragma unroll
         for (int j = 0; j < MAXB; ++j) acc[j] = v16i{};
@@ -231,15 +269,49 @@ __global__ __launch_bounds__(NT, 1) void skinny_kernel(Args g) {
             }
         }
         // lane holds C[m][n .. n + 3] for m = row lane % 32 of the wavefront's
-        // block and n = 32 j + 8 q + 4 (lane / 32).  The block (32 rows of N)
-        // goes through the wavefront's LDS area so that it leaves as one
-        // contiguous run of 32 N int32: rows at pitch N + 4 when N is a
-        // multiple of 4 (16-byte pieces never straddle rows), else at pitch N
-        // (the run itself, written a value at a time).
+        // block and n = 32 j + 8 q + 4 (lane / 32).  The stage's rows of C
+        // are one resource (their bytes stay below 2^31).
+        const int64_t srows = g.M - m0 < RS ? g.M - m0 : RS;
+        const __amdgpu_buffer_rsrc_t cr = rsrc(g.c + m0 * g.N, srows * g.N * 4);
+        if (N4) {
+            // N a multiple of 4: the four values leave as one aligned 16-byte
+            // store (a wavefront writes 32 bytes of each of 32 rows per
+            // instruction, and the L2 joins the rows' pieces); rows past M
+            // and columns past N are not stored.  Rows past M and columns
+            // past N hold 0 (zero A rows, zero-padded B), so the max and min
+            // run over every value without a test.
+            const int r = lane & 31;
+            const uint32_t rb = uint32_t((32 * wave + r) * g.N) * 4u;
+            // (20 stores on every path, those outside C dropped; blocks past
+            // nb hold zeros)
+            int32_t mx = 0, mn = 0;
+#pragma unroll
+            for (int j = 0; j < MAXB; ++j) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int n = 32 * j + 8 * q + 4 * (lane >> 5);
+                    v4i x = {acc[j][4 * q], acc[j][4 * q + 1], acc[j][4 * q + 2], acc[j][4 * q + 3]};
+                    const uint32_t w = masked ? mk[4 * j + q] : 0x01010101u;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) x[e] = int8_t(uint8_t(w >> (8 * e))) > 0 ? x[e] : 0;
+                    mx = max(mx, max(max(x[0], x[1]), max(x[2], x[3])));
+                    mn = min(mn, min(min(x[0], x[1]), min(x[2], x[3])));
+                    __builtin_amdgcn_raw_buffer_store_b128(
+                        x, cr, int(j < nb && n < g.N && r < brows ? rb + 4u * uint32_t(n) : OOB), 0, 0);
+                }
+            }
+            amax = max(amax, max(uint32_t(mx), 0u - uint32_t(mn)));
+            buf ^= 1;
+            sidx = nxt;
+            __syncthreads();
+            continue;
+        }
+        // Otherwise the block (32 rows of N) goes through the wavefront's LDS
+        // area, the run itself at pitch N written a value at a time, so that
+        // it leaves as one contiguous, 16-byte aligned run of 32 N int32.
         int32_t *ob = out_lds + wave * 32 * PO;
-        const bool n4 = (g.N & 3) == 0;
-        const int pn = n4 ? g.N + 4 : g.N;
         {
+            // (blocks wholly inside N: four values a lane, no test)
             const int r = lane & 31;
 #pragma unroll
             for (int j = 0; j < MAXB; ++j) {
@@ -247,14 +319,13 @@ __global__ __launch_bounds__(NT, 1) void skinny_kernel(Args g) {
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const int n = 32 * j + 8 * q + 4 * (lane >> 5);
-                    if (n >= g.N) continue;
-                    if (n4) {
-                        *reinterpret_cast<v4i *>(ob + r * pn + n) =
-                            v4i{acc[j][4 * q], acc[j][4 * q + 1], acc[j][4 * q + 2], acc[j][4 * q + 3]};
+                    if (32 * (j + 1) <= g.N) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) ob[r * g.N + n + e] = acc[j][4 * q + e];
                     } else {
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
-                            if (n + e < g.N) ob[r * pn + n + e] = acc[j][4 * q + e];
+                            if (n + e < g.N) ob[r * g.N + n + e] = acc[j][4 * q + e];
                     }
                 }
             }
@@ -262,47 +333,49 @@ __global__ __launch_bounds__(NT, 1) void skinny_kernel(Args g) {
         __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the wavefront's LDS writes done
         __builtin_amdgcn_wave_barrier();
         {
-            // piece p = lane + 64 i holds values 4 p .. 4 p + 3 of the run:
-            // in two halves, all of a half's LDS reads first, then its stores
-            const int q4 = g.N >> 2;
-            int32_t *cb = g.c + mb * g.N;
+            // piece p = lane + 64 i holds values 4 p .. 4 p + 3 of the run
+            // (the LDS area holds 1280 pieces, so every read stays inside
+            // it): in two halves, a half's LDS reads first, then its stores;
+            // pieces past the run are neither stored nor counted in the max
+            const uint32_t cb = uint32_t(32 * wave * g.N) * 4u;
+            int32_t mx = 0, mn = 0;
 #pragma unroll
             for (int h = 0; h < NP; h += NP / 2) {
                 v4i r4[NP / 2];
 #pragma unroll
-                for (int i = 0; i < NP / 2; ++i) {
-                    const int p = lane + 64 * (h + i);
-                    if (4 * p < valid) {
-                        if (n4) {
-                            const int row = int(uint32_t(p) / uint32_t(q4)), col = 4 * (p - row * q4);
-                            r4[i] = *reinterpret_cast<const v4i *>(ob + row * pn + col);
-                        } else {
-                            r4[i] = *reinterpret_cast<const v4i *>(ob + 4 * p);
-                        }
-                    }
-                }
+                for (int i = 0; i < NP / 2; ++i)
+                    r4[i] = *reinterpret_cast<const v4i *>(ob + 4 * (lane + 64 * (h + i)));
 #pragma unroll
                 for (int i = 0; i < NP / 2; ++i) {
                     const int e0 = 4 * (lane + 64 * (h + i));
-                    if (e0 >= valid) continue;
-                    v4i r = r4[i];
+                    const bool in = e0 + 4 <= valid;
+                    // a value is kept where its mask byte is positive: all
+                    // ones without a mask, none past the run
+                    uint32_t w = masked ? mk[h + i] : 0x01010101u;
+                    w = in ? w : 0u;
+                    v4i x = r4[i];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (int8_t(uint8_t(mk[h + i] >> (8 * e))) <= 0) r[e] = 0;
-                    if (e0 + 4 <= valid) {
-                        *reinterpret_cast<v4i *>(cb + e0) = r;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) amax = max(amax, abs_u32(r[e]));
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (e0 + e < valid) {
-                                cb[e0 + e] = r[e];
-                                amax = max(amax, abs_u32(r[e]));
-                            }
-                    }
+                    for (int e = 0; e < 4; ++e) x[e] = int8_t(uint8_t(w >> (8 * e))) > 0 ? x[e] : 0;
+                    mx = max(mx, max(max(x[0], x[1]), max(x[2], x[3])));
+                    mn = min(mn, min(min(x[0], x[1]), min(x[2], x[3])));
+                    __builtin_amdgcn_raw_buffer_store_b128(x, cr, int(in ? cb + 4u * uint32_t(e0) : OOB), 0, 0);
                 }
             }
+            // the word the run ends inside: lane e < valid mod 4 stores value
+            // 4 wq + e (one store on every lane, the rest dropped)
+            {
+                const int wq = valid >> 2;
+                const bool ok = lane < (valid & 3);
+                int32_t x = ok ? ob[4 * wq + (lane & 3)] : 0;
+                // (used here, not earlier: waiting for tb, the last load
+                // issued, would wait for every load before it)
+                asm volatile("" : "+v"(tb));
+                if (masked && int8_t(uint8_t(tb)) <= 0) x = 0;
+                mx = max(mx, x);
+                mn = min(mn, x);
+                __builtin_amdgcn_raw_buffer_store_b32(x, cr, int(ok ? cb + 4u * uint32_t(4 * wq + lane) : OOB), 0, 0);
+            }
+            amax = max(amax, max(uint32_t(mx), 0u - uint32_t(mn)));
         }
         __syncthreads();
         buf ^= 1;
@@ -330,8 +403,11 @@ inline void skinny_launch(bool bt, const int8_t *a, const int8_t *w, int32_t *c,
     const int64_t nstages = (int64_t(M) + RS - 1) / RS;
     const int64_t cus = device_cus();
     const unsigned grid = unsigned(nstages < cus ? nstages : cus);
-    if (bt) skinny_kernel<true><<<dim3(grid), dim3(NT), 0, st>>>(g);
-    else skinny_kernel<false><<<dim3(grid), dim3(NT), 0, st>>>(g);
+    const bool n4 = N % 4 == 0;
+    if (bt && n4) skinny_kernel<true, true><<<dim3(grid), dim3(NT), 0, st>>>(g);
+    else if (bt) skinny_kernel<true, false><<<dim3(grid), dim3(NT), 0, st>>>(g);
+    else if (n4) skinny_kernel<false, true><<<dim3(grid), dim3(NT), 0, st>>>(g);
+    else skinny_kernel<false, false><<<dim3(grid), dim3(NT), 0, st>>>(g);
 }
 
 }  // namespace sk

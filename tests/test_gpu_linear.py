@@ -55,7 +55,11 @@ def test_contractions_vs_oracle(B, IN, OUT):
 # path of fwd and dgrad (rows of any byte length, fragments built with
 # v_alignbyte, bytes past K masked), ragged last stages, single columns
 SKINNY = [(65536, 147, 160), (65536, 160, 2), (65536, 2, 160), (4096, 160, 147), (4112, 147, 160),
-          (4096, 1, 1), (8192, 160, 160), (4096, 33, 31), (4128, 64, 96), (6000, 100, 5)]
+          (4096, 1, 1), (8192, 160, 160), (4096, 33, 31), (4128, 64, 96), (6000, 100, 5),
+          # a last block of brows rows whose brows N values end inside a word
+          # (masked dgrad N = 147, fwd N = 7 and N = 2), and ragged rows with N
+          # a multiple of 4 (dgrad N = 160 under the mask, fwd N = 32)
+          (4099, 147, 160), (4101, 32, 7), (4101, 32, 2), (4099, 160, 32)]
 
 
 @pytest.mark.parametrize("B,IN,OUT", SKINNY)
