@@ -224,7 +224,7 @@ int int_linear_wgrad(const int8_t *dY, const int8_t *X, int32_t *G, int64_t B, i
 
 size_t int_linear_wgrad_workspace_bytes(int64_t B, int64_t IN, int64_t OUT) {
     if (!dims_ok(B, IN, OUT) || !wl::wgrad_long_fits(B, OUT, IN, nullptr, nullptr)) return 0;
-    return size_t(wl::wgrad_long_groups(B)) * size_t(OUT * IN) * sizeof(int32_t);
+    return size_t(wl::wgrad_long_groups(B)) * size_t(wl::wgrad_long_part_elems(OUT, IN)) * sizeof(int32_t);
 }
 
 int int_linear_wgrad_ws(const int8_t *dY, const int8_t *X, int32_t *G, int64_t B, int64_t IN, int64_t OUT,
@@ -245,7 +245,11 @@ int int_linear_wgrad_ws(const int8_t *dY, const int8_t *X, int32_t *G, int64_t B
     int32_t *part = static_cast<int32_t *>(workspace);
     const int nw = wl::wgrad_long_launch(dY, X, B, int(OUT), int(IN), G, part, st);
     if (int rc = check_launch("int_linear_wgrad_ws")) return rc;
-    wl::sum_partials(part, nw, OUT * IN, G, absmax_G, st);
+    if (wl::wgrad_long_blocked(OUT, IN, part))
+        wl::sum_partials_blocked(part, nw, int(((OUT + 31) / 32) * ((IN + 31) / 32)), int((IN + 31) / 32), int(OUT),
+                                 int(IN), G, absmax_G, st);
+    else
+        wl::sum_partials(part, nw, OUT * IN, G, absmax_G, st);
     return check_launch("int_linear_wgrad_ws");
 }
 

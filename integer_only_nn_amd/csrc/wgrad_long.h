@@ -30,7 +30,8 @@ struct Args {
     int M, N, mb, nb;     // G is M x N, mb x nb blocks of 32
     int pa, pb;           // LDS pitches (multiples of 16)
     int32_t *G;           // atomics into the zeroed G, or (part != nullptr)
-    int32_t *part;        // the workgroup's partial G at part[w][M][N]
+    int32_t *part;        // the workgroup's partial G: part[w][M][N], or blocked
+    int blk;              // partials blocked: part[w][block][lane][16] (see wgrad_long_blocked)
 };
 
 // One stage of a row-major operand [K][C] with contiguous rows (pitch C):
@@ -150,6 +151,22 @@ __global__ __launch_bounds__(NT) void wgrad_long_kernel(Args g) {
     }
     // lane holds G[m][n .. n + 3] for m = 32 bm + lane % 32 and
     // n = 32 bn + 8 (v / 4) + 4 (lane / 32)
+    if (g.part && g.blk) {
+        // the accumulators as they lie: block q's 16 values of each lane at
+        // part[w][q][lane], 64 contiguous bytes a lane (values outside G
+        // included; the sum pass drops them)
+#pragma unroll
+        for (int i = 0; i < MAXBLK / 4; ++i) {
+            const int q = wave + 4 * i;
+            if (q < nblk) {
+                v4i *dst = reinterpret_cast<v4i *>(g.part + ((int64_t(blockIdx.x) * nblk + q) * 64 + lane) * 16);
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    dst[c] = v4i{acc[i][4 * c], acc[i][4 * c + 1], acc[i][4 * c + 2], acc[i][4 * c + 3]};
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < MAXBLK / 4; ++i) {
         const int q = wave + 4 * i;
@@ -177,9 +194,14 @@ __global__ __launch_bounds__(NT) void wgrad_long_kernel(Args g) {
 // part[w][i .. i + 3] for i = i0 + 4 q and w = z, z + SL, ... (eight loads
 // in flight), and the SL slices meet in LDS.  More slices suit fewer
 // outputs over more partials (sum_partials picks SL).
-template <int SL>
+// BLK: the partial rows are blocked (see wgrad_long_kernel): element j is
+// block j / 1024 (bm, bn of nb blocks a row), lane (j / 16) % 64, value
+// j % 16, i.e. G[32 bm + lane % 32][32 bn + 8 (v / 4) + 4 (lane / 32) + v % 4]
+// when inside the M x N of G, else dropped.
+template <int SL, bool BLK = false>
 __global__ __launch_bounds__(256) void wgrad_long_sum(const int32_t *__restrict__ part, int nw, int64_t n,
-                                                      int32_t *__restrict__ G, uint32_t *__restrict__ absmax) {
+                                                      int32_t *__restrict__ G, uint32_t *__restrict__ absmax,
+                                                      int nb = 0, int M = 0, int N = 0) {
     static_assert(SL == 16 || SL == 64, "16 or 64 slices");
     constexpr int GR = 256 / SL, E = 4 * GR;
     typedef unsigned v4u __attribute__((ext_vector_type(4)));  // sums wrap modulo 2^32
@@ -231,8 +253,19 @@ __global__ __launch_bounds__(256) void wgrad_long_sum(const int32_t *__restrict_
             uint32_t tot = 0;
 #pragma unroll
             for (int zz = 0; zz < SL; ++zz) tot += red[zz][threadIdx.x];
-            G[i0 + threadIdx.x] = int32_t(tot);
-            amax = max(amax, abs_u32(int32_t(tot)));
+            if (BLK) {
+                const int64_t j = i0 + threadIdx.x;
+                const int q = int(j >> 10), ln = int(j >> 4) & 63, v = int(j) & 15;
+                const int bm = q / nb, bn = q - bm * nb;
+                const int m = 32 * bm + (ln & 31), c = 32 * bn + 8 * (v >> 2) + 4 * (ln >> 5) + (v & 3);
+                if (m < M && c < N) {
+                    G[int64_t(m) * N + c] = int32_t(tot);
+                    amax = max(amax, abs_u32(int32_t(tot)));
+                }
+            } else {
+                G[i0 + threadIdx.x] = int32_t(tot);
+                amax = max(amax, abs_u32(int32_t(tot)));
+            }
         }
     }
     if (absmax) {
@@ -257,6 +290,35 @@ inline void sum_partials(const int32_t *part, int nw, int64_t n, int32_t *G, uin
         wgrad_long_sum<64><<<dim3(blocks(16)), dim3(256), 0, st>>>(part, nw, n, G, absmax);
 }
 
+// The same sum over blocked partials (nblk blocks of 1024 a row, nb a row
+// of G's blocks) into the M x N of G.
+inline void sum_partials_blocked(const int32_t *part, int nw, int nblk, int nb, int M, int N, int32_t *G,
+                                 uint32_t *absmax, hipStream_t st) {
+    const int64_t n = int64_t(nblk) * 1024;
+    const int64_t b = (n + 63) / 64;
+    wgrad_long_sum<16, true><<<dim3(unsigned(b > 2048 ? 2048 : b)), dim3(256), 0, st>>>(part, nw, n, G, absmax,
+                                                                                       nb, M, N);
+}
+
+// Whether the partials are kept blocked: the accumulators' own layout
+// (each lane's 16 values of a block in 64 contiguous bytes) instead of rows
+// of G, whose 16-byte pieces do not line up with G's rows for N not a
+// multiple of 4 (one dword store per value: 16 us for 160 x 147 partials,
+// a third of the kernel).  Blocks pad G to multiples of 32, so only when
+// that adds at most a quarter.
+// The blocked partials take 16-byte stores, so also a 16-byte aligned
+// workspace (part == nullptr: the size query, which covers both layouts).
+inline bool wgrad_long_blocked(int64_t M, int64_t N, const void *part = nullptr) {
+    const int64_t nblk = ((M + 31) / 32) * ((N + 31) / 32);
+    return nblk * 1024 * 4 <= 5 * M * N && (part == nullptr || aligned(part, 16));
+}
+
+// int32 elements of one workgroup's partial G (the blocked layout's when
+// the shape takes it, never fewer than the rows' M N).
+inline int64_t wgrad_long_part_elems(int64_t M, int64_t N) {
+    return wgrad_long_blocked(M, N) ? ((M + 31) / 32) * ((N + 31) / 32) * 1024 : M * N;
+}
+
 // Workgroups of a launch over a reduction of length K: at least 256 rows
 // (four stages) each, at most 256.  A stage carries little work, so each
 // workgroup's chain of stage loads sets the time: 128 workgroups of 512
@@ -276,7 +338,8 @@ inline bool wgrad_long_fits(int64_t K, int64_t M, int64_t N, const void *a, cons
 }
 
 // Partial sums go to part when it is not null (it holds wgrad_long_groups(K)
-// x M x N int32; the caller sums them), else into the zeroed G by atomics.
+// x wgrad_long_part_elems(M, N) int32, blocked when wgrad_long_blocked(M, N,
+// part); the caller sums them), else into the zeroed G by atomics.
 // Returns the number of workgroups (of partials).
 inline int wgrad_long_launch(const int8_t *a, const int8_t *b, int64_t K, int M, int N, int32_t *G,
                               int32_t *part, hipStream_t st) {
@@ -292,6 +355,7 @@ inline int wgrad_long_launch(const int8_t *a, const int8_t *b, int64_t K, int M,
     g.pa = 32 * g.mb + 16;
     g.pb = 32 * g.nb + 16;
     g.G = G;
+    g.blk = part != nullptr && wgrad_long_blocked(M, N, part);
     int64_t wgs = wgrad_long_groups(K);
     g.rows = ((K + wgs - 1) / wgs + R - 1) / R * R;
     wgs = (K + g.rows - 1) / g.rows;  // at most wgrad_long_groups(K)

@@ -118,6 +118,23 @@ def test_wgrad_long_batch_workspace(B, IN, OUT):
         assert u32(am) == oracle.absmax(want)
 
 
+def test_wgrad_long_batch_workspace_4byte_aligned():
+    # a workspace 4 bytes past a 16-byte boundary: the partials go in rows of
+    # G instead of the 32 x 32 blocks (whose 16-byte stores need alignment)
+    B, IN, OUT = 65536, 147, 160
+    say("wgrad long ws misaligned", B, IN, OUT)
+    need = ops.int_linear_wgrad_workspace_bytes(B, IN, OUT)
+    ws = torch.empty(need + 16, dtype=torch.uint8, device=dev())[4:]
+    d = ionn_synth.single_linear(B=B, IN=IN, OUT=OUT, seed=11)
+    X, dY = d["X"], d["dY"]
+    G = torch.full((OUT, IN), 99, dtype=torch.int32, device=dev())
+    am = torch.zeros(1, dtype=torch.int32, device=dev())
+    ops.int_linear_wgrad_ws(to_dev(dY), to_dev(X), G, ws, absmax_G=am)
+    want = fast.linear_wgrad(dY, X)
+    np.testing.assert_array_equal(host(G), want)
+    assert u32(am) == oracle.absmax(want)
+
+
 def test_wgrad_long_batch_extremes():
     # every product 16384 or -16256: the largest sums the long path meets
     B, IN, OUT = 8192, 40, 24

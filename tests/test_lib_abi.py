@@ -50,9 +50,11 @@ def test_linear_validation():
 
 def test_linear_wgrad_workspace_query_and_checks():
     # a small G over a long batch takes the partial-sums path: groups of at
-    # least 256 rows, at most 256, times the G size
+    # least 256 rows, at most 256, times the G size, or times its 32 x 32
+    # blocks (1024 values each) when they pad G by at most a quarter
     need = lib.int_linear_wgrad_workspace_bytes(65536, 147, 160)
-    assert need == 256 * 147 * 160 * 4
+    assert need == 256 * 25 * 1024 * 4
+    assert lib.int_linear_wgrad_workspace_bytes(65536, 160, 2) == 256 * 160 * 2 * 4
     assert lib.int_linear_wgrad_workspace_bytes(5000, 33, 7) == 20 * 33 * 7 * 4
     assert lib.int_linear_wgrad_workspace_bytes(200000, 33, 7) == 256 * 33 * 7 * 4
     # short batches, large G, bad sizes: no workspace (the call is int_linear_wgrad)
