@@ -245,6 +245,11 @@ __global__ __launch_bounds__(NT, 1) void gemm256_kernel(const int8_t *__restrict
     __shared__ __attribute__((aligned(1024))) int8_t sB0[TILE_BYTES];
     __shared__ __attribute__((aligned(1024))) int8_t sA1[TILE_BYTES];
     __shared__ __attribute__((aligned(1024))) int8_t sB1[TILE_BYTES];
+    // static OSS: the tile's 256 columns of offset, multiplier and k (as
+    // int32 each), loaded with the first step, so that the epilogue reads
+    // them from LDS (a global load there, issued after earlier stores,
+    // would wait for those stores as well: the counter retires in order)
+    __shared__ __attribute__((aligned(16))) int32_t sP[OSS ? 3 * BN : 1];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -287,7 +292,18 @@ __global__ __launch_bounds__(NT, 1) void gemm256_kernel(const int8_t *__restrict
     // pending into the loop (it would force a full LDS wait at its head).
     ta.issue(0, sA0, wave);
     tb.issue(0, sB0, wave);
+    int32_t po = 0, pm = 0, pk = 0;
+    if (OSS) {
+        po = ep.oss_off[n0 + tid];
+        pm = ep.oss_mult[n0 + tid];
+        pk = int(uint8_t(ep.oss_k[n0 + tid]));  // k as the byte it is (0..255)
+    }
     __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+    if (OSS) {
+        sP[tid] = po;
+        sP[BN + tid] = pm;
+        sP[2 * BN + tid] = pk;
+    }
     __builtin_amdgcn_s_barrier();
     dma2(0, BK, sA1, sB1);
     dma2(2, BK, sA1, sB1);
@@ -369,38 +385,53 @@ __global__ __launch_bounds__(NT, 1) void gemm256_kernel(const int8_t *__restrict
     const int em = lane & 31, en = (lane >> 5) * 4;
     if (OSS) {
         // static OSS: int8 out, four columns per dword; per-column parameters
-        // come from L1 (the same 16 column groups for every row block)
+        // from LDS (the same 16 column groups for every row block)
+        const int cl = wn * 128 + en;  // the lane's first column within the tile
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int64_t m = m0 + wm * 128 + i * 32 + em;
-            const int64_t nb = n0 + wn * 128 + en;
+            const int64_t nb = n0 + cl;
             int8_t *orow = ep.out8 + m * ep.ldc + nb;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const int dn = j * 32 + 8 * q;
-                    const v4i o = *reinterpret_cast<const v4i *>(ep.oss_off + nb + dn);
-                    const v4i mu = *reinterpret_cast<const v4i *>(ep.oss_mult + nb + dn);
-                    const uint32_t kk = *reinterpret_cast<const uint32_t *>(ep.oss_k + nb + dn);
+                    const v4i o = *reinterpret_cast<const v4i *>(sP + cl + dn);
+                    const v4i mu = *reinterpret_cast<const v4i *>(sP + BN + cl + dn);
+                    const v4i kk = *reinterpret_cast<const v4i *>(sP + 2 * BN + cl + dn);
                     const int lo = ep.oss_lo;
                     *reinterpret_cast<uint32_t *>(orow + dn) =
-                        pack4_u8(oss_elem(acc[i][j][4 * q], o.x, mu.x, int(kk & 0xffu), lo),
-                                 oss_elem(acc[i][j][4 * q + 1], o.y, mu.y, int((kk >> 8) & 0xffu), lo),
-                                 oss_elem(acc[i][j][4 * q + 2], o.z, mu.z, int((kk >> 16) & 0xffu), lo),
-                                 oss_elem(acc[i][j][4 * q + 3], o.w, mu.w, int(kk >> 24), lo));
+                        pack4_u8(oss_elem(acc[i][j][4 * q], o.x, mu.x, kk.x, lo),
+                                 oss_elem(acc[i][j][4 * q + 1], o.y, mu.y, kk.y, lo),
+                                 oss_elem(acc[i][j][4 * q + 2], o.z, mu.z, kk.z, lo),
+                                 oss_elem(acc[i][j][4 * q + 3], o.w, mu.w, kk.w, lo));
                 }
             }
         }
         return;
     }
     int32_t vmax = INT32_MIN, vmin = INT32_MAX;
+    // ReLU mask: every word of the lane loaded before the first store, so
+    // that waiting for a word never waits for a store (the counter retires
+    // in order)
+    uint32_t mk[RELU ? 4 : 1][RELU ? 16 : 1];
+    if (RELU) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int8_t *arow = ep.act + (m0 + wm * 128 + i * 32 + em) * ep.ldc + n0 + wn * 128 + en;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    mk[RELU ? i : 0][RELU ? 4 * j + q : 0] = *reinterpret_cast<const uint32_t *>(arow + j * 32 + 8 * q);
+        }
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int64_t m = m0 + wm * 128 + i * 32 + em;
         const int64_t nb = n0 + wn * 128 + en;
         int32_t *row = ep.C + m * ep.ldc + nb;
-        const int8_t *arow = RELU ? ep.act + m * ep.ldc + nb : nullptr;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
 #pragma unroll
@@ -408,7 +439,7 @@ __global__ __launch_bounds__(NT, 1) void gemm256_kernel(const int8_t *__restrict
                 const int dn = j * 32 + 8 * q;
                 v4i v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
                 if (RELU) {
-                    const uint32_t a = *reinterpret_cast<const uint32_t *>(arow + dn);
+                    const uint32_t a = mk[RELU ? i : 0][RELU ? 4 * j + q : 0];
 #pragma unroll
                     for (int c = 0; c < 4; ++c)
                         if (int8_t(uint8_t(a >> (8 * c))) <= 0) v[c] = 0;
