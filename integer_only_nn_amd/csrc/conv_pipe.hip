@@ -405,6 +405,11 @@ __global__ __launch_bounds__(NTP, 1) void conv_pipe_kernel(const int8_t *__restr
 #pragma unroll
             for (int j = 0; j < 4; ++j) halo_load(g1, i, j);
     }
+    // Every prologue load waited for here, once: otherwise registers they
+    // fill and the loop reuses carry a pending load into the loop head, and
+    // the compiler's wait for it (vmcnt(0), the counter retiring in order)
+    // would run in every tile and drain the previous tile's stores.
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
     Prev pv = none;
     bool last_in_1 = false;  // which set holds the last tile's sums
     while (t < ntiles) {

@@ -24,12 +24,14 @@ __global__ __launch_bounds__(256) void mse_grad_kernel(const int8_t *__restrict_
                                                        const int8_t *__restrict__ tmc,
                                                        const int8_t *__restrict__ tmw, int32_t *__restrict__ g,
                                                        uint32_t *__restrict__ absmax) {
+    // B C < 2^31: 32-bit indices; both targets of the column are loaded with
+    // the label and the output, so no load waits for another
     uint32_t m = 0;
-    for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < B * C;
-         i += int64_t(gridDim.x) * blockDim.x) {
-        const int64_t b = i / C, c = i - b * C;
-        const int32_t t = c == int64_t(labels[b]) ? int32_t(tmc[c]) : int32_t(tmw[c]);
-        const int32_t v = int32_t(out[i]) - t;
+    const uint32_t n = uint32_t(B * C), Cu = uint32_t(C);
+    for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) {
+        const uint32_t b = i / Cu, c = i - b * Cu;
+        const int32_t lab = labels[b], o = out[i], tc = tmc[c], tw = tmw[c];
+        const int32_t v = o - (int32_t(c) == lab ? tc : tw);
         g[i] = v;
         m = max(m, abs_u32(v));
     }
