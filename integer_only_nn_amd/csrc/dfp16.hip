@@ -487,6 +487,10 @@ __global__ __launch_bounds__(NT, 1) void dfp_kernel(Args g) {
     };
     la.load(g.a, g.lda, m0, 64 * c0, tid);
     lb.load(g.b, g.ldb, n0, 64 * c0, tid);
+    // the output exponent of the one-range form, read once here: read at
+    // each store, the compiler reloads it after every earlier store (which
+    // might alias it) and waits for that store with it
+    const int e_out = !BLK && g.split == 1 ? *g.ea + g.shift + *g.eb : 0;
     if (BLK) {
         eload(m0, n0, c0);
         if (tid < 256) bexp[0][tid] = ereg;
@@ -593,9 +597,8 @@ __global__ __launch_bounds__(NT, 1) void dfp_kernel(Args g) {
                     int32_t *cp = g.acc + (int64_t(u / ntiles) * g.M + m) * g.N + n;
                     v4i v = {acc[j][4 * q], acc[j][4 * q + 1], acc[j][4 * q + 2], acc[j][4 * q + 3]};
                     if (!BLK && g.split == 1) {
-                        const int e = *g.ea + g.shift + *g.eb;
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) v[i] = __float_as_int(scale_f32(__int_as_float(v[i]), e));
+                        for (int i = 0; i < 4; ++i) v[i] = __float_as_int(scale_f32(__int_as_float(v[i]), e_out));
                     }
                     *reinterpret_cast<v4i *>(cp) = v;
                 }
