@@ -88,30 +88,48 @@ __global__ __launch_bounds__(256) void update_kernel(const int32_t *__restrict__
     if (tid < n_clear) clear[tid] = 0u;
     int64_t done = 0;
     if (VEC) {
+        // Two chunks a wavefront and step, both loaded before the first one's
+        // stores: the vector-memory counter retires in order and counts
+        // stores, so loads issued after a chunk's stores would wait for them;
+        // this way the first chunk's writes overlap the second one's reads.
+        // Past the last chunk the second one re-reads the first and writes the
+        // same bytes again: no branch, so the compiler neither sinks the
+        // second chunk's loads into one nor loses its count of the loads and
+        // stores in flight.
         const int lane = threadIdx.x & 63;
         const int64_t wave = tid >> 6, nwaves = nthreads >> 6;
         const int64_t nfull = n / kChunk * kChunk;
-        for (int64_t base = wave * kChunk; base < nfull; base += nwaves * kChunk) {
-            v4i g[kInstr];
-            uint32_t w[kInstr];
+        for (int64_t base = wave * 2 * kChunk; base < nfull; base += nwaves * 2 * kChunk) {
+            const bool two = base + kChunk < nfull;
+            const int64_t base2 = two ? base + kChunk : base;
+            v4i g[2][kInstr];
+            uint32_t w[2][kInstr];
 #pragma unroll
-            for (int c = 0; c < kInstr; ++c) {
-                const int64_t e = base + c * 256 + 4 * lane;
-                g[c] = __builtin_nontemporal_load(reinterpret_cast<const v4i *>(G + e));
-                w[c] = *reinterpret_cast<const uint32_t *>(W + e);
-            }
+            for (int h = 0; h < 2; ++h)
 #pragma unroll
-            for (int c = 0; c < kInstr; ++c) {
-                const int64_t e = base + c * 256 + 4 * lane;
-                v4i gq;
-                gq.x = rhu(g[c].x, s);
-                gq.y = rhu(g[c].y, s);
-                gq.z = rhu(g[c].z, s);
-                gq.w = rhu(g[c].w, s);
-                if (GQ) *reinterpret_cast<v4i *>(gq_out + e) = gq;
-                *reinterpret_cast<uint32_t *>(W + e) =
-                    pack4_i8(sat8(byte_i8(w[c], 0) - rhu(gq.x, ws)), sat8(byte_i8(w[c], 1) - rhu(gq.y, ws)),
-                             sat8(byte_i8(w[c], 2) - rhu(gq.z, ws)), sat8(byte_i8(w[c], 3) - rhu(gq.w, ws)));
+                for (int c = 0; c < kInstr; ++c) {
+                    const int64_t e = (h ? base2 : base) + c * 256 + 4 * lane;
+                    g[h][c] = __builtin_nontemporal_load(reinterpret_cast<const v4i *>(G + e));
+                    w[h][c] = *reinterpret_cast<const uint32_t *>(W + e);
+                }
+            // (kept ahead of every store: the scheduler would otherwise sink
+            // the second chunk's loads below the first chunk's stores)
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+#pragma unroll
+                for (int c = 0; c < kInstr; ++c) {
+                    const int64_t e = (h ? base2 : base) + c * 256 + 4 * lane;
+                    v4i gq;
+                    gq.x = rhu(g[h][c].x, s);
+                    gq.y = rhu(g[h][c].y, s);
+                    gq.z = rhu(g[h][c].z, s);
+                    gq.w = rhu(g[h][c].w, s);
+                    if (GQ) *reinterpret_cast<v4i *>(gq_out + e) = gq;
+                    *reinterpret_cast<uint32_t *>(W + e) =
+                        pack4_i8(sat8(byte_i8(w[h][c], 0) - rhu(gq.x, ws)), sat8(byte_i8(w[h][c], 1) - rhu(gq.y, ws)),
+                                 sat8(byte_i8(w[h][c], 2) - rhu(gq.z, ws)), sat8(byte_i8(w[h][c], 3) - rhu(gq.w, ws)));
+                }
             }
         }
         done = nfull;
@@ -147,6 +165,14 @@ __global__ __launch_bounds__(256) void output_error_kernel(const int8_t *__restr
 // One kChunk per wavefront (4 per block) up to 2048 blocks, looping beyond.
 static unsigned stream_blocks(int64_t n) {
     int64_t b = (n + 4 * kChunk - 1) / (4 * kChunk);
+    if (b < 1) b = 1;
+    if (b > 2048) b = 2048;
+    return unsigned(b);
+}
+
+// The update's grid: two chunks per wavefront and step.
+static unsigned update_blocks(int64_t n) {
+    int64_t b = (n + 8 * kChunk - 1) / (8 * kChunk);
     if (b < 1) b = 1;
     if (b > 2048) b = 2048;
     return unsigned(b);
@@ -196,7 +222,7 @@ int niti_quantize_update(const int32_t *G, int64_t n, const uint32_t *absmax, in
                      aligned(gq_out, 4),
                  IONN_ERR_ALIGN, "niti_quantize_update: int32 pointers must be 4-byte aligned");
     const bool vec = aligned(G, 16) && aligned(W, 4) && aligned(gq_out, 16);
-    dim3 grid(stream_blocks(n)), block(256);
+    dim3 grid(update_blocks(n)), block(256);
     hipStream_t st = as_stream(stream);
     if (vec && gq_out) update_kernel<true, true><<<grid, block, 0, st>>>(G, n, absmax, target_bits, mu_weight, W, shifts_out, gq_out);
     else if (vec) update_kernel<true, false><<<grid, block, 0, st>>>(G, n, absmax, target_bits, mu_weight, W, shifts_out, gq_out);
@@ -227,7 +253,7 @@ int niti_quantize_update_clear(const int32_t *G, int64_t n, const uint32_t *absm
                      aligned(clear, 4),
                  IONN_ERR_ALIGN, "niti_quantize_update_clear: int32 pointers must be 4-byte aligned");
     const bool vec = aligned(G, 16) && aligned(W, 4) && aligned(gq_out, 16);
-    dim3 grid(stream_blocks(n)), block(256);
+    dim3 grid(update_blocks(n)), block(256);
     hipStream_t st = as_stream(stream);
     const int nc = int(n_clear);
     if (vec && gq_out) update_kernel<true, true><<<grid, block, 0, st>>>(G, n, absmax, target_bits, mu_weight, W, shifts_out, gq_out, clear, nc);
