@@ -50,15 +50,24 @@ __global__ __launch_bounds__(256) void quantize_kernel(const int32_t *__restrict
         const int lane = threadIdx.x & 63;
         const int64_t wave = tid >> 6, nwaves = nthreads >> 6;
         const int64_t nfull = n / kChunk * kChunk;
-        for (int64_t base = wave * kChunk; base < nfull; base += nwaves * kChunk) {
-            v4i a[kInstr];
+        // two chunks a wavefront and step, loaded before either is stored
+        // (as in update_kernel below)
+        for (int64_t base = wave * 2 * kChunk; base < nfull; base += nwaves * 2 * kChunk) {
+            const int64_t base2 = base + kChunk < nfull ? base + kChunk : base;
+            v4i a[2][kInstr];
 #pragma unroll
-            for (int c = 0; c < kInstr; ++c)
-                a[c] = __builtin_nontemporal_load(reinterpret_cast<const v4i *>(acc + base + c * 256 + 4 * lane));
+            for (int h = 0; h < 2; ++h)
 #pragma unroll
-            for (int c = 0; c < kInstr; ++c)
-                *reinterpret_cast<uint32_t *>(out + base + c * 256 + 4 * lane) =
-                    pack4_i8(q(a[c].x), q(a[c].y), q(a[c].z), q(a[c].w));
+                for (int c = 0; c < kInstr; ++c)
+                    a[h][c] = __builtin_nontemporal_load(
+                        reinterpret_cast<const v4i *>(acc + (h ? base2 : base) + c * 256 + 4 * lane));
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int c = 0; c < kInstr; ++c)
+                    *reinterpret_cast<uint32_t *>(out + (h ? base2 : base) + c * 256 + 4 * lane) =
+                        pack4_i8(q(a[h][c].x), q(a[h][c].y), q(a[h][c].z), q(a[h][c].w));
         }
         done = nfull;
     }
@@ -162,15 +171,8 @@ __global__ __launch_bounds__(256) void output_error_kernel(const int8_t *__restr
     }
 }
 
-// One kChunk per wavefront (4 per block) up to 2048 blocks, looping beyond.
-static unsigned stream_blocks(int64_t n) {
-    int64_t b = (n + 4 * kChunk - 1) / (4 * kChunk);
-    if (b < 1) b = 1;
-    if (b > 2048) b = 2048;
-    return unsigned(b);
-}
 
-// The update's grid: two chunks per wavefront and step.
+// The quantiser's and the update's grid: two chunks per wavefront and step.
 static unsigned update_blocks(int64_t n) {
     int64_t b = (n + 8 * kChunk - 1) / (8 * kChunk);
     if (b < 1) b = 1;
@@ -197,7 +199,7 @@ int niti_quantize(const int32_t *acc, int64_t n, const uint32_t *absmax, int tar
     IONN_REQUIRE(aligned(acc, 4) && aligned(absmax, 4) && aligned(shift_out, 4), IONN_ERR_ALIGN,
                  "niti_quantize: int32 pointers must be 4-byte aligned");
     const bool vec = aligned(acc, 16) && aligned(out, 4);
-    dim3 grid(stream_blocks(n)), block(256);
+    dim3 grid(update_blocks(n)), block(256);
     hipStream_t st = as_stream(stream);
     if (vec && relu) quantize_kernel<true, true><<<grid, block, 0, st>>>(acc, n, absmax, target_bits, out, shift_out);
     else if (vec) quantize_kernel<true, false><<<grid, block, 0, st>>>(acc, n, absmax, target_bits, out, shift_out);

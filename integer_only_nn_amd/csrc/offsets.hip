@@ -30,10 +30,13 @@ constexpr size_t kBgScratchBytes = size_t(2) << 20;
 constexpr size_t kBgScratchInts = kBgScratchBytes / sizeof(int32_t);
 constexpr int64_t kChunk = 256 * kInstr;   // int32 elements per wavefront and iteration
 
+// One kChunk per wavefront (4 per block), up to 16384 blocks: a wavefront
+// that looped would issue its next chunk's loads after its stores and wait
+// for them (the counter retires in order).
 unsigned stream_blocks(int64_t n) {
     int64_t b = (n + 4 * kChunk - 1) / (4 * kChunk);
     if (b < 1) b = 1;
-    if (b > 2048) b = 2048;
+    if (b > 16384) b = 16384;
     return unsigned(b);
 }
 
@@ -60,19 +63,27 @@ __global__ __launch_bounds__(256) void oss_kernel(const int32_t *__restrict__ ac
 #pragma unroll
             for (int c = 0; c < kInstr; ++c)
                 a[c] = __builtin_nontemporal_load(reinterpret_cast<const v4i *>(acc + base + c * 256 + 4 * lane));
+            // every piece's parameters loaded before the first store (the
+            // vector-memory counter retires in order and counts stores, so a
+            // load issued after a store would wait for it as well)
             const uint32_t ch0 = uint32_t((base + 4 * lane) % C);
+            v4i o[kInstr], m[kInstr];
+            uint32_t kk[kInstr];
 #pragma unroll
             for (int c = 0; c < kInstr; ++c) {
                 const uint32_t ch = (ch0 + uint32_t(c * 256)) % Cu;
-                const v4i o = *reinterpret_cast<const v4i *>(offset + ch);
-                const v4i m = *reinterpret_cast<const v4i *>(mult + ch);
-                const uint32_t kk = *reinterpret_cast<const uint32_t *>(k + ch);
-                *reinterpret_cast<uint32_t *>(out + base + c * 256 + 4 * lane) =
-                    pack4_u8(oss_elem(a[c].x, o.x, m.x, int(kk & 0xffu), lo),
-                          oss_elem(a[c].y, o.y, m.y, int((kk >> 8) & 0xffu), lo),
-                          oss_elem(a[c].z, o.z, m.z, int((kk >> 16) & 0xffu), lo),
-                          oss_elem(a[c].w, o.w, m.w, int(kk >> 24), lo));
+                o[c] = *reinterpret_cast<const v4i *>(offset + ch);
+                m[c] = *reinterpret_cast<const v4i *>(mult + ch);
+                kk[c] = *reinterpret_cast<const uint32_t *>(k + ch);
             }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int c = 0; c < kInstr; ++c)
+                *reinterpret_cast<uint32_t *>(out + base + c * 256 + 4 * lane) =
+                    pack4_u8(oss_elem(a[c].x, o[c].x, m[c].x, int(kk[c] & 0xffu), lo),
+                             oss_elem(a[c].y, o[c].y, m[c].y, int((kk[c] >> 8) & 0xffu), lo),
+                             oss_elem(a[c].z, o[c].z, m[c].z, int((kk[c] >> 16) & 0xffu), lo),
+                             oss_elem(a[c].w, o[c].w, m[c].w, int(kk[c] >> 24), lo));
         }
         done = nfull;
     }
