@@ -30,6 +30,11 @@ void launch_linear(const SA &sa, const SB &sb, const Epi &ep, int M, int N, int 
         launch<256, 256, 64, 2, 2, false>(sa, sb, ep, M, N, K, 1, st);
     else if (M >= 1024 && N >= 1024)
         launch<256, 256, 64, 2, 2, true>(sa, sb, ep, M, N, K, 1, st);
+    else if (K >= 128)
+        // few, small tiles: each K step is a load round trip the workgroup
+        // waits for, so 256-deep steps (a 784-long reduction in 4 of them
+        // instead of 13)
+        launch<64, 64, 256, 2, 2, true>(sa, sb, ep, M, N, K, 1, st);
     else
         launch<64, 64, 64, 2, 2, true>(sa, sb, ep, M, N, K, 1, st);
 }
