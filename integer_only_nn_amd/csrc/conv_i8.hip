@@ -423,6 +423,11 @@ __device__ __forceinline__ bool rows_geo(const SmallGeo &g) { return g.P == 0 &&
 // Y (int32, [n][ho][co]) for groups of g.spb staged samples: one (sample,
 // output row) per thread, its L / 4 window words read as two aligned LDS
 // dwords and v_alignbyte, one v_dot4 per word and channel.
+// CO = Cout (1 .. kRowsMaxCout) as a template parameter: the per-channel
+// loop is then straight-line, so each window word's CO weight reads are in
+// flight together (with a run-time channel test around each, every v_dot4
+// waited for its own LDS read).
+template <int CO>
 __global__ __launch_bounds__(256) void conv_rows_fwd(const int8_t *__restrict__ X, const int8_t *__restrict__ Wt,
                                                      int32_t *__restrict__ Y, int64_t N, SmallGeo g,
                                                      uint32_t *__restrict__ absmax) {
@@ -430,7 +435,8 @@ __global__ __launch_bounds__(256) void conv_rows_fwd(const int8_t *__restrict__ 
     int8_t *ws = lds, *xs = lds + round16(g.w_b);
     copy_to_lds(ws, Wt, g.w_b);
     const uint32_t *w32 = reinterpret_cast<const uint32_t *>(ws);
-    const int RB = g.W * g.Cin, LW = g.KH * RB / 4, Cout = g.Cout;
+    const int RB = g.W * g.Cin, LW = g.KH * RB / 4;
+    constexpr int Cout = CO;
     const int dsm = 256 / g.Ho, dho = 256 - dsm * g.Ho;  // (sample, row) step per 256 pairs
     uint32_t amax = 0;
     for (int64_t n0 = int64_t(blockIdx.x) * g.spb; n0 < N; n0 += int64_t(gridDim.x) * g.spb) {
@@ -443,25 +449,25 @@ __global__ __launch_bounds__(256) void conv_rows_fwd(const int8_t *__restrict__ 
             const int start = x0 + sm * g.in_b + ho * RB;
             const uint32_t *d = reinterpret_cast<const uint32_t *>(xs + (start & ~3));
             const uint32_t sh = uint32_t(start & 3);
-            int32_t acc[kRowsMaxCout];
+            int32_t acc[CO];
 #pragma unroll
-            for (int co = 0; co < kRowsMaxCout; ++co) acc[co] = 0;
+            for (int co = 0; co < CO; ++co) acc[co] = 0;
             uint32_t lo = d[0];
+#pragma unroll 4
             for (int i = 0; i < LW; ++i) {
                 const uint32_t hi = d[i + 1];
                 const int w = int(__builtin_amdgcn_alignbyte(hi, lo, sh));  // window bytes 4i .. 4i + 3
                 lo = hi;
 #pragma unroll
-                for (int co = 0; co < kRowsMaxCout; ++co)
-                    if (co < Cout) acc[co] = __builtin_amdgcn_sdot4(w, int(w32[co * LW + i]), acc[co], false);
+                for (int co = 0; co < CO; ++co)
+                    acc[co] = __builtin_amdgcn_sdot4(w, int(w32[co * LW + i]), acc[co], false);
             }
             int32_t *yp = Y + ((n0 + sm) * g.Ho + ho) * Cout;
 #pragma unroll
-            for (int co = 0; co < kRowsMaxCout; ++co)
-                if (co < Cout) {
-                    yp[co] = acc[co];
-                    amax = max(amax, abs_u32(acc[co]));
-                }
+            for (int co = 0; co < CO; ++co) {
+                yp[co] = acc[co];
+                amax = max(amax, abs_u32(acc[co]));
+            }
             sm += dsm;
             ho += dho;
             if (ho >= g.Ho) {
@@ -690,8 +696,18 @@ int int_conv_fwd(const int8_t *X, const int8_t *Wt, int32_t *Y, const ionn_conv_
             // the window reads run up to 3 bytes past the staged samples
             SmallGeo rg = sg;
             while (rg.spb > 1 && ((rg.w_b + 15) & ~15) + int64_t(rg.spb) * rg.in_b + 16 > kSmallLds) --rg.spb;
-            conv_rows_fwd<<<dim3(small_blocks(desc->N, rg.spb, 2048)), dim3(256), 0, as_stream(stream)>>>(
-                X, Wt, Y, desc->N, rg, absmax_Y);
+            const dim3 grid(small_blocks(desc->N, rg.spb, 2048)), block(256);
+            hipStream_t st = as_stream(stream);
+            switch (rg.Cout) {
+            case 1: conv_rows_fwd<1><<<grid, block, 0, st>>>(X, Wt, Y, desc->N, rg, absmax_Y); break;
+            case 2: conv_rows_fwd<2><<<grid, block, 0, st>>>(X, Wt, Y, desc->N, rg, absmax_Y); break;
+            case 3: conv_rows_fwd<3><<<grid, block, 0, st>>>(X, Wt, Y, desc->N, rg, absmax_Y); break;
+            case 4: conv_rows_fwd<4><<<grid, block, 0, st>>>(X, Wt, Y, desc->N, rg, absmax_Y); break;
+            case 5: conv_rows_fwd<5><<<grid, block, 0, st>>>(X, Wt, Y, desc->N, rg, absmax_Y); break;
+            case 6: conv_rows_fwd<6><<<grid, block, 0, st>>>(X, Wt, Y, desc->N, rg, absmax_Y); break;
+            case 7: conv_rows_fwd<7><<<grid, block, 0, st>>>(X, Wt, Y, desc->N, rg, absmax_Y); break;
+            default: conv_rows_fwd<8><<<grid, block, 0, st>>>(X, Wt, Y, desc->N, rg, absmax_Y); break;
+            }
             return check_launch("int_conv_fwd");
         }
         if (sg.spb > 0 && Cin > 0) {
