@@ -29,7 +29,11 @@ def _run(d, M, K, N):
 @pytest.mark.parametrize("M,K,N", [(1, 1, 1), (3, 64, 5), (17, 40, 9), (128, 128, 128), (200, 256, 136),
                                    (128, 64, 128), (640, 128, 384), (1024, 384, 128),
                                    (256, 320, 1024), (1000, 64, 48), (4096, 256, 256),
-                                   (2304, 128, 2048)])
+                                   (2304, 128, 2048),
+                                   # more output tiles than compute units, a last round
+                                   # that leaves most workgroups idle: fwd (456 tiles of
+                                   # 3 chunks), dgrad (456 tiles of 3 chunks, 272 of 2)
+                                   (3072, 192, 2432), (3072, 2432, 192), (2176, 2048, 128)])
 def test_dfp16_step_vs_oracle(M, K, N):
     say("dfp16", M, K, N)
     d = ionn_synth.dfp16_gemm(M=M, K=K, N=N, seed=M + K)
@@ -74,7 +78,7 @@ def test_dfp16_extreme_mantissas(M, K, N):
     np.testing.assert_array_equal(host(buf.G), want["G"])
 
 
-@pytest.mark.parametrize("M,K,N", [(256, 256, 128), (512, 128, 256)])
+@pytest.mark.parametrize("M,K,N", [(256, 256, 128), (512, 128, 256), (4352, 128, 1024)])
 def test_dfp16_blocks_far_below_the_tensor_shift(M, K, N):
     """Row blocks of X and dY at scales from zero to full range.  Without K
     splits the contractions store every 32-row block at its own shift, and
