@@ -540,9 +540,10 @@ def bench_small(torch, nsteps):
 
 def _timed(torch, step, nsteps):
     """Step time over nsteps (one event pair) and per-launch averages from a
-    second, event-bracketed run."""
-    for _ in range(5):
-        step(None)
+    second, event-bracketed run, after the clocks have settled on this
+    workload as for the headline (at least 0.3 s of untimed steps and two
+    consecutive nsteps windows within 1%)."""
+    settle(torch, lambda: step(None), nsteps, 0.3)
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
