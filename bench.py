@@ -927,14 +927,24 @@ def measured_traffic():
 
 
 def _cpu_model():
+    """The host CPU's model name, with its family, model and stepping
+    numbers (a virtual machine may report only a generic name)."""
+    info = {}
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+                if ":" in line:
+                    k, v = (x.strip() for x in line.split(":", 1))
+                    info.setdefault(k, v)
+                elif info:
+                    break
     except OSError:
-        pass
-    return None
+        return None
+    name = info.get("model name")
+    if name is None:
+        return None
+    ids = [f"{k} {info[k]}" for k in ("cpu family", "model", "stepping") if k in info]
+    return f"{name} ({', '.join(ids)})" if ids else name
 
 
 def cpu_baseline(rows, threads=None):
