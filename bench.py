@@ -479,6 +479,18 @@ def bench_small(torch, nsteps):
         "us_per_step": round(ems * 1e3, 2), "graph_us_per_step": round(gms * 1e3, 2),
         "GOPS": round(ops1 / (ems * 1e-3) / 1e9, 3), "graph_GOPS": round(ops1 / (gms * 1e-3) / 1e9, 3),
         "launches_per_step": 6, "note": "W evolves from step to step; the kernels' work does not depend on it"}
+    # the same step in one launch (one workgroup, operands in LDS)
+    bufs = st.LinearStepBuffers.make(16, 64, 32, dev)
+
+    def one_small(stream=None):
+        st.linear_step_small(X, W, dY, bufs, stream=stream)
+
+    fms = eager_ms(one_small, nsteps)
+    fgms = graph_ms(one_small, 10)
+    out["single_linear_16x64x32"]["one_launch"] = {
+        "entry_point": "int_linear_step_small", "us_per_step": round(fms * 1e3, 2),
+        "graph_us_per_step": round(fgms * 1e3, 2), "GOPS": round(ops1 / (fms * 1e-3) / 1e9, 3),
+        "graph_GOPS": round(ops1 / (fgms * 1e-3) / 1e9, 3), "launches_per_step": 1}
 
     m = ionn_synth.mlp()
     Ws0 = [to(w) for w in m["Ws"]]

@@ -153,6 +153,35 @@ int niti_quantize_update(const int32_t *G, int64_t n, const uint32_t *absmax,
                          int target_bits, int mu_weight, int8_t *W,
                          int32_t *shifts_out, int32_t *gq_out, void *stream);
 
+/* One whole NITI step of a small Linear layer in one launch, for layers of
+ * microcontroller size ([TI] section 3 "The NITI Algorithm", steps 1-5, and
+ * the weight index of the TiGrIS "Compilation Pipeline" page), in this order:
+ *   Y[b][o]  = sum_i X[b][i] * W[o][i]                  (int32)
+ *   dX[b][i] = sum_o dY[b][o] * W[o][i]                 (int32, W before the update)
+ *   delta    = sat8(rhu(dX, s_d)), s_d = max(0, bitlen(max |dX|) - tb_d)
+ *   G[o][i]  = sum_b dY[b][o] * X[b][i]                 (int32)
+ *   s = max(0, bitlen(max |G|) - tb_w), ws = max(0, s - mu_weight),
+ *   Gq = rhu(G, s), W[o][i] = sat8(W[o][i] - rhu(Gq, ws)) (in place).
+ * The same results as int_linear_fwd, int_linear_dgrad, niti_quantize,
+ * int_linear_wgrad and niti_quantize_update in sequence, from one
+ * workgroup.  Device buffers: X int8 [B][IN]; W int8 [OUT][IN] (read, then
+ * rewritten); dY int8 [B][OUT]; Y int32 [B][OUT], dX int32 [B][IN], delta
+ * int8 [B][IN], G int32 [OUT][IN], gq (nullable) int32 [OUT][IN], all
+ * written; maxima uint32[3] receives max |Y|, max |dX|, max |G| (written,
+ * not max-combined: nothing needs clearing first); shifts int32[3] receives
+ * s_d, s, ws.  Requires int_linear_step_small_fits(B, IN, OUT): X, W and dY
+ * together within 32 KiB (IONN_ERR_SHAPE otherwise); tb_w, tb_d in [1, 31];
+ * mu_weight in [0, 31]. */
+int int_linear_step_small(const int8_t *X, int8_t *W, const int8_t *dY,
+                          int64_t B, int64_t IN, int64_t OUT, int tb_w,
+                          int mu_weight, int tb_d, int32_t *Y, int32_t *dX,
+                          int8_t *delta, int32_t *G, int32_t *gq,
+                          uint32_t *maxima, int32_t *shifts, void *stream);
+
+/* 1 when int_linear_step_small takes a layer of this shape (B, IN, OUT >= 1
+ * and B*IN + OUT*IN + B*OUT <= 32768), else 0. */
+int int_linear_step_small_fits(int64_t B, int64_t IN, int64_t OUT);
+
 /* niti_quantize_update, which also sets clear[0 .. n_clear) to 0 (device
  * uint32, 0 <= n_clear <= 256, must not overlap *absmax).  For a training
  * loop that alternates two sets of max-combined scalars: the update of one

@@ -30,6 +30,8 @@ SIGNATURES = {
     "niti_quantize": (_I, [_P, _I64, _P, _I, _I, _P, _P, _P]),
     "niti_quantize_update": (_I, [_P, _I64, _P, _I, _I, _P, _P, _P, _P]),
     "niti_quantize_update_clear": (_I, [_P, _I64, _P, _I, _I, _P, _P, _P, _P, _I64, _P]),
+    "int_linear_step_small": (_I, [_P, _P, _P, _I64, _I64, _I64, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "int_linear_step_small_fits": (_I, [_I64, _I64, _I64]),
     "int_output_error": (_I, [_P, _P, _I64, _I64, _I, _P, _P, _P]),
     "int_conv_fwd": (_I, [_P, _P, _P, _P, _P, _P]),
     "int_conv_dgrad": (_I, [_P, _P, _P, _P, _P, _P]),

@@ -112,6 +112,25 @@ def niti_quantize_update(G, absmax, target_bits, mu_weight, W, shifts_out=None, 
           "niti_quantize_update")
 
 
+def int_linear_step_small_fits(B, IN, OUT):
+    return bool(lib().int_linear_step_small_fits(int(B), int(IN), int(OUT)))
+
+
+def int_linear_step_small(X, W, dY, tb_w, mu_weight, tb_d, Y, dX, delta, G, maxima, shifts, gq=None,
+                          stream=None):
+    B, IN = X.shape
+    OUT = W.shape[0]
+    assert tuple(W.shape) == (OUT, IN) and tuple(dY.shape) == (B, OUT), "shape mismatch"
+    assert tuple(Y.shape) == (B, OUT) and tuple(dX.shape) == (B, IN) and tuple(delta.shape) == (B, IN)
+    assert tuple(G.shape) == (OUT, IN) and (gq is None or tuple(gq.shape) == (OUT, IN))
+    check(lib().int_linear_step_small(_p(X, i8, name="X"), _p(W, i8, name="W"), _p(dY, i8, name="dY"), B, IN,
+                                      OUT, int(tb_w), int(mu_weight), int(tb_d), _p(Y, i32, name="Y"),
+                                      _p(dX, i32, name="dX"), _p(delta, i8, name="delta"), _p(G, i32, name="G"),
+                                      _p(gq, i32, OUT * IN, "gq"), _p(maxima, u32, 3, "maxima"),
+                                      _p(shifts, i32, 3, "shifts"), _stream(stream)),
+          "int_linear_step_small")
+
+
 def niti_quantize_update_clear(G, absmax, target_bits, mu_weight, W, clear, shifts_out=None, gq_out=None,
                                stream=None):
     assert G.numel() == W.numel()

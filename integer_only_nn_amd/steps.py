@@ -98,6 +98,17 @@ def linear_step(X, W, dY, buf: LinearStepBuffers, requant_delta=True, tb_w=TB_WE
                                        stream=stream)
 
 
+def linear_step_small(X, W, dY, buf: LinearStepBuffers, tb_w=TB_WEIGHT, mu=MU_WEIGHT, tb_d=TB_DELTA,
+                      stream=None):
+    """The same step as linear_step (with the delta requantised) in one
+    launch, for layers that int_linear_step_small_fits takes: the maxima go
+    to buf.scal[0:3] (written, not combined) and the shifts s_d, s, ws to
+    buf.scal[3:6]."""
+    s = buf.scal
+    ops.int_linear_step_small(X, W, dY, tb_w, mu, tb_d, buf.Y, buf.dX, buf.delta, buf.G, s[0:3], s[3:6],
+                              gq=buf.gq, stream=stream)
+
+
 # ---------------------------------------------------------------------------
 # Multi-layer perceptron (all layers trainable).
 # ---------------------------------------------------------------------------

@@ -263,3 +263,18 @@ def test_update_clear_validation():
     assert f(FAKE, 8, P(0x2000), 8, 2, FAKE, None, None, None, 2, None) == ARG
     assert f(FAKE, 8, P(0x2000), 8, 2, FAKE, None, None, P(0x3002), 2, None) == ALIGN
     assert f(FAKE, 8, P(0x2000), 0, 2, FAKE, None, None, P(0x3000), 2, None) == RANGE
+
+
+def test_linear_step_small_validation():
+    fits = lib.int_linear_step_small_fits
+    assert fits(16, 64, 32) == 1 and fits(128, 128, 64) == 1
+    assert fits(128, 128, 65) == 0 and fits(0, 4, 4) == 0 and fits(4, -1, 4) == 0
+    step = lib.int_linear_step_small
+    args = lambda B, IN, OUT, tbw=8, mu=2, tbd=7, Y=FAKE: (FAKE, FAKE, FAKE, B, IN, OUT, tbw, mu, tbd, Y, FAKE,
+                                                          FAKE, FAKE, None, FAKE, FAKE, None)
+    assert step(*args(256, 784, 256)) == SHAPE
+    assert "32768" in _err()
+    assert step(*args(16, 64, 32, Y=None)) == ARG
+    assert step(*args(16, 64, 32, tbw=0)) == RANGE
+    assert step(*args(16, 64, 32, mu=32)) == RANGE
+    assert step(*args(16, 64, 32, Y=FAKE_ODD)) == ALIGN
