@@ -26,7 +26,9 @@ using namespace gemm;
 template <class SA, class SB>
 void launch_linear(const SA &sa, const SB &sb, const Epi &ep, int M, int N, int K, bool fast,
                    hipStream_t st) {
-    if (fast)
+    // 256 x 256 tiles only with at least 16 of them: a 256 x 256 output as
+    // one workgroup took 25 us where 16 tiles of 64 x 64 take 8
+    if (fast && M >= 1024 && N >= 1024)
         launch<256, 256, 64, 2, 2, false>(sa, sb, ep, M, N, K, 1, st);
     else if (M >= 1024 && N >= 1024)
         launch<256, 256, 64, 2, 2, true>(sa, sb, ep, M, N, K, 1, st);
